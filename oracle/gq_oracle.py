@@ -1,0 +1,267 @@
+"""fp64 CPU oracle for the GuidedQuant Fisher and the LNQ alternating optimisation.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+CPU-baseline leg may import this module.  The product path (the HIP library and
+its Python binding) never imports, calls or links it, and this module imports
+nothing from the product package.
+
+Every function is the plain definition (or, for the iterative LNQ, the steps in
+the pages' order), in float64 with NumPy.  Sources:
+
+  [GQ-obj]   "GuidedQuant" blog page (jinukkim.me/blog/guidedquant), the
+             GuidedQuant objective equation and the sentence after it (block-
+             diagonal Fisher, grouped and averaged within each group).
+  [GQ-lw]    same page, item 1: layer-wise output reconstruction equation.
+  [LNQ-prob] same page, section "LNQ": the per-row problem over a one-hot
+             assignment P^(j) with P 1_m = 1 and a codebook c^(j).
+  [LNQ-alg]  same page, section "LNQ": the repeat-loop with the "(codebook)"
+             closed form and the "(assignment)" coordinate loop i = 1..d_in.
+  [GQ-abs]   aitopics.org "squeezellm" page, GuidedQuant abstract: the
+             non-uniform scalar algorithm decreases the objective monotonically.
+
+Readings where the pages are silent (the same readings the GPU library uses):
+  * F_j = X^T diag(G[:, j]^2) X without the 1/n factor (the objective equation
+    carries a leading n and leaves F_j undefined; LNQ is invariant to scaling F).
+  * Groups are contiguous equal blocks of output channels; averaging F_j over a
+    group equals using s_g[t] = mean_{j in g} G[t, j]^2 (linearity).
+  * Damping: F' = F_g + lambda_g I with lambda_g = rho * mean(diag F_g); F' is
+    used everywhere (objective, codebook, sweep).
+  * Initial codebook: m quantiles of w_j at levels (q + 1/2)/m with linear
+    interpolation between order statistics, stored as float32; initial codes
+    are the nearest entry (lowest index on ties).  Parity unpinned by the pages
+    (they do not state an initialisation); pinned only to the textbook
+    quantile definition.
+  * Empty code q (no coordinate assigned): c_q is kept unchanged.
+  * Assignment: coordinates in ascending order; a coordinate moves only on a
+    strict decrease of the objective, to the lowest-index minimiser.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "group_scale", "fisher", "fisher_entry", "fisher_per_channel", "ridge_lambda",
+    "damped", "init_quantile", "one_hot", "codebook_system", "codebook_update",
+    "assign_deltas", "assign_sweep", "objective", "lnq_row", "guided_loss",
+    "replay_sweep",
+]
+
+
+# ----------------------------------------------------------------------------
+# Fisher [GQ-obj]
+# ----------------------------------------------------------------------------
+
+def group_scale(G: np.ndarray, groups: int) -> np.ndarray:
+    """s_g[t] = mean over the output channels j of group g of G[t, j]^2  -> [groups][n].
+
+    [GQ-obj]: the per-channel blocks F_j are averaged within each group; with
+    F_j = X^T diag(G[:, j]^2) X the average is X^T diag(s_g) X.
+    """
+    G = np.asarray(G, dtype=np.float64)
+    n, d_out = G.shape
+    if d_out % groups:
+        raise ValueError("d_out must be a multiple of groups")
+    size = d_out // groups
+    S = np.empty((groups, n))
+    for g in range(groups):
+        S[g] = np.mean(G[:, g * size:(g + 1) * size] ** 2, axis=1)
+    return S
+
+
+def fisher(X: np.ndarray, G: np.ndarray, groups: int) -> np.ndarray:
+    """Grouped Fisher blocks F_g = X^T diag(s_g) X -> [groups][d_in][d_in]  [GQ-obj]."""
+    X = np.asarray(X, dtype=np.float64)
+    S = group_scale(G, groups)
+    return np.stack([X.T @ (S[g][:, None] * X) for g in range(groups)])
+
+
+def fisher_entry(x_a: np.ndarray, x_b: np.ndarray, s_g: np.ndarray) -> float:
+    """One entry F_g[a, b] = sum_t s_g[t] X[t, a] X[t, b]  [GQ-obj]."""
+    return float(np.dot(np.asarray(s_g, np.float64) * np.asarray(x_a, np.float64),
+                        np.asarray(x_b, np.float64)))
+
+
+def fisher_per_channel(X: np.ndarray, G: np.ndarray) -> np.ndarray:
+    """Per-output-channel blocks F_j = X^T diag(G[:, j]^2) X -> [d_out][d_in][d_in]  [GQ-obj]."""
+    X = np.asarray(X, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    return np.stack([X.T @ ((G[:, j] ** 2)[:, None] * X) for j in range(G.shape[1])])
+
+
+def guided_loss(X: np.ndarray, G: np.ndarray, W: np.ndarray, W_hat: np.ndarray) -> float:
+    """|| G (.) (X W^T - X W_hat^T) ||_F^2 with W stored [d_out][d_in]  [GQ-obj] left side."""
+    X = np.asarray(X, np.float64)
+    Z = X @ np.asarray(W, np.float64).T
+    Z_hat = X @ np.asarray(W_hat, np.float64).T
+    return float(np.sum((np.asarray(G, np.float64) * (Z - Z_hat)) ** 2))
+
+
+# ----------------------------------------------------------------------------
+# Damping (reading: GPTQ-style relative ridge on F itself)
+# ----------------------------------------------------------------------------
+
+def ridge_lambda(F_g: np.ndarray, rho: float) -> float:
+    """lambda_g = rho * mean(diag F_g)."""
+    F_g = np.asarray(F_g, np.float64)
+    return float(rho * np.trace(F_g) / F_g.shape[0])
+
+
+def damped(F_g: np.ndarray, rho: float) -> np.ndarray:
+    """F' = F_g + lambda_g I."""
+    F_g = np.asarray(F_g, np.float64)
+    return F_g + ridge_lambda(F_g, rho) * np.eye(F_g.shape[0])
+
+
+# ----------------------------------------------------------------------------
+# LNQ [LNQ-prob], [LNQ-alg]
+# ----------------------------------------------------------------------------
+
+def init_quantile(w: np.ndarray, m: int):
+    """Initial codebook (m quantiles of w at levels (q+1/2)/m, float32-stored) and codes.
+
+    Quantile at level t of N sorted values: position h = (N-1) t, value
+    x[floor h] + frac(h) * (x[floor h + 1] - x[floor h]).  The position is
+    formed as (N-1)(2q+1) / (2m).  Codes: index of the nearest entry, the
+    lowest index on ties, compared in float64 on the stored float32 values.
+    """
+    w = np.asarray(w, np.float64)
+    xs = np.sort(w)
+    N = xs.shape[0]
+    c = np.empty(m)
+    for q in range(m):
+        h = float((N - 1) * (2 * q + 1)) / float(2 * m)
+        lo = int(np.floor(h))
+        frac = h - lo
+        hi = min(lo + 1, N - 1)
+        c[q] = xs[lo] + frac * (xs[hi] - xs[lo])
+    c = c.astype(np.float32).astype(np.float64)
+    p = np.argmin(np.abs(w[:, None] - c[None, :]), axis=1).astype(np.int64)
+    return c, p
+
+
+def one_hot(p: np.ndarray, m: int) -> np.ndarray:
+    """P^(j) in {0,1}^{d_in x m} with P 1_m = 1  [LNQ-prob]."""
+    p = np.asarray(p, np.int64)
+    Q = np.zeros((p.shape[0], m))
+    Q[np.arange(p.shape[0]), p] = 1.0
+    return Q
+
+
+def codebook_system(Fp: np.ndarray, w: np.ndarray, p: np.ndarray, m: int):
+    """A = P^T F' P and b = P^T F' w of the "(codebook)" step  [LNQ-alg]."""
+    Q = one_hot(p, m)
+    A = Q.T @ Fp @ Q
+    b = Q.T @ (Fp @ np.asarray(w, np.float64))
+    return A, b
+
+
+def codebook_update(Fp: np.ndarray, w: np.ndarray, p: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """c <- (P^T F' P)^{-1} P^T F' w on the non-empty codes; empty codes keep c  [LNQ-alg]."""
+    m = c.shape[0]
+    A, b = codebook_system(Fp, w, p, m)
+    counts = np.bincount(np.asarray(p, np.int64), minlength=m)
+    S = np.nonzero(counts > 0)[0]
+    L = np.linalg.cholesky(A[np.ix_(S, S)])
+    y = np.linalg.solve(L, b[S])
+    x = np.linalg.solve(L.T, y)
+    c_new = np.array(c, dtype=np.float64, copy=True)
+    c_new[S] = x
+    return c_new
+
+
+def objective(Fp: np.ndarray, w: np.ndarray, c: np.ndarray, p: np.ndarray) -> float:
+    """(w_hat - w)^T F' (w_hat - w) with w_hat = P c  [LNQ-prob], [GQ-obj]."""
+    e = np.asarray(c, np.float64)[np.asarray(p, np.int64)] - np.asarray(w, np.float64)
+    return float(e @ (Fp @ e))
+
+
+def assign_deltas(Fp_ii: float, r_i: float, c: np.ndarray, cur: float) -> np.ndarray:
+    """Exact objective change when coordinate i moves from value `cur` to each c_q.
+
+    With r = F'(w_hat - w) and delta = c_q - cur:
+      (e + delta u_i)^T F' (e + delta u_i) - e^T F' e = delta (F'_ii delta + 2 r_i).
+    """
+    delta = np.asarray(c, np.float64) - cur
+    return delta * (Fp_ii * delta + 2.0 * r_i)
+
+
+def assign_sweep(Fp: np.ndarray, w: np.ndarray, c: np.ndarray, p: np.ndarray,
+                 return_steps: bool = False):
+    """One "(assignment)" pass over i = 1..d_in in order  [LNQ-alg].
+
+    For each coordinate, pick the codebook entry minimising the row objective
+    with every other coordinate fixed; keep the current entry unless some entry
+    strictly decreases it, then take the lowest-index minimiser.
+    """
+    c = np.asarray(c, np.float64)
+    p = np.array(p, dtype=np.int64, copy=True)
+    w = np.asarray(w, np.float64)
+    r = Fp @ (c[p] - w)
+    steps = []
+    for i in range(w.shape[0]):
+        D = assign_deltas(Fp[i, i], r[i], c, c[p[i]])
+        q = int(np.argmin(D))          # first occurrence = lowest index
+        if return_steps:
+            steps.append(D.copy())
+        if D[q] < 0.0:
+            r += (c[q] - c[p[i]]) * Fp[:, i]
+            p[i] = q
+    if return_steps:
+        return p, steps
+    return p
+
+
+def lnq_row(Fp: np.ndarray, w: np.ndarray, m: int, iters: int, c0=None, p0=None):
+    """LNQ for one row: init, then `iters` x (codebook, assignment)  [LNQ-alg].
+
+    Returns (c, p, trace) with trace[0] the objective at the start and
+    trace[2t-1], trace[2t] after the codebook and assignment steps of pass t.
+    """
+    if c0 is None:
+        c, p = init_quantile(w, m)
+    else:
+        c = np.asarray(c0, np.float64).copy()
+        p = np.asarray(p0, np.int64).copy()
+    trace = [objective(Fp, w, c, p)]
+    for _ in range(iters):
+        c = codebook_update(Fp, w, p, c)
+        trace.append(objective(Fp, w, c, p))
+        p = assign_sweep(Fp, w, c, p)
+        trace.append(objective(Fp, w, c, p))
+    return c, p, np.array(trace)
+
+
+def replay_sweep(Fp: np.ndarray, w: np.ndarray, c: np.ndarray, p_start: np.ndarray,
+                 p_dev: np.ndarray, tol_rel: float):
+    """Walk one assignment pass in order but follow the device's decisions.
+
+    At each coordinate the exact fp64 changes D_q are formed from the current
+    state; the device's choice q_dev must satisfy
+        D[q_dev] <= min(min_q D_q, 0) + tol_rel * |objective of the row so far|.
+    Returns (worst excess over the allowance (<= 0 means every decision is
+    valid), number of decisions that differ from the fp64 choice).
+    """
+    c = np.asarray(c, np.float64)
+    p = np.array(p_start, dtype=np.int64, copy=True)
+    p_dev = np.asarray(p_dev, np.int64)
+    w = np.asarray(w, np.float64)
+    e = c[p] - w
+    r = Fp @ e
+    obj = float(e @ r)
+    worst = -np.inf
+    differ = 0
+    for i in range(w.shape[0]):
+        D = assign_deltas(Fp[i, i], r[i], c, c[p[i]])
+        q_ref = int(np.argmin(D))
+        best = min(float(D[q_ref]), 0.0)
+        if not D[q_ref] < 0.0:
+            q_ref = int(p[i])
+        q = int(p_dev[i])
+        worst = max(worst, float(D[q]) - best - tol_rel * abs(obj))
+        if q != q_ref:
+            differ += 1
+        if q != p[i]:
+            r += (c[q] - c[p[i]]) * Fp[:, i]
+            obj += float(D[q])
+            p[i] = q
+    return worst, differ

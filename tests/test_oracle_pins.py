@@ -1,0 +1,408 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a hand-worked
+example, brute force, a closed-form identity, or a textbook special case.
+CPU only.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from post_weight_quantization_gq_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+def _spd(rng, d, n=None, diag_boost=0.0):
+    n = n or 3 * d
+    y = rng.standard_normal((n, d))
+    return y.T @ y / n + diag_boost * np.eye(d)
+
+
+# --------------------------------------------------------------------------
+# Hand-worked examples (GuidedQuant blog page: objective equation, LNQ box)
+# --------------------------------------------------------------------------
+
+def test_golden_fisher():
+    ex = json.load(open(GOLDEN))["fisher"]
+    X, G = np.array(ex["X"]), np.array(ex["G"])
+    np.testing.assert_allclose(O.fisher(X, G, 1), np.array(ex["groups_1"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(O.fisher(X, G, 2), np.array(ex["groups_2"]), rtol=0, atol=1e-13)
+
+
+def test_golden_codebook():
+    ex = json.load(open(GOLDEN))["codebook"]
+    F, w, p = np.array(ex["F"]), np.array(ex["w"]), np.array(ex["p"])
+    A, b = O.codebook_system(F, w, p, 2)
+    np.testing.assert_allclose(A, np.array(ex["A"]), atol=1e-14)
+    np.testing.assert_allclose(b, np.array(ex["b"]), atol=1e-14)
+    c = O.codebook_update(F, w, p, np.array(ex["c_old"]))
+    np.testing.assert_allclose(c, np.array(ex["c"]), rtol=1e-15)
+
+
+def test_golden_sweep():
+    ex = json.load(open(GOLDEN))["sweep"]
+    F, w, c = np.array(ex["F"]), np.array(ex["w"]), np.array(ex["c"])
+    p0 = np.array(ex["p_start"])
+    assert O.objective(F, w, c, p0) == pytest.approx(ex["objective_start"], abs=1e-14)
+    p1 = O.assign_sweep(F, w, c, p0)
+    assert list(p1) == ex["p_end"]
+    assert O.objective(F, w, c, p1) == pytest.approx(ex["objective_end"], abs=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Fisher: brute-force sums, the GuidedQuant identity, invariants
+# --------------------------------------------------------------------------
+
+def test_fisher_bruteforce_loops():
+    rng = _rng(1)
+    n, d, d_out = 7, 4, 6
+    X = rng.standard_normal((n, d))
+    G = rng.laplace(0, 1.0, (n, d_out))
+    for groups in (1, 2, 3, 6):
+        F = O.fisher(X, G, groups)
+        size = d_out // groups
+        for g in range(groups):
+            for a in range(d):
+                for b in range(d):
+                    acc = 0.0
+                    for t in range(n):
+                        s = sum(G[t, j] * G[t, j] for j in range(g * size, (g + 1) * size)) / size
+                        acc += s * X[t, a] * X[t, b]
+                    assert F[g, a, b] == pytest.approx(acc, rel=1e-12, abs=1e-14)
+
+
+def test_guidedquant_identity_tiny_workload():
+    """|| G (.) (X W^T - X W_hat^T) ||^2 = sum_j e_j^T F_j e_j  (objective equation, no 1/n)."""
+    inp = synth.make_inputs("tiny", seed=3)
+    X, W, G = (synth.decode(inp[k]) for k in ("X", "W", "G"))
+    rng = _rng(2)
+    W_hat = W + 0.01 * rng.standard_normal(W.shape)
+    lhs = O.guided_loss(X, G, W, W_hat)
+    Fj = O.fisher_per_channel(X, G)
+    E = W_hat - W
+    rhs = sum(E[j] @ Fj[j] @ E[j] for j in range(W.shape[0]))
+    assert lhs == pytest.approx(rhs, rel=1e-10)
+    # group average of the per-channel blocks equals the grouped Fisher
+    for groups in (1, 2, 4):
+        Fg = O.fisher(X, G, groups)
+        size = W.shape[0] // groups
+        for g in range(groups):
+            np.testing.assert_allclose(Fg[g], Fj[g * size:(g + 1) * size].mean(0), rtol=1e-12,
+                                       atol=1e-12 * np.abs(Fg[g]).max())
+
+
+def test_layerwise_special_case():
+    """G == 1 reduces the guided loss to the layer-wise reconstruction loss (item 1)."""
+    rng = _rng(4)
+    n, d, d_out = 40, 8, 5
+    X = rng.standard_normal((n, d))
+    W = rng.standard_normal((d_out, d))
+    W_hat = W + 0.1 * rng.standard_normal(W.shape)
+    G = np.ones((n, d_out))
+    lhs = float(np.sum((X @ W.T - X @ W_hat.T) ** 2))
+    F = O.fisher(X, G, 1)[0]
+    rhs = sum((W_hat[j] - W[j]) @ F @ (W_hat[j] - W[j]) for j in range(d_out))
+    assert lhs == pytest.approx(rhs, rel=1e-12)
+    assert O.guided_loss(X, G, W, W_hat) == pytest.approx(lhs, rel=1e-13)
+
+
+def test_fisher_invariants():
+    rng = _rng(5)
+    n, d, d_out = 64, 12, 8
+    X = rng.standard_normal((n, d))
+    G = rng.laplace(0, 1e-3, (n, d_out))
+    F = O.fisher(X, G, 2)
+    S = O.group_scale(G, 2)
+    for g in range(2):
+        assert np.abs(F[g] - F[g].T).max() <= 1e-12 * np.abs(F[g]).max()
+        assert np.linalg.eigvalsh(F[g]).min() >= -1e-12 * np.abs(F[g]).max()
+        assert np.trace(F[g]) == pytest.approx(float(np.sum(S[g] * np.sum(X * X, 1))), rel=1e-12)
+    # additivity over token chunks
+    F1 = O.fisher(X[:20], G[:20], 2)
+    F2 = O.fisher(X[20:], G[20:], 2)
+    np.testing.assert_allclose(F1 + F2, F, rtol=1e-12, atol=1e-15)
+
+
+def test_fisher_entry_matches_definition():
+    rng = _rng(6)
+    X = rng.standard_normal((50, 6))
+    G = rng.standard_normal((50, 4))
+    F = O.fisher(X, G, 2)
+    S = O.group_scale(G, 2)
+    for g, a, b in [(0, 0, 0), (1, 2, 5), (0, 5, 3)]:
+        assert O.fisher_entry(X[:, a], X[:, b], S[g]) == pytest.approx(F[g, a, b], rel=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Assignment step: residual-form deltas against brute-force re-evaluation
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sweep_deltas_bruteforce(seed):
+    rng = _rng(10 + seed)
+    d, m = 9, 4
+    F = _spd(rng, d)
+    w = rng.standard_normal(d)
+    c = np.sort(rng.standard_normal(m))
+    p = rng.integers(0, m, d)
+    p_end, steps = O.assign_sweep(F, w, c, p, return_steps=True)
+    # replay and check every delta by re-evaluating the objective directly
+    pc = p.copy()
+    for i in range(d):
+        base = O.objective(F, w, c, pc)
+        for q in range(m):
+            trial = pc.copy()
+            trial[i] = q
+            assert steps[i][q] == pytest.approx(O.objective(F, w, c, trial) - base,
+                                                rel=1e-9, abs=1e-12)
+        best = int(np.argmin(steps[i]))
+        if steps[i][best] < 0:
+            pc[i] = best
+    assert np.array_equal(pc, p_end)
+
+
+def test_sweep_is_one_opt_at_fixed_point():
+    rng = _rng(20)
+    d, m = 8, 3
+    F = _spd(rng, d)
+    w = rng.standard_normal(d)
+    c = np.sort(rng.standard_normal(m))
+    p = rng.integers(0, m, d)
+    for _ in range(50):
+        p_new = O.assign_sweep(F, w, c, p)
+        if np.array_equal(p_new, p):
+            break
+        p = p_new
+    base = O.objective(F, w, c, p)
+    for i in range(d):
+        for q in range(m):
+            t = p.copy()
+            t[i] = q
+            assert O.objective(F, w, c, t) >= base - 1e-12
+
+
+def test_sweep_diagonal_F_is_global_optimum():
+    """Diagonal F: one sweep reaches the brute-force optimum over all m^d assignments."""
+    rng = _rng(21)
+    d, m = 7, 4
+    F = np.diag(rng.uniform(0.5, 2.0, d))
+    w = rng.standard_normal(d)
+    c = np.sort(rng.standard_normal(m))
+    p0 = rng.integers(0, m, d)
+    p = O.assign_sweep(F, w, c, p0)
+    best = min(O.objective(F, w, c, np.array(t)) for t in itertools.product(range(m), repeat=d))
+    assert O.objective(F, w, c, p) == pytest.approx(best, rel=1e-12, abs=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Codebook step: normal equations, exact minimiser, empty codes
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(3))
+def test_codebook_normal_equations_and_minimiser(seed):
+    rng = _rng(30 + seed)
+    d, m = 24, 8
+    F = _spd(rng, d)
+    w = rng.standard_normal(d)
+    p = rng.integers(0, m - 2, d)          # codes m-2, m-1 stay empty
+    c_old = np.sort(rng.standard_normal(m))
+    c = O.codebook_update(F, w, p, c_old)
+    e = c[p] - w
+    grad = O.one_hot(p, m).T @ (F @ e)     # P^T F (w_hat - w)
+    S = np.bincount(p, minlength=m) > 0
+    assert np.abs(grad[S]).max() <= 1e-10 * np.abs(O.one_hot(p, m).T @ F @ w).max()
+    np.testing.assert_array_equal(c[~S], c_old[~S])
+    base = O.objective(F, w, c, p)
+    for q in np.nonzero(S)[0]:
+        for eps in (1e-3, -1e-3, 1e-6, -1e-6):
+            cc = c.copy()
+            cc[q] += eps
+            assert O.objective(F, w, cc, p) >= base
+
+
+def test_codebook_identity_F_is_cluster_mean():
+    rng = _rng(40)
+    d, m = 30, 4
+    w = rng.standard_normal(d)
+    p = rng.integers(0, m, d)
+    c = O.codebook_update(np.eye(d), w, p, np.zeros(m))
+    for q in range(m):
+        if np.any(p == q):
+            assert c[q] == pytest.approx(float(np.mean(w[p == q])), rel=1e-12, abs=1e-15)
+
+
+def test_codebook_diagonal_F_is_weighted_mean():
+    rng = _rng(41)
+    d, m = 30, 4
+    f = rng.uniform(0.1, 3.0, d)
+    w = rng.standard_normal(d)
+    p = rng.integers(0, m, d)
+    c = O.codebook_update(np.diag(f), w, p, np.zeros(m))
+    for q in range(m):
+        sel = p == q
+        if np.any(sel):
+            assert c[q] == pytest.approx(float(np.sum(f[sel] * w[sel]) / np.sum(f[sel])), rel=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Whole LNQ loop
+# --------------------------------------------------------------------------
+
+def _lloyd_1d(w, c, p, iters):
+    """Textbook 1-D Lloyd k-means with LNQ's conventions (empty centre kept,
+    move only to a strictly closer centre, lowest index among the closest)."""
+    c = c.copy()
+    p = p.copy()
+    for _ in range(iters):
+        for q in range(len(c)):
+            members = [w[i] for i in range(len(w)) if p[i] == q]
+            if members:
+                c[q] = sum(members) / len(members)
+        for i in range(len(w)):
+            dist = [(w[i] - c[q]) ** 2 for q in range(len(c))]
+            best = min(range(len(c)), key=lambda q: (dist[q], q))
+            if dist[best] < dist[p[i]]:
+                p[i] = best
+    return c, p
+
+
+def test_lnq_identity_F_is_lloyd():
+    rng = _rng(50)
+    d, m = 200, 8
+    w = rng.standard_normal(d) * 0.02
+    c0, p0 = O.init_quantile(w, m)
+    c, p, trace = O.lnq_row(np.eye(d), w, m, 6)
+    cl, pl = _lloyd_1d(w, c0, p0, 6)
+    assert np.array_equal(p, pl)
+    np.testing.assert_allclose(c, cl, rtol=1e-12, atol=1e-16)
+
+
+def test_lnq_monotone_and_bruteforce_bound():
+    rng = _rng(51)
+    d, m = 8, 3
+    F = _spd(rng, d, n=5)                 # rank-deficient: the ridge keeps F' PD
+    Fp = O.damped(F, 1e-6)
+    w = rng.standard_normal(d)
+    c, p, trace = O.lnq_row(Fp, w, m, 8)
+    assert np.all(np.diff(trace) <= 1e-12 * trace[0])
+    # joint brute force: for each assignment, the best codebook is the codebook step
+    best = np.inf
+    for t in itertools.product(range(m), repeat=d):
+        t = np.array(t)
+        cc = O.codebook_update(Fp, w, t, np.zeros(m))
+        best = min(best, O.objective(Fp, w, cc, t))
+    assert trace[-1] >= best - 1e-12 * abs(best)
+
+
+def test_lnq_monotone_on_tiny_workload_rows():
+    inp = synth.make_inputs("tiny", seed=0)
+    X, W, G = (synth.decode(inp[k]) for k in ("X", "W", "G"))
+    Fp = O.damped(O.fisher(X, G, 1)[0], 1e-6)
+    for j in range(6):
+        c, p, trace = O.lnq_row(Fp, W[j], 8, 5)
+        assert np.all(np.diff(trace) <= 1e-12 * trace[0])
+        assert trace[-1] < trace[0]
+
+
+def test_lnq_scale_invariance():
+    rng = _rng(52)
+    d, m = 40, 4
+    F = _spd(rng, d)
+    w = rng.standard_normal(d)
+    r1 = O.lnq_row(O.damped(F, 1e-6), w, m, 4)
+    r2 = O.lnq_row(O.damped(37.5 * F, 1e-6), w, m, 4)
+    assert np.array_equal(r1[1], r2[1])
+    np.testing.assert_allclose(r1[0], r2[0], rtol=1e-10)
+
+
+def test_ridge_makes_rank_deficient_fisher_solvable():
+    rng = _rng(53)
+    d, m = 16, 4
+    y = rng.standard_normal((3, d))          # rank 3 < d
+    F = y.T @ y
+    w = rng.standard_normal(d)
+    p = rng.integers(0, m, d)
+    c = O.codebook_update(O.damped(F, 1e-6), w, p, np.zeros(m))
+    assert np.all(np.isfinite(c))
+
+
+# --------------------------------------------------------------------------
+# Initialisation (reading; pinned to the textbook linear quantile)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,m", [(128, 8), (4096, 8), (11008, 4), (100, 16), (5, 2)])
+def test_init_quantile_is_textbook_linear_quantile(N, m):
+    rng = _rng(N + m)
+    w = synth.decode(synth.f32_to_bf16_bits(rng.standard_normal(N).astype(np.float32) * 0.02))
+    c, p = O.init_quantile(w, m)
+    ref = np.quantile(w, (np.arange(m) + 0.5) / m, method="linear").astype(np.float32)
+    ulp = np.spacing(np.abs(ref).astype(np.float32))
+    assert np.all(np.abs(c - ref.astype(np.float64)) <= ulp)
+    assert np.all(np.diff(c) >= 0)
+    for i in range(N):
+        dist = np.abs(w[i] - c)
+        assert dist[p[i]] == dist.min()
+        assert p[i] == int(np.nonzero(dist == dist.min())[0][0])
+
+
+# --------------------------------------------------------------------------
+# Teacher-forced replay (the device-decision checker)
+# --------------------------------------------------------------------------
+
+def test_replay_accepts_own_decisions_and_rejects_a_planted_one():
+    rng = _rng(60)
+    d, m = 64, 8
+    F = _spd(rng, d)
+    w = rng.standard_normal(d)
+    c = np.sort(rng.standard_normal(m))
+    p0 = rng.integers(0, m, d)
+    p1 = O.assign_sweep(F, w, c, p0)
+    worst, differ = O.replay_sweep(F, w, c, p0, p1, 1e-5)
+    assert worst <= 0 and differ == 0
+    bad = p1.copy()
+    # plant a clearly worse choice at the first coordinate
+    D = O.assign_deltas(F[0, 0], (F @ (c[p0] - w))[0], c, c[p0[0]])
+    bad[0] = int(np.argmax(D))
+    worst, differ = O.replay_sweep(F, w, c, p0, bad, 1e-5)
+    assert worst > 0 and differ >= 1
+
+
+# --------------------------------------------------------------------------
+# Input generator (not the method): bf16 rounding and determinism
+# --------------------------------------------------------------------------
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    rng = _rng(70)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    x[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0]   # exact ties
+    ours = synth.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    back = synth.bf16_bits_to_f32(ours)
+    assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_generator_deterministic_and_prefix_stable():
+    a = synth.make_inputs("tiny", seed=7)
+    b = synth.make_inputs("tiny", seed=7)
+    for k in ("X", "W", "G"):
+        assert np.array_equal(a[k], b[k])
+    c = synth.make_inputs("tiny", seed=7, tokens=100, rows=10)
+    assert np.array_equal(c["X"], a["X"][:100])
+    assert np.array_equal(c["W"], a["W"][:10])
+    wl = synth.workload("tiny")
+    X = synth.decode(a["X"])
+    # four outlier columns scaled x20
+    big = np.sort(np.argsort(np.std(X, 0))[-4:])
+    assert np.array_equal(big, a["outlier_cols"])
+    assert wl.m == 8
