@@ -1,0 +1,228 @@
+"""Benchmark of the GuidedQuant Fisher + LNQ hot path on one MI355X.
+
+One step = the whole path on one synthetic layer with inputs resident in HBM:
+grouped Fisher accumulation from (X, G), then LNQ (init + `iters` x (codebook
+step, assignment pass) + objective trace) on every output row.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is rows quantized per second for the whole
+layer (Fisher included); the Fisher TFLOP/s, the LNQ-only rows/s and the
+per-stage times (HIP events recorded by the library on its stream) are extra
+fields.  `roofline` is for the stage that takes the most time.  The
+`cpu_baseline` leg times the fp64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_MFMA = 2500e12      # dense bf16 matrix-core FLOP/s
+PEAK_FP32_VALU = 157.3e12     # fp32 vector FLOP/s (FMA = 2 flops, packed)
+PEAK_HBM = 8e12               # bytes/s
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama2_7b_attn")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    return ap.parse_args()
+
+
+def _stage_units(stage, wl, changed_total):
+    """Algorithmic work of a stage in one step: (bound, amount, peak, unit)."""
+    n, d, d_out, G, m, it = wl.n, wl.d_in, wl.d_out, wl.groups, wl.m, wl.iters
+    if stage == "fisher_mfma":
+        # unique entries of the symmetric F_g: n d (d + 1) flops per group
+        return "mfma", n * d * (d + 1) * G, PEAK_BF16_MFMA, "TFLOP/s"
+    if stage == "lnq_u":
+        # the codebook gather: each row sums F' over the coordinates of each code,
+        # d^2 adds per row and codebook step (add-only: half the FMA peak)
+        return "alu", it * d_out * d * d, PEAK_FP32_VALU / 2, "TFLOP/s"
+    if stage == "lnq_sweep":
+        # m candidate changes (3 flops each) per coordinate, 2 d flops per move
+        return "alu", it * d_out * d * 3 * m + 2 * d * changed_total, PEAK_FP32_VALU, "TFLOP/s"
+    if stage == "lnq_solve":
+        # per codebook step: read U (m values), V, codes, W; write the residual
+        return "hbm", (it + 1) * d_out * d * (4 * m + 4 + 1 + 2 + 4), PEAK_HBM, "GB/s"
+    if stage == "group_scale":
+        return "hbm", 2 * n * d_out + 4 * G * n, PEAK_HBM, "GB/s"
+    if stage == "lnq_wf":
+        return "mfma", 2 * d_out * d * d, PEAK_BF16_MFMA, "TFLOP/s"
+    return None
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import post_weight_quantization_gq_amd as gq
+    from post_weight_quantization_gq_amd import synth
+
+    dev = torch.device("cuda:0")
+    wl = synth.workload(args.workload)
+    print(f"[bench] workload {wl.name}: d_in={wl.d_in} d_out={wl.d_out} n={wl.n} "
+          f"groups={wl.groups} bits={wl.bits} iters={wl.iters} block={wl.block}",
+          file=sys.stderr, flush=True)
+    t0 = time.time()
+    inp = synth.make_inputs(wl, seed=args.seed)
+
+    def dv(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    X, G, W = dv(inp["X"]), dv(inp["G"]), dv(inp["W"])
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    F = torch.empty((wl.groups, wl.d_in, wl.d_in), dtype=torch.float32, device=dev)
+    ws_f = torch.empty(max(1, gq.fisher_workspace_size(wl.n, wl.d_in, wl.d_out, wl.groups)),
+                       dtype=torch.uint8, device=dev)
+    ws_l = torch.empty(max(1, gq.lnq_workspace_size(wl.d_out, wl.d_in, wl.groups, wl.bits)),
+                       dtype=torch.uint8, device=dev)
+    C = torch.empty((wl.d_out, wl.m), dtype=torch.float32, device=dev)
+    P = torch.empty((wl.d_out, wl.d_in), dtype=torch.uint8, device=dev)
+
+    def step():
+        gq.gq_fisher_accumulate(X, G, wl.groups, F=F, ws=ws_f)
+        return gq.lnq_quantize(W, F, wl.bits, wl.iters, block=wl.block, ridge_rel=1e-6, C=C,
+                               P=P, init=gq.GQ_INIT_QUANTILE, ws=ws_l)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+
+    gq.gq_timing_read()               # drop anything recorded so far
+    gq.gq_timing_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    outs = None
+    for _ in range(args.steps):
+        outs = step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    gq.gq_timing_enable(False)
+    stages = gq.gq_timing_read()
+    ms_step = (t_end - t_start) * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_step:.2f} ms/step", file=sys.stderr, flush=True)
+
+    trace = outs[2].cpu().numpy()
+    nchg = outs[3].cpu().numpy()
+    per_step = {k: v[0] / args.steps for k, v in stages.items() if v[1]}
+    launches = {k: v[1] / args.steps for k, v in stages.items() if v[1]}
+    fisher_ms = per_step.get("group_scale", 0) + per_step.get("fisher_mfma", 0) + \
+        per_step.get("fisher_finalize", 0) + per_step.get("fisher_plain", 0)
+    lnq_ms = sum(v for k, v in per_step.items() if k.startswith("lnq"))
+    sym_flops = wl.n * wl.d_in * (wl.d_in + 1) * wl.groups
+
+    # roofline of the stage with the largest share of the step
+    dom = max(per_step, key=per_step.get)
+    roof = None
+    spec = _stage_units(dom, wl, float(np.sum(nchg)))
+    if spec is not None:
+        bound, amount, peak, unit = spec
+        avg_ms = per_step[dom] / launches[dom]
+        per_launch = amount / launches[dom]
+        achieved = per_launch / (avg_ms * 1e-3)
+        scale = 1e9 if unit == "GB/s" else 1e12
+        roof = {"kernel": dom, "bound": bound, "achieved": achieved / scale, "peak": peak / scale,
+                "unit": unit, "frac": achieved / peak, "traffic": None,
+                "avg_launch_ms": avg_ms, "units_per_launch": per_launch}
+
+    result = {
+        "metric": "LNQ rows quantized/s + Fisher TFLOP/s at 4096x4096, 3-bit, 1 MI355X",
+        "value": wl.d_out / (ms_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "d_in": wl.d_in, "d_out": wl.d_out, "n_tokens": wl.n,
+                   "groups": wl.groups, "bits": wl.bits, "iters": wl.iters, "block": wl.block},
+        "fisher_tflops": sym_flops / (fisher_ms * 1e-3) / 1e12 if fisher_ms else None,
+        "fisher_tflops_gemm_convention": (2 * wl.n * wl.d_in ** 2 * wl.groups) /
+        (fisher_ms * 1e-3) / 1e12 if fisher_ms else None,
+        "lnq_rows_per_s": wl.d_out / (lnq_ms * 1e-3) if lnq_ms else None,
+        "s_per_layer": ms_step * 1e-3,
+        "stage_ms_per_step": {k: round(v, 4) for k, v in per_step.items()},
+        "stage_launches_per_step": launches,
+        "changed_per_sweep": [int(x) for x in nchg],
+        "objective_trace": [float(x) for x in trace],
+        "monotone": bool(np.all(trace[1:] <= trace[:-1] * (1 + 1e-6))),
+        "roofline": roof,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, inp, F, args)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, inp, F, args):
+    """Time the fp64 oracle on a bounded sample of the same layer, scaled to rows/s."""
+    import oracle as O
+    from post_weight_quantization_gq_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    print("[bench] cpu baseline: oracle Fisher on a token sample", file=sys.stderr, flush=True)
+    nt = min(args.cpu_tokens, wl.n)
+    Xs = synth.decode(inp["X"][:nt])
+    Gs = synth.decode(inp["G"][:nt])
+    t0 = time.perf_counter()
+    O.fisher(Xs, Gs, wl.groups)
+    t_f = (time.perf_counter() - t0) * (wl.n / nt)
+    print(f"[bench] cpu baseline: oracle LNQ on {args.cpu_rows} rows", file=sys.stderr,
+          flush=True)
+    F64 = F.cpu().double().numpy()
+    w = synth.decode(inp["W"])
+    rpg = wl.d_out // wl.groups
+    rows = [(r * rpg) % wl.d_out for r in range(args.cpu_rows)]
+    t_rows = 0.0
+    for j in rows:
+        Fp = O.damped(F64[j // rpg], 1e-6)
+        t0 = time.perf_counter()
+        O.lnq_row(Fp, w[j], wl.m, wl.iters)
+        t_rows += time.perf_counter() - t0
+    t_row = t_rows / len(rows)
+    t_layer = t_f + t_row * wl.d_out
+    return {"value": wl.d_out / t_layer, "unit": "rows/s", "cores": blas_threads,
+            "kind": "oracle",
+            "sample": f"Fisher on the first {nt} of {wl.n} tokens (scaled x{wl.n / nt:g}, "
+                      f"{t_f * nt / wl.n:.1f}s measured) + LNQ on {len(rows)} rows "
+                      f"({t_row:.2f}s/row, scaled to {wl.d_out} rows); LNQ rows run on one "
+                      f"core, the Fisher matmul on {blas_threads} BLAS threads",
+            "fisher_s_est": t_f, "lnq_s_per_row": t_row}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+/*
+ * gq.h — C ABI of libgq.so: grouped Fisher accumulation (GuidedQuant) and the
+ * LNQ alternating optimisation on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources (the "GuidedQuant" blog page, jinukkim.me/blog/guidedquant):
+ *   - GuidedQuant objective equation: || dl/dZ (.) (XW - XW_hat) ||_F^2
+ *     = n sum_j (w_j - w_hat_j)^T F_j (w_j - w_hat_j), with block-diagonal
+ *     Fisher blocks F_j that are grouped and averaged within each group.
+ *   - Section "LNQ": per-row problem over a one-hot assignment P^(j)
+ *     (P 1_m = 1) and a codebook c^(j) in R^m; the algorithm box alternates
+ *     "(codebook)" c <- (P^T F P)^{-1} P^T F w and "(assignment)" over
+ *     i = 1..d_in, each coordinate taking the codebook entry that minimises
+ *     (w_hat - w)^T F (w_hat - w).
+ *
+ * Conventions shared by every entry point
+ *   Layout.   Row-major, contiguous.  X [n][d_in] (calibration activations,
+ *             one token per row), G [n][d_out] (end-loss gradients dl/dZ),
+ *             W [d_out][d_in] (row j is the page's column w_j), F
+ *             [groups][d_in][d_in] float32 symmetric, C [d_out][m] float32,
+ *             P [d_out][d_in] uint8 codes in [0, m).  m = 2^bits.
+ *   Groups.   Output channel j belongs to group j / (d_out / groups); groups
+ *             are contiguous equal blocks (d_out % groups == 0).
+ *   F_g.      X^T diag(s_g) X with s_g[t] = mean_{j in g} G[t, j]^2 (the
+ *             1/n of the objective equation is not applied; LNQ does not
+ *             depend on the scale of F).
+ *   Damping.  Every LNQ call works with F'_g = F_g + lambda_g I,
+ *             lambda_g = ridge_rel * mean(diag F_g), formed on the fly.
+ *   Memory.   Every array argument is a device pointer (HIP global memory)
+ *             unless stated otherwise.  The caller owns all buffers; the
+ *             library keeps no pointer after a call returns.
+ *   Alignment. X, G, W, F and P must be 16-byte aligned, ws 256-byte aligned
+ *             (GQ_EINVAL otherwise).  F must be exactly symmetric, as
+ *             gq_fisher_accumulate writes it.
+ *   Workspace. ws/ws_bytes is caller-owned device scratch of at least the
+ *             size the matching *_workspace_size() returns.  ws == NULL asks
+ *             the library to allocate it stream-ordered (hipMallocAsync /
+ *             hipFreeAsync on `stream`).
+ *   Streams.  `stream` is a hipStream_t (NULL = default stream).  Calls only
+ *             enqueue work; outputs are valid once the stream is synchronised.
+ *             Calls on one stream are ordered; the library holds no global
+ *             mutable state besides the thread-local error string.
+ *   Errors.   Arguments are validated before anything is enqueued; on a
+ *             non-OK status no output has been touched and gq_last_error()
+ *             (thread-local) says why.  GQ_EHIP reports a failed HIP call.
+ *   Precision. Fisher: bfloat16 inputs, MFMA with float32 accumulation; the
+ *             gradient-square scale is applied to one operand, rounded to
+ *             bfloat16.  float32 inputs take a float64-accumulating path.
+ *             LNQ: F' is split into bfloat16 planes (hi + lo) for the matrix
+ *             cores, residuals and codebook systems are accumulated in
+ *             float32, the m x m solve and all objectives are float64.
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQ_ABI_VERSION 1
+
+typedef enum {
+    GQ_OK = 0,
+    GQ_EINVAL = 1,    /* bad argument value (null pointer, bits, block, iters, workspace too small) */
+    GQ_ESHAPE = 2,    /* inconsistent sizes (d_out % groups, d_in % block, empty shapes) */
+    GQ_EDTYPE = 3,    /* unsupported dtype code */
+    GQ_ENOMEM = 4,    /* library-side workspace allocation failed */
+    GQ_EHIP = 5,      /* a HIP runtime call or kernel launch failed */
+    GQ_ENOTIMPL = 8   /* valid request outside what this build supports */
+} gq_status;
+
+typedef enum { GQ_F32 = 0, GQ_BF16 = 1 } gq_dtype;
+
+typedef enum { GQ_INIT_QUANTILE = 0, GQ_INIT_GIVEN = 1 } gq_lnq_init;
+
+typedef struct {
+    int32_t block;      /* assignment block B: coordinates decided exactly in on-chip memory
+                           before their effect on later coordinates is applied on the matrix
+                           cores.  Any of 32, 64, 128, 256 with d_in % B == 0.  Does not change
+                           results (coordinates are always visited in ascending order).
+                           Default 128. */
+    float ridge_rel;    /* rho in lambda_g = rho * mean(diag F_g).  Default 1e-6. */
+    int32_t init;       /* gq_lnq_init.  QUANTILE: c_j = m quantiles of w_j at levels
+                           (q + 1/2)/m (linear interpolation between order statistics),
+                           codes = nearest entry (lowest index on ties).  GIVEN: start from
+                           the C and P passed in.  Default QUANTILE. */
+    int32_t reserved;   /* must be 0 */
+} gq_lnq_options;
+
+/* ABI version of the loaded library (GQ_ABI_VERSION). */
+int gq_abi_version(void);
+
+/* Message for the most recent non-OK status on this thread ("" if none).
+   Owned by the library; valid until the next call on this thread. */
+const char* gq_last_error(void);
+
+/* Fills *opt with the defaults listed in gq_lnq_options.  opt: host pointer. */
+void gq_lnq_options_default(gq_lnq_options* opt);
+
+/* Workspace bytes gq_fisher_accumulate needs for these sizes. */
+size_t gq_fisher_workspace_size(int64_t n, int64_t d_in, int64_t d_out, int32_t groups,
+                                gq_dtype x_dt);
+
+/*
+ * Grouped Fisher blocks (GuidedQuant objective equation and the grouping
+ * sentence after it):  F[g] (=|+=) X^T diag(s_g) X,
+ *   s_g[t] = (1/|g|) sum_{j in g} G[t, j]^2.
+ * X [n][d_in] of dtype x_dt, G [n][d_out] of dtype g_dt, F [groups][d_in][d_in]
+ * float32 output; accumulate = 0 overwrites F, 1 adds to it (token chunks can be
+ * streamed through repeated calls, F being a sum over tokens).  The result is
+ * exactly symmetric (the upper triangle is computed and mirrored).
+ * Requires n >= 1, d_in >= 1, d_out >= 1, 1 <= groups, d_out % groups == 0,
+ * x_dt == g_dt.
+ */
+gq_status gq_fisher_accumulate(const void* X, gq_dtype x_dt, int64_t n, int64_t d_in,
+                               const void* G, gq_dtype g_dt, int64_t d_out, int32_t groups,
+                               float* F, int32_t accumulate,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes every lnq_* call below needs for these sizes and W dtype. */
+size_t gq_lnq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_t bits,
+                             gq_dtype w_dt);
+
+/*
+ * One "(codebook)" step of the LNQ algorithm box for every row j:
+ *   c_j <- (P_j^T F' P_j)^{-1} P_j^T F' w_j   on the codes that own at least one
+ * coordinate; codes that own none keep their value.  F' = F_g(j) + lambda I.
+ * F [groups][d_in][d_in], W [d_out][d_in] (w_dt), P [d_out][d_in] (read),
+ * C [d_out][m] (read, then overwritten).  A row whose m x m system is not
+ * positive definite (possible only with ridge_rel == 0) keeps its codebook and
+ * is counted in *n_not_pd (device int64, may be NULL; incremented, not reset).
+ * Shape limits shared by every lnq_* call: 1 <= bits <= 4, d_out % groups == 0,
+ * d_in % 32 == 0, 32 <= d_in <= 32768, ridge_rel finite and >= 0 (GQ_EINVAL /
+ * GQ_ESHAPE otherwise).
+ */
+gq_status lnq_codebook_update(const float* F, int32_t groups, int64_t d_in,
+                              const void* W, gq_dtype w_dt, int64_t d_out,
+                              const uint8_t* P, int32_t bits, float* C, float ridge_rel,
+                              int64_t* n_not_pd, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One "(assignment)" pass of the LNQ algorithm box for every row j: for
+ * i = 0..d_in-1 in ascending order, coordinate i takes the codebook entry
+ * that minimises (w_hat - w)^T F' (w_hat - w) with every other coordinate
+ * fixed; the current entry is kept unless another strictly lowers the
+ * objective, and among equal minimisers the lowest index wins.
+ * P [d_out][d_in] is read and overwritten; C [d_out][m] is read.  The number of
+ * coordinates that changed is added to *n_changed (device int64, may be NULL).
+ * block: as gq_lnq_options.block.
+ */
+gq_status lnq_assign_sweep(const float* F, int32_t groups, int64_t d_in,
+                           const void* W, gq_dtype w_dt, int64_t d_out,
+                           const float* C, int32_t bits, uint8_t* P, float ridge_rel,
+                           int32_t block, int64_t* n_changed,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Per-row objective (LNQ problem statement with F' in place of X^T X, i.e.
+ * the GuidedQuant objective of the row):  obj_rows[j] = e_j^T F' e_j,
+ * e_j = C[j][P[j]] - w_j, as float64 (device, [d_out]).  obj_total (device
+ * float64, may be NULL) receives sum_j obj_rows[j].
+ */
+gq_status lnq_objective(const float* F, int32_t groups, int64_t d_in,
+                        const void* W, gq_dtype w_dt, int64_t d_out,
+                        const float* C, const uint8_t* P, int32_t bits, float ridge_rel,
+                        double* obj_rows, double* obj_total,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Whole LNQ on a layer: initialise (opt->init), then `iters` times
+ * (codebook step, assignment pass), as in the LNQ algorithm box.
+ * W [d_out][d_in] (w_dt), F [groups][d_in][d_in]; C [d_out][2^bits] and
+ * P [d_out][d_in] are outputs (inputs too when opt->init == GQ_INIT_GIVEN).
+ * obj_trace (device float64 [2*iters+1], may be NULL): layer objective
+ * sum_j e_j^T F' e_j at the start and after every half-step; each entry is
+ * evaluated from scratch from (C, P).  n_changed (device int64 [iters], may be
+ * NULL): coordinates changed by each assignment pass (overwritten).
+ * opt == NULL means the defaults.  Requires 1 <= bits <= 4, iters >= 0.
+ */
+gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in,
+                       const float* F, int32_t groups, int32_t bits, int32_t iters,
+                       const gq_lnq_options* opt, float* C, uint8_t* P,
+                       double* obj_trace, int64_t* n_changed,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Diagnostics: per-stage kernel timing with HIP events.
+ * gq_timing_enable(1) makes every later call bracket each of its stages with two
+ * events recorded on the call's stream (events are created on first use and
+ * kept in a pool).  gq_timing_read synchronises the recorded events, writes the
+ * summed milliseconds and the number of timed launch sequences per stage into
+ * ms[GQ_STAGE_COUNT] and launches[GQ_STAGE_COUNT] (host arrays), and clears
+ * the record.  Timing adds one event record per stage boundary; results of the
+ * computation do not change.  GQ_EHIP if an event call failed.
+ */
+typedef enum {
+    GQ_STAGE_GROUP_SCALE = 0,   /* s_g from G */
+    GQ_STAGE_FISHER_MFMA,       /* the matrix-core Fisher contraction */
+    GQ_STAGE_FISHER_FINALIZE,   /* split-K sum + mirror write of F */
+    GQ_STAGE_FISHER_PLAIN,      /* float32-input Fisher */
+    GQ_STAGE_LNQ_PREPARE,       /* ridge and F' planes */
+    GQ_STAGE_LNQ_WF,            /* V = W F' */
+    GQ_STAGE_LNQ_INIT,          /* quantile codebooks and nearest codes */
+    GQ_STAGE_LNQ_U,             /* U_j = F' P_j */
+    GQ_STAGE_LNQ_SOLVE,         /* codebook systems, solves, residuals, objectives */
+    GQ_STAGE_LNQ_SWEEP,         /* the assignment pass */
+    GQ_STAGE_LNQ_SMALL,         /* sums and counters */
+    GQ_STAGE_COUNT
+} gq_stage;
+
+void gq_timing_enable(int on);
+gq_status gq_timing_read(double* ms, int64_t* launches);
+/* Short name of a stage ("" for an unknown id); static storage. */
+const char* gq_stage_name(int stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQ_H */

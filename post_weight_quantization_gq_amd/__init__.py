@@ -1,9 +1,11 @@
 """MI355X (gfx950) GuidedQuant Fisher + LNQ hot path.
 
-The compute runs in the HIP library `libgq.so` (C ABI declared in include/gq.h);
-`binding` marshals torch tensors to it.  Nothing here computes on the CPU.
+The compute runs in the HIP library `_lib/libgq.so` (C ABI declared in
+include/gq.h); `binding` marshals torch tensors to it.  Nothing here computes
+on the CPU, and nothing here imports the oracle.
 """
 from .binding import (  # noqa: F401
-    GQError, library, abi_version, fisher, lnq_codebook_update, lnq_assign_sweep,
-    lnq_objective, lnq_quantize, lnq_options,
+    GQError, library, abi_version, options, fisher, gq_fisher_accumulate, lnq_codebook_update,
+    lnq_assign_sweep, lnq_objective, lnq_quantize, fisher_workspace_size, lnq_workspace_size,
+    gq_timing_enable, gq_timing_read, EXPORTS, GQ_F32, GQ_BF16, GQ_INIT_QUANTILE, GQ_INIT_GIVEN,
 )

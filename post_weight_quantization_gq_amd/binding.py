@@ -1,5 +1,277 @@
-"""placeholder; replaced below"""
+"""Python binding of libgq.so (C ABI in include/gq.h).
+
+Argument marshalling only: torch tensors supply device memory and the HIP
+stream; every step of the computation runs in the library's kernels.  Each
+function has the name of the C entry point it calls.  A non-OK status raises
+GQError(status, message).  If the built library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libgq.so")
+
+GQ_OK, GQ_EINVAL, GQ_ESHAPE, GQ_EDTYPE, GQ_ENOMEM, GQ_EHIP, GQ_ENOTIMPL = 0, 1, 2, 3, 4, 5, 8
+GQ_F32, GQ_BF16 = 0, 1
+GQ_INIT_QUANTILE, GQ_INIT_GIVEN = 0, 1
+ABI_VERSION = 1
+
+# every symbol include/gq.h declares
+EXPORTS = (
+    "gq_abi_version", "gq_last_error", "gq_lnq_options_default", "gq_fisher_workspace_size",
+    "gq_fisher_accumulate", "gq_lnq_workspace_size", "lnq_codebook_update", "lnq_assign_sweep",
+    "lnq_objective", "lnq_quantize", "gq_timing_enable", "gq_timing_read", "gq_stage_name",
+)
+STAGE_COUNT = 11
+
+
 class GQError(RuntimeError):
-    pass
-def library(): raise GQError("not built")
-abi_version = fisher = lnq_codebook_update = lnq_assign_sweep = lnq_objective = lnq_quantize = lnq_options = library
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libgq status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+class lnq_options(ctypes.Structure):
+    """gq_lnq_options (block, ridge_rel, init, reserved)."""
+    _fields_ = [("block", ctypes.c_int32), ("ridge_rel", ctypes.c_float),
+                ("init", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+
+_SIGS = {
+    "gq_abi_version": (ctypes.c_int, []),
+    "gq_last_error": (ctypes.c_char_p, []),
+    "gq_lnq_options_default": (None, [ctypes.POINTER(lnq_options)]),
+    "gq_fisher_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32]),
+    "gq_fisher_accumulate": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _i32, _vp,
+                                            _i32, _vp, _sz, _vp]),
+    "gq_lnq_workspace_size": (_sz, [_i64, _i64, _i32, _i32, _i32]),
+    "lnq_codebook_update": (ctypes.c_int, [_vp, _i32, _i64, _vp, _i32, _i64, _vp, _i32, _vp, _f32,
+                                           _vp, _vp, _sz, _vp]),
+    "lnq_assign_sweep": (ctypes.c_int, [_vp, _i32, _i64, _vp, _i32, _i64, _vp, _i32, _vp, _f32,
+                                        _i32, _vp, _vp, _sz, _vp]),
+    "lnq_objective": (ctypes.c_int, [_vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp, _i32, _f32, _vp,
+                                     _vp, _vp, _sz, _vp]),
+    "lnq_quantize": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _i32,
+                                    ctypes.POINTER(lnq_options), _vp, _vp, _vp, _vp, _vp, _sz,
+                                    _vp]),
+    "gq_timing_enable": (None, [ctypes.c_int]),
+    "gq_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
+    "gq_stage_name": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_lib = None
+
+
+def library(path: str | None = None) -> ctypes.CDLL:
+    """Load libgq.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise GQError(GQ_ENOTIMPL, f"{p} is missing: build it with "
+                                   "`python -m post_weight_quantization_gq_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.gq_abi_version() != ABI_VERSION:
+        raise GQError(GQ_ENOTIMPL, "libgq ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != GQ_OK:
+        raise GQError(status, library().gq_last_error().decode(errors="replace"))
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GQ_F32
+    if t.dtype == torch.bfloat16:
+        return GQ_BF16
+    raise GQError(GQ_EDTYPE, f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise GQError(GQ_EINVAL, f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise GQError(GQ_EINVAL, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise GQError(GQ_EDTYPE, f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ws(nbytes: int, device):
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def abi_version() -> int:
+    return library().gq_abi_version()
+
+
+def options(block: int = 128, ridge_rel: float = 1e-6, init: int = GQ_INIT_QUANTILE) -> lnq_options:
+    o = lnq_options()
+    library().gq_lnq_options_default(ctypes.byref(o))
+    o.block, o.ridge_rel, o.init = block, ridge_rel, init
+    return o
+
+
+def fisher_workspace_size(n, d_in, d_out, groups, dtype=GQ_BF16) -> int:
+    return int(library().gq_fisher_workspace_size(n, d_in, d_out, groups, dtype))
+
+
+def lnq_workspace_size(d_out, d_in, groups, bits, w_dtype=GQ_BF16) -> int:
+    return int(library().gq_lnq_workspace_size(d_out, d_in, groups, bits, w_dtype))
+
+
+def gq_fisher_accumulate(X, G, groups: int, F=None, accumulate: bool = False, ws=None,
+                         stream=None) -> torch.Tensor:
+    """F[g] (=|+=) X^T diag(s_g) X; X [n][d_in], G [n][d_out] (float32 or bfloat16)."""
+    lib = library()
+    _dev(X, "X")
+    _dev(G, "G")
+    n, d_in = X.shape
+    d_out = G.shape[1]
+    if G.shape[0] != n:
+        raise GQError(GQ_ESHAPE, "X and G need the same number of tokens")
+    if F is None:
+        F = torch.empty((groups, d_in, d_in), dtype=torch.float32, device=X.device)
+        if accumulate:
+            raise GQError(GQ_EINVAL, "accumulate needs an existing F")
+    _dev(F, "F", torch.float32)
+    if tuple(F.shape) != (groups, d_in, d_in):
+        raise GQError(GQ_ESHAPE, "F must be [groups][d_in][d_in]")
+    if ws is None:
+        ws = _ws(fisher_workspace_size(n, d_in, d_out, groups, _dt(X)), X.device)
+    _check(lib.gq_fisher_accumulate(_ptr(X), _dt(X), n, d_in, _ptr(G), _dt(G), d_out, groups,
+                                    _ptr(F), int(bool(accumulate)), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(stream)))
+    return F
+
+
+fisher = gq_fisher_accumulate
+
+
+def _lnq_common(F, W, groups):
+    _dev(F, "F", torch.float32)
+    _dev(W, "W")
+    d_out, d_in = W.shape
+    if tuple(F.shape) != (groups, d_in, d_in):
+        raise GQError(GQ_ESHAPE, "F must be [groups][d_in][d_in]")
+    return d_out, d_in
+
+
+def _lnq_ws(ws, d_out, d_in, groups, bits, W):
+    if ws is None:
+        ws = _ws(lnq_workspace_size(d_out, d_in, groups, bits, _dt(W)), W.device)
+    return ws, (0 if ws is None else ws.numel())
+
+
+def lnq_codebook_update(F, W, P, C, bits: int, ridge_rel: float = 1e-6, n_not_pd=None,
+                        ws=None, stream=None) -> torch.Tensor:
+    """One codebook step; C [d_out][2^bits] float32 is updated in place."""
+    lib = library()
+    groups = F.shape[0]
+    d_out, d_in = _lnq_common(F, W, groups)
+    _dev(P, "P", torch.uint8)
+    _dev(C, "C", torch.float32)
+    ws, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
+    _check(lib.lnq_codebook_update(_ptr(F), groups, d_in, _ptr(W), _dt(W), d_out, _ptr(P), bits,
+                                   _ptr(C), ridge_rel, _ptr(n_not_pd), _ptr(ws), nb,
+                                   _stream(stream)))
+    return C
+
+
+def lnq_assign_sweep(F, W, C, P, bits: int, ridge_rel: float = 1e-6, block: int = 128,
+                     n_changed=None, ws=None, stream=None) -> torch.Tensor:
+    """One assignment pass; P [d_out][d_in] uint8 is updated in place."""
+    lib = library()
+    groups = F.shape[0]
+    d_out, d_in = _lnq_common(F, W, groups)
+    _dev(P, "P", torch.uint8)
+    _dev(C, "C", torch.float32)
+    ws, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
+    _check(lib.lnq_assign_sweep(_ptr(F), groups, d_in, _ptr(W), _dt(W), d_out, _ptr(C), bits,
+                                _ptr(P), ridge_rel, block, _ptr(n_changed), _ptr(ws), nb,
+                                _stream(stream)))
+    return P
+
+
+def lnq_objective(F, W, C, P, bits: int, ridge_rel: float = 1e-6, obj_total=None, ws=None,
+                  stream=None) -> torch.Tensor:
+    """Per-row objectives e_j^T F' e_j (float64 [d_out])."""
+    lib = library()
+    groups = F.shape[0]
+    d_out, d_in = _lnq_common(F, W, groups)
+    _dev(P, "P", torch.uint8)
+    _dev(C, "C", torch.float32)
+    rows = torch.empty(d_out, dtype=torch.float64, device=W.device)
+    ws, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
+    _check(lib.lnq_objective(_ptr(F), groups, d_in, _ptr(W), _dt(W), d_out, _ptr(C), _ptr(P),
+                             bits, ridge_rel, _ptr(rows), _ptr(obj_total), _ptr(ws), nb,
+                             _stream(stream)))
+    return rows
+
+
+def lnq_quantize(W, F, bits: int, iters: int, block: int = 128, ridge_rel: float = 1e-6,
+                 C=None, P=None, init: int | None = None, trace: bool = True,
+                 ws=None, stream=None):
+    """Whole LNQ on a layer.  Returns (C, P, obj_trace or None, n_changed).
+
+    With C and P given and init unset, starts from them (GQ_INIT_GIVEN).
+    """
+    lib = library()
+    groups = F.shape[0]
+    d_out, d_in = _lnq_common(F, W, groups)
+    m = 1 << bits
+    if init is None:
+        init = GQ_INIT_GIVEN if (C is not None and P is not None) else GQ_INIT_QUANTILE
+    if C is None:
+        C = torch.empty((d_out, m), dtype=torch.float32, device=W.device)
+    if P is None:
+        P = torch.empty((d_out, d_in), dtype=torch.uint8, device=W.device)
+    _dev(C, "C", torch.float32)
+    _dev(P, "P", torch.uint8)
+    tr = torch.empty(2 * iters + 1, dtype=torch.float64, device=W.device) if trace else None
+    nch = torch.zeros(max(iters, 1), dtype=torch.int64, device=W.device)
+    opt = options(block, ridge_rel, init)
+    ws, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
+    _check(lib.lnq_quantize(_ptr(W), _dt(W), d_out, d_in, _ptr(F), groups, bits, iters,
+                            ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), _ptr(ws),
+                            nb, _stream(stream)))
+    return C, P, tr, nch[:iters]
+
+
+def gq_timing_enable(on: bool = True) -> None:
+    """Bracket every later stage with HIP events on its stream (diagnostics)."""
+    library().gq_timing_enable(int(bool(on)))
+
+
+def gq_timing_read() -> dict:
+    """{stage name: (milliseconds, launch sequences)} since the last read; clears."""
+    lib = library()
+    ms = (ctypes.c_double * STAGE_COUNT)()
+    cnt = (_i64 * STAGE_COUNT)()
+    _check(lib.gq_timing_read(ms, cnt))
+    return {lib.gq_stage_name(i).decode(): (ms[i], cnt[i]) for i in range(STAGE_COUNT)}

@@ -1,0 +1,365 @@
+// C ABI of libgq (declared in include/gq.h): argument validation, workspace
+// handling and the launch sequences of the GuidedQuant Fisher and of LNQ.
+#include "gq_common.h"
+#include "gq_internal.h"
+#include "gq.h"
+
+static_assert((int)gq::ST_COUNT == (int)GQ_STAGE_COUNT, "stage ids of gq.h and the library differ");
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+// ---------------------------------------------------------------------------
+// Per-stage HIP-event timing.  When enabled, every launch sequence of a stage is
+// bracketed by two events recorded on the stream the kernels run on; reading
+// synchronises the recorded events, sums their elapsed times per stage and
+// returns the events to a pool.
+// ---------------------------------------------------------------------------
+namespace gq {
+namespace {
+std::atomic<bool> g_timing{false};
+std::mutex g_tmu;
+struct Mark { int stage; hipEvent_t start, stop; };
+std::vector<Mark> g_marks;          // completed (start, stop) pairs
+std::vector<hipEvent_t> g_pool;     // reusable events
+hipEvent_t g_open[ST_COUNT];        // start event of a stage in progress
+bool g_err = false;                 // an event call failed since the last read
+
+hipEvent_t take_event() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+bool timing_on() { return g_timing.load(std::memory_order_relaxed); }
+
+void timing_mark(Stage s, hipStream_t st, bool begin) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    hipEvent_t e = take_event();
+    if (!e || hipEventRecord(e, st) != hipSuccess) {
+        g_err = true;
+        if (e) g_pool.push_back(e);
+        if (!begin && g_open[s]) { g_pool.push_back(g_open[s]); g_open[s] = nullptr; }
+        return;
+    }
+    if (begin) {
+        if (g_open[s]) g_pool.push_back(g_open[s]);
+        g_open[s] = e;
+    } else if (g_open[s]) {
+        g_marks.push_back({(int)s, g_open[s], e});
+        g_open[s] = nullptr;
+    } else {
+        g_pool.push_back(e);
+    }
+}
+}  // namespace gq
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gq_status fail(gq_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+gq_status hip_fail(hipError_t e, const char* where) {
+    return fail(GQ_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool dtype_ok(gq_dtype t) { return t == GQ_F32 || t == GQ_BF16; }
+
+// The kernels use 16-byte vector loads on X, G, W, F and P.
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Workspace that is either the caller's or allocated stream-ordered for one call.
+struct Scratch {
+    void* ptr = nullptr;
+    bool owned = false;
+    hipStream_t st = nullptr;
+    gq_status acquire(void* ws, size_t ws_bytes, size_t need, hipStream_t s) {
+        st = s;
+        if (ws) {
+            if (ws_bytes < need)
+                return fail(GQ_EINVAL, "workspace too small: %zu bytes given, %zu needed", ws_bytes,
+                            need);
+            ptr = ws;
+            return GQ_OK;
+        }
+        if (need == 0) return GQ_OK;
+        hipError_t e = hipMallocAsync(&ptr, need, s);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(GQ_ENOMEM, "hipMallocAsync(%zu) failed: %s", need, hipGetErrorString(e));
+        }
+        owned = true;
+        return GQ_OK;
+    }
+    ~Scratch() {
+        if (owned && ptr) (void)hipFreeAsync(ptr, st);
+    }
+};
+
+gq_status check_lnq_shape(const float* F, int32_t groups, int64_t d_in, const void* W,
+                          gq_dtype w_dt, int64_t d_out, int32_t bits, float ridge_rel) {
+    if (!F || !W) return fail(GQ_EINVAL, "null F or W");
+    if (!dtype_ok(w_dt)) return fail(GQ_EDTYPE, "unsupported W dtype %d", (int)w_dt);
+    if (groups < 1) return fail(GQ_EINVAL, "groups must be >= 1 (got %d)", groups);
+    if (d_out < 1 || d_in < 1) return fail(GQ_ESHAPE, "empty shape d_out=%lld d_in=%lld",
+                                           (long long)d_out, (long long)d_in);
+    if (d_out % groups) return fail(GQ_ESHAPE, "d_out=%lld is not a multiple of groups=%d",
+                                    (long long)d_out, groups);
+    if (d_in % 32) return fail(GQ_ESHAPE, "d_in=%lld must be a multiple of 32", (long long)d_in);
+    if (d_in > 32768) return fail(GQ_ENOTIMPL, "d_in=%lld above 32768", (long long)d_in);
+    if (bits < 1 || bits > 4) return fail(GQ_EINVAL, "bits=%d outside [1, 4]", bits);
+    if (!(ridge_rel >= 0.f) || !std::isfinite(ridge_rel))
+        return fail(GQ_EINVAL, "ridge_rel must be finite and >= 0");
+    if (!al16(F) || !al16(W)) return fail(GQ_EINVAL, "F and W must be 16-byte aligned");
+    return GQ_OK;
+}
+
+bool block_ok(int32_t b) { return b == 32 || b == 64 || b == 128 || b == 256; }
+
+}  // namespace
+
+extern "C" {
+
+int gq_abi_version(void) { return GQ_ABI_VERSION; }
+
+void gq_timing_enable(int on) { gq::g_timing.store(on != 0); }
+
+gq_status gq_timing_read(double* ms, int64_t* launches) {
+    if (!ms || !launches) return fail(GQ_EINVAL, "null ms or launches");
+    std::lock_guard<std::mutex> lk(gq::g_tmu);
+    for (int i = 0; i < GQ_STAGE_COUNT; ++i) { ms[i] = 0.0; launches[i] = 0; }
+    gq_status rc = GQ_OK;
+    if (gq::g_err) rc = fail(GQ_EHIP, "an event record failed while timing");
+    for (const gq::Mark& m : gq::g_marks) {
+        float t = 0.f;
+        hipError_t e = hipEventSynchronize(m.stop);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, m.start, m.stop);
+        if (e != hipSuccess) {
+            rc = hip_fail(e, "gq_timing_read");
+        } else {
+            ms[m.stage] += (double)t;
+            launches[m.stage] += 1;
+        }
+        gq::g_pool.push_back(m.start);
+        gq::g_pool.push_back(m.stop);
+    }
+    gq::g_marks.clear();
+    gq::g_err = false;
+    return rc;
+}
+
+const char* gq_stage_name(int stage) {
+    static const char* names[GQ_STAGE_COUNT] = {
+        "group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain", "lnq_prepare",
+        "lnq_wf", "lnq_init", "lnq_u", "lnq_solve", "lnq_sweep", "lnq_small"};
+    if (stage < 0 || stage >= GQ_STAGE_COUNT) return "";
+    return names[stage];
+}
+
+const char* gq_last_error(void) { return g_last_error.c_str(); }
+
+void gq_lnq_options_default(gq_lnq_options* opt) {
+    if (!opt) return;
+    opt->block = 128;
+    opt->ridge_rel = 1e-6f;
+    opt->init = GQ_INIT_QUANTILE;
+    opt->reserved = 0;
+}
+
+size_t gq_fisher_workspace_size(int64_t n, int64_t d_in, int64_t d_out, int32_t groups,
+                                gq_dtype x_dt) {
+    (void)d_out;
+    if (n < 1 || d_in < 1 || groups < 1) return 0;
+    return gq::fisher_workspace(n, d_in, groups, x_dt == GQ_BF16);
+}
+
+gq_status gq_fisher_accumulate(const void* X, gq_dtype x_dt, int64_t n, int64_t d_in,
+                               const void* G, gq_dtype g_dt, int64_t d_out, int32_t groups,
+                               float* F, int32_t accumulate, void* ws, size_t ws_bytes,
+                               void* stream) {
+    if (!X || !G || !F) return fail(GQ_EINVAL, "null X, G or F");
+    if (!dtype_ok(x_dt) || !dtype_ok(g_dt)) return fail(GQ_EDTYPE, "unsupported dtype");
+    if (x_dt != g_dt) return fail(GQ_EDTYPE, "X and G must share a dtype");
+    if (n < 1 || d_in < 1 || d_out < 1) return fail(GQ_ESHAPE, "empty shape");
+    if (groups < 1) return fail(GQ_EINVAL, "groups must be >= 1");
+    if (d_out % groups) return fail(GQ_ESHAPE, "d_out=%lld is not a multiple of groups=%d",
+                                    (long long)d_out, groups);
+    if (accumulate != 0 && accumulate != 1) return fail(GQ_EINVAL, "accumulate must be 0 or 1");
+    if (!al16(X) || !al16(G) || !al16(F) || !al16(ws))
+        return fail(GQ_EINVAL, "X, G, F and ws must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    const bool bf16 = x_dt == GQ_BF16;
+    Scratch s;
+    gq_status rc = s.acquire(ws, ws_bytes, gq::fisher_workspace(n, d_in, groups, bf16), st);
+    if (rc != GQ_OK) return rc;
+    hipError_t e = gq::fisher_run(X, G, bf16, n, d_in, d_out, groups, F, accumulate, s.ptr, st);
+    if (e != hipSuccess) return hip_fail(e, "gq_fisher_accumulate");
+    return GQ_OK;
+}
+
+size_t gq_lnq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_t bits,
+                             gq_dtype w_dt) {
+    if (d_out < 1 || d_in < 1 || groups < 1 || bits < 1 || bits > 8) return 0;
+    return gq::lnq_sizes(d_out, d_in, groups, 1 << bits, w_dt == GQ_F32).total;
+}
+
+gq_status lnq_codebook_update(const float* F, int32_t groups, int64_t d_in, const void* W,
+                              gq_dtype w_dt, int64_t d_out, const uint8_t* P, int32_t bits,
+                              float* C, float ridge_rel, int64_t* n_not_pd, void* ws,
+                              size_t ws_bytes, void* stream) {
+    gq_status rc = check_lnq_shape(F, groups, d_in, W, w_dt, d_out, bits, ridge_rel);
+    if (rc != GQ_OK) return rc;
+    if (!P || !C) return fail(GQ_EINVAL, "null P or C");
+    if (!al16(P) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "P must be 16-byte and ws 256-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    const bool wb = w_dt == GQ_BF16;
+    const int m = 1 << bits;
+    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m, !wb);
+    Scratch s;
+    if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
+    gq::LnqWs w = gq::lnq_carve(s.ptr, z, !wb);
+    hipError_t e;
+    if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
+    if ((e = gq::lnq_compute_v(W, wb, d_out, d_in, groups, w, st)) != hipSuccess) return hip_fail(e, "W F'");
+    if ((e = gq::lnq_u_solve(0, W, wb, d_out, d_in, groups, m, P, C, w, nullptr, w.objA, w.objB,
+                             (unsigned long long*)n_not_pd, st)) != hipSuccess)
+        return hip_fail(e, "codebook");
+    return GQ_OK;
+}
+
+gq_status lnq_assign_sweep(const float* F, int32_t groups, int64_t d_in, const void* W,
+                           gq_dtype w_dt, int64_t d_out, const float* C, int32_t bits,
+                           uint8_t* P, float ridge_rel, int32_t block, int64_t* n_changed,
+                           void* ws, size_t ws_bytes, void* stream) {
+    gq_status rc = check_lnq_shape(F, groups, d_in, W, w_dt, d_out, bits, ridge_rel);
+    if (rc != GQ_OK) return rc;
+    if (!P || !C) return fail(GQ_EINVAL, "null P or C");
+    if (!al16(P) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "P must be 16-byte and ws 256-byte aligned");
+    if (!block_ok(block)) return fail(GQ_EINVAL, "block=%d not in {32, 64, 128, 256}", block);
+    if (d_in % block) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of block=%d",
+                                  (long long)d_in, block);
+    hipStream_t st = (hipStream_t)stream;
+    const bool wb = w_dt == GQ_BF16;
+    const int m = 1 << bits;
+    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m, !wb);
+    Scratch s;
+    if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
+    gq::LnqWs w = gq::lnq_carve(s.ptr, z, !wb);
+    hipError_t e;
+    if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
+    if ((e = gq::lnq_compute_v(W, wb, d_out, d_in, groups, w, st)) != hipSuccess) return hip_fail(e, "W F'");
+    if ((e = gq::lnq_u_solve(1, W, wb, d_out, d_in, groups, m, P, (float*)C, w, w.R, w.objA,
+                             w.objB, nullptr, st)) != hipSuccess)
+        return hip_fail(e, "residual");
+    if ((e = gq::lnq_sweep_run(block, F, d_out, d_in, groups, C, m, P, w, w.objB, w.objC,
+                               (unsigned long long*)n_changed, st)) != hipSuccess)
+        return hip_fail(e, "sweep");
+    return GQ_OK;
+}
+
+gq_status lnq_objective(const float* F, int32_t groups, int64_t d_in, const void* W,
+                        gq_dtype w_dt, int64_t d_out, const float* C, const uint8_t* P,
+                        int32_t bits, float ridge_rel, double* obj_rows, double* obj_total,
+                        void* ws, size_t ws_bytes, void* stream) {
+    gq_status rc = check_lnq_shape(F, groups, d_in, W, w_dt, d_out, bits, ridge_rel);
+    if (rc != GQ_OK) return rc;
+    if (!P || !C || !obj_rows) return fail(GQ_EINVAL, "null P, C or obj_rows");
+    if (!al16(P) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "P must be 16-byte and ws 256-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    const bool wb = w_dt == GQ_BF16;
+    const int m = 1 << bits;
+    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m, !wb);
+    Scratch s;
+    if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
+    gq::LnqWs w = gq::lnq_carve(s.ptr, z, !wb);
+    hipError_t e;
+    if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
+    if ((e = gq::lnq_compute_v(W, wb, d_out, d_in, groups, w, st)) != hipSuccess) return hip_fail(e, "W F'");
+    if ((e = gq::lnq_u_solve(1, W, wb, d_out, d_in, groups, m, P, (float*)C, w, nullptr, nullptr,
+                             obj_rows, nullptr, st)) != hipSuccess)
+        return hip_fail(e, "objective");
+    if (obj_total && (e = gq::lnq_reduce(obj_rows, d_out, obj_total, st)) != hipSuccess)
+        return hip_fail(e, "objective sum");
+    return GQ_OK;
+}
+
+gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in, const float* F,
+                       int32_t groups, int32_t bits, int32_t iters, const gq_lnq_options* opt,
+                       float* C, uint8_t* P, double* obj_trace, int64_t* n_changed, void* ws,
+                       size_t ws_bytes, void* stream) {
+    gq_lnq_options o;
+    gq_lnq_options_default(&o);
+    if (opt) o = *opt;
+    gq_status rc = check_lnq_shape(F, groups, d_in, W, w_dt, d_out, bits, o.ridge_rel);
+    if (rc != GQ_OK) return rc;
+    if (!P || !C) return fail(GQ_EINVAL, "null P or C");
+    if (!al16(P) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "P must be 16-byte and ws 256-byte aligned");
+    if (iters < 0) return fail(GQ_EINVAL, "iters must be >= 0");
+    if (o.reserved != 0) return fail(GQ_EINVAL, "options.reserved must be 0");
+    if (o.init != GQ_INIT_QUANTILE && o.init != GQ_INIT_GIVEN)
+        return fail(GQ_EINVAL, "unknown init %d", o.init);
+    if (!block_ok(o.block)) return fail(GQ_EINVAL, "block=%d not in {32, 64, 128, 256}", o.block);
+    if (d_in % o.block) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of block=%d",
+                                    (long long)d_in, o.block);
+    hipStream_t st = (hipStream_t)stream;
+    const bool wb = w_dt == GQ_BF16;
+    const int m = 1 << bits;
+    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m, !wb);
+    Scratch s;
+    if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
+    gq::LnqWs w = gq::lnq_carve(s.ptr, z, !wb);
+    hipError_t e;
+    if ((e = gq::lnq_prepare(F, groups, d_in, o.ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
+    if ((e = gq::lnq_compute_v(W, wb, d_out, d_in, groups, w, st)) != hipSuccess) return hip_fail(e, "W F'");
+    if (o.init == GQ_INIT_QUANTILE &&
+        (e = gq::lnq_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
+        return hip_fail(e, "init");
+    for (int t = 1; t <= iters; ++t) {
+        // codebook step; also the from-scratch objective before it (entry 2t-2)
+        if ((e = gq::lnq_u_solve(0, W, wb, d_out, d_in, groups, m, P, C, w, w.R, w.objA, w.objB,
+                                 w.cnt + 1, st)) != hipSuccess)
+            return hip_fail(e, "codebook");
+        if (obj_trace) {
+            if ((e = gq::lnq_reduce(w.objA, d_out, obj_trace + 2 * t - 2, st)) != hipSuccess ||
+                (e = gq::lnq_reduce(w.objB, d_out, obj_trace + 2 * t - 1, st)) != hipSuccess)
+                return hip_fail(e, "trace");
+        }
+        if ((e = gq::lnq_zero_counter(w.cnt, st)) != hipSuccess) return hip_fail(e, "counter");
+        if ((e = gq::lnq_sweep_run(o.block, F, d_out, d_in, groups, C, m, P, w, w.objB, w.objC,
+                                   w.cnt, st)) != hipSuccess)
+            return hip_fail(e, "sweep");
+        if (n_changed && (e = gq::lnq_store_counter(w.cnt, n_changed + (t - 1), st)) != hipSuccess)
+            return hip_fail(e, "counter");
+    }
+    if (obj_trace) {
+        // objective of the final (C, P), from scratch
+        if ((e = gq::lnq_u_solve(1, W, wb, d_out, d_in, groups, m, P, C, w, nullptr, nullptr,
+                                 w.objA, nullptr, st)) != hipSuccess)
+            return hip_fail(e, "final objective");
+        if ((e = gq::lnq_reduce(w.objA, d_out, obj_trace + 2 * iters, st)) != hipSuccess)
+            return hip_fail(e, "trace");
+    }
+    return GQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+"""The C-ABI library: it loads, exports every symbol include/gq.h declares, and
+rejects invalid arguments before anything is enqueued (CPU only: every call
+below returns during argument validation, so no pointer is dereferenced and no
+kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import post_weight_quantization_gq_amd as gq
+from post_weight_quantization_gq_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "gq.h")
+
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced (validation fails first)
+FAKE_ODD = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", src))
+
+
+def test_exports_every_declared_symbol():
+    lib = gq.library()
+    declared = _declared()
+    assert declared == set(B.EXPORTS), declared ^ set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert gq.abi_version() == 1
+
+
+def test_options_default():
+    o = gq.options()
+    d = B.lnq_options()
+    gq.library().gq_lnq_options_default(ctypes.byref(d))
+    assert (d.block, d.init, d.reserved) == (128, 0, 0)
+    assert d.ridge_rel == pytest.approx(1e-6)
+    assert o.block == 128
+
+
+def _err(lib):
+    return lib.gq_last_error().decode()
+
+
+def test_fisher_argument_errors():
+    lib = gq.library()
+    call = lambda **k: lib.gq_fisher_accumulate(
+        k.get("X", FAKE), k.get("xdt", 1), k.get("n", 16), k.get("d", 64), k.get("G", FAKE),
+        k.get("gdt", 1), k.get("d_out", 8), k.get("groups", 2), k.get("F", FAKE),
+        k.get("acc", 0), k.get("ws", FAKE), k.get("wsb", 0), None)
+    assert call(X=None) == B.GQ_EINVAL and "null" in _err(lib)
+    assert call(xdt=7) == B.GQ_EDTYPE
+    assert call(gdt=0) == B.GQ_EDTYPE
+    assert call(n=0) == B.GQ_ESHAPE
+    assert call(d_out=9) == B.GQ_ESHAPE and "multiple" in _err(lib)
+    assert call(groups=0) == B.GQ_EINVAL
+    assert call(acc=2) == B.GQ_EINVAL
+    assert call(F=FAKE_ODD) == B.GQ_EINVAL and "aligned" in _err(lib)
+    assert call(wsb=16) == B.GQ_EINVAL and "workspace too small" in _err(lib)
+
+
+def test_lnq_argument_errors():
+    lib = gq.library()
+    q = lambda **k: lib.lnq_quantize(
+        k.get("W", FAKE), k.get("wdt", 1), k.get("d_out", 64), k.get("d_in", 256),
+        k.get("F", FAKE), k.get("groups", 2), k.get("bits", 3), k.get("iters", 2),
+        k.get("opt", None), k.get("C", FAKE), k.get("P", FAKE), None, None, k.get("ws", FAKE),
+        k.get("wsb", 0), None)
+    assert q(F=None) == B.GQ_EINVAL
+    assert q(wdt=5) == B.GQ_EDTYPE
+    assert q(d_out=63) == B.GQ_ESHAPE
+    assert q(d_in=250) == B.GQ_ESHAPE
+    assert q(d_in=65536) == B.GQ_ENOTIMPL
+    assert q(bits=5) == B.GQ_EINVAL and "bits" in _err(lib)
+    assert q(bits=0) == B.GQ_EINVAL
+    assert q(iters=-1) == B.GQ_EINVAL
+    assert q(P=FAKE_ODD) == B.GQ_EINVAL
+    o = B.lnq_options()
+    lib.gq_lnq_options_default(ctypes.byref(o))
+    o.block = 96
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "block" in _err(lib)
+    o.block = 256
+    assert q(d_in=384, opt=ctypes.byref(o)) == B.GQ_ESHAPE
+    o.block, o.init = 128, 9
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL
+    o.init, o.ridge_rel = 0, -1.0
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "ridge" in _err(lib)
+    o.ridge_rel = 1e-6
+    assert q(opt=ctypes.byref(o), wsb=100) == B.GQ_EINVAL and "workspace" in _err(lib)
+    # the per-stage entry points share the checks
+    assert lib.lnq_assign_sweep(FAKE, 2, 256, FAKE, 1, 64, FAKE, 3, FAKE, 1e-6, 48, None, FAKE,
+                                0, None) == B.GQ_EINVAL
+    assert lib.lnq_codebook_update(FAKE, 3, 256, FAKE, 1, 64, FAKE, 3, FAKE, 1e-6, None, FAKE,
+                                   0, None) == B.GQ_ESHAPE
+    assert lib.lnq_objective(FAKE, 2, 256, FAKE, 1, 64, FAKE, FAKE, 3, 1e-6, None, None, FAKE, 0,
+                             None) == B.GQ_EINVAL
+
+
+def test_workspace_sizes_grow_with_shape():
+    small = gq.lnq_workspace_size(64, 256, 2, 3)
+    big = gq.lnq_workspace_size(4096, 4096, 4, 3)
+    assert 0 < small < big
+    assert gq.lnq_workspace_size(0, 256, 2, 3) == 0
+    assert gq.fisher_workspace_size(131072, 4096, 4096, 4) > gq.fisher_workspace_size(
+        1024, 256, 64, 4) > 0
+
+
+def test_timing_read_empty():
+    gq.gq_timing_enable(False)
+    t = gq.gq_timing_read()
+    assert set(t) == {"group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain",
+                      "lnq_prepare", "lnq_wf", "lnq_init", "lnq_u", "lnq_solve", "lnq_sweep",
+                      "lnq_small"}
+    assert all(v == (0.0, 0) for v in t.values())
