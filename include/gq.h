@@ -76,11 +76,12 @@ typedef enum { GQ_F32 = 0, GQ_BF16 = 1 } gq_dtype;
 typedef enum { GQ_INIT_QUANTILE = 0, GQ_INIT_GIVEN = 1 } gq_lnq_init;
 
 typedef struct {
-    int32_t block;      /* assignment block B: coordinates decided exactly in on-chip memory
-                           before their effect on later coordinates is applied on the matrix
-                           cores.  Any of 32, 64, 128, 256 with d_in % B == 0.  Does not change
-                           results (coordinates are always visited in ascending order).
-                           Default 128. */
+    int32_t block;      /* assignment block B: the effect of earlier moves of a pass on the
+                           residuals of the next B coordinates is applied once per B-block on
+                           the matrix cores; inside it, coordinates are decided 64 at a time
+                           in registers.  One of 64, 128, 256 with d_in % B == 0.  Changes only
+                           the float32 summation order (coordinates are always visited in
+                           ascending order).  Default 128. */
     float ridge_rel;    /* rho in lambda_g = rho * mean(diag F_g).  Default 1e-6. */
     int32_t init;       /* gq_lnq_init.  QUANTILE: c_j = m quantiles of w_j at levels
                            (q + 1/2)/m (linear interpolation between order statistics),

@@ -134,7 +134,7 @@ gq_status check_lnq_shape(const float* F, int32_t groups, int64_t d_in, const vo
     return GQ_OK;
 }
 
-bool block_ok(int32_t b) { return b == 32 || b == 64 || b == 128 || b == 256; }
+bool block_ok(int32_t b) { return b == 64 || b == 128 || b == 256; }
 
 }  // namespace
 
@@ -255,7 +255,7 @@ gq_status lnq_assign_sweep(const float* F, int32_t groups, int64_t d_in, const v
     if (rc != GQ_OK) return rc;
     if (!P || !C) return fail(GQ_EINVAL, "null P or C");
     if (!al16(P) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "P must be 16-byte and ws 256-byte aligned");
-    if (!block_ok(block)) return fail(GQ_EINVAL, "block=%d not in {32, 64, 128, 256}", block);
+    if (!block_ok(block)) return fail(GQ_EINVAL, "block=%d not in {64, 128, 256}", block);
     if (d_in % block) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of block=%d",
                                   (long long)d_in, block);
     hipStream_t st = (hipStream_t)stream;
@@ -318,7 +318,7 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
     if (o.reserved != 0) return fail(GQ_EINVAL, "options.reserved must be 0");
     if (o.init != GQ_INIT_QUANTILE && o.init != GQ_INIT_GIVEN)
         return fail(GQ_EINVAL, "unknown init %d", o.init);
-    if (!block_ok(o.block)) return fail(GQ_EINVAL, "block=%d not in {32, 64, 128, 256}", o.block);
+    if (!block_ok(o.block)) return fail(GQ_EINVAL, "block=%d not in {64, 128, 256}", o.block);
     if (d_in % o.block) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of block=%d",
                                     (long long)d_in, o.block);
     hipStream_t st = (hipStream_t)stream;

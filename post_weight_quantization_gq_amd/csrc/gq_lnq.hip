@@ -497,44 +497,124 @@ __global__ __launch_bounds__(256) void k_solve(
 }
 
 // ---------------------------------------------------------------------------
-// k_sweep: assignment pass.  One block = 16 rows of one group; wave w owns rows
-// 4w..4w+3 with 16 lanes per row.  Coordinates run in blocks of B; lane l of a
-// row holds block coordinates l*NB .. l*NB+NB-1 (residual, current value, code,
-// recorded value change).  Per block:
-//   1. left-looking correction corr = D[rows, 0:bs] F'[0:bs, block] on MFMA
-//      (16x16x32 bf16, D and F' as hi+lo planes, three products), skipping
-//      32-coordinate chunks in which none of the block's rows changed;
-//   2. the exact chain: for each coordinate in order, every lane of the row
-//      evaluates one code, a 16-lane argmin (lowest index on ties) picks the
-//      move, and a strict decrease applies delta * F[i, block] to the row's
-//      residual (F rows of the block staged NB at a time through LDS);
-//   3. codes and the value changes (as hi+lo bf16) are written out.
+// k_sweep: the assignment pass.  One block = 16 rows of one group, one row per
+// wave (16 waves).  Coordinates are visited in ascending order in sub-blocks of
+// 64, one coordinate per lane.
+//   * Deferred update: once per B-block, the effect of every earlier move of
+//     this pass on the block's residuals is gathered left-looking on the matrix
+//     cores, corr = D[rows, 0:bB] F'[0:bB, B-block] with v_mfma_f32_16x16x32_bf16
+//     and three products of the bf16 hi/lo planes (D hi.F hi + D hi.F lo +
+//     D lo.F hi); 16 waves split it into NCT column tiles x NSL k-slices whose
+//     partials are summed in a fixed order.  32-coordinate chunks in which no
+//     row of the block moved are skipped.  Inside a B-block, each later 64-wide
+//     sub-block gets the same correction from the block's earlier sub-blocks.
+//   * Chain (per wave, per sub-block): for coordinate t the residual, current
+//     value and damped diagonal are read from lane t (v_readlane); lanes
+//     0..m-1 each evaluate one candidate change
+//         Delta_q = delta_q (F'_tt delta_q + 2 r_t),  delta_q = c_q - w_hat_t,
+//     a 16-lane DPP min gives the best change, a ballot + find-first-set gives
+//     the lowest index attaining it, and a strict decrease applies
+//     r += delta F'[t, sub-block] in registers (F' column of the sub-block held
+//     in 64 registers per lane, staged once through LDS for the 16 rows).
+//   * The codes and the value changes (bf16 hi + lo) are written back.
 // ---------------------------------------------------------------------------
+constexpr int SW_ROWS = 16;     // rows (= waves) per block
+constexpr int SW_SUB = 64;      // chain sub-block (one coordinate per lane)
+constexpr int SW_PF = 2;        // k-chunks in flight per wave in the deferred update
+constexpr int SW_SEG = 8;       // chain steps unrolled per F' column preload
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// Integer key with the order of the float values (finite or infinite; -0.0 maps
+// to -1, +0.0 to 0), so a float minimum becomes one v_min_i32 per DPP step.
+__device__ __forceinline__ int f32_order_key(float x) {
+    const int b = __float_as_int(x);
+    return b ^ ((b >> 31) & 0x7fffffff);
+}
+
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+
+// minimum over each row of 16 lanes, available in all 16 lanes
+__device__ __forceinline__ int row16_min_i(int v) {
+    v = imin(v, dpp_mov_i<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = imin(v, dpp_mov_i<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = imin(v, dpp_mov_i<0x141>(v));   // row_half_mirror
+    v = imin(v, dpp_mov_i<0x140>(v));   // row_mirror
+    return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// acc += D[arow, kk..kk+7] . F'[ncol, kk..kk+7] over the 32-wide k-chunks
+// k_first, k_first + kstride, ... < k_end; chunks whose flag is 0 are skipped
+// (the flag is block-uniform).  Rows past the group's end read a valid row's D:
+// their outputs are never used.
+__device__ __forceinline__ void sweep_corr(f32x4& acc, const uint16_t* __restrict__ Dh,
+                                           const uint16_t* __restrict__ Dl,
+                                           const uint16_t* __restrict__ Fh,
+                                           const uint16_t* __restrict__ Fl,
+                                           int64_t k_first, int64_t k_end, int64_t kstride,
+                                           const uint32_t* flags, int lane) {
+    const int ko = 8 * (lane >> 4);
+    for (int64_t k0 = k_first; k0 < k_end; k0 += SW_PF * kstride) {
+        u32x4 dh[SW_PF], dl[SW_PF], fh[SW_PF], fl[SW_PF];
+        bool on[SW_PF];
+#pragma unroll
+        for (int u = 0; u < SW_PF; ++u) {
+            const int64_t kc = k0 + u * kstride;
+            on[u] = kc < k_end && __builtin_amdgcn_readfirstlane((int)flags[kc >> 5]) != 0;
+            if (on[u]) {
+                dh[u] = *(const u32x4*)(Dh + kc + ko);
+                dl[u] = *(const u32x4*)(Dl + kc + ko);
+                fh[u] = *(const u32x4*)(Fh + kc + ko);
+                fl[u] = *(const u32x4*)(Fl + kc + ko);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < SW_PF; ++u) {
+            if (on[u]) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh[u]), as_bf16x8(fh[u]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh[u]), as_bf16x8(fl[u]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dl[u]), as_bf16x8(fh[u]), acc, 0, 0, 0);
+            }
+        }
+    }
+}
+
 template <int B>
-__global__ __launch_bounds__(256, (B >= 256 ? 1 : 2)) void k_sweep(
+__global__ __launch_bounds__(1024, 1) void k_sweep(
     const float* __restrict__ F, const float* __restrict__ dF,
     const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo,
-    int64_t d, int64_t rows_per_group, int wgs_per_group,
+    int64_t d, int64_t rows_per_group, int wgs_per_group, int total_wgs,
     const float* __restrict__ C, int m, uint8_t* __restrict__ P,
     const float* __restrict__ R, uint16_t* __restrict__ Dhi, uint16_t* __restrict__ Dlo,
     const double* __restrict__ obj_in, double* __restrict__ obj_out,
     unsigned long long* __restrict__ n_changed) {
-    constexpr int NB = B / 16;                    // coordinates per lane per block
-    constexpr int NCT = B / 16;                   // 16-column MFMA tiles per block
-    constexpr int SUBF = NB * B;                  // floats in one staged sub-block
-    constexpr int PER = (SUBF + 255) / 256;       // staged floats per thread
-    __shared__ float corr[16][B + 4];
-    __shared__ __attribute__((aligned(16))) float fsub[2][NB][B];
-    __shared__ float fdiag[B];
-    extern __shared__ uint32_t sweep_flags[];           // [d/32] any-change flags of this block's rows
+    constexpr int NCT = B / 16;          // 16-column tiles of a B-block
+    constexpr int NSL = 256 / B;         // k-slices of the B-block correction
+    constexpr int NSUB = B / SW_SUB;     // 64-wide sub-blocks per B-block
+    __shared__ float corr_b[NSL][SW_ROWS][B];          // 16 KB
+    __shared__ float corr_s[4][SW_ROWS][SW_SUB];       // 16 KB
+    __shared__ __attribute__((aligned(16))) float fdb[SW_SUB][SW_SUB];   // 16 KB
+    __shared__ float fdd[SW_SUB];                      // diag(F') of the sub-block
+    extern __shared__ uint32_t sweep_flags[];          // [d / 32]
+
+    // XCD-aware order: hardware block h runs on XCD h % 8; consecutive logical
+    // blocks (the rows of one group) go to the same XCD and share F' in its L2.
+    const int nb = gridDim.x;
+    const int hw = blockIdx.x;
+    const int lin = (hw & 7) * (nb >> 3) + (hw >> 3);
+    if (lin >= total_wgs) return;        // whole block exits together
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = blockIdx.x / wgs_per_group;
-    const int64_t local = (int64_t)(blockIdx.x % wgs_per_group) * 16;
-    const int rg = lane >> 4;            // row within the wave
-    const int l16 = lane & 15;           // lane within the row
-    const int rloc = 4 * wave + rg;      // row within the block (0..15)
-    const int64_t jl = local + rloc;
+    const int g = lin / wgs_per_group;
+    const int64_t local = (int64_t)(lin % wgs_per_group) * SW_ROWS;
+    const int64_t jl = local + wave;
     const bool rvalid = jl < rows_per_group;
     const int64_t j = (int64_t)g * rows_per_group + (rvalid ? jl : 0);
 
@@ -543,146 +623,113 @@ __global__ __launch_bounds__(256, (B >= 256 ? 1 : 2)) void k_sweep(
     const uint16_t* Fh = Fhi + (size_t)g * d * d;
     const uint16_t* Fl = Flo + (size_t)g * d * d;
 
-    for (int i = tid; i < (int)(d / 32); i += 256) sweep_flags[i] = 0u;
+    for (int i = tid; i < (int)(d / 32); i += 1024) sweep_flags[i] = 0u;
 
-    const float cl = (l16 < m && rvalid) ? C[j * m + l16] : 0.f;   // this lane's code value
+    const float cl = (lane < m && rvalid) ? C[j * m + lane] : 0.f;   // candidate of this lane
     double dsum = 0.0;
-    unsigned cnt = 0;
+    unsigned moves = 0;
+
+    // operand rows of the correction products: the block's 16 rows
+    const int64_t arow_l = local + (lane & 15);
+    const bool arow_ok = arow_l < rows_per_group;
+    const int64_t arow = (int64_t)g * rows_per_group + (arow_ok ? arow_l : 0);
+    const uint16_t* Dh_row = Dhi + arow * d;
+    const uint16_t* Dl_row = Dlo + arow * d;
     __syncthreads();
 
-    const int nblk = (int)(d / B);
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int64_t bs = (int64_t)blk * B;
-        // ---- 1. correction from all earlier blocks
-        for (int ct = wave; ct < NCT; ct += 4) {
+    for (int64_t bB = 0; bB < d; bB += B) {
+        // ---- deferred update of the B-block from all earlier B-blocks
+        {
+            const int ct = wave % NCT, sl = wave / NCT;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int64_t ncol = bs + ct * 16 + (lane & 15);
-            const int64_t arow_l = local + (lane & 15);
-            const bool arow_ok = arow_l < rows_per_group;
-            const int64_t arow = (int64_t)g * rows_per_group + (arow_ok ? arow_l : 0);
-            for (int64_t k0 = 0; k0 < bs; k0 += 32) {
-                if (sweep_flags[k0 >> 5] == 0u) continue;   // same value in every lane
-                const int64_t kk = k0 + 8 * (lane >> 4);
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                const u32x4 dh = arow_ok ? *(const u32x4*)(Dhi + arow * d + kk) : z;
-                const u32x4 dl = arow_ok ? *(const u32x4*)(Dlo + arow * d + kk) : z;
-                const u32x4 fh = *(const u32x4*)(Fh + ncol * d + kk);
-                const u32x4 fl = *(const u32x4*)(Fl + ncol * d + kk);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fh), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fl), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dl), as_bf16x8(fh), acc, 0, 0, 0);
+            const int64_t ncol = bB + ct * 16 + (lane & 15);
+            sweep_corr(acc, Dh_row, Dl_row, Fh + ncol * d, Fl + ncol * d, (int64_t)sl * 32, bB,
+                       (int64_t)32 * NSL, sweep_flags, lane);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) corr_b[sl][4 * (lane >> 4) + t][ct * 16 + (lane & 15)] = acc[t];
+        }
+        for (int s = 0; s < NSUB; ++s) {
+            const int64_t bs = bB + (int64_t)s * SW_SUB;
+            // stage the diagonal 64 x 64 block of F (rows bs.., columns bs..)
+            {
+                const int rr = tid >> 4, cc = (tid & 15) * 4;
+                *(float4*)&fdb[rr][cc] = *(const float4*)(Fg + (bs + rr) * d + bs + cc);
+                if (tid < SW_SUB) fdd[tid] = dFg[bs + tid];
             }
+            // in-block correction from this B-block's earlier sub-blocks
+            if (s > 0) {
+                const int ct = wave & 3, sl = wave >> 2;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                const int64_t ncol = bs + ct * 16 + (lane & 15);
+                sweep_corr(acc, Dh_row, Dl_row, Fh + ncol * d, Fl + ncol * d,
+                           bB + (int64_t)sl * 32, bs, 128, sweep_flags, lane);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) corr[4 * (lane >> 4) + t][ct * 16 + (lane & 15)] = acc[t];
-        }
-        // stage sub-block 0 of the diagonal block and the block's diag(F')
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int idx = tid * PER + e;
-            if (idx < SUBF) {
-                const int rr = idx / B, cc = idx - rr * B;
-                fsub[0][rr][cc] = Fg[(bs + rr) * d + bs + cc];
+                for (int t = 0; t < 4; ++t) corr_s[sl][4 * (lane >> 4) + t][ct * 16 + (lane & 15)] = acc[t];
             }
-        }
-        if (tid < B) fdiag[tid] = dFg[bs + tid];
-        __syncthreads();
+            __syncthreads();
 
-        float r[NB], wh[NB], dv[NB];
-        int code[NB];
+            if (rvalid) {
+                const int64_t col = bs + lane;
+                float r = R[j * d + col];
 #pragma unroll
-        for (int t = 0; t < NB; ++t) {
-            const int64_t col = bs + l16 * NB + t;
-            code[t] = rvalid ? P[j * d + col] : 0;
-            r[t] = (rvalid ? R[j * d + col] : 0.f) + corr[rloc][l16 * NB + t];
-            dv[t] = 0.f;
-        }
+                for (int k = 0; k < NSL; ++k) r += corr_b[k][wave][s * SW_SUB + lane];
+                if (s > 0) {
 #pragma unroll
-        for (int t = 0; t < NB; ++t) wh[t] = __shfl(cl, code[t], 16);
-
-        // ---- 2. exact chain over the block, NB coordinates per sub-block
-        for (int o = 0; o < 16; ++o) {
-            const int buf = o & 1;
-            const bool more = o + 1 < 16;
-            float pre[PER];
-            if (more) {
+                    for (int k = 0; k < 4; ++k) r += corr_s[k][wave][lane];
+                }
+                int code = P[j * d + col];
+                float wh = __shfl(cl, code, 64);
+                const float wh0 = wh;
+                const bool cand = lane < m;
+                const float fdiag = fdd[lane];            // F'[col][col]
+                for (int t0 = 0; t0 < SW_SUB; t0 += SW_SEG) {
+                    float fc[SW_SEG];                     // F[bs + t][bs + lane], t = t0..
 #pragma unroll
-                for (int e = 0; e < PER; ++e) {
-                    const int idx = tid * PER + e;
-                    if (idx < SUBF) {
-                        const int rr = idx / B, cc = idx - rr * B;
-                        pre[e] = Fg[(bs + (o + 1) * NB + rr) * d + bs + cc];
+                    for (int u = 0; u < SW_SEG; ++u) fc[u] = fdb[t0 + u][lane];
+#pragma unroll
+                    for (int u = 0; u < SW_SEG; ++u) {
+                        const int t = t0 + u;
+                        const float ft = readlane_f(fdiag, t);
+                        const float rt = readlane_f(r, t);
+                        const float wt = readlane_f(wh, t);
+                        const float dl = cl - wt;
+                        const float dq = dl * fmaf(ft, dl, 2.f * rt);
+                        const int key = cand ? f32_order_key(dq) : 0x7fffffff;
+                        const int bk = __builtin_amdgcn_readlane(row16_min_i(key), 0);
+                        if (bk < -1) {                    // a strictly negative change exists
+                            const int q = __ffsll((long long)__ballot(key == bk)) - 1;
+                            const float cq = readlane_f(cl, q);
+                            const float delta = cq - wt;
+                            r = fmaf(delta, fc[u], r);
+                            if (lane == __builtin_amdgcn_readfirstlane(t)) {
+                                code = q;
+                                wh = cq;
+                            }
+                            dsum += (double)readlane_f(dq, q);
+                            moves += 1;
+                        }
                     }
                 }
-            }
-#pragma unroll
-            for (int t = 0; t < NB; ++t) {
-                const int i = o * NB + t;                 // coordinate within the block
-                const float ri = __shfl(r[t], o, 16);
-                const float wi = __shfl(wh[t], o, 16);
-                const float fii = fdiag[i];
-                float best = __builtin_inff();
-                int bq = l16;
-                if (l16 < m) {
-                    const float dl = cl - wi;
-                    best = dl * fmaf(fii, dl, 2.f * ri);
-                }
-#pragma unroll
-                for (int off = 8; off > 0; off >>= 1) {
-                    const float ob = __shfl_xor(best, off, 16);
-                    const int oq = __shfl_xor(bq, off, 16);
-                    if (ob < best || (ob == best && oq < bq)) { best = ob; bq = oq; }
-                }
-                const bool changed = best < 0.f;
-                const float cq = __shfl(cl, bq, 16);
-                const float delta = changed ? cq - wi : 0.f;
-                const float* frow = &fsub[buf][t][l16 * NB];
-#pragma unroll
-                for (int t2 = 0; t2 < NB; ++t2) r[t2] = fmaf(delta, frow[t2], r[t2]);
-                if (changed && l16 == o) {
-                    code[t] = bq;
-                    wh[t] = cq;
-                    dv[t] = delta;
-                }
-                if (changed) {
-                    dsum += (double)best;
-                    cnt += 1;
-                }
-            }
-            if (more) {
-#pragma unroll
-                for (int e = 0; e < PER; ++e) {
-                    const int idx = tid * PER + e;
-                    if (idx < SUBF) {
-                        const int rr = idx / B, cc = idx - rr * B;
-                        fsub[buf ^ 1][rr][cc] = pre[e];
-                    }
+                P[j * d + col] = (uint8_t)code;
+                const float dv = wh - wh0;
+                const uint32_t hb = f32_to_bf16_bits(dv);
+                Dhi[j * d + col] = (uint16_t)hb;
+                Dlo[j * d + col] = (uint16_t)f32_to_bf16_bits(dv - __uint_as_float(hb << 16));
+                const unsigned long long moved = __ballot(dv != 0.f);
+                if (lane == 0) {
+                    if (moved & 0xffffffffull) sweep_flags[bs >> 5] = 1u;
+                    if (moved >> 32) sweep_flags[(bs >> 5) + 1] = 1u;
                 }
             }
             __syncthreads();
         }
-
-        // ---- 3. codes and value changes of this block; mark changed 32-chunks
-        bool any = false;
-#pragma unroll
-        for (int t = 0; t < NB; ++t) any |= (dv[t] != 0.f);
-        if (rvalid) {
-#pragma unroll
-            for (int t = 0; t < NB; ++t) {
-                const int64_t col = bs + l16 * NB + t;
-                P[j * d + col] = (uint8_t)code[t];
-                const uint32_t hb = f32_to_bf16_bits(dv[t]);
-                Dhi[j * d + col] = (uint16_t)hb;
-                Dlo[j * d + col] = (uint16_t)f32_to_bf16_bits(dv[t] - __uint_as_float(hb << 16));
-            }
-            if (any) sweep_flags[(bs + l16 * NB) >> 5] = 1u;
-        }
-        __syncthreads();
     }
-    if (rvalid && l16 == 0) {
+    if (rvalid && lane == 0) {
         obj_out[j] = obj_in[j] + dsum;
-        if (n_changed) atomicAdd(n_changed, (unsigned long long)cnt);
+        if (n_changed) atomicAdd(n_changed, (unsigned long long)moves);
     }
 }
+
 
 // float64 sums of consecutive rows in a fixed order: out[0] = sum_j x[j]
 __global__ __launch_bounds__(256) void k_reduce_rows(const double* __restrict__ x, int64_t n,
@@ -884,11 +931,13 @@ static hipError_t launch_sweep(const float* F, int64_t d_out, int64_t d, int gro
                                const double* obj_in, double* obj_out,
                                unsigned long long* counter, hipStream_t st) {
     const int64_t rpg = d_out / groups;
-    const int wgs = (int)((rpg + 15) / 16);
+    const int wgs = (int)((rpg + SW_ROWS - 1) / SW_ROWS);
+    const int total = wgs * groups;
+    const int grid = (total + 7) / 8 * 8;          // the XCD remap needs a multiple of 8
     const size_t lds = (size_t)(d / 32) * sizeof(uint32_t);
     StageTimer tm(ST_LNQ_SWEEP, st);
-    hipLaunchKernelGGL(k_sweep<B>, dim3((unsigned)(wgs * groups)), dim3(256), lds, st, F, w.dF,
-                       w.fhi, w.flo, d, rpg, wgs, C, m, P, w.R, w.dhi, w.dlo, obj_in, obj_out,
+    hipLaunchKernelGGL(k_sweep<B>, dim3((unsigned)grid), dim3(1024), lds, st, F, w.dF, w.fhi,
+                       w.flo, d, rpg, wgs, total, C, m, P, w.R, w.dhi, w.dlo, obj_in, obj_out,
                        counter);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
@@ -899,7 +948,6 @@ hipError_t lnq_sweep_run(int block, const float* F, int64_t d_out, int64_t d, in
                          const double* obj_in, double* obj_out, unsigned long long* counter,
                          hipStream_t st) {
     switch (block) {
-        case 32: return launch_sweep<32>(F, d_out, d, groups, C, m, P, w, obj_in, obj_out, counter, st);
         case 64: return launch_sweep<64>(F, d_out, d, groups, C, m, P, w, obj_in, obj_out, counter, st);
         case 128: return launch_sweep<128>(F, d_out, d, groups, C, m, P, w, obj_in, obj_out, counter, st);
         case 256: return launch_sweep<256>(F, d_out, d, groups, C, m, P, w, obj_in, obj_out, counter, st);

@@ -120,7 +120,7 @@ def _sweep_check(prob, C, P0, P1, tol=1e-5, frac=0.999):
     return P_ref
 
 
-@pytest.mark.parametrize("block", [32, 64, 128, 256])
+@pytest.mark.parametrize("block", [64, 128, 256])
 def test_sweep_parity(device, mid, block):
     rng = np.random.default_rng(block)
     m = 8
@@ -210,7 +210,7 @@ def test_lnq_deterministic(device, mid):
 
 
 @pytest.mark.parametrize("d_in,d_out,groups,bits,block", [
-    (544, 200, 2, 2, 32),      # ragged matrix-core tiles, ragged 16-row sweep groups
+    (576, 200, 2, 2, 64),      # ragged matrix-core tiles, ragged 16-row sweep groups
     (256, 48, 1, 4, 256),      # m = 16, block 256
     (1024, 64, 4, 1, 64),      # m = 2, four groups of 16 rows
 ])
