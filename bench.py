@@ -52,7 +52,7 @@ def _stage_units(stage, wl, changed_total):
     if stage == "fisher_mfma":
         # unique entries of the symmetric F_g: n d (d + 1) flops per group
         return "mfma", n * d * (d + 1) * G, PEAK_BF16_MFMA, "TFLOP/s"
-    if stage == "lnq_u":
+    if stage == "lnq_gram":
         # the codebook gather: each row sums F' over the coordinates of each code,
         # d^2 adds per row and codebook step (add-only: half the FMA peak)
         return "alu", it * d_out * d * d, PEAK_FP32_VALU / 2, "TFLOP/s"
@@ -64,7 +64,7 @@ def _stage_units(stage, wl, changed_total):
         return "hbm", (it + 1) * d_out * d * (4 * m + 4 + 1 + 2 + 4), PEAK_HBM, "GB/s"
     if stage == "group_scale":
         return "hbm", 2 * n * d_out + 4 * G * n, PEAK_HBM, "GB/s"
-    if stage == "lnq_wf":
+    if stage == "lnq_resid":
         return "mfma", 2 * d_out * d * d, PEAK_BF16_MFMA, "TFLOP/s"
     return None
 
@@ -83,7 +83,7 @@ def main():
     dev = torch.device("cuda:0")
     wl = synth.workload(args.workload)
     print(f"[bench] workload {wl.name}: d_in={wl.d_in} d_out={wl.d_out} n={wl.n} "
-          f"groups={wl.groups} bits={wl.bits} iters={wl.iters} block={wl.block}",
+          f"groups={wl.groups} bits={wl.bits} iters={wl.iters}",
           file=sys.stderr, flush=True)
     t0 = time.time()
     inp = synth.make_inputs(wl, seed=args.seed)
@@ -107,7 +107,7 @@ def main():
 
     def step():
         gq.gq_fisher_accumulate(X, G, wl.groups, F=F, ws=ws_f)
-        return gq.lnq_quantize(W, F, wl.bits, wl.iters, block=wl.block, ridge_rel=1e-6, C=C,
+        return gq.lnq_quantize(W, F, wl.bits, wl.iters, block=64, ridge_rel=1e-6, C=C,
                                P=P, init=gq.GQ_INIT_QUANTILE, ws=ws_l)
 
     for i in range(args.warmup):
@@ -166,7 +166,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "d_in": wl.d_in, "d_out": wl.d_out, "n_tokens": wl.n,
-                   "groups": wl.groups, "bits": wl.bits, "iters": wl.iters, "block": wl.block},
+                   "groups": wl.groups, "bits": wl.bits, "iters": wl.iters, "block": 64},
         "fisher_tflops": sym_flops / (fisher_ms * 1e-3) / 1e12 if fisher_ms else None,
         "fisher_tflops_gemm_convention": (2 * wl.n * wl.d_in ** 2 * wl.groups) /
         (fisher_ms * 1e-3) / 1e12 if fisher_ms else None,

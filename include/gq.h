@@ -76,12 +76,12 @@ typedef enum { GQ_F32 = 0, GQ_BF16 = 1 } gq_dtype;
 typedef enum { GQ_INIT_QUANTILE = 0, GQ_INIT_GIVEN = 1 } gq_lnq_init;
 
 typedef struct {
-    int32_t block;      /* assignment block B: the effect of earlier moves of a pass on the
-                           residuals of the next B coordinates is applied once per B-block on
-                           the matrix cores; inside it, coordinates are decided 64 at a time
-                           in registers.  One of 64, 128, 256 with d_in % B == 0.  Changes only
-                           the float32 summation order (coordinates are always visited in
-                           ascending order).  Default 128. */
+    int32_t block;      /* assignment block: coordinates decided exactly in registers (one per
+                           lane of a 64-wide wavefront) before the effect of their moves on the
+                           following coordinates is applied on the matrix cores.  Must be 64
+                           (d_in % 64 == 0); the block size changes only the float32 summation
+                           order, never the order in which coordinates are visited.
+                           Default 64. */
     float ridge_rel;    /* rho in lambda_g = rho * mean(diag F_g).  Default 1e-6. */
     int32_t init;       /* gq_lnq_init.  QUANTILE: c_j = m quantiles of w_j at levels
                            (q + 1/2)/m (linear interpolation between order statistics),
@@ -149,7 +149,7 @@ gq_status lnq_codebook_update(const float* F, int32_t groups, int64_t d_in,
  * objective, and among equal minimisers the lowest index wins.
  * P [d_out][d_in] is read and overwritten; C [d_out][m] is read.  The number of
  * coordinates that changed is added to *n_changed (device int64, may be NULL).
- * block: as gq_lnq_options.block.
+ * block: as gq_lnq_options.block (64).
  */
 gq_status lnq_assign_sweep(const float* F, int32_t groups, int64_t d_in,
                            const void* W, gq_dtype w_dt, int64_t d_out,
@@ -202,10 +202,10 @@ typedef enum {
     GQ_STAGE_FISHER_FINALIZE,   /* split-K sum + mirror write of F */
     GQ_STAGE_FISHER_PLAIN,      /* float32-input Fisher */
     GQ_STAGE_LNQ_PREPARE,       /* ridge and F' planes */
-    GQ_STAGE_LNQ_WF,            /* V = W F' */
+    GQ_STAGE_LNQ_RESID,         /* residual R = F'(C[P] - W) on the matrix cores */
     GQ_STAGE_LNQ_INIT,          /* quantile codebooks and nearest codes */
-    GQ_STAGE_LNQ_U,             /* U_j = F' P_j */
-    GQ_STAGE_LNQ_SOLVE,         /* codebook systems, solves, residuals, objectives */
+    GQ_STAGE_LNQ_GRAM,          /* P_j^T F' P_j on the matrix cores */
+    GQ_STAGE_LNQ_SOLVE,         /* codebook solves and row objectives */
     GQ_STAGE_LNQ_SWEEP,         /* the assignment pass */
     GQ_STAGE_LNQ_SMALL,         /* sums and counters */
     GQ_STAGE_COUNT

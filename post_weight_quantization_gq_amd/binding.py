@@ -130,7 +130,7 @@ def abi_version() -> int:
     return library().gq_abi_version()
 
 
-def options(block: int = 128, ridge_rel: float = 1e-6, init: int = GQ_INIT_QUANTILE) -> lnq_options:
+def options(block: int = 64, ridge_rel: float = 1e-6, init: int = GQ_INIT_QUANTILE) -> lnq_options:
     o = lnq_options()
     library().gq_lnq_options_default(ctypes.byref(o))
     o.block, o.ridge_rel, o.init = block, ridge_rel, init
@@ -203,7 +203,7 @@ def lnq_codebook_update(F, W, P, C, bits: int, ridge_rel: float = 1e-6, n_not_pd
     return C
 
 
-def lnq_assign_sweep(F, W, C, P, bits: int, ridge_rel: float = 1e-6, block: int = 128,
+def lnq_assign_sweep(F, W, C, P, bits: int, ridge_rel: float = 1e-6, block: int = 64,
                      n_changed=None, ws=None, stream=None) -> torch.Tensor:
     """One assignment pass; P [d_out][d_in] uint8 is updated in place."""
     lib = library()
@@ -234,7 +234,7 @@ def lnq_objective(F, W, C, P, bits: int, ridge_rel: float = 1e-6, obj_total=None
     return rows
 
 
-def lnq_quantize(W, F, bits: int, iters: int, block: int = 128, ridge_rel: float = 1e-6,
+def lnq_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float = 1e-6,
                  C=None, P=None, init: int | None = None, trace: bool = True,
                  ws=None, stream=None):
     """Whole LNQ on a layer.  Returns (C, P, obj_trace or None, n_changed).

@@ -134,7 +134,7 @@ gq_status check_lnq_shape(const float* F, int32_t groups, int64_t d_in, const vo
     return GQ_OK;
 }
 
-bool block_ok(int32_t b) { return b == 64 || b == 128 || b == 256; }
+bool block_ok(int32_t b) { return b == 64; }
 
 }  // namespace
 
@@ -171,7 +171,7 @@ gq_status gq_timing_read(double* ms, int64_t* launches) {
 const char* gq_stage_name(int stage) {
     static const char* names[GQ_STAGE_COUNT] = {
         "group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain", "lnq_prepare",
-        "lnq_wf", "lnq_init", "lnq_u", "lnq_solve", "lnq_sweep", "lnq_small"};
+        "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep", "lnq_small"};
     if (stage < 0 || stage >= GQ_STAGE_COUNT) return "";
     return names[stage];
 }
@@ -180,7 +180,7 @@ const char* gq_last_error(void) { return g_last_error.c_str(); }
 
 void gq_lnq_options_default(gq_lnq_options* opt) {
     if (!opt) return;
-    opt->block = 128;
+    opt->block = 64;
     opt->ridge_rel = 1e-6f;
     opt->init = GQ_INIT_QUANTILE;
     opt->reserved = 0;
@@ -220,7 +220,7 @@ gq_status gq_fisher_accumulate(const void* X, gq_dtype x_dt, int64_t n, int64_t 
 size_t gq_lnq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_t bits,
                              gq_dtype w_dt) {
     if (d_out < 1 || d_in < 1 || groups < 1 || bits < 1 || bits > 8) return 0;
-    return gq::lnq_sizes(d_out, d_in, groups, 1 << bits, w_dt == GQ_F32).total;
+    return gq::lnq_sizes(d_out, d_in, groups, 1 << bits).total;
 }
 
 gq_status lnq_codebook_update(const float* F, int32_t groups, int64_t d_in, const void* W,
@@ -234,15 +234,14 @@ gq_status lnq_codebook_update(const float* F, int32_t groups, int64_t d_in, cons
     hipStream_t st = (hipStream_t)stream;
     const bool wb = w_dt == GQ_BF16;
     const int m = 1 << bits;
-    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m, !wb);
+    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m);
     Scratch s;
     if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
-    gq::LnqWs w = gq::lnq_carve(s.ptr, z, !wb);
+    gq::LnqWs w = gq::lnq_carve(s.ptr, z);
     hipError_t e;
     if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
-    if ((e = gq::lnq_compute_v(W, wb, d_out, d_in, groups, w, st)) != hipSuccess) return hip_fail(e, "W F'");
-    if ((e = gq::lnq_u_solve(0, W, wb, d_out, d_in, groups, m, P, C, w, nullptr, w.objA, w.objB,
-                             (unsigned long long*)n_not_pd, st)) != hipSuccess)
+    if ((e = gq::lnq_codebook_step(W, wb, d_out, d_in, groups, m, P, C, w, w.objA,
+                                   (unsigned long long*)n_not_pd, st)) != hipSuccess)
         return hip_fail(e, "codebook");
     return GQ_OK;
 }
@@ -255,24 +254,20 @@ gq_status lnq_assign_sweep(const float* F, int32_t groups, int64_t d_in, const v
     if (rc != GQ_OK) return rc;
     if (!P || !C) return fail(GQ_EINVAL, "null P or C");
     if (!al16(P) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "P must be 16-byte and ws 256-byte aligned");
-    if (!block_ok(block)) return fail(GQ_EINVAL, "block=%d not in {64, 128, 256}", block);
+    if (!block_ok(block)) return fail(GQ_EINVAL, "block=%d: the pass uses blocks of 64 coordinates", block);
     if (d_in % block) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of block=%d",
                                   (long long)d_in, block);
     hipStream_t st = (hipStream_t)stream;
     const bool wb = w_dt == GQ_BF16;
     const int m = 1 << bits;
-    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m, !wb);
+    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m);
     Scratch s;
     if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
-    gq::LnqWs w = gq::lnq_carve(s.ptr, z, !wb);
+    gq::LnqWs w = gq::lnq_carve(s.ptr, z);
     hipError_t e;
     if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
-    if ((e = gq::lnq_compute_v(W, wb, d_out, d_in, groups, w, st)) != hipSuccess) return hip_fail(e, "W F'");
-    if ((e = gq::lnq_u_solve(1, W, wb, d_out, d_in, groups, m, P, (float*)C, w, w.R, w.objA,
-                             w.objB, nullptr, st)) != hipSuccess)
-        return hip_fail(e, "residual");
-    if ((e = gq::lnq_sweep_run(block, F, d_out, d_in, groups, C, m, P, w, w.objB, w.objC,
-                               (unsigned long long*)n_changed, st)) != hipSuccess)
+    if ((e = gq::lnq_sweep_step(block, F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB, w.objC,
+                                (unsigned long long*)n_changed, st)) != hipSuccess)
         return hip_fail(e, "sweep");
     return GQ_OK;
 }
@@ -288,15 +283,13 @@ gq_status lnq_objective(const float* F, int32_t groups, int64_t d_in, const void
     hipStream_t st = (hipStream_t)stream;
     const bool wb = w_dt == GQ_BF16;
     const int m = 1 << bits;
-    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m, !wb);
+    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m);
     Scratch s;
     if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
-    gq::LnqWs w = gq::lnq_carve(s.ptr, z, !wb);
+    gq::LnqWs w = gq::lnq_carve(s.ptr, z);
     hipError_t e;
     if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
-    if ((e = gq::lnq_compute_v(W, wb, d_out, d_in, groups, w, st)) != hipSuccess) return hip_fail(e, "W F'");
-    if ((e = gq::lnq_u_solve(1, W, wb, d_out, d_in, groups, m, P, (float*)C, w, nullptr, nullptr,
-                             obj_rows, nullptr, st)) != hipSuccess)
+    if ((e = gq::lnq_objective_rows(W, wb, d_out, d_in, groups, m, P, C, w, obj_rows, st)) != hipSuccess)
         return hip_fail(e, "objective");
     if (obj_total && (e = gq::lnq_reduce(obj_rows, d_out, obj_total, st)) != hipSuccess)
         return hip_fail(e, "objective sum");
@@ -318,43 +311,43 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
     if (o.reserved != 0) return fail(GQ_EINVAL, "options.reserved must be 0");
     if (o.init != GQ_INIT_QUANTILE && o.init != GQ_INIT_GIVEN)
         return fail(GQ_EINVAL, "unknown init %d", o.init);
-    if (!block_ok(o.block)) return fail(GQ_EINVAL, "block=%d not in {64, 128, 256}", o.block);
+    if (!block_ok(o.block)) return fail(GQ_EINVAL, "block=%d: the pass uses blocks of 64 coordinates", o.block);
     if (d_in % o.block) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of block=%d",
                                     (long long)d_in, o.block);
     hipStream_t st = (hipStream_t)stream;
     const bool wb = w_dt == GQ_BF16;
     const int m = 1 << bits;
-    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m, !wb);
+    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m);
     Scratch s;
     if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
-    gq::LnqWs w = gq::lnq_carve(s.ptr, z, !wb);
+    gq::LnqWs w = gq::lnq_carve(s.ptr, z);
     hipError_t e;
     if ((e = gq::lnq_prepare(F, groups, d_in, o.ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
-    if ((e = gq::lnq_compute_v(W, wb, d_out, d_in, groups, w, st)) != hipSuccess) return hip_fail(e, "W F'");
     if (o.init == GQ_INIT_QUANTILE &&
         (e = gq::lnq_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
         return hip_fail(e, "init");
     for (int t = 1; t <= iters; ++t) {
-        // codebook step; also the from-scratch objective before it (entry 2t-2)
-        if ((e = gq::lnq_u_solve(0, W, wb, d_out, d_in, groups, m, P, C, w, w.R, w.objA, w.objB,
-                                 w.cnt + 1, st)) != hipSuccess)
+        // codebook step; objA = objective before it (trace entry 2t-2), from scratch
+        if ((e = gq::lnq_codebook_step(W, wb, d_out, d_in, groups, m, P, C, w, w.objA, w.cnt + 1,
+                                       st)) != hipSuccess)
             return hip_fail(e, "codebook");
+        if ((e = gq::lnq_zero_counter(w.cnt, st)) != hipSuccess) return hip_fail(e, "counter");
+        // assignment pass; objB = objective after the codebook step (entry 2t-1), from scratch
+        if ((e = gq::lnq_sweep_step(o.block, F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB,
+                                    w.objC, w.cnt, st)) != hipSuccess)
+            return hip_fail(e, "sweep");
         if (obj_trace) {
             if ((e = gq::lnq_reduce(w.objA, d_out, obj_trace + 2 * t - 2, st)) != hipSuccess ||
                 (e = gq::lnq_reduce(w.objB, d_out, obj_trace + 2 * t - 1, st)) != hipSuccess)
                 return hip_fail(e, "trace");
         }
-        if ((e = gq::lnq_zero_counter(w.cnt, st)) != hipSuccess) return hip_fail(e, "counter");
-        if ((e = gq::lnq_sweep_run(o.block, F, d_out, d_in, groups, C, m, P, w, w.objB, w.objC,
-                                   w.cnt, st)) != hipSuccess)
-            return hip_fail(e, "sweep");
         if (n_changed && (e = gq::lnq_store_counter(w.cnt, n_changed + (t - 1), st)) != hipSuccess)
             return hip_fail(e, "counter");
     }
     if (obj_trace) {
         // objective of the final (C, P), from scratch
-        if ((e = gq::lnq_u_solve(1, W, wb, d_out, d_in, groups, m, P, C, w, nullptr, nullptr,
-                                 w.objA, nullptr, st)) != hipSuccess)
+        if ((e = gq::lnq_objective_rows(W, wb, d_out, d_in, groups, m, P, C, w, w.objA, st)) !=
+            hipSuccess)
             return hip_fail(e, "final objective");
         if ((e = gq::lnq_reduce(w.objA, d_out, obj_trace + 2 * iters, st)) != hipSuccess)
             return hip_fail(e, "trace");

@@ -9,7 +9,7 @@ namespace gq {
 // ---- per-stage HIP-event timing (gq_api.hip); stage ids are gq_stage of gq.h
 enum Stage {
     ST_GROUP_SCALE = 0, ST_FISHER_MFMA, ST_FISHER_FINALIZE, ST_FISHER_PLAIN, ST_LNQ_PREPARE,
-    ST_LNQ_WF, ST_LNQ_INIT, ST_LNQ_U, ST_LNQ_SOLVE, ST_LNQ_SWEEP, ST_LNQ_SMALL, ST_COUNT
+    ST_LNQ_RESID, ST_LNQ_INIT, ST_LNQ_GRAM, ST_LNQ_SOLVE, ST_LNQ_SWEEP, ST_LNQ_SMALL, ST_COUNT
 };
 bool timing_on();
 void timing_mark(Stage s, hipStream_t st, bool begin);
@@ -33,42 +33,46 @@ hipError_t fisher_run(const void* X, const void* G, bool bf16, int64_t n, int64_
                       int64_t d_out, int groups, float* F, int accumulate, void* ws,
                       hipStream_t st);
 
-// ---- LNQ (gq_lnq.hip)
+// ---- LNQ (gq_lnq.hip, gq_lnq_mm.hip)
 struct LnqSizes {
-    size_t o_fhi, o_flo, o_dF, o_lam, o_V, o_U, o_R, o_dhi, o_dlo, o_whi, o_wlo;
+    size_t o_fhi, o_flo, o_dF, o_lam, o_R, o_ehi, o_elo, o_part;
     size_t o_objA, o_objB, o_objC, o_cnt, total;
-    int gchunk;
 };
 struct LnqWs {
     uint16_t *fhi, *flo;          // F' planes [groups][d][d]
     float* dF;                    // diag F' [groups][d]
     double* lam;                  // [groups]
-    float* V;                     // W F' [d_out][d]
-    float* U;                     // F' P_j for gchunk groups [rows*m][d]
-    float* R;                     // residual [d_out][d]
-    uint16_t *dhi, *dlo;          // value changes of the current pass [d_out][d]
-    uint16_t *whi, *wlo;          // float32 W split into bf16 planes (else null)
+    float* R;                     // residual F'(C[P] - W) [d_out][d]
+    uint16_t *ehi, *elo;          // C[P] - W as bf16 planes; the sweep's value changes
+    float* part;                  // Gram partials [d / 256][d_out * m][m]
     double *objA, *objB, *objC;   // per-row objectives [d_out]
     unsigned long long* cnt;      // counters [16]
-    int gchunk;                   // groups per U chunk
 };
 
-LnqSizes lnq_sizes(int64_t d_out, int64_t d, int groups, int m, bool w_f32);
-LnqWs lnq_carve(void* base, const LnqSizes& z, bool w_f32);
+LnqSizes lnq_sizes(int64_t d_out, int64_t d, int groups, int m);
+LnqWs lnq_carve(void* base, const LnqSizes& z);
+size_t lnq_gram_partial_floats(int64_t d_out, int64_t d, int m);
 hipError_t lnq_prepare(const float* F, int groups, int64_t d, double rho, const LnqWs& w,
                        hipStream_t st);
-hipError_t lnq_compute_v(const void* W, bool w_bf16, int64_t d_out, int64_t d, int groups,
-                         const LnqWs& w, hipStream_t st);
 hipError_t lnq_init_run(const void* W, bool w_bf16, int64_t d_out, int64_t d, int m, float* C,
                         uint8_t* P, hipStream_t st);
-hipError_t lnq_u_solve(int mode, const void* W, bool w_bf16, int64_t d_out, int64_t d,
-                       int groups, int m, const uint8_t* P, float* C, const LnqWs& w, float* R,
-                       double* obj_old, double* obj_new, unsigned long long* n_not_pd,
-                       hipStream_t st);
-hipError_t lnq_sweep_run(int block, const float* F, int64_t d_out, int64_t d, int groups,
-                         const float* C, int m, uint8_t* P, const LnqWs& w,
-                         const double* obj_in, double* obj_out, unsigned long long* counter,
-                         hipStream_t st);
+hipError_t lnq_residual(const uint16_t* Ehi, const uint16_t* Elo, int64_t d_out, int64_t d,
+                        int groups, const uint16_t* Fhi, const uint16_t* Flo, float* R,
+                        hipStream_t st);
+hipError_t lnq_gram(const uint8_t* P, int m, int64_t d_out, int64_t d, int groups,
+                    const uint16_t* Fhi, const uint16_t* Flo, float* part, hipStream_t st);
+// codebook step on every row; obj_before[j] = objective of (C, P) before it
+hipError_t lnq_codebook_step(const void* W, bool w_bf16, int64_t d_out, int64_t d, int groups,
+                             int m, const uint8_t* P, float* C, const LnqWs& w, double* obj_before,
+                             unsigned long long* n_not_pd, hipStream_t st);
+hipError_t lnq_objective_rows(const void* W, bool w_bf16, int64_t d_out, int64_t d, int groups,
+                              int m, const uint8_t* P, const float* C, const LnqWs& w,
+                              double* obj, hipStream_t st);
+// assignment pass; obj_start/obj_end[j] = objective before / after it (may be null)
+hipError_t lnq_sweep_step(int block, const float* F, const void* W, bool w_bf16, int64_t d_out,
+                          int64_t d, int groups, const float* C, int m, uint8_t* P,
+                          const LnqWs& w, double* obj_start, double* obj_end,
+                          unsigned long long* counter, hipStream_t st);
 hipError_t lnq_reduce(const double* rows, int64_t n, double* out, hipStream_t st);
 hipError_t lnq_zero_counter(unsigned long long* c, hipStream_t st);
 hipError_t lnq_store_counter(const unsigned long long* c, int64_t* dst, hipStream_t st);

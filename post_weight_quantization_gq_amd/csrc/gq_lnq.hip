@@ -13,17 +13,17 @@
 //   k_split        F' -> two bfloat16 planes hi + lo (F' ~= hi + lo to ~2^-17),
 //                  plus diag(F') in float32
 //   k_lnq_init     per row: sort w_j in LDS, m linear quantiles, nearest codes
-//   k_fgemm        MFMA products with F': V = W F' (iteration invariant) and
-//                  U_j = F' P_j for every row (P_j one-hot, built from the codes
-//                  while staging; exact in bfloat16)
-//   k_solve        per row: A_j = P_j^T U_j, b_j = P_j^T v_j, float64 Cholesky on
-//                  the non-empty codes, residual r_j = U_j c_j - v_j and objectives
-//   k_sweep        per 16-row group: ascending coordinate descent on the residual;
-//                  inside a block of B coordinates every update is applied at once
-//                  (registers + LDS), the effect of earlier blocks on the next one
-//                  is gathered on MFMA from the recorded value changes (left-looking)
+//   k_err_split    E = C[P] - W in float32, split into bfloat16 hi + lo planes
+//   k_mm (gq_lnq_mm.hip)  residual R = E F' and the codebook Gram blocks
+//                  P_j^T F' P_j on the matrix cores
+//   k_solve        per row: g = P_j^T r_j, the m x m system from the Gram
+//                  partials, float64 Cholesky on the non-empty codes and the
+//                  closed-form codebook c <- c - A^{-1} g (= A^{-1} P^T F' w);
+//                  also the row objective e . r
+//   k_sweep        per 16-row group: the ascending coordinate pass (see there)
 //   k_reduce_rows  float64 layer sums in a fixed order
 #include "gq_common.h"
+#include "gq_internal.h"
 
 namespace gq {
 
@@ -81,29 +81,6 @@ __global__ __launch_bounds__(256) void k_split(const float* __restrict__ F, int6
         float r1 = f1 - __uint_as_float(hb & 0xffff0000u);
         h[k] = hb;
         l[k] = pack_bf16x2(r0, r1);
-    }
-    *(u32x4*)(hi_plane + e0) = h;
-    *(u32x4*)(lo_plane + e0) = l;
-}
-
-// float32 rows -> bf16 planes (hi, lo), 8 elements per thread (d % 8 == 0)
-__global__ __launch_bounds__(256) void k_split_rows(const float* __restrict__ W,
-                                                   uint16_t* __restrict__ hi_plane,
-                                                   uint16_t* __restrict__ lo_plane,
-                                                   int64_t total8) {
-    const int64_t idx8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx8 >= total8) return;
-    const int64_t e0 = idx8 * 8;
-    const float4* src = (const float4*)(W + e0);
-    float4 x0 = src[0], x1 = src[1];
-    float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    u32x4 h, l;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t hb = pack_bf16x2(v[2 * k], v[2 * k + 1]);
-        h[k] = hb;
-        l[k] = pack_bf16x2(v[2 * k] - __uint_as_float(hb << 16),
-                           v[2 * k + 1] - __uint_as_float(hb & 0xffff0000u));
     }
     *(u32x4*)(hi_plane + e0) = h;
     *(u32x4*)(lo_plane + e0) = l;
@@ -172,263 +149,139 @@ __global__ __launch_bounds__(1024) void k_lnq_init(const void* __restrict__ W, i
 }
 
 // ---------------------------------------------------------------------------
-// k_fgemm: out[g][n][a] (=|+=) sum_i A[n][i] * F'_g[i][a]   (F' symmetric: F'[i][a]
-// is read as row a of the plane).  A is either a bf16 matrix (rows of W or of a
-// bf16 plane of W) or the one-hot expansion of the codes: row n = j*m + q is
-// [P[j][i] == q].  Block tile 256 (n) x 256 (a), 4 waves of 128 x 128 = 4x4 MFMA
-// 32x32x16 tiles, K staged 32 at a time through LDS (pitch 40 = conflict-free).
+// E = C[j][P[j][i]] - W[j][i] (float32) -> bf16 planes hi + lo.  8 elements per
+// thread (d % 8 == 0, so they share a row).
 // ---------------------------------------------------------------------------
-constexpr int GT = 256;
-constexpr int GKC = 32;
-constexpr int GPITCH = 40;
-constexpr int G_PLANE = GT * GPITCH;         // bf16 elements per staged 256x32 operand
-
-template <bool ONEHOT, int NPB>
-__global__ __launch_bounds__(256, 1) void k_fgemm(
-    const uint16_t* __restrict__ Abf,  // bf16 rows [rows_total][d] (ONEHOT=false)
-    const uint8_t* __restrict__ codes, // [rows_total][d] (ONEHOT=true)
-    int m, int64_t rows_per_group, int g_first,
-    const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo, int64_t d,
-    int n_tiles_n, int n_tiles_a, int accumulate, float* __restrict__ out) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t fgemm_lds[];
-    // per stage: A plane (or codes) + NPB F' planes
-    constexpr int STAGE = G_PLANE * (1 + NPB);
-    auto stage_base = [&](int b) { return fgemm_lds + b * STAGE; };
-
-    const int bid = blockIdx.x;
-    const int tn = bid % n_tiles_n;
-    const int ta = (bid / n_tiles_n) % n_tiles_a;
-    const int gl = bid / (n_tiles_n * n_tiles_a);     // group within this launch
-    const int g = g_first + gl;
-    const int64_t N = ONEHOT ? rows_per_group * m : rows_per_group;
-    const int64_t n0 = (int64_t)tn * GT, a0 = (int64_t)ta * GT;
-    const int64_t row_base = (int64_t)g * rows_per_group;   // first W/code row of group
-    const uint16_t* Fh = Fhi + (size_t)g * d * d;
-    const uint16_t* Fl = (NPB > 1) ? Flo + (size_t)g * d * d : nullptr;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 1, wa = wave >> 1;
-
-    f32x16 acc[4][4];
+template <bool WBF16>
+__global__ __launch_bounds__(256) void k_err_split(const float* __restrict__ C, int m,
+                                                  const uint8_t* __restrict__ P,
+                                                  const void* __restrict__ W, int64_t d,
+                                                  uint16_t* __restrict__ Ehi,
+                                                  uint16_t* __restrict__ Elo, int64_t total8) {
+    const int64_t idx8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx8 >= total8) return;
+    const int64_t e0 = idx8 * 8;
+    const int64_t j = e0 / d;
+    const float* cj = C + j * m;
+    const u32x2 pc = *(const u32x2*)(P + e0);
+    float w[8];
+    if constexpr (WBF16) {
+        const u32x4 wv = *(const u32x4*)((const uint16_t*)W + e0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    // staging map: 256 rows x 4 quads of 8 elements; thread covers rows r0 + 64*s
-    const int sr = tid >> 2, sq = tid & 3;
-    u32x4 pa[4], pf[NPB][4];
-    u32x4 pc = {0u, 0u, 0u, 0u};  // ONEHOT: 16 codes of one j-row
-    const int jrows = ONEHOT ? GT / m : 0;   // distinct j-rows in an n tile
-
-    auto fetch = [&](int64_t k0) {
-        const int64_t kk = k0 + 8 * sq;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int r = sr + 64 * s;
-            const int64_t arow = a0 + r;
-#pragma unroll
-            for (int p = 0; p < NPB; ++p) {
-                const uint16_t* base = (p == 0) ? Fh : Fl;
-                pf[p][s] = (arow < d && kk < d) ? *(const u32x4*)(base + arow * d + kk)
-                                                : u32x4{0u, 0u, 0u, 0u};
-            }
-            if constexpr (!ONEHOT) {
-                const int64_t nrow = n0 + r;
-                pa[s] = (nrow < N && kk < d) ? *(const u32x4*)(Abf + (row_base + nrow) * d + kk)
-                                             : u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int k = 0; k < 4; ++k) {
+            w[2 * k] = __uint_as_float(wv[k] << 16);
+            w[2 * k + 1] = __uint_as_float(wv[k] & 0xffff0000u);
         }
-        if constexpr (ONEHOT) {
-            // jrows (<= 128) rows x 32 codes: thread covers row tid/2, bytes 16*(tid%2)
-            const int r = tid >> 1;
-            const int64_t jl = n0 / m + r;
-            const int64_t kc = k0 + 16 * (tid & 1);
-            if (r < jrows && jl < rows_per_group && kc < d) {
-                pc = *(const u32x4*)(codes + (row_base + jl) * d + kc);
-            } else {
-                pc = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};  // matches no code
-            }
-        }
-    };
-    auto stage = [&](int buf) {
-        uint16_t* S = stage_base(buf);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int r = sr + 64 * s;
-#pragma unroll
-            for (int p = 0; p < NPB; ++p)
-                *(u32x4*)(S + G_PLANE * (1 + p) + r * GPITCH + 8 * sq) = pf[p][s];
-            if constexpr (!ONEHOT) *(u32x4*)(S + r * GPITCH + 8 * sq) = pa[s];
-        }
-        if constexpr (ONEHOT) {
-            uint8_t* cs = (uint8_t*)S;
-            *(u32x4*)(cs + (tid >> 1) * 32 + 16 * (tid & 1)) = pc;
-        }
-    };
-
-    const int nk = (int)((d + GKC - 1) / GKC);
-    fetch(0);
-    stage(0);
-    __syncthreads();
-    for (int kc = 0; kc < nk; ++kc) {
-        const int buf = kc & 1;
-        const bool more = kc + 1 < nk;
-        if (more) fetch((int64_t)(kc + 1) * GKC);
-        const uint16_t* S = stage_base(buf);
-#pragma unroll 1
-        for (int ks = 0; ks < GKC / 16; ++ks) {
-            const int koff = ks * 16 + 8 * (lane >> 5);
-            bf16x8 af[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int nl = 128 * wn + 32 * i + (lane & 31);
-                if constexpr (ONEHOT) {
-                    const int jr = nl / m, q = nl - jr * m;
-                    const u32x2 cv = *(const u32x2*)((const uint8_t*)S + jr * 32 + koff);
-                    u32x4 o;
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        const uint32_t word = cv[h >> 1];
-                        const uint32_t b0 = (word >> (16 * (h & 1))) & 0xffu;
-                        const uint32_t b1 = (word >> (16 * (h & 1) + 8)) & 0xffu;
-                        o[h] = ((b0 == (uint32_t)q) ? 0x3F80u : 0u) |
-                               ((b1 == (uint32_t)q) ? 0x3F800000u : 0u);
-                    }
-                    af[i] = as_bf16x8(o);
-                } else {
-                    af[i] = as_bf16x8(*(const u32x4*)(S + nl * GPITCH + koff));
-                }
-            }
-#pragma unroll
-            for (int p = 0; p < NPB; ++p) {
-                bf16x8 bfr[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    bfr[j] = as_bf16x8(*(const u32x4*)(S + G_PLANE * (1 + p) +
-                                                       (128 * wa + 32 * j + (lane & 31)) * GPITCH + koff));
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-            }
-        }
-        if (more) stage(buf ^ 1);
-        __syncthreads();
+    } else {
+        const float4 a = *(const float4*)((const float*)W + e0);
+        const float4 b = *(const float4*)((const float*)W + e0 + 4);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
     }
-
-    float* O = out + (size_t)gl * N * d + (size_t)n0 * d + a0;
-    const int nrem = (int)((N - n0) < GT ? (N - n0) : GT);
-    const int arem = (int)((d - a0) < GT ? (d - a0) : GT);
-    const int di = (int)d;
+    u32x4 h, l;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int acol = 128 * wa + 32 * j + (lane & 31);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int nrow = 128 * wn + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (nrow < nrem && acol < arem) {
-                    float* dst = O + (size_t)(nrow * di) + acol;
-                    float x = acc[i][j][v];
-                    if (accumulate) x += *dst;
-                    *dst = x;
-                }
-            }
-        }
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t c0 = (pc[k >> 1] >> (16 * (k & 1))) & 0xffu;
+        const uint32_t c1 = (pc[k >> 1] >> (16 * (k & 1) + 8)) & 0xffu;
+        const float x0 = cj[c0 < (uint32_t)m ? c0 : 0] - w[2 * k];
+        const float x1 = cj[c1 < (uint32_t)m ? c1 : 0] - w[2 * k + 1];
+        const uint32_t hb = pack_bf16x2(x0, x1);
+        h[k] = hb;
+        l[k] = pack_bf16x2(x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u));
+    }
+    *(u32x4*)(Ehi + e0) = h;
+    *(u32x4*)(Elo + e0) = l;
 }
 
 // ---------------------------------------------------------------------------
 // k_solve: one wave per row (4 rows per block).
-//   MODE 0 (SOLVE): codebook step on the non-empty codes, then r = U c_new - v
-//   MODE 1 (RESID): keep c, r = U c - v
-// Writes R[j] (if R != null), obj_old[j] = e_old . r_old, obj_new[j] = e_new . r_new.
-// U holds the rows of the current group chunk: U[(j - j_first) * m + q][a].
+//   Always: obj[j] = sum_a e_a r_a (float64), e = C[j][P[j][a]] - W[j][a].
+//   SOLVE:  g = P^T r (the objective's gradient in c, halved), counts per code,
+//           A = B + B^T from the Gram partials (summed over a-tiles in order),
+//           float64 Cholesky of A on the non-empty codes S and
+//               c_S <- c_S - A_SS^{-1} g_S,
+//           which is the closed form (P^T F' P)^{-1} P^T F' w because
+//           g = P^T F'(P c - w) = A c - P^T F' w.  Empty codes keep c.
 // ---------------------------------------------------------------------------
-template <bool BF16, int MODE>
-__global__ __launch_bounds__(256) void k_solve(
-    const float* __restrict__ U, int64_t j_first, int64_t j_count, const float* __restrict__ V,
-    const uint8_t* __restrict__ P, const void* __restrict__ W, float* __restrict__ C, int m,
-    int64_t d, float* __restrict__ R, double* __restrict__ obj_old, double* __restrict__ obj_new,
-    unsigned long long* __restrict__ n_not_pd) {
-    __shared__ double sA[4][MAX_M][MAX_M];
-    __shared__ double sL[4][MAX_M][MAX_M];
-    __shared__ double sb[4][MAX_M];
-    __shared__ double sy[4][MAX_M];
-    __shared__ int scnt[4][MAX_M];
-    __shared__ int sidx[4][MAX_M];
-    __shared__ float sc_old[4][MAX_M];
-    __shared__ float sc_new[4][MAX_M];
+template <int M, bool WBF16, bool SOLVE>
+__global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, int ntile_a,
+                                              const float* __restrict__ R,
+                                              const uint8_t* __restrict__ P,
+                                              const void* __restrict__ W, float* __restrict__ C,
+                                              int64_t d, int64_t d_out,
+                                              double* __restrict__ obj,
+                                              unsigned long long* __restrict__ n_not_pd) {
+    __shared__ double sB[4][M][M];
+    __shared__ double sL[4][M][M];
+    __shared__ double sg[4][M];
+    __shared__ double sy[4][M];
+    __shared__ int scnt[4][M];
+    __shared__ int sidx[4][M];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t jl = (int64_t)blockIdx.x * 4 + wave;
-    const bool valid = jl < j_count;
-    const int64_t j = j_first + (valid ? jl : 0);
-    const float* Uj = U + (size_t)(valid ? jl : 0) * m * d;
-    const float* vj = V + (size_t)j * d;
-    const uint8_t* pj = P + (size_t)j * d;
+    const int64_t j0 = (int64_t)blockIdx.x * 4 + wave;
+    const bool valid = j0 < d_out;
+    const int64_t j = valid ? j0 : 0;
 
-    if (lane < m) sc_old[wave][lane] = valid ? C[j * m + lane] : 0.f;
-    if (MODE == 0 && valid) {
-        // b = P^T v and the code counts
-        float bacc[MAX_M];
-        int cnt[MAX_M];
+    float cv[M];
 #pragma unroll
-        for (int k = 0; k < MAX_M; ++k) { bacc[k] = 0.f; cnt[k] = 0; }
+    for (int k = 0; k < M; ++k) cv[k] = C[j * M + k];
+
+    double o = 0.0;
+    float gl[M];
+    int cnt[M];
+#pragma unroll
+    for (int k = 0; k < M; ++k) { gl[k] = 0.f; cnt[k] = 0; }
+    if (valid) {
         for (int64_t a = lane; a < d; a += 64) {
-            const int code = pj[a];
-            const float v = vj[a];
+            const int code = P[j * d + a];
+            const float r = R[j * d + a];
+            float ck = cv[0];
 #pragma unroll
-            for (int k = 0; k < MAX_M; ++k) {
-                bacc[k] += (code == k) ? v : 0.f;
-                cnt[k] += (code == k) ? 1 : 0;
-            }
-        }
+            for (int k = 1; k < M; ++k) ck = (code == k) ? cv[k] : ck;
+            const float e = ck - load_elem<WBF16>(W, j * d + a);
+            o += (double)e * (double)r;
+            if (SOLVE) {
 #pragma unroll
-        for (int k = 0; k < MAX_M; ++k) {
-            if (k < m) {
-                const double sum = wave_sum_f64((double)bacc[k]);
-                int c = cnt[k];
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-                if (lane == 0) { sb[wave][k] = sum; scnt[wave][k] = c; }
-            }
-        }
-        // A[:, q] = P^T U[:, q]
-        for (int q = 0; q < m; ++q) {
-            float aacc[MAX_M];
-#pragma unroll
-            for (int k = 0; k < MAX_M; ++k) aacc[k] = 0.f;
-            const float* Uq = Uj + (size_t)q * d;
-            for (int64_t a = lane; a < d; a += 64) {
-                const int code = pj[a];
-                const float u = Uq[a];
-#pragma unroll
-                for (int k = 0; k < MAX_M; ++k) aacc[k] += (code == k) ? u : 0.f;
-            }
-#pragma unroll
-            for (int k = 0; k < MAX_M; ++k) {
-                if (k < m) {
-                    const double sum = wave_sum_f64((double)aacc[k]);
-                    if (lane == 0) sA[wave][k][q] = sum;
+                for (int k = 0; k < M; ++k) {
+                    gl[k] += (code == k) ? r : 0.f;
+                    cnt[k] += (code == k) ? 1 : 0;
                 }
             }
         }
     }
+    o = wave_sum_f64(o);
+    if (valid && lane == 0 && obj) obj[j] = o;
+    if (!SOLVE) return;
+
+#pragma unroll
+    for (int k = 0; k < M; ++k) {
+        const double s = wave_sum_f64((double)gl[k]);
+        int c = cnt[k];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+        if (lane == 0) { sg[wave][k] = s; scnt[wave][k] = c; }
+    }
+    // B_j[q'][q] = sum over a-tiles of part[ta][(j M + q) M + q'], stored as sB[q][q']
+    if (valid) {
+        for (int e = lane; e < M * M; e += 64) {
+            const int q = e / M, qp = e - q * M;
+            double s = 0.0;
+            for (int ta = 0; ta < ntile_a; ++ta)
+                s += (double)part[((size_t)ta * d_out * M + (size_t)(j * M + q)) * M + qp];
+            sB[wave][q][qp] = s;
+        }
+    }
     __syncthreads();
-    if (MODE == 0 && valid && lane == 0) {
-        // float64 Cholesky of the symmetric part of A on the non-empty codes
+    if (valid && lane == 0) {
         int ns = 0;
-        for (int k = 0; k < m; ++k)
+        for (int k = 0; k < M; ++k)
             if (scnt[wave][k] > 0) sidx[wave][ns++] = k;
         bool ok = true;
+        // A[q'][q] = B[q'][q] + B[q][q'] = sB[q][q'] + sB[q'][q]
         for (int r = 0; r < ns && ok; ++r) {
             for (int c = 0; c <= r; ++c) {
                 const int ir = sidx[wave][r], ic = sidx[wave][c];
-                double sum = 0.5 * (sA[wave][ir][ic] + sA[wave][ic][ir]);
+                double sum = sB[wave][ir][ic] + sB[wave][ic][ir];
                 for (int k = 0; k < c; ++k) sum -= sL[wave][r][k] * sL[wave][c][k];
                 if (r == c) {
                     if (!(sum > 0.0)) { ok = false; break; }
@@ -438,90 +291,59 @@ __global__ __launch_bounds__(256) void k_solve(
                 }
             }
         }
-        for (int k = 0; k < m; ++k) sc_new[wave][k] = sc_old[wave][k];
         if (ok) {
             for (int r = 0; r < ns; ++r) {
-                double sum = sb[wave][sidx[wave][r]];
+                double sum = -sg[wave][sidx[wave][r]];
                 for (int k = 0; k < r; ++k) sum -= sL[wave][r][k] * sy[wave][k];
                 sy[wave][r] = sum / sL[wave][r][r];
             }
             for (int r = ns - 1; r >= 0; --r) {
                 double sum = sy[wave][r];
                 for (int k = r + 1; k < ns; ++k) sum -= sL[wave][k][r] * sy[wave][k];
-                sy[wave][r] = sum / sL[wave][r][r];     // x overwrites y from the back
+                sy[wave][r] = sum / sL[wave][r][r];
             }
-            for (int r = 0; r < ns; ++r) sc_new[wave][sidx[wave][r]] = (float)sy[wave][r];
+            for (int r = 0; r < ns; ++r) {
+                const int k = sidx[wave][r];
+                C[j * M + k] = (float)((double)C[j * M + k] + sy[wave][r]);
+            }
         } else if (n_not_pd) {
             atomicAdd(n_not_pd, 1ull);
         }
-    }
-    if (MODE == 1 && lane < m) sc_new[wave][lane] = sc_old[wave][lane];
-    __syncthreads();
-    if (!valid) return;
-    if (MODE == 0 && lane < m) C[j * m + lane] = sc_new[wave][lane];
-
-    double o_old = 0.0, o_new = 0.0;
-    float cn[MAX_M], co[MAX_M];
-#pragma unroll
-    for (int k = 0; k < MAX_M; ++k) {
-        cn[k] = (k < m) ? sc_new[wave][k] : 0.f;
-        co[k] = (k < m) ? sc_old[wave][k] : 0.f;
-    }
-    for (int64_t a = lane; a < d; a += 64) {
-        float rn = 0.f, ro = 0.f;
-#pragma unroll
-        for (int k = 0; k < MAX_M; ++k) {
-            if (k < m) {
-                const float u = Uj[(size_t)k * d + a];
-                rn = fmaf(cn[k], u, rn);
-                ro = fmaf(co[k], u, ro);
-            }
-        }
-        const float v = vj[a];
-        rn -= v;
-        ro -= v;
-        const int code = pj[a];
-        const double w = (double)load_elem<BF16>(W, j * d + a);
-        const double en = (double)sc_new[wave][code] - w;
-        const double eo = (double)sc_old[wave][code] - w;
-        o_new += en * (double)rn;
-        o_old += eo * (double)ro;
-        if (R) R[j * d + a] = rn;
-    }
-    o_new = wave_sum_f64(o_new);
-    o_old = wave_sum_f64(o_old);
-    if (lane == 0) {
-        if (obj_new) obj_new[j] = o_new;
-        if (obj_old) obj_old[j] = o_old;
     }
 }
 
 // ---------------------------------------------------------------------------
 // k_sweep: the assignment pass.  One block = 16 rows of one group, one row per
-// wave (16 waves).  Coordinates are visited in ascending order in sub-blocks of
-// 64, one coordinate per lane.
-//   * Deferred update: once per B-block, the effect of every earlier move of
-//     this pass on the block's residuals is gathered left-looking on the matrix
-//     cores, corr = D[rows, 0:bB] F'[0:bB, B-block] with v_mfma_f32_16x16x32_bf16
-//     and three products of the bf16 hi/lo planes (D hi.F hi + D hi.F lo +
-//     D lo.F hi); 16 waves split it into NCT column tiles x NSL k-slices whose
-//     partials are summed in a fixed order.  32-coordinate chunks in which no
-//     row of the block moved are skipped.  Inside a B-block, each later 64-wide
-//     sub-block gets the same correction from the block's earlier sub-blocks.
-//   * Chain (per wave, per sub-block): for coordinate t the residual, current
-//     value and damped diagonal are read from lane t (v_readlane); lanes
-//     0..m-1 each evaluate one candidate change
+// wave (16 waves).  Coordinates are visited in ascending order in blocks of 64
+// (one coordinate per lane), grouped into super-blocks of 512.
+//   * Effect of earlier moves on later residuals, in two levels on the matrix
+//     cores (v_mfma_f32_16x16x32_bf16, three products of bf16 hi/lo planes,
+//     D hi.F hi + D hi.F lo + D lo.F hi, float32 accumulation):
+//       - inside a super-block, before each 64-block, left-looking from the
+//         super-block's earlier blocks, corr = D_sb[:, 0:o] F'[sb:sb+o, block],
+//         with D_sb (the value changes of the super-block) held in LDS;
+//       - at the end of a super-block, right-looking into the residual array,
+//         R[:, later] += D_sb F'[sb, later], streaming long contiguous panels
+//         of F' (each residual element is owned by one wave; no atomics).
+//     32-coordinate chunks in which no row of the block moved are skipped.
+//   * Chain (per wave): for coordinate t the residual, current value and damped
+//     diagonal are read from lane t (v_readlane); lanes 0..m-1 each evaluate one
+//     candidate change
 //         Delta_q = delta_q (F'_tt delta_q + 2 r_t),  delta_q = c_q - w_hat_t,
-//     a 16-lane DPP min gives the best change, a ballot + find-first-set gives
-//     the lowest index attaining it, and a strict decrease applies
-//     r += delta F'[t, sub-block] in registers (F' column of the sub-block held
-//     in 64 registers per lane, staged once through LDS for the 16 rows).
-//   * The codes and the value changes (bf16 hi + lo) are written back.
+//     a 16-lane DPP minimum on an order-preserving integer key gives the best
+//     change, a ballot + find-first-set the lowest index attaining it, and a
+//     strict decrease applies r += delta F'[t, block] in registers (the F'
+//     columns of the block are staged once through LDS for the 16 rows).
+//   * The row objective e.r at the start of the pass is summed (float64) before
+//     any update; the objective after it adds the accepted changes.
+//   The residual array R is updated in place (it is workspace).
 // ---------------------------------------------------------------------------
 constexpr int SW_ROWS = 16;     // rows (= waves) per block
-constexpr int SW_SUB = 64;      // chain sub-block (one coordinate per lane)
-constexpr int SW_PF = 2;        // k-chunks in flight per wave in the deferred update
+constexpr int SW_SUB = 64;      // coordinates per chain block (one per lane)
+constexpr int SW_SB = 512;      // coordinates per super-block
+constexpr int SW_DP = SW_SB + 8;  // bf16 pitch of the LDS rows of D_sb
 constexpr int SW_SEG = 8;       // chain steps unrolled per F' column preload
+constexpr int SW_RB = 4;        // F' chunks in flight per wave in the right-looking update
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_mov_i(int v) {
@@ -550,59 +372,20 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// acc += D[arow, kk..kk+7] . F'[ncol, kk..kk+7] over the 32-wide k-chunks
-// k_first, k_first + kstride, ... < k_end; chunks whose flag is 0 are skipped
-// (the flag is block-uniform).  Rows past the group's end read a valid row's D:
-// their outputs are never used.
-__device__ __forceinline__ void sweep_corr(f32x4& acc, const uint16_t* __restrict__ Dh,
-                                           const uint16_t* __restrict__ Dl,
-                                           const uint16_t* __restrict__ Fh,
-                                           const uint16_t* __restrict__ Fl,
-                                           int64_t k_first, int64_t k_end, int64_t kstride,
-                                           const uint32_t* flags, int lane) {
-    const int ko = 8 * (lane >> 4);
-    for (int64_t k0 = k_first; k0 < k_end; k0 += SW_PF * kstride) {
-        u32x4 dh[SW_PF], dl[SW_PF], fh[SW_PF], fl[SW_PF];
-        bool on[SW_PF];
-#pragma unroll
-        for (int u = 0; u < SW_PF; ++u) {
-            const int64_t kc = k0 + u * kstride;
-            on[u] = kc < k_end && __builtin_amdgcn_readfirstlane((int)flags[kc >> 5]) != 0;
-            if (on[u]) {
-                dh[u] = *(const u32x4*)(Dh + kc + ko);
-                dl[u] = *(const u32x4*)(Dl + kc + ko);
-                fh[u] = *(const u32x4*)(Fh + kc + ko);
-                fl[u] = *(const u32x4*)(Fl + kc + ko);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < SW_PF; ++u) {
-            if (on[u]) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh[u]), as_bf16x8(fh[u]), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh[u]), as_bf16x8(fl[u]), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dl[u]), as_bf16x8(fh[u]), acc, 0, 0, 0);
-            }
-        }
-    }
-}
-
-template <int B>
+template <bool WBF16>
 __global__ __launch_bounds__(1024, 1) void k_sweep(
     const float* __restrict__ F, const float* __restrict__ dF,
     const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo,
     int64_t d, int64_t rows_per_group, int wgs_per_group, int total_wgs,
-    const float* __restrict__ C, int m, uint8_t* __restrict__ P,
-    const float* __restrict__ R, uint16_t* __restrict__ Dhi, uint16_t* __restrict__ Dlo,
-    const double* __restrict__ obj_in, double* __restrict__ obj_out,
+    const float* __restrict__ C, int m, uint8_t* __restrict__ P, const void* __restrict__ W,
+    float* __restrict__ R, double* __restrict__ obj_start, double* __restrict__ obj_end,
     unsigned long long* __restrict__ n_changed) {
-    constexpr int NCT = B / 16;          // 16-column tiles of a B-block
-    constexpr int NSL = 256 / B;         // k-slices of the B-block correction
-    constexpr int NSUB = B / SW_SUB;     // 64-wide sub-blocks per B-block
-    __shared__ float corr_b[NSL][SW_ROWS][B];          // 16 KB
-    __shared__ float corr_s[4][SW_ROWS][SW_SUB];       // 16 KB
-    __shared__ __attribute__((aligned(16))) float fdb[SW_SUB][SW_SUB];   // 16 KB
-    __shared__ float fdd[SW_SUB];                      // diag(F') of the sub-block
-    extern __shared__ uint32_t sweep_flags[];          // [d / 32]
+    __shared__ __attribute__((aligned(16))) uint16_t dsb_hi[SW_ROWS][SW_DP];   // 16.3 KB
+    __shared__ __attribute__((aligned(16))) uint16_t dsb_lo[SW_ROWS][SW_DP];   // 16.3 KB
+    __shared__ float corr_p[4][SW_ROWS][SW_SUB];                               // 16 KB
+    __shared__ __attribute__((aligned(16))) float fdb[SW_SUB][SW_SUB];         // 16 KB
+    __shared__ float fdd[SW_SUB];                      // diag(F') of the block
+    __shared__ uint32_t chunk_moved[SW_SB / 32];       // a move in a 32-chunk of the super-block
 
     // XCD-aware order: hardware block h runs on XCD h % 8; consecutive logical
     // blocks (the rows of one group) go to the same XCD and share F' in its L2.
@@ -617,66 +400,73 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
     const int64_t jl = local + wave;
     const bool rvalid = jl < rows_per_group;
     const int64_t j = (int64_t)g * rows_per_group + (rvalid ? jl : 0);
+    const int64_t row0 = (int64_t)g * rows_per_group + local;      // first row of the block
+    const int nrows = (int)((rows_per_group - local) < SW_ROWS ? (rows_per_group - local) : SW_ROWS);
 
     const float* Fg = F + (size_t)g * d * d;
     const float* dFg = dF + (size_t)g * d;
     const uint16_t* Fh = Fhi + (size_t)g * d * d;
     const uint16_t* Fl = Flo + (size_t)g * d * d;
 
-    for (int i = tid; i < (int)(d / 32); i += 1024) sweep_flags[i] = 0u;
-
     const float cl = (lane < m && rvalid) ? C[j * m + lane] : 0.f;   // candidate of this lane
-    double dsum = 0.0;
+    double dsum = 0.0;       // sum of the accepted changes (uniform in the wave)
     unsigned moves = 0;
 
-    // operand rows of the correction products: the block's 16 rows
-    const int64_t arow_l = local + (lane & 15);
-    const bool arow_ok = arow_l < rows_per_group;
-    const int64_t arow = (int64_t)g * rows_per_group + (arow_ok ? arow_l : 0);
-    const uint16_t* Dh_row = Dhi + arow * d;
-    const uint16_t* Dl_row = Dlo + arow * d;
-    __syncthreads();
-
-    for (int64_t bB = 0; bB < d; bB += B) {
-        // ---- deferred update of the B-block from all earlier B-blocks
-        {
-            const int ct = wave % NCT, sl = wave / NCT;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int64_t ncol = bB + ct * 16 + (lane & 15);
-            sweep_corr(acc, Dh_row, Dl_row, Fh + ncol * d, Fl + ncol * d, (int64_t)sl * 32, bB,
-                       (int64_t)32 * NSL, sweep_flags, lane);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) corr_b[sl][4 * (lane >> 4) + t][ct * 16 + (lane & 15)] = acc[t];
+    // objective at the start of the pass, before R is updated
+    double ostart = 0.0;
+    if (rvalid) {
+        for (int64_t col = lane; col < d; col += 64) {
+            const float wv = load_elem<WBF16>(W, j * d + col);
+            const float cv = __shfl(cl, (int)P[j * d + col], 64);
+            ostart += (double)(cv - wv) * (double)R[j * d + col];
         }
-        for (int s = 0; s < NSUB; ++s) {
-            const int64_t bs = bB + (int64_t)s * SW_SUB;
+    }
+    ostart = wave_sum_f64(ostart);
+
+    const int ko = 8 * (lane >> 4);      // k offset of this lane in a 32-wide MFMA step
+    const int mrow = lane & 15;          // A-operand row / B-operand column of this lane
+
+    for (int64_t sb0 = 0; sb0 < d; sb0 += SW_SB) {
+        const int sblen = (int)((d - sb0) < SW_SB ? (d - sb0) : SW_SB);
+        if (tid < SW_SB / 32) chunk_moved[tid] = 0u;
+        __syncthreads();
+        for (int o = 0; o < sblen; o += SW_SUB) {
+            const int64_t bs = sb0 + o;
+            // ---- left-looking correction from this super-block's earlier blocks:
+            // 4 column tiles x 4 k-slices of 32-chunks
+            {
+                const int ct = wave & 3, sl = wave >> 2;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                const int64_t fcol = bs + ct * 16 + mrow;
+                const uint16_t* Fh_c = Fh + fcol * d + sb0 + ko;
+                const uint16_t* Fl_c = Fl + fcol * d + sb0 + ko;
+                for (int c = sl; c < o / 32; c += 4) {
+                    if (__builtin_amdgcn_readfirstlane((int)chunk_moved[c]) == 0) continue;
+                    const u32x4 fh = *(const u32x4*)(Fh_c + c * 32);
+                    const u32x4 fl = *(const u32x4*)(Fl_c + c * 32);
+                    const u32x4 dh = *(const u32x4*)(&dsb_hi[mrow][c * 32 + ko]);
+                    const u32x4 dl = *(const u32x4*)(&dsb_lo[mrow][c * 32 + ko]);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fh), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fl), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dl), as_bf16x8(fh), acc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) corr_p[sl][4 * (lane >> 4) + t][ct * 16 + mrow] = acc[t];
+            }
             // stage the diagonal 64 x 64 block of F (rows bs.., columns bs..)
             {
                 const int rr = tid >> 4, cc = (tid & 15) * 4;
                 *(float4*)&fdb[rr][cc] = *(const float4*)(Fg + (bs + rr) * d + bs + cc);
                 if (tid < SW_SUB) fdd[tid] = dFg[bs + tid];
             }
-            // in-block correction from this B-block's earlier sub-blocks
-            if (s > 0) {
-                const int ct = wave & 3, sl = wave >> 2;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                const int64_t ncol = bs + ct * 16 + (lane & 15);
-                sweep_corr(acc, Dh_row, Dl_row, Fh + ncol * d, Fl + ncol * d,
-                           bB + (int64_t)sl * 32, bs, 128, sweep_flags, lane);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) corr_s[sl][4 * (lane >> 4) + t][ct * 16 + (lane & 15)] = acc[t];
-            }
             __syncthreads();
 
+            float dv = 0.f;
             if (rvalid) {
                 const int64_t col = bs + lane;
                 float r = R[j * d + col];
 #pragma unroll
-                for (int k = 0; k < NSL; ++k) r += corr_b[k][wave][s * SW_SUB + lane];
-                if (s > 0) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) r += corr_s[k][wave][lane];
-                }
+                for (int k = 0; k < 4; ++k) r += corr_p[k][wave][lane];
                 int code = P[j * d + col];
                 float wh = __shfl(cl, code, 64);
                 const float wh0 = wh;
@@ -711,25 +501,70 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
                     }
                 }
                 P[j * d + col] = (uint8_t)code;
-                const float dv = wh - wh0;
-                const uint32_t hb = f32_to_bf16_bits(dv);
-                Dhi[j * d + col] = (uint16_t)hb;
-                Dlo[j * d + col] = (uint16_t)f32_to_bf16_bits(dv - __uint_as_float(hb << 16));
+                dv = wh - wh0;
                 const unsigned long long moved = __ballot(dv != 0.f);
                 if (lane == 0) {
-                    if (moved & 0xffffffffull) sweep_flags[bs >> 5] = 1u;
-                    if (moved >> 32) sweep_flags[(bs >> 5) + 1] = 1u;
+                    if (moved & 0xffffffffull) chunk_moved[o / 32] = 1u;
+                    if (moved >> 32) chunk_moved[o / 32 + 1] = 1u;
                 }
             }
+            const uint32_t hb = f32_to_bf16_bits(dv);
+            dsb_hi[wave][o + lane] = (uint16_t)hb;
+            dsb_lo[wave][o + lane] = (uint16_t)f32_to_bf16_bits(dv - __uint_as_float(hb << 16));
             __syncthreads();
         }
+        // ---- right-looking update of the later residuals of the block's rows:
+        // R[rows, sb_end:] += D_sb F'[sb0:sb_end, sb_end:], one 16-column tile per wave
+        const int64_t sb_end = sb0 + sblen;
+        const int ntiles = (int)((d - sb_end) / 16);
+        const int nch = sblen / 32;
+        uint32_t mv = 0u;                                  // moved chunks as a bit mask
+        for (int c = 0; c < nch; ++c) mv |= (chunk_moved[c] != 0u ? 1u : 0u) << c;
+        mv = __builtin_amdgcn_readfirstlane(mv);
+        for (int ctile = wave; ctile < ntiles; ctile += SW_ROWS) {
+            const int64_t fcol = sb_end + (int64_t)ctile * 16 + mrow;
+            const uint16_t* Fh_c = Fh + fcol * d + sb0 + ko;
+            const uint16_t* Fl_c = Fl + fcol * d + sb0 + ko;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int c0 = 0; c0 < nch; c0 += SW_RB) {
+                u32x4 fh[SW_RB], fl[SW_RB];
+#pragma unroll
+                for (int u = 0; u < SW_RB; ++u) {
+                    const int c = c0 + u;
+                    if (c < nch && ((mv >> c) & 1u)) {
+                        fh[u] = *(const u32x4*)(Fh_c + c * 32);
+                        fl[u] = *(const u32x4*)(Fl_c + c * 32);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < SW_RB; ++u) {
+                    const int c = c0 + u;
+                    if (c < nch && ((mv >> c) & 1u)) {
+                        const u32x4 dh = *(const u32x4*)(&dsb_hi[mrow][c * 32 + ko]);
+                        const u32x4 dl = *(const u32x4*)(&dsb_lo[mrow][c * 32 + ko]);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fh[u]), acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fl[u]), acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dl), as_bf16x8(fh[u]), acc, 0, 0, 0);
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int rr = 4 * (lane >> 4) + t;
+                if (rr < nrows) {
+                    float* dst = R + (row0 + rr) * d + sb_end + (int64_t)ctile * 16 + mrow;
+                    *dst += acc[t];
+                }
+            }
+        }
+        __syncthreads();
     }
     if (rvalid && lane == 0) {
-        obj_out[j] = obj_in[j] + dsum;
+        if (obj_start) obj_start[j] = ostart;
+        if (obj_end) obj_end[j] = ostart + dsum;
         if (n_changed) atomicAdd(n_changed, (unsigned long long)moves);
     }
 }
-
 
 // float64 sums of consecutive rows in a fixed order: out[0] = sum_j x[j]
 __global__ __launch_bounds__(256) void k_reduce_rows(const double* __restrict__ x, int64_t n,
@@ -764,34 +599,22 @@ __global__ void k_zero_u64(unsigned long long* __restrict__ p, int n) {
 // ===========================================================================
 // Host launchers
 // ===========================================================================
-#include "gq_internal.h"
-
 namespace gq {
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-LnqSizes lnq_sizes(int64_t d_out, int64_t d, int groups, int m, bool w_f32) {
+LnqSizes lnq_sizes(int64_t d_out, int64_t d, int groups, int m) {
     LnqSizes z{};
-    const int64_t rpg = d_out / groups;
-    const size_t u_group = (size_t)rpg * m * d * sizeof(float);
-    const size_t u_budget = (size_t)4 << 30;
-    int gchunk = (int)(u_budget / (u_group ? u_group : 1));
-    if (gchunk < 1) gchunk = 1;
-    if (gchunk > groups) gchunk = groups;
-    z.gchunk = gchunk;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     z.o_fhi = take((size_t)groups * d * d * 2);
     z.o_flo = take((size_t)groups * d * d * 2);
     z.o_dF = take((size_t)groups * d * 4);
     z.o_lam = take((size_t)groups * 8);
-    z.o_V = take((size_t)d_out * d * 4);
-    z.o_U = take(u_group * gchunk);
     z.o_R = take((size_t)d_out * d * 4);
-    z.o_dhi = take((size_t)d_out * d * 2);
-    z.o_dlo = take((size_t)d_out * d * 2);
-    z.o_whi = w_f32 ? take((size_t)d_out * d * 2) : 0;
-    z.o_wlo = w_f32 ? take((size_t)d_out * d * 2) : 0;
+    z.o_ehi = take((size_t)d_out * d * 2);
+    z.o_elo = take((size_t)d_out * d * 2);
+    z.o_part = take(lnq_gram_partial_floats(d_out, d, m) * 4);
     z.o_objA = take((size_t)d_out * 8);
     z.o_objB = take((size_t)d_out * 8);
     z.o_objC = take((size_t)d_out * 8);
@@ -800,25 +623,21 @@ LnqSizes lnq_sizes(int64_t d_out, int64_t d, int groups, int m, bool w_f32) {
     return z;
 }
 
-LnqWs lnq_carve(void* base, const LnqSizes& z, bool w_f32) {
+LnqWs lnq_carve(void* base, const LnqSizes& z) {
     char* b = (char*)base;
     LnqWs w{};
     w.fhi = (uint16_t*)(b + z.o_fhi);
     w.flo = (uint16_t*)(b + z.o_flo);
     w.dF = (float*)(b + z.o_dF);
     w.lam = (double*)(b + z.o_lam);
-    w.V = (float*)(b + z.o_V);
-    w.U = (float*)(b + z.o_U);
     w.R = (float*)(b + z.o_R);
-    w.dhi = (uint16_t*)(b + z.o_dhi);
-    w.dlo = (uint16_t*)(b + z.o_dlo);
-    w.whi = w_f32 ? (uint16_t*)(b + z.o_whi) : nullptr;
-    w.wlo = w_f32 ? (uint16_t*)(b + z.o_wlo) : nullptr;
+    w.ehi = (uint16_t*)(b + z.o_ehi);
+    w.elo = (uint16_t*)(b + z.o_elo);
+    w.part = (float*)(b + z.o_part);
     w.objA = (double*)(b + z.o_objA);
     w.objB = (double*)(b + z.o_objB);
     w.objC = (double*)(b + z.o_objC);
     w.cnt = (unsigned long long*)(b + z.o_cnt);
-    w.gchunk = z.gchunk;
     return w;
 }
 
@@ -832,42 +651,6 @@ hipError_t lnq_prepare(const float* F, int groups, int64_t d, double rho, const 
                        w.lam, w.fhi, w.flo, w.dF, total8);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
-}
-
-template <bool ONEHOT, int NPB>
-static hipError_t launch_fgemm(const uint16_t* A, const uint8_t* codes, int m, int64_t rpg,
-                               int g_first, int g_count, const LnqWs& w, int64_t d,
-                               int accumulate, float* out, hipStream_t st) {
-    const int64_t N = ONEHOT ? rpg * m : rpg;
-    const int ntn = (int)((N + GT - 1) / GT);
-    const int nta = (int)((d + GT - 1) / GT);
-    const size_t lds = (size_t)2 * G_PLANE * (1 + NPB) * sizeof(uint16_t);
-    hipError_t e = hipFuncSetAttribute((const void*)k_fgemm<ONEHOT, NPB>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    const unsigned nblocks = (unsigned)ntn * nta * g_count;
-    StageTimer tm(ONEHOT ? ST_LNQ_U : ST_LNQ_WF, st);
-    hipLaunchKernelGGL((k_fgemm<ONEHOT, NPB>), dim3(nblocks), dim3(256), lds, st, A, codes, m,
-                       rpg, g_first, w.fhi, w.flo, d, ntn, nta, accumulate, out);
-    GQ_LAUNCH_CHECK();
-    return hipSuccess;
-}
-
-hipError_t lnq_compute_v(const void* W, bool w_bf16, int64_t d_out, int64_t d, int groups,
-                         const LnqWs& w, hipStream_t st) {
-    const int64_t rpg = d_out / groups;
-    if (w_bf16) {
-        return launch_fgemm<false, 2>((const uint16_t*)W, nullptr, 1, rpg, 0, groups, w, d, 0,
-                                      w.V, st);
-    }
-    const int64_t total8 = d_out * d / 8;
-    StageTimer tm(ST_LNQ_WF, st);
-    hipLaunchKernelGGL(k_split_rows, dim3((unsigned)((total8 + 255) / 256)), dim3(256), 0, st,
-                       (const float*)W, w.whi, w.wlo, total8);
-    GQ_LAUNCH_CHECK();
-    hipError_t e = launch_fgemm<false, 2>(w.whi, nullptr, 1, rpg, 0, groups, w, d, 0, w.V, st);
-    if (e != hipSuccess) return e;
-    return launch_fgemm<false, 1>(w.wlo, nullptr, 1, rpg, 0, groups, w, d, 1, w.V, st);
 }
 
 hipError_t lnq_init_run(const void* W, bool w_bf16, int64_t d_out, int64_t d, int m, float* C,
@@ -893,66 +676,94 @@ hipError_t lnq_init_run(const void* W, bool w_bf16, int64_t d_out, int64_t d, in
     return hipSuccess;
 }
 
-hipError_t lnq_u_solve(int mode, const void* W, bool w_bf16, int64_t d_out, int64_t d,
-                       int groups, int m, const uint8_t* P, float* C, const LnqWs& w, float* R,
-                       double* obj_old, double* obj_new, unsigned long long* n_not_pd,
-                       hipStream_t st) {
-    const int64_t rpg = d_out / groups;
-    for (int g0 = 0; g0 < groups; g0 += w.gchunk) {
-        const int gc = (g0 + w.gchunk <= groups) ? w.gchunk : groups - g0;
-        hipError_t e = launch_fgemm<true, 2>(nullptr, P, m, rpg, g0, gc, w, d, 0, w.U, st);
-        if (e != hipSuccess) return e;
-        const int64_t jf = (int64_t)g0 * rpg, jc = (int64_t)gc * rpg;
-        const dim3 grid((unsigned)((jc + 3) / 4));
-        StageTimer tm(ST_LNQ_SOLVE, st);
-        if (w_bf16) {
-            if (mode == 0)
-                hipLaunchKernelGGL((k_solve<true, 0>), grid, dim3(256), 0, st, w.U, jf, jc, w.V, P,
-                                   W, C, m, d, R, obj_old, obj_new, n_not_pd);
-            else
-                hipLaunchKernelGGL((k_solve<true, 1>), grid, dim3(256), 0, st, w.U, jf, jc, w.V, P,
-                                   W, C, m, d, R, obj_old, obj_new, n_not_pd);
-        } else {
-            if (mode == 0)
-                hipLaunchKernelGGL((k_solve<false, 0>), grid, dim3(256), 0, st, w.U, jf, jc, w.V,
-                                   P, W, C, m, d, R, obj_old, obj_new, n_not_pd);
-            else
-                hipLaunchKernelGGL((k_solve<false, 1>), grid, dim3(256), 0, st, w.U, jf, jc, w.V,
-                                   P, W, C, m, d, R, obj_old, obj_new, n_not_pd);
-        }
+hipError_t lnq_residual_from(const float* C, int m, const uint8_t* P, const void* W, bool w_bf16,
+                             int64_t d_out, int64_t d, int groups, const LnqWs& w,
+                             hipStream_t st) {
+    {
+        StageTimer tm(ST_LNQ_RESID, st);
+        const int64_t total8 = d_out * d / 8;
+        const dim3 grid((unsigned)((total8 + 255) / 256));
+        if (w_bf16)
+            hipLaunchKernelGGL(k_err_split<true>, grid, dim3(256), 0, st, C, m, P, W, d, w.ehi,
+                               w.elo, total8);
+        else
+            hipLaunchKernelGGL(k_err_split<false>, grid, dim3(256), 0, st, C, m, P, W, d, w.ehi,
+                               w.elo, total8);
         GQ_LAUNCH_CHECK();
     }
-    return hipSuccess;
+    return lnq_residual(w.ehi, w.elo, d_out, d, groups, w.fhi, w.flo, w.R, st);
 }
 
-template <int B>
-static hipError_t launch_sweep(const float* F, int64_t d_out, int64_t d, int groups,
-                               const float* C, int m, uint8_t* P, const LnqWs& w,
-                               const double* obj_in, double* obj_out,
-                               unsigned long long* counter, hipStream_t st) {
-    const int64_t rpg = d_out / groups;
-    const int wgs = (int)((rpg + SW_ROWS - 1) / SW_ROWS);
-    const int total = wgs * groups;
-    const int grid = (total + 7) / 8 * 8;          // the XCD remap needs a multiple of 8
-    const size_t lds = (size_t)(d / 32) * sizeof(uint32_t);
-    StageTimer tm(ST_LNQ_SWEEP, st);
-    hipLaunchKernelGGL(k_sweep<B>, dim3((unsigned)grid), dim3(1024), lds, st, F, w.dF, w.fhi,
-                       w.flo, d, rpg, wgs, total, C, m, P, w.R, w.dhi, w.dlo, obj_in, obj_out,
-                       counter);
+template <int M, bool WB, bool SOLVE>
+static hipError_t launch_solve(const float* part, int nta, const float* R, const uint8_t* P,
+                               const void* W, float* C, int64_t d, int64_t d_out, double* obj,
+                               unsigned long long* n_not_pd, hipStream_t st) {
+    hipLaunchKernelGGL((k_solve<M, WB, SOLVE>), dim3((unsigned)((d_out + 3) / 4)), dim3(256), 0,
+                       st, part, nta, R, P, W, C, d, d_out, obj, n_not_pd);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }
 
-hipError_t lnq_sweep_run(int block, const float* F, int64_t d_out, int64_t d, int groups,
-                         const float* C, int m, uint8_t* P, const LnqWs& w,
-                         const double* obj_in, double* obj_out, unsigned long long* counter,
-                         hipStream_t st) {
-    switch (block) {
-        case 64: return launch_sweep<64>(F, d_out, d, groups, C, m, P, w, obj_in, obj_out, counter, st);
-        case 128: return launch_sweep<128>(F, d_out, d, groups, C, m, P, w, obj_in, obj_out, counter, st);
-        case 256: return launch_sweep<256>(F, d_out, d, groups, C, m, P, w, obj_in, obj_out, counter, st);
+template <bool WB, bool SOLVE>
+static hipError_t solve_m(int m, const float* part, int nta, const float* R, const uint8_t* P,
+                          const void* W, float* C, int64_t d, int64_t d_out, double* obj,
+                          unsigned long long* n_not_pd, hipStream_t st) {
+    switch (m) {
+        case 2: return launch_solve<2, WB, SOLVE>(part, nta, R, P, W, C, d, d_out, obj, n_not_pd, st);
+        case 4: return launch_solve<4, WB, SOLVE>(part, nta, R, P, W, C, d, d_out, obj, n_not_pd, st);
+        case 8: return launch_solve<8, WB, SOLVE>(part, nta, R, P, W, C, d, d_out, obj, n_not_pd, st);
+        case 16: return launch_solve<16, WB, SOLVE>(part, nta, R, P, W, C, d, d_out, obj, n_not_pd, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t lnq_codebook_step(const void* W, bool w_bf16, int64_t d_out, int64_t d, int groups,
+                             int m, const uint8_t* P, float* C, const LnqWs& w, double* obj_before,
+                             unsigned long long* n_not_pd, hipStream_t st) {
+    hipError_t e = lnq_residual_from(C, m, P, W, w_bf16, d_out, d, groups, w, st);
+    if (e != hipSuccess) return e;
+    if ((e = lnq_gram(P, m, d_out, d, groups, w.fhi, w.flo, w.part, st)) != hipSuccess) return e;
+    const int nta = (int)((d + 255) / 256);
+    StageTimer tm(ST_LNQ_SOLVE, st);
+    return w_bf16 ? solve_m<true, true>(m, w.part, nta, w.R, P, W, C, d, d_out, obj_before, n_not_pd, st)
+                  : solve_m<false, true>(m, w.part, nta, w.R, P, W, C, d, d_out, obj_before, n_not_pd, st);
+}
+
+hipError_t lnq_objective_rows(const void* W, bool w_bf16, int64_t d_out, int64_t d, int groups,
+                              int m, const uint8_t* P, const float* C, const LnqWs& w,
+                              double* obj, hipStream_t st) {
+    hipError_t e = lnq_residual_from(C, m, P, W, w_bf16, d_out, d, groups, w, st);
+    if (e != hipSuccess) return e;
+    StageTimer tm(ST_LNQ_SOLVE, st);
+    return w_bf16 ? solve_m<true, false>(m, nullptr, 0, w.R, P, W, (float*)C, d, d_out, obj, nullptr, st)
+                  : solve_m<false, false>(m, nullptr, 0, w.R, P, W, (float*)C, d, d_out, obj, nullptr, st);
+}
+
+template <bool WB>
+static hipError_t launch_sweep(const float* F, const void* W, int64_t d_out, int64_t d,
+                               int groups, const float* C, int m, uint8_t* P, const LnqWs& w,
+                               double* obj_start, double* obj_end, unsigned long long* counter,
+                               hipStream_t st) {
+    const int64_t rpg = d_out / groups;
+    const int wgs = (int)((rpg + SW_ROWS - 1) / SW_ROWS);
+    const int total = wgs * groups;
+    const int grid = (total + 7) / 8 * 8;          // the XCD remap needs a multiple of 8
+    hipLaunchKernelGGL((k_sweep<WB>), dim3((unsigned)grid), dim3(1024), 0, st, F, w.dF, w.fhi,
+                       w.flo, d, rpg, wgs, total, C, m, P, W, w.R, obj_start, obj_end, counter);
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
+}
+
+hipError_t lnq_sweep_step(int block, const float* F, const void* W, bool w_bf16, int64_t d_out,
+                          int64_t d, int groups, const float* C, int m, uint8_t* P,
+                          const LnqWs& w, double* obj_start, double* obj_end,
+                          unsigned long long* counter, hipStream_t st) {
+    hipError_t e = lnq_residual_from(C, m, P, W, w_bf16, d_out, d, groups, w, st);
+    if (e != hipSuccess) return e;
+    if (block != SW_SUB) return hipErrorInvalidValue;
+    StageTimer tm(ST_LNQ_SWEEP, st);
+    return w_bf16 ? launch_sweep<true>(F, W, d_out, d, groups, C, m, P, w, obj_start, obj_end, counter, st)
+                  : launch_sweep<false>(F, W, d_out, d, groups, C, m, P, w, obj_start, obj_end, counter, st);
 }
 
 hipError_t lnq_reduce(const double* rows, int64_t n, double* out, hipStream_t st) {

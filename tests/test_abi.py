@@ -37,9 +37,9 @@ def test_options_default():
     o = gq.options()
     d = B.lnq_options()
     gq.library().gq_lnq_options_default(ctypes.byref(d))
-    assert (d.block, d.init, d.reserved) == (128, 0, 0)
+    assert (d.block, d.init, d.reserved) == (64, 0, 0)
     assert d.ridge_rel == pytest.approx(1e-6)
-    assert o.block == 128
+    assert o.block == 64
 
 
 def _err(lib):
@@ -83,9 +83,10 @@ def test_lnq_argument_errors():
     lib.gq_lnq_options_default(ctypes.byref(o))
     o.block = 96
     assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "block" in _err(lib)
-    o.block = 256
-    assert q(d_in=384, opt=ctypes.byref(o)) == B.GQ_ESHAPE
-    o.block, o.init = 128, 9
+    o.block = 128
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL
+    assert q(d_in=352) == B.GQ_ESHAPE          # multiple of 32, not of the 64-wide block
+    o.block, o.init = 64, 9
     assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL
     o.init, o.ridge_rel = 0, -1.0
     assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "ridge" in _err(lib)
@@ -113,6 +114,6 @@ def test_timing_read_empty():
     gq.gq_timing_enable(False)
     t = gq.gq_timing_read()
     assert set(t) == {"group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain",
-                      "lnq_prepare", "lnq_wf", "lnq_init", "lnq_u", "lnq_solve", "lnq_sweep",
+                      "lnq_prepare", "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep",
                       "lnq_small"}
     assert all(v == (0.0, 0) for v in t.values())

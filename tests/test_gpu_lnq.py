@@ -3,7 +3,10 @@
 Bars (per stage, from identical inputs; the oracle upcasts the GPU's own
 float32 F to float64 and damps it the same way):
   * objective: per row within 1e-4 relative (float32 residuals of a float64 sum);
-  * codebook: per row ||c_gpu - c_ref|| / ||c_ref|| <= 1e-4; empty codes bitwise;
+  * codebook: per row ||c_gpu - c_ref|| / ||c_ref|| <= 1e-4 from the states LNQ
+    visits; from random states relative to max(||c_ref||, ||c_ref - c_old||);
+    every row attains the oracle's minimum objective within 1e-7; empty codes
+    bitwise;
   * sweep: >= 99.9% identical codes, and every GPU decision valid under the
     teacher-forced replay: D(q_gpu) <= min(min_q D_q, 0) + 1e-5 |obj_row|;
   * end to end: final objective (evaluated by the oracle) within 1e-3 of the
@@ -82,26 +85,69 @@ def test_objective_parity(device, mid):
     assert abs(tot.item() - rows.sum()) <= 1e-12 * rows.sum()
 
 
-@pytest.mark.parametrize("bits,empty", [(3, 0), (3, 2), (2, 1), (4, 0), (1, 0)])
-def test_codebook_parity(device, mid, bits, empty):
-    rng = np.random.default_rng(bits * 10 + empty)
-    m = 1 << bits
-    P, C = _random_state(rng, MID.d_out, MID.d_in, m, empty=empty)
-    Cd = to_dev(C, device)
+def _codebook_gpu(device, prob, P, C, bits):
+    Cd = to_dev(np.ascontiguousarray(C, np.float32), device)
     npd = torch.zeros(1, dtype=torch.int64, device=device)
-    gq.lnq_codebook_update(mid.F, mid.W, to_dev(P, device), Cd, bits, RHO, n_not_pd=npd)
+    gq.lnq_codebook_update(prob.F, prob.W, to_dev(np.ascontiguousarray(P, np.uint8), device), Cd,
+                           bits, RHO, n_not_pd=npd)
     torch.cuda.synchronize()
-    got = f64(Cd)
     assert npd.item() == 0
+    return f64(Cd)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_parity_lnq_states(device, mid, bits):
+    """Codebook step from the states LNQ visits: the quantile init of every row, and
+    for every fourth row the state after two oracle iterations.  Bar: 1e-4 relative."""
+    m = 1 << bits
+    C = np.empty((MID.d_out, m), np.float32)
+    P = np.empty((MID.d_out, MID.d_in), np.uint8)
+    for j in range(MID.d_out):
+        if j % 4 == 0:
+            c, p, _ = O.lnq_row(mid.Fp_row(j), mid.w[j], m, 2)
+        else:
+            c, p = O.init_quantile(mid.w[j], m)
+        C[j], P[j] = c.astype(np.float32), p
+    got = _codebook_gpu(device, mid, P, C, bits)
     worst = 0.0
     for j in range(MID.d_out):
         ref = O.codebook_update(mid.Fp_row(j), mid.w[j], P[j], C[j].astype(np.float64))
-        err = np.linalg.norm(got[j] - ref) / np.linalg.norm(ref)
-        worst = max(worst, err)
-        if empty:
-            np.testing.assert_array_equal(got[j][m - empty:], C[j][m - empty:].astype(np.float64))
-    print("max codebook rel error", worst)
+        worst = max(worst, np.linalg.norm(got[j] - ref) / np.linalg.norm(ref))
+    print("max codebook rel error (LNQ states)", worst)
     assert worst <= 1e-4
+
+
+@pytest.mark.parametrize("bits,empty", [(3, 0), (3, 2), (2, 1), (4, 0), (1, 0)])
+def test_codebook_parity_random_states(device, mid, bits, empty):
+    """Codebook step from random (c, P), some codes left empty.
+
+    From a random state the step c_ref - c_old can be many times larger than
+    c_ref itself (random codes give clusters with nearly equal means), and the
+    rounding error of any evaluation at the start state scales with that step.
+    Bars: empty codes bitwise; ||c_gpu - c_ref|| <= 1e-4 max(||c_ref||,
+    ||c_ref - c_old||) per row; on every row the objective at the GPU codebook
+    within 1e-7 relative of the oracle's minimum (the step's defining property).
+    """
+    rng = np.random.default_rng(bits * 10 + empty)
+    m = 1 << bits
+    P, C = _random_state(rng, MID.d_out, MID.d_in, m, empty=empty)
+    got = _codebook_gpu(device, mid, P, C, bits)
+    worst = worst_obj = 0.0
+    for j in range(MID.d_out):
+        Fp = mid.Fp_row(j)
+        c_old = C[j].astype(np.float64)
+        ref = O.codebook_update(Fp, mid.w[j], P[j], c_old)
+        if empty:
+            np.testing.assert_array_equal(got[j][m - empty:], c_old[m - empty:])
+        scale = max(np.linalg.norm(ref), np.linalg.norm(ref - c_old))
+        worst = max(worst, np.linalg.norm(got[j] - ref) / scale)
+        o_ref = O.objective(Fp, mid.w[j], ref, P[j])
+        o_gpu = O.objective(Fp, mid.w[j], got[j], P[j])
+        worst_obj = max(worst_obj, (o_gpu - o_ref) / o_ref)
+    print(f"random states: max step-relative error {worst:.2e}, max objective excess "
+          f"{worst_obj:.2e}")
+    assert worst <= 1e-4
+    assert worst_obj <= 1e-7
 
 
 def _sweep_check(prob, C, P0, P1, tol=1e-5, frac=0.999):
@@ -120,9 +166,10 @@ def _sweep_check(prob, C, P0, P1, tol=1e-5, frac=0.999):
     return P_ref
 
 
-@pytest.mark.parametrize("block", [64, 128, 256])
-def test_sweep_parity(device, mid, block):
-    rng = np.random.default_rng(block)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_sweep_parity(device, mid, seed):
+    rng = np.random.default_rng(100 + seed)
+    block = 64
     m = 8
     P0, C = _random_state(rng, MID.d_out, MID.d_in, m)
     Pd = to_dev(P0, device)
@@ -146,12 +193,12 @@ def test_sweep_from_codebook_state(device, mid):
         C[j] = c.astype(np.float32)
         P0[j] = p
     Pd = to_dev(P0, device)
-    gq.lnq_assign_sweep(mid.F, mid.W, to_dev(C, device), Pd, 3, RHO, block=128)
+    gq.lnq_assign_sweep(mid.F, mid.W, to_dev(C, device), Pd, 3, RHO, block=64)
     torch.cuda.synchronize()
     _sweep_check(mid, C, P0, Pd.cpu().numpy())
 
 
-def _end_to_end(device, prob, bits, iters, block, rows_checked=None, tol=1e-3):
+def _end_to_end(device, prob, bits, iters, block=64, rows_checked=None, tol=1e-3):
     wl = prob.wl
     m = 1 << bits
     C, P, tr, nch = gq.lnq_quantize(prob.W, prob.F, bits, iters, block=block, ridge_rel=RHO)
@@ -190,7 +237,7 @@ def test_lnq_init_matches_oracle(device, mid):
 
 
 def test_lnq_end_to_end_mid(device, mid):
-    _end_to_end(device, mid, 3, 5, 128)
+    _end_to_end(device, mid, 3, 5)
 
 
 def test_lnq_given_init_resumes_exactly(device, mid):
@@ -211,7 +258,7 @@ def test_lnq_deterministic(device, mid):
 
 @pytest.mark.parametrize("d_in,d_out,groups,bits,block", [
     (576, 200, 2, 2, 64),      # ragged matrix-core tiles, ragged 16-row sweep groups
-    (256, 48, 1, 4, 256),      # m = 16, block 256
+    (256, 48, 1, 4, 64),       # m = 16
     (1024, 64, 4, 1, 64),      # m = 2, four groups of 16 rows
 ])
 def test_lnq_end_to_end_shapes(device, d_in, d_out, groups, bits, block):
@@ -226,7 +273,7 @@ def test_lnq_tiny_workload_from_activations(device):
     inp = synth.make_inputs(wl, seed=0)
     X, G, W = (to_dev(inp[k], device) for k in ("X", "G", "W"))
     F = gq.gq_fisher_accumulate(X, G, 1)
-    C, P, tr, _ = gq.lnq_quantize(W, F, wl.bits, wl.iters, block=wl.block, ridge_rel=RHO)
+    C, P, tr, _ = gq.lnq_quantize(W, F, wl.bits, wl.iters, ridge_rel=RHO)
     torch.cuda.synchronize()
     assert np.all(tr.cpu().numpy()[1:] <= tr.cpu().numpy()[:-1] * (1 + 1e-6))
     Fref = O.damped(O.fisher(synth.decode(inp["X"]), synth.decode(inp["G"]), 1)[0], RHO)
@@ -242,7 +289,7 @@ def test_lnq_tiny_workload_from_activations(device):
 
 
 def test_lnq_llama2_7b_attn_full_size_sampled_rows(device):
-    """4096 x 4096, 4 groups, 3-bit, 10 iterations, block 128 (the benchmarked launch).
+    """4096 x 4096, 4 groups, 3-bit, 10 iterations (the benchmarked launch).
 
     Rows are independent given their group's F', so the oracle runs a seeded
     sample of rows from the same F and the comparison is exact per row.
@@ -252,4 +299,4 @@ def test_lnq_llama2_7b_attn_full_size_sampled_rows(device):
     rng = np.random.default_rng(7)
     rows = sorted(int(g * prob.rpg + r) for g in range(wl.groups)
                   for r in rng.choice(prob.rpg, 2, replace=False))
-    _end_to_end(device, prob, wl.bits, wl.iters, wl.block, rows_checked=rows)
+    _end_to_end(device, prob, wl.bits, wl.iters, rows_checked=rows)
