@@ -89,28 +89,13 @@ __device__ __forceinline__ void tri_pair(int p, int T, int& ta, int& tb) {
     tb = a + p;
 }
 
-__device__ __forceinline__ void load_piece(const uint16_t* __restrict__ X, int64_t d_in,
-                                           int64_t tok0, int64_t tok_end, int64_t f0,
-                                           u32x4 (&v)[8]) {
-    const bool fok = f0 < d_in;   // d_in % 8 == 0, so the 8 features are all valid or none
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        int64_t t = tok0 + r;
-        if (fok && t < tok_end) {
-            v[r] = *(const u32x4*)(X + t * d_in + f0);
-        } else {
-            v[r] = u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-}
-
 __device__ __forceinline__ void scale_piece(u32x4 (&v)[8], const float (&s)[8]) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            float lo = __uint_as_float(v[r][k] << 16) * s[r];
-            float hi = __uint_as_float(v[r][k] & 0xffff0000u) * s[r];
+            const float lo = __uint_as_float(v[r][k] << 16) * s[r];
+            const float hi = __uint_as_float(v[r][k] & 0xffff0000u) * s[r];
             v[r][k] = pack_bf16x2(lo, hi);
         }
     }
@@ -173,16 +158,35 @@ __global__ __launch_bounds__(256, 1) void k_fisher_mfma(
 
     const int nchunks = (int)((ke - kb + FKC - 1) / FKC);
 
+    // Loads use a block-uniform base pointer for the stage and 32-bit per-lane
+    // byte offsets (no 64-bit address arithmetic per load, no branches).  Rows
+    // past the split's end (only in its last stage) load the stage's first
+    // token, a valid address, and get a zero scale; features past d_in load
+    // feature 0 and are never written.
+    const uint32_t fa = (uint32_t)((a0 + 8 * fc < d_in) ? a0 + 8 * fc : 0);
+    const uint32_t fb = (uint32_t)((b0 + 8 * fc < d_in) ? b0 + 8 * fc : 0);
+    const uint32_t row0 = (uint32_t)(8 * tg) * (uint32_t)d_in;
     u32x4 pa[8], pb[8];
-    float sv[8];
+    float sraw[8];
     auto fetch = [&](int c) {
-        const int64_t tok0 = kb + (int64_t)c * FKC + 8 * tg;
-        load_piece(X, d_in, tok0, ke, a0 + 8 * fc, pa);
-        load_piece(X, d_in, tok0, ke, b0 + 8 * fc, pb);
+        const int64_t t0 = kb + (int64_t)c * FKC;          // first token of the stage
+        const char* Xs = (const char*)(X + t0 * d_in);
+        const bool full = t0 + FKC <= ke;                  // block-uniform
 #pragma unroll
-        for (int r = 0; r < 8; ++r) sv[r] = (tok0 + r < ke) ? Sg[tok0 + r] : 0.f;
+        for (int r = 0; r < 8; ++r) {
+            uint32_t ro = row0 + (uint32_t)r * (uint32_t)d_in;
+            if (!full && t0 + 8 * tg + r >= ke) ro = 0;
+            pa[r] = *(const u32x4*)(Xs + 2u * (ro + fa));
+            pb[r] = *(const u32x4*)(Xs + 2u * (ro + fb));
+            const int64_t tk = t0 + 8 * tg + r;
+            sraw[r] = Sg[(tk < ke) ? tk : t0];
+        }
     };
-    auto stage = [&](int buf) {
+    auto stage = [&](int c, int buf) {
+        const int64_t tok0 = kb + (int64_t)c * FKC + 8 * tg;
+        float sv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) sv[r] = (tok0 + r < ke) ? sraw[r] : 0.f;
         scale_piece(pb, sv);
         store_piece_T(sA(buf) + (8 * fc) * FPITCH + 8 * tg, pa);
         store_piece_T(sB(buf) + (8 * fc) * FPITCH + 8 * tg, pb);
@@ -190,32 +194,46 @@ __global__ __launch_bounds__(256, 1) void k_fisher_mfma(
 
     if (nchunks > 0) {
         fetch(0);
-        stage(0);
+        stage(0, 0);
     }
     __syncthreads();
     for (int c = 0; c < nchunks; ++c) {
         const int buf = c & 1;
-        const bool more = c + 1 < nchunks;
-        if (more) fetch(c + 1);
+        // the next stage's loads (a stage past the last one is staged but never read)
+        if (c + 1 < nchunks) fetch(c + 1);
         const uint16_t* A = sA(buf);
         const uint16_t* B = sB(buf);
-#pragma unroll
-        for (int ks = 0; ks < FKC / 16; ++ks) {
+        // fragments of k-step ks + 1 are read from LDS while the MFMAs of k-step ks run
+        bf16x8 af[2][4], bfr[2][4];
+        auto read_frags = [&](int ks, int set) {
             const int koff = ks * 16 + 8 * (lane >> 5);
-            bf16x8 af[4], bfr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                af[i] = as_bf16x8(*(const u32x4*)(A + (128 * wa + 32 * i + (lane & 31)) * FPITCH + koff));
+                af[set][i] = as_bf16x8(*(const u32x4*)(A + (128 * wa + 32 * i + (lane & 31)) * FPITCH + koff));
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                bfr[j] = as_bf16x8(*(const u32x4*)(B + (128 * wb + 32 * j + (lane & 31)) * FPITCH + koff));
+                bfr[set][j] = as_bf16x8(*(const u32x4*)(B + (128 * wb + 32 * j + (lane & 31)) * FPITCH + koff));
+        };
+        read_frags(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < FKC / 16; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < FKC / 16) read_frags(ks + 1, cur ^ 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+            if (ks + 1 < FKC / 16) {
+                // interleave: 2 MFMAs, 1 LDS read, repeated
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
         }
-        if (more) stage(buf ^ 1);
+        if (c + 1 < nchunks) stage(c + 1, buf ^ 1);
         __syncthreads();
     }
 
