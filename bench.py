@@ -9,8 +9,10 @@ step, assignment pass) + objective trace) on every output row.
 
 Prints one JSON line.  `value` is rows quantized per second for the whole
 layer (Fisher included); the Fisher TFLOP/s, the LNQ-only rows/s and the
-per-stage times (HIP events recorded by the library on its stream) are extra
-fields.  `roofline` is for the stage that takes the most time.  The
+per-stage times are extra fields.  The per-stage times come from the last
+warmup step, run with every stage bracketed by HIP events on the library's
+stream; the timed steps carry events around the dominant stage only, and
+`roofline` is computed for that stage from those events.  The
 `cpu_baseline` leg times the fp64 oracle on a bounded sample of the same
 workload on the host cores.
 """
@@ -110,13 +112,25 @@ def main():
         return gq.lnq_quantize(W, F, wl.bits, wl.iters, block=64, ridge_rel=1e-6, C=C,
                                P=P, init=gq.GQ_INIT_QUANTILE, ws=ws_l)
 
-    for i in range(args.warmup):
+    warm = max(1, args.warmup)
+    for i in range(warm):
+        if i == warm - 1:
+            # the last warmup step records every stage with HIP events: that is the
+            # per-stage breakdown; the timed steps below carry events for one stage only
+            gq.gq_timing_read()
+            gq.gq_timing_enable(True)
         step()
         torch.cuda.synchronize()
-        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+        print(f"[bench] warmup {i + 1}/{warm} done", file=sys.stderr, flush=True)
+    gq.gq_timing_enable(False)
+    breakdown = gq.gq_timing_read()
+    per_step = {k: v[0] for k, v in breakdown.items() if v[1]}
+    launches = {k: v[1] for k, v in breakdown.items() if v[1]}
+    dom = max(per_step, key=per_step.get)
 
-    gq.gq_timing_read()               # drop anything recorded so far
-    gq.gq_timing_enable(True)
+    # timed region: events only around the dominant stage's launches, on the stream
+    # the library launches them on (the caller's current stream)
+    gq.gq_timing_enable([dom])
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     outs = None
@@ -125,32 +139,32 @@ def main():
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     gq.gq_timing_enable(False)
-    stages = gq.gq_timing_read()
+    timed = gq.gq_timing_read()
     ms_step = (t_end - t_start) * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_step:.2f} ms/step", file=sys.stderr, flush=True)
 
     trace = outs[2].cpu().numpy()
     nchg = outs[3].cpu().numpy()
-    per_step = {k: v[0] / args.steps for k, v in stages.items() if v[1]}
-    launches = {k: v[1] / args.steps for k, v in stages.items() if v[1]}
     fisher_ms = per_step.get("group_scale", 0) + per_step.get("fisher_mfma", 0) + \
         per_step.get("fisher_finalize", 0) + per_step.get("fisher_plain", 0)
     lnq_ms = sum(v for k, v in per_step.items() if k.startswith("lnq"))
     sym_flops = wl.n * wl.d_in * (wl.d_in + 1) * wl.groups
 
-    # roofline of the stage with the largest share of the step
-    dom = max(per_step, key=per_step.get)
+    # roofline of the stage with the largest share of the step, from the events of
+    # the timed region
     roof = None
     spec = _stage_units(dom, wl, float(np.sum(nchg)))
-    if spec is not None:
+    if spec is not None and timed[dom][1]:
         bound, amount, peak, unit = spec
-        avg_ms = per_step[dom] / launches[dom]
-        per_launch = amount / launches[dom]
+        n_launch = timed[dom][1] / args.steps
+        avg_ms = timed[dom][0] / timed[dom][1]
+        per_launch = amount / n_launch
         achieved = per_launch / (avg_ms * 1e-3)
         scale = 1e9 if unit == "GB/s" else 1e12
         roof = {"kernel": dom, "bound": bound, "achieved": achieved / scale, "peak": peak / scale,
                 "unit": unit, "frac": achieved / peak, "traffic": None,
-                "avg_launch_ms": avg_ms, "units_per_launch": per_launch}
+                "avg_launch_ms": avg_ms, "units_per_launch": per_launch,
+                "launches_per_step": n_launch}
 
     result = {
         "metric": "LNQ rows quantized/s + Fisher TFLOP/s at 4096x4096, 3-bit, 1 MI355X",
@@ -174,6 +188,7 @@ def main():
         "s_per_layer": ms_step * 1e-3,
         "stage_ms_per_step": {k: round(v, 4) for k, v in per_step.items()},
         "stage_launches_per_step": launches,
+        "stage_breakdown_from": "last warmup step, every stage bracketed by HIP events",
         "changed_per_sweep": [int(x) for x in nchg],
         "objective_trace": [float(x) for x in trace],
         "monotone": bool(np.all(trace[1:] <= trace[:-1] * (1 + 1e-6))),

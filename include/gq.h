@@ -188,12 +188,14 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
 
 /*
  * Diagnostics: per-stage kernel timing with HIP events.
- * gq_timing_enable(1) makes every later call bracket each of its stages with two
- * events recorded on the call's stream (events are created on first use and
- * kept in a pool).  gq_timing_read synchronises the recorded events, writes the
- * summed milliseconds and the number of timed launch sequences per stage into
- * ms[GQ_STAGE_COUNT] and launches[GQ_STAGE_COUNT] (host arrays), and clears
- * the record.  Timing adds one event record per stage boundary; results of the
+ * gq_timing_enable(mask) makes every later call bracket each launch sequence of
+ * the stages whose bit (1 << gq_stage) is set in `mask` with two events recorded
+ * on the call's stream (events are created on first use and kept in a pool);
+ * mask 0 turns timing off, -1 times every stage.  gq_timing_read synchronises
+ * the recorded events, writes the summed milliseconds and the number of timed
+ * launch sequences per stage into ms[GQ_STAGE_COUNT] and
+ * launches[GQ_STAGE_COUNT] (host arrays), and clears the record.  Each timed
+ * stage boundary adds one event record to the stream; results of the
  * computation do not change.  GQ_EHIP if an event call failed.
  */
 typedef enum {
@@ -211,7 +213,7 @@ typedef enum {
     GQ_STAGE_COUNT
 } gq_stage;
 
-void gq_timing_enable(int on);
+void gq_timing_enable(int mask);
 gq_status gq_timing_read(double* ms, int64_t* launches);
 /* Short name of a stage ("" for an unknown id); static storage. */
 const char* gq_stage_name(int stage);

@@ -263,9 +263,25 @@ def lnq_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float 
     return C, P, tr, nch[:iters]
 
 
-def gq_timing_enable(on: bool = True) -> None:
-    """Bracket every later stage with HIP events on its stream (diagnostics)."""
-    library().gq_timing_enable(int(bool(on)))
+STAGES = ("group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain", "lnq_prepare",
+          "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep", "lnq_small")
+
+
+def gq_timing_enable(on=True) -> None:
+    """Bracket later launch sequences with HIP events on their stream (diagnostics).
+
+    on: True (every stage), False (off), a stage name, or an iterable of names.
+    """
+    if on is True:
+        mask = -1
+    elif on is False or on is None:
+        mask = 0
+    else:
+        names = [on] if isinstance(on, str) else list(on)
+        mask = 0
+        for n in names:
+            mask |= 1 << STAGES.index(n)
+    library().gq_timing_enable(mask)
 
 
 def gq_timing_read() -> dict:

@@ -22,7 +22,7 @@ static_assert((int)gq::ST_COUNT == (int)GQ_STAGE_COUNT, "stage ids of gq.h and t
 // ---------------------------------------------------------------------------
 namespace gq {
 namespace {
-std::atomic<bool> g_timing{false};
+std::atomic<int> g_timing{0};      // bit mask of timed stages
 std::mutex g_tmu;
 struct Mark { int stage; hipEvent_t start, stop; };
 std::vector<Mark> g_marks;          // completed (start, stop) pairs
@@ -42,7 +42,7 @@ hipEvent_t take_event() {
 }
 }  // namespace
 
-bool timing_on() { return g_timing.load(std::memory_order_relaxed); }
+bool timing_on(Stage s) { return (g_timing.load(std::memory_order_relaxed) >> (int)s) & 1; }
 
 void timing_mark(Stage s, hipStream_t st, bool begin) {
     std::lock_guard<std::mutex> lk(g_tmu);
@@ -142,7 +142,7 @@ extern "C" {
 
 int gq_abi_version(void) { return GQ_ABI_VERSION; }
 
-void gq_timing_enable(int on) { gq::g_timing.store(on != 0); }
+void gq_timing_enable(int mask) { gq::g_timing.store(mask & ((1 << GQ_STAGE_COUNT) - 1)); }
 
 gq_status gq_timing_read(double* ms, int64_t* launches) {
     if (!ms || !launches) return fail(GQ_EINVAL, "null ms or launches");

@@ -11,7 +11,7 @@ enum Stage {
     ST_GROUP_SCALE = 0, ST_FISHER_MFMA, ST_FISHER_FINALIZE, ST_FISHER_PLAIN, ST_LNQ_PREPARE,
     ST_LNQ_RESID, ST_LNQ_INIT, ST_LNQ_GRAM, ST_LNQ_SOLVE, ST_LNQ_SWEEP, ST_LNQ_SMALL, ST_COUNT
 };
-bool timing_on();
+bool timing_on(Stage s);
 void timing_mark(Stage s, hipStream_t st, bool begin);
 // Records a start event on construction and a stop event on destruction when
 // timing is on; the launches in between are attributed to the stage.
@@ -19,7 +19,7 @@ struct StageTimer {
     Stage s;
     hipStream_t st;
     bool on;
-    StageTimer(Stage s_, hipStream_t st_) : s(s_), st(st_), on(timing_on()) {
+    StageTimer(Stage s_, hipStream_t st_) : s(s_), st(st_), on(timing_on(s_)) {
         if (on) timing_mark(s, st, true);
     }
     ~StageTimer() {

@@ -98,35 +98,3 @@ def test_fisher_deterministic(device):
     F1 = _run(device, inp, 4)
     F2 = _run(device, inp, 4)
     assert torch.equal(F1, F2)
-
-
-def test_fisher_llama2_7b_attn_full_size_sampled(device):
-    """Full 4096 x 4096 projection, 131072 tokens, 4 groups: sampled entries vs the oracle.
-
-    Entry bar: |F_gpu[a,b] - F_ref[a,b]| <= 2e-3 * sqrt(F_ref[a,a] F_ref[b,b]); the
-    sampled relative Frobenius error must also stay under 2e-3.
-    """
-    wl = synth.workload("llama2_7b_attn")
-    inp = synth.make_inputs(wl, seed=0)
-    F = _run(device, inp, wl.groups)
-    _check_symmetric(F)
-    X = inp["X"]
-    S = O.group_scale(synth.decode(inp["G"]), wl.groups)
-    rng = np.random.default_rng(0)
-    cols = list(rng.choice(wl.d_in, 12, replace=False)) + list(inp["outlier_cols"][:4])
-    cols = sorted(set(int(c) for c in cols))
-    xc = {c: synth.decode(X[:, c]) for c in cols}
-    num = den = 0.0
-    for g in range(wl.groups):
-        Fg = F[g]
-        diag = {c: O.fisher_entry(xc[c], xc[c], S[g]) for c in cols}
-        for a in cols:
-            for b in cols:
-                if b < a:
-                    continue
-                ref = O.fisher_entry(xc[a], xc[b], S[g]) if a != b else diag[a]
-                got = float(Fg[a, b].item())
-                assert abs(got - ref) <= BF16_TOL * np.sqrt(diag[a] * diag[b]), (g, a, b, got, ref)
-                num += (got - ref) ** 2
-                den += ref ** 2
-    assert np.sqrt(num / den) <= BF16_TOL
