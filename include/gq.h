@@ -210,6 +210,7 @@ typedef enum {
     GQ_STAGE_LNQ_SOLVE,         /* codebook solves and row objectives */
     GQ_STAGE_LNQ_SWEEP,         /* the assignment pass */
     GQ_STAGE_LNQ_SMALL,         /* sums and counters */
+    GQ_STAGE_FISHER_PACK,       /* feature-major bf16 operands of the Fisher contraction */
     GQ_STAGE_COUNT
 } gq_stage;
 

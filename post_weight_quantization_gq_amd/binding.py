@@ -25,7 +25,7 @@ EXPORTS = (
     "gq_fisher_accumulate", "gq_lnq_workspace_size", "lnq_codebook_update", "lnq_assign_sweep",
     "lnq_objective", "lnq_quantize", "gq_timing_enable", "gq_timing_read", "gq_stage_name",
 )
-STAGE_COUNT = 11
+STAGE_COUNT = 12
 
 
 class GQError(RuntimeError):
@@ -264,7 +264,8 @@ def lnq_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float 
 
 
 STAGES = ("group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain", "lnq_prepare",
-          "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep", "lnq_small")
+          "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep", "lnq_small",
+          "fisher_pack")
 
 
 def gq_timing_enable(on=True) -> None:

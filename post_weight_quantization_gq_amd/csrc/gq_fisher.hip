@@ -7,11 +7,12 @@
 //
 // Kernels
 //   k_group_scale     s_g[t] for every token (HBM stream over G).
-//   k_fisher_mfma     bf16 MFMA (v_mfma_f32_32x32x16_bf16) SYRK-like contraction over
-//                     tokens for the upper-triangle 256x256 tiles of every F_g; the
-//                     gradient-square scale is fused into the LDS staging of one
-//                     operand; tokens may be split across blocks (split-K) to fill the
-//                     chip, each split writing its own partial tile.
+//   k_fisher_pack     packs X feature-major (XT) and, per group, the scaled copy
+//                     YT[g] = (s_g * X)^T in bf16, zero-padded to whole tiles.
+//   k_fisher_mfma     bf16 MFMA (v_mfma_f32_32x32x16_bf16) contraction XT YT[g]^T over
+//                     tokens for the upper-triangle 256x256 tiles of every F_g;
+//                     tokens may be split across blocks (split-K) to fill the chip,
+//                     each split writing its own partial tile.
 //   k_fisher_finalize sums the split partials in a fixed order and writes the tile
 //                     and its mirror image (exactly symmetric F), optionally adding.
 //   k_fisher_plain    float64-accumulating path for float32 inputs (and the fallback
@@ -66,61 +67,125 @@ __global__ __launch_bounds__(256) void k_group_scale(const void* __restrict__ G,
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA Fisher.  Block tile 256 (a) x 256 (b) of one group, 4 waves in a 2x2
-// arrangement, each wave owning 128 x 128 outputs as 4x4 MFMA 32x32 tiles.
-// Tokens are staged 64 at a time through LDS in [feature][token] layout (token
-// contiguous, 72-element pitch), the layout the MFMA operand reads want.  Each
-// thread loads an 8-token x 8-feature piece of both operands (16-byte global
-// loads along the feature axis), transposes it in registers with v_perm_b32 and
-// writes 16-byte rows; the B operand is scaled by s_g[t] and rounded to bf16
-// before the transpose.
+// Operand packing.  The contraction reads both operands feature-major with tokens
+// contiguous, the layout the MFMA operand fragments want, blocked by 32 tokens:
+//     XT[t/32][a][t%32]    = X[t][a]
+//     YT[g][t/32][a][t%32] = bf16(s_g[t] * X[t][a])   (float32 product, one rounding)
+// so that the 256 feature rows of one 32-token stage of a tile are 16 KB of
+// contiguous memory.  Features are padded with zero rows to a multiple of 256 and
+// tokens with zeros to a multiple of 64, so every tile and stage is whole.  One
+// block per 64-token x 64-feature tile: 16-byte loads along the features into
+// LDS, then 16-byte stores of 8 consecutive tokens per feature.
 // ---------------------------------------------------------------------------
-constexpr int FT = 256;        // tile edge
-constexpr int FKC = 64;        // tokens per LDS stage
-constexpr int FPITCH = 72;     // bf16 elements per LDS row (144 B: conflict-free reads and writes)
-constexpr int F_STAGE_ELEMS = FT * FPITCH;               // one operand, one stage
-constexpr size_t F_LDS_BYTES = (size_t)4 * F_STAGE_ELEMS * 2;  // 2 operands x 2 stages
+constexpr int PK = 64;
+constexpr int PK_G = 16;       // groups whose scales are staged in LDS at a time
 
-__device__ __forceinline__ void tri_pair(int p, int T, int& ta, int& tb) {
-    // p enumerates (ta <= tb) row by row: row ta holds T - ta pairs.
-    int a = 0;
-    while (p >= T - a) { p -= T - a; ++a; }
-    ta = a;
-    tb = a + p;
+// element offset of (token t, feature a) in a blocked operand (t % 8 == 0 here)
+__device__ __forceinline__ int64_t blk_off(int64_t t, int64_t a, int64_t d_pad) {
+    return ((t >> 5) * d_pad + a) * 32 + (t & 31);
 }
 
-__device__ __forceinline__ void scale_piece(u32x4 (&v)[8], const float (&s)[8]) {
+__global__ __launch_bounds__(256) void k_fisher_pack(const uint16_t* __restrict__ X,
+                                                    const float* __restrict__ S, int64_t n,
+                                                    int64_t n_pad, int64_t d, int64_t d_pad,
+                                                    int groups, uint16_t* __restrict__ XT,
+                                                    uint16_t* __restrict__ YT) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[PK][PK + 8];   // [token][feature]
+    __shared__ __attribute__((aligned(16))) float ss[PK_G][PK];          // s_g[t0 + t]
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * PK;
+    const int64_t f0 = (int64_t)blockIdx.y * PK;
+    const int fc = tid & 7;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int h = 0; h < 2; ++h) {
+        const int r = (tid >> 3) + 32 * h;
+        const int64_t t = t0 + r, f = f0 + 8 * fc;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (t < n && f < d) v = *(const u32x4*)(X + t * d + f);     // d % 8 == 0
+        *(u32x4*)&tile[r][8 * fc] = v;
+    }
+    __syncthreads();
+    const int c = tid & 7;                 // token chunk: tokens t0 + 8c .. + 7
+    const int64_t col = t0 + 8 * c;
+    uint32_t xs[2][8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float lo = __uint_as_float(v[r][k] << 16) * s[r];
-            const float hi = __uint_as_float(v[r][k] & 0xffff0000u) * s[r];
-            v[r][k] = pack_bf16x2(lo, hi);
+    for (int h = 0; h < 2; ++h) {
+        const int a = (tid >> 3) + 32 * h;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) xs[h][k] = tile[8 * c + k][a];
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = xs[h][2 * k] | (xs[h][2 * k + 1] << 16);
+        *(u32x4*)(XT + blk_off(col, f0 + a, d_pad)) = o;     // f0 + a < d_pad: whole 64-tiles
+    }
+    for (int g0 = 0; g0 < groups; g0 += PK_G) {
+        const int gn = (groups - g0) < PK_G ? (groups - g0) : PK_G;
+        __syncthreads();
+        for (int e = tid; e < gn * PK; e += 256) {
+            const int gi = e / PK, tt = e - gi * PK;
+            ss[gi][tt] = (t0 + tt < n) ? S[(int64_t)(g0 + gi) * n + t0 + tt] : 0.f;
+        }
+        __syncthreads();
+        for (int gi = 0; gi < gn; ++gi) {
+            const float4 s_lo = *(const float4*)&ss[gi][8 * c];
+            const float4 s_hi = *(const float4*)&ss[gi][8 * c + 4];
+            const float sv[8] = {s_lo.x, s_lo.y, s_lo.z, s_lo.w, s_hi.x, s_hi.y, s_hi.z, s_hi.w};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int a = (tid >> 3) + 32 * h;
+                u32x4 y;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    y[k] = pack_bf16x2(__uint_as_float(xs[h][2 * k] << 16) * sv[2 * k],
+                                       __uint_as_float(xs[h][2 * k + 1] << 16) * sv[2 * k + 1]);
+                *(u32x4*)(YT + (int64_t)(g0 + gi) * d_pad * n_pad + blk_off(col, f0 + a, d_pad)) = y;
+            }
         }
     }
 }
 
-// transpose an 8 (token) x 8 (feature) bf16 piece and store 8 rows of 8 tokens
-__device__ __forceinline__ void store_piece_T(uint16_t* lds_rows, const u32x4 (&v)[8]) {
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-        const int p = f >> 1;
-        const uint32_t sel = (f & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 o;
-        o[0] = __builtin_amdgcn_perm(v[1][p], v[0][p], sel);
-        o[1] = __builtin_amdgcn_perm(v[3][p], v[2][p], sel);
-        o[2] = __builtin_amdgcn_perm(v[5][p], v[4][p], sel);
-        o[3] = __builtin_amdgcn_perm(v[7][p], v[6][p], sel);
-        *(u32x4*)(lds_rows + f * FPITCH) = o;
-    }
+// ---------------------------------------------------------------------------
+// bf16 MFMA Fisher: upper-triangle 256 (a) x 256 (b) tiles of F_g = XT YT[g]^T.
+// 4 waves in a 2x2 arrangement, each owning 128 x 128 outputs as 4x4
+// v_mfma_f32_32x32x16_bf16 tiles (the 256 accumulator registers of a lane).
+// Tokens are staged 32 at a time in a ring of 4 LDS stages (4 x 32 KB), filled by
+// direct buffer-to-LDS loads issued three stages ahead, so no staging registers
+// and no LDS stores are needed.  An operand row of a stage is 64 bytes of the
+// blocked XT or YT, kept as four 16-byte slots; chunk c of row r sits in slot
+// r*4 + (c ^ ((r >> 2) & 3)).  Each load instruction fills 16 whole rows (1 KB
+// of consecutive LDS), and a fragment read (one chunk of 16 consecutive rows per
+// quarter-wave) touches 16 distinct 16-byte bank groups.  One barrier per stage.
+// ---------------------------------------------------------------------------
+constexpr int FT = 256;        // tile edge
+constexpr int FKC = 32;        // tokens per LDS stage
+constexpr int FRING = 4;       // LDS stages in flight (4 x 32 KB = 128 KB)
+constexpr int F_SLOTS = FT * 4;                                     // 16-byte slots, one operand, one stage
+constexpr size_t F_LDS_BYTES = (size_t)FRING * 2 * F_SLOTS * 16;
+
+// Pairs (ta <= tb) are enumerated column by column (column tb holds tb + 1 pairs),
+// so consecutive logical blocks share the b band, the per-group operand, and
+// differ in the a band, which all groups share.
+__device__ __forceinline__ void tri_pair(int p, int T, int& ta, int& tb) {
+    int b = 0;
+    while (p > b) { p -= b + 1; ++b; }
+    (void)T;
+    ta = p;
+    tb = b;
 }
 
-__global__ __launch_bounds__(256, 1) void k_fisher_mfma(
-    const uint16_t* __restrict__ X, const float* __restrict__ S, int64_t n, int64_t d_in,
-    int groups, int T, int npairs, int nsplit, int64_t ksplit, int total_blocks,
+// wait until at most n vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fisher_mfma(
+    const uint16_t* __restrict__ XT, const uint16_t* __restrict__ YT, int64_t n_pad,
+    int64_t d_pad, int groups, int T, int npairs, int64_t ksplit, int total_blocks,
     float* __restrict__ part) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t fisher_lds[];
+    extern __shared__ u32x4 fisher_lds[];
     // XCD-aware remap: hardware block h lands on XCD h % 8; give each XCD a
     // contiguous range of logical blocks (same split, neighbouring tiles, all groups).
     const int nb = gridDim.x;
@@ -132,21 +197,44 @@ __global__ __launch_bounds__(256, 1) void k_fisher_mfma(
     const int split = lin / (groups * npairs);
     int ta, tb;
     tri_pair(pair, T, ta, tb);
-    const int64_t a0 = (int64_t)ta * FT, b0 = (int64_t)tb * FT;
     const int64_t kb = (int64_t)split * ksplit;
-    const int64_t ke = (kb + ksplit < n) ? kb + ksplit : n;
-    const float* __restrict__ Sg = S + (int64_t)g * n;
+    const int64_t ke = (kb + ksplit < n_pad) ? kb + ksplit : n_pad;
+    const int nst = kb < ke ? (int)((ke - kb) / FKC) : 0;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the LDS targets go to M0
     const int wa = wave & 1, wb = wave >> 1;
-    const int fc = tid >> 3;     // feature group: features 8*fc .. 8*fc+7
-    const int tg = tid & 7;      // token group: tokens 8*tg .. 8*tg+7
 
-    // stage b: A operand at fisher_lds + 2b*STAGE, B operand right after it
-    auto sA = [&](int b) { return fisher_lds + (2 * b) * F_STAGE_ELEMS; };
-    auto sB = [&](int b) { return fisher_lds + (2 * b + 1) * F_STAGE_ELEMS; };
+    // A stage of the a band is 256 rows x 64 bytes, contiguous in the blocked XT
+    // (likewise the b band in YT[g]).  Load instruction k of a wave fills rows
+    // 16q .. 16q + 15 (q = 4k + wave): lane L takes row 16q + L/4 and slot L%4,
+    // i.e. chunk (L%4) ^ ((L/16)%4), at byte 1024 q + 64 (L/4) + 16 chunk of the
+    // stage: a per-lane vector offset plus a uniform scalar offset, against a
+    // buffer descriptor rebuilt per stage (scalar arithmetic only).
+    const uint16_t* Abase = XT + ((kb >> 5) * d_pad + (int64_t)ta * FT) * 32;
+    const uint16_t* Bbase = YT + (int64_t)g * d_pad * n_pad + ((kb >> 5) * d_pad + (int64_t)tb * FT) * 32;
+    const int64_t stage_elems = d_pad * 32;
+    const uint32_t voff = (uint32_t)(lane >> 2) * 64u +
+                          16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+
+    auto sA = [&](int st) { return fisher_lds + st * (2 * F_SLOTS); };
+    auto sB = [&](int st) { return fisher_lds + st * (2 * F_SLOTS) + F_SLOTS; };
+
+    auto issue = [&](int s) {
+        const int st = s % FRING;
+        const __amdgpu_buffer_rsrc_t Ar = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Abase + (int64_t)s * stage_elems), (short)0, F_SLOTS * 16, 0x00020000);
+        const __amdgpu_buffer_rsrc_t Br = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Bbase + (int64_t)s * stage_elems), (short)0, F_SLOTS * 16, 0x00020000);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int q = 4 * k + wave;
+            const uint32_t so = (uint32_t)q * 1024u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(Ar, (lds_ptr_t)(sA(st) + 64 * q), 16, voff, so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(Br, (lds_ptr_t)(sB(st) + 64 * q), 16, voff, so, 0, 0);
+        }
+    };
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -156,85 +244,52 @@ __global__ __launch_bounds__(256, 1) void k_fisher_mfma(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    const int nchunks = (int)((ke - kb + FKC - 1) / FKC);
-
-    // Loads use a block-uniform base pointer for the stage and 32-bit per-lane
-    // byte offsets (no 64-bit address arithmetic per load, no branches).  Rows
-    // past the split's end (only in its last stage) load the stage's first
-    // token, a valid address, and get a zero scale; features past d_in load
-    // feature 0 and are never written.
-    const uint32_t fa = (uint32_t)((a0 + 8 * fc < d_in) ? a0 + 8 * fc : 0);
-    const uint32_t fb = (uint32_t)((b0 + 8 * fc < d_in) ? b0 + 8 * fc : 0);
-    const uint32_t row0 = (uint32_t)(8 * tg) * (uint32_t)d_in;
-    u32x4 pa[8], pb[8];
-    float sraw[8];
-    auto fetch = [&](int c) {
-        const int64_t t0 = kb + (int64_t)c * FKC;          // first token of the stage
-        const char* Xs = (const char*)(X + t0 * d_in);
-        const bool full = t0 + FKC <= ke;                  // block-uniform
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            uint32_t ro = row0 + (uint32_t)r * (uint32_t)d_in;
-            if (!full && t0 + 8 * tg + r >= ke) ro = 0;
-            pa[r] = *(const u32x4*)(Xs + 2u * (ro + fa));
-            pb[r] = *(const u32x4*)(Xs + 2u * (ro + fb));
-            const int64_t tk = t0 + 8 * tg + r;
-            sraw[r] = Sg[(tk < ke) ? tk : t0];
-        }
+    const int sw = (lane >> 2) & 3;      // slot swizzle of the fragment rows
+    // wait until stage `want` has landed, given stages up to `last` issued
+    auto wait_stage = [&](int want, int last) {
+        const int newer = last - want;
+        if (newer >= 4) wait_vmcnt<32>();
+        else if (newer == 3) wait_vmcnt<24>();
+        else if (newer == 2) wait_vmcnt<16>();
+        else if (newer == 1) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
     };
-    auto stage = [&](int c, int buf) {
-        const int64_t tok0 = kb + (int64_t)c * FKC + 8 * tg;
-        float sv[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) sv[r] = (tok0 + r < ke) ? sraw[r] : 0.f;
-        scale_piece(pb, sv);
-        store_piece_T(sA(buf) + (8 * fc) * FPITCH + 8 * tg, pa);
-        store_piece_T(sB(buf) + (8 * fc) * FPITCH + 8 * tg, pb);
-    };
-
-    if (nchunks > 0) {
-        fetch(0);
-        stage(0, 0);
+    {
+        const int pre = nst < FRING - 1 ? nst : FRING - 1;
+        for (int s = 0; s < pre; ++s) issue(s);
     }
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        // the next stage's loads (a stage past the last one is staged but never read)
-        if (c + 1 < nchunks) fetch(c + 1);
-        const uint16_t* A = sA(buf);
-        const uint16_t* B = sB(buf);
-        // fragments of k-step ks + 1 are read from LDS while the MFMAs of k-step ks run
+    int slot = 0;                        // ring slot of stage s
+    for (int s = 0; s < nst; ++s) {
+        // this wave's loads of stage s are done (later stages may still be in flight),
+        // then every wave's are
+        const int last = (s + FRING - 2 < nst) ? s + FRING - 2 : nst - 1;
+        wait_stage(s, last);
+        __builtin_amdgcn_s_barrier();
+        // every wave has finished stage s - 1: its slot of the ring takes stage s + FRING - 1
+        if (s + FRING - 1 < nst) issue(s + FRING - 1);
+        const u32x4* A = fisher_lds + slot * (2 * F_SLOTS);
+        const u32x4* B = A + F_SLOTS;
         bf16x8 af[2][4], bfr[2][4];
-        auto read_frags = [&](int ks, int set) {
-            const int koff = ks * 16 + 8 * (lane >> 5);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int cs = (2 * ks + (lane >> 5)) ^ sw;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                af[set][i] = as_bf16x8(*(const u32x4*)(A + (128 * wa + 32 * i + (lane & 31)) * FPITCH + koff));
+                af[ks][i] = as_bf16x8(A[(128 * wa + 32 * i + (lane & 31)) * 4 + cs]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                bfr[set][j] = as_bf16x8(*(const u32x4*)(B + (128 * wb + 32 * j + (lane & 31)) * FPITCH + koff));
-        };
-        read_frags(0, 0);
+                bfr[ks][j] = as_bf16x8(B[(128 * wb + 32 * j + (lane & 31)) * 4 + cs]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < FKC / 16; ++ks) {
-            const int cur = ks & 1;
-            if (ks + 1 < FKC / 16) read_frags(ks + 1, cur ^ 1);
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
-            if (ks + 1 < FKC / 16) {
-                // interleave: 2 MFMAs, 1 LDS read, repeated
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-            }
-        }
-        if (c + 1 < nchunks) stage(c + 1, buf ^ 1);
-        __syncthreads();
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        slot = (slot + 1 == FRING) ? 0 : slot + 1;
     }
 
     // partial tile [256][256] row-major (a_local, b_local)
@@ -251,51 +306,82 @@ __global__ __launch_bounds__(256, 1) void k_fisher_mfma(
             }
 }
 
-// Sum split partials (fixed order) and write the tile plus its mirror.
+// Sum split partials (fixed order) and write the tile plus its mirror.  One block
+// per 64 x 64 sub-tile of a (pair, group): each thread sums 4 rows x 4 columns
+// with float4 loads, writes F[a][b] and, through LDS, the mirror F[b][a] with
+// float4 stores (d_in % 8 == 0 on this path, F 16-byte aligned).
 __global__ __launch_bounds__(256) void k_fisher_finalize(const float* __restrict__ part,
                                                         int64_t d_in, int groups, int T,
                                                         int npairs, int nsplit,
                                                         int accumulate, float* __restrict__ F) {
     __shared__ float sub[64][65];
-    const int pair = blockIdx.x;
+    const int pair = blockIdx.x >> 4;
+    const int sbk = blockIdx.x & 15;
     const int g = blockIdx.y;
     int ta, tb;
     tri_pair(pair, T, ta, tb);
+    const int sr = (sbk >> 2) * 64, sc = (sbk & 3) * 64;
+    const int64_t a0 = (int64_t)ta * FT + sr, b0 = (int64_t)tb * FT + sc;
+    if (a0 >= d_in || b0 >= d_in) return;
+    if (ta == tb && sr > sc) return;                 // strictly below the diagonal
     const int tid = threadIdx.x;
+    const int c4 = (tid & 15) * 4;
     float* Fg = F + (size_t)g * d_in * d_in;
-    for (int sb = 0; sb < 16; ++sb) {
-        const int sr = (sb >> 2) * 64, sc = (sb & 3) * 64;
-        // direct write F[a][b]
-        const int col = tid & 63;
-#pragma unroll 4
-        for (int k = 0; k < 16; ++k) {
-            const int r = (tid >> 6) + 4 * k;
-            float v = 0.f;
-            for (int s = 0; s < nsplit; ++s) {
-                const size_t lin = ((size_t)s * npairs + pair) * groups + g;
-                v += part[lin * (FT * FT) + (size_t)(sr + r) * FT + (sc + col)];
-            }
-            sub[r][col] = v;
-            const int64_t a = (int64_t)ta * FT + sr + r, b = (int64_t)tb * FT + sc + col;
-            if (a < d_in && b < d_in && (ta < tb || a <= b)) {
-                float* dst = Fg + a * d_in + b;
-                *dst = accumulate ? *dst + v : v;
-            }
+    float4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < nsplit; ++s) {
+        const size_t lin = ((size_t)s * npairs + pair) * groups + g;
+        const float* P = part + lin * (FT * FT) + (size_t)sr * FT + sc + c4;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float4 x = *(const float4*)(P + (size_t)((tid >> 4) + 16 * k) * FT);
+            v[k].x += x.x; v[k].y += x.y; v[k].z += x.z; v[k].w += x.w;
         }
-        __syncthreads();
-        // mirror write F[b][a]
-        const int rr = tid & 63;
-#pragma unroll 4
-        for (int k = 0; k < 16; ++k) {
-            const int cc = (tid >> 6) + 4 * k;
-            const int64_t a = (int64_t)ta * FT + sr + rr, b = (int64_t)tb * FT + sc + cc;
-            if (a < d_in && b < d_in && (ta < tb || a < b)) {
-                float v = sub[rr][cc];
-                float* dst = Fg + b * d_in + a;
-                *dst = accumulate ? *dst + v : v;
+    }
+    const bool diag = (ta == tb) && (sr == sc);      // a <= b needed per element
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int r = (tid >> 4) + 16 * k;
+        sub[r][c4] = v[k].x; sub[r][c4 + 1] = v[k].y; sub[r][c4 + 2] = v[k].z; sub[r][c4 + 3] = v[k].w;
+        const int64_t a = a0 + r, b = b0 + c4;
+        if (a >= d_in || b >= d_in) continue;        // d_in % 8 == 0: b + 3 < d_in too
+        float* dst = Fg + a * d_in + b;
+        if (!diag) {
+            float4 o = v[k];
+            if (accumulate) {
+                const float4 y = *(const float4*)dst;
+                o.x += y.x; o.y += y.y; o.z += y.z; o.w += y.w;
             }
+            *(float4*)dst = o;
+        } else {
+            const float e[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (a <= b + q) dst[q] = accumulate ? dst[q] + e[q] : e[q];
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    // mirror: F[b][a] for a < b
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int rb = (tid >> 4) + 16 * k;         // b offset
+        const int64_t b = b0 + rb, a = a0 + c4;
+        if (a >= d_in || b >= d_in) continue;
+        float* dst = Fg + b * d_in + a;
+        const float e[4] = {sub[c4][rb], sub[c4 + 1][rb], sub[c4 + 2][rb], sub[c4 + 3][rb]};
+        if (!diag) {
+            float4 o = make_float4(e[0], e[1], e[2], e[3]);
+            if (accumulate) {
+                const float4 y = *(const float4*)dst;
+                o.x += y.x; o.y += y.y; o.z += y.z; o.w += y.w;
+            }
+            *(float4*)dst = o;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (a + q < b) dst[q] = accumulate ? dst[q] + e[q] : e[q];
+        }
     }
 }
 
@@ -331,55 +417,73 @@ __global__ __launch_bounds__(256) void k_fisher_plain(const void* __restrict__ X
 // ---------------------------------------------------------------------------
 struct FisherPlan {
     bool mfma;
+    int64_t n;                 // tokens per pass (the call's n, or the pass limit)
+    int64_t n_pad, d_pad;
     int T, npairs, nsplit;
     int64_t ksplit;
     int total, grid;
-    size_t part_bytes;
+    size_t s_bytes, xt_bytes, yt_bytes, part_bytes;
 };
 
-FisherPlan fisher_plan(int64_t n, int64_t d_in, int groups, bool bf16) {
+// The packed operands take (1 + groups) * d_pad * n_pad * 2 bytes.  Token ranges
+// whose packed operands would exceed this budget run as several passes, each
+// adding into F.
+constexpr size_t F_PACK_BUDGET = (size_t)16 << 30;
+
+static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+FisherPlan fisher_plan(int64_t n_call, int64_t d_in, int groups, bool bf16,
+                       int max_split = 16) {
     FisherPlan p{};
     p.mfma = bf16 && (d_in % 8 == 0);
+    {
+        const int64_t d_pad = (d_in + FT - 1) / FT * FT;
+        int64_t cap = (int64_t)(F_PACK_BUDGET / ((size_t)(1 + groups) * d_pad * 2)) / PK * PK;
+        if (cap < PK) cap = PK;
+        p.n = (bf16 && d_in % 8 == 0 && n_call > cap) ? cap : n_call;
+    }
+    p.s_bytes = al256((size_t)groups * p.n * sizeof(float));
     if (!p.mfma) return p;
+    p.n_pad = (p.n + PK - 1) / PK * PK;            // the packing tile
     p.T = (int)((d_in + FT - 1) / FT);
+    p.d_pad = (int64_t)p.T * FT;
     p.npairs = p.T * (p.T + 1) / 2;
     const int tiles = p.npairs * groups;
-    const int slots = 256;  // one 144 KB block per CU
+    const int slots = 256;  // one 128 KB block per CU
     // model: time ~ ceil(tiles*s/slots) * (n/s) + s * tiles * finalize_cost
     double best = 1e300;
     int best_s = 1;
-    for (int s = 1; s <= 16; ++s) {
-        const int64_t chunk = ((n + s - 1) / s + FKC - 1) / FKC * FKC;
+    for (int s = 1; s <= max_split; ++s) {
+        const int64_t chunk = ((p.n_pad + s - 1) / s + FKC - 1) / FKC * FKC;
         if (s > 1 && chunk < 2048) break;
         const double rounds = (double)((tiles * (int64_t)s + slots - 1) / slots);
-        // one token-step of a 256x256 block costs ~ 131072 flop; one partial tile
-        // read+write in the finalize ~ 256 KB at ~5 TB/s
+        // one token-step of a 256x256 block costs 131072 flop at ~60 % of a CU's
+        // bf16 peak; one partial tile read + write in the finalize ~256 KB at ~5 TB/s
         const double t_main = rounds * (double)chunk * 131072.0 / (9.77e12 * 0.6);
         const double t_fin = (double)s * tiles * 262144.0 / 5e12;
         const double t = t_main + t_fin;
         if (t < best * 0.999) { best = t; best_s = s; }
     }
     p.nsplit = best_s;
-    p.ksplit = ((n + best_s - 1) / best_s + FKC - 1) / FKC * FKC;
+    p.ksplit = ((p.n_pad + best_s - 1) / best_s + FKC - 1) / FKC * FKC;
     p.total = tiles * p.nsplit;
     p.grid = (p.total + 7) / 8 * 8;
+    p.xt_bytes = al256((size_t)p.d_pad * p.n_pad * 2);
+    p.yt_bytes = al256((size_t)groups * p.d_pad * p.n_pad * 2);
     p.part_bytes = (size_t)p.total * FT * FT * sizeof(float);
     return p;
 }
 
 size_t fisher_workspace(int64_t n, int64_t d_in, int groups, bool bf16) {
     FisherPlan p = fisher_plan(n, d_in, groups, bf16);
-    size_t s_bytes = ((size_t)groups * n * sizeof(float) + 255) / 256 * 256;
-    return s_bytes + (p.mfma ? p.part_bytes : 0);
+    return p.s_bytes + (p.mfma ? p.xt_bytes + p.yt_bytes + p.part_bytes : 0);
 }
 
-hipError_t fisher_run(const void* X, const void* G, bool bf16, int64_t n, int64_t d_in,
-                      int64_t d_out, int groups, float* F, int accumulate, void* ws,
-                      hipStream_t st) {
-    FisherPlan p = fisher_plan(n, d_in, groups, bf16);
+static hipError_t fisher_pass(const FisherPlan& p, const void* X, const void* G, bool bf16,
+                              int64_t n, int64_t d_in, int64_t d_out, int groups, float* F,
+                              int accumulate, void* ws, hipStream_t st) {
     float* S = (float*)ws;
-    size_t s_bytes = ((size_t)groups * n * sizeof(float) + 255) / 256 * 256;
-    float* part = (float*)((char*)ws + s_bytes);
+    char* w = (char*)ws + p.s_bytes;
     dim3 gs((unsigned)((n + 3) / 4), (unsigned)groups);
     {
         StageTimer tm(ST_GROUP_SCALE, st);
@@ -390,6 +494,10 @@ hipError_t fisher_run(const void* X, const void* G, bool bf16, int64_t n, int64_
         GQ_LAUNCH_CHECK();
     }
     if (p.mfma) {
+        uint16_t* XT = (uint16_t*)w;
+        uint16_t* YT = (uint16_t*)(w + p.xt_bytes);
+        float* part = (float*)(w + p.xt_bytes + p.yt_bytes);
+        const int64_t n_pad = (n + PK - 1) / PK * PK;
         static bool attr_set = false;
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute((const void*)k_fisher_mfma,
@@ -399,15 +507,24 @@ hipError_t fisher_run(const void* X, const void* G, bool bf16, int64_t n, int64_
             attr_set = true;
         }
         {
+            StageTimer tm(ST_FISHER_PACK, st);
+            dim3 gp((unsigned)(n_pad / PK), (unsigned)(p.d_pad / PK));
+            hipLaunchKernelGGL(k_fisher_pack, gp, dim3(256), 0, st, (const uint16_t*)X, S, n,
+                               n_pad, d_in, p.d_pad, groups, XT, YT);
+            GQ_LAUNCH_CHECK();
+        }
+        // the split plan of this pass's token count (no more partial tiles than the
+        // workspace holds)
+        const FisherPlan q = fisher_plan(n, d_in, groups, bf16, p.nsplit);
+        {
             StageTimer tm(ST_FISHER_MFMA, st);
-            hipLaunchKernelGGL(k_fisher_mfma, dim3(p.grid), dim3(256), F_LDS_BYTES, st,
-                               (const uint16_t*)X, S, n, d_in, groups, p.T, p.npairs, p.nsplit,
-                               p.ksplit, p.total, part);
+            hipLaunchKernelGGL(k_fisher_mfma, dim3(q.grid), dim3(256), F_LDS_BYTES, st, XT, YT,
+                               n_pad, q.d_pad, groups, q.T, q.npairs, q.ksplit, q.total, part);
             GQ_LAUNCH_CHECK();
         }
         StageTimer tm(ST_FISHER_FINALIZE, st);
-        hipLaunchKernelGGL(k_fisher_finalize, dim3(p.npairs, groups), dim3(256), 0, st, part,
-                           d_in, groups, p.T, p.npairs, p.nsplit, accumulate, F);
+        hipLaunchKernelGGL(k_fisher_finalize, dim3(q.npairs * 16, groups), dim3(256), 0, st, part,
+                           d_in, groups, q.T, q.npairs, q.nsplit, accumulate, F);
         GQ_LAUNCH_CHECK();
     } else {
         dim3 gp((unsigned)((d_in + 15) / 16), (unsigned)((d_in + 15) / 16), (unsigned)groups);
@@ -419,6 +536,21 @@ hipError_t fisher_run(const void* X, const void* G, bool bf16, int64_t n, int64_
             hipLaunchKernelGGL(k_fisher_plain<false>, gp, dim3(256), 0, st, X, S, n, d_in,
                                accumulate, F);
         GQ_LAUNCH_CHECK();
+    }
+    return hipSuccess;
+}
+
+hipError_t fisher_run(const void* X, const void* G, bool bf16, int64_t n, int64_t d_in,
+                      int64_t d_out, int groups, float* F, int accumulate, void* ws,
+                      hipStream_t st) {
+    const FisherPlan p = fisher_plan(n, d_in, groups, bf16);
+    const size_t esz = bf16 ? 2 : 4;
+    for (int64_t t0 = 0; t0 < n; t0 += p.n) {
+        const int64_t nt = (n - t0) < p.n ? (n - t0) : p.n;
+        hipError_t e = fisher_pass(p, (const char*)X + (size_t)t0 * d_in * esz,
+                                   (const char*)G + (size_t)t0 * d_out * esz, bf16, nt, d_in,
+                                   d_out, groups, F, (t0 > 0) ? 1 : accumulate, ws, st);
+        if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }

@@ -115,5 +115,5 @@ def test_timing_read_empty():
     t = gq.gq_timing_read()
     assert set(t) == {"group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain",
                       "lnq_prepare", "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep",
-                      "lnq_small"}
+                      "lnq_small", "fisher_pack"}
     assert all(v == (0.0, 0) for v in t.values())
