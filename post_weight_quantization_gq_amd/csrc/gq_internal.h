@@ -34,16 +34,22 @@ hipError_t fisher_run(const void* X, const void* G, bool bf16, int64_t n, int64_
                       hipStream_t st);
 
 // ---- LNQ (gq_lnq.hip, gq_lnq_mm.hip)
+// The bf16 planes of F' ([groups][d / 16][a_pad][16]) and of E = C[P] - W
+// ([d / 16][groups * rpg_pad][16]) are blocked by 16 along k: element (row, k) of a
+// plane with `rows` rows sits at ((k / 16) * rows + row) * 16 + k % 16.  Rows are
+// padded with zeros to whole 256-row tiles.
+__host__ __device__ inline int64_t lnq_pad256(int64_t x) { return (x + 255) / 256 * 256; }
+
 struct LnqSizes {
     size_t o_fhi, o_flo, o_dF, o_lam, o_R, o_ehi, o_elo, o_part;
     size_t o_objA, o_objB, o_objC, o_cnt, total;
 };
 struct LnqWs {
-    uint16_t *fhi, *flo;          // F' planes [groups][d][d]
+    uint16_t *fhi, *flo;          // F' planes, k-blocked: [groups][d / 16][a_pad][16]
     float* dF;                    // diag F' [groups][d]
     double* lam;                  // [groups]
     float* R;                     // residual F'(C[P] - W) [d_out][d]
-    uint16_t *ehi, *elo;          // C[P] - W as bf16 planes; the sweep's value changes
+    uint16_t *ehi, *elo;          // C[P] - W as k-blocked bf16 planes [d / 16][groups * rpg_pad][16]
     float* part;                  // Gram partials [d / 256][d_out * m][m]
     double *objA, *objB, *objC;   // per-row objectives [d_out]
     unsigned long long* cnt;      // counters [16]

@@ -49,41 +49,52 @@ __global__ __launch_bounds__(256) void k_ridge(const float* __restrict__ F, int6
 }
 
 // ---------------------------------------------------------------------------
-// F' = F + lambda I -> bf16 planes (hi, lo) and float32 diagonal.  8 elems / thread.
+// F' = F + lambda I -> k-blocked bf16 planes (hi, lo) and float32 diagonal.  One
+// thread per (group, 16-block of k, row a of the padded plane): 16 elements of
+// row a (zeros for padding rows), written as 32 contiguous bytes per plane.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_split(const float* __restrict__ F, int64_t d,
-                                              const double* __restrict__ lam,
+                                              int64_t a_pad, const double* __restrict__ lam,
                                               uint16_t* __restrict__ hi_plane,
                                               uint16_t* __restrict__ lo_plane,
-                                              float* __restrict__ dF, int64_t total8) {
-    const int64_t idx8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx8 >= total8) return;
-    const int64_t e0 = idx8 * 8;
-    const int64_t dd = d * d;
-    const int64_t g = e0 / dd;
-    const int64_t rem = e0 - g * dd;
-    const int64_t a = rem / d;
-    const int64_t i0 = rem - a * d;       // d % 8 == 0: the 8 elements share a row
-    const float4* src = (const float4*)(F + e0);
-    float4 x0 = src[0], x1 = src[1];
-    float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    if (a >= i0 && a < i0 + 8) {
-        const int k = (int)(a - i0);
-        v[k] = (float)((double)v[k] + lam[g]);
-        dF[g * d + a] = v[k];
-    }
-    u32x4 h, l;
+                                              float* __restrict__ dF, int64_t total) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int64_t nkb = d / 16;
+    const int64_t a = idx % a_pad;
+    const int64_t kb = (idx / a_pad) % nkb;
+    const int64_t g = idx / (a_pad * nkb);
+    float v[16];
+    if (a < d) {
+        const float4* src = (const float4*)(F + (g * d + a) * d + kb * 16);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float f0 = v[2 * k], f1 = v[2 * k + 1];
-        uint32_t hb = pack_bf16x2(f0, f1);
-        float r0 = f0 - __uint_as_float(hb << 16);
-        float r1 = f1 - __uint_as_float(hb & 0xffff0000u);
-        h[k] = hb;
-        l[k] = pack_bf16x2(r0, r1);
+        for (int k = 0; k < 4; ++k) {
+            const float4 x = src[k];
+            v[4 * k] = x.x; v[4 * k + 1] = x.y; v[4 * k + 2] = x.z; v[4 * k + 3] = x.w;
+        }
+        if (a >= kb * 16 && a < kb * 16 + 16) {
+            const int k = (int)(a - kb * 16);
+            v[k] = (float)((double)v[k] + lam[g]);
+            dF[g * d + a] = v[k];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = 0.f;
     }
-    *(u32x4*)(hi_plane + e0) = h;
-    *(u32x4*)(lo_plane + e0) = l;
+    u32x4 h[2], l[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float f0 = v[2 * k], f1 = v[2 * k + 1];
+        const uint32_t hb = pack_bf16x2(f0, f1);
+        h[k >> 2][k & 3] = hb;
+        l[k >> 2][k & 3] = pack_bf16x2(f0 - __uint_as_float(hb << 16),
+                                       f1 - __uint_as_float(hb & 0xffff0000u));
+    }
+    const int64_t off = ((g * nkb + kb) * a_pad + a) * 16;
+    *(u32x4*)(hi_plane + off) = h[0];
+    *(u32x4*)(hi_plane + off + 8) = h[1];
+    *(u32x4*)(lo_plane + off) = l[0];
+    *(u32x4*)(lo_plane + off + 8) = l[1];
 }
 
 // ---------------------------------------------------------------------------
@@ -149,48 +160,63 @@ __global__ __launch_bounds__(1024) void k_lnq_init(const void* __restrict__ W, i
 }
 
 // ---------------------------------------------------------------------------
-// E = C[j][P[j][i]] - W[j][i] (float32) -> bf16 planes hi + lo.  8 elements per
-// thread (d % 8 == 0, so they share a row).
+// E = C[j][P[j][i]] - W[j][i] (float32) -> k-blocked bf16 planes hi + lo.  One
+// thread per (16-block of k, padded row): 16 elements, 32 contiguous bytes per
+// plane; padding rows (past a group's rows) are zero.
 // ---------------------------------------------------------------------------
 template <bool WBF16>
 __global__ __launch_bounds__(256) void k_err_split(const float* __restrict__ C, int m,
                                                   const uint8_t* __restrict__ P,
                                                   const void* __restrict__ W, int64_t d,
+                                                  int64_t rpg, int64_t rpg_pad, int64_t erows,
                                                   uint16_t* __restrict__ Ehi,
-                                                  uint16_t* __restrict__ Elo, int64_t total8) {
-    const int64_t idx8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx8 >= total8) return;
-    const int64_t e0 = idx8 * 8;
-    const int64_t j = e0 / d;
-    const float* cj = C + j * m;
-    const u32x2 pc = *(const u32x2*)(P + e0);
-    float w[8];
-    if constexpr (WBF16) {
-        const u32x4 wv = *(const u32x4*)((const uint16_t*)W + e0);
+                                                  uint16_t* __restrict__ Elo, int64_t total) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int64_t rowp = idx % erows;
+    const int64_t kb = idx / erows;
+    const int64_t g = rowp / rpg_pad, jl = rowp - g * rpg_pad;
+    u32x4 h[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}}, l[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    if (jl < rpg) {
+        const int64_t j = g * rpg + jl;
+        const int64_t e0 = j * d + kb * 16;
+        const float* cj = C + j * m;
+        const u32x4 pc = *(const u32x4*)(P + e0);
+        float w[16];
+        if constexpr (WBF16) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            w[2 * k] = __uint_as_float(wv[k] << 16);
-            w[2 * k + 1] = __uint_as_float(wv[k] & 0xffff0000u);
+            for (int hh = 0; hh < 2; ++hh) {
+                const u32x4 wv = *(const u32x4*)((const uint16_t*)W + e0 + 8 * hh);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    w[8 * hh + 2 * k] = __uint_as_float(wv[k] << 16);
+                    w[8 * hh + 2 * k + 1] = __uint_as_float(wv[k] & 0xffff0000u);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float4 x = *(const float4*)((const float*)W + e0 + 4 * k);
+                w[4 * k] = x.x; w[4 * k + 1] = x.y; w[4 * k + 2] = x.z; w[4 * k + 3] = x.w;
+            }
         }
-    } else {
-        const float4 a = *(const float4*)((const float*)W + e0);
-        const float4 b = *(const float4*)((const float*)W + e0 + 4);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    }
-    u32x4 h, l;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t c0 = (pc[k >> 1] >> (16 * (k & 1))) & 0xffu;
-        const uint32_t c1 = (pc[k >> 1] >> (16 * (k & 1) + 8)) & 0xffu;
-        const float x0 = cj[c0 < (uint32_t)m ? c0 : 0] - w[2 * k];
-        const float x1 = cj[c1 < (uint32_t)m ? c1 : 0] - w[2 * k + 1];
-        const uint32_t hb = pack_bf16x2(x0, x1);
-        h[k] = hb;
-        l[k] = pack_bf16x2(x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u));
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t c0 = (pc[k >> 1] >> (16 * (k & 1))) & 0xffu;
+            const uint32_t c1 = (pc[k >> 1] >> (16 * (k & 1) + 8)) & 0xffu;
+            const float x0 = cj[c0 < (uint32_t)m ? c0 : 0] - w[2 * k];
+            const float x1 = cj[c1 < (uint32_t)m ? c1 : 0] - w[2 * k + 1];
+            const uint32_t hb = pack_bf16x2(x0, x1);
+            h[k >> 2][k & 3] = hb;
+            l[k >> 2][k & 3] = pack_bf16x2(x0 - __uint_as_float(hb << 16),
+                                           x1 - __uint_as_float(hb & 0xffff0000u));
+        }
     }
-    *(u32x4*)(Ehi + e0) = h;
-    *(u32x4*)(Elo + e0) = l;
+    const int64_t off = (kb * erows + rowp) * 16;
+    *(u32x4*)(Ehi + off) = h[0];
+    *(u32x4*)(Ehi + off + 8) = h[1];
+    *(u32x4*)(Elo + off) = l[0];
+    *(u32x4*)(Elo + off + 8) = l[1];
 }
 
 // ---------------------------------------------------------------------------
@@ -405,8 +431,16 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
 
     const float* Fg = F + (size_t)g * d * d;
     const float* dFg = dF + (size_t)g * d;
-    const uint16_t* Fh = Fhi + (size_t)g * d * d;
-    const uint16_t* Fl = Flo + (size_t)g * d * d;
+    // k-blocked F' planes: element (a, k) at ((k / 16) * a_pad + a) * 16 + k % 16; the
+    // 8 elements (a, k .. k + 7) with k % 8 == 0 are contiguous, and k + 32 is
+    // 32 * a_pad elements further on
+    const int64_t a_pad = lnq_pad256(d);
+    const uint16_t* Fh = Fhi + (size_t)g * d * a_pad;
+    const uint16_t* Fl = Flo + (size_t)g * d * a_pad;
+    const uint32_t kstep32 = (uint32_t)(32 * a_pad);        // < 2^31 for d <= 32768
+    auto plane_at = [&](const uint16_t* base, int64_t a, int64_t k) {
+        return base + ((k >> 4) * a_pad + a) * 16 + (k & 15);
+    };
 
     const float cl = (lane < m && rvalid) ? C[j * m + lane] : 0.f;   // candidate of this lane
     double dsum = 0.0;       // sum of the accepted changes (uniform in the wave)
@@ -438,12 +472,12 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
                 const int ct = wave & 3, sl = wave >> 2;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 const int64_t fcol = bs + ct * 16 + mrow;
-                const uint16_t* Fh_c = Fh + fcol * d + sb0 + ko;
-                const uint16_t* Fl_c = Fl + fcol * d + sb0 + ko;
+                const uint16_t* Fh_c = plane_at(Fh, fcol, sb0 + ko);
+                const uint16_t* Fl_c = plane_at(Fl, fcol, sb0 + ko);
                 for (int c = sl; c < o / 32; c += 4) {
                     if (__builtin_amdgcn_readfirstlane((int)chunk_moved[c]) == 0) continue;
-                    const u32x4 fh = *(const u32x4*)(Fh_c + c * 32);
-                    const u32x4 fl = *(const u32x4*)(Fl_c + c * 32);
+                    const u32x4 fh = *(const u32x4*)(Fh_c + (uint32_t)c * kstep32);
+                    const u32x4 fl = *(const u32x4*)(Fl_c + (uint32_t)c * kstep32);
                     const u32x4 dh = *(const u32x4*)(&dsb_hi[mrow][c * 32 + ko]);
                     const u32x4 dl = *(const u32x4*)(&dsb_lo[mrow][c * 32 + ko]);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fh), acc, 0, 0, 0);
@@ -523,8 +557,8 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
         mv = __builtin_amdgcn_readfirstlane(mv);
         for (int ctile = wave; ctile < ntiles; ctile += SW_ROWS) {
             const int64_t fcol = sb_end + (int64_t)ctile * 16 + mrow;
-            const uint16_t* Fh_c = Fh + fcol * d + sb0 + ko;
-            const uint16_t* Fl_c = Fl + fcol * d + sb0 + ko;
+            const uint16_t* Fh_c = plane_at(Fh, fcol, sb0 + ko);
+            const uint16_t* Fl_c = plane_at(Fl, fcol, sb0 + ko);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int c0 = 0; c0 < nch; c0 += SW_RB) {
                 u32x4 fh[SW_RB], fl[SW_RB];
@@ -532,8 +566,8 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
                 for (int u = 0; u < SW_RB; ++u) {
                     const int c = c0 + u;
                     if (c < nch && ((mv >> c) & 1u)) {
-                        fh[u] = *(const u32x4*)(Fh_c + c * 32);
-                        fl[u] = *(const u32x4*)(Fl_c + c * 32);
+                        fh[u] = *(const u32x4*)(Fh_c + (uint32_t)c * kstep32);
+                        fl[u] = *(const u32x4*)(Fl_c + (uint32_t)c * kstep32);
                     }
                 }
 #pragma unroll
@@ -607,13 +641,14 @@ LnqSizes lnq_sizes(int64_t d_out, int64_t d, int groups, int m) {
     LnqSizes z{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-    z.o_fhi = take((size_t)groups * d * d * 2);
-    z.o_flo = take((size_t)groups * d * d * 2);
+    const int64_t a_pad = lnq_pad256(d), rpg_pad = lnq_pad256(d_out / groups);
+    z.o_fhi = take((size_t)groups * d * a_pad * 2);
+    z.o_flo = take((size_t)groups * d * a_pad * 2);
     z.o_dF = take((size_t)groups * d * 4);
     z.o_lam = take((size_t)groups * 8);
     z.o_R = take((size_t)d_out * d * 4);
-    z.o_ehi = take((size_t)d_out * d * 2);
-    z.o_elo = take((size_t)d_out * d * 2);
+    z.o_ehi = take((size_t)groups * rpg_pad * d * 2);
+    z.o_elo = take((size_t)groups * rpg_pad * d * 2);
     z.o_part = take(lnq_gram_partial_floats(d_out, d, m) * 4);
     z.o_objA = take((size_t)d_out * 8);
     z.o_objB = take((size_t)d_out * 8);
@@ -646,9 +681,10 @@ hipError_t lnq_prepare(const float* F, int groups, int64_t d, double rho, const 
     StageTimer tm(ST_LNQ_PREPARE, st);
     hipLaunchKernelGGL(k_ridge, dim3(groups), dim3(256), 0, st, F, d, rho, w.lam);
     GQ_LAUNCH_CHECK();
-    const int64_t total8 = (int64_t)groups * d * d / 8;
-    hipLaunchKernelGGL(k_split, dim3((unsigned)((total8 + 255) / 256)), dim3(256), 0, st, F, d,
-                       w.lam, w.fhi, w.flo, w.dF, total8);
+    const int64_t a_pad = lnq_pad256(d);
+    const int64_t total = (int64_t)groups * (d / 16) * a_pad;
+    hipLaunchKernelGGL(k_split, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, F, d,
+                       a_pad, w.lam, w.fhi, w.flo, w.dF, total);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }
@@ -681,14 +717,16 @@ hipError_t lnq_residual_from(const float* C, int m, const uint8_t* P, const void
                              hipStream_t st) {
     {
         StageTimer tm(ST_LNQ_RESID, st);
-        const int64_t total8 = d_out * d / 8;
-        const dim3 grid((unsigned)((total8 + 255) / 256));
+        const int64_t rpg = d_out / groups, rpg_pad = lnq_pad256(rpg);
+        const int64_t erows = (int64_t)groups * rpg_pad;
+        const int64_t total = erows * (d / 16);
+        const dim3 grid((unsigned)((total + 255) / 256));
         if (w_bf16)
-            hipLaunchKernelGGL(k_err_split<true>, grid, dim3(256), 0, st, C, m, P, W, d, w.ehi,
-                               w.elo, total8);
+            hipLaunchKernelGGL(k_err_split<true>, grid, dim3(256), 0, st, C, m, P, W, d, rpg,
+                               rpg_pad, erows, w.ehi, w.elo, total);
         else
-            hipLaunchKernelGGL(k_err_split<false>, grid, dim3(256), 0, st, C, m, P, W, d, w.ehi,
-                               w.elo, total8);
+            hipLaunchKernelGGL(k_err_split<false>, grid, dim3(256), 0, st, C, m, P, W, d, rpg,
+                               rpg_pad, erows, w.ehi, w.elo, total);
         GQ_LAUNCH_CHECK();
     }
     return lnq_residual(w.ehi, w.elo, d_out, d, groups, w.fhi, w.flo, w.R, st);

@@ -6,41 +6,42 @@
 // residual r_j = F'(w_hat_j - w_j).  Two products over all rows of a group do
 // the dense work:
 //
-//   MM_RESID  R[j][a] = sum_i E[j][i] F'[a][i],  E = C[P] - W split into bf16
-//             hi + lo planes, F' as bf16 hi + lo planes; three products
-//             (Ehi Fhi + Ehi Flo + Elo Fhi) give float32-level accuracy.
-//   MM_GRAM   A_j = P_j^T F' P_j.  With the one-hot P_j built from the codes in
-//             registers (exact in bf16) the kernel forms
-//                 T[a][(j,q)] = sum_{i >= tile(a)} F'[a][i] [P[j][i] == q]
-//             over the upper-triangle tiles of F' only (the diagonal tile at
-//             half weight), and the epilogue bins T by the code of coordinate a:
-//                 B_j[q'][q] += sum_a [P[j][a] == q'] T[a][(j,q)].
-//             Then A_j = B_j + B_j^T (by the symmetry of F').  Per-a-tile
-//             partials are written in a fixed layout and summed in a fixed order.
+//   k_resid  R[j][a] = sum_i E[j][i] F'[a][i],  E = C[P] - W split into bf16
+//            hi + lo planes, F' as bf16 hi + lo planes; three products
+//            (Ehi Fhi + Ehi Flo + Elo Fhi) give float32-level accuracy.
+//   k_gram   A_j = P_j^T F' P_j.  With the one-hot P_j (exact in bf16) the kernel
+//            forms
+//                T[a][(j,q)] = sum_{i >= tile(a)} F'[a][i] [P[j][i] == q]
+//            over the upper-triangle tiles of F' only (the diagonal tile at half
+//            weight), and the epilogue bins T by the code of coordinate a:
+//                B_j[q'][q] += sum_a [P[j][a] == q'] T[a][(j,q)].
+//            Then A_j = B_j + B_j^T (by the symmetry of F').  Per-a-tile partials
+//            are written in a fixed layout and summed in a fixed order.
 //
-// Block tile 256 x 256, 4 waves of 128 x 128 as 4 x 4 v_mfma_f32_32x32x16_bf16
-// tiles, k staged 32 at a time through LDS (80-byte rows), register prefetch of
-// the next stage while the current one is multiplied.
+// Both operands live in k-blocked bf16 planes (element (row, k) at
+// ((k / 16) * rows + row) * 16 + k % 16, rows padded to whole 256-row tiles), so
+// one 16-deep stage of a 256-row band is 8 KB of contiguous memory.  Block tile
+// 256 x 256, 4 waves of 128 x 128 as 4 x 4 v_mfma_f32_32x32x16_bf16 tiles.  The
+// stages go through a ring of 4 LDS stages filled by direct buffer-to-LDS loads
+// three stages ahead; a 32-byte operand row sits in two 16-byte slots, chunk c
+// of row r in slot 2 r + (c ^ ((r >> 3) & 1)), so each quarter-wave fragment
+// read (16 consecutive rows) touches 16 distinct bank groups.  The one-hot
+// operand of k_gram is built once per stage into LDS, one stage ahead.
 #include "gq_common.h"
 #include "gq_internal.h"
 
 namespace gq {
 
-constexpr int MT = 256;        // block tile edge
-constexpr int MKC = 32;        // k per LDS stage
-constexpr int MPITCH = 40;     // bf16 per staged row
-constexpr int M_PLANE = MT * MPITCH;
-constexpr int MM_RESID = 0, MM_GRAM = 1;
+constexpr int MT = 256;                 // block tile edge
+constexpr int MRING = 4;                // LDS stages in the ring
+constexpr int M_SLOTS = MT * 2;         // 16-byte slots of one 256-row, 16-deep operand band
 
-template <int MODE>
-constexpr int mm_stage_elems() {
-    // RESID: Ehi, Elo, Fhi, Flo planes.  GRAM: Fhi, Flo planes + up to 128 rows x 32 code bytes.
-    return MODE == MM_RESID ? 4 * M_PLANE : 2 * M_PLANE + (128 * 32) / 2;
-}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int MODE>
-constexpr size_t mm_lds_bytes() {
-    return (size_t)2 * mm_stage_elems<MODE>() * sizeof(uint16_t);
+template <int N>
+__device__ __forceinline__ void mm_wait_vmcnt() {
+    // vmcnt(N), and lgkmcnt(0): the LDS writes of this wave are done too
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
 // Hardware block h -> logical block: within each round of 256 blocks, XCD x
@@ -49,39 +50,69 @@ __device__ __forceinline__ int mm_remap(int hw) {
     return (hw & ~255) + (hw & 7) * 32 + ((hw & 255) >> 3);
 }
 
-template <int MODE, int M>
-__global__ __launch_bounds__(256, 1) void k_mm(
-    const uint16_t* __restrict__ Ehi, const uint16_t* __restrict__ Elo,
-    const uint8_t* __restrict__ codes, int64_t rpg, int g_first, int g_count,
-    const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo, int64_t d,
-    int ntile_n, int ntile_a, int total, float* __restrict__ out, int64_t d_out) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t mm_lds[];
-    constexpr int STAGE = mm_stage_elems<MODE>();
+// Buffer descriptor on one stage of a 256-row band (8 KB).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t band_rsrc(const uint16_t* p) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, M_SLOTS * 16, 0x00020000);
+}
+
+// Copy one stage of a 256-row band (rows of 32 bytes) into 512 LDS slots: wave w
+// issues instructions q = 2w, 2w + 1, each filling rows 32q .. 32q + 31; lane L
+// takes row 32q + L/2 and slot L%2, i.e. chunk (L%2) ^ ((L/16)%2).
+__device__ __forceinline__ void band_to_lds(__amdgpu_buffer_rsrc_t r, u32x4* dst, int wave,
+                                            uint32_t voff) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = 2 * wave + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 64 * q), 16, voff,
+                                                 (uint32_t)q * 1024u, 0, 0);
+    }
+}
+
+__device__ __forceinline__ uint32_t band_voff(int lane) {
+    return (uint32_t)(lane >> 1) * 32u + 16u * (uint32_t)((lane & 1) ^ ((lane >> 4) & 1));
+}
+
+// fragment slot of row `row` (its low 5 bits from the lane) for a 16-deep k-step
+__device__ __forceinline__ int frag_slot(int row, int lane) {
+    return row * 2 + ((lane >> 5) ^ ((lane >> 3) & 1));
+}
+
+// ---------------------------------------------------------------------------
+// R = E F'.  Tile (256 rows j of a group) x (256 coordinates a).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_resid(
+    const uint16_t* __restrict__ Ehi, const uint16_t* __restrict__ Elo, int64_t erows,
+    int64_t rpg_pad, const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo,
+    int64_t a_pad, int64_t d, int64_t rpg, int ntn, int nta, int total, float* __restrict__ R) {
+    extern __shared__ u32x4 mm_lds[];
     const int lin = mm_remap(blockIdx.x);
     if (lin >= total) return;
+    const int ta = lin % nta;
+    const int tn = (lin / nta) % ntn;
+    const int g = lin / (nta * ntn);
+    const int64_t a0 = (int64_t)ta * MT, n0 = (int64_t)tn * MT;
 
-    int tn, ta, gl;
-    if (MODE == MM_RESID) {
-        ta = lin % ntile_a;
-        tn = (lin / ntile_a) % ntile_n;
-        gl = lin / (ntile_a * ntile_n);
-    } else {
-        tn = lin % ntile_n;
-        gl = (lin / ntile_n) % g_count;
-        ta = lin / (ntile_n * g_count);
-    }
-    const int g = g_first + gl;
-    const int64_t a0 = (int64_t)ta * MT;
-    const int64_t n0 = (int64_t)tn * MT;
-    // number of valid rows of the "n" operand: RESID rows of E; GRAM (j, q) pairs
-    const int64_t N = (MODE == MM_RESID) ? rpg : rpg * M;
-    const int64_t row_base = (int64_t)g * rpg;           // first row j of the group
-    const uint16_t* Fh = Fhi + (size_t)g * d * d;
-    const uint16_t* Fl = Flo + (size_t)g * d * d;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int w0 = wave & 1, w1 = wave >> 1;
-    const int sr = tid >> 2, sq = tid & 3;
+    const uint32_t voff = band_voff(lane);
+
+    // stage s of each band: + s * (rows of the plane) * 16 elements
+    const uint16_t* Eh = Ehi + ((int64_t)g * rpg_pad + n0) * 16;
+    const uint16_t* El = Elo + ((int64_t)g * rpg_pad + n0) * 16;
+    const int64_t fg = (int64_t)g * d * a_pad;
+    const uint16_t* Fh = Fhi + fg + a0 * 16;
+    const uint16_t* Fl = Flo + fg + a0 * 16;
+    const int64_t estep = erows * 16, fstep = a_pad * 16;
+    const int nst = (int)(d / 16);
+
+    auto issue = [&](int s) {
+        u32x4* base = mm_lds + (s % MRING) * (4 * M_SLOTS);
+        band_to_lds(band_rsrc(Eh + s * estep), base, wave, voff);
+        band_to_lds(band_rsrc(El + s * estep), base + M_SLOTS, wave, voff);
+        band_to_lds(band_rsrc(Fh + s * fstep), base + 2 * M_SLOTS, wave, voff);
+        band_to_lds(band_rsrc(Fl + s * fstep), base + 3 * M_SLOTS, wave, voff);
+    };
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -91,231 +122,268 @@ __global__ __launch_bounds__(256, 1) void k_mm(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
 
-    const int64_t k_begin = (MODE == MM_GRAM) ? a0 : 0;
-    const int nk = (int)((d - k_begin + MKC - 1) / MKC);
-    const int ndiag = (MODE == MM_GRAM) ? (int)((((d - a0) < MT ? (d - a0) : MT) + MKC - 1) / MKC) : 0;
-
-    constexpr int NPL = (MODE == MM_RESID) ? 4 : 2;
-    u32x4 pf[NPL][4];
-    u32x4 pc = {0u, 0u, 0u, 0u};
-    const int jrows = MT / M;                 // GRAM: code rows per n tile
-
-    auto fetch = [&](int64_t k0) {
-        const int64_t kk = k0 + 8 * sq;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int r = sr + 64 * s;
-            if (MODE == MM_RESID) {
-                const int64_t nrow = n0 + r, arow = a0 + r;
-                const bool nok = nrow < N && kk < d, aok = arow < d && kk < d;
-                pf[0][s] = nok ? *(const u32x4*)(Ehi + (row_base + nrow) * d + kk) : z;
-                pf[1][s] = nok ? *(const u32x4*)(Elo + (row_base + nrow) * d + kk) : z;
-                pf[2][s] = aok ? *(const u32x4*)(Fh + arow * d + kk) : z;
-                pf[3][s] = aok ? *(const u32x4*)(Fl + arow * d + kk) : z;
-            } else {
-                const int64_t arow = a0 + r;
-                const bool aok = arow < d && kk < d;
-                pf[0][s] = aok ? *(const u32x4*)(Fh + arow * d + kk) : z;
-                pf[1][s] = aok ? *(const u32x4*)(Fl + arow * d + kk) : z;
-            }
-        }
-        if (MODE == MM_GRAM) {
-            // jrows rows x 32 code bytes: thread covers row tid/2, bytes 16*(tid%2)
-            const int r = tid >> 1;
-            const int64_t jl = n0 / M + r;
-            const int64_t kc = k0 + 16 * (tid & 1);
-            pc = (r < jrows && jl < rpg && kc < d)
-                     ? *(const u32x4*)(codes + (row_base + jl) * d + kc)
-                     : u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-        }
-    };
-    auto stage = [&](int buf) {
-        uint16_t* S = mm_lds + buf * STAGE;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int r = sr + 64 * s;
-#pragma unroll
-            for (int p = 0; p < NPL; ++p) *(u32x4*)(S + p * M_PLANE + r * MPITCH + 8 * sq) = pf[p][s];
-        }
-        if (MODE == MM_GRAM) {
-            uint8_t* cs = (uint8_t*)(S + 2 * M_PLANE);
-            *(u32x4*)(cs + (tid >> 1) * 32 + 16 * (tid & 1)) = pc;
-        }
-    };
-
-    fetch(k_begin);
-    stage(0);
-    __syncthreads();
-    for (int kc = 0; kc < nk; ++kc) {
-        const int buf = kc & 1;
-        const bool more = kc + 1 < nk;
-        if (more) fetch(k_begin + (int64_t)(kc + 1) * MKC);
-        const uint16_t* S = mm_lds + buf * STAGE;
-#pragma unroll
-        for (int ks = 0; ks < MKC / 16; ++ks) {
-            const int koff = ks * 16 + 8 * (lane >> 5);
-            if (MODE == MM_RESID) {
-                bf16x8 eh[4], el[4], fh[4], fl[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = (128 * w0 + 32 * i + (lane & 31)) * MPITCH + koff;
-                    eh[i] = as_bf16x8(*(const u32x4*)(S + rr));
-                    el[i] = as_bf16x8(*(const u32x4*)(S + M_PLANE + rr));
-                }
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int rr = (128 * w1 + 32 * jj + (lane & 31)) * MPITCH + koff;
-                    fh[jj] = as_bf16x8(*(const u32x4*)(S + 2 * M_PLANE + rr));
-                    fl[jj] = as_bf16x8(*(const u32x4*)(S + 3 * M_PLANE + rr));
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(eh[i], fh[jj], acc[i][jj], 0, 0, 0);
-                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(eh[i], fl[jj], acc[i][jj], 0, 0, 0);
-                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(el[i], fh[jj], acc[i][jj], 0, 0, 0);
-                    }
-            } else {
-                bf16x8 fh[4], fl[4], oh[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = (128 * w0 + 32 * i + (lane & 31)) * MPITCH + koff;
-                    fh[i] = as_bf16x8(*(const u32x4*)(S + rr));
-                    fl[i] = as_bf16x8(*(const u32x4*)(S + M_PLANE + rr));
-                }
-                const uint8_t* cs = (const uint8_t*)(S + 2 * M_PLANE);
-                // the diagonal tile enters B_j at half weight: one-hot value 0.5 (exact)
-                const uint32_t one = (kc < ndiag) ? 0x3F00u : 0x3F80u;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int nl = 128 * w1 + 32 * jj + (lane & 31);
-                    const int jr = nl / M, q = nl - jr * M;
-                    const u32x2 cv = *(const u32x2*)(cs + jr * 32 + koff);
-                    u32x4 o;
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        const uint32_t word = cv[h >> 1];
-                        const uint32_t b0 = (word >> (16 * (h & 1))) & 0xffu;
-                        const uint32_t b1 = (word >> (16 * (h & 1) + 8)) & 0xffu;
-                        o[h] = ((b0 == (uint32_t)q) ? one : 0u) | ((b1 == (uint32_t)q) ? (one << 16) : 0u);
-                    }
-                    oh[jj] = as_bf16x8(o);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[i], oh[jj], acc[i][jj], 0, 0, 0);
-                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[i], oh[jj], acc[i][jj], 0, 0, 0);
-                    }
-            }
-        }
-        if (more) stage(buf ^ 1);
-        __syncthreads();
+    {
+        const int pre = nst < MRING - 1 ? nst : MRING - 1;
+        for (int s = 0; s < pre; ++s) issue(s);
     }
-
-    if (MODE == MM_RESID) {
-        float* O = out + (size_t)row_base * d;
-        const int nrem = (int)((N - n0) < MT ? (N - n0) : MT);
-        const int arem = (int)((d - a0) < MT ? (d - a0) : MT);
+    int slot = 0;
+    for (int s = 0; s < nst; ++s) {
+        // 8 load instructions per stage and wave: stage s has landed once at most
+        // 8 x (later stages issued) are outstanding
+        const int newer = ((s + MRING - 2 < nst) ? s + MRING - 2 : nst - 1) - s;
+        if (newer >= 2) mm_wait_vmcnt<16>();
+        else if (newer == 1) mm_wait_vmcnt<8>();
+        else mm_wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (s + MRING - 1 < nst) issue(s + MRING - 1);
+        const u32x4* S = mm_lds + slot * (4 * M_SLOTS);
+        bf16x8 eh[4], el[4], fh[4], fl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int sl = frag_slot(128 * w0 + 32 * i + (lane & 31), lane);
+            eh[i] = as_bf16x8(S[sl]);
+            el[i] = as_bf16x8(S[M_SLOTS + sl]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int sl = frag_slot(128 * w1 + 32 * jj + (lane & 31), lane);
+            fh[jj] = as_bf16x8(S[2 * M_SLOTS + sl]);
+            fl[jj] = as_bf16x8(S[3 * M_SLOTS + sl]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int acol = 128 * w1 + 32 * jj + (lane & 31);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int nrow = 128 * w0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    if (nrow < nrem && acol < arem)
-                        O[(size_t)(n0 + nrow) * d + a0 + acol] = acc[i][jj][v];
-                }
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(eh[i], fh[jj], acc[i][jj], 0, 0, 0);
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(eh[i], fl[jj], acc[i][jj], 0, 0, 0);
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(el[i], fh[jj], acc[i][jj], 0, 0, 0);
             }
-    } else {
-        // ---- epilogue: bin T[a][(j,q)] by the code of coordinate a
-        // stage the codes of the block's rows for its 256 coordinates: jrows x 256 bytes
-        uint8_t* ctile = (uint8_t*)mm_lds;       // the stages are free after the last sync
-        for (int e = tid; e < jrows * (MT / 16); e += 256) {
-            const int r = e / (MT / 16), c16 = (e - r * (MT / 16)) * 16;
-            const int64_t jl = n0 / M + r;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (jl < rpg && a0 + c16 < d) v = *(const u32x4*)(codes + (row_base + jl) * d + a0 + c16);
-            *(u32x4*)(ctile + r * MT + c16) = v;
-        }
-        __syncthreads();
-        float* xch = (float*)(mm_lds + (MT / M) * MT / 2 + 64);   // after the code tile
-        const int arem = (int)((d - a0) < MT ? (d - a0) : MT);
+        __builtin_amdgcn_sched_barrier(0);
+        slot = (slot + 1 == MRING) ? 0 : slot + 1;
+    }
+
+    float* O = R + ((int64_t)g * rpg) * d;
+    const int nrem = (int)((rpg - n0) < MT ? (rpg - n0) : MT);
+    const int arem = (int)((d - a0) < MT ? (d - a0) : MT);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const int nl = 128 * w1 + 32 * jj + (lane & 31);
-            const int jr = nl / M, q = nl - jr * M;
-            float bins[M];
+            const int acol = 128 * w1 + 32 * jj + (lane & 31);
 #pragma unroll
-            for (int k = 0; k < M; ++k) bins[k] = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4) {
-                    const int al = 128 * w0 + 32 * i + 8 * v4 + 4 * (lane >> 5);
-                    const uint32_t cw = *(const uint32_t*)(ctile + jr * MT + al);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t code = (cw >> (8 * e)) & 0xffu;
-                        const float x = (al + e < arem) ? acc[i][jj][4 * v4 + e] : 0.f;
-#pragma unroll
-                        for (int k = 0; k < M; ++k) bins[k] += (code == (uint32_t)k) ? x : 0.f;
-                    }
-                }
-            // lanes l and l + 32 hold the same (j, q) for the other half of the a's
-#pragma unroll
-            for (int k = 0; k < M; ++k) bins[k] += __shfl_xor(bins[k], 32, 64);
-            // waves with w0 = 1 hand their sums to the waves with w0 = 0
-            if (w0 == 1 && lane < 32) {
-#pragma unroll
-                for (int k = 0; k < M; ++k) xch[(w1 * 32 + lane) * M + k] = bins[k];
+            for (int v = 0; v < 16; ++v) {
+                const int nrow = 128 * w0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (nrow < nrem && acol < arem)
+                    O[(n0 + nrow) * d + a0 + acol] = acc[i][jj][v];
             }
-            __syncthreads();
-            if (w0 == 0 && lane < 32) {
-                const int64_t n = n0 + nl;
-                if (n < N) {
-                    float* dst = out + ((size_t)ta * d_out * M + (size_t)(row_base * M + n)) * M;
-#pragma unroll
-                    for (int k = 0; k < M; ++k) dst[k] = bins[k] + xch[(w1 * 32 + lane) * M + k];
-                }
-            }
-            __syncthreads();
         }
+}
+
+// ---------------------------------------------------------------------------
+// Gram partials.  Tile (256 coordinates a) x (256 columns (j, q): 256 / M rows j
+// of a group, M codes each), k from a0 to d.
+// ---------------------------------------------------------------------------
+// One-hot of 4 code bytes against q: the bf16 pair `onepair` where the byte
+// equals q, else 0; returns the halfwords of bytes 0,1 (lo) and 2,3 (hi).
+__device__ __forceinline__ u32x2 onehot4(uint32_t codes, uint32_t qq, uint32_t onepair) {
+    const uint32_t y = codes ^ qq;                                   // zero byte <=> equal
+    const uint32_t nz = (((y & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | y) & 0x80808080u;
+    const uint32_t eq = (nz ^ 0x80808080u) >> 7;                     // 1 per equal byte
+    const uint32_t m8 = (eq << 8) - eq;                              // 0xFF per equal byte
+    u32x2 r;
+    r[0] = __builtin_amdgcn_perm(m8, m8, 0x01010000u) & onepair;
+    r[1] = __builtin_amdgcn_perm(m8, m8, 0x03030202u) & onepair;
+    return r;
+}
+
+template <int M>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gram(
+    const uint8_t* __restrict__ P, int64_t rpg, int64_t d_out, int groups,
+    const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo, int64_t a_pad,
+    int64_t d, int ntn, int nta, int total, float* __restrict__ out) {
+    extern __shared__ u32x4 mm_lds[];
+    // LDS: ring of MRING (Fhi, Flo) band stages; two one-hot stages (512 slots);
+    // ring of MRING code stages (one 16-byte slot per thread)
+    u32x4* ohbuf = mm_lds + MRING * 2 * M_SLOTS;
+    u32x4* cring = ohbuf + 2 * M_SLOTS;
+    const int lin = mm_remap(blockIdx.x);
+    if (lin >= total) return;
+    const int tn = lin % ntn;
+    const int g = (lin / ntn) % groups;
+    const int ta = lin / (ntn * groups);
+    const int64_t a0 = (int64_t)ta * MT;
+    const int64_t n0 = (int64_t)tn * MT;                 // first (j, q) column
+    const int64_t N = rpg * M;
+    const int64_t row_base = (int64_t)g * rpg;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w0 = wave & 1, w1 = wave >> 1;
+    const uint32_t voff = band_voff(lane);
+
+    const int64_t fg = (int64_t)g * d * a_pad;
+    const int64_t k_begin = a0;
+    const int nst = (int)((d - k_begin) / 16);
+    const int ndiag = (int)((((d - a0) < MT ? (d - a0) : MT)) / 16);   // stages at half weight
+    const uint16_t* Fh = Fhi + fg + ((k_begin >> 4) * a_pad + a0) * 16;
+    const uint16_t* Fl = Flo + fg + ((k_begin >> 4) * a_pad + a0) * 16;
+    const int64_t fstep = a_pad * 16;
+
+    // one-hot column of this thread: (j, q) = n0 + tid; its 16 codes of stage x are
+    // copied into slot tid of code stage x (a row past the group's end reads the
+    // group's first row and is masked when the one-hot is built)
+    const int64_t jl = n0 / M + tid / M;
+    const uint32_t q = (uint32_t)(tid % M);
+    const uint32_t qq = q * 0x01010101u;
+    const bool jvalid = jl < rpg;
+    const uint8_t* Pg = P + row_base * d + k_begin;
+    const uint32_t coff = (uint32_t)((jvalid ? jl : 0) * d);
+    auto issue_codes = [&](int x) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Pg + (int64_t)x * 16), (short)0, (int)0x7fffffff, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(cring + (x % MRING) * 256 + 64 * wave),
+                                                 16, coff, 0, 0, 0);
+    };
+    const int oh_slot0 = tid * 2, oh_sw = (tid >> 3) & 1;
+    auto build = [&](int x) {
+        u32x4 cv = cring[(x % MRING) * 256 + tid];
+        if (!jvalid) cv = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+        const uint32_t one = (x < ndiag) ? 0x3F00u : 0x3F80u;       // 0.5 on the diagonal tile
+        const uint32_t onepair = one | (one << 16);
+        const u32x2 h0 = onehot4(cv[0], qq, onepair), h1 = onehot4(cv[1], qq, onepair);
+        const u32x2 h2 = onehot4(cv[2], qq, onepair), h3 = onehot4(cv[3], qq, onepair);
+        const u32x4 k0 = {h0[0], h0[1], h1[0], h1[1]};              // k 0..7
+        const u32x4 k1 = {h2[0], h2[1], h3[0], h3[1]};              // k 8..15
+        u32x4* O = ohbuf + (x & 1) * M_SLOTS;
+        O[oh_slot0 + (0 ^ oh_sw)] = k0;
+        O[oh_slot0 + (1 ^ oh_sw)] = k1;
+    };
+    // batch x: the two bands of stage x, then the codes of stage x + 1 (5 loads per wave)
+    auto issue = [&](int x) {
+        u32x4* base = mm_lds + (x % MRING) * (2 * M_SLOTS);
+        band_to_lds(band_rsrc(Fh + x * fstep), base, wave, voff);
+        band_to_lds(band_rsrc(Fl + x * fstep), base + M_SLOTS, wave, voff);
+        if (x + 1 < nst) issue_codes(x + 1);
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
+
+    if (nst > 0) {
+        issue_codes(0);
+        const int pre = nst < MRING - 1 ? nst : MRING - 1;
+        for (int x = 0; x < pre; ++x) issue(x);
+        // codes of stage 0: the oldest load of this wave
+        if (pre >= 3) mm_wait_vmcnt<14>();
+        else if (pre == 2) mm_wait_vmcnt<9>();
+        else mm_wait_vmcnt<4>();
+        __builtin_amdgcn_s_barrier();
+        build(0);
+    }
+    int slot = 0;
+    for (int s = 0; s < nst; ++s) {
+        // batch s (bands of s, codes of s + 1) has landed once at most 5 x (later
+        // batches issued) loads are outstanding; a batch's code load exists only if
+        // its stage + 1 < nst, so the tail waits are exact or stricter
+        const int newer = ((s + MRING - 2 < nst) ? s + MRING - 2 : nst - 1) - s;
+        if (newer >= 2) mm_wait_vmcnt<9>();
+        else if (newer == 1) mm_wait_vmcnt<4>();
+        else mm_wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (s + MRING - 1 < nst) issue(s + MRING - 1);
+        if (s + 1 < nst) build(s + 1);
+        const u32x4* S = mm_lds + slot * (2 * M_SLOTS);
+        const u32x4* OH = ohbuf + (s & 1) * M_SLOTS;
+        bf16x8 fh[4], fl[4], oh[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int sl = frag_slot(128 * w0 + 32 * i + (lane & 31), lane);
+            fh[i] = as_bf16x8(S[sl]);
+            fl[i] = as_bf16x8(S[M_SLOTS + sl]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            oh[jj] = as_bf16x8(OH[frag_slot(128 * w1 + 32 * jj + (lane & 31), lane)]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[i], oh[jj], acc[i][jj], 0, 0, 0);
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[i], oh[jj], acc[i][jj], 0, 0, 0);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        slot = (slot + 1 == MRING) ? 0 : slot + 1;
+    }
+    __syncthreads();
+
+    // ---- epilogue: bin T[a][(j,q)] by the code of coordinate a
+    // stage the codes of the block's rows for its 256 coordinates: jrows x 256 bytes
+    constexpr int jrows = MT / M;
+    uint8_t* ctile = (uint8_t*)mm_lds;
+    for (int e = tid; e < jrows * (MT / 16); e += 256) {
+        const int r = e / (MT / 16), c16 = (e - r * (MT / 16)) * 16;
+        const int64_t jr = n0 / M + r;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (jr < rpg && a0 + c16 < d) v = *(const u32x4*)(P + (row_base + jr) * d + a0 + c16);
+        *(u32x4*)(ctile + r * MT + c16) = v;
+    }
+    __syncthreads();
+    float* xch = (float*)(ctile + jrows * MT);
+    const int arem = (int)((d - a0) < MT ? (d - a0) : MT);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int nl = 128 * w1 + 32 * jj + (lane & 31);
+        const int jr = nl / M;
+        float bins[M];
+#pragma unroll
+        for (int k = 0; k < M; ++k) bins[k] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int al = 128 * w0 + 32 * i + 8 * v4 + 4 * (lane >> 5);
+                const uint32_t cw = *(const uint32_t*)(ctile + jr * MT + al);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t code = (cw >> (8 * e)) & 0xffu;
+                    const float x = (al + e < arem) ? acc[i][jj][4 * v4 + e] : 0.f;
+#pragma unroll
+                    for (int k = 0; k < M; ++k) bins[k] += (code == (uint32_t)k) ? x : 0.f;
+                }
+            }
+        // lanes l and l + 32 hold the same (j, q) for the other half of the a's
+#pragma unroll
+        for (int k = 0; k < M; ++k) bins[k] += __shfl_xor(bins[k], 32, 64);
+        // waves with w0 = 1 hand their sums to the waves with w0 = 0
+        if (w0 == 1 && lane < 32) {
+#pragma unroll
+            for (int k = 0; k < M; ++k) xch[(w1 * 32 + lane) * M + k] = bins[k];
+        }
+        __syncthreads();
+        if (w0 == 0 && lane < 32) {
+            const int64_t n = n0 + nl;
+            if (n < N) {
+                float* dst = out + ((size_t)ta * d_out * M + (size_t)(row_base * M + n)) * M;
+#pragma unroll
+                for (int k = 0; k < M; ++k) dst[k] = bins[k] + xch[(w1 * 32 + lane) * M + k];
+            }
+        }
+        __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <int MODE, int M>
-static hipError_t launch_mm(const uint16_t* Ehi, const uint16_t* Elo, const uint8_t* codes,
-                            int64_t rpg, int g_first, int g_count, const uint16_t* Fhi,
-                            const uint16_t* Flo, int64_t d, float* out, int64_t d_out,
-                            hipStream_t st) {
-    const int64_t N = (MODE == MM_RESID) ? rpg : rpg * M;
-    const int ntn = (int)((N + MT - 1) / MT);
-    const int nta = (int)((d + MT - 1) / MT);
-    const int total = ntn * nta * g_count;
-    const int grid = (total + 255) / 256 * 256;        // whole rounds for the XCD remap
-    const size_t lds = mm_lds_bytes<MODE>();
-    static bool attr_done = false;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_mm<MODE, M>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
-    StageTimer tm(MODE == MM_RESID ? ST_LNQ_RESID : ST_LNQ_GRAM, st);
-    hipLaunchKernelGGL((k_mm<MODE, M>), dim3((unsigned)grid), dim3(256), lds, st, Ehi, Elo, codes,
-                       rpg, g_first, g_count, Fhi, Flo, d, ntn, nta, total, out, d_out);
-    GQ_LAUNCH_CHECK();
-    return hipSuccess;
-}
+constexpr size_t RESID_LDS = (size_t)MRING * 4 * M_SLOTS * 16;          // 128 KB
+constexpr size_t GRAM_LDS = ((size_t)(MRING * 2 + 2) * M_SLOTS + MRING * 256) * 16;   // 96 KB
 
 size_t lnq_gram_partial_floats(int64_t d_out, int64_t d, int m) {
     const int64_t nta = (d + MT - 1) / MT;
@@ -325,18 +393,59 @@ size_t lnq_gram_partial_floats(int64_t d_out, int64_t d, int m) {
 hipError_t lnq_residual(const uint16_t* Ehi, const uint16_t* Elo, int64_t d_out, int64_t d,
                         int groups, const uint16_t* Fhi, const uint16_t* Flo, float* R,
                         hipStream_t st) {
-    return launch_mm<MM_RESID, 1>(Ehi, Elo, nullptr, d_out / groups, 0, groups, Fhi, Flo, d, R,
-                                  d_out, st);
+    const int64_t rpg = d_out / groups;
+    const int64_t rpg_pad = lnq_pad256(rpg), a_pad = lnq_pad256(d);
+    const int ntn = (int)(rpg_pad / MT);
+    const int nta = (int)(a_pad / MT);
+    const int total = ntn * nta * groups;
+    const int grid = (total + 255) / 256 * 256;        // whole rounds for the XCD remap
+    static bool attr_done = false;
+    if (!attr_done) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_resid,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)RESID_LDS);
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    StageTimer tm(ST_LNQ_RESID, st);
+    hipLaunchKernelGGL(k_resid, dim3((unsigned)grid), dim3(256), RESID_LDS, st, Ehi, Elo,
+                       (int64_t)groups * rpg_pad, rpg_pad, Fhi, Flo, a_pad, d, rpg, ntn, nta,
+                       total, R);
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
+}
+
+template <int M>
+static hipError_t launch_gram(const uint8_t* P, int64_t d_out, int64_t d, int groups,
+                              const uint16_t* Fhi, const uint16_t* Flo, float* part,
+                              hipStream_t st) {
+    const int64_t rpg = d_out / groups;
+    const int ntn = (int)((rpg * M + MT - 1) / MT);
+    const int nta = (int)((d + MT - 1) / MT);
+    const int total = ntn * nta * groups;
+    const int grid = (total + 255) / 256 * 256;
+    static bool attr_done = false;
+    if (!attr_done) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_gram<M>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)GRAM_LDS);
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    StageTimer tm(ST_LNQ_GRAM, st);
+    hipLaunchKernelGGL((k_gram<M>), dim3((unsigned)grid), dim3(256), GRAM_LDS, st, P, rpg, d_out,
+                       groups, Fhi, Flo, lnq_pad256(d), d, ntn, nta, total, part);
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
 }
 
 hipError_t lnq_gram(const uint8_t* P, int m, int64_t d_out, int64_t d, int groups,
                     const uint16_t* Fhi, const uint16_t* Flo, float* part, hipStream_t st) {
-    const int64_t rpg = d_out / groups;
     switch (m) {
-        case 2: return launch_mm<MM_GRAM, 2>(nullptr, nullptr, P, rpg, 0, groups, Fhi, Flo, d, part, d_out, st);
-        case 4: return launch_mm<MM_GRAM, 4>(nullptr, nullptr, P, rpg, 0, groups, Fhi, Flo, d, part, d_out, st);
-        case 8: return launch_mm<MM_GRAM, 8>(nullptr, nullptr, P, rpg, 0, groups, Fhi, Flo, d, part, d_out, st);
-        case 16: return launch_mm<MM_GRAM, 16>(nullptr, nullptr, P, rpg, 0, groups, Fhi, Flo, d, part, d_out, st);
+        case 2: return launch_gram<2>(P, d_out, d, groups, Fhi, Flo, part, st);
+        case 4: return launch_gram<4>(P, d_out, d, groups, Fhi, Flo, part, st);
+        case 8: return launch_gram<8>(P, d_out, d, groups, Fhi, Flo, part, st);
+        case 16: return launch_gram<16>(P, d_out, d, groups, Fhi, Flo, part, st);
         default: return hipErrorInvalidValue;
     }
 }
