@@ -352,14 +352,17 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
 //         R[:, later] += D_sb F'[sb, later], streaming long contiguous panels
 //         of F' (each residual element is owned by one wave; no atomics).
 //     32-coordinate chunks in which no row of the block moved are skipped.
-//   * Chain (per wave): for coordinate t the residual, current value and damped
-//     diagonal are read from lane t (v_readlane); lanes 0..m-1 each evaluate one
-//     candidate change
+//   * Chain (per wave), first-mover form: every lane t of the 64-block not yet
+//     visited evaluates, from the current residual, its m candidate changes
 //         Delta_q = delta_q (F'_tt delta_q + 2 r_t),  delta_q = c_q - w_hat_t,
-//     a 16-lane DPP minimum on an order-preserving integer key gives the best
-//     change, a ballot + find-first-set the lowest index attaining it, and a
-//     strict decrease applies r += delta F'[t, block] in registers (the F'
-//     columns of the block are staged once through LDS for the 16 rows).
+//     keeping the lowest q among equal minima.  Coordinates are visited in
+//     ascending order and only a strict decrease changes r, so every coordinate
+//     before the first lane with a strictly negative best change keeps its code,
+//     exactly as a one-at-a-time pass would decide; a ballot + find-first-set
+//     gives that lane t, its move applies r += delta F'[t, block] in registers
+//     (the F' rows of the block are staged once through LDS for the 16 rows),
+//     and the scan resumes after t.  A block costs (its moves + 1) scans instead
+//     of 64 dependent steps, with the same decisions and the same arithmetic.
 //   * The row objective e.r at the start of the pass is summed (float64) before
 //     any update; the objective after it adds the accepted changes.
 //   The residual array R is updated in place (it is workspace).
@@ -368,7 +371,6 @@ constexpr int SW_ROWS = 16;     // rows (= waves) per block
 constexpr int SW_SUB = 64;      // coordinates per chain block (one per lane)
 constexpr int SW_SB = 512;      // coordinates per super-block
 constexpr int SW_DP = SW_SB + 8;  // bf16 pitch of the LDS rows of D_sb
-constexpr int SW_SEG = 8;       // chain steps unrolled per F' column preload
 constexpr int SW_RB = 4;        // F' chunks in flight per wave in the right-looking update
 
 template <int CTRL>
@@ -398,7 +400,7 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-template <bool WBF16>
+template <bool WBF16, int M>
 __global__ __launch_bounds__(1024, 1) void k_sweep(
     const float* __restrict__ F, const float* __restrict__ dF,
     const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo,
@@ -420,7 +422,8 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
     const int lin = (hw & 7) * (nb >> 3) + (hw >> 3);
     if (lin >= total_wgs) return;        // whole block exits together
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lin / wgs_per_group;
     const int64_t local = (int64_t)(lin % wgs_per_group) * SW_ROWS;
     const int64_t jl = local + wave;
@@ -442,7 +445,10 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
         return base + ((k >> 4) * a_pad + a) * 16 + (k & 15);
     };
 
-    const float cl = (lane < m && rvalid) ? C[j * m + lane] : 0.f;   // candidate of this lane
+    const float cl = (lane < M && rvalid) ? C[j * M + lane] : 0.f;   // candidate of this lane
+    float cq[M];                                                     // the row's codebook
+#pragma unroll
+    for (int q = 0; q < M; ++q) cq[q] = rvalid ? C[j * M + q] : 0.f;
     double dsum = 0.0;       // sum of the accepted changes (uniform in the wave)
     unsigned moves = 0;
 
@@ -504,35 +510,29 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
                 int code = P[j * d + col];
                 float wh = __shfl(cl, code, 64);
                 const float wh0 = wh;
-                const bool cand = lane < m;
                 const float fdiag = fdd[lane];            // F'[col][col]
-                for (int t0 = 0; t0 < SW_SUB; t0 += SW_SEG) {
-                    float fc[SW_SEG];                     // F[bs + t][bs + lane], t = t0..
+                int start = 0;                            // first coordinate not yet visited
+                while (true) {
+                    float best = 0.f, bdl = 0.f, bc = 0.f;
+                    int bq = -1;
 #pragma unroll
-                    for (int u = 0; u < SW_SEG; ++u) fc[u] = fdb[t0 + u][lane];
-#pragma unroll
-                    for (int u = 0; u < SW_SEG; ++u) {
-                        const int t = t0 + u;
-                        const float ft = readlane_f(fdiag, t);
-                        const float rt = readlane_f(r, t);
-                        const float wt = readlane_f(wh, t);
-                        const float dl = cl - wt;
-                        const float dq = dl * fmaf(ft, dl, 2.f * rt);
-                        const int key = cand ? f32_order_key(dq) : 0x7fffffff;
-                        const int bk = __builtin_amdgcn_readlane(row16_min_i(key), 0);
-                        if (bk < -1) {                    // a strictly negative change exists
-                            const int q = __ffsll((long long)__ballot(key == bk)) - 1;
-                            const float cq = readlane_f(cl, q);
-                            const float delta = cq - wt;
-                            r = fmaf(delta, fc[u], r);
-                            if (lane == __builtin_amdgcn_readfirstlane(t)) {
-                                code = q;
-                                wh = cq;
-                            }
-                            dsum += (double)readlane_f(dq, q);
-                            moves += 1;
-                        }
+                    for (int q = 0; q < M; ++q) {
+                        const float dl = cq[q] - wh;
+                        const float dq = dl * fmaf(fdiag, dl, 2.f * r);
+                        if (dq < best) { best = dq; bq = q; bdl = dl; bc = cq[q]; }
                     }
+                    const unsigned long long want = __ballot(lane >= start && bq >= 0);
+                    if (want == 0ull) break;
+                    const int t = __ffsll((long long)want) - 1;
+                    const float delta = readlane_f(bdl, t);
+                    dsum += (double)readlane_f(best, t);
+                    moves += 1;
+                    r = fmaf(delta, fdb[t][lane], r);     // F[bs + t][bs + lane]
+                    if (lane == t) {
+                        code = bq;
+                        wh = bc;
+                    }
+                    start = t + 1;
                 }
                 P[j * d + col] = (uint8_t)code;
                 dv = wh - wh0;
@@ -786,7 +786,9 @@ static hipError_t launch_sweep(const float* F, const void* W, int64_t d_out, int
     const int wgs = (int)((rpg + SW_ROWS - 1) / SW_ROWS);
     const int total = wgs * groups;
     const int grid = (total + 7) / 8 * 8;          // the XCD remap needs a multiple of 8
-    hipLaunchKernelGGL((k_sweep<WB>), dim3((unsigned)grid), dim3(1024), 0, st, F, w.dF, w.fhi,
+    auto kern = (m == 2) ? k_sweep<WB, 2> : (m == 4) ? k_sweep<WB, 4> : (m == 8) ? k_sweep<WB, 8>
+                                                                         : k_sweep<WB, 16>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(1024), 0, st, F, w.dF, w.fhi,
                        w.flo, d, rpg, wgs, total, C, m, P, W, w.R, obj_start, obj_end, counter);
     GQ_LAUNCH_CHECK();
     return hipSuccess;

@@ -297,7 +297,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         else mm_wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         if (s + MRING - 1 < nst) issue(s + MRING - 1);
-        if (s + 1 < nst) build(s + 1);
         const u32x4* S = mm_lds + slot * (2 * M_SLOTS);
         const u32x4* OH = ohbuf + (s & 1) * M_SLOTS;
         bf16x8 fh[4], fl[4], oh[4];
@@ -310,7 +309,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
             oh[jj] = as_bf16x8(OH[frag_slot(128 * w1 + 32 * jj + (lane & 31), lane)]);
-        __builtin_amdgcn_sched_barrier(0);
+        // the one-hot of stage s + 1 (past the last stage it fills a buffer no one
+        // reads, from a ring slot in bounds), built while the MFMAs of stage s run
+        build(s + 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -318,7 +319,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[i], oh[jj], acc[i][jj], 0, 0, 0);
                 acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[i], oh[jj], acc[i][jj], 0, 0, 0);
             }
-        __builtin_amdgcn_sched_barrier(0);
+        // order: the 12 fragment reads and the code read, then one MFMA per two
+        // VALU operations of the build, its two LDS writes, the remaining MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 13, 0);
+#pragma unroll
+        for (int k = 0; k < 24; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         slot = (slot + 1 == MRING) ? 0 : slot + 1;
     }
     __syncthreads();
