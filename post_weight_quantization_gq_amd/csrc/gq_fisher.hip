@@ -146,8 +146,9 @@ __global__ __launch_bounds__(256) void k_fisher_pack(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA Fisher: upper-triangle 256 (a) x 256 (b) tiles of F_g = XT YT[g]^T.
-// 4 waves in a 2x2 arrangement, each owning 128 x 128 outputs as 4x4
-// v_mfma_f32_32x32x16_bf16 tiles (the 256 accumulator registers of a lane).
+// 8 waves (two per SIMD, so one covers the other's barrier and LDS waits) in a
+// 2 (a) x 4 (b) arrangement, each owning 128 x 64 outputs as 4x2
+// v_mfma_f32_32x32x16_bf16 tiles (128 accumulator registers of a lane).
 // Tokens are staged 32 at a time in a ring of 4 LDS stages (4 x 32 KB), filled by
 // direct buffer-to-LDS loads issued three stages ahead, so no staging registers
 // and no LDS stores are needed.  An operand row of a stage is 64 bytes of the
@@ -173,7 +174,7 @@ __device__ __forceinline__ void tri_pair(int p, int T, int& ta, int& tb) {
     tb = b;
 }
 
-// wait until at most n vector-memory operations of this wave are outstanding
+// wait until at most N vector-memory operations of this wave are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
@@ -181,7 +182,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fisher_mfma(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fisher_mfma(
     const uint16_t* __restrict__ XT, const uint16_t* __restrict__ YT, int64_t n_pad,
     int64_t d_pad, int groups, int T, int npairs, int64_t ksplit, int total_blocks,
     float* __restrict__ part) {
@@ -204,11 +205,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the LDS targets go to M0
-    const int wa = wave & 1, wb = wave >> 1;
+    const int wa = wave & 1, wb = wave >> 1;   // wa 0..1 (128 rows), wb 0..3 (64 columns)
 
     // A stage of the a band is 256 rows x 64 bytes, contiguous in the blocked XT
     // (likewise the b band in YT[g]).  Load instruction k of a wave fills rows
-    // 16q .. 16q + 15 (q = 4k + wave): lane L takes row 16q + L/4 and slot L%4,
+    // 16q .. 16q + 15 (q = 8k + wave): lane L takes row 16q + L/4 and slot L%4,
     // i.e. chunk (L%4) ^ ((L/16)%4), at byte 1024 q + 64 (L/4) + 16 chunk of the
     // stage: a per-lane vector offset plus a uniform scalar offset, against a
     // buffer descriptor rebuilt per stage (scalar arithmetic only).
@@ -228,19 +229,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const __amdgpu_buffer_rsrc_t Br = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(Bbase + (int64_t)s * stage_elems), (short)0, F_SLOTS * 16, 0x00020000);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int q = 4 * k + wave;
+        for (int k = 0; k < 2; ++k) {
+            const int q = 8 * k + wave;
             const uint32_t so = (uint32_t)q * 1024u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(Ar, (lds_ptr_t)(sA(st) + 64 * q), 16, voff, so, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(Br, (lds_ptr_t)(sB(st) + 64 * q), 16, voff, so, 0, 0);
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -248,10 +249,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // wait until stage `want` has landed, given stages up to `last` issued
     auto wait_stage = [&](int want, int last) {
         const int newer = last - want;
-        if (newer >= 4) wait_vmcnt<32>();
-        else if (newer == 3) wait_vmcnt<24>();
-        else if (newer == 2) wait_vmcnt<16>();
-        else if (newer == 1) wait_vmcnt<8>();
+        if (newer >= 4) wait_vmcnt<16>();
+        else if (newer == 3) wait_vmcnt<12>();
+        else if (newer == 2) wait_vmcnt<8>();
+        else if (newer == 1) wait_vmcnt<4>();
         else wait_vmcnt<0>();
     };
     {
@@ -260,8 +261,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     int slot = 0;                        // ring slot of stage s
     for (int s = 0; s < nst; ++s) {
-        // this wave's loads of stage s are done (later stages may still be in flight),
-        // then every wave's are
+        // this wave's loads of stage s are done (4 per stage and wave; later stages
+        // may still be in flight), then every wave's are
         const int last = (s + FRING - 2 < nst) ? s + FRING - 2 : nst - 1;
         wait_stage(s, last);
         __builtin_amdgcn_s_barrier();
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (s + FRING - 1 < nst) issue(s + FRING - 1);
         const u32x4* A = fisher_lds + slot * (2 * F_SLOTS);
         const u32x4* B = A + F_SLOTS;
-        bf16x8 af[2][4], bfr[2][4];
+        bf16x8 af[2][4], bfr[2][2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int cs = (2 * ks + (lane >> 5)) ^ sw;
@@ -277,8 +278,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int i = 0; i < 4; ++i)
                 af[ks][i] = as_bf16x8(A[(128 * wa + 32 * i + (lane & 31)) * 4 + cs]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[ks][j] = as_bf16x8(B[(128 * wb + 32 * j + (lane & 31)) * 4 + cs]);
+            for (int j = 0; j < 2; ++j)
+                bfr[ks][j] = as_bf16x8(B[(64 * wb + 32 * j + (lane & 31)) * 4 + cs]);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         slot = (slot + 1 == FRING) ? 0 : slot + 1;
@@ -297,11 +298,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int al = 128 * wa + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                const int bl = 128 * wb + 32 * j + (lane & 31);
+                const int bl = 64 * wb + 32 * j + (lane & 31);
                 P[al * FT + bl] = acc[i][j][v];
             }
 }
@@ -518,7 +519,7 @@ static hipError_t fisher_pass(const FisherPlan& p, const void* X, const void* G,
         const FisherPlan q = fisher_plan(n, d_in, groups, bf16, p.nsplit);
         {
             StageTimer tm(ST_FISHER_MFMA, st);
-            hipLaunchKernelGGL(k_fisher_mfma, dim3(q.grid), dim3(256), F_LDS_BYTES, st, XT, YT,
+            hipLaunchKernelGGL(k_fisher_mfma, dim3(q.grid), dim3(512), F_LDS_BYTES, st, XT, YT,
                                n_pad, q.d_pad, groups, q.T, q.npairs, q.ksplit, q.total, part);
             GQ_LAUNCH_CHECK();
         }

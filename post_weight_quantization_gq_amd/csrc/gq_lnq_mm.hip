@@ -21,7 +21,8 @@
 // Both operands live in k-blocked bf16 planes (element (row, k) at
 // ((k / 16) * rows + row) * 16 + k % 16, rows padded to whole 256-row tiles), so
 // one 16-deep stage of a 256-row band is 8 KB of contiguous memory.  Block tile
-// 256 x 256, 4 waves of 128 x 128 as 4 x 4 v_mfma_f32_32x32x16_bf16 tiles.  The
+// 256 x 256, 8 waves (two per SIMD) of 128 x 64 as 4 x 2 v_mfma_f32_32x32x16_bf16
+// tiles.  The
 // stages go through a ring of 4 LDS stages filled by direct buffer-to-LDS loads
 // three stages ahead; a 32-byte operand row sits in two 16-byte slots, chunk c
 // of row r in slot 2 r + (c ^ ((r >> 3) & 1)), so each quarter-wave fragment
@@ -56,16 +57,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t band_rsrc(const uint16_t* p) {
 }
 
 // Copy one stage of a 256-row band (rows of 32 bytes) into 512 LDS slots: wave w
-// issues instructions q = 2w, 2w + 1, each filling rows 32q .. 32q + 31; lane L
-// takes row 32q + L/2 and slot L%2, i.e. chunk (L%2) ^ ((L/16)%2).
+// (of 8) issues one instruction filling rows 32w .. 32w + 31; lane L takes row
+// 32w + L/2 and slot L%2, i.e. chunk (L%2) ^ ((L/16)%2).
 __device__ __forceinline__ void band_to_lds(__amdgpu_buffer_rsrc_t r, u32x4* dst, int wave,
                                             uint32_t voff) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int q = 2 * wave + i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 64 * q), 16, voff,
-                                                 (uint32_t)q * 1024u, 0, 0);
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 64 * wave), 16, voff,
+                                             (uint32_t)wave * 1024u, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t band_voff(int lane) {
@@ -80,7 +77,7 @@ __device__ __forceinline__ int frag_slot(int row, int lane) {
 // ---------------------------------------------------------------------------
 // R = E F'.  Tile (256 rows j of a group) x (256 coordinates a).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_resid(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_resid(
     const uint16_t* __restrict__ Ehi, const uint16_t* __restrict__ Elo, int64_t erows,
     int64_t rpg_pad, const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo,
     int64_t a_pad, int64_t d, int64_t rpg, int ntn, int nta, int total, float* __restrict__ R) {
@@ -114,11 +111,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         band_to_lds(band_rsrc(Fl + s * fstep), base + 3 * M_SLOTS, wave, voff);
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
 
@@ -128,16 +125,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     int slot = 0;
     for (int s = 0; s < nst; ++s) {
-        // 8 load instructions per stage and wave: stage s has landed once at most
-        // 8 x (later stages issued) are outstanding
+        // 4 load instructions per stage and wave: stage s has landed once at most
+        // 4 x (later stages issued) are outstanding
         const int newer = ((s + MRING - 2 < nst) ? s + MRING - 2 : nst - 1) - s;
-        if (newer >= 2) mm_wait_vmcnt<16>();
-        else if (newer == 1) mm_wait_vmcnt<8>();
+        if (newer >= 2) mm_wait_vmcnt<8>();
+        else if (newer == 1) mm_wait_vmcnt<4>();
         else mm_wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         if (s + MRING - 1 < nst) issue(s + MRING - 1);
         const u32x4* S = mm_lds + slot * (4 * M_SLOTS);
-        bf16x8 eh[4], el[4], fh[4], fl[4];
+        bf16x8 eh[4], el[4], fh[2], fl[2];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int sl = frag_slot(128 * w0 + 32 * i + (lane & 31), lane);
@@ -145,8 +142,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             el[i] = as_bf16x8(S[M_SLOTS + sl]);
         }
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int sl = frag_slot(128 * w1 + 32 * jj + (lane & 31), lane);
+        for (int jj = 0; jj < 2; ++jj) {
+            const int sl = frag_slot(64 * w1 + 32 * jj + (lane & 31), lane);
             fh[jj] = as_bf16x8(S[2 * M_SLOTS + sl]);
             fl[jj] = as_bf16x8(S[3 * M_SLOTS + sl]);
         }
@@ -154,7 +151,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
+            for (int jj = 0; jj < 2; ++jj) {
                 acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(eh[i], fh[jj], acc[i][jj], 0, 0, 0);
                 acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(eh[i], fl[jj], acc[i][jj], 0, 0, 0);
                 acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(el[i], fh[jj], acc[i][jj], 0, 0, 0);
@@ -169,8 +166,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int acol = 128 * w1 + 32 * jj + (lane & 31);
+        for (int jj = 0; jj < 2; ++jj) {
+            const int acol = 64 * w1 + 32 * jj + (lane & 31);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int nrow = 128 * w0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -198,7 +195,7 @@ __device__ __forceinline__ u32x2 onehot4(uint32_t codes, uint32_t qq, uint32_t o
 }
 
 template <int M>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gram(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gram(
     const uint8_t* __restrict__ P, int64_t rpg, int64_t d_out, int groups,
     const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo, int64_t a_pad,
     int64_t d, int ntn, int nta, int total, float* __restrict__ out) {
@@ -230,34 +227,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint16_t* Fl = Flo + fg + ((k_begin >> 4) * a_pad + a0) * 16;
     const int64_t fstep = a_pad * 16;
 
-    // one-hot column of this thread: (j, q) = n0 + tid; its 16 codes of stage x are
-    // copied into slot tid of code stage x (a row past the group's end reads the
-    // group's first row and is masked when the one-hot is built)
-    const int64_t jl = n0 / M + tid / M;
-    const uint32_t q = (uint32_t)(tid % M);
-    const uint32_t qq = q * 0x01010101u;
+    // The 16 codes of stage x for one-hot column c ((j, q) = n0 + c) are copied into
+    // slot c of code stage x (a row past the group's end reads the group's first row
+    // and is masked when the one-hot is built).
+    const int ccol = 32 * wave + (lane & 31);
+    const int64_t jl = n0 / M + ccol / M;
     const bool jvalid = jl < rpg;
     const uint8_t* Pg = P + row_base * d + k_begin;
     const uint32_t coff = (uint32_t)((jvalid ? jl : 0) * d);
+    // code load: lanes 0..31 of wave w copy the 16 codes of columns 32w .. 32w + 31
     auto issue_codes = [&](int x) {
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(Pg + (int64_t)x * 16), (short)0, (int)0x7fffffff, 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(cring + (x % MRING) * 256 + 64 * wave),
-                                                 16, coff, 0, 0, 0);
+        if (lane < 32)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(cring + (x % MRING) * 256 + 32 * wave),
+                                                     16, coff, 0, 0, 0);
     };
-    const int oh_slot0 = tid * 2, oh_sw = (tid >> 3) & 1;
+    // thread t builds k-half h = t / 256 of column c = t % 256
+    const int bcol = tid & 255, bh = tid >> 8;
+    const int64_t bjl = n0 / M + bcol / M;
+    const uint32_t bqq = (uint32_t)(bcol % M) * 0x01010101u;
+    const bool bvalid = bjl < rpg;
+    const int oh_slot = bcol * 2 + (bh ^ ((bcol >> 3) & 1));
     auto build = [&](int x) {
-        u32x4 cv = cring[(x % MRING) * 256 + tid];
-        if (!jvalid) cv = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+        u32x2 cv = ((const u32x2*)(cring + (x % MRING) * 256 + bcol))[bh];
+        if (!bvalid) cv = u32x2{0xffffffffu, 0xffffffffu};
         const uint32_t one = (x < ndiag) ? 0x3F00u : 0x3F80u;       // 0.5 on the diagonal tile
         const uint32_t onepair = one | (one << 16);
-        const u32x2 h0 = onehot4(cv[0], qq, onepair), h1 = onehot4(cv[1], qq, onepair);
-        const u32x2 h2 = onehot4(cv[2], qq, onepair), h3 = onehot4(cv[3], qq, onepair);
-        const u32x4 k0 = {h0[0], h0[1], h1[0], h1[1]};              // k 0..7
-        const u32x4 k1 = {h2[0], h2[1], h3[0], h3[1]};              // k 8..15
-        u32x4* O = ohbuf + (x & 1) * M_SLOTS;
-        O[oh_slot0 + (0 ^ oh_sw)] = k0;
-        O[oh_slot0 + (1 ^ oh_sw)] = k1;
+        const u32x2 h0 = onehot4(cv[0], bqq, onepair), h1 = onehot4(cv[1], bqq, onepair);
+        ohbuf[(x & 1) * M_SLOTS + oh_slot] = u32x4{h0[0], h0[1], h1[0], h1[1]};
     };
     // batch x: the two bands of stage x, then the codes of stage x + 1 (5 loads per wave)
     auto issue = [&](int x) {
@@ -267,11 +265,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (x + 1 < nst) issue_codes(x + 1);
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
 
@@ -280,26 +278,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int pre = nst < MRING - 1 ? nst : MRING - 1;
         for (int x = 0; x < pre; ++x) issue(x);
         // codes of stage 0: the oldest load of this wave
-        if (pre >= 3) mm_wait_vmcnt<14>();
-        else if (pre == 2) mm_wait_vmcnt<9>();
-        else mm_wait_vmcnt<4>();
+        if (pre >= 3) mm_wait_vmcnt<8>();
+        else if (pre == 2) mm_wait_vmcnt<5>();
+        else mm_wait_vmcnt<2>();
         __builtin_amdgcn_s_barrier();
         build(0);
     }
     int slot = 0;
     for (int s = 0; s < nst; ++s) {
-        // batch s (bands of s, codes of s + 1) has landed once at most 5 x (later
-        // batches issued) loads are outstanding; a batch's code load exists only if
-        // its stage + 1 < nst, so the tail waits are exact or stricter
+        // batch s (bands of s, codes of s + 1) has landed once at most 3 x (later
+        // batches issued) loads of this wave are outstanding; a batch's code load
+        // exists only if its stage + 1 < nst, so the tail waits are exact or stricter
         const int newer = ((s + MRING - 2 < nst) ? s + MRING - 2 : nst - 1) - s;
-        if (newer >= 2) mm_wait_vmcnt<9>();
-        else if (newer == 1) mm_wait_vmcnt<4>();
+        if (newer >= 2) mm_wait_vmcnt<5>();
+        else if (newer == 1) mm_wait_vmcnt<2>();
         else mm_wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         if (s + MRING - 1 < nst) issue(s + MRING - 1);
         const u32x4* S = mm_lds + slot * (2 * M_SLOTS);
         const u32x4* OH = ohbuf + (s & 1) * M_SLOTS;
-        bf16x8 fh[4], fl[4], oh[4];
+        bf16x8 fh[4], fl[4], oh[2];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int sl = frag_slot(128 * w0 + 32 * i + (lane & 31), lane);
@@ -307,28 +305,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             fl[i] = as_bf16x8(S[M_SLOTS + sl]);
         }
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            oh[jj] = as_bf16x8(OH[frag_slot(128 * w1 + 32 * jj + (lane & 31), lane)]);
+        for (int jj = 0; jj < 2; ++jj)
+            oh[jj] = as_bf16x8(OH[frag_slot(64 * w1 + 32 * jj + (lane & 31), lane)]);
         // the one-hot of stage s + 1 (past the last stage it fills a buffer no one
         // reads, from a ring slot in bounds), built while the MFMAs of stage s run
         build(s + 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
+            for (int jj = 0; jj < 2; ++jj) {
                 acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[i], oh[jj], acc[i][jj], 0, 0, 0);
                 acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[i], oh[jj], acc[i][jj], 0, 0, 0);
             }
-        // order: the 12 fragment reads and the code read, then one MFMA per two
-        // VALU operations of the build, its two LDS writes, the remaining MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 13, 0);
+        // order: the 10 fragment reads and the code read, then one MFMA per two
+        // VALU operations of the build, its LDS write, the remaining MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 11, 0);
 #pragma unroll
-        for (int k = 0; k < 24; ++k) {
+        for (int k = 0; k < 12; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         slot = (slot + 1 == MRING) ? 0 : slot + 1;
     }
     __syncthreads();
@@ -337,7 +335,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // stage the codes of the block's rows for its 256 coordinates: jrows x 256 bytes
     constexpr int jrows = MT / M;
     uint8_t* ctile = (uint8_t*)mm_lds;
-    for (int e = tid; e < jrows * (MT / 16); e += 256) {
+    for (int e = tid; e < jrows * (MT / 16); e += 512) {
         const int r = e / (MT / 16), c16 = (e - r * (MT / 16)) * 16;
         const int64_t jr = n0 / M + r;
         u32x4 v = {0u, 0u, 0u, 0u};
@@ -348,8 +346,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float* xch = (float*)(ctile + jrows * MT);
     const int arem = (int)((d - a0) < MT ? (d - a0) : MT);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        const int nl = 128 * w1 + 32 * jj + (lane & 31);
+    for (int jj = 0; jj < 2; ++jj) {
+        const int nl = 64 * w1 + 32 * jj + (lane & 31);
         const int jr = nl / M;
         float bins[M];
 #pragma unroll
@@ -418,7 +416,7 @@ hipError_t lnq_residual(const uint16_t* Ehi, const uint16_t* Elo, int64_t d_out,
         attr_done = true;
     }
     StageTimer tm(ST_LNQ_RESID, st);
-    hipLaunchKernelGGL(k_resid, dim3((unsigned)grid), dim3(256), RESID_LDS, st, Ehi, Elo,
+    hipLaunchKernelGGL(k_resid, dim3((unsigned)grid), dim3(512), RESID_LDS, st, Ehi, Elo,
                        (int64_t)groups * rpg_pad, rpg_pad, Fhi, Flo, a_pad, d, rpg, ntn, nta,
                        total, R);
     GQ_LAUNCH_CHECK();
@@ -443,7 +441,7 @@ static hipError_t launch_gram(const uint8_t* P, int64_t d_out, int64_t d, int gr
         attr_done = true;
     }
     StageTimer tm(ST_LNQ_GRAM, st);
-    hipLaunchKernelGGL((k_gram<M>), dim3((unsigned)grid), dim3(256), GRAM_LDS, st, P, rpg, d_out,
+    hipLaunchKernelGGL((k_gram<M>), dim3((unsigned)grid), dim3(512), GRAM_LDS, st, P, rpg, d_out,
                        groups, Fhi, Flo, lnq_pad256(d), d, ntn, nta, total, part);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
