@@ -58,12 +58,12 @@ def _parse():
 # figure no longer describes the kernel and is reported as null.
 _CSRC = os.path.join(ROOT, "post_weight_quantization_gq_amd", "csrc")
 _TRAFFIC = {
-    # stage: (workload, source file, digest, bytes read, bytes written)
-    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "55603ac889a4a2af", 1194786000, 258160000),
-    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "22b8f430fbe80c00", 9501532000,
-                    1140851000),
-    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "33d3a8a520e2f27b", 715068000, 67109000),
-    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "33d3a8a520e2f27b", 271150000, 16777000),
+    # stage: (workload, source file, digest, bytes read, bytes written) of its main kernel
+    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "27613b3830b49cb1", 269647000, 16777216),
+    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "9fa836b8c1b617ea", 16732700000,
+                    1140850688),
+    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "19ba356279e40eef", 748165000, 251854656),
+    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "27613b3830b49cb1", 604172000, 67108864),
 }
 
 
@@ -84,25 +84,36 @@ def _traffic(stage, wl):
 
 
 def _stage_units(stage, wl, changed_total):
-    """Algorithmic work of a stage in one step: (bound, amount, peak, unit)."""
+    """Algorithmic work of a stage in one step: (bound, amount, peak, unit).
+
+    The contractions count the flops of the bf16 products the method runs: F' and the
+    error E enter as bf16 hi + lo pairs to reach float32-level accuracy, so the
+    residual is three bf16 products and the codebook Gram two (its one-hot operand
+    is exact in bf16), over the upper triangle of 256-wide tiles of F'.
+    """
     n, d, d_out, G, m, it = wl.n, wl.d_in, wl.d_out, wl.groups, wl.m, wl.iters
     if stage == "fisher_mfma":
         # unique entries of the symmetric F_g: n d (d + 1) flops per group
         return "mfma", n * d * (d + 1) * G, PEAK_BF16_MFMA, "TFLOP/s"
     if stage == "lnq_gram":
-        # the codebook gather: each row sums F' over the coordinates of each code,
-        # d^2 adds per row and codebook step (add-only: half the FMA peak)
-        return "alu", it * d_out * d * d, PEAK_FP32_VALU / 2, "TFLOP/s"
+        ntile = (d + 255) // 256
+        tri = sum(min(256, d - 256 * t) * (d - 256 * t) for t in range(ntile))
+        return "mfma", it * 2 * 2 * tri * d_out * m, PEAK_BF16_MFMA, "TFLOP/s"
+    if stage == "lnq_resid":
+        # 2 iters + 1 residuals per step, each E F' per group as three bf16 products
+        return "mfma", (2 * it + 1) * 3 * 2 * d_out * d * d, PEAK_BF16_MFMA, "TFLOP/s"
     if stage == "lnq_sweep":
         # m candidate changes (3 flops each) per coordinate, 2 d flops per move
         return "alu", it * d_out * d * 3 * m + 2 * d * changed_total, PEAK_FP32_VALU, "TFLOP/s"
     if stage == "lnq_solve":
-        # per codebook step: read U (m values), V, codes, W; write the residual
-        return "hbm", (it + 1) * d_out * d * (4 * m + 4 + 1 + 2 + 4), PEAK_HBM, "GB/s"
+        # per call: read R, P, W and the Gram partials
+        ntile = (d + 255) // 256
+        return "hbm", (it + 1) * d_out * (d * (4 + 1 + 2) + ntile * m * m * 4), PEAK_HBM, "GB/s"
     if stage == "group_scale":
         return "hbm", 2 * n * d_out + 4 * G * n, PEAK_HBM, "GB/s"
-    if stage == "lnq_resid":
-        return "mfma", 2 * d_out * d * d, PEAK_BF16_MFMA, "TFLOP/s"
+    if stage == "fisher_pack":
+        # read X, write XT and YT (bf16)
+        return "hbm", 2 * n * d + 2 * (1 + G) * n * d, PEAK_HBM, "GB/s"
     return None
 
 
