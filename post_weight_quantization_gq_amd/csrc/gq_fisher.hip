@@ -187,11 +187,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int64_t d_pad, int groups, int T, int npairs, int64_t ksplit, int total_blocks,
     float* __restrict__ part) {
     extern __shared__ u32x4 fisher_lds[];
-    // XCD-aware remap: hardware block h lands on XCD h % 8; give each XCD a
-    // contiguous range of logical blocks (same split, neighbouring tiles, all groups).
-    const int nb = gridDim.x;
+    // XCD-aware remap: hardware block h lands on XCD h % 8.  Within each round of
+    // 256 blocks, XCD x takes 32 consecutive logical blocks (neighbouring tile pairs,
+    // all groups: their bands meet in its L2), and a round covers consecutive logical
+    // blocks, so all XCDs stream the same token split at once (shared in the MALL).
     const int hw = blockIdx.x;
-    const int lin = (hw & 7) * (nb >> 3) + (hw >> 3);
+    const int lin = (hw & ~255) + (hw & 7) * 32 + ((hw & 255) >> 3);
     if (lin >= total_blocks) return;
     const int g = lin % groups;
     const int pair = (lin / groups) % npairs;
@@ -468,7 +469,7 @@ FisherPlan fisher_plan(int64_t n_call, int64_t d_in, int groups, bool bf16,
     p.nsplit = best_s;
     p.ksplit = ((p.n_pad + best_s - 1) / best_s + FKC - 1) / FKC * FKC;
     p.total = tiles * p.nsplit;
-    p.grid = (p.total + 7) / 8 * 8;
+    p.grid = (p.total + 255) / 256 * 256;         // whole rounds for the remap
     p.xt_bytes = al256((size_t)p.d_pad * p.n_pad * 2);
     p.yt_bytes = al256((size_t)groups * p.d_pad * p.n_pad * 2);
     p.part_bytes = (size_t)p.total * FT * FT * sizeof(float);

@@ -27,7 +27,8 @@
 // three stages ahead; a 32-byte operand row sits in two 16-byte slots, chunk c
 // of row r in slot 2 r + (c ^ ((r >> 3) & 1)), so each quarter-wave fragment
 // read (16 consecutive rows) touches 16 distinct bank groups.  The one-hot
-// operand of k_gram is built once per stage into LDS, one stage ahead.
+// operand of k_gram is built once per stage into LDS, one stage ahead; k_gram
+// takes 32-deep stages (two k-blocks) through a ring of 3.
 #include "gq_common.h"
 #include "gq_internal.h"
 
@@ -194,16 +195,22 @@ __device__ __forceinline__ u32x2 onehot4(uint32_t codes, uint32_t qq, uint32_t o
     return r;
 }
 
+// The Gram kernel runs 32-deep stages (two 16-deep k-blocks) through a ring of
+// GRING stages, to halve the per-stage barrier and fragment-read overhead against
+// its 16 MFMAs per k-block and wave.
+constexpr int GRING = 3;
+
 template <int M>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gram(
     const uint8_t* __restrict__ P, int64_t rpg, int64_t d_out, int groups,
     const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo, int64_t a_pad,
     int64_t d, int ntn, int nta, int total, float* __restrict__ out) {
     extern __shared__ u32x4 mm_lds[];
-    // LDS: ring of MRING (Fhi, Flo) band stages; two one-hot stages (512 slots);
-    // ring of MRING code stages (one 16-byte slot per thread)
-    u32x4* ohbuf = mm_lds + MRING * 2 * M_SLOTS;
-    u32x4* cring = ohbuf + 2 * M_SLOTS;
+    // LDS: ring of GRING stages of four bands (Fhi and Flo of two k-blocks); two
+    // one-hot stages of two k-blocks (512 slots each); ring of GRING code stages
+    // (slot 64 w + 32 h + c for column 32 w + c, codes 16 h .. 16 h + 15)
+    u32x4* ohbuf = mm_lds + GRING * 4 * M_SLOTS;
+    u32x4* cring = ohbuf + 4 * M_SLOTS;
     const int lin = mm_remap(blockIdx.x);
     if (lin >= total) return;
     const int tn = lin % ntn;
@@ -221,47 +228,51 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     const int64_t fg = (int64_t)g * d * a_pad;
     const int64_t k_begin = a0;
-    const int nst = (int)((d - k_begin) / 16);
-    const int ndiag = (int)((((d - a0) < MT ? (d - a0) : MT)) / 16);   // stages at half weight
+    const int nst = (int)((d - k_begin) / 32);          // d % 32 == 0, a0 % 256 == 0
+    const int ndiag = (int)((((d - a0) < MT ? (d - a0) : MT)) / 16);   // k-blocks at half weight
     const uint16_t* Fh = Fhi + fg + ((k_begin >> 4) * a_pad + a0) * 16;
     const uint16_t* Fl = Flo + fg + ((k_begin >> 4) * a_pad + a0) * 16;
-    const int64_t fstep = a_pad * 16;
+    const int64_t fstep = a_pad * 16;                   // one 16-deep k-block
 
-    // The 16 codes of stage x for one-hot column c ((j, q) = n0 + c) are copied into
-    // slot c of code stage x (a row past the group's end reads the group's first row
-    // and is masked when the one-hot is built).
+    // code load: lane L of wave w copies codes 16 (L / 32) .. + 15 of stage x for
+    // one-hot column c = 32 w + L % 32 ((j, q) = n0 + c); a row past the group's end
+    // reads the group's first row and is masked when the one-hot is built
     const int ccol = 32 * wave + (lane & 31);
     const int64_t jl = n0 / M + ccol / M;
     const bool jvalid = jl < rpg;
     const uint8_t* Pg = P + row_base * d + k_begin;
-    const uint32_t coff = (uint32_t)((jvalid ? jl : 0) * d);
-    // code load: lanes 0..31 of wave w copy the 16 codes of columns 32w .. 32w + 31
+    const uint32_t coff = (uint32_t)((jvalid ? jl : 0) * d) + 16u * (uint32_t)(lane >> 5);
     auto issue_codes = [&](int x) {
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(Pg + (int64_t)x * 16), (short)0, (int)0x7fffffff, 0x00020000);
-        if (lane < 32)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(cring + (x % MRING) * 256 + 32 * wave),
-                                                     16, coff, 0, 0, 0);
+            (void*)(Pg + (int64_t)x * 32), (short)0, (int)0x7fffffff, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(cring + (x % GRING) * 512 + 64 * wave),
+                                                 16, coff, 0, 0, 0);
     };
-    // thread t builds k-half h = t / 256 of column c = t % 256
-    const int bcol = tid & 255, bh = tid >> 8;
+    // thread t builds k-block kb = t / 256 of column c = t % 256
+    const int bcol = tid & 255, bkb = tid >> 8;
     const int64_t bjl = n0 / M + bcol / M;
     const uint32_t bqq = (uint32_t)(bcol % M) * 0x01010101u;
     const bool bvalid = bjl < rpg;
-    const int oh_slot = bcol * 2 + (bh ^ ((bcol >> 3) & 1));
+    const int csl = 64 * (bcol >> 5) + 32 * bkb + (bcol & 31);
+    const int osw = (bcol >> 3) & 1;
     auto build = [&](int x) {
-        u32x2 cv = ((const u32x2*)(cring + (x % MRING) * 256 + bcol))[bh];
-        if (!bvalid) cv = u32x2{0xffffffffu, 0xffffffffu};
-        const uint32_t one = (x < ndiag) ? 0x3F00u : 0x3F80u;       // 0.5 on the diagonal tile
+        u32x4 cv = cring[(x % GRING) * 512 + csl];
+        if (!bvalid) cv = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+        const uint32_t one = (2 * x + bkb < ndiag) ? 0x3F00u : 0x3F80u;   // 0.5 on the diagonal tile
         const uint32_t onepair = one | (one << 16);
         const u32x2 h0 = onehot4(cv[0], bqq, onepair), h1 = onehot4(cv[1], bqq, onepair);
-        ohbuf[(x & 1) * M_SLOTS + oh_slot] = u32x4{h0[0], h0[1], h1[0], h1[1]};
+        const u32x2 h2 = onehot4(cv[2], bqq, onepair), h3 = onehot4(cv[3], bqq, onepair);
+        u32x4* O = ohbuf + ((x & 1) * 2 + bkb) * M_SLOTS + bcol * 2;
+        O[0 ^ osw] = u32x4{h0[0], h0[1], h1[0], h1[1]};          // k 0..7 of the k-block
+        O[1 ^ osw] = u32x4{h2[0], h2[1], h3[0], h3[1]};          // k 8..15
     };
-    // batch x: the two bands of stage x, then the codes of stage x + 1 (5 loads per wave)
+    // batch x: the four bands of stage x, then the codes of stage x + 1 (5 loads per wave)
     auto issue = [&](int x) {
-        u32x4* base = mm_lds + (x % MRING) * (2 * M_SLOTS);
-        band_to_lds(band_rsrc(Fh + x * fstep), base, wave, voff);
-        band_to_lds(band_rsrc(Fl + x * fstep), base + M_SLOTS, wave, voff);
+        u32x4* base = mm_lds + (x % GRING) * (4 * M_SLOTS);
+        band_to_lds(band_rsrc(Fh + (2 * x) * fstep), base, wave, voff);
+        band_to_lds(band_rsrc(Fh + (2 * x + 1) * fstep), base + M_SLOTS, wave, voff);
+        band_to_lds(band_rsrc(Fl + (2 * x) * fstep), base + 2 * M_SLOTS, wave, voff);
+        band_to_lds(band_rsrc(Fl + (2 * x + 1) * fstep), base + 3 * M_SLOTS, wave, voff);
         if (x + 1 < nst) issue_codes(x + 1);
     };
 
@@ -275,59 +286,60 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     if (nst > 0) {
         issue_codes(0);
-        const int pre = nst < MRING - 1 ? nst : MRING - 1;
+        const int pre = nst < GRING - 1 ? nst : GRING - 1;
         for (int x = 0; x < pre; ++x) issue(x);
         // codes of stage 0: the oldest load of this wave
-        if (pre >= 3) mm_wait_vmcnt<8>();
-        else if (pre == 2) mm_wait_vmcnt<5>();
-        else mm_wait_vmcnt<2>();
+        if (pre >= 2) mm_wait_vmcnt<9>();
+        else mm_wait_vmcnt<4>();
         __builtin_amdgcn_s_barrier();
         build(0);
     }
     int slot = 0;
     for (int s = 0; s < nst; ++s) {
-        // batch s (bands of s, codes of s + 1) has landed once at most 3 x (later
-        // batches issued) loads of this wave are outstanding; a batch's code load
-        // exists only if its stage + 1 < nst, so the tail waits are exact or stricter
-        const int newer = ((s + MRING - 2 < nst) ? s + MRING - 2 : nst - 1) - s;
-        if (newer >= 2) mm_wait_vmcnt<5>();
-        else if (newer == 1) mm_wait_vmcnt<2>();
+        // batch s (bands of s, codes of s + 1) has landed once at most 4 loads of
+        // this wave (batch s + 1, if issued) are outstanding
+        if (s + 1 < nst) mm_wait_vmcnt<4>();
         else mm_wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        if (s + MRING - 1 < nst) issue(s + MRING - 1);
-        const u32x4* S = mm_lds + slot * (2 * M_SLOTS);
-        const u32x4* OH = ohbuf + (s & 1) * M_SLOTS;
-        bf16x8 fh[4], fl[4], oh[2];
+        if (s + GRING - 1 < nst) issue(s + GRING - 1);
+        const u32x4* S = mm_lds + slot * (4 * M_SLOTS);
+        const u32x4* OH = ohbuf + (s & 1) * 2 * M_SLOTS;
+        bf16x8 fh[2][4], fl[2][4], oh[2][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int sl = frag_slot(128 * w0 + 32 * i + (lane & 31), lane);
-            fh[i] = as_bf16x8(S[sl]);
-            fl[i] = as_bf16x8(S[M_SLOTS + sl]);
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sl = frag_slot(128 * w0 + 32 * i + (lane & 31), lane);
+                fh[kb][i] = as_bf16x8(S[kb * M_SLOTS + sl]);
+                fl[kb][i] = as_bf16x8(S[(2 + kb) * M_SLOTS + sl]);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                oh[kb][jj] = as_bf16x8(OH[kb * M_SLOTS + frag_slot(64 * w1 + 32 * jj + (lane & 31), lane)]);
         }
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-            oh[jj] = as_bf16x8(OH[frag_slot(64 * w1 + 32 * jj + (lane & 31), lane)]);
         // the one-hot of stage s + 1 (past the last stage it fills a buffer no one
         // reads, from a ring slot in bounds), built while the MFMAs of stage s run
         build(s + 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[i], oh[jj], acc[i][jj], 0, 0, 0);
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[i], oh[jj], acc[i][jj], 0, 0, 0);
-            }
-        // order: the 10 fragment reads and the code read, then one MFMA per two
-        // VALU operations of the build, its LDS write, the remaining MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 11, 0);
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int k = 0; k < 12; ++k) {
+                for (int jj = 0; jj < 2; ++jj) {
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[kb][i], oh[kb][jj], acc[i][jj], 0, 0, 0);
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[kb][i], oh[kb][jj], acc[i][jj], 0, 0, 0);
+                }
+        // order: the 20 fragment reads and the code read, then one MFMA per two
+        // VALU operations of the build, its LDS writes, the remaining MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 21, 0);
+#pragma unroll
+        for (int k = 0; k < 22; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        slot = (slot + 1 == MRING) ? 0 : slot + 1;
+        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+        slot = (slot + 1 == GRING) ? 0 : slot + 1;
     }
     __syncthreads();
 
@@ -391,7 +403,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // Host launchers
 // ---------------------------------------------------------------------------
 constexpr size_t RESID_LDS = (size_t)MRING * 4 * M_SLOTS * 16;          // 128 KB
-constexpr size_t GRAM_LDS = ((size_t)(MRING * 2 + 2) * M_SLOTS + MRING * 256) * 16;   // 96 KB
+constexpr size_t GRAM_LDS = ((size_t)(GRING * 4 + 4) * M_SLOTS + GRING * 512) * 16;   // 152 KB
 
 size_t lnq_gram_partial_floats(int64_t d_out, int64_t d, int m) {
     const int64_t nta = (d + MT - 1) / MT;
