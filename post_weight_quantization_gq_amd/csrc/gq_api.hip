@@ -327,23 +327,22 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
     if (o.init == GQ_INIT_QUANTILE &&
         (e = gq::lnq_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
         return hip_fail(e, "init");
+    if (iters > 0 && (e = gq::lnq_zero_counter(w.cnt, st)) != hipSuccess)
+        return hip_fail(e, "counter");
     for (int t = 1; t <= iters; ++t) {
         // codebook step; objA = objective before it (trace entry 2t-2), from scratch
         if ((e = gq::lnq_codebook_step(W, wb, d_out, d_in, groups, m, P, C, w, w.objA, w.cnt + 1,
                                        st)) != hipSuccess)
             return hip_fail(e, "codebook");
-        if ((e = gq::lnq_zero_counter(w.cnt, st)) != hipSuccess) return hip_fail(e, "counter");
         // assignment pass; objB = objective after the codebook step (entry 2t-1), from scratch
         if ((e = gq::lnq_sweep_step(o.block, F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB,
                                     w.objC, w.cnt, st)) != hipSuccess)
             return hip_fail(e, "sweep");
-        if (obj_trace) {
-            if ((e = gq::lnq_reduce(w.objA, d_out, obj_trace + 2 * t - 2, st)) != hipSuccess ||
-                (e = gq::lnq_reduce(w.objB, d_out, obj_trace + 2 * t - 1, st)) != hipSuccess)
-                return hip_fail(e, "trace");
-        }
-        if (n_changed && (e = gq::lnq_store_counter(w.cnt, n_changed + (t - 1), st)) != hipSuccess)
-            return hip_fail(e, "counter");
+        // trace entries 2t-2 and 2t-1, the pass's move count, counter cleared
+        if ((e = gq::lnq_iter_tail(w.objA, w.objB, d_out,
+                                   obj_trace ? obj_trace + 2 * t - 2 : nullptr, w.cnt,
+                                   n_changed ? n_changed + (t - 1) : nullptr, st)) != hipSuccess)
+            return hip_fail(e, "iteration tail");
     }
     if (obj_trace) {
         // objective of the final (C, P), from scratch

@@ -81,6 +81,10 @@ hipError_t lnq_sweep_step(int block, const float* F, const void* W, bool w_bf16,
                           unsigned long long* counter, hipStream_t st);
 hipError_t lnq_reduce(const double* rows, int64_t n, double* out, hipStream_t st);
 hipError_t lnq_zero_counter(unsigned long long* c, hipStream_t st);
+// after iteration t: trace[0..1] = sums of objA and objB (if trace), *n_changed = *cnt
+// (if n_changed), *cnt = 0
+hipError_t lnq_iter_tail(const double* objA, const double* objB, int64_t n, double* trace,
+                         unsigned long long* cnt, int64_t* n_changed, hipStream_t st);
 hipError_t lnq_store_counter(const unsigned long long* c, int64_t* dst, hipStream_t st);
 
 }  // namespace gq

@@ -22,6 +22,7 @@
 //                  also the row objective e . r
 //   k_sweep        per 16-row group: the ascending coordinate pass (see there)
 //   k_reduce_rows  float64 layer sums in a fixed order
+//   k_iter_tail    per iteration: the two trace sums, the move count, counter reset
 #include "gq_common.h"
 #include "gq_internal.h"
 
@@ -160,9 +161,11 @@ __global__ __launch_bounds__(1024) void k_lnq_init(const void* __restrict__ W, i
 }
 
 // ---------------------------------------------------------------------------
-// E = C[j][P[j][i]] - W[j][i] (float32) -> k-blocked bf16 planes hi + lo.  One
-// thread per (16-block of k, padded row): 16 elements, 32 contiguous bytes per
-// plane; padding rows (past a group's rows) are zero.
+// E = C[j][P[j][i]] - W[j][i] (float32) -> k-blocked bf16 planes hi + lo.  A block
+// covers 64 padded rows x 64 k; thread t takes row t / 4 and k-block t % 4 (16
+// elements), so a wave reads 16 rows x 64 contiguous bytes of codes (x 128 of
+// weights) and writes, per k-block, 16 consecutive rows = 512 contiguous bytes
+// per plane.  Padding rows (past a group's rows) are zero.
 // ---------------------------------------------------------------------------
 template <bool WBF16>
 __global__ __launch_bounds__(256) void k_err_split(const float* __restrict__ C, int m,
@@ -170,17 +173,17 @@ __global__ __launch_bounds__(256) void k_err_split(const float* __restrict__ C, 
                                                   const void* __restrict__ W, int64_t d,
                                                   int64_t rpg, int64_t rpg_pad, int64_t erows,
                                                   uint16_t* __restrict__ Ehi,
-                                                  uint16_t* __restrict__ Elo, int64_t total) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= total) return;
-    const int64_t rowp = idx % erows;
-    const int64_t kb = idx / erows;
+                                                  uint16_t* __restrict__ Elo, int64_t unused) {
+    (void)unused;
+    const int64_t rowp = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+    const int64_t kb = (int64_t)blockIdx.y * 4 + (threadIdx.x & 3);
+    if (rowp >= erows || kb * 16 >= d) return;
     const int64_t g = rowp / rpg_pad, jl = rowp - g * rpg_pad;
     u32x4 h[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}}, l[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     if (jl < rpg) {
         const int64_t j = g * rpg + jl;
-        const int64_t e0 = j * d + kb * 16;
         const float* cj = C + j * m;
+        const int64_t e0 = j * d + kb * 16;
         const u32x4 pc = *(const u32x4*)(P + e0);
         float w[16];
         if constexpr (WBF16) {
@@ -258,19 +261,38 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
 #pragma unroll
     for (int k = 0; k < M; ++k) { gl[k] = 0.f; cnt[k] = 0; }
     if (valid) {
-        for (int64_t a = lane; a < d; a += 64) {
-            const int code = P[j * d + a];
-            const float r = R[j * d + a];
-            float ck = cv[0];
+        // 4 consecutive coordinates per lane and step (d % 32 == 0: aligned vectors)
+        const uint8_t* Pj = P + j * d;
+        const float* Rj = R + j * d;
+#pragma unroll 2
+        for (int64_t a0 = 4 * lane; a0 < d; a0 += 256) {
+            const uint32_t c4 = *(const uint32_t*)(Pj + a0);
+            const float4 r4 = *(const float4*)(Rj + a0);
+            float wv[4];
+            if constexpr (WBF16) {
+                const u32x2 w2 = *(const u32x2*)((const uint16_t*)W + j * d + a0);
+                wv[0] = __uint_as_float(w2[0] << 16); wv[1] = __uint_as_float(w2[0] & 0xffff0000u);
+                wv[2] = __uint_as_float(w2[1] << 16); wv[3] = __uint_as_float(w2[1] & 0xffff0000u);
+            } else {
+                const float4 w4 = *(const float4*)((const float*)W + j * d + a0);
+                wv[0] = w4.x; wv[1] = w4.y; wv[2] = w4.z; wv[3] = w4.w;
+            }
+            const float rv[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
-            for (int k = 1; k < M; ++k) ck = (code == k) ? cv[k] : ck;
-            const float e = ck - load_elem<WBF16>(W, j * d + a);
-            o += (double)e * (double)r;
-            if (SOLVE) {
+            for (int u = 0; u < 4; ++u) {
+                const int code = (int)((c4 >> (8 * u)) & 0xffu);
+                const float r = rv[u];
+                float ck = cv[0];
 #pragma unroll
-                for (int k = 0; k < M; ++k) {
-                    gl[k] += (code == k) ? r : 0.f;
-                    cnt[k] += (code == k) ? 1 : 0;
+                for (int k = 1; k < M; ++k) ck = (code == k) ? cv[k] : ck;
+                const float e = ck - wv[u];
+                o += (double)e * (double)r;
+                if (SOLVE) {
+#pragma unroll
+                    for (int k = 0; k < M; ++k) {
+                        gl[k] += (code == k) ? r : 0.f;
+                        cnt[k] += (code == k) ? 1 : 0;
+                    }
                 }
             }
         }
@@ -623,6 +645,36 @@ __global__ void k_add_i64(const unsigned long long* __restrict__ src, int64_t* _
     *dst += (int64_t)*src;
 }
 
+// End of one LNQ iteration, in one launch: block 0 sums the objectives before the
+// codebook step (trace entry 2t - 2), block 1 those before the assignment pass
+// (entry 2t - 1), each in a fixed order; block 2 stores the pass's move count and
+// clears the counter for the next pass.
+__global__ __launch_bounds__(256) void k_iter_tail(const double* __restrict__ objA,
+                                                  const double* __restrict__ objB, int64_t n,
+                                                  double* __restrict__ trace,
+                                                  unsigned long long* __restrict__ cnt,
+                                                  int64_t* __restrict__ n_changed) {
+    __shared__ double red[256];
+    if (blockIdx.x == 2) {
+        if (threadIdx.x == 0) {
+            if (n_changed) *n_changed = (int64_t)*cnt;
+            *cnt = 0ull;
+        }
+        return;
+    }
+    if (!trace) return;
+    const double* x = blockIdx.x == 0 ? objA : objB;
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += 256) s += x[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) trace[blockIdx.x] = red[0];
+}
+
 __global__ void k_zero_u64(unsigned long long* __restrict__ p, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0ull;
@@ -719,8 +771,8 @@ hipError_t lnq_residual_from(const float* C, int m, const uint8_t* P, const void
         StageTimer tm(ST_LNQ_RESID, st);
         const int64_t rpg = d_out / groups, rpg_pad = lnq_pad256(rpg);
         const int64_t erows = (int64_t)groups * rpg_pad;
-        const int64_t total = erows * (d / 16);
-        const dim3 grid((unsigned)((total + 255) / 256));
+        const int64_t total = 0;
+        const dim3 grid((unsigned)(erows / 64), (unsigned)((d / 16 + 3) / 4));   // erows % 256 == 0
         if (w_bf16)
             hipLaunchKernelGGL(k_err_split<true>, grid, dim3(256), 0, st, C, m, P, W, d, rpg,
                                rpg_pad, erows, w.ehi, w.elo, total);
@@ -809,6 +861,15 @@ hipError_t lnq_sweep_step(int block, const float* F, const void* W, bool w_bf16,
 hipError_t lnq_reduce(const double* rows, int64_t n, double* out, hipStream_t st) {
     StageTimer tm(ST_LNQ_SMALL, st);
     hipLaunchKernelGGL(k_reduce_rows, dim3(1), dim3(256), 0, st, rows, n, out);
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
+}
+
+hipError_t lnq_iter_tail(const double* objA, const double* objB, int64_t n, double* trace,
+                         unsigned long long* cnt, int64_t* n_changed, hipStream_t st) {
+    StageTimer tm(ST_LNQ_SMALL, st);
+    hipLaunchKernelGGL(k_iter_tail, dim3(3), dim3(256), 0, st, objA, objB, n, trace, cnt,
+                       n_changed);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }
