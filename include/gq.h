@@ -130,8 +130,10 @@ size_t gq_lnq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_
  * coordinate; codes that own none keep their value.  F' = F_g(j) + lambda I.
  * F [groups][d_in][d_in], W [d_out][d_in] (w_dt), P [d_out][d_in] (read),
  * C [d_out][m] (read, then overwritten).  A row whose m x m system is not
- * positive definite (possible only with ridge_rel == 0) keeps its codebook and
- * is counted in *n_not_pd (device int64, may be NULL; incremented, not reset).
+ * positive definite keeps its codebook and is counted in *n_not_pd (device
+ * int64, may be NULL; incremented, not reset).  This happens for every row of a
+ * group whose Fisher is zero (all its output gradients vanish, so lambda = 0 and
+ * F' = 0), and can happen with ridge_rel == 0.
  * Shape limits shared by every lnq_* call: 1 <= bits <= 4, d_out % groups == 0,
  * d_in % 32 == 0, 32 <= d_in <= 32768, ridge_rel finite and >= 0 (GQ_EINVAL /
  * GQ_ESHAPE otherwise).

@@ -156,12 +156,20 @@ def codebook_system(Fp: np.ndarray, w: np.ndarray, p: np.ndarray, m: int):
 
 
 def codebook_update(Fp: np.ndarray, w: np.ndarray, p: np.ndarray, c: np.ndarray) -> np.ndarray:
-    """c <- (P^T F' P)^{-1} P^T F' w on the non-empty codes; empty codes keep c  [LNQ-alg]."""
+    """c <- (P^T F' P)^{-1} P^T F' w on the non-empty codes; empty codes keep c  [LNQ-alg].
+
+    When P^T F' P on the non-empty codes is not positive definite (F' = 0, the
+    damped Fisher of a group whose gradients all vanish) the closed form does not
+    exist and the codebook is kept unchanged.
+    """
     m = c.shape[0]
     A, b = codebook_system(Fp, w, p, m)
     counts = np.bincount(np.asarray(p, np.int64), minlength=m)
     S = np.nonzero(counts > 0)[0]
-    L = np.linalg.cholesky(A[np.ix_(S, S)])
+    try:
+        L = np.linalg.cholesky(A[np.ix_(S, S)])
+    except np.linalg.LinAlgError:
+        return np.array(c, dtype=np.float64, copy=True)
     y = np.linalg.solve(L, b[S])
     x = np.linalg.solve(L.T, y)
     c_new = np.array(c, dtype=np.float64, copy=True)

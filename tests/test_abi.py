@@ -73,6 +73,8 @@ def test_lnq_argument_errors():
     assert q(F=None) == B.GQ_EINVAL
     assert q(wdt=5) == B.GQ_EDTYPE
     assert q(d_out=63) == B.GQ_ESHAPE
+    assert q(d_out=0) == B.GQ_ESHAPE and "empty" in _err(lib)
+    assert q(d_in=0) == B.GQ_ESHAPE and "empty" in _err(lib)
     assert q(d_in=250) == B.GQ_ESHAPE
     assert q(d_in=65536) == B.GQ_ENOTIMPL
     assert q(bits=5) == B.GQ_EINVAL and "bits" in _err(lib)

@@ -339,6 +339,55 @@ def test_ridge_makes_rank_deficient_fisher_solvable():
 # Initialisation (reading; pinned to the textbook linear quantile)
 # --------------------------------------------------------------------------
 
+
+def test_zero_fisher_group_keeps_state():
+    """A group whose gradients all vanish has F = 0, hence lambda = 0 and F' = 0.
+    Every objective is 0, the codebook system P^T F' P = 0 has no unique solution
+    (the codebook is kept), no coordinate strictly decreases the objective (no
+    move), so LNQ returns its quantile initialisation unchanged."""
+    rng = _rng(77)
+    d, m = 64, 8
+    X = rng.standard_normal((50, d))
+    G = np.zeros((50, 4))
+    G[:, :2] = rng.standard_normal((50, 2))
+    F = O.fisher(X, G, 2)
+    assert np.all(F[1] == 0.0) and np.any(F[0] != 0.0)
+    Fp = O.damped(F[1], 1e-6)
+    assert O.ridge_lambda(F[1], 1e-6) == 0.0 and np.all(Fp == 0.0)
+    w = rng.standard_normal(d)
+    c0, p0 = O.init_quantile(w, m)
+    c, p, tr = O.lnq_row(Fp, w, m, 3)
+    np.testing.assert_array_equal(c, c0)
+    np.testing.assert_array_equal(p, p0)
+    assert np.all(tr == 0.0)
+    # with a positive definite F' the same state does move
+    c1, p1, _ = O.lnq_row(O.damped(F[0], 1e-6), w, m, 1)
+    assert np.any(c1 != c0)
+
+
+def test_degenerate_rows_init_and_lnq():
+    """All-zero and constant rows: every quantile is that constant, every
+    coordinate takes code 0 (lowest index on ties), the objective is 0 at the start
+    and stays 0; a row with two distinct values is reproduced exactly (each
+    coordinate lands on an entry equal to its own value)."""
+    rng = _rng(78)
+    d, m = 64, 8
+    F = _spd(rng, d)
+    Fp = O.damped(F, 1e-6)
+    for val in (0.0, 0.0137):
+        w = np.full(d, val)
+        c, p = O.init_quantile(w, m)
+        np.testing.assert_array_equal(c, np.full(m, np.float64(np.float32(val))))
+        np.testing.assert_array_equal(p, np.zeros(d, np.int64))
+        c3, p3, tr = O.lnq_row(Fp, w, m, 3)
+        np.testing.assert_array_equal(p3, p)
+        assert tr[-1] <= 1e-28 + 1e-12 * (w @ Fp @ w)
+    w = np.where(rng.random(d) < 0.3, -0.5, 0.25)
+    c, p, tr = O.lnq_row(Fp, w, m, 2)
+    assert tr[-1] <= 1e-12 * (w @ Fp @ w)
+    dist = np.minimum(np.abs(c[p] + 0.5), np.abs(c[p] - 0.25))
+    assert dist.max() <= 1e-12
+
 @pytest.mark.parametrize("N,m", [(128, 8), (4096, 8), (11008, 4), (100, 16), (5, 2)])
 def test_init_quantile_is_textbook_linear_quantile(N, m):
     rng = _rng(N + m)
