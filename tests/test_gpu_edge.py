@@ -19,6 +19,12 @@
     exact (objective 0, codebook unchanged); the final objective of the other
     classes within 1e-3 relative of the oracle's own run, or 1e-9 of the
     objective of quantising every weight to zero where the oracle reaches 0.
+  * The widest layer the LNQ entry points take, d_in = 32768 (one group's bf16
+    plane of F' is 2 GiB): initial codebooks and codes identical to the
+    oracle's on every row, the GPU trace monotone, and one sampled row per group
+    within 1e-3 of the oracle's own run (one LNQ iteration).  F is torch's
+    float32 product of the seeded activations, made exactly symmetric, so no
+    oracle input comes from the library.
 """
 import sys
 
@@ -208,3 +214,44 @@ def test_lnq_degenerate_rows(device, bits):
             scale += w[j] @ Fj @ w[j]
         _progress(f"degenerate rows {lo}-{hi} bits={bits}: gpu {gpu:.6e} oracle {ref:.6e}")
         assert abs(gpu - ref) <= 1e-3 * ref + 1e-9 * scale
+
+
+@pytest.mark.timeout(900)
+def test_lnq_max_width(device):
+    wl = _wl("maxwidth", 32768, 32, 4096, 2, bits=3, index=45)
+    inp = synth.make_inputs(wl, seed=0)
+    _progress(f"max width: d_in={wl.d_in} d_out={wl.d_out} groups={wl.groups}")
+    S = O.group_scale(synth.decode(inp["G"]), wl.groups).astype(np.float32)
+    X = to_dev(inp["X"], device).float()
+    XT = X.t().contiguous()
+    F = torch.empty((wl.groups, wl.d_in, wl.d_in), dtype=torch.float32, device=device)
+    for g in range(wl.groups):
+        Fg = torch.mm(XT, X * torch.from_numpy(S[g]).to(device)[:, None])
+        F[g] = (Fg + Fg.t()) * 0.5
+        del Fg
+    del X, XT
+    W = to_dev(inp["W"], device)
+    w = synth.decode(inp["W"])
+    m, rpg, iters = wl.m, wl.d_out // wl.groups, 1
+    C0, P0, _, _ = gq.lnq_quantize(W, F, wl.bits, 0)
+    C, P, tr, _ = gq.lnq_quantize(W, F, wl.bits, iters, ridge_rel=RHO)
+    torch.cuda.synchronize()
+    _progress("max width: GPU LNQ done")
+    C0, P0 = f64(C0), P0.cpu().numpy()
+    C, P, tr = f64(C), P.cpu().numpy(), tr.cpu().numpy()
+    assert np.all(tr[1:] <= tr[:-1] * (1 + 1e-6)), tr
+    for j in range(wl.d_out):
+        c_init, p_init = O.init_quantile(w[j], m)
+        np.testing.assert_array_equal(C0[j], c_init)
+        np.testing.assert_array_equal(P0[j], p_init)
+    rng = np.random.default_rng(7)
+    for g in range(wl.groups):
+        Fp = O.damped(F[g].cpu().double().numpy(), RHO)
+        j = g * rpg + int(rng.integers(rpg))
+        _, _, t_ref = O.lnq_row(Fp, w[j], m, iters)
+        gpu = O.objective(Fp, w[j], C[j], P[j])
+        _progress(f"max width: row {j} gpu {gpu:.6e} oracle {t_ref[-1]:.6e}")
+        assert abs(gpu - t_ref[-1]) <= 1e-3 * t_ref[-1]
+        del Fp
+    del F
+    torch.cuda.empty_cache()
