@@ -83,37 +83,61 @@ def _traffic(stage, wl):
     return t[3] + t[4]
 
 
-def _stage_units(stage, wl, changed_total):
-    """Algorithmic work of a stage in one step: (bound, amount, peak, unit).
+def _incremental_iters(wl, nchg):
+    """Iterations whose codebook step updates A and the residual from the previous
+    pass's changed coordinates (the library's switch: at most d_out d_in (m + 3) 3 / 1000
+    changes), given the per-pass change counts."""
+    lim = wl.d_out * wl.d_in * (wl.m + 3) * 3 // 1000
+    return [t for t in range(2, wl.iters + 1) if nchg[t - 2] <= lim]
+
+
+def _stage_units(stage, wl, nchg):
+    """Algorithmic work of a stage in one step: (bound, amount, peak, unit, launches).
 
     The contractions count the flops of the bf16 products the method runs: F' and the
     error E enter as bf16 hi + lo pairs to reach float32-level accuracy, so the
     residual is three bf16 products and the codebook Gram two (its one-hot operand
-    is exact in bf16), over the upper triangle of 256-wide tiles of F'.
+    is exact in bf16), over the upper triangle of 256-wide tiles of F'.  `launches` is
+    the number of launches per step that do the work (a step after a pass with few
+    changes skips the Gram and the residual before it; those launches return at
+    once), or None when every launch does.
     """
     n, d, d_out, G, m, it = wl.n, wl.d_in, wl.d_out, wl.groups, wl.m, wl.iters
+    incr = _incremental_iters(wl, nchg)
+    dense = it - len(incr)
     if stage == "fisher_mfma":
         # unique entries of the symmetric F_g: n d (d + 1) flops per group
-        return "mfma", n * d * (d + 1) * G, PEAK_BF16_MFMA, "TFLOP/s"
+        return "mfma", n * d * (d + 1) * G, PEAK_BF16_MFMA, "TFLOP/s", None
     if stage == "lnq_gram":
         ntile = (d + 255) // 256
         tri = sum(min(256, d - 256 * t) * (d - 256 * t) for t in range(ntile))
-        return "mfma", it * 2 * 2 * tri * d_out * m, PEAK_BF16_MFMA, "TFLOP/s"
+        return "mfma", dense * 2 * 2 * tri * d_out * m, PEAK_BF16_MFMA, "TFLOP/s", dense
     if stage == "lnq_resid":
-        # 2 iters + 1 residuals per step, each E F' per group as three bf16 products
-        return "mfma", (2 * it + 1) * 3 * 2 * d_out * d * d, PEAK_BF16_MFMA, "TFLOP/s"
+        # before each recomputed codebook step, before each pass, and the final objective;
+        # each E F' per group as three bf16 products
+        calls = dense + it + 1
+        return "mfma", calls * 3 * 2 * d_out * d * d, PEAK_BF16_MFMA, "TFLOP/s", calls
+    if stage == "lnq_delta":
+        # per updated step: one float32 row of F per changed coordinate, old and new codes,
+        # the residual read and written, the per-slice shares of A written
+        nsl = (d + 511) // 512
+        amount = sum(4 * d * float(nchg[t - 2]) + d_out * d * (1 + 1 + 4 + 4) +
+                     d_out * nsl * m * m * 4 for t in incr)
+        return "hbm", amount, PEAK_HBM, "GB/s", len(incr)
     if stage == "lnq_sweep":
         # m candidate changes (3 flops each) per coordinate, 2 d flops per move
-        return "alu", it * d_out * d * 3 * m + 2 * d * changed_total, PEAK_FP32_VALU, "TFLOP/s"
+        return ("alu", it * d_out * d * 3 * m + 2 * d * float(np.sum(nchg)), PEAK_FP32_VALU,
+                "TFLOP/s", None)
     if stage == "lnq_solve":
         # per call: read R, P, W and the Gram partials
         ntile = (d + 255) // 256
-        return "hbm", (it + 1) * d_out * (d * (4 + 1 + 2) + ntile * m * m * 4), PEAK_HBM, "GB/s"
+        return ("hbm", (it + 1) * d_out * (d * (4 + 1 + 2) + ntile * m * m * 4), PEAK_HBM,
+                "GB/s", None)
     if stage == "group_scale":
-        return "hbm", 2 * n * d_out + 4 * G * n, PEAK_HBM, "GB/s"
+        return "hbm", 2 * n * d_out + 4 * G * n, PEAK_HBM, "GB/s", None
     if stage == "fisher_pack":
         # read X, write XT and YT (bf16)
-        return "hbm", 2 * n * d + 2 * (1 + G) * n * d, PEAK_HBM, "GB/s"
+        return "hbm", 2 * n * d + 2 * (1 + G) * n * d, PEAK_HBM, "GB/s", None
     return None
 
 
@@ -209,11 +233,11 @@ def main():
     # roofline of the stage with the largest share of the step, from the events of
     # the timed region
     roof = None
-    spec = _stage_units(dom, wl, float(np.sum(nchg)))
+    spec = _stage_units(dom, wl, nchg)
     if spec is not None and timed[dom][1]:
-        bound, amount, peak, unit = spec
-        n_launch = timed[dom][1] / args.steps
-        avg_ms = timed[dom][0] / timed[dom][1]
+        bound, amount, peak, unit, working = spec
+        n_launch = timed[dom][1] / args.steps if working is None else working
+        avg_ms = timed[dom][0] / args.steps / n_launch
         per_launch = amount / n_launch
         achieved = per_launch / (avg_ms * 1e-3)
         scale = 1e9 if unit == "GB/s" else 1e12
@@ -248,6 +272,7 @@ def main():
         "stage_launches_per_step": launches,
         "stage_breakdown_from": "last warmup step, every stage bracketed by HIP events",
         "changed_per_sweep": [int(x) for x in nchg],
+        "codebook_steps_from_changes": _incremental_iters(wl, nchg),
         "objective_trace": [float(x) for x in trace],
         "monotone": bool(np.all(trace[1:] <= trace[:-1] * (1 + 1e-6))),
         "roofline": roof,

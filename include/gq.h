@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 1
+#define GQ_ABI_VERSION 2
 
 typedef enum {
     GQ_OK = 0,
@@ -75,6 +75,8 @@ typedef enum { GQ_F32 = 0, GQ_BF16 = 1 } gq_dtype;
 
 typedef enum { GQ_INIT_QUANTILE = 0, GQ_INIT_GIVEN = 1 } gq_lnq_init;
 
+typedef enum { GQ_GRAM_AUTO = 0, GQ_GRAM_DENSE = 1 } gq_gram_update;
+
 typedef struct {
     int32_t block;      /* assignment block: coordinates decided exactly in registers (one per
                            lane of a 64-wide wavefront) before the effect of their moves on the
@@ -87,7 +89,13 @@ typedef struct {
                            (q + 1/2)/m (linear interpolation between order statistics),
                            codes = nearest entry (lowest index on ties).  GIVEN: start from
                            the C and P passed in.  Default QUANTILE. */
-    int32_t reserved;   /* must be 0 */
+    int32_t gram_update; /* gq_gram_update: how each codebook step after the first obtains
+                           A_j = P_j^T F' P_j and the residual F'(C[P] - W).  DENSE:
+                           recomputed from scratch on the matrix cores.  AUTO: when the
+                           previous assignment pass changed at most a set share of the
+                           codes (see lnq_quantize), updated from the changed coordinates
+                           only (equal up to float rounding), else recomputed.
+                           Default AUTO. */
 } gq_lnq_options;
 
 /* ABI version of the loaded library (GQ_ABI_VERSION). */
@@ -177,9 +185,13 @@ gq_status lnq_objective(const float* F, int32_t groups, int64_t d_in,
  * W [d_out][d_in] (w_dt), F [groups][d_in][d_in]; C [d_out][2^bits] and
  * P [d_out][d_in] are outputs (inputs too when opt->init == GQ_INIT_GIVEN).
  * obj_trace (device float64 [2*iters+1], may be NULL): layer objective
- * sum_j e_j^T F' e_j at the start and after every half-step; each entry is
- * evaluated from scratch from (C, P).  n_changed (device int64 [iters], may be
- * NULL): coordinates changed by each assignment pass (overwritten).
+ * sum_j e_j^T F' e_j at the start and after every half-step, from the residual
+ * F'(C[P] - W) each step uses: recomputed from (C, P), except that under
+ * GQ_GRAM_AUTO the entry before a codebook step that follows a pass with at most
+ * d_out * d_in * (2^bits + 3) * 3 / 1000 changes comes from the residual updated
+ * by the changed coordinates (equal up to float rounding).  The last entry is
+ * always recomputed.  n_changed (device int64 [iters], may be NULL): coordinates
+ * changed by each assignment pass (overwritten).
  * opt == NULL means the defaults.  Requires 1 <= bits <= 4, iters >= 0.
  */
 gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in,
@@ -213,6 +225,7 @@ typedef enum {
     GQ_STAGE_LNQ_SWEEP,         /* the assignment pass */
     GQ_STAGE_LNQ_SMALL,         /* sums and counters */
     GQ_STAGE_FISHER_PACK,       /* feature-major bf16 operands of the Fisher contraction */
+    GQ_STAGE_LNQ_DELTA,         /* Gram and residual updates from the changed coordinates */
     GQ_STAGE_COUNT
 } gq_stage;
 

@@ -17,7 +17,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "li
 GQ_OK, GQ_EINVAL, GQ_ESHAPE, GQ_EDTYPE, GQ_ENOMEM, GQ_EHIP, GQ_ENOTIMPL = 0, 1, 2, 3, 4, 5, 8
 GQ_F32, GQ_BF16 = 0, 1
 GQ_INIT_QUANTILE, GQ_INIT_GIVEN = 0, 1
-ABI_VERSION = 1
+GQ_GRAM_AUTO, GQ_GRAM_DENSE = 0, 1
+ABI_VERSION = 2
 
 # every symbol include/gq.h declares
 EXPORTS = (
@@ -25,7 +26,7 @@ EXPORTS = (
     "gq_fisher_accumulate", "gq_lnq_workspace_size", "lnq_codebook_update", "lnq_assign_sweep",
     "lnq_objective", "lnq_quantize", "gq_timing_enable", "gq_timing_read", "gq_stage_name",
 )
-STAGE_COUNT = 12
+STAGE_COUNT = 13
 
 
 class GQError(RuntimeError):
@@ -36,9 +37,9 @@ class GQError(RuntimeError):
 
 
 class lnq_options(ctypes.Structure):
-    """gq_lnq_options (block, ridge_rel, init, reserved)."""
+    """gq_lnq_options (block, ridge_rel, init, gram_update)."""
     _fields_ = [("block", ctypes.c_int32), ("ridge_rel", ctypes.c_float),
-                ("init", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("init", ctypes.c_int32), ("gram_update", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -130,10 +131,11 @@ def abi_version() -> int:
     return library().gq_abi_version()
 
 
-def options(block: int = 64, ridge_rel: float = 1e-6, init: int = GQ_INIT_QUANTILE) -> lnq_options:
+def options(block: int = 64, ridge_rel: float = 1e-6, init: int = GQ_INIT_QUANTILE,
+            gram_update: int = GQ_GRAM_AUTO) -> lnq_options:
     o = lnq_options()
     library().gq_lnq_options_default(ctypes.byref(o))
-    o.block, o.ridge_rel, o.init = block, ridge_rel, init
+    o.block, o.ridge_rel, o.init, o.gram_update = block, ridge_rel, init, gram_update
     return o
 
 
@@ -236,7 +238,7 @@ def lnq_objective(F, W, C, P, bits: int, ridge_rel: float = 1e-6, obj_total=None
 
 def lnq_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float = 1e-6,
                  C=None, P=None, init: int | None = None, trace: bool = True,
-                 ws=None, stream=None):
+                 ws=None, stream=None, gram_update: int = GQ_GRAM_AUTO):
     """Whole LNQ on a layer.  Returns (C, P, obj_trace or None, n_changed).
 
     With C and P given and init unset, starts from them (GQ_INIT_GIVEN).
@@ -255,7 +257,7 @@ def lnq_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float 
     _dev(P, "P", torch.uint8)
     tr = torch.empty(2 * iters + 1, dtype=torch.float64, device=W.device) if trace else None
     nch = torch.zeros(max(iters, 1), dtype=torch.int64, device=W.device)
-    opt = options(block, ridge_rel, init)
+    opt = options(block, ridge_rel, init, gram_update)
     ws, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
     _check(lib.lnq_quantize(_ptr(W), _dt(W), d_out, d_in, _ptr(F), groups, bits, iters,
                             ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), _ptr(ws),
@@ -265,7 +267,7 @@ def lnq_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float 
 
 STAGES = ("group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain", "lnq_prepare",
           "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep", "lnq_small",
-          "fisher_pack")
+          "fisher_pack", "lnq_delta")
 
 
 def gq_timing_enable(on=True) -> None:

@@ -172,7 +172,7 @@ const char* gq_stage_name(int stage) {
     static const char* names[GQ_STAGE_COUNT] = {
         "group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain", "lnq_prepare",
         "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep", "lnq_small",
-        "fisher_pack"};
+        "fisher_pack", "lnq_delta"};
     if (stage < 0 || stage >= GQ_STAGE_COUNT) return "";
     return names[stage];
 }
@@ -184,7 +184,7 @@ void gq_lnq_options_default(gq_lnq_options* opt) {
     opt->block = 64;
     opt->ridge_rel = 1e-6f;
     opt->init = GQ_INIT_QUANTILE;
-    opt->reserved = 0;
+    opt->gram_update = GQ_GRAM_AUTO;
 }
 
 size_t gq_fisher_workspace_size(int64_t n, int64_t d_in, int64_t d_out, int32_t groups,
@@ -241,8 +241,8 @@ gq_status lnq_codebook_update(const float* F, int32_t groups, int64_t d_in, cons
     gq::LnqWs w = gq::lnq_carve(s.ptr, z);
     hipError_t e;
     if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
-    if ((e = gq::lnq_codebook_step(W, wb, d_out, d_in, groups, m, P, C, w, w.objA,
-                                   (unsigned long long*)n_not_pd, st)) != hipSuccess)
+    if ((e = gq::lnq_codebook_step(F, W, wb, d_out, d_in, groups, m, P, C, w, w.objA,
+                                   (unsigned long long*)n_not_pd, nullptr, st)) != hipSuccess)
         return hip_fail(e, "codebook");
     return GQ_OK;
 }
@@ -268,7 +268,7 @@ gq_status lnq_assign_sweep(const float* F, int32_t groups, int64_t d_in, const v
     hipError_t e;
     if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
     if ((e = gq::lnq_sweep_step(block, F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB, w.objC,
-                                (unsigned long long*)n_changed, st)) != hipSuccess)
+                                (unsigned long long*)n_changed, false, st)) != hipSuccess)
         return hip_fail(e, "sweep");
     return GQ_OK;
 }
@@ -309,7 +309,8 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
     if (!P || !C) return fail(GQ_EINVAL, "null P or C");
     if (!al16(P) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "P must be 16-byte and ws 256-byte aligned");
     if (iters < 0) return fail(GQ_EINVAL, "iters must be >= 0");
-    if (o.reserved != 0) return fail(GQ_EINVAL, "options.reserved must be 0");
+    if (o.gram_update != GQ_GRAM_AUTO && o.gram_update != GQ_GRAM_DENSE)
+        return fail(GQ_EINVAL, "unknown gram_update %d", o.gram_update);
     if (o.init != GQ_INIT_QUANTILE && o.init != GQ_INIT_GIVEN)
         return fail(GQ_EINVAL, "unknown init %d", o.init);
     if (!block_ok(o.block)) return fail(GQ_EINVAL, "block=%d: the pass uses blocks of 64 coordinates", o.block);
@@ -327,21 +328,34 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
     if (o.init == GQ_INIT_QUANTILE &&
         (e = gq::lnq_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
         return hip_fail(e, "init");
-    if (iters > 0 && (e = gq::lnq_zero_counter(w.cnt, st)) != hipSuccess)
+    // w.cnt: [0] moves of the pass, [1] rows not positive definite, [2] update mode
+    if (iters > 0 && (e = gq::lnq_zero_counter(w.cnt, 3, st)) != hipSuccess)
         return hip_fail(e, "counter");
+    // A codebook step after a pass that changed at most incr_max codes updates A and the
+    // residual from the changed coordinates (about 4 d bytes of F read per change)
+    // instead of recomputing them (2 d^2 d_out (m + 3) matrix-core flops).
+    const bool incremental = o.gram_update == GQ_GRAM_AUTO;
+    const int64_t incr_max = incremental ? d_out * d_in * (m + 3) * 3 / 1000 : -1;
     for (int t = 1; t <= iters; ++t) {
-        // codebook step; objA = objective before it (trace entry 2t-2), from scratch
-        if ((e = gq::lnq_codebook_step(W, wb, d_out, d_in, groups, m, P, C, w, w.objA, w.cnt + 1,
-                                       st)) != hipSuccess)
+        // codebook step; objA = objective before it (trace entry 2t-2)
+        if ((e = gq::lnq_codebook_step(F, W, wb, d_out, d_in, groups, m, P, C, w, w.objA,
+                                       w.cnt + 1, incremental ? w.cnt + 2 : nullptr, st)) !=
+            hipSuccess)
             return hip_fail(e, "codebook");
+        // the codes before the pass, for the next step's update
+        if (incremental && t < iters &&
+            (e = hipMemcpyAsync(w.pprev, P, (size_t)d_out * d_in, hipMemcpyDeviceToDevice, st)) !=
+                hipSuccess)
+            return hip_fail(e, "code copy");
         // assignment pass; objB = objective after the codebook step (entry 2t-1), from scratch
         if ((e = gq::lnq_sweep_step(o.block, F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB,
-                                    w.objC, w.cnt, st)) != hipSuccess)
+                                    w.objC, w.cnt, incremental && t < iters, st)) != hipSuccess)
             return hip_fail(e, "sweep");
-        // trace entries 2t-2 and 2t-1, the pass's move count, counter cleared
+        // trace entries 2t-2 and 2t-1, the pass's move count, counter cleared, next mode
         if ((e = gq::lnq_iter_tail(w.objA, w.objB, d_out,
                                    obj_trace ? obj_trace + 2 * t - 2 : nullptr, w.cnt,
-                                   n_changed ? n_changed + (t - 1) : nullptr, st)) != hipSuccess)
+                                   n_changed ? n_changed + (t - 1) : nullptr, incr_max, st)) !=
+            hipSuccess)
             return hip_fail(e, "iteration tail");
     }
     if (obj_trace) {

@@ -9,7 +9,8 @@ namespace gq {
 // ---- per-stage HIP-event timing (gq_api.hip); stage ids are gq_stage of gq.h
 enum Stage {
     ST_GROUP_SCALE = 0, ST_FISHER_MFMA, ST_FISHER_FINALIZE, ST_FISHER_PLAIN, ST_LNQ_PREPARE,
-    ST_LNQ_RESID, ST_LNQ_INIT, ST_LNQ_GRAM, ST_LNQ_SOLVE, ST_LNQ_SWEEP, ST_LNQ_SMALL, ST_FISHER_PACK, ST_COUNT
+    ST_LNQ_RESID, ST_LNQ_INIT, ST_LNQ_GRAM, ST_LNQ_SOLVE, ST_LNQ_SWEEP, ST_LNQ_SMALL, ST_FISHER_PACK,
+    ST_LNQ_DELTA, ST_COUNT
 };
 bool timing_on(Stage s);
 void timing_mark(Stage s, hipStream_t st, bool begin);
@@ -42,7 +43,8 @@ __host__ __device__ inline int64_t lnq_pad256(int64_t x) { return (x + 255) / 25
 
 struct LnqSizes {
     size_t o_fhi, o_flo, o_dF, o_lam, o_R, o_ehi, o_elo, o_part;
-    size_t o_objA, o_objB, o_objC, o_cnt, total;
+    size_t o_objA, o_objB, o_objC, o_cnt, o_pprev, o_afull, o_clist, o_ccount, o_order, o_dA;
+    size_t total;
 };
 struct LnqWs {
     uint16_t *fhi, *flo;          // F' planes, k-blocked: [groups][d / 16][a_pad][16]
@@ -52,7 +54,16 @@ struct LnqWs {
     uint16_t *ehi, *elo;          // C[P] - W as k-blocked bf16 planes [d / 16][groups * rpg_pad][16]
     float* part;                  // Gram partials [d / 256][d_out * m][m]
     double *objA, *objB, *objC;   // per-row objectives [d_out]
-    unsigned long long* cnt;      // counters [16]
+    unsigned long long* cnt;      // [0] moves of the pass, [1] rows not positive definite,
+                                  // [2] update mode of the next codebook step (0 from
+                                  // scratch, 1 from the changed coordinates)
+    uint8_t* pprev;               // codes before the last assignment pass [d_out][d]
+    double* afull;                // A_j = P_j^T F' P_j of the last codebook step [d_out][m][m]
+    uint32_t* clist;              // moves of the last pass per row, ascending [d_out][d]:
+                                  // coordinate | old code << 16 | new code << 24
+    int* ccount;                  // number of moves per row [d_out]
+    int* order;                   // rows, most moves first [d_out]
+    float* dA;                    // per (row, coordinate slice): share of A_new - A_old
 };
 
 LnqSizes lnq_sizes(int64_t d_out, int64_t d, int groups, int m);
@@ -62,29 +73,37 @@ hipError_t lnq_prepare(const float* F, int groups, int64_t d, double rho, const 
                        hipStream_t st);
 hipError_t lnq_init_run(const void* W, bool w_bf16, int64_t d_out, int64_t d, int m, float* C,
                         uint8_t* P, hipStream_t st);
+// `skip` (device, may be null): the launch does nothing when *skip != 0
 hipError_t lnq_residual(const uint16_t* Ehi, const uint16_t* Elo, int64_t d_out, int64_t d,
                         int groups, const uint16_t* Fhi, const uint16_t* Flo, float* R,
-                        hipStream_t st);
+                        const unsigned long long* skip, hipStream_t st);
 hipError_t lnq_gram(const uint8_t* P, int m, int64_t d_out, int64_t d, int groups,
-                    const uint16_t* Fhi, const uint16_t* Flo, float* part, hipStream_t st);
-// codebook step on every row; obj_before[j] = objective of (C, P) before it
-hipError_t lnq_codebook_step(const void* W, bool w_bf16, int64_t d_out, int64_t d, int groups,
-                             int m, const uint8_t* P, float* C, const LnqWs& w, double* obj_before,
-                             unsigned long long* n_not_pd, hipStream_t st);
+                    const uint16_t* Fhi, const uint16_t* Flo, float* part,
+                    const unsigned long long* skip, hipStream_t st);
+// codebook step on every row; obj_before[j] = objective of (C, P) before it.  With
+// `mode` (device, may be null) set to 1, A and the residual are brought up to date
+// from the coordinates the last pass changed (w.pprev -> P, F the raw Fisher)
+// instead of being recomputed.
+hipError_t lnq_codebook_step(const float* F, const void* W, bool w_bf16, int64_t d_out, int64_t d,
+                             int groups, int m, const uint8_t* P, float* C, const LnqWs& w,
+                             double* obj_before, unsigned long long* n_not_pd,
+                             const unsigned long long* mode, hipStream_t st);
 hipError_t lnq_objective_rows(const void* W, bool w_bf16, int64_t d_out, int64_t d, int groups,
                               int m, const uint8_t* P, const float* C, const LnqWs& w,
                               double* obj, hipStream_t st);
-// assignment pass; obj_start/obj_end[j] = objective before / after it (may be null)
+// assignment pass; obj_start/obj_end[j] = objective before / after it (may be null);
+// record: list the moves of each row (w.clist, w.ccount) for an update from them
 hipError_t lnq_sweep_step(int block, const float* F, const void* W, bool w_bf16, int64_t d_out,
                           int64_t d, int groups, const float* C, int m, uint8_t* P,
                           const LnqWs& w, double* obj_start, double* obj_end,
-                          unsigned long long* counter, hipStream_t st);
+                          unsigned long long* counter, bool record, hipStream_t st);
 hipError_t lnq_reduce(const double* rows, int64_t n, double* out, hipStream_t st);
-hipError_t lnq_zero_counter(unsigned long long* c, hipStream_t st);
-// after iteration t: trace[0..1] = sums of objA and objB (if trace), *n_changed = *cnt
-// (if n_changed), *cnt = 0
+hipError_t lnq_zero_counter(unsigned long long* c, int n, hipStream_t st);
+// after iteration t: trace[0..1] = sums of objA and objB (if trace), *n_changed = cnt[0]
+// (if n_changed), cnt[2] = (0 <= incr_max && cnt[0] <= incr_max), cnt[0] = 0
 hipError_t lnq_iter_tail(const double* objA, const double* objB, int64_t n, double* trace,
-                         unsigned long long* cnt, int64_t* n_changed, hipStream_t st);
+                         unsigned long long* cnt, int64_t* n_changed, int64_t incr_max,
+                         hipStream_t st);
 hipError_t lnq_store_counter(const unsigned long long* c, int64_t* dst, hipStream_t st);
 
 }  // namespace gq

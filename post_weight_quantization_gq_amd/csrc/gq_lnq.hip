@@ -173,8 +173,9 @@ __global__ __launch_bounds__(256) void k_err_split(const float* __restrict__ C, 
                                                   const void* __restrict__ W, int64_t d,
                                                   int64_t rpg, int64_t rpg_pad, int64_t erows,
                                                   uint16_t* __restrict__ Ehi,
-                                                  uint16_t* __restrict__ Elo, int64_t unused) {
-    (void)unused;
+                                                  uint16_t* __restrict__ Elo,
+                                                  const unsigned long long* __restrict__ skip) {
+    if (skip && *skip != 0ull) return;
     const int64_t rowp = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
     const int64_t kb = (int64_t)blockIdx.y * 4 + (threadIdx.x & 3);
     if (rowp >= erows || kb * 16 >= d) return;
@@ -239,7 +240,11 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
                                               const void* __restrict__ W, float* __restrict__ C,
                                               int64_t d, int64_t d_out,
                                               double* __restrict__ obj,
-                                              unsigned long long* __restrict__ n_not_pd) {
+                                              unsigned long long* __restrict__ n_not_pd,
+                                              const unsigned long long* __restrict__ mode,
+                                              double* __restrict__ afull,
+                                              const int* __restrict__ ccount,
+                                              const float* __restrict__ dA, int nslices) {
     __shared__ double sB[4][M][M];
     __shared__ double sL[4][M][M];
     __shared__ double sg[4][M];
@@ -309,17 +314,37 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
         for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
         if (lane == 0) { sg[wave][k] = s; scnt[wave][k] = c; }
     }
-    // B_j[q'][q] = sum over a-tiles of part[ta][(j M + q) M + q'], stored as sB[q][q']
+    // B_j[q'][q] = sum over a-tiles of part[ta][(j M + q) M + q'], stored as sB[q][q'],
+    // so that A = B + B^T.  From the changed coordinates instead (mode 1): sB = A / 2
+    // with A = the stored matrix plus the slices' updates, in slice order.  A is stored
+    // for the next step.
+    const bool incr = mode && *mode != 0ull;
+    double* Aj = afull ? afull + (size_t)j * M * M : nullptr;
     if (valid) {
+        const bool moved = incr && ccount[j] > 0;
         for (int e = lane; e < M * M; e += 64) {
             const int q = e / M, qp = e - q * M;
             double s = 0.0;
-            for (int ta = 0; ta < ntile_a; ++ta)
-                s += (double)part[((size_t)ta * d_out * M + (size_t)(j * M + q)) * M + qp];
+            if (incr) {
+                s = Aj[e];
+                if (moved)
+                    for (int sl = 0; sl < nslices; ++sl)
+                        s += (double)dA[((size_t)j * nslices + sl) * M * M + e];
+                s *= 0.5;
+            } else {
+                for (int ta = 0; ta < ntile_a; ++ta)
+                    s += (double)part[((size_t)ta * d_out * M + (size_t)(j * M + q)) * M + qp];
+            }
             sB[wave][q][qp] = s;
         }
     }
     __syncthreads();
+    if (valid && Aj) {
+        for (int e = lane; e < M * M; e += 64) {
+            const int q = e / M, qp = e - q * M;
+            Aj[e] = sB[wave][q][qp] + sB[wave][qp][q];
+        }
+    }
     if (valid && lane == 0) {
         int ns = 0;
         for (int k = 0; k < M; ++k)
@@ -429,7 +454,8 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
     int64_t d, int64_t rows_per_group, int wgs_per_group, int total_wgs,
     const float* __restrict__ C, int m, uint8_t* __restrict__ P, const void* __restrict__ W,
     float* __restrict__ R, double* __restrict__ obj_start, double* __restrict__ obj_end,
-    unsigned long long* __restrict__ n_changed) {
+    unsigned long long* __restrict__ n_changed, uint32_t* __restrict__ clist,
+    int* __restrict__ ccount) {
     __shared__ __attribute__((aligned(16))) uint16_t dsb_hi[SW_ROWS][SW_DP];   // 16.3 KB
     __shared__ __attribute__((aligned(16))) uint16_t dsb_lo[SW_ROWS][SW_DP];   // 16.3 KB
     __shared__ float corr_p[4][SW_ROWS][SW_SUB];                               // 16 KB
@@ -548,12 +574,15 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
                     const int t = __ffsll((long long)want) - 1;
                     const float delta = readlane_f(bdl, t);
                     dsum += (double)readlane_f(best, t);
-                    moves += 1;
                     r = fmaf(delta, fdb[t][lane], r);     // F[bs + t][bs + lane]
                     if (lane == t) {
+                        if (clist)                        // (coordinate, old code, new code)
+                            clist[j * d + moves] = (uint32_t)col | ((uint32_t)code << 16) |
+                                                   ((uint32_t)bq << 24);
                         code = bq;
                         wh = bc;
                     }
+                    moves += 1;
                     start = t + 1;
                 }
                 P[j * d + col] = (uint8_t)code;
@@ -619,7 +648,282 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
         if (obj_start) obj_start[j] = ostart;
         if (obj_end) obj_end[j] = ostart + dsum;
         if (n_changed) atomicAdd(n_changed, (unsigned long long)moves);
+        if (ccount) ccount[j] = (int)moves;
     }
+}
+
+// ---------------------------------------------------------------------------
+// k_delta: the inputs of the codebook step after an assignment pass that changed
+// few coordinates, from those coordinates alone instead of from scratch.
+//   Gram: with Delta = P_new - P_old (row i equal to e_v - e_u for a coordinate i
+//   that moved from code u to code v, zero elsewhere),
+//       A_new - A_old = Delta^T F' P_old + P_new^T F' Delta = X + Y^T,
+//       X[q][q'] = sum_i (e_v - e_u)[q] (F' P_old)[i][q'],  Y likewise with P_new,
+//   so each changed coordinate needs row i of F' summed by its old and by its new
+//   codes: 2m sums over d, taken on the matrix cores as row i times an exact
+//   one-hot of [old codes | new codes].  F' rows come from the float32 Fisher
+//   (contiguous rows; the diagonal from diag F'), split into bf16 hi + lo as the
+//   dense planes are.
+//   Residual: the pass has already added each move's effect on the coordinates of
+//   later super-blocks; the rest, r[k] += delta_i F'[i][k] for k before the end of
+//   i's super-block, is summed in float32 from the same rows.
+//   Work item = (row, slice of DL_SL coordinates); one block (4 waves) each, rows
+//   taken heaviest first.  The pass lists each row's moves (coordinate, old code,
+//   new code) in ascending order; an item takes them DL_G at a time (tiles of 16,
+//   one MFMA row block each), its waves interleaving the slice's 32-coordinate
+//   chunks.  An item updates the residual of its own coordinates and leaves its
+//   share of A_new - A_old (summed per entry in float64 over the changes, in order)
+//   for the solve, which adds the slices in order.
+// ---------------------------------------------------------------------------
+constexpr int DL_TILES = 4;               // 16-change tiles per group
+constexpr int DL_G = 16 * DL_TILES;       // changes per group
+constexpr int DL_SL = 512;                // coordinates per work item
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// sum over each row of 16 lanes, available in all 16 lanes
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);     // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);     // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v);    // row_half_mirror
+    v += dpp_f<0x140>(v);    // row_mirror
+    return v;
+}
+
+// One wave's share of a group of NT tiles (16 changes each): the interleaved
+// 32-coordinate chunks c_begin + wave, + 4, ... below c_end.  Each batch issues the loads of CB
+// chunks x NT tiles (at most 4 row segments of F per lane), the codes and the
+// residual of those chunks, before any of them is used.  Leaves the wave's partial
+// sums of the F' rows by [old | new] code in hw[change][column].
+template <int M, int NT>
+__device__ __forceinline__ void delta_pass(int n, const int* s_i, const float* s_dl,
+                                           const uint8_t* __restrict__ po,
+                                           const uint8_t* __restrict__ pn,
+                                           const float* __restrict__ Fg,
+                                           const float* __restrict__ dFg, float* __restrict__ Rj,
+                                           int64_t d, int c_begin, int c_end, int wave,
+                                           int lane, float (*hw)[16 * ((2 * M + 15) / 16)]) {
+    constexpr int NB = (2 * M + 15) / 16;
+    constexpr int CB = NT == 1 ? 4 : NT == 2 ? 2 : 1;
+    const int mr = lane & 15, ko = 8 * (lane >> 4);
+    int ci[NT], sbi[NT];
+    float dl[NT];
+    const float* frow[NT];                       // row ci of F (row 0 for an empty slot)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int idx = 16 * t + mr;
+        const bool ok = idx < n;
+        ci[t] = ok ? s_i[idx] : -1;
+        dl[t] = ok ? s_dl[idx] : 0.f;
+        sbi[t] = ok ? ci[t] / SW_SB : -1;
+        frow[t] = Fg + (ok ? (int64_t)ci[t] * d : 0);
+    }
+    f32x4 acc[NT][NB];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[t][nb] = {0.f, 0.f, 0.f, 0.f};
+
+    for (int cb = c_begin + wave; cb < c_end; cb += 4 * CB) {
+        u32x2 co[CB], cn[CB];
+        float4 rr[CB];
+        float f[CB][NT][8];
+#pragma unroll
+        for (int b = 0; b < CB; ++b) {
+            const int c = cb + 4 * b;
+            const int k0 = 32 * c + ko;
+            const bool live = c < c_end;
+            co[b] = live ? *(const u32x2*)(po + k0) : u32x2{0u, 0u};
+            cn[b] = live ? *(const u32x2*)(pn + k0) : u32x2{0u, 0u};
+            rr[b] = (live && mr < 2) ? *(const float4*)(Rj + k0 + 4 * mr)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (live && ci[t] >= 0) {
+                    const float4* src = (const float4*)(frow[t] + k0);
+                    const float4 x0 = src[0], x1 = src[1];
+                    f[b][t][0] = x0.x; f[b][t][1] = x0.y; f[b][t][2] = x0.z; f[b][t][3] = x0.w;
+                    f[b][t][4] = x1.x; f[b][t][5] = x1.y; f[b][t][6] = x1.z; f[b][t][7] = x1.w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) f[b][t][e] = 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < CB; ++b) {
+            const int c = cb + 4 * b;
+            if (c >= c_end) continue;                    // uniform in the wave
+            const int k0 = 32 * c + ko;                  // this lane's 8 coordinates
+            const int sbk = (32 * c) / SW_SB;
+            u32x4 oh[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int col = 16 * nb + mr;
+                const bool isold = col < M, used = col < 2 * M;
+                const uint32_t tgt = (uint32_t)(isold ? col : col - M);
+                const u32x2 cc = isold ? co[b] : cn[b];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t b0 = (cc[e >> 1] >> (16 * (e & 1))) & 0xffu;
+                    const uint32_t b1 = (cc[e >> 1] >> (16 * (e & 1) + 8)) & 0xffu;
+                    oh[nb][e] = ((used && b0 == tgt) ? 0x3F80u : 0u) |
+                                ((used && b1 == tgt) ? 0x3F800000u : 0u);
+                }
+            }
+            float pr[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pr[e] = 0.f;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int off = ci[t] - k0;
+                if ((unsigned)off < 8u) {                 // F'[i][i] = diag F'
+                    const float di = dFg[ci[t]];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (off == e) f[b][t][e] = di;
+                }
+                u32x4 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float f0 = f[b][t][2 * e], f1 = f[b][t][2 * e + 1];
+                    const uint32_t hb = pack_bf16x2(f0, f1);
+                    hi[e] = hb;
+                    lo[e] = pack_bf16x2(f0 - __uint_as_float(hb << 16),
+                                        f1 - __uint_as_float(hb & 0xffff0000u));
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(hi), as_bf16x8(oh[nb]), acc[t][nb], 0, 0, 0);
+                    acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lo), as_bf16x8(oh[nb]), acc[t][nb], 0, 0, 0);
+                }
+                const float dd = (sbi[t] >= sbk) ? dl[t] : 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pr[e] = fmaf(dd, f[b][t][e], pr[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pr[e] = row16_sum(pr[e]);
+            if (mr < 2) {
+                float4 x = rr[b];
+                x.x += mr ? pr[4] : pr[0];
+                x.y += mr ? pr[5] : pr[1];
+                x.z += mr ? pr[6] : pr[2];
+                x.w += mr ? pr[7] : pr[3];
+                *(float4*)(Rj + k0 + 4 * mr) = x;
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hw[16 * t + 4 * (lane >> 4) + e][16 * nb + mr] = acc[t][nb][e];
+}
+
+// Rows in decreasing order of their change counts (buckets of 16 changes, heaviest
+// first), so that the longest work items start first.  One block of 1024 threads.
+__global__ __launch_bounds__(1024) void k_order_rows(const unsigned long long* __restrict__ mode,
+                                                    const int* __restrict__ ccount, int64_t n,
+                                                    int* __restrict__ order) {
+    constexpr int NBK = 64;
+    __shared__ int hist[NBK];
+    __shared__ int base[NBK];
+    if (*mode == 0ull) return;
+    const int tid = threadIdx.x;
+    if (tid < NBK) hist[tid] = 0;
+    __syncthreads();
+    auto bucket = [](int c) {
+        int b = (c + 15) >> 4;
+        b = b < 0 ? 0 : (b > NBK - 1 ? NBK - 1 : b);
+        return NBK - 1 - b;
+    };
+    for (int64_t j = tid; j < n; j += 1024) atomicAdd(&hist[bucket(ccount[j])], 1);
+    __syncthreads();
+    if (tid == 0) {
+        int a = 0;
+        for (int b = 0; b < NBK; ++b) { base[b] = a; a += hist[b]; }
+    }
+    __syncthreads();
+    for (int64_t j = tid; j < n; j += 1024) order[atomicAdd(&base[bucket(ccount[j])], 1)] = (int)j;
+}
+
+template <int M>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(M <= 8 ? 3 : 2, 4))) void k_delta(
+    const unsigned long long* __restrict__ mode, const float* __restrict__ F,
+    const float* __restrict__ dF, int64_t d, int64_t rows_per_group,
+    const uint8_t* __restrict__ Pold, const uint8_t* __restrict__ Pnew,
+    const float* __restrict__ C, float* __restrict__ R, const uint32_t* __restrict__ clist,
+    const int* __restrict__ ccount, const int* __restrict__ order, int nslices,
+    float* __restrict__ dA) {
+    constexpr int NB = (2 * M + 15) / 16;     // 16-column blocks of [old | new] one-hots
+    __shared__ int s_i[DL_G];                 // coordinate of each change of the group
+    __shared__ int s_uv[DL_G];                // old code | new code << 8
+    __shared__ float s_dl[DL_G];              // c[new] - c[old]
+    __shared__ float s_h[4][DL_G][16 * NB];   // per-wave partial sums of the F' rows
+    if (*mode == 0ull) return;
+
+    const int64_t j = order[blockIdx.x / nslices];
+    const int slice = blockIdx.x % nslices;
+    const int K = ccount[j];
+    if (K == 0) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t g = j / rows_per_group;
+    const uint8_t* po = Pold + j * d;
+    const uint8_t* pn = Pnew + j * d;
+    const float* Fg = F + (size_t)g * d * d;
+    const float* dFg = dF + (size_t)g * d;
+    float* Rj = R + j * d;
+    const float* cj = C + j * M;
+    const uint32_t* lj = clist + j * d;
+    const int nch = (int)(d / 32);
+    const int c_begin = slice * (DL_SL / 32);
+    const int c_end = (c_begin + DL_SL / 32) < nch ? (c_begin + DL_SL / 32) : nch;
+    const int aq = tid / M, aqq = tid % M;    // entry of A owned by threads tid < M * M
+    double accA = 0.0;
+
+    for (int g0 = 0; g0 < K; g0 += DL_G) {
+        const int n = (K - g0) < DL_G ? (K - g0) : DL_G;
+        if (tid < n) {
+            const uint32_t e = lj[g0 + tid];
+            const int u = (int)((e >> 16) & 0xffu), v = (int)(e >> 24);
+            s_i[tid] = (int)(e & 0xffffu);
+            s_uv[tid] = u | (v << 8);
+            s_dl[tid] = cj[v] - cj[u];
+        }
+        __syncthreads();
+        switch ((n + 15) >> 4) {
+            case 1: delta_pass<M, 1>(n, s_i, s_dl, po, pn, Fg, dFg, Rj, d, c_begin, c_end, wave, lane, s_h[wave]); break;
+            case 2: delta_pass<M, 2>(n, s_i, s_dl, po, pn, Fg, dFg, Rj, d, c_begin, c_end, wave, lane, s_h[wave]); break;
+            case 3: delta_pass<M, 3>(n, s_i, s_dl, po, pn, Fg, dFg, Rj, d, c_begin, c_end, wave, lane, s_h[wave]); break;
+            default: delta_pass<M, 4>(n, s_i, s_dl, po, pn, Fg, dFg, Rj, d, c_begin, c_end, wave, lane, s_h[wave]); break;
+        }
+        __syncthreads();
+        // ---- this slice's part of A_new - A_old, entry (aq, aqq): X[aq][aqq] + Y[aqq][aq]
+        if (tid < M * M) {
+            for (int kk = 0; kk < n; ++kk) {
+                const int uv = s_uv[kk], u = uv & 0xff, v = uv >> 8;
+                const int sg1 = (v == aq) - (u == aq);
+                const int sg2 = (v == aqq) - (u == aqq);
+                if (sg1) {
+                    const double h = (double)s_h[0][kk][aqq] + s_h[1][kk][aqq] + s_h[2][kk][aqq] +
+                                     s_h[3][kk][aqq];
+                    accA += sg1 * h;
+                }
+                if (sg2) {
+                    const double h = (double)s_h[0][kk][M + aq] + s_h[1][kk][M + aq] +
+                                     s_h[2][kk][M + aq] + s_h[3][kk][M + aq];
+                    accA += sg2 * h;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (tid < M * M) dA[((size_t)j * nslices + slice) * M * M + tid] = (float)accA;
 }
 
 // float64 sums of consecutive rows in a fixed order: out[0] = sum_j x[j]
@@ -653,12 +957,15 @@ __global__ __launch_bounds__(256) void k_iter_tail(const double* __restrict__ ob
                                                   const double* __restrict__ objB, int64_t n,
                                                   double* __restrict__ trace,
                                                   unsigned long long* __restrict__ cnt,
-                                                  int64_t* __restrict__ n_changed) {
+                                                  int64_t* __restrict__ n_changed,
+                                                  int64_t incr_max) {
     __shared__ double red[256];
     if (blockIdx.x == 2) {
         if (threadIdx.x == 0) {
-            if (n_changed) *n_changed = (int64_t)*cnt;
-            *cnt = 0ull;
+            const unsigned long long moves = cnt[0];
+            if (n_changed) *n_changed = (int64_t)moves;
+            cnt[2] = (incr_max >= 0 && moves <= (unsigned long long)incr_max) ? 1ull : 0ull;
+            cnt[0] = 0ull;
         }
         return;
     }
@@ -706,6 +1013,12 @@ LnqSizes lnq_sizes(int64_t d_out, int64_t d, int groups, int m) {
     z.o_objB = take((size_t)d_out * 8);
     z.o_objC = take((size_t)d_out * 8);
     z.o_cnt = take(16 * 8);
+    z.o_pprev = take((size_t)d_out * d);
+    z.o_afull = take((size_t)d_out * m * m * 8);
+    z.o_clist = take((size_t)d_out * d * 4);
+    z.o_ccount = take((size_t)d_out * 4);
+    z.o_order = take((size_t)d_out * 4);
+    z.o_dA = take((size_t)d_out * ((d + DL_SL - 1) / DL_SL) * m * m * 4);
     z.total = off;
     return z;
 }
@@ -725,6 +1038,12 @@ LnqWs lnq_carve(void* base, const LnqSizes& z) {
     w.objB = (double*)(b + z.o_objB);
     w.objC = (double*)(b + z.o_objC);
     w.cnt = (unsigned long long*)(b + z.o_cnt);
+    w.pprev = (uint8_t*)(b + z.o_pprev);
+    w.afull = (double*)(b + z.o_afull);
+    w.clist = (uint32_t*)(b + z.o_clist);
+    w.ccount = (int*)(b + z.o_ccount);
+    w.order = (int*)(b + z.o_order);
+    w.dA = (float*)(b + z.o_dA);
     return w;
 }
 
@@ -766,30 +1085,32 @@ hipError_t lnq_init_run(const void* W, bool w_bf16, int64_t d_out, int64_t d, in
 
 hipError_t lnq_residual_from(const float* C, int m, const uint8_t* P, const void* W, bool w_bf16,
                              int64_t d_out, int64_t d, int groups, const LnqWs& w,
-                             hipStream_t st) {
+                             const unsigned long long* skip, hipStream_t st) {
     {
         StageTimer tm(ST_LNQ_RESID, st);
         const int64_t rpg = d_out / groups, rpg_pad = lnq_pad256(rpg);
         const int64_t erows = (int64_t)groups * rpg_pad;
-        const int64_t total = 0;
         const dim3 grid((unsigned)(erows / 64), (unsigned)((d / 16 + 3) / 4));   // erows % 256 == 0
         if (w_bf16)
             hipLaunchKernelGGL(k_err_split<true>, grid, dim3(256), 0, st, C, m, P, W, d, rpg,
-                               rpg_pad, erows, w.ehi, w.elo, total);
+                               rpg_pad, erows, w.ehi, w.elo, skip);
         else
             hipLaunchKernelGGL(k_err_split<false>, grid, dim3(256), 0, st, C, m, P, W, d, rpg,
-                               rpg_pad, erows, w.ehi, w.elo, total);
+                               rpg_pad, erows, w.ehi, w.elo, skip);
         GQ_LAUNCH_CHECK();
     }
-    return lnq_residual(w.ehi, w.elo, d_out, d, groups, w.fhi, w.flo, w.R, st);
+    return lnq_residual(w.ehi, w.elo, d_out, d, groups, w.fhi, w.flo, w.R, skip, st);
 }
 
 template <int M, bool WB, bool SOLVE>
 static hipError_t launch_solve(const float* part, int nta, const float* R, const uint8_t* P,
                                const void* W, float* C, int64_t d, int64_t d_out, double* obj,
-                               unsigned long long* n_not_pd, hipStream_t st) {
+                               unsigned long long* n_not_pd, const unsigned long long* mode,
+                               const LnqWs* w, hipStream_t st) {
+    const int nsl = (int)((d + DL_SL - 1) / DL_SL);
     hipLaunchKernelGGL((k_solve<M, WB, SOLVE>), dim3((unsigned)((d_out + 3) / 4)), dim3(256), 0,
-                       st, part, nta, R, P, W, C, d, d_out, obj, n_not_pd);
+                       st, part, nta, R, P, W, C, d, d_out, obj, n_not_pd, mode,
+                       w ? w->afull : nullptr, w ? w->ccount : nullptr, w ? w->dA : nullptr, nsl);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }
@@ -797,43 +1118,78 @@ static hipError_t launch_solve(const float* part, int nta, const float* R, const
 template <bool WB, bool SOLVE>
 static hipError_t solve_m(int m, const float* part, int nta, const float* R, const uint8_t* P,
                           const void* W, float* C, int64_t d, int64_t d_out, double* obj,
-                          unsigned long long* n_not_pd, hipStream_t st) {
+                          unsigned long long* n_not_pd, const unsigned long long* mode,
+                          const LnqWs* w, hipStream_t st) {
     switch (m) {
-        case 2: return launch_solve<2, WB, SOLVE>(part, nta, R, P, W, C, d, d_out, obj, n_not_pd, st);
-        case 4: return launch_solve<4, WB, SOLVE>(part, nta, R, P, W, C, d, d_out, obj, n_not_pd, st);
-        case 8: return launch_solve<8, WB, SOLVE>(part, nta, R, P, W, C, d, d_out, obj, n_not_pd, st);
-        case 16: return launch_solve<16, WB, SOLVE>(part, nta, R, P, W, C, d, d_out, obj, n_not_pd, st);
+        case 2: return launch_solve<2, WB, SOLVE>(part, nta, R, P, W, C, d, d_out, obj, n_not_pd, mode, w, st);
+        case 4: return launch_solve<4, WB, SOLVE>(part, nta, R, P, W, C, d, d_out, obj, n_not_pd, mode, w, st);
+        case 8: return launch_solve<8, WB, SOLVE>(part, nta, R, P, W, C, d, d_out, obj, n_not_pd, mode, w, st);
+        case 16: return launch_solve<16, WB, SOLVE>(part, nta, R, P, W, C, d, d_out, obj, n_not_pd, mode, w, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t lnq_codebook_step(const void* W, bool w_bf16, int64_t d_out, int64_t d, int groups,
-                             int m, const uint8_t* P, float* C, const LnqWs& w, double* obj_before,
-                             unsigned long long* n_not_pd, hipStream_t st) {
-    hipError_t e = lnq_residual_from(C, m, P, W, w_bf16, d_out, d, groups, w, st);
+template <int M>
+static hipError_t launch_delta(const unsigned long long* mode, const float* F, int64_t d,
+                               int64_t d_out, int groups, const uint8_t* P, const float* C,
+                               const LnqWs& w, hipStream_t st) {
+    const int nsl = (int)((d + DL_SL - 1) / DL_SL);
+    hipLaunchKernelGGL(k_order_rows, dim3(1), dim3(1024), 0, st, mode, w.ccount, d_out, w.order);
+    GQ_LAUNCH_CHECK();
+    hipLaunchKernelGGL((k_delta<M>), dim3((unsigned)(d_out * nsl)), dim3(256), 0, st, mode, F,
+                       w.dF, d, d_out / groups, w.pprev, P, C, w.R, w.clist, w.ccount, w.order,
+                       nsl, w.dA);
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
+}
+
+static hipError_t delta_m(int m, const unsigned long long* mode, const float* F, int64_t d,
+                          int64_t d_out, int groups, const uint8_t* P, const float* C,
+                          const LnqWs& w, hipStream_t st) {
+    switch (m) {
+        case 2: return launch_delta<2>(mode, F, d, d_out, groups, P, C, w, st);
+        case 4: return launch_delta<4>(mode, F, d, d_out, groups, P, C, w, st);
+        case 8: return launch_delta<8>(mode, F, d, d_out, groups, P, C, w, st);
+        case 16: return launch_delta<16>(mode, F, d, d_out, groups, P, C, w, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t lnq_codebook_step(const float* F, const void* W, bool w_bf16, int64_t d_out, int64_t d,
+                             int groups, int m, const uint8_t* P, float* C, const LnqWs& w,
+                             double* obj_before, unsigned long long* n_not_pd,
+                             const unsigned long long* mode, hipStream_t st) {
+    // from scratch (skipped on the device when *mode != 0)
+    hipError_t e = lnq_residual_from(C, m, P, W, w_bf16, d_out, d, groups, w, mode, st);
     if (e != hipSuccess) return e;
-    if ((e = lnq_gram(P, m, d_out, d, groups, w.fhi, w.flo, w.part, st)) != hipSuccess) return e;
+    if ((e = lnq_gram(P, m, d_out, d, groups, w.fhi, w.flo, w.part, mode, st)) != hipSuccess)
+        return e;
+    if (mode) {
+        // from the changed coordinates (nothing when *mode == 0)
+        StageTimer tm(ST_LNQ_DELTA, st);
+        if ((e = delta_m(m, mode, F, d, d_out, groups, P, C, w, st)) != hipSuccess) return e;
+    }
     const int nta = (int)((d + 255) / 256);
     StageTimer tm(ST_LNQ_SOLVE, st);
-    return w_bf16 ? solve_m<true, true>(m, w.part, nta, w.R, P, W, C, d, d_out, obj_before, n_not_pd, st)
-                  : solve_m<false, true>(m, w.part, nta, w.R, P, W, C, d, d_out, obj_before, n_not_pd, st);
+    return w_bf16 ? solve_m<true, true>(m, w.part, nta, w.R, P, W, C, d, d_out, obj_before, n_not_pd, mode, &w, st)
+                  : solve_m<false, true>(m, w.part, nta, w.R, P, W, C, d, d_out, obj_before, n_not_pd, mode, &w, st);
 }
 
 hipError_t lnq_objective_rows(const void* W, bool w_bf16, int64_t d_out, int64_t d, int groups,
                               int m, const uint8_t* P, const float* C, const LnqWs& w,
                               double* obj, hipStream_t st) {
-    hipError_t e = lnq_residual_from(C, m, P, W, w_bf16, d_out, d, groups, w, st);
+    hipError_t e = lnq_residual_from(C, m, P, W, w_bf16, d_out, d, groups, w, nullptr, st);
     if (e != hipSuccess) return e;
     StageTimer tm(ST_LNQ_SOLVE, st);
-    return w_bf16 ? solve_m<true, false>(m, nullptr, 0, w.R, P, W, (float*)C, d, d_out, obj, nullptr, st)
-                  : solve_m<false, false>(m, nullptr, 0, w.R, P, W, (float*)C, d, d_out, obj, nullptr, st);
+    return w_bf16 ? solve_m<true, false>(m, nullptr, 0, w.R, P, W, (float*)C, d, d_out, obj, nullptr, nullptr, nullptr, st)
+                  : solve_m<false, false>(m, nullptr, 0, w.R, P, W, (float*)C, d, d_out, obj, nullptr, nullptr, nullptr, st);
 }
 
 template <bool WB>
 static hipError_t launch_sweep(const float* F, const void* W, int64_t d_out, int64_t d,
                                int groups, const float* C, int m, uint8_t* P, const LnqWs& w,
                                double* obj_start, double* obj_end, unsigned long long* counter,
-                               hipStream_t st) {
+                               bool record, hipStream_t st) {
     const int64_t rpg = d_out / groups;
     const int wgs = (int)((rpg + SW_ROWS - 1) / SW_ROWS);
     const int total = wgs * groups;
@@ -841,7 +1197,8 @@ static hipError_t launch_sweep(const float* F, const void* W, int64_t d_out, int
     auto kern = (m == 2) ? k_sweep<WB, 2> : (m == 4) ? k_sweep<WB, 4> : (m == 8) ? k_sweep<WB, 8>
                                                                          : k_sweep<WB, 16>;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(1024), 0, st, F, w.dF, w.fhi,
-                       w.flo, d, rpg, wgs, total, C, m, P, W, w.R, obj_start, obj_end, counter);
+                       w.flo, d, rpg, wgs, total, C, m, P, W, w.R, obj_start, obj_end, counter,
+                       record ? w.clist : nullptr, record ? w.ccount : nullptr);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }
@@ -849,13 +1206,13 @@ static hipError_t launch_sweep(const float* F, const void* W, int64_t d_out, int
 hipError_t lnq_sweep_step(int block, const float* F, const void* W, bool w_bf16, int64_t d_out,
                           int64_t d, int groups, const float* C, int m, uint8_t* P,
                           const LnqWs& w, double* obj_start, double* obj_end,
-                          unsigned long long* counter, hipStream_t st) {
-    hipError_t e = lnq_residual_from(C, m, P, W, w_bf16, d_out, d, groups, w, st);
+                          unsigned long long* counter, bool record, hipStream_t st) {
+    hipError_t e = lnq_residual_from(C, m, P, W, w_bf16, d_out, d, groups, w, nullptr, st);
     if (e != hipSuccess) return e;
     if (block != SW_SUB) return hipErrorInvalidValue;
     StageTimer tm(ST_LNQ_SWEEP, st);
-    return w_bf16 ? launch_sweep<true>(F, W, d_out, d, groups, C, m, P, w, obj_start, obj_end, counter, st)
-                  : launch_sweep<false>(F, W, d_out, d, groups, C, m, P, w, obj_start, obj_end, counter, st);
+    return w_bf16 ? launch_sweep<true>(F, W, d_out, d, groups, C, m, P, w, obj_start, obj_end, counter, record, st)
+                  : launch_sweep<false>(F, W, d_out, d, groups, C, m, P, w, obj_start, obj_end, counter, record, st);
 }
 
 hipError_t lnq_reduce(const double* rows, int64_t n, double* out, hipStream_t st) {
@@ -866,17 +1223,18 @@ hipError_t lnq_reduce(const double* rows, int64_t n, double* out, hipStream_t st
 }
 
 hipError_t lnq_iter_tail(const double* objA, const double* objB, int64_t n, double* trace,
-                         unsigned long long* cnt, int64_t* n_changed, hipStream_t st) {
+                         unsigned long long* cnt, int64_t* n_changed, int64_t incr_max,
+                         hipStream_t st) {
     StageTimer tm(ST_LNQ_SMALL, st);
     hipLaunchKernelGGL(k_iter_tail, dim3(3), dim3(256), 0, st, objA, objB, n, trace, cnt,
-                       n_changed);
+                       n_changed, incr_max);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }
 
-hipError_t lnq_zero_counter(unsigned long long* c, hipStream_t st) {
+hipError_t lnq_zero_counter(unsigned long long* c, int n, hipStream_t st) {
     StageTimer tm(ST_LNQ_SMALL, st);
-    hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, st, c, 1);
+    hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, st, c, n);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }

@@ -81,8 +81,10 @@ __device__ __forceinline__ int frag_slot(int row, int lane) {
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_resid(
     const uint16_t* __restrict__ Ehi, const uint16_t* __restrict__ Elo, int64_t erows,
     int64_t rpg_pad, const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo,
-    int64_t a_pad, int64_t d, int64_t rpg, int ntn, int nta, int total, float* __restrict__ R) {
+    int64_t a_pad, int64_t d, int64_t rpg, int ntn, int nta, int total, float* __restrict__ R,
+    const unsigned long long* __restrict__ skip) {
     extern __shared__ u32x4 mm_lds[];
+    if (skip && *skip != 0ull) return;
     const int lin = mm_remap(blockIdx.x);
     if (lin >= total) return;
     const int ta = lin % nta;
@@ -204,8 +206,10 @@ template <int M>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gram(
     const uint8_t* __restrict__ P, int64_t rpg, int64_t d_out, int groups,
     const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo, int64_t a_pad,
-    int64_t d, int ntn, int nta, int total, float* __restrict__ out) {
+    int64_t d, int ntn, int nta, int total, float* __restrict__ out,
+    const unsigned long long* __restrict__ skip) {
     extern __shared__ u32x4 mm_lds[];
+    if (skip && *skip != 0ull) return;
     // LDS: ring of GRING stages of four bands (Fhi and Flo of two k-blocks); two
     // one-hot stages of two k-blocks (512 slots each); ring of GRING code stages
     // (slot 64 w + 32 h + c for column 32 w + c, codes 16 h .. 16 h + 15)
@@ -412,7 +416,7 @@ size_t lnq_gram_partial_floats(int64_t d_out, int64_t d, int m) {
 
 hipError_t lnq_residual(const uint16_t* Ehi, const uint16_t* Elo, int64_t d_out, int64_t d,
                         int groups, const uint16_t* Fhi, const uint16_t* Flo, float* R,
-                        hipStream_t st) {
+                        const unsigned long long* skip, hipStream_t st) {
     const int64_t rpg = d_out / groups;
     const int64_t rpg_pad = lnq_pad256(rpg), a_pad = lnq_pad256(d);
     const int ntn = (int)(rpg_pad / MT);
@@ -430,7 +434,7 @@ hipError_t lnq_residual(const uint16_t* Ehi, const uint16_t* Elo, int64_t d_out,
     StageTimer tm(ST_LNQ_RESID, st);
     hipLaunchKernelGGL(k_resid, dim3((unsigned)grid), dim3(512), RESID_LDS, st, Ehi, Elo,
                        (int64_t)groups * rpg_pad, rpg_pad, Fhi, Flo, a_pad, d, rpg, ntn, nta,
-                       total, R);
+                       total, R, skip);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }
@@ -438,7 +442,7 @@ hipError_t lnq_residual(const uint16_t* Ehi, const uint16_t* Elo, int64_t d_out,
 template <int M>
 static hipError_t launch_gram(const uint8_t* P, int64_t d_out, int64_t d, int groups,
                               const uint16_t* Fhi, const uint16_t* Flo, float* part,
-                              hipStream_t st) {
+                              const unsigned long long* skip, hipStream_t st) {
     const int64_t rpg = d_out / groups;
     const int ntn = (int)((rpg * M + MT - 1) / MT);
     const int nta = (int)((d + MT - 1) / MT);
@@ -454,18 +458,19 @@ static hipError_t launch_gram(const uint8_t* P, int64_t d_out, int64_t d, int gr
     }
     StageTimer tm(ST_LNQ_GRAM, st);
     hipLaunchKernelGGL((k_gram<M>), dim3((unsigned)grid), dim3(512), GRAM_LDS, st, P, rpg, d_out,
-                       groups, Fhi, Flo, lnq_pad256(d), d, ntn, nta, total, part);
+                       groups, Fhi, Flo, lnq_pad256(d), d, ntn, nta, total, part, skip);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }
 
 hipError_t lnq_gram(const uint8_t* P, int m, int64_t d_out, int64_t d, int groups,
-                    const uint16_t* Fhi, const uint16_t* Flo, float* part, hipStream_t st) {
+                    const uint16_t* Fhi, const uint16_t* Flo, float* part,
+                    const unsigned long long* skip, hipStream_t st) {
     switch (m) {
-        case 2: return launch_gram<2>(P, d_out, d, groups, Fhi, Flo, part, st);
-        case 4: return launch_gram<4>(P, d_out, d, groups, Fhi, Flo, part, st);
-        case 8: return launch_gram<8>(P, d_out, d, groups, Fhi, Flo, part, st);
-        case 16: return launch_gram<16>(P, d_out, d, groups, Fhi, Flo, part, st);
+        case 2: return launch_gram<2>(P, d_out, d, groups, Fhi, Flo, part, skip, st);
+        case 4: return launch_gram<4>(P, d_out, d, groups, Fhi, Flo, part, skip, st);
+        case 8: return launch_gram<8>(P, d_out, d, groups, Fhi, Flo, part, skip, st);
+        case 16: return launch_gram<16>(P, d_out, d, groups, Fhi, Flo, part, skip, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -30,14 +30,14 @@ def test_exports_every_declared_symbol():
     assert declared == set(B.EXPORTS), declared ^ set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert gq.abi_version() == 1
+    assert gq.abi_version() == 2
 
 
 def test_options_default():
     o = gq.options()
     d = B.lnq_options()
     gq.library().gq_lnq_options_default(ctypes.byref(d))
-    assert (d.block, d.init, d.reserved) == (64, 0, 0)
+    assert (d.block, d.init, d.gram_update) == (64, 0, 0)
     assert d.ridge_rel == pytest.approx(1e-6)
     assert o.block == 64
 
@@ -93,6 +93,9 @@ def test_lnq_argument_errors():
     o.init, o.ridge_rel = 0, -1.0
     assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "ridge" in _err(lib)
     o.ridge_rel = 1e-6
+    o.gram_update = 7
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "gram_update" in _err(lib)
+    o.gram_update = B.GQ_GRAM_DENSE
     assert q(opt=ctypes.byref(o), wsb=100) == B.GQ_EINVAL and "workspace" in _err(lib)
     # the per-stage entry points share the checks
     assert lib.lnq_assign_sweep(FAKE, 2, 256, FAKE, 1, 64, FAKE, 3, FAKE, 1e-6, 48, None, FAKE,
@@ -117,5 +120,5 @@ def test_timing_read_empty():
     t = gq.gq_timing_read()
     assert set(t) == {"group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain",
                       "lnq_prepare", "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep",
-                      "lnq_small", "fisher_pack"}
+                      "lnq_small", "fisher_pack", "lnq_delta"}
     assert all(v == (0.0, 0) for v in t.values())

@@ -286,3 +286,64 @@ def test_lnq_tiny_workload_from_activations(device):
         gpu += O.objective(Fref, w[j], C[j], P[j])
     print(f"tiny: gpu {gpu:.6e} oracle {ref:.6e}")
     assert abs(gpu - ref) / ref <= 1e-3
+
+
+def _incr_max(d_out, d_in, m):
+    # the library's switch: a codebook step updates A and the residual from the changed
+    # coordinates when the preceding pass changed at most this many codes
+    return d_out * d_in * (m + 3) * 3 // 1000
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_incremental_codebook_step(device, mid, bits):
+    """The codebook step that follows a pass with few changes takes A = P^T F' P and
+    the residual from the changed coordinates.  From the state the dense run reaches
+    just before the first such step: the codebook it produces matches the oracle's
+    closed form (1e-4 relative per row) and the dense path's (1e-5); the objective
+    before it, from the updated residual, matches the oracle's (1e-4)."""
+    m = 1 << bits
+    T = 16
+    Cd, Pd, trd, nchd = gq.lnq_quantize(mid.W, mid.F, bits, T, gram_update=gq.GQ_GRAM_DENSE)
+    torch.cuda.synchronize()
+    nch = nchd.cpu().numpy()
+    lim = _incr_max(MID.d_out, MID.d_in, m)
+    ts = [t for t in range(2, T + 1) if nch[t - 2] <= lim]
+    assert ts, (nch, lim)
+    t = ts[0]                       # first iteration whose codebook step is incremental
+    Cp, Pp, trp, _ = gq.lnq_quantize(mid.W, mid.F, bits, t - 1, gram_update=gq.GQ_GRAM_DENSE)
+    Ca, Pa, tra, ncha = gq.lnq_quantize(mid.W, mid.F, bits, t)
+    Cb, Pb, trb, _ = gq.lnq_quantize(mid.W, mid.F, bits, t, gram_update=gq.GQ_GRAM_DENSE)
+    torch.cuda.synchronize()
+    # identical up to the switch
+    assert torch.equal(ncha[:t - 1].cpu(), nchd[:t - 1].cpu())
+    Cp, Pp = f64(Cp), Pp.cpu().numpy()
+    Ca, Cb = f64(Ca), f64(Cb)
+    worst_ref = worst_dense = 0.0
+    obj_ref = 0.0
+    for j in range(MID.d_out):
+        Fp = mid.Fp_row(j)
+        ref = O.codebook_update(Fp, mid.w[j], Pp[j], Cp[j])
+        obj_ref += O.objective(Fp, mid.w[j], Cp[j], Pp[j])
+        worst_ref = max(worst_ref, np.linalg.norm(Ca[j] - ref) / np.linalg.norm(ref))
+        worst_dense = max(worst_dense, np.linalg.norm(Ca[j] - Cb[j]) / np.linalg.norm(Cb[j]))
+    before = tra.cpu().numpy()[2 * t - 2]
+    print(f"bits={bits}: incremental step at iteration {t} (changes {nch[t - 2]} <= {lim}); "
+          f"codebook vs oracle {worst_ref:.2e}, vs dense {worst_dense:.2e}; objective before "
+          f"{before:.9e} oracle {obj_ref:.9e}")
+    assert worst_ref <= 1e-4
+    assert worst_dense <= 1e-5
+    assert abs(before - obj_ref) <= 1e-4 * obj_ref
+
+
+def test_incremental_and_dense_runs_agree(device, mid):
+    """Whole runs with and without the incremental steps (at least three of them):
+    monotone, and final objectives within 1e-4 of each other."""
+    T = 16
+    C1, P1, tr1, n1 = gq.lnq_quantize(mid.W, mid.F, 3, T)
+    C2, P2, tr2, _ = gq.lnq_quantize(mid.W, mid.F, 3, T, gram_update=gq.GQ_GRAM_DENSE)
+    torch.cuda.synchronize()
+    assert (n1.cpu().numpy()[:-1] <= _incr_max(MID.d_out, MID.d_in, 8)).sum() >= 3
+    a, b = tr1.cpu().numpy(), tr2.cpu().numpy()
+    assert np.all(a[1:] <= a[:-1] * (1 + 1e-6)), a
+    print(f"final objective auto {a[-1]:.9e} dense {b[-1]:.9e}")
+    assert abs(a[-1] - b[-1]) <= 1e-4 * b[-1]

@@ -25,9 +25,22 @@ independent given their group's F', so a sampled row is compared exactly.
     but the 99.9 % bar is counted per decision.
   * codebook, from the same random state: step-relative error <= 1e-4 and the
     objective within 1e-7 of the oracle's minimum on the sampled rows.
-  * end to end (quantile init + the layer's iterations): the GPU trace is
-    monotone, and on the sampled rows the final objective (evaluated by the
-    oracle) is within 1e-3 of the oracle's own run.
+  * end to end, teacher-forced: the GPU trajectory from the quantile init is
+    taken one iteration at a time (each call starts from the previous call's
+    C and P; the chain reproduces a single call bit for bit).  On the sampled
+    rows the initial codebook and codes are identical to the oracle's, every
+    codebook step is within 1e-4 of the oracle's closed form from the GPU's
+    own state before it, and every pass is replayed decision by decision as
+    above (every decision valid, >= 99.9 % identical).  A free-running
+    comparison of a few rows is not a sound end-to-end bar at these lengths:
+    after one valid near-tie decision a row follows another valid trajectory,
+    and a few-ulp perturbation of the GPU's own run moves the mean objective of
+    a 4-row sample of the 28672 -> 8192 layer by 1.8e-3 at the 95th percentile
+    (single rows by up to 6 %), while layer totals move by under 1e-4.
+  * the layer-wide final objective of the default run (codebook steps after
+    passes with few changes updated from the changed coordinates) is within
+    1e-3 of the run that recomputes every step; the default run's trace is
+    monotone.
 """
 import sys
 import time
@@ -149,18 +162,36 @@ def test_lnq_full_size_sampled_rows(device, layer):
     npd = torch.zeros(1, dtype=torch.int64, device=device)
     gq.lnq_codebook_update(F, W, to_dev(P0, device), Cd, wl.bits, RHO, n_not_pd=npd)
     C, P, tr, _ = gq.lnq_quantize(W, F, wl.bits, wl.iters, block=64, ridge_rel=RHO)
+    Cx, Px, trx, _ = gq.lnq_quantize(W, F, wl.bits, wl.iters, block=64, ridge_rel=RHO,
+                                     gram_update=gq.GQ_GRAM_DENSE)
     torch.cuda.synchronize()
     assert npd.item() == 0
-    tr = tr.cpu().numpy()
+    tr, trx = tr.cpu().numpy(), trx.cpu().numpy()
     assert np.all(tr[1:] <= tr[:-1] * (1 + 1e-6)), tr
     _progress(f"{wl.name}: GPU sweep, codebook and {wl.iters}-iteration LNQ done; "
-              f"objective {tr[0]:.4e} -> {tr[-1]:.4e}")
+              f"objective {tr[0]:.4e} -> {tr[-1]:.4e} (recomputing every step: {trx[-1]:.4e})")
+    assert abs(tr[-1] - trx[-1]) <= 1e-3 * trx[-1]
 
     per_sweep, per_e2e = ROWS[wl.name]
     sweep_rows = _sample_rows(wl, per_sweep, 5)
+    # the GPU trajectory one iteration at a time; sampled rows of every state kept
+    e2e_rows = sorted(j for g in range(wl.groups) for j in sweep_rows[g][:per_e2e])
+    idx = torch.tensor(e2e_rows, device=device)
+    Ct, Pt, _, _ = gq.lnq_quantize(W, F, wl.bits, 0)
+    states = [(Ct.index_select(0, idx).cpu().double().numpy(), Pt.index_select(0, idx).cpu().numpy())]
+    for t in range(wl.iters):
+        Ct, Pt, _, _ = gq.lnq_quantize(W, F, wl.bits, 1, C=Ct.clone(), P=Pt.clone(), ridge_rel=RHO,
+                                       gram_update=gq.GQ_GRAM_DENSE)
+        states.append((Ct.index_select(0, idx).cpu().double().numpy(),
+                       Pt.index_select(0, idx).cpu().numpy()))
+    torch.cuda.synchronize()
+    assert torch.equal(Ct, Cx) and torch.equal(Pt, Px)
+    del Ct, Pt, Cx, Px
+    _progress(f"{wl.name}: GPU trajectory taken one iteration at a time")
     agree = n_codes = n_differ = 0
     worst_replay = worst_step = worst_obj = -np.inf
-    gpu_obj = ref_obj = 0.0
+    tf_step = tf_obj = tf_replay = -np.inf
+    tf_dec = tf_differ = 0
     for g in range(wl.groups):
         Fp = O.damped(F[g].cpu().double().numpy(), RHO)
         for k, j in enumerate(sweep_rows[g]):
@@ -188,22 +219,40 @@ def test_lnq_full_size_sampled_rows(device, layer):
             worst_step = max(worst_step, np.linalg.norm(got - ref) / scale)
             o_ref = O.objective(Fp, w, ref, P0[j])
             worst_obj = max(worst_obj, (O.objective(Fp, w, got, P0[j]) - o_ref) / o_ref)
-            # end to end
+            # end to end, teacher-forced along the GPU trajectory
             if k < per_e2e:
-                _, _, t_ref = O.lnq_row(Fp, w, m, wl.iters)
-                ref_obj += t_ref[-1]
-                gpu_obj += O.objective(Fp, w, C[j].cpu().double().numpy(), P[j].cpu().numpy())
+                r = e2e_rows.index(j)
+                c_init, p_init = O.init_quantile(w, m)
+                np.testing.assert_array_equal(states[0][0][r], c_init)
+                np.testing.assert_array_equal(states[0][1][r], p_init)
+                for t in range(1, wl.iters + 1):
+                    c_prev, p_prev = states[t - 1][0][r], states[t - 1][1][r]
+                    c_t, p_t = states[t][0][r], states[t][1][r]
+                    ref = O.codebook_update(Fp, w, p_prev, c_prev)
+                    tf_step = max(tf_step, np.linalg.norm(c_t - ref) / np.linalg.norm(ref))
+                    o_ref = O.objective(Fp, w, ref, p_prev)
+                    tf_obj = max(tf_obj, (O.objective(Fp, w, c_t, p_prev) - o_ref) / o_ref)
+                    ex, differ = O.replay_sweep(Fp, w, c_t, p_prev, p_t, 1e-5)
+                    tf_replay = max(tf_replay, ex)
+                    tf_differ += differ
+                    tf_dec += wl.d_in
+                _progress(f"{wl.name}: row {j}: {wl.iters} GPU iterations checked step by step")
         del Fp
         _progress(f"{wl.name}: group {g} rows checked")
     frac = agree / n_codes
     frac_dec = 1.0 - n_differ / n_codes
-    rel = abs(gpu_obj - ref_obj) / ref_obj
+    tf_frac = 1.0 - tf_differ / tf_dec
     _progress(f"{wl.name}: sweep decisions identical {frac_dec:.6f}, final codes identical "
               f"{frac:.6f}, worst replay excess {worst_replay:.2e}; "
               f"codebook step-relative {worst_step:.2e}, objective excess {worst_obj:.2e}; "
-              f"end to end gpu {gpu_obj:.6e} oracle {ref_obj:.6e} rel {rel:.2e}")
+              f"end to end (teacher-forced, {wl.iters} iterations): codebook {tf_step:.2e}, "
+              f"objective excess {tf_obj:.2e}, decisions identical {tf_frac:.6f}, worst replay "
+              f"excess {tf_replay:.2e}")
     assert worst_replay <= 0.0
     assert frac_dec >= 0.999
     assert worst_step <= 1e-4
     assert worst_obj <= 1e-7
-    assert rel <= 1e-3
+    assert tf_step <= 1e-4
+    assert tf_obj <= 1e-7
+    assert tf_replay <= 0.0
+    assert tf_frac >= 0.999
