@@ -85,9 +85,9 @@ def _traffic(stage, wl):
 
 def _incremental_iters(wl, nchg):
     """Iterations whose codebook step updates A and the residual from the previous
-    pass's changed coordinates (the library's switch: at most d_out d_in (m + 3) 3 / 1000
+    pass's changed coordinates (the library's switch: at most d_out d_in (m + 3) 17 / 10000
     changes), given the per-pass change counts."""
-    lim = wl.d_out * wl.d_in * (wl.m + 3) * 3 // 1000
+    lim = wl.d_out * wl.d_in * (wl.m + 3) * 17 // 10000
     return [t for t in range(2, wl.iters + 1) if nchg[t - 2] <= lim]
 
 

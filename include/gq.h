@@ -188,7 +188,7 @@ gq_status lnq_objective(const float* F, int32_t groups, int64_t d_in,
  * sum_j e_j^T F' e_j at the start and after every half-step, from the residual
  * F'(C[P] - W) each step uses: recomputed from (C, P), except that under
  * GQ_GRAM_AUTO the entry before a codebook step that follows a pass with at most
- * d_out * d_in * (2^bits + 3) * 3 / 1000 changes comes from the residual updated
+ * d_out * d_in * (2^bits + 3) * 17 / 10000 changes comes from the residual updated
  * by the changed coordinates (equal up to float rounding).  The last entry is
  * always recomputed.  n_changed (device int64 [iters], may be NULL): coordinates
  * changed by each assignment pass (overwritten).

@@ -332,10 +332,12 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
     if (iters > 0 && (e = gq::lnq_zero_counter(w.cnt, 3, st)) != hipSuccess)
         return hip_fail(e, "counter");
     // A codebook step after a pass that changed at most incr_max codes updates A and the
-    // residual from the changed coordinates (about 4 d bytes of F read per change)
-    // instead of recomputing them (2 d^2 d_out (m + 3) matrix-core flops).
+    // residual from the changed coordinates (4 d bytes of F read per change, about
+    // 3.5 ns per change at d = 4096) instead of recomputing them (2 d^2 d_out (m + 3)
+    // matrix-core flops, about 1.7e-15 s per unit); the two costs meet near
+    // 0.0017 d d_out (m + 3) changes.
     const bool incremental = o.gram_update == GQ_GRAM_AUTO;
-    const int64_t incr_max = incremental ? d_out * d_in * (m + 3) * 3 / 1000 : -1;
+    const int64_t incr_max = incremental ? d_out * d_in * (m + 3) * 17 / 10000 : -1;
     for (int t = 1; t <= iters; ++t) {
         // codebook step; objA = objective before it (trace entry 2t-2)
         if ((e = gq::lnq_codebook_step(F, W, wb, d_out, d_in, groups, m, P, C, w, w.objA,
