@@ -58,12 +58,14 @@ def _parse():
 # figure no longer describes the kernel and is reported as null.
 _CSRC = os.path.join(ROOT, "post_weight_quantization_gq_amd", "csrc")
 _TRAFFIC = {
-    # stage: (workload, source file, digest, bytes read, bytes written) of its main kernel
-    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "27613b3830b49cb1", 269647000, 16777216),
-    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "9fa836b8c1b617ea", 16732700000,
+    # stage: (workload, source file, digest, bytes read, bytes written) of its main kernel,
+    # averaged over the launches that do the work
+    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "3a1b27a0fe44d80f", 269413545, 16777216),
+    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "556cea64837144d7", 16896399901,
                     1140850688),
-    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "19ba356279e40eef", 748165000, 251854656),
-    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "27613b3830b49cb1", 604172000, 67108864),
+    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "ed4bcafe3d6f08a0", 762629622, 254978077),
+    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "3a1b27a0fe44d80f", 604188222, 67108864),
+    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "ed4bcafe3d6f08a0", 1602985311, 85659200),
 }
 
 
