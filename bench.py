@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 PEAK_BF16_MFMA = 2500e12      # dense bf16 matrix-core FLOP/s
 PEAK_FP32_VALU = 157.3e12     # fp32 vector FLOP/s (FMA = 2 flops, packed)
 PEAK_HBM = 8e12               # bytes/s
+PEAK_FP32_ADD = 78.6e12       # fp32 vector adds/s (one add per lane per cycle)
 
 
 def _parse():
@@ -91,6 +92,26 @@ def _incremental_iters(wl, nchg):
     changes), given the per-pass change counts."""
     lim = wl.d_out * wl.d_in * (wl.m + 3) * 17 // 10000
     return [t for t in range(2, wl.iters + 1) if nchg[t - 2] <= lim]
+
+
+def _layer_roofline(wl, nchg, ms_step):
+    """Composite lower bound on the time of one layer (Fisher + LNQ), term by term:
+      group scale        bytes 2 n d_out + 4 G n at the HBM peak;
+      Fisher             n d_in (d_in + 1) G flops (unique entries) at the bf16 MFMA peak;
+      per iteration      max(d_out d_in^2 adds at the fp32 add peak (the gather-reduce of
+                         P^T F' P), 4 G d_in^2 + d_out d_in bytes at the HBM peak)
+                         + (2 d_in m per row for the residual refresh + 2 d_in per changed
+                         coordinate) fp32 flops at the fp32 vector peak.
+    frac = t_roof / t_measured."""
+    n, d, d_out, G, m, it = wl.n, wl.d_in, wl.d_out, wl.groups, wl.m, wl.iters
+    t_scale = (2 * n * d_out + 4 * G * n) / PEAK_HBM
+    t_fisher = n * d * (d + 1) * G / PEAK_BF16_MFMA
+    t_gram = it * max(d_out * d * d / PEAK_FP32_ADD, (4 * G * d * d + d_out * d) / PEAK_HBM)
+    t_upd = (it * d_out * 2 * d * m + 2 * d * float(np.sum(nchg))) / PEAK_FP32_VALU
+    t_roof = t_scale + t_fisher + t_gram + t_upd
+    return {"t_roof_ms": t_roof * 1e3, "t_measured_ms": ms_step, "frac": t_roof * 1e3 / ms_step,
+            "terms_ms": {"group_scale": t_scale * 1e3, "fisher": t_fisher * 1e3,
+                         "codebook_systems": t_gram * 1e3, "residual_and_moves": t_upd * 1e3}}
 
 
 def _stage_units(stage, wl, nchg):
@@ -277,6 +298,7 @@ def main():
         "codebook_steps_from_changes": _incremental_iters(wl, nchg),
         "objective_trace": [float(x) for x in trace],
         "monotone": bool(np.all(trace[1:] <= trace[:-1] * (1 + 1e-6))),
+        "layer_roofline": _layer_roofline(wl, nchg, ms_step),
         "roofline": roof,
     }
 
