@@ -223,6 +223,21 @@ __global__ __launch_bounds__(256) void k_err_split(const float* __restrict__ C, 
     *(u32x4*)(Elo + off + 8) = l[1];
 }
 
+// s + x(0) + x(1) + ... + x(n-1), added in that order, the loads issued 8 at a time
+template <typename Get>
+__device__ __forceinline__ double ordered_sum(int n, Get x, double s) {
+    int t = 0;
+    for (; t + 8 <= n; t += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = x(t + u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += (double)v[u];
+    }
+    for (; t < n; ++t) s += (double)x(t);
+    return s;
+}
+
 // ---------------------------------------------------------------------------
 // k_solve: one wave per row (4 rows per block).
 //   Always: obj[j] = sum_a e_a r_a (float64), e = C[j][P[j][a]] - W[j][a].
@@ -269,7 +284,7 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
         // 4 consecutive coordinates per lane and step (d % 32 == 0: aligned vectors)
         const uint8_t* Pj = P + j * d;
         const float* Rj = R + j * d;
-#pragma unroll 2
+#pragma unroll 4
         for (int64_t a0 = 4 * lane; a0 < d; a0 += 256) {
             const uint32_t c4 = *(const uint32_t*)(Pj + a0);
             const float4 r4 = *(const float4*)(Rj + a0);
@@ -328,12 +343,12 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
             if (incr) {
                 s = Aj[e];
                 if (moved)
-                    for (int sl = 0; sl < nslices; ++sl)
-                        s += (double)dA[((size_t)j * nslices + sl) * M * M + e];
+                    s = ordered_sum(nslices, [&](int sl) {
+                        return dA[((size_t)j * nslices + sl) * M * M + e]; }, s);
                 s *= 0.5;
             } else {
-                for (int ta = 0; ta < ntile_a; ++ta)
-                    s += (double)part[((size_t)ta * d_out * M + (size_t)(j * M + q)) * M + qp];
+                s = ordered_sum(ntile_a, [&](int ta) {
+                    return part[((size_t)ta * d_out * M + (size_t)(j * M + q)) * M + qp]; }, s);
             }
             sB[wave][q][qp] = s;
         }
