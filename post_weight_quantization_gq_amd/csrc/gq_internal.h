@@ -44,6 +44,7 @@ __host__ __device__ inline int64_t lnq_pad256(int64_t x) { return (x + 255) / 25
 struct LnqSizes {
     size_t o_fhi, o_flo, o_dF, o_lam, o_R, o_ehi, o_elo, o_part;
     size_t o_objA, o_objB, o_objC, o_cnt, o_pprev, o_afull, o_clist, o_ccount, o_order, o_dA;
+    size_t o_items, o_nitems;
     size_t total;
 };
 struct LnqWs {
@@ -63,6 +64,8 @@ struct LnqWs {
                                   // coordinate | old code << 16 | new code << 24
     int* ccount;                  // number of moves per row [d_out]
     int* order;                   // rows, most moves first [d_out]
+    unsigned long long* items;    // work items of the update, longest first
+    int* nitems;                  // their number
     float* dA;                    // per (row, coordinate slice): share of A_new - A_old
 };
 

@@ -682,9 +682,10 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
 //   Residual: the pass has already added each move's effect on the coordinates of
 //   later super-blocks; the rest, r[k] += delta_i F'[i][k] for k before the end of
 //   i's super-block, is summed in float32 from the same rows.
-//   Work item = (row, slice of DL_SL coordinates); one block (4 waves) each, rows
-//   taken heaviest first.  The pass lists each row's moves (coordinate, old code,
-//   new code) in ascending order; an item takes them DL_G at a time (tiles of 16,
+//   Work item = (row, range of DL_SL-coordinate slices, wider for rows with fewer
+//   moves); one block (4 waves) each, longest items first.  The pass lists each row's
+//   moves (coordinate, old code, new code) in ascending order; an item takes them DL_G
+//   at a time (tiles of 16,
 //   one MFMA row block each), its waves interleaving the slice's 32-coordinate
 //   chunks.  An item updates the residual of its own coordinates and leaves its
 //   share of A_new - A_old (summed per entry in float64 over the changes, in order)
@@ -839,17 +840,25 @@ __device__ __forceinline__ void delta_pass(int n, const int* s_i, const float* s
             for (int e = 0; e < 4; ++e) hw[16 * t + 4 * (lane >> 4) + e][16 * nb + mr] = acc[t][nb][e];
 }
 
-// Rows in decreasing order of their change counts (buckets of 16 changes, heaviest
-// first), so that the longest work items start first.  One block of 1024 threads.
+// Work items, longest first.  Rows are ordered by decreasing move count (buckets of
+// 16 moves; the order within a bucket is arbitrary and affects scheduling only).  A
+// row with K moves is split into min(slices, ceil(K / 16)) items over contiguous
+// ranges of DL_SL-coordinate slices, so that items carry similar work and none is long.
+// Item: row | first slice << 32 | end slice << 48.  One block of 1024 threads.
 __global__ __launch_bounds__(1024) void k_order_rows(const unsigned long long* __restrict__ mode,
                                                     const int* __restrict__ ccount, int64_t n,
-                                                    int* __restrict__ order) {
+                                                    int nslices, int* __restrict__ order,
+                                                    unsigned long long* __restrict__ items,
+                                                    int* __restrict__ nitems) {
     constexpr int NBK = 64;
     __shared__ int hist[NBK];
     __shared__ int base[NBK];
+    __shared__ int wsum[16];
+    __shared__ int run;
     if (*mode == 0ull) return;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid < NBK) hist[tid] = 0;
+    if (tid == 0) run = 0;
     __syncthreads();
     auto bucket = [](int c) {
         int b = (c + 15) >> 4;
@@ -864,6 +873,40 @@ __global__ __launch_bounds__(1024) void k_order_rows(const unsigned long long* _
     }
     __syncthreads();
     for (int64_t j = tid; j < n; j += 1024) order[atomicAdd(&base[bucket(ccount[j])], 1)] = (int)j;
+    __syncthreads();
+    // items in that order: an exclusive scan of the item counts, 1024 rows at a time
+    for (int64_t c0 = 0; c0 < n; c0 += 1024) {
+        const int64_t p = c0 + tid;
+        int row = 0, k = 0, cnt = 0;
+        if (p < n) {
+            row = order[p];
+            k = ccount[row];
+            cnt = k <= 0 ? 0 : ((k + 15) / 16 < nslices ? (k + 15) / 16 : nslices);
+        }
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int ex = run + incl - cnt;
+        for (int w = 0; w < wave; ++w) ex += wsum[w];
+        for (int i = 0; i < cnt; ++i) {
+            const unsigned long long lo = (unsigned long long)(i * nslices / cnt);
+            const unsigned long long hi = (unsigned long long)((i + 1) * nslices / cnt);
+            items[ex + i] = (unsigned long long)(unsigned)row | (lo << 32) | (hi << 48);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int tot = 0;
+            for (int w = 0; w < 16; ++w) tot += wsum[w];
+            run += tot;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) *nitems = run;
 }
 
 template <int M>
@@ -872,8 +915,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(M <= 8 ? 3 
     const float* __restrict__ dF, int64_t d, int64_t rows_per_group,
     const uint8_t* __restrict__ Pold, const uint8_t* __restrict__ Pnew,
     const float* __restrict__ C, float* __restrict__ R, const uint32_t* __restrict__ clist,
-    const int* __restrict__ ccount, const int* __restrict__ order, int nslices,
-    float* __restrict__ dA) {
+    const int* __restrict__ ccount, const unsigned long long* __restrict__ items,
+    const int* __restrict__ nitems, int nslices, float* __restrict__ dA) {
     constexpr int NB = (2 * M + 15) / 16;     // 16-column blocks of [old | new] one-hots
     __shared__ int s_i[DL_G];                 // coordinate of each change of the group
     __shared__ int s_uv[DL_G];                // old code | new code << 8
@@ -881,10 +924,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(M <= 8 ? 3 
     __shared__ float s_h[4][DL_G][16 * NB];   // per-wave partial sums of the F' rows
     if (*mode == 0ull) return;
 
-    const int64_t j = order[blockIdx.x / nslices];
-    const int slice = blockIdx.x % nslices;
+    if ((int)blockIdx.x >= *nitems) return;
+    const unsigned long long item = items[blockIdx.x];
+    const int64_t j = (int64_t)(item & 0xffffffffull);
+    const int s_lo = (int)((item >> 32) & 0xffffu), s_hi = (int)(item >> 48);
     const int K = ccount[j];
-    if (K == 0) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t g = j / rows_per_group;
@@ -896,8 +940,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(M <= 8 ? 3 
     const float* cj = C + j * M;
     const uint32_t* lj = clist + j * d;
     const int nch = (int)(d / 32);
-    const int c_begin = slice * (DL_SL / 32);
-    const int c_end = (c_begin + DL_SL / 32) < nch ? (c_begin + DL_SL / 32) : nch;
+    const int c_begin = s_lo * (DL_SL / 32);
+    const int c_end = (s_hi * (DL_SL / 32)) < nch ? (s_hi * (DL_SL / 32)) : nch;
     const int aq = tid / M, aqq = tid % M;    // entry of A owned by threads tid < M * M
     double accA = 0.0;
 
@@ -938,7 +982,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(M <= 8 ? 3 
         }
         __syncthreads();
     }
-    if (tid < M * M) dA[((size_t)j * nslices + slice) * M * M + tid] = (float)accA;
+    // the item's share goes to its first slice; the other slices it covers hold zero
+    if (tid < M * M) {
+        dA[((size_t)j * nslices + s_lo) * M * M + tid] = (float)accA;
+        for (int sl = s_lo + 1; sl < s_hi; ++sl) dA[((size_t)j * nslices + sl) * M * M + tid] = 0.f;
+    }
 }
 
 // float64 sums of consecutive rows in a fixed order: out[0] = sum_j x[j]
@@ -1033,6 +1081,8 @@ LnqSizes lnq_sizes(int64_t d_out, int64_t d, int groups, int m) {
     z.o_clist = take((size_t)d_out * d * 4);
     z.o_ccount = take((size_t)d_out * 4);
     z.o_order = take((size_t)d_out * 4);
+    z.o_items = take((size_t)d_out * ((d + DL_SL - 1) / DL_SL) * 8);
+    z.o_nitems = take(8);
     z.o_dA = take((size_t)d_out * ((d + DL_SL - 1) / DL_SL) * m * m * 4);
     z.total = off;
     return z;
@@ -1058,6 +1108,8 @@ LnqWs lnq_carve(void* base, const LnqSizes& z) {
     w.clist = (uint32_t*)(b + z.o_clist);
     w.ccount = (int*)(b + z.o_ccount);
     w.order = (int*)(b + z.o_order);
+    w.items = (unsigned long long*)(b + z.o_items);
+    w.nitems = (int*)(b + z.o_nitems);
     w.dA = (float*)(b + z.o_dA);
     return w;
 }
@@ -1149,10 +1201,11 @@ static hipError_t launch_delta(const unsigned long long* mode, const float* F, i
                                int64_t d_out, int groups, const uint8_t* P, const float* C,
                                const LnqWs& w, hipStream_t st) {
     const int nsl = (int)((d + DL_SL - 1) / DL_SL);
-    hipLaunchKernelGGL(k_order_rows, dim3(1), dim3(1024), 0, st, mode, w.ccount, d_out, w.order);
+    hipLaunchKernelGGL(k_order_rows, dim3(1), dim3(1024), 0, st, mode, w.ccount, d_out, nsl,
+                       w.order, w.items, w.nitems);
     GQ_LAUNCH_CHECK();
     hipLaunchKernelGGL((k_delta<M>), dim3((unsigned)(d_out * nsl)), dim3(256), 0, st, mode, F,
-                       w.dF, d, d_out / groups, w.pprev, P, C, w.R, w.clist, w.ccount, w.order,
+                       w.dF, d, d_out / groups, w.pprev, P, C, w.R, w.clist, w.ccount, w.items, w.nitems,
                        nsl, w.dA);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
