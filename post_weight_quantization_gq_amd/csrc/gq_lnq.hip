@@ -12,7 +12,8 @@
 //   k_ridge        lambda_g = rho * mean(diag F_g)                       (float64)
 //   k_split        F' -> two bfloat16 planes hi + lo (F' ~= hi + lo to ~2^-17),
 //                  plus diag(F') in float32
-//   k_lnq_init     per row: sort w_j in LDS, m linear quantiles, nearest codes
+//   k_lnq_init     per row: m linear quantiles of w_j (float32 weights: from a sort in
+//                  LDS; bfloat16: order statistics by radix select), nearest codes
 //   k_err_split    E = C[P] - W in float32, split into bfloat16 hi + lo planes
 //   k_mm (gq_lnq_mm.hip)  residual R = E F' and the codebook Gram blocks
 //                  P_j^T F' P_j on the matrix cores
@@ -150,6 +151,138 @@ __global__ __launch_bounds__(1024) void k_lnq_init(const void* __restrict__ W, i
     __syncthreads();
     for (int64_t i = tid; i < d; i += 1024) {
         const double w = (double)load_elem<BF16>(W, j * d + i);
+        double best = fabs(w - (double)cb[0]);
+        int bq = 0;
+        for (int q = 1; q < m; ++q) {
+            const double dist = fabs(w - (double)cb[q]);
+            if (dist < best) { best = dist; bq = q; }
+        }
+        P[j * d + i] = (uint8_t)bq;
+    }
+}
+
+// The same initial codebook and codes for bfloat16 weights, with the order statistics
+// found by a two-pass radix select instead of a sort.  A bfloat16 value maps to a
+// 16-bit key whose unsigned order is the value order (sign set: all bits flipped;
+// else the sign bit set).  Pass 1 counts the keys by high byte; each needed rank
+// (positions floor(h_q) and floor(h_q) + 1) is located in its high-byte bin; pass 2
+// counts the low bytes of the keys in those bins; a scan of that count gives the key
+// at the rank.  The quantiles are then formed exactly as from the sorted row.  One
+// block (256 threads) per row.
+__device__ __forceinline__ uint32_t bf16_order_key(uint32_t b) {
+    return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
+}
+__device__ __forceinline__ float bf16_from_order_key(uint32_t k) {
+    const uint32_t b = (k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu);
+    return __uint_as_float(b << 16);
+}
+
+__global__ __launch_bounds__(256) void k_lnq_init_select(const uint16_t* __restrict__ W,
+                                                         int64_t d, int m,
+                                                         float* __restrict__ C,
+                                                         uint8_t* __restrict__ P) {
+    constexpr int NR = 2 * MAX_M;                // ranks: floor(h_q) and the next, per q
+    __shared__ int hist1[256];
+    __shared__ int pre1[257];
+    __shared__ int hist2[NR][256];
+    __shared__ int slot_of_bin[256];
+    __shared__ int rank_bin[NR], rank_rem[NR];
+    __shared__ float ostat[NR];
+    __shared__ float cb[MAX_M];
+    const int64_t j = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint16_t* Wj = W + j * d;
+    const int nr = 2 * m;
+    hist1[tid] = 0;
+    slot_of_bin[tid] = -1;
+    for (int e = tid; e < NR * 256; e += 256) (&hist2[0][0])[e] = 0;
+    __syncthreads();
+    // pass 1: high bytes (d % 32 == 0: 8 elements per 16-byte load)
+    for (int64_t i = 8 * (int64_t)tid; i < d; i += 8 * 256) {
+        const u32x4 v = *(const u32x4*)(Wj + i);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            atomicAdd(&hist1[bf16_order_key((v[e >> 1] >> (16 * (e & 1))) & 0xffffu) >> 8], 1);
+    }
+    __syncthreads();
+    if (wave == 0) {              // exclusive scan of the 256 counts, 4 per lane
+        int c[4], t = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { c[u] = hist1[4 * lane + u]; t += c[u]; }
+        int incl = t;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        int run = incl - t;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { pre1[4 * lane + u] = run; run += c[u]; }
+        if (lane == 63) pre1[256] = incl;
+    }
+    __syncthreads();
+    if (tid < nr) {               // the bin of each rank
+        const int q = tid >> 1;
+        const double h = (double)((d - 1) * (int64_t)(2 * q + 1)) / (double)(2 * m);
+        const int64_t lo = (int64_t)floor(h);
+        const int64_t r = (tid & 1) ? ((lo + 1 < d) ? lo + 1 : d - 1) : lo;
+        int b = 0;
+        for (int st = 128; st > 0; st >>= 1)
+            if (pre1[b + st] <= r) b += st;
+        rank_bin[tid] = b;
+        rank_rem[tid] = (int)(r - pre1[b]);
+    }
+    __syncthreads();
+    if (tid == 0)                 // one low-byte count per distinct bin
+        for (int t = 0; t < nr; ++t)
+            if (slot_of_bin[rank_bin[t]] < 0) slot_of_bin[rank_bin[t]] = t;
+    __syncthreads();
+    // pass 2: low bytes of the keys in those bins
+    for (int64_t i = 8 * (int64_t)tid; i < d; i += 8 * 256) {
+        const u32x4 v = *(const u32x4*)(Wj + i);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t key = bf16_order_key((v[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            const int sl = slot_of_bin[key >> 8];
+            if (sl >= 0) atomicAdd(&hist2[sl][key & 0xffu], 1);
+        }
+    }
+    __syncthreads();
+    for (int t = wave; t < nr; t += 4) {   // the key at each rank: a scan per rank
+        const int* hb = hist2[slot_of_bin[rank_bin[t]]];
+        const int want = rank_rem[t];
+        int c[4], tot = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { c[u] = hb[4 * lane + u]; tot += c[u]; }
+        int incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        int run = incl - tot, low = -1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (low < 0 && want >= run && want < run + c[u]) low = 4 * lane + u;
+            run += c[u];
+        }
+        const unsigned long long hit = __ballot(low >= 0);
+        const int src = __ffsll((long long)hit) - 1;
+        const int lb = __shfl(low, src, 64);
+        if (lane == 0) ostat[t] = bf16_from_order_key(((uint32_t)rank_bin[t] << 8) | (uint32_t)lb);
+    }
+    __syncthreads();
+    if (tid < m) {
+        const double h = (double)((d - 1) * (int64_t)(2 * tid + 1)) / (double)(2 * m);
+        const double fl = floor(h);
+        const double v = quantile_interp((double)ostat[2 * tid], (double)ostat[2 * tid + 1], h - fl);
+        const float cf = (float)v;
+        cb[tid] = cf;
+        C[j * m + tid] = cf;
+    }
+    __syncthreads();
+    for (int64_t i = tid; i < d; i += 256) {
+        const double w = (double)bf16_bits_to_f32(Wj[i]);
         double best = fabs(w - (double)cb[0]);
         int bq = 0;
         for (int q = 1; q < m; ++q) {
@@ -1134,11 +1267,8 @@ hipError_t lnq_init_run(const void* W, bool w_bf16, int64_t d_out, int64_t d, in
     const size_t lds = (size_t)npow2 * sizeof(float);
     StageTimer tm(ST_LNQ_INIT, st);
     if (w_bf16) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_lnq_init<true>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_lnq_init<true>, dim3((unsigned)d_out), dim3(1024), lds, st, W, d,
-                           npow2, m, C, P);
+        hipLaunchKernelGGL(k_lnq_init_select, dim3((unsigned)d_out), dim3(256), 0, st,
+                           (const uint16_t*)W, d, m, C, P);
     } else {
         hipError_t e = hipFuncSetAttribute((const void*)k_lnq_init<false>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
