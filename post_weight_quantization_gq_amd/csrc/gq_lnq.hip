@@ -356,6 +356,14 @@ __global__ __launch_bounds__(256) void k_err_split(const float* __restrict__ C, 
     *(u32x4*)(Elo + off + 8) = l[1];
 }
 
+// lane l's value of v, in every lane
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)b, l);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __hiloint2double(hi, lo);
+}
+
 // s + x(0) + x(1) + ... + x(n-1), added in that order, the loads issued 8 at a time
 template <typename Get>
 __device__ __forceinline__ double ordered_sum(int n, Get x, double s) {
@@ -394,11 +402,8 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
                                               const int* __restrict__ ccount,
                                               const float* __restrict__ dA, int nslices) {
     __shared__ double sB[4][M][M];
-    __shared__ double sL[4][M][M];
     __shared__ double sg[4][M];
-    __shared__ double sy[4][M];
     __shared__ int scnt[4][M];
-    __shared__ int sidx[4][M];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t j0 = (int64_t)blockIdx.x * 4 + wave;
     const bool valid = j0 < d_out;
@@ -493,41 +498,59 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
             Aj[e] = sB[wave][q][qp] + sB[wave][qp][q];
         }
     }
-    if (valid && lane == 0) {
-        int ns = 0;
-        for (int k = 0; k < M; ++k)
-            if (scnt[wave][k] > 0) sidx[wave][ns++] = k;
+    // Cholesky and the two triangular solves, spread over the wave: lane r holds row r
+    // of A (then of L) in registers.  An empty code's row and column are replaced by
+    // those of the identity (with g = 0), which leaves the factor of the non-empty
+    // codes, taken in increasing code order, unchanged and gives that code a zero
+    // step.  Every entry sees the same operations in the same order as the textbook
+    // left-looking recurrences
+    //     L_rc = (A_rc - sum_{k<c} L_rk L_ck) / L_cc,  L_cc = sqrt(A_cc - sum_{k<c} L_ck^2),
+    //     y_r = (-g_r - sum_{k<r} L_rk y_k) / L_rr,    x_r = (y_r - sum_{k>r} L_kr x_k) / L_rr.
+    if (valid) {
+        const int r = lane;
+        const bool rin = r < M;
+        const int rr = rin ? r : 0;
+        const bool ract = rin && scnt[wave][rr] > 0;
+        double a[M];
+#pragma unroll
+        for (int c = 0; c < M; ++c)
+            a[c] = (ract && scnt[wave][c] > 0) ? sB[wave][rr][c] + sB[wave][c][rr]
+                                               : ((r == c) ? 1.0 : 0.0);
         bool ok = true;
-        // A[q'][q] = B[q'][q] + B[q][q'] = sB[q][q'] + sB[q'][q]
-        for (int r = 0; r < ns && ok; ++r) {
-            for (int c = 0; c <= r; ++c) {
-                const int ir = sidx[wave][r], ic = sidx[wave][c];
-                double sum = sB[wave][ir][ic] + sB[wave][ic][ir];
-                for (int k = 0; k < c; ++k) sum -= sL[wave][r][k] * sL[wave][c][k];
-                if (r == c) {
-                    if (!(sum > 0.0)) { ok = false; break; }
-                    sL[wave][r][r] = sqrt(sum);
-                } else {
-                    sL[wave][r][c] = sum / sL[wave][c][c];
-                }
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            const double piv = readlane_d(a[k], k);
+            if (!(piv > 0.0)) { ok = false; break; }
+            const double lkk = sqrt(piv);
+            if (r == k) a[k] = lkk;
+            else if (r > k) a[k] = a[k] / lkk;
+#pragma unroll
+            for (int c = k + 1; c < M; ++c) {
+                const double lck = readlane_d(a[k], c);
+                if (r >= c) a[c] = fma(-a[k], lck, a[c]);
             }
         }
         if (ok) {
-            for (int r = 0; r < ns; ++r) {
-                double sum = -sg[wave][sidx[wave][r]];
-                for (int k = 0; k < r; ++k) sum -= sL[wave][r][k] * sy[wave][k];
-                sy[wave][r] = sum / sL[wave][r][r];
+            double t = ract ? -sg[wave][rr] : 0.0;
+            double x[M];                  // uniform across the wave
+#pragma unroll
+            for (int k = 0; k < M; ++k) {
+                x[k] = readlane_d(t, k) / readlane_d(a[k], k);
+                if (r > k) t = fma(-a[k], x[k], t);
             }
-            for (int r = ns - 1; r >= 0; --r) {
-                double sum = sy[wave][r];
-                for (int k = r + 1; k < ns; ++k) sum -= sL[wave][k][r] * sy[wave][k];
-                sy[wave][r] = sum / sL[wave][r][r];
+#pragma unroll
+            for (int q = M - 1; q >= 0; --q) {
+                double s2 = x[q];
+#pragma unroll
+                for (int k = q + 1; k < M; ++k) s2 = fma(-readlane_d(a[q], k), x[k], s2);
+                x[q] = s2 / readlane_d(a[q], q);
             }
-            for (int r = 0; r < ns; ++r) {
-                const int k = sidx[wave][r];
-                C[j * M + k] = (float)((double)C[j * M + k] + sy[wave][r]);
+            if (lane == 0) {
+#pragma unroll
+                for (int k = 0; k < M; ++k)
+                    if (scnt[wave][k] > 0) C[j * M + k] = (float)((double)C[j * M + k] + x[k]);
             }
-        } else if (n_not_pd) {
+        } else if (lane == 0 && n_not_pd) {
             atomicAdd(n_not_pd, 1ull);
         }
     }
