@@ -34,6 +34,10 @@ Readings where the pages are silent (the same readings the GPU library uses):
   * Empty code q (no coordinate assigned): c_q is kept unchanged.
   * Assignment: coordinates in ascending order; a coordinate moves only on a
     strict decrease of the objective, to the lowest-index minimiser.
+  * Fixed-grid backend (the blog page's remark that the objective plugs into
+    any layer-wise quantizer): a uniform min-max grid per row, kept fixed, and
+    the assignment pass only.  The grid is the plain definition of an equally
+    spaced grid from the row's minimum to its maximum.
 """
 from __future__ import annotations
 
@@ -43,7 +47,7 @@ __all__ = [
     "group_scale", "fisher", "fisher_entry", "fisher_per_channel", "ridge_lambda",
     "damped", "init_quantile", "one_hot", "codebook_system", "codebook_update",
     "assign_deltas", "assign_sweep", "objective", "lnq_row", "guided_loss",
-    "replay_sweep",
+    "replay_sweep", "init_uniform_grid", "grid_row",
 ]
 
 
@@ -273,3 +277,46 @@ def replay_sweep(Fp: np.ndarray, w: np.ndarray, c: np.ndarray, p_start: np.ndarr
             obj += float(D[q])
             p[i] = q
     return worst, differ
+
+
+# ----------------------------------------------------------------------------
+# Fixed-grid scalar backend [GQ-obj], [LNQ-alg]
+# ----------------------------------------------------------------------------
+# The blog page says the GuidedQuant objective can serve any layer-wise
+# quantizer.  The plainest scalar one keeps a uniform grid per row and runs only
+# the "(assignment)" pass of the LNQ algorithm box on that objective.
+
+def init_uniform_grid(w: np.ndarray, m: int):
+    """Uniform grid of a row and its nearest codes.
+
+    m >= 2 equally spaced values from lo = min(w) to hi = max(w):
+    c_q = lo + q * ((hi - lo) / (m - 1)), each product and sum rounded in
+    float64, then stored as float32.  Codes: index of the nearest entry, the
+    lowest index on ties, compared in float64 on the stored values.  The pages
+    name no grid; this is the min-max grid's definition.
+    """
+    w = np.asarray(w, np.float64)
+    lo, hi = float(np.min(w)), float(np.max(w))
+    step = (hi - lo) / float(m - 1)
+    c = np.array([lo + float(q) * step for q in range(m)])
+    c = c.astype(np.float32).astype(np.float64)
+    p = np.argmin(np.abs(w[:, None] - c[None, :]), axis=1).astype(np.int64)
+    return c, p
+
+
+def grid_row(Fp: np.ndarray, w: np.ndarray, m: int, iters: int, c0=None, p0=None):
+    """Fixed-grid backend for one row: the grid stays, `iters` assignment passes.
+
+    Returns (c, p, trace) with trace[t] the objective before pass t + 1 and
+    trace[iters] the objective after the last pass.
+    """
+    if c0 is None:
+        c, p = init_uniform_grid(w, m)
+    else:
+        c = np.asarray(c0, np.float64).copy()
+        p = np.asarray(p0, np.int64).copy()
+    trace = [objective(Fp, w, c, p)]
+    for _ in range(iters):
+        p = assign_sweep(Fp, w, c, p)
+        trace.append(objective(Fp, w, c, p))
+    return c, p, np.array(trace)

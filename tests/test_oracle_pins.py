@@ -455,3 +455,76 @@ def test_generator_deterministic_and_prefix_stable():
     big = np.sort(np.argsort(np.std(X, 0))[-4:])
     assert np.array_equal(big, a["outlier_cols"])
     assert wl.m == 8
+
+
+# --------------------------------------------------------------------------
+# Fixed-grid backend: uniform min-max grid, assignment passes only
+# --------------------------------------------------------------------------
+
+def test_uniform_grid_hand_example():
+    """w = (-1, 0.5, 2), m = 4: grid -1, 0, 1, 2; 0.5 is equally far from 0 and 1 and
+    takes the lower index; codes (0, 1, 3)."""
+    c, p = O.init_uniform_grid(np.array([-1.0, 0.5, 2.0]), 4)
+    np.testing.assert_array_equal(c, [-1.0, 0.0, 1.0, 2.0])
+    np.testing.assert_array_equal(p, [0, 1, 3])
+
+
+@pytest.mark.parametrize("m", [2, 4, 8, 16])
+def test_uniform_grid_definition(m):
+    """Endpoints at the row's minimum and maximum, equal spacing, nearest codes
+    (brute force over the grid, lowest index on ties)."""
+    rng = _rng(70 + m)
+    for _ in range(20):
+        w = (rng.standard_normal(257) * 0.02).astype(np.float32).astype(np.float64)
+        c, p = O.init_uniform_grid(w, m)
+        assert c[0] == w.min()
+        ulp = np.spacing(np.float32(abs(w.max())))
+        assert abs(c[-1] - w.max()) <= ulp
+        assert np.all(np.diff(c) > 0)
+        step = (w.max() - w.min()) / (m - 1)
+        assert np.max(np.abs(np.diff(c) - step)) <= 2 * np.spacing(np.float32(np.abs(c).max()))
+        for i in range(w.shape[0]):
+            dist = np.abs(w[i] - c)
+            assert dist[p[i]] == dist.min()
+            assert p[i] == np.flatnonzero(dist == dist.min())[0]
+
+
+def test_uniform_grid_constant_row():
+    c, p = O.init_uniform_grid(np.full(9, 0.25), 8)
+    assert np.all(c == 0.25) and np.all(p == 0)
+
+
+def test_grid_row_diagonal_F_keeps_nearest_codes():
+    """Diagonal F': the objective separates over coordinates and the nearest grid
+    point is each coordinate's minimiser, so no pass moves a code."""
+    rng = _rng(80)
+    d, m = 40, 8
+    F = np.diag(rng.uniform(0.1, 3.0, d))
+    w = rng.standard_normal(d) * 0.02
+    c0, p0 = O.init_uniform_grid(w, m)
+    c, p, tr = O.grid_row(F, w, m, 3)
+    np.testing.assert_array_equal(p, p0)
+    np.testing.assert_array_equal(c, c0)
+    assert np.all(tr == tr[0])
+
+
+def test_grid_row_monotone_local_min_and_bruteforce_bound():
+    """Coupled F': the trace never increases; once a pass changes nothing the codes
+    are a one-coordinate local minimum (every single change checked), and the
+    brute-force optimum over all m^d codes on the same grid is no larger."""
+    rng = _rng(81)
+    d, m = 6, 4
+    for _ in range(5):
+        F = _spd(rng, d, n=d + 2)
+        w = rng.standard_normal(d)
+        c, p, tr = O.grid_row(F, w, m, 12)
+        assert np.all(np.diff(tr) <= 1e-15)
+        assert np.array_equal(O.assign_sweep(F, w, c, p), p)
+        base = O.objective(F, w, c, p)
+        for i in range(d):
+            for q in range(m):
+                t = p.copy()
+                t[i] = q
+                assert O.objective(F, w, c, t) >= base - 1e-12
+        best = min(O.objective(F, w, c, np.array(t)) for t in itertools.product(range(m), repeat=d))
+        assert best <= base + 1e-15
