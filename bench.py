@@ -5,7 +5,11 @@ grouped Fisher accumulation from (X, G), then LNQ (init + `iters` x (codebook
 step, assignment pass) + objective trace) on every output row.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--path lnq|grid] [--no-cpu-baseline]
+
+--path grid replaces LNQ by the fixed-grid backend (uniform min-max grid per
+row, `iters` assignment passes, no codebook step) and reports that path's own
+metric.
 
 Prints one JSON line.  `value` is rows quantized per second for the whole
 layer (Fisher included); the Fisher TFLOP/s, the LNQ-only rows/s and the
@@ -42,6 +46,7 @@ def _parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama2_7b_attn")
+    ap.add_argument("--path", choices=("lnq", "grid"), default="lnq")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -94,6 +99,24 @@ def _incremental_iters(wl, nchg):
     return [t for t in range(2, wl.iters + 1) if nchg[t - 2] <= lim]
 
 
+def _grid_roofline(wl, nchg, ms_step):
+    """Composite lower bound on one layer with the fixed-grid backend:
+      group scale and Fisher as for LNQ;
+      per pass           4 G d_in^2 (F' read once) + d_out d_in (codes) bytes at the HBM peak
+                         + (3 m d_in per row for the candidate changes + 2 d_in per changed
+                         coordinate) fp32 flops at the fp32 vector peak.
+    frac = t_roof / t_measured."""
+    n, d, d_out, G, m, it = wl.n, wl.d_in, wl.d_out, wl.groups, wl.m, wl.iters
+    t_scale = (2 * n * d_out + 4 * G * n) / PEAK_HBM
+    t_fisher = n * d * (d + 1) * G / PEAK_BF16_MFMA
+    t_bytes = it * (4 * G * d * d + d_out * d) / PEAK_HBM
+    t_alu = (it * d_out * 3 * m * d + 2 * d * float(np.sum(nchg))) / PEAK_FP32_VALU
+    t_roof = t_scale + t_fisher + t_bytes + t_alu
+    return {"t_roof_ms": t_roof * 1e3, "t_measured_ms": ms_step, "frac": t_roof * 1e3 / ms_step,
+            "terms_ms": {"group_scale": t_scale * 1e3, "fisher": t_fisher * 1e3,
+                         "passes_bytes": t_bytes * 1e3, "passes_alu": t_alu * 1e3}}
+
+
 def _layer_roofline(wl, nchg, ms_step):
     """Composite lower bound on the time of one layer (Fisher + LNQ), term by term:
       group scale        bytes 2 n d_out + 4 G n at the HBM peak;
@@ -114,7 +137,7 @@ def _layer_roofline(wl, nchg, ms_step):
                          "codebook_systems": t_gram * 1e3, "residual_and_moves": t_upd * 1e3}}
 
 
-def _stage_units(stage, wl, nchg):
+def _stage_units(stage, wl, nchg, grid=False):
     """Algorithmic work of a stage in one step: (bound, amount, peak, unit, launches).
 
     The contractions count the flops of the bf16 products the method runs: F' and the
@@ -126,8 +149,8 @@ def _stage_units(stage, wl, nchg):
     once), or None when every launch does.
     """
     n, d, d_out, G, m, it = wl.n, wl.d_in, wl.d_out, wl.groups, wl.m, wl.iters
-    incr = _incremental_iters(wl, nchg)
-    dense = it - len(incr)
+    incr = [] if grid else _incremental_iters(wl, nchg)
+    dense = 0 if grid else it - len(incr)
     if stage == "fisher_mfma":
         # unique entries of the symmetric F_g: n d (d + 1) flops per group
         return "mfma", n * d * (d + 1) * G, PEAK_BF16_MFMA, "TFLOP/s", None
@@ -137,7 +160,8 @@ def _stage_units(stage, wl, nchg):
         return "mfma", dense * 2 * 2 * tri * d_out * m, PEAK_BF16_MFMA, "TFLOP/s", dense
     if stage == "lnq_resid":
         # before each recomputed codebook step, before each pass, and the final objective;
-        # each E F' per group as three bf16 products
+        # each E F' per group as three bf16 products (the fixed-grid path: before each
+        # pass and the final objective)
         calls = dense + it + 1
         return "mfma", calls * 3 * 2 * d_out * d * d, PEAK_BF16_MFMA, "TFLOP/s", calls
     if stage == "lnq_delta":
@@ -152,8 +176,11 @@ def _stage_units(stage, wl, nchg):
         return ("alu", it * d_out * d * 3 * m + 2 * d * float(np.sum(nchg)), PEAK_FP32_VALU,
                 "TFLOP/s", None)
     if stage == "lnq_solve":
-        # per call: read R, P, W and the Gram partials
+        # per call: read R, P, W and the Gram partials (the fixed-grid path: the final
+        # objective only)
         ntile = (d + 255) // 256
+        if grid:
+            return "hbm", d_out * d * (4 + 1 + 2), PEAK_HBM, "GB/s", None
         return ("hbm", (it + 1) * d_out * (d * (4 + 1 + 2) + ntile * m * m * 4), PEAK_HBM,
                 "GB/s", None)
     if stage == "group_scale":
@@ -210,8 +237,13 @@ def main():
     C = torch.empty((wl.d_out, wl.m), dtype=torch.float32, device=dev)
     P = torch.empty((wl.d_out, wl.d_in), dtype=torch.uint8, device=dev)
 
+    grid = args.path == "grid"
+
     def step():
         gq.gq_fisher_accumulate(X, G, wl.groups, F=F, ws=ws_f)
+        if grid:
+            return gq.grid_quantize(W, F, wl.bits, wl.iters, block=64, ridge_rel=1e-6, C=C,
+                                    P=P, init=gq.GQ_INIT_UNIFORM, ws=ws_l)
         return gq.lnq_quantize(W, F, wl.bits, wl.iters, block=64, ridge_rel=1e-6, C=C,
                                P=P, init=gq.GQ_INIT_QUANTILE, ws=ws_l)
 
@@ -256,7 +288,7 @@ def main():
     # roofline of the stage with the largest share of the step, from the events of
     # the timed region
     roof = None
-    spec = _stage_units(dom, wl, nchg)
+    spec = _stage_units(dom, wl, nchg, grid)
     if spec is not None and timed[dom][1]:
         bound, amount, peak, unit, working = spec
         n_launch = timed[dom][1] / args.steps if working is None else working
@@ -271,8 +303,11 @@ def main():
                 "avg_launch_ms": avg_ms, "units_per_launch": per_launch,
                 "launches_per_step": n_launch}
 
+    metric = ("Fixed-grid GuidedQuant rows quantized/s (Fisher + uniform grid + assignment "
+              f"passes) at {wl.d_in}x{wl.d_out}, {wl.bits}-bit, 1 MI355X" if grid else
+              "LNQ rows quantized/s + Fisher TFLOP/s at 4096x4096, 3-bit, 1 MI355X")
     result = {
-        "metric": "LNQ rows quantized/s + Fisher TFLOP/s at 4096x4096, 3-bit, 1 MI355X",
+        "metric": metric,
         "value": wl.d_out / (ms_step * 1e-3),
         "unit": "rows/s",
         "n_gpus": 1,
@@ -284,8 +319,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "d_in": wl.d_in, "d_out": wl.d_out, "n_tokens": wl.n,
-                   "groups": wl.groups, "bits": wl.bits, "iters": wl.iters, "block": 64},
+        "config": {"workload": wl.name, "path": args.path, "d_in": wl.d_in, "d_out": wl.d_out,
+                   "n_tokens": wl.n, "groups": wl.groups, "bits": wl.bits, "iters": wl.iters,
+                   "block": 64},
         "fisher_tflops": sym_flops / (fisher_ms * 1e-3) / 1e12 if fisher_ms else None,
         "fisher_tflops_gemm_convention": (2 * wl.n * wl.d_in ** 2 * wl.groups) /
         (fisher_ms * 1e-3) / 1e12 if fisher_ms else None,
@@ -295,10 +331,10 @@ def main():
         "stage_launches_per_step": launches,
         "stage_breakdown_from": "last warmup step, every stage bracketed by HIP events",
         "changed_per_sweep": [int(x) for x in nchg],
-        "codebook_steps_from_changes": _incremental_iters(wl, nchg),
+        "codebook_steps_from_changes": [] if grid else _incremental_iters(wl, nchg),
         "objective_trace": [float(x) for x in trace],
         "monotone": bool(np.all(trace[1:] <= trace[:-1] * (1 + 1e-6))),
-        "layer_roofline": _layer_roofline(wl, nchg, ms_step),
+        "layer_roofline": (_grid_roofline if grid else _layer_roofline)(wl, nchg, ms_step),
         "roofline": roof,
     }
 
@@ -323,24 +359,25 @@ def cpu_baseline(wl, inp, F, args):
     t0 = time.perf_counter()
     O.fisher(Xs, Gs, wl.groups)
     t_f = (time.perf_counter() - t0) * (wl.n / nt)
-    print(f"[bench] cpu baseline: oracle LNQ on {args.cpu_rows} rows", file=sys.stderr,
+    print(f"[bench] cpu baseline: oracle {args.path} on {args.cpu_rows} rows", file=sys.stderr,
           flush=True)
     F64 = F.cpu().double().numpy()
     w = synth.decode(inp["W"])
     rpg = wl.d_out // wl.groups
     rows = [(r * rpg) % wl.d_out for r in range(args.cpu_rows)]
     t_rows = 0.0
+    row_fn = O.grid_row if args.path == "grid" else O.lnq_row
     for j in rows:
         Fp = O.damped(F64[j // rpg], 1e-6)
         t0 = time.perf_counter()
-        O.lnq_row(Fp, w[j], wl.m, wl.iters)
+        row_fn(Fp, w[j], wl.m, wl.iters)
         t_rows += time.perf_counter() - t0
     t_row = t_rows / len(rows)
     t_layer = t_f + t_row * wl.d_out
     return {"value": wl.d_out / t_layer, "unit": "rows/s", "cores": blas_threads,
             "kind": "oracle",
             "sample": f"Fisher on the first {nt} of {wl.n} tokens (scaled x{wl.n / nt:g}, "
-                      f"{t_f * nt / wl.n:.1f}s measured) + LNQ on {len(rows)} rows "
+                      f"{t_f * nt / wl.n:.1f}s measured) + {'fixed-grid passes' if args.path == 'grid' else 'LNQ'} on {len(rows)} rows "
                       f"({t_row:.2f}s/row, scaled to {wl.d_out} rows); LNQ rows run on one "
                       f"core, the Fisher matmul on {blas_threads} BLAS threads",
             "fisher_s_est": t_f, "lnq_s_per_row": t_row}

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 2
+#define GQ_ABI_VERSION 3
 
 typedef enum {
     GQ_OK = 0,
@@ -73,7 +73,7 @@ typedef enum {
 
 typedef enum { GQ_F32 = 0, GQ_BF16 = 1 } gq_dtype;
 
-typedef enum { GQ_INIT_QUANTILE = 0, GQ_INIT_GIVEN = 1 } gq_lnq_init;
+typedef enum { GQ_INIT_QUANTILE = 0, GQ_INIT_GIVEN = 1, GQ_INIT_UNIFORM = 2 } gq_lnq_init;
 
 typedef enum { GQ_GRAM_AUTO = 0, GQ_GRAM_DENSE = 1 } gq_gram_update;
 
@@ -87,8 +87,12 @@ typedef struct {
     float ridge_rel;    /* rho in lambda_g = rho * mean(diag F_g).  Default 1e-6. */
     int32_t init;       /* gq_lnq_init.  QUANTILE: c_j = m quantiles of w_j at levels
                            (q + 1/2)/m (linear interpolation between order statistics),
+                           codes = nearest entry (lowest index on ties).  UNIFORM: the
+                           row's uniform grid c_q = lo + q (hi - lo)/(m - 1), lo and hi the
+                           row's minimum and maximum, formed in float64 and stored float32,
                            codes = nearest entry (lowest index on ties).  GIVEN: start from
-                           the C and P passed in.  Default QUANTILE. */
+                           the C and P passed in.  Default QUANTILE (grid_quantize: UNIFORM
+                           when opt is NULL; it rejects QUANTILE). */
     int32_t gram_update; /* gq_gram_update: how each codebook step after the first obtains
                            A_j = P_j^T F' P_j and the residual F'(C[P] - W).  DENSE:
                            recomputed from scratch on the matrix cores.  AUTO: when the
@@ -199,6 +203,29 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
                        const gq_lnq_options* opt, float* C, uint8_t* P,
                        double* obj_trace, int64_t* n_changed,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Fixed-grid scalar backend with the GuidedQuant objective.  The blog page says
+ * its objective can be used by any layer-wise quantizer; this entry point is
+ * the plainest such backend: each row keeps a fixed uniform grid (opt->init ==
+ * GQ_INIT_UNIFORM, the min-max grid described under gq_lnq_options.init, or
+ * GQ_INIT_GIVEN: the C and P passed in) and only the "(assignment)" pass of the
+ * LNQ algorithm box is run, `iters` times; there is no codebook step.
+ * Arguments as for lnq_quantize: W [d_out][d_in] (w_dt), F [groups][d_in][d_in];
+ * C [d_out][2^bits] and P [d_out][d_in] outputs (inputs too under GIVEN).
+ * obj_trace (device float64 [iters+1], may be NULL): layer objective
+ * sum_j e_j^T F' e_j before each pass and after the last, each recomputed
+ * from (C, P); it never increases.  n_changed (device int64 [iters], may be
+ * NULL): coordinates changed by each pass (overwritten).  opt == NULL means the
+ * defaults with init UNIFORM; opt->gram_update is ignored.  Requires
+ * 1 <= bits <= 4, iters >= 0; GQ_EINVAL for init == GQ_INIT_QUANTILE.  Workspace:
+ * gq_lnq_workspace_size.
+ */
+gq_status grid_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in,
+                        const float* F, int32_t groups, int32_t bits, int32_t iters,
+                        const gq_lnq_options* opt, float* C, uint8_t* P,
+                        double* obj_trace, int64_t* n_changed,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Diagnostics: per-stage kernel timing with HIP events.

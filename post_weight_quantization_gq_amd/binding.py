@@ -16,15 +16,15 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "li
 
 GQ_OK, GQ_EINVAL, GQ_ESHAPE, GQ_EDTYPE, GQ_ENOMEM, GQ_EHIP, GQ_ENOTIMPL = 0, 1, 2, 3, 4, 5, 8
 GQ_F32, GQ_BF16 = 0, 1
-GQ_INIT_QUANTILE, GQ_INIT_GIVEN = 0, 1
+GQ_INIT_QUANTILE, GQ_INIT_GIVEN, GQ_INIT_UNIFORM = 0, 1, 2
 GQ_GRAM_AUTO, GQ_GRAM_DENSE = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # every symbol include/gq.h declares
 EXPORTS = (
     "gq_abi_version", "gq_last_error", "gq_lnq_options_default", "gq_fisher_workspace_size",
     "gq_fisher_accumulate", "gq_lnq_workspace_size", "lnq_codebook_update", "lnq_assign_sweep",
-    "lnq_objective", "lnq_quantize", "gq_timing_enable", "gq_timing_read", "gq_stage_name",
+    "lnq_objective", "lnq_quantize", "grid_quantize", "gq_timing_enable", "gq_timing_read", "gq_stage_name",
 )
 STAGE_COUNT = 13
 
@@ -61,6 +61,9 @@ _SIGS = {
     "lnq_quantize": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _i32,
                                     ctypes.POINTER(lnq_options), _vp, _vp, _vp, _vp, _vp, _sz,
                                     _vp]),
+    "grid_quantize": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _i32,
+                                     ctypes.POINTER(lnq_options), _vp, _vp, _vp, _vp, _vp, _sz,
+                                     _vp]),
     "gq_timing_enable": (None, [ctypes.c_int]),
     "gq_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "gq_stage_name": (ctypes.c_char_p, [ctypes.c_int]),
@@ -262,6 +265,36 @@ def lnq_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float 
     _check(lib.lnq_quantize(_ptr(W), _dt(W), d_out, d_in, _ptr(F), groups, bits, iters,
                             ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), _ptr(ws),
                             nb, _stream(stream)))
+    return C, P, tr, nch[:iters]
+
+
+def grid_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float = 1e-6,
+                  C=None, P=None, init: int | None = None, trace: bool = True,
+                  ws=None, stream=None):
+    """Fixed-grid backend: uniform grid per row, `iters` assignment passes.
+
+    Returns (C, P, obj_trace [iters+1] or None, n_changed [iters]).  With C and P
+    given and init unset, starts from them (GQ_INIT_GIVEN).
+    """
+    lib = library()
+    groups = F.shape[0]
+    d_out, d_in = _lnq_common(F, W, groups)
+    m = 1 << bits
+    if init is None:
+        init = GQ_INIT_GIVEN if (C is not None and P is not None) else GQ_INIT_UNIFORM
+    if C is None:
+        C = torch.empty((d_out, m), dtype=torch.float32, device=W.device)
+    if P is None:
+        P = torch.empty((d_out, d_in), dtype=torch.uint8, device=W.device)
+    _dev(C, "C", torch.float32)
+    _dev(P, "P", torch.uint8)
+    tr = torch.empty(iters + 1, dtype=torch.float64, device=W.device) if trace else None
+    nch = torch.zeros(max(iters, 1), dtype=torch.int64, device=W.device)
+    opt = options(block, ridge_rel, init)
+    ws, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
+    _check(lib.grid_quantize(_ptr(W), _dt(W), d_out, d_in, _ptr(F), groups, bits, iters,
+                             ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), _ptr(ws),
+                             nb, _stream(stream)))
     return C, P, tr, nch[:iters]
 
 

@@ -311,7 +311,7 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
     if (iters < 0) return fail(GQ_EINVAL, "iters must be >= 0");
     if (o.gram_update != GQ_GRAM_AUTO && o.gram_update != GQ_GRAM_DENSE)
         return fail(GQ_EINVAL, "unknown gram_update %d", o.gram_update);
-    if (o.init != GQ_INIT_QUANTILE && o.init != GQ_INIT_GIVEN)
+    if (o.init != GQ_INIT_QUANTILE && o.init != GQ_INIT_GIVEN && o.init != GQ_INIT_UNIFORM)
         return fail(GQ_EINVAL, "unknown init %d", o.init);
     if (!block_ok(o.block)) return fail(GQ_EINVAL, "block=%d: the pass uses blocks of 64 coordinates", o.block);
     if (d_in % o.block) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of block=%d",
@@ -327,6 +327,9 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
     if ((e = gq::lnq_prepare(F, groups, d_in, o.ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
     if (o.init == GQ_INIT_QUANTILE &&
         (e = gq::lnq_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
+        return hip_fail(e, "init");
+    if (o.init == GQ_INIT_UNIFORM &&
+        (e = gq::grid_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
         return hip_fail(e, "init");
     // w.cnt: [0] moves of the pass, [1] rows not positive definite, [2] update mode
     if (iters > 0 && (e = gq::lnq_zero_counter(w.cnt, 3, st)) != hipSuccess)
@@ -366,6 +369,62 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
             hipSuccess)
             return hip_fail(e, "final objective");
         if ((e = gq::lnq_reduce(w.objA, d_out, obj_trace + 2 * iters, st)) != hipSuccess)
+            return hip_fail(e, "trace");
+    }
+    return GQ_OK;
+}
+
+gq_status grid_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in, const float* F,
+                        int32_t groups, int32_t bits, int32_t iters, const gq_lnq_options* opt,
+                        float* C, uint8_t* P, double* obj_trace, int64_t* n_changed, void* ws,
+                        size_t ws_bytes, void* stream) {
+    gq_lnq_options o;
+    gq_lnq_options_default(&o);
+    o.init = GQ_INIT_UNIFORM;
+    if (opt) o = *opt;
+    gq_status rc = check_lnq_shape(F, groups, d_in, W, w_dt, d_out, bits, o.ridge_rel);
+    if (rc != GQ_OK) return rc;
+    if (!P || !C) return fail(GQ_EINVAL, "null P or C");
+    if (!al16(P) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "P must be 16-byte and ws 256-byte aligned");
+    if (iters < 0) return fail(GQ_EINVAL, "iters must be >= 0");
+    if (o.init != GQ_INIT_UNIFORM && o.init != GQ_INIT_GIVEN)
+        return fail(GQ_EINVAL, "grid_quantize keeps a uniform grid: init must be UNIFORM or GIVEN, not %d",
+                    o.init);
+    if (!block_ok(o.block)) return fail(GQ_EINVAL, "block=%d: the pass uses blocks of 64 coordinates", o.block);
+    if (d_in % o.block) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of block=%d",
+                                    (long long)d_in, o.block);
+    hipStream_t st = (hipStream_t)stream;
+    const bool wb = w_dt == GQ_BF16;
+    const int m = 1 << bits;
+    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m);
+    Scratch s;
+    if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
+    gq::LnqWs w = gq::lnq_carve(s.ptr, z);
+    hipError_t e;
+    if ((e = gq::lnq_prepare(F, groups, d_in, o.ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
+    if (o.init == GQ_INIT_UNIFORM &&
+        (e = gq::grid_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
+        return hip_fail(e, "init");
+    if (iters > 0 && (e = gq::lnq_zero_counter(w.cnt, 3, st)) != hipSuccess)
+        return hip_fail(e, "counter");
+    for (int t = 1; t <= iters; ++t) {
+        // assignment pass; objB = the objective before it, from the residual recomputed
+        // from (C, P) at its start (trace entry t - 1)
+        if ((e = gq::lnq_sweep_step(o.block, F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB,
+                                    w.objC, w.cnt, false, st)) != hipSuccess)
+            return hip_fail(e, "sweep");
+        if (obj_trace && (e = gq::lnq_reduce(w.objB, d_out, obj_trace + t - 1, st)) != hipSuccess)
+            return hip_fail(e, "trace");
+        // the pass's move count, counter cleared
+        if ((e = gq::lnq_iter_tail(w.objA, w.objB, d_out, nullptr, w.cnt,
+                                   n_changed ? n_changed + (t - 1) : nullptr, -1, st)) != hipSuccess)
+            return hip_fail(e, "iteration tail");
+    }
+    if (obj_trace) {
+        if ((e = gq::lnq_objective_rows(W, wb, d_out, d_in, groups, m, P, C, w, w.objA, st)) !=
+            hipSuccess)
+            return hip_fail(e, "final objective");
+        if ((e = gq::lnq_reduce(w.objA, d_out, obj_trace + iters, st)) != hipSuccess)
             return hip_fail(e, "trace");
     }
     return GQ_OK;

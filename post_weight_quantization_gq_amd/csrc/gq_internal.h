@@ -76,6 +76,9 @@ hipError_t lnq_prepare(const float* F, int groups, int64_t d, double rho, const 
                        hipStream_t st);
 hipError_t lnq_init_run(const void* W, bool w_bf16, int64_t d_out, int64_t d, int m, float* C,
                         uint8_t* P, hipStream_t st);
+// uniform min-max grid per row (float32) and nearest codes
+hipError_t grid_init_run(const void* W, bool w_bf16, int64_t d_out, int64_t d, int m, float* C,
+                         uint8_t* P, hipStream_t st);
 // `skip` (device, may be null): the launch does nothing when *skip != 0
 hipError_t lnq_residual(const uint16_t* Ehi, const uint16_t* Elo, int64_t d_out, int64_t d,
                         int groups, const uint16_t* Fhi, const uint16_t* Flo, float* R,

@@ -14,6 +14,7 @@
 //                  plus diag(F') in float32
 //   k_lnq_init     per row: m linear quantiles of w_j (float32 weights: from a sort in
 //                  LDS; bfloat16: order statistics by radix select), nearest codes
+//   k_grid_init    per row: the uniform min-max grid of the fixed-grid backend, nearest codes
 //   k_err_split    E = C[P] - W in float32, split into bfloat16 hi + lo planes
 //   k_mm (gq_lnq_mm.hip)  residual R = E F' and the codebook Gram blocks
 //                  P_j^T F' P_j on the matrix cores
@@ -150,6 +151,60 @@ __global__ __launch_bounds__(1024) void k_lnq_init(const void* __restrict__ W, i
     }
     __syncthreads();
     for (int64_t i = tid; i < d; i += 1024) {
+        const double w = (double)load_elem<BF16>(W, j * d + i);
+        double best = fabs(w - (double)cb[0]);
+        int bq = 0;
+        for (int q = 1; q < m; ++q) {
+            const double dist = fabs(w - (double)cb[q]);
+            if (dist < best) { best = dist; bq = q; }
+        }
+        P[j * d + i] = (uint8_t)bq;
+    }
+}
+
+// Fixed uniform grid of a row, the scalar backend the GuidedQuant objective is
+// plugged into when the codebook is not optimised: m equally spaced values from
+// lo = min_i w_i to hi = max_i w_i, c_q = lo + q (hi - lo)/(m - 1) formed in float64
+// (no fused multiply-add) and stored float32; codes: nearest entry, lowest index
+// on ties, compared in float64.  One block (256 threads) per row.
+__device__ __noinline__ double grid_point(double lo, double step, int q) {
+#pragma clang fp contract(off)
+    double prod = (double)q * step;
+    return lo + prod;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_grid_init(const void* __restrict__ W, int64_t d, int m,
+                                                  float* __restrict__ C,
+                                                  uint8_t* __restrict__ P) {
+    __shared__ float red[2][4];
+    __shared__ float cb[MAX_M];
+    const int64_t j = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float lo = __builtin_inff(), hi = -__builtin_inff();
+    for (int64_t i = tid; i < d; i += 256) {
+        const float v = load_elem<BF16>(W, j * d + i);
+        lo = fminf(lo, v);
+        hi = fmaxf(hi, v);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off, 64));
+        hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+    }
+    if (lane == 0) { red[0][wave] = lo; red[1][wave] = hi; }
+    __syncthreads();
+    if (tid < m) {
+        float l = red[0][0], h = red[1][0];
+#pragma unroll
+        for (int k = 1; k < 4; ++k) { l = fminf(l, red[0][k]); h = fmaxf(h, red[1][k]); }
+        const double step = ((double)h - (double)l) / (double)(m - 1);
+        const float cf = (float)grid_point((double)l, step, tid);
+        cb[tid] = cf;
+        C[j * m + tid] = cf;
+    }
+    __syncthreads();
+    for (int64_t i = tid; i < d; i += 256) {
         const double w = (double)load_elem<BF16>(W, j * d + i);
         double best = fabs(w - (double)cb[0]);
         int bq = 0;
@@ -1299,6 +1354,17 @@ hipError_t lnq_init_run(const void* W, bool w_bf16, int64_t d_out, int64_t d, in
         hipLaunchKernelGGL(k_lnq_init<false>, dim3((unsigned)d_out), dim3(1024), lds, st, W, d,
                            npow2, m, C, P);
     }
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
+}
+
+hipError_t grid_init_run(const void* W, bool w_bf16, int64_t d_out, int64_t d, int m, float* C,
+                         uint8_t* P, hipStream_t st) {
+    StageTimer tm(ST_LNQ_INIT, st);
+    if (w_bf16)
+        hipLaunchKernelGGL(k_grid_init<true>, dim3((unsigned)d_out), dim3(256), 0, st, W, d, m, C, P);
+    else
+        hipLaunchKernelGGL(k_grid_init<false>, dim3((unsigned)d_out), dim3(256), 0, st, W, d, m, C, P);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }

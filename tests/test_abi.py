@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(B.EXPORTS), declared ^ set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert gq.abi_version() == 2
+    assert gq.abi_version() == 3
 
 
 def test_options_default():
@@ -104,6 +104,35 @@ def test_lnq_argument_errors():
                                    0, None) == B.GQ_ESHAPE
     assert lib.lnq_objective(FAKE, 2, 256, FAKE, 1, 64, FAKE, FAKE, 3, 1e-6, None, None, FAKE, 0,
                              None) == B.GQ_EINVAL
+
+
+def test_grid_argument_errors():
+    lib = gq.library()
+    q = lambda **k: lib.grid_quantize(
+        k.get("W", FAKE), k.get("wdt", 1), k.get("d_out", 64), k.get("d_in", 256),
+        k.get("F", FAKE), k.get("groups", 2), k.get("bits", 3), k.get("iters", 2),
+        k.get("opt", None), k.get("C", FAKE), k.get("P", FAKE), None, None, k.get("ws", FAKE),
+        k.get("wsb", 0), None)
+    assert q(F=None) == B.GQ_EINVAL
+    assert q(wdt=5) == B.GQ_EDTYPE
+    assert q(d_out=63) == B.GQ_ESHAPE
+    assert q(d_in=0) == B.GQ_ESHAPE
+    assert q(bits=5) == B.GQ_EINVAL and "bits" in _err(lib)
+    assert q(iters=-1) == B.GQ_EINVAL
+    assert q(P=FAKE_ODD) == B.GQ_EINVAL
+    o = B.lnq_options()
+    lib.gq_lnq_options_default(ctypes.byref(o))
+    # the options' default init (QUANTILE) is not a grid
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "UNIFORM" in _err(lib)
+    o.init = B.GQ_INIT_UNIFORM
+    o.block = 96
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "block" in _err(lib)
+    o.block = 64
+    # NULL options: defaults with init UNIFORM; fails only on the workspace size
+    assert q(wsb=100) == B.GQ_EINVAL and "workspace" in _err(lib)
+    assert q(opt=ctypes.byref(o), wsb=100) == B.GQ_EINVAL and "workspace" in _err(lib)
+    o.init = B.GQ_INIT_GIVEN
+    assert q(opt=ctypes.byref(o), wsb=100) == B.GQ_EINVAL and "workspace" in _err(lib)
 
 
 def test_workspace_sizes_grow_with_shape():
