@@ -34,6 +34,10 @@ Readings where the pages are silent (the same readings the GPU library uses):
   * Empty code q (no coordinate assigned): c_q is kept unchanged.
   * Assignment: coordinates in ascending order; a coordinate moves only on a
     strict decrease of the objective, to the lowest-index minimiser.
+  * LUT dequantisation GEMV: y = W_hat x with W_hat[j][i] = c^(j)[p_ji]; the
+    packed index layout is this library's own (the pages fix none).  For
+    bfloat16 activations the lookup table holds the codebook rounded to
+    bfloat16 (the inference kernel the pages refer to keeps a 16-bit table).
   * Fixed-grid backend (the blog page's remark that the objective plugs into
     any layer-wise quantizer): a uniform min-max grid per row, kept fixed, and
     the assignment pass only.  The grid is the plain definition of an equally
@@ -47,7 +51,8 @@ __all__ = [
     "group_scale", "fisher", "fisher_entry", "fisher_per_channel", "ridge_lambda",
     "damped", "init_quantile", "one_hot", "codebook_system", "codebook_update",
     "assign_deltas", "assign_sweep", "objective", "lnq_row", "guided_loss",
-    "replay_sweep", "init_uniform_grid", "grid_row",
+    "replay_sweep", "init_uniform_grid", "grid_row", "lut_codes_per_word", "lut_row_words",
+    "lut_pack", "lut_unpack", "bf16_round", "lut_gemv",
 ]
 
 
@@ -320,3 +325,74 @@ def grid_row(Fp: np.ndarray, w: np.ndarray, m: int, iters: int, c0=None, p0=None
         p = assign_sweep(Fp, w, c, p)
         trace.append(objective(Fp, w, c, p))
     return c, p, np.array(trace)
+
+
+# ----------------------------------------------------------------------------
+# LUT dequantisation GEMV for the (C, P) format [LNQ-prob]
+# ----------------------------------------------------------------------------
+# The blog page notes that LNQ's output runs on the same lookup-table kernel as
+# SqueezeLLM: each row keeps its codebook c^(j) and b-bit indices P^(j), and a
+# product with activations reads w_hat_ji = c^(j)[p_ji].  The packed layout is
+# this library's own (the pages fix none):
+#   * codes are taken in pairs (i, i + 1); a pair forms the 2b-bit index
+#     code_i | code_{i+1} << b;
+#   * a 32-bit word holds floor(16 / b) pairs, the first pair in the low bits;
+#     codes per word cpw = 2 floor(16 / b): 32, 16, 10, 8 for b = 1, 2, 3, 4;
+#   * a row is ceil(d_in / cpw) words, padded with zero words to a multiple of
+#     4 words; code slots past d_in hold 0.
+
+def lut_codes_per_word(bits: int) -> int:
+    return 2 * (16 // bits)
+
+
+def lut_row_words(d_in: int, bits: int) -> int:
+    cpw = lut_codes_per_word(bits)
+    return -(-(-(-d_in // cpw)) // 4) * 4
+
+
+def lut_pack(P: np.ndarray, bits: int) -> np.ndarray:
+    """Packed codes [d_out][row words] (uint32) of P [d_out][d_in], per the layout above."""
+    P = np.asarray(P, np.int64)
+    d_out, d_in = P.shape
+    cpw = lut_codes_per_word(bits)
+    rw = lut_row_words(d_in, bits)
+    Q = np.zeros((d_out, rw), dtype=np.uint64)
+    for i in range(d_in):
+        word, slot = divmod(i, cpw)
+        shift = bits * slot            # pair slot // 2 at 2b (slot // 2), half at b (slot % 2)
+        Q[:, word] |= (P[:, i] & ((1 << bits) - 1)).astype(np.uint64) << np.uint64(shift)
+    return Q.astype(np.uint32)
+
+
+def lut_unpack(Q: np.ndarray, d_in: int, bits: int) -> np.ndarray:
+    """Codes [d_out][d_in] back from the packed words."""
+    Q = np.asarray(Q, np.uint64)
+    cpw = lut_codes_per_word(bits)
+    i = np.arange(d_in)
+    words = Q[:, i // cpw]
+    return ((words >> (np.uint64(bits) * (i % cpw).astype(np.uint64))) &
+            np.uint64((1 << bits) - 1)).astype(np.int64)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bfloat16 (ties to even), returned as float64.
+
+    The high 16 bits of the float32 pattern after adding 0x7FFF plus the lowest
+    kept bit; finite inputs only.
+    """
+    b = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    r = (b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return (r.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def lut_gemv(C: np.ndarray, P: np.ndarray, x: np.ndarray, lut_bf16: bool) -> np.ndarray:
+    """y[b][j] = sum_i v(C[j][P[j][i]]) x[b][i] in float64.
+
+    v rounds the codebook entry to bfloat16 when the lookup table is held in
+    bfloat16 (the path taken for bfloat16 activations), else keeps float32.
+    """
+    C = np.asarray(C, np.float32)
+    Cv = bf16_round(C) if lut_bf16 else C.astype(np.float64)
+    W_hat = np.take_along_axis(Cv, np.asarray(P, np.int64), axis=1)
+    x = np.atleast_2d(np.asarray(x, np.float64))
+    return x @ W_hat.T

@@ -528,3 +528,76 @@ def test_grid_row_monotone_local_min_and_bruteforce_bound():
                 assert O.objective(F, w, c, t) >= base - 1e-12
         best = min(O.objective(F, w, c, np.array(t)) for t in itertools.product(range(m), repeat=d))
         assert best <= base + 1e-15
+
+
+# --------------------------------------------------------------------------
+# LUT dequantisation GEMV: packing layout and the product
+# --------------------------------------------------------------------------
+
+def test_lut_pack_hand_examples():
+    """bits 3: ten codes per word at shifts 0, 3, ..., 27:
+    1 + 2*2^3 + 3*2^6 + 4*2^9 + 5*2^12 + 6*2^15 + 7*2^18 + 0*2^21 + 5*2^24 + 2*2^27
+    = 0x151F58D1; the 11th code opens word 1; rows padded to 4 words.
+    bits 4: eight codes per word, 0xA + 0x5*2^4 + 0xF*2^8 + 0x1*2^12 = 0x1F5A."""
+    Q = O.lut_pack(np.array([[1, 2, 3, 4, 5, 6, 7, 0, 5, 2, 3]]), 3)
+    np.testing.assert_array_equal(Q, [[0x151F58D1, 3, 0, 0]])
+    Q = O.lut_pack(np.array([[0xA, 0x5, 0xF, 0x1, 0, 0, 0, 0, 0x3]]), 4)
+    np.testing.assert_array_equal(Q, [[0x1F5A, 3, 0, 0]])
+    assert [O.lut_codes_per_word(b) for b in (1, 2, 3, 4)] == [32, 16, 10, 8]
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_lut_pack_roundtrip(bits):
+    rng = _rng(90 + bits)
+    for d_in in (1, 9, 64, 333, 4096):
+        P = rng.integers(0, 1 << bits, size=(5, d_in))
+        Q = O.lut_pack(P, bits)
+        rw = O.lut_row_words(d_in, bits)
+        assert Q.shape == (5, rw) and rw % 4 == 0
+        assert rw * 32 >= d_in * bits and (rw - 4) * O.lut_codes_per_word(bits) < d_in
+        np.testing.assert_array_equal(O.lut_unpack(Q, d_in, bits), P)
+        # every slot past d_in is zero
+        cpw = O.lut_codes_per_word(bits)
+        full = O.lut_unpack(Q, rw * cpw, bits)
+        assert np.all(full[:, d_in:] == 0)
+
+
+def test_oracle_bf16_round_matches_torch():
+    import torch
+    rng = _rng(91)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    x[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0]   # exact ties
+    ref = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(O.bf16_round(x), ref)
+
+
+@pytest.mark.parametrize("lut_bf16", [False, True])
+def test_lut_gemv_one_hot_codebook_gives_masked_sums(lut_bf16):
+    """c^(j) = e_q: y_j is the sum of the activations whose code is q."""
+    rng = _rng(92)
+    d_out, d_in, m = 6, 50, 8
+    P = rng.integers(0, m, size=(d_out, d_in))
+    x = rng.standard_normal((3, d_in))
+    for q in range(m):
+        C = np.zeros((d_out, m), np.float32)
+        C[:, q] = 1.0
+        y = O.lut_gemv(C, P, x, lut_bf16)
+        for b in range(3):
+            for j in range(d_out):
+                assert y[b, j] == pytest.approx(np.sum(x[b][P[j] == q]), rel=1e-15, abs=1e-15)
+
+
+def test_lut_gemv_bruteforce_loops():
+    """Small integer case against plain loops (exact in float64)."""
+    rng = _rng(93)
+    d_out, d_in, m = 3, 7, 4
+    P = rng.integers(0, m, size=(d_out, d_in))
+    C = rng.integers(-8, 9, size=(d_out, m)).astype(np.float32)
+    x = rng.integers(-5, 6, size=(2, d_in)).astype(np.float64)
+    y = O.lut_gemv(C, P, x, True)
+    for b in range(2):
+        for j in range(d_out):
+            s = 0.0
+            for i in range(d_in):
+                s += float(C[j, P[j, i]]) * x[b, i]
+            assert y[b, j] == s
