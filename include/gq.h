@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 3
+#define GQ_ABI_VERSION 4
 
 typedef enum {
     GQ_OK = 0,
@@ -228,6 +228,40 @@ gq_status grid_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_i
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Lookup-table dequantisation product for the (C, P) format.  Section "LNQ" of
+ * the blog page keeps per row j a codebook c^(j) and b-bit indices P^(j), and
+ * notes that the result runs on the same lookup-table kernel as SqueezeLLM; the
+ * product is y[b][j] = sum_i c^(j)[P[j][i]] x[b][i].
+ *
+ * Packed layout (this library's own; the pages fix none): codes are taken in
+ * pairs (i, i + 1), a pair being the 2b-bit index code_i | code_{i+1} << b; a
+ * 32-bit word holds 16 / b pairs (integer division), the first pair in the low
+ * bits, i.e. 32, 16, 10 or 8 codes per word for b = 1, 2, 3, 4; each row is
+ * lut_packed_row_words(d_in, bits) words (a multiple of 4), code slots past
+ * d_in are 0.  lut_packed_row_words returns 0 for d_in < 1 or bits outside 1..4.
+ */
+int64_t lut_packed_row_words(int64_t d_in, int32_t bits);
+
+/*
+ * P [d_out][d_in] uint8 codes (each taken modulo 2^bits) -> Q [d_out][row words]
+ * uint32 in the layout above.  Q 16-byte aligned.  1 <= bits <= 4.
+ */
+gq_status lut_pack_codes(const uint8_t* P, int64_t d_out, int64_t d_in, int32_t bits,
+                         uint32_t* Q, void* stream);
+
+/*
+ * y [batch][d_out] float32 = the product above for x [batch][d_in] (x_dt),
+ * 1 <= batch <= 8, Q from lut_pack_codes, C [d_out][2^bits] float32.
+ * bfloat16 x: the codebook enters as bfloat16 (rounded to nearest even, as a
+ * 16-bit lookup table holds it), each product of two bfloat16 values is exact
+ * and the sums are float32; the staged activations must fit the LDS
+ * (batch * row words * ((16 / bits) | 1) * 4 + 8 * 4^bits * 4 <= 160 KiB, else
+ * GQ_ENOTIMPL).  float32 x: float32 codebook and float32 fused multiply-adds.
+ */
+gq_status lut_gemv(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in, int32_t bits,
+                   const void* x, gq_dtype x_dt, int32_t batch, float* y, void* stream);
+
+/*
  * Diagnostics: per-stage kernel timing with HIP events.
  * gq_timing_enable(mask) makes every later call bracket each launch sequence of
  * the stages whose bit (1 << gq_stage) is set in `mask` with two events recorded
@@ -253,6 +287,8 @@ typedef enum {
     GQ_STAGE_LNQ_SMALL,         /* sums and counters */
     GQ_STAGE_FISHER_PACK,       /* feature-major bf16 operands of the Fisher contraction */
     GQ_STAGE_LNQ_DELTA,         /* Gram and residual updates from the changed coordinates */
+    GQ_STAGE_LUT_PACK,          /* code packing for the lookup-table product */
+    GQ_STAGE_LUT_GEMV,          /* the lookup-table product */
     GQ_STAGE_COUNT
 } gq_stage;
 

@@ -18,15 +18,16 @@ GQ_OK, GQ_EINVAL, GQ_ESHAPE, GQ_EDTYPE, GQ_ENOMEM, GQ_EHIP, GQ_ENOTIMPL = 0, 1, 
 GQ_F32, GQ_BF16 = 0, 1
 GQ_INIT_QUANTILE, GQ_INIT_GIVEN, GQ_INIT_UNIFORM = 0, 1, 2
 GQ_GRAM_AUTO, GQ_GRAM_DENSE = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 # every symbol include/gq.h declares
 EXPORTS = (
     "gq_abi_version", "gq_last_error", "gq_lnq_options_default", "gq_fisher_workspace_size",
     "gq_fisher_accumulate", "gq_lnq_workspace_size", "lnq_codebook_update", "lnq_assign_sweep",
-    "lnq_objective", "lnq_quantize", "grid_quantize", "gq_timing_enable", "gq_timing_read", "gq_stage_name",
+    "lnq_objective", "lnq_quantize", "grid_quantize", "lut_packed_row_words", "lut_pack_codes",
+    "lut_gemv", "gq_timing_enable", "gq_timing_read", "gq_stage_name",
 )
-STAGE_COUNT = 13
+STAGE_COUNT = 15
 
 
 class GQError(RuntimeError):
@@ -64,6 +65,9 @@ _SIGS = {
     "grid_quantize": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _i32,
                                      ctypes.POINTER(lnq_options), _vp, _vp, _vp, _vp, _vp, _sz,
                                      _vp]),
+    "lut_packed_row_words": (_i64, [_i64, _i32]),
+    "lut_pack_codes": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
+    "lut_gemv": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _vp, _i32, _i32, _vp, _vp]),
     "gq_timing_enable": (None, [ctypes.c_int]),
     "gq_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "gq_stage_name": (ctypes.c_char_p, [ctypes.c_int]),
@@ -298,9 +302,45 @@ def grid_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float
     return C, P, tr, nch[:iters]
 
 
+def lut_packed_row_words(d_in: int, bits: int) -> int:
+    return int(library().lut_packed_row_words(d_in, bits))
+
+
+def lut_pack_codes(P, bits: int, Q=None, stream=None) -> torch.Tensor:
+    """P [d_out][d_in] uint8 -> packed codes Q [d_out][row words] (int32 storage of the
+    uint32 words)."""
+    lib = library()
+    _dev(P, "P", torch.uint8)
+    d_out, d_in = P.shape
+    rw = lut_packed_row_words(d_in, bits)
+    if Q is None:
+        Q = torch.empty((d_out, max(rw, 1)), dtype=torch.int32, device=P.device)
+    _dev(Q, "Q", torch.int32)
+    _check(lib.lut_pack_codes(_ptr(P), d_out, d_in, bits, _ptr(Q), _stream(stream)))
+    return Q
+
+
+def lut_gemv(Q, C, x, bits: int, d_in: int | None = None, y=None, stream=None) -> torch.Tensor:
+    """y [batch][d_out] = sum_i C[j][code_ji] x[b][i]; x [batch][d_in] or [d_in]."""
+    lib = library()
+    _dev(Q, "Q", torch.int32)
+    _dev(C, "C", torch.float32)
+    _dev(x, "x")
+    xx = x if x.dim() == 2 else x.unsqueeze(0)
+    batch, dx = xx.shape
+    d_in = dx if d_in is None else d_in
+    d_out = C.shape[0]
+    if y is None:
+        y = torch.empty((batch, d_out), dtype=torch.float32, device=x.device)
+    _dev(y, "y", torch.float32)
+    _check(lib.lut_gemv(_ptr(Q), _ptr(C), d_out, d_in, bits, _ptr(xx), _dt(xx), batch, _ptr(y),
+                        _stream(stream)))
+    return y if x.dim() == 2 else y[0]
+
+
 STAGES = ("group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain", "lnq_prepare",
           "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep", "lnq_small",
-          "fisher_pack", "lnq_delta")
+          "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv")
 
 
 def gq_timing_enable(on=True) -> None:

@@ -172,7 +172,7 @@ const char* gq_stage_name(int stage) {
     static const char* names[GQ_STAGE_COUNT] = {
         "group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain", "lnq_prepare",
         "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep", "lnq_small",
-        "fisher_pack", "lnq_delta"};
+        "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv"};
     if (stage < 0 || stage >= GQ_STAGE_COUNT) return "";
     return names[stage];
 }
@@ -427,6 +427,41 @@ gq_status grid_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_i
         if ((e = gq::lnq_reduce(w.objA, d_out, obj_trace + iters, st)) != hipSuccess)
             return hip_fail(e, "trace");
     }
+    return GQ_OK;
+}
+
+int64_t lut_packed_row_words(int64_t d_in, int32_t bits) {
+    if (d_in < 1 || bits < 1 || bits > 4) return 0;
+    return gq::lut_row_words(d_in, bits);
+}
+
+gq_status lut_pack_codes(const uint8_t* P, int64_t d_out, int64_t d_in, int32_t bits, uint32_t* Q,
+                         void* stream) {
+    if (!P || !Q) return fail(GQ_EINVAL, "null P or Q");
+    if (d_out < 1 || d_in < 1) return fail(GQ_ESHAPE, "empty shape");
+    if (bits < 1 || bits > 4) return fail(GQ_EINVAL, "bits=%d: the packed layout takes 1..4", bits);
+    if ((uintptr_t)Q & 15u) return fail(GQ_EINVAL, "Q must be 16-byte aligned");
+    hipError_t e = gq::lut_pack_run(P, d_out, d_in, bits, Q, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "lut_pack_codes");
+    return GQ_OK;
+}
+
+gq_status lut_gemv(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in, int32_t bits,
+                   const void* x, gq_dtype x_dt, int32_t batch, float* y, void* stream) {
+    if (!Q || !C || !x || !y) return fail(GQ_EINVAL, "null Q, C, x or y");
+    if (!dtype_ok(x_dt)) return fail(GQ_EDTYPE, "unsupported dtype");
+    if (d_out < 1 || d_in < 1) return fail(GQ_ESHAPE, "empty shape");
+    if (bits < 1 || bits > 4) return fail(GQ_EINVAL, "bits=%d: the packed layout takes 1..4", bits);
+    if (batch < 1 || batch > 8) return fail(GQ_EINVAL, "batch=%d: 1..8 activation vectors", batch);
+    if (((uintptr_t)Q & 15u) || ((uintptr_t)C & 3u) || ((uintptr_t)y & 3u) ||
+        ((uintptr_t)x & (x_dt == GQ_BF16 ? 1u : 3u)))
+        return fail(GQ_EINVAL, "Q must be 16-byte aligned, C, y and x element-aligned");
+    const bool xb = x_dt == GQ_BF16;
+    if (xb && gq::lut_gemv_lds_bytes(d_in, bits, batch) > 160 * 1024)
+        return fail(GQ_ENOTIMPL, "d_in=%lld with batch=%d: the staged activations exceed the LDS",
+                    (long long)d_in, batch);
+    hipError_t e = gq::lut_gemv_run(Q, C, d_out, d_in, bits, x, xb, batch, y, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "lut_gemv");
     return GQ_OK;
 }
 

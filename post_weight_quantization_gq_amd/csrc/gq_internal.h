@@ -10,7 +10,7 @@ namespace gq {
 enum Stage {
     ST_GROUP_SCALE = 0, ST_FISHER_MFMA, ST_FISHER_FINALIZE, ST_FISHER_PLAIN, ST_LNQ_PREPARE,
     ST_LNQ_RESID, ST_LNQ_INIT, ST_LNQ_GRAM, ST_LNQ_SOLVE, ST_LNQ_SWEEP, ST_LNQ_SMALL, ST_FISHER_PACK,
-    ST_LNQ_DELTA, ST_COUNT
+    ST_LNQ_DELTA, ST_LUT_PACK, ST_LUT_GEMV, ST_COUNT
 };
 bool timing_on(Stage s);
 void timing_mark(Stage s, hipStream_t st, bool begin);
@@ -111,5 +111,13 @@ hipError_t lnq_iter_tail(const double* objA, const double* objB, int64_t n, doub
                          unsigned long long* cnt, int64_t* n_changed, int64_t incr_max,
                          hipStream_t st);
 hipError_t lnq_store_counter(const unsigned long long* c, int64_t* dst, hipStream_t st);
+
+// LUT dequantisation GEMV (gq_lut.hip)
+int64_t lut_row_words(int64_t d_in, int bits);          // 32-bit words per packed row
+size_t lut_gemv_lds_bytes(int64_t d_in, int bits, int batch);
+hipError_t lut_pack_run(const uint8_t* P, int64_t d_out, int64_t d_in, int bits, uint32_t* Q,
+                        hipStream_t st);
+hipError_t lut_gemv_run(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in, int bits,
+                        const void* x, bool x_bf16, int batch, float* y, hipStream_t st);
 
 }  // namespace gq

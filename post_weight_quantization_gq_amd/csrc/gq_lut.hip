@@ -1,0 +1,252 @@
+// Lookup-table dequantisation GEMV for LNQ's output on gfx950.
+//
+// GuidedQuant blog page (jinukkim.me/blog/guidedquant), section "LNQ": each row j
+// of the quantized layer is a codebook c^(j) (m = 2^b entries) and b-bit indices
+// P^(j); the page notes that the result runs on the same lookup-table kernel as
+// SqueezeLLM.  This file holds that consumer:
+//
+//   k_lut_pack       P [d_out][d_in] (one byte per code) -> packed words.  Codes are
+//                    taken in pairs (i, i + 1); a pair is the 2b-bit index
+//                    code_i | code_{i+1} << b, and a 32-bit word holds 16 / b pairs
+//                    (integer division), low bits first: 32, 16, 10 or 8 codes per
+//                    word for b = 1..4.  A row is padded with zero words to a
+//                    multiple of 4 words.
+//   k_lut_gemv_bf16  y[b][j] = sum_i c^(j)[p_ji] x[b][i] for bfloat16 activations:
+//                    per row a table of the m^2 codebook pairs as packed bfloat16
+//                    (the codebook rounded to nearest even), one table read per
+//                    code pair, and v_dot2c_f32_bf16 (both products exact, float32
+//                    accumulation).  x is staged once per block in LDS as bfloat16
+//                    pairs, word w's pairs at w * XST + p with XST = (16 / b) | 1
+//                    (odd), so lanes reading consecutive words hit distinct banks.
+//   k_lut_gemv_f32   the same product for float32 activations with the float32
+//                    codebook and float32 FMAs (a reference-precision path).
+//
+// Bound: HBM (the packed codes, b/8 bytes per weight); x, the codebook and y are
+// small next to them.
+#include "gq_common.h"
+#include "gq_internal.h"
+
+namespace gq {
+
+constexpr int LUT_WAVES = 8;          // waves per block of the GEMV
+constexpr int LUT_UNROLL = 8;         // code words in flight per lane
+
+__host__ __device__ constexpr int lut_ppw(int bits) { return 16 / bits; }      // pairs per word
+__host__ __device__ constexpr int lut_xst(int bits) { return (16 / bits) | 1; }
+
+int64_t lut_row_words(int64_t d_in, int bits) {
+    const int64_t cpw = 2 * lut_ppw(bits);
+    return ((d_in + cpw - 1) / cpw + 3) / 4 * 4;
+}
+
+// one thread per packed word
+__global__ __launch_bounds__(256) void k_lut_pack(const uint8_t* __restrict__ P, int64_t d_out,
+                                                 int64_t d_in, int bits, int64_t rw,
+                                                 uint32_t* __restrict__ Q) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= d_out * rw) return;
+    const int64_t j = t / rw, w = t - j * rw;
+    const int cpw = 2 * (16 / bits);
+    const uint32_t mask = (1u << bits) - 1u;
+    const int64_t i0 = w * cpw;
+    uint32_t word = 0u;
+    for (int s = 0; s < cpw; ++s) {
+        const int64_t i = i0 + s;
+        if (i < d_in) word |= ((uint32_t)P[j * d_in + i] & mask) << (bits * s);
+    }
+    Q[t] = word;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// LDS: x pairs [B][rw * XST] then one pair table [M * M] per wave.  Rows: block r
+// takes rows r * rows_per_block .. + rows_per_block - 1, wave w every LUT_WAVES-th.
+template <int BITS, int B>
+__global__ __launch_bounds__(64 * LUT_WAVES) void k_lut_gemv_bf16(
+    const uint32_t* __restrict__ Q, int64_t rw, const float* __restrict__ C, int64_t d_out,
+    int64_t d_in, const uint16_t* __restrict__ x, int rows_per_block, float* __restrict__ y) {
+    constexpr int M = 1 << BITS;
+    constexpr int PPW = lut_ppw(BITS);
+    constexpr int XST = lut_xst(BITS);
+    constexpr uint32_t PMASK = (uint32_t)(M * M - 1);
+    extern __shared__ uint32_t lut_lds[];
+    const int64_t xwords = rw * XST;
+    uint32_t* table = lut_lds + B * xwords;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // stage x: pair pr = w * PPW + p holds elements 2 pr, 2 pr + 1 (zero past d_in)
+    const int64_t npairs = rw * PPW;
+    for (int64_t e = tid; e < B * npairs; e += 64 * LUT_WAVES) {
+        const int b = (int)(e / npairs);
+        const int64_t pr = e - (int64_t)b * npairs;
+        const int64_t i = 2 * pr;
+        const uint32_t lo = i < d_in ? x[(int64_t)b * d_in + i] : 0u;
+        const uint32_t hi = i + 1 < d_in ? x[(int64_t)b * d_in + i + 1] : 0u;
+        const int64_t w = pr / PPW;
+        lut_lds[(int64_t)b * xwords + w * XST + (pr - w * PPW)] = lo | (hi << 16);
+    }
+    __syncthreads();
+
+    uint32_t* tab = table + wave * (M * M);
+    const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+    for (int rr = wave; rr < rows_per_block; rr += LUT_WAVES) {
+        const int64_t j = r0 + rr;
+        if (j >= d_out) break;
+        // the row's pair table: entry q0 | q1 << BITS = (bf16 c_q0, bf16 c_q1)
+        for (int e = lane; e < M * M; e += 64)
+            tab[e] = pack_bf16x2(C[j * M + (e & (M - 1))], C[j * M + (e >> BITS)]);
+        float acc[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = 0.f;
+        const uint32_t* Qj = Q + j * rw;
+        for (int64_t w0 = lane; w0 < rw; w0 += 64 * LUT_UNROLL) {
+            uint32_t wv[LUT_UNROLL];
+#pragma unroll
+            for (int u = 0; u < LUT_UNROLL; ++u) {
+                const int64_t wi = w0 + 64 * u;
+                wv[u] = wi < rw ? Qj[wi] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < LUT_UNROLL; ++u) {
+                const int64_t wi = w0 + 64 * u;
+                if (wi < rw) {
+                    const uint32_t* xw = lut_lds + wi * XST;
+#pragma unroll
+                    for (int p = 0; p < PPW; ++p) {
+                        const uint32_t lv = tab[(wv[u] >> (2 * BITS * p)) & PMASK];
+#pragma unroll
+                        for (int b = 0; b < B; ++b) acc[b] = dot2_bf16(lv, xw[b * xwords + p], acc[b]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float s = wave_sum_f32(acc[b]);
+            if (lane == 0) y[(int64_t)b * d_out + j] = s;
+        }
+    }
+}
+
+// float32 activations: float32 codebook, float32 FMAs, x read from global memory.
+template <int BITS>
+__global__ __launch_bounds__(256) void k_lut_gemv_f32(const uint32_t* __restrict__ Q, int64_t rw,
+                                                     const float* __restrict__ C, int64_t d_out,
+                                                     int64_t d_in, const float* __restrict__ x,
+                                                     int batch, float* __restrict__ y) {
+    constexpr int M = 1 << BITS;
+    constexpr int CPW = 2 * lut_ppw(BITS);
+    const int lane = threadIdx.x & 63;
+    const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (j >= d_out) return;
+    const float cl = lane < M ? C[j * M + lane] : 0.f;
+    const uint32_t* Qj = Q + j * rw;
+    for (int b = 0; b < batch; ++b) {
+        const float* xb = x + (int64_t)b * d_in;
+        float acc = 0.f;
+        // uniform trip count: every lane takes part in the table shuffles
+        for (int64_t w0 = 0; w0 < rw; w0 += 64) {
+            const int64_t w = w0 + lane;
+            const uint32_t word = w < rw ? Qj[w] : 0u;
+#pragma unroll
+            for (int s = 0; s < CPW; ++s) {
+                const int code = (int)((word >> (BITS * s)) & (uint32_t)(M - 1));
+                const float v = __shfl(cl, code, 64);
+                const int64_t i = w * CPW + s;
+                if (w < rw && i < d_in) acc = fmaf(v, xb[i], acc);
+            }
+        }
+        const float s = wave_sum_f32(acc);
+        if (lane == 0) y[(int64_t)b * d_out + j] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+hipError_t lut_pack_run(const uint8_t* P, int64_t d_out, int64_t d_in, int bits, uint32_t* Q,
+                        hipStream_t st) {
+    const int64_t rw = lut_row_words(d_in, bits);
+    const int64_t n = d_out * rw;
+    StageTimer tm(ST_LUT_PACK, st);
+    hipLaunchKernelGGL(k_lut_pack, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P, d_out,
+                       d_in, bits, rw, Q);
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
+}
+
+size_t lut_gemv_lds_bytes(int64_t d_in, int bits, int batch) {
+    const int64_t rw = lut_row_words(d_in, bits);
+    const int m = 1 << bits;
+    return (size_t)(batch * rw * lut_xst(bits) + LUT_WAVES * m * m) * 4;
+}
+
+template <int BITS, int B>
+static hipError_t launch_bf16(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in,
+                              const uint16_t* x, float* y, hipStream_t st) {
+    const int64_t rw = lut_row_words(d_in, BITS);
+    const size_t lds = lut_gemv_lds_bytes(d_in, BITS, B);
+    static size_t attr = 0;          // dynamic LDS the kernel is enabled for
+    if (lds > attr) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_lut_gemv_bf16<BITS, B>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr = lds;
+    }
+    // about two blocks per compute unit, at least one row per wave
+    int64_t rpb = (d_out + 511) / 512;
+    if (rpb < LUT_WAVES) rpb = LUT_WAVES;
+    const int64_t grid = (d_out + rpb - 1) / rpb;
+    hipLaunchKernelGGL((k_lut_gemv_bf16<BITS, B>), dim3((unsigned)grid), dim3(64 * LUT_WAVES), lds,
+                       st, Q, rw, C, d_out, d_in, x, (int)rpb, y);
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
+}
+
+template <int BITS>
+static hipError_t launch_bf16_b(int batch, const uint32_t* Q, const float* C, int64_t d_out,
+                                int64_t d_in, const uint16_t* x, float* y, hipStream_t st) {
+    switch (batch) {
+        case 1: return launch_bf16<BITS, 1>(Q, C, d_out, d_in, x, y, st);
+        case 2: return launch_bf16<BITS, 2>(Q, C, d_out, d_in, x, y, st);
+        case 3: return launch_bf16<BITS, 3>(Q, C, d_out, d_in, x, y, st);
+        case 4: return launch_bf16<BITS, 4>(Q, C, d_out, d_in, x, y, st);
+        case 5: return launch_bf16<BITS, 5>(Q, C, d_out, d_in, x, y, st);
+        case 6: return launch_bf16<BITS, 6>(Q, C, d_out, d_in, x, y, st);
+        case 7: return launch_bf16<BITS, 7>(Q, C, d_out, d_in, x, y, st);
+        default: return launch_bf16<BITS, 8>(Q, C, d_out, d_in, x, y, st);
+    }
+}
+
+hipError_t lut_gemv_run(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in, int bits,
+                        const void* x, bool x_bf16, int batch, float* y, hipStream_t st) {
+    StageTimer tm(ST_LUT_GEMV, st);
+    if (x_bf16) {
+        const uint16_t* xb = (const uint16_t*)x;
+        switch (bits) {
+            case 1: return launch_bf16_b<1>(batch, Q, C, d_out, d_in, xb, y, st);
+            case 2: return launch_bf16_b<2>(batch, Q, C, d_out, d_in, xb, y, st);
+            case 3: return launch_bf16_b<3>(batch, Q, C, d_out, d_in, xb, y, st);
+            default: return launch_bf16_b<4>(batch, Q, C, d_out, d_in, xb, y, st);
+        }
+    }
+    const int64_t rw = lut_row_words(d_in, bits);
+    const dim3 grid((unsigned)((d_out + 3) / 4));
+    const float* xf = (const float*)x;
+    switch (bits) {
+        case 1: hipLaunchKernelGGL(k_lut_gemv_f32<1>, grid, dim3(256), 0, st, Q, rw, C, d_out, d_in, xf, batch, y); break;
+        case 2: hipLaunchKernelGGL(k_lut_gemv_f32<2>, grid, dim3(256), 0, st, Q, rw, C, d_out, d_in, xf, batch, y); break;
+        case 3: hipLaunchKernelGGL(k_lut_gemv_f32<3>, grid, dim3(256), 0, st, Q, rw, C, d_out, d_in, xf, batch, y); break;
+        default: hipLaunchKernelGGL(k_lut_gemv_f32<4>, grid, dim3(256), 0, st, Q, rw, C, d_out, d_in, xf, batch, y); break;
+    }
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
+}
+
+}  // namespace gq

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(B.EXPORTS), declared ^ set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert gq.abi_version() == 3
+    assert gq.abi_version() == 4
 
 
 def test_options_default():
@@ -135,6 +135,30 @@ def test_grid_argument_errors():
     assert q(opt=ctypes.byref(o), wsb=100) == B.GQ_EINVAL and "workspace" in _err(lib)
 
 
+def test_lut_argument_errors():
+    lib = gq.library()
+    assert gq.lut_packed_row_words(4096, 3) == 412        # 410 words of 10 codes, to 4k
+    assert gq.lut_packed_row_words(28672, 4) == 3584
+    assert gq.lut_packed_row_words(0, 3) == 0 and gq.lut_packed_row_words(64, 5) == 0
+    pk = lambda **k: lib.lut_pack_codes(k.get("P", FAKE), k.get("d_out", 8), k.get("d_in", 64),
+                                        k.get("bits", 3), k.get("Q", FAKE), None)
+    assert pk(P=None) == B.GQ_EINVAL
+    assert pk(d_in=0) == B.GQ_ESHAPE
+    assert pk(bits=5) == B.GQ_EINVAL and "bits" in _err(lib)
+    assert pk(Q=FAKE_ODD) == B.GQ_EINVAL
+    mv = lambda **k: lib.lut_gemv(k.get("Q", FAKE), k.get("C", FAKE), k.get("d_out", 8),
+                                  k.get("d_in", 64), k.get("bits", 3), k.get("x", FAKE),
+                                  k.get("xdt", 1), k.get("batch", 1), k.get("y", FAKE), None)
+    assert mv(y=None) == B.GQ_EINVAL
+    assert mv(xdt=7) == B.GQ_EDTYPE
+    assert mv(d_out=0) == B.GQ_ESHAPE
+    assert mv(bits=0) == B.GQ_EINVAL
+    assert mv(batch=9) == B.GQ_EINVAL and "batch" in _err(lib)
+    assert mv(Q=FAKE_ODD) == B.GQ_EINVAL
+    assert mv(d_in=1 << 20) == B.GQ_ENOTIMPL and "LDS" in _err(lib)
+    assert mv(d_in=1 << 20, xdt=0, y=None) == B.GQ_EINVAL
+
+
 def test_workspace_sizes_grow_with_shape():
     small = gq.lnq_workspace_size(64, 256, 2, 3)
     big = gq.lnq_workspace_size(4096, 4096, 4, 3)
@@ -149,5 +173,5 @@ def test_timing_read_empty():
     t = gq.gq_timing_read()
     assert set(t) == {"group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain",
                       "lnq_prepare", "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep",
-                      "lnq_small", "fisher_pack", "lnq_delta"}
+                      "lnq_small", "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv"}
     assert all(v == (0.0, 0) for v in t.values())
