@@ -255,7 +255,8 @@ gq_status lut_pack_codes(const uint8_t* P, int64_t d_out, int64_t d_in, int32_t 
  * bfloat16 x: the codebook enters as bfloat16 (rounded to nearest even, as a
  * 16-bit lookup table holds it), each product of two bfloat16 values is exact
  * and the sums are float32; the staged activations must fit the LDS
- * (batch * row words * ((16 / bits) | 1) * 4 + 8 * 4^bits * 4 <= 160 KiB, else
+ * (batch * (row words + 1) * X * 4 + 8 * 4^bits * 4 <= 160 KiB with X = 16 / bits for
+ * bits 1, 2, 4 and X = 5 for bits 3, else
  * GQ_ENOTIMPL).  float32 x: float32 codebook and float32 fused multiply-adds.
  */
 gq_status lut_gemv(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in, int32_t bits,

@@ -30,9 +30,15 @@ namespace gq {
 
 constexpr int LUT_WAVES = 8;          // waves per block of the GEMV
 constexpr int LUT_UNROLL = 8;         // code words in flight per lane
+constexpr int LUT_SPAN = 64 * LUT_UNROLL;   // words per chunk of a row
 
 __host__ __device__ constexpr int lut_ppw(int bits) { return 16 / bits; }      // pairs per word
-__host__ __device__ constexpr int lut_xst(int bits) { return (16 / bits) | 1; }
+// LDS words per staged word of x: its 16 / b pairs, as 16-byte vectors when that is a
+// whole number of them (b = 1, 2, 4), else padded to an odd count (b = 3: 5) so lanes
+// reading consecutive words touch distinct banks
+__host__ __device__ constexpr int lut_xst(int bits) {
+    return (16 / bits) % 4 == 0 ? 16 / bits : (16 / bits) | 1;
+}
 
 int64_t lut_row_words(int64_t d_in, int bits) {
     const int64_t cpw = 2 * lut_ppw(bits);
@@ -64,73 +70,154 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// LDS: x pairs [B][rw * XST] then one pair table [M * M] per wave.  Rows: block r
-// takes rows r * rows_per_block .. + rows_per_block - 1, wave w every LUT_WAVES-th.
+// staged words per activation vector: the row words and one word of zeros, which
+// every word past the row reads (as code 0)
+__host__ __device__ inline int64_t lut_staged_words(int64_t rw) { return rw + 1; }
+
+// LDS: one table of M * M words per wave (wave w's at w * M * M, so a table index is
+// or-ed onto its base), then x pairs [B][staged words * XST].  Rows: block r takes rows
+// r * rows_per_block .. + rows_per_block - 1, wave w every LUT_WAVES-th.
 template <int BITS, int B>
 __global__ __launch_bounds__(64 * LUT_WAVES) void k_lut_gemv_bf16(
     const uint32_t* __restrict__ Q, int64_t rw, const float* __restrict__ C, int64_t d_out,
-    int64_t d_in, const uint16_t* __restrict__ x, int rows_per_block, float* __restrict__ y) {
+    int64_t d_in, const uint16_t* __restrict__ x, int whole_pairs, int rows_per_block,
+    float* __restrict__ y) {
     constexpr int M = 1 << BITS;
     constexpr int PPW = lut_ppw(BITS);
     constexpr int XST = lut_xst(BITS);
     constexpr uint32_t PMASK = (uint32_t)(M * M - 1);
     extern __shared__ uint32_t lut_lds[];
-    const int64_t xwords = rw * XST;
-    uint32_t* table = lut_lds + B * xwords;
+    const int64_t xwords = lut_staged_words(rw) * XST;
+    uint32_t* const xlds = lut_lds + LUT_WAVES * M * M;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t* tab = lut_lds + wave * (M * M);
+    const uint32_t tab_bytes = (uint32_t)(wave * M * M) * 4u;
 
-    // stage x: pair pr = w * PPW + p holds elements 2 pr, 2 pr + 1 (zero past d_in)
-    const int64_t npairs = rw * PPW;
-    for (int64_t e = tid; e < B * npairs; e += 64 * LUT_WAVES) {
-        const int b = (int)(e / npairs);
-        const int64_t pr = e - (int64_t)b * npairs;
-        const int64_t i = 2 * pr;
-        const uint32_t lo = i < d_in ? x[(int64_t)b * d_in + i] : 0u;
-        const uint32_t hi = i + 1 < d_in ? x[(int64_t)b * d_in + i + 1] : 0u;
-        const int64_t w = pr / PPW;
-        lut_lds[(int64_t)b * xwords + w * XST + (pr - w * PPW)] = lo | (hi << 16);
+    // Work of a wave: its rows (every LUT_WAVES-th of the block's), each in chunks of
+    // LUT_SPAN words; item t = (row k, chunk c).  The codes (and, at a row's start, the
+    // codebook) of item t + 1 are loaded while item t is computed.
+    const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+    int nrows = 0;
+    for (int rr = wave; rr < rows_per_block && r0 + rr < d_out; rr += LUT_WAVES) ++nrows;
+    const int nch = (int)((rw + LUT_SPAN - 1) / LUT_SPAN);
+    const int nitems = nrows * nch;
+    auto fetch = [&](int t, uint32_t (&wv)[LUT_UNROLL], float& cv) {
+        const int k = t / nch, c = t - k * nch;
+        const int64_t j = r0 + wave + (int64_t)LUT_WAVES * k;
+        const uint32_t* Qj = Q + j * rw;
+        const int w0 = c * LUT_SPAN + lane;
+        if ((int64_t)(c + 1) * LUT_SPAN <= rw) {
+#pragma unroll
+            for (int u = 0; u < LUT_UNROLL; ++u) wv[u] = Qj[w0 + 64 * u];
+        } else {
+#pragma unroll
+            for (int u = 0; u < LUT_UNROLL; ++u) {
+                const int wi = w0 + 64 * u;
+                wv[u] = wi < rw ? Qj[wi] : 0u;
+            }
+        }
+        if (c == 0) cv = lane < M ? C[j * M + lane] : 0.f;
+    };
+    uint32_t cur[LUT_UNROLL];
+    float ccur = 0.f;
+    if (nitems > 0) fetch(0, cur, ccur);
+
+    // stage x: pair pr = w * PPW + p holds elements 2 pr, 2 pr + 1 (zero past d_in);
+    // whole_pairs (even d_in, x 4-byte aligned): each pair is one 4-byte load
+    const int64_t npairs = lut_staged_words(rw) * PPW;
+    const int64_t dpairs = d_in >> 1;
+    const bool even = whole_pairs != 0;
+    for (int b = 0; b < B; ++b) {
+        const uint16_t* xb = x + (int64_t)b * d_in;
+        uint32_t* xs = xlds + (int64_t)b * xwords;
+        for (int64_t pr = tid; pr < npairs; pr += 64 * LUT_WAVES) {
+            uint32_t v;
+            if (even) {
+                v = pr < dpairs ? ((const uint32_t*)xb)[pr] : 0u;
+            } else {
+                const int64_t i = 2 * pr;
+                const uint32_t lo = i < d_in ? xb[i] : 0u;
+                const uint32_t hi = i + 1 < d_in ? xb[i + 1] : 0u;
+                v = lo | (hi << 16);
+            }
+            const int64_t w = pr / PPW;
+            xs[w * XST + (pr - w * PPW)] = v;
+        }
     }
     __syncthreads();
 
-    uint32_t* tab = table + wave * (M * M);
-    const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
-    for (int rr = wave; rr < rows_per_block; rr += LUT_WAVES) {
-        const int64_t j = r0 + rr;
-        if (j >= d_out) break;
-        // the row's pair table: entry q0 | q1 << BITS = (bf16 c_q0, bf16 c_q1)
-        for (int e = lane; e < M * M; e += 64)
-            tab[e] = pack_bf16x2(C[j * M + (e & (M - 1))], C[j * M + (e >> BITS)]);
-        float acc[B];
+    // two accumulator sets (even and odd words of a chunk) for independent chains
+    float acc[2][B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) acc[b] = 0.f;
-        const uint32_t* Qj = Q + j * rw;
-        for (int64_t w0 = lane; w0 < rw; w0 += 64 * LUT_UNROLL) {
-            uint32_t wv[LUT_UNROLL];
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int u = 0; u < LUT_UNROLL; ++u) {
-                const int64_t wi = w0 + 64 * u;
-                wv[u] = wi < rw ? Qj[wi] : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < LUT_UNROLL; ++u) {
-                const int64_t wi = w0 + 64 * u;
-                if (wi < rw) {
-                    const uint32_t* xw = lut_lds + wi * XST;
-#pragma unroll
-                    for (int p = 0; p < PPW; ++p) {
-                        const uint32_t lv = tab[(wv[u] >> (2 * BITS * p)) & PMASK];
-#pragma unroll
-                        for (int b = 0; b < B; ++b) acc[b] = dot2_bf16(lv, xw[b * xwords + p], acc[b]);
-                    }
-                }
-            }
-        }
+        for (int b = 0; b < B; ++b) acc[h][b] = 0.f;
+    const char* lds_bytes = (const char*)lut_lds;
+    auto word_step = [&](uint32_t word, int wi, int h) {
+        const uint32_t* xw = xlds + wi * XST;
+        uint32_t xv[B][PPW];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            const float s = wave_sum_f32(acc[b]);
-            if (lane == 0) y[(int64_t)b * d_out + j] = s;
+            if constexpr (PPW % 4 == 0) {          // XST == PPW: whole 16-byte vectors
+#pragma unroll
+                for (int q = 0; q < PPW / 4; ++q) {
+                    const u32x4 v = *(const u32x4*)(xw + b * xwords + 4 * q);
+                    xv[b][4 * q] = v[0]; xv[b][4 * q + 1] = v[1];
+                    xv[b][4 * q + 2] = v[2]; xv[b][4 * q + 3] = v[3];
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < PPW; ++p) xv[b][p] = xw[b * xwords + p];
+            }
         }
+#pragma unroll
+        for (int p = 0; p < PPW; ++p) {
+            // byte address of table entry ((word >> 2 b p) & PMASK) of this wave's table
+            const uint32_t off = (2 * BITS * p >= 2)
+                ? ((word >> (2 * BITS * p - 2)) & (PMASK << 2)) | tab_bytes
+                : ((word << 2) & (PMASK << 2)) | tab_bytes;
+            const uint32_t lv = *(const uint32_t*)(lds_bytes + off);
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[h][b] = dot2_bf16(lv, xv[b][p], acc[h][b]);
+        }
+    };
+    for (int t = 0; t < nitems; ++t) {
+        const int k = t / nch, c = t - k * nch;
+        uint32_t nxt[LUT_UNROLL];
+        float cnxt = 0.f;
+        if (t + 1 < nitems) fetch(t + 1, nxt, cnxt);
+        if (c == 0) {
+            // the row's pair table: entry q0 | q1 << BITS = (bf16 c_q0, bf16 c_q1); the
+            // previous row's reads of it came earlier in this wave's LDS order
+            for (int e = lane; e < M * M; e += 64)
+                tab[e] = pack_bf16x2(__shfl(ccur, e & (M - 1), 64), __shfl(ccur, e >> BITS, 64));
+        }
+        // a word past the row is code 0 against the staged zero word
+        const int w0 = c * LUT_SPAN + lane;
+        if ((int64_t)(c + 1) * LUT_SPAN <= rw) {
+#pragma unroll
+            for (int u = 0; u < LUT_UNROLL; ++u) word_step(cur[u], w0 + 64 * u, u & 1);
+        } else {
+#pragma unroll
+            for (int u = 0; u < LUT_UNROLL; ++u) {
+                const int wi = w0 + 64 * u;
+                word_step(cur[u], wi < rw ? wi : (int)rw, u & 1);
+            }
+        }
+        if (c == nch - 1) {
+            const int64_t j = r0 + wave + (int64_t)LUT_WAVES * k;
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const float s = wave_sum_f32(acc[0][b] + acc[1][b]);
+                if (lane == 0) y[(int64_t)b * d_out + j] = s;
+                acc[0][b] = 0.f;
+                acc[1][b] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < LUT_UNROLL; ++u) cur[u] = nxt[u];
+        if (c == nch - 1) ccur = cnxt;
     }
 }
 
@@ -184,7 +271,7 @@ hipError_t lut_pack_run(const uint8_t* P, int64_t d_out, int64_t d_in, int bits,
 size_t lut_gemv_lds_bytes(int64_t d_in, int bits, int batch) {
     const int64_t rw = lut_row_words(d_in, bits);
     const int m = 1 << bits;
-    return (size_t)(batch * rw * lut_xst(bits) + LUT_WAVES * m * m) * 4;
+    return (size_t)(batch * lut_staged_words(rw) * lut_xst(bits) + LUT_WAVES * m * m) * 4;
 }
 
 template <int BITS, int B>
@@ -204,7 +291,8 @@ static hipError_t launch_bf16(const uint32_t* Q, const float* C, int64_t d_out, 
     if (rpb < LUT_WAVES) rpb = LUT_WAVES;
     const int64_t grid = (d_out + rpb - 1) / rpb;
     hipLaunchKernelGGL((k_lut_gemv_bf16<BITS, B>), dim3((unsigned)grid), dim3(64 * LUT_WAVES), lds,
-                       st, Q, rw, C, d_out, d_in, x, (int)rpb, y);
+                       st, Q, rw, C, d_out, d_in, x,
+                       (int)((d_in % 2 == 0) && (((uintptr_t)x & 3u) == 0)), (int)rpb, y);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }
