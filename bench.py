@@ -5,11 +5,13 @@ grouped Fisher accumulation from (X, G), then LNQ (init + `iters` x (codebook
 step, assignment pass) + objective trace) on every output row.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--path lnq|grid] [--no-cpu-baseline]
+                    [--path lnq|grid|lut] [--no-cpu-baseline]
 
 --path grid replaces LNQ by the fixed-grid backend (uniform min-max grid per
 row, `iters` assignment passes, no codebook step) and reports that path's own
-metric.
+metric.  --path lut times the lookup-table product y = W_hat x of the packed
+(C, P) format instead (default layer 28672 -> 8192, 4-bit, one bfloat16
+activation vector): a step is --lut-reps back-to-back products.
 
 Prints one JSON line.  `value` is rows quantized per second for the whole
 layer (Fisher included); the Fisher TFLOP/s, the LNQ-only rows/s and the
@@ -45,8 +47,11 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama2_7b_attn")
-    ap.add_argument("--path", choices=("lnq", "grid"), default="lnq")
+    ap.add_argument("--workload", default=None,
+                    help="llama2_7b_attn by default; llama2_70b_down for --path lut")
+    ap.add_argument("--path", choices=("lnq", "grid", "lut"), default="lnq")
+    ap.add_argument("--lut-reps", type=int, default=100)
+    ap.add_argument("--lut-batch", type=int, default=1)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -72,6 +77,7 @@ _TRAFFIC = {
     "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "ed4bcafe3d6f08a0", 762629622, 254978077),
     "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "3a1b27a0fe44d80f", 604188222, 67108864),
     "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "ed4bcafe3d6f08a0", 1602985311, 85659200),
+    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "6af0965646e0e749", 118503969, 48253),
 }
 
 
@@ -213,7 +219,10 @@ def main():
         print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes,
                           "copies": 3}), flush=True)
         return
-    wl = synth.workload(args.workload)
+    if args.path == "lut":
+        run_lut(args)
+        return
+    wl = synth.workload(args.workload or "llama2_7b_attn")
     print(f"[bench] workload {wl.name}: d_in={wl.d_in} d_out={wl.d_out} n={wl.n} "
           f"groups={wl.groups} bits={wl.bits} iters={wl.iters}",
           file=sys.stderr, flush=True)
@@ -340,6 +349,93 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, F, args)
+    print(json.dumps(result), flush=True)
+
+
+def run_lut(args):
+    """The lookup-table product on one layer's shape: seeded random codes (uniform over
+    the 2^bits entries), sorted N(0, 0.02^2) codebooks, N(0, 1) bfloat16 activations."""
+    import torch
+    import post_weight_quantization_gq_amd as gq
+    from post_weight_quantization_gq_amd import synth
+    dev = torch.device("cuda:0")
+    wl = synth.workload(args.workload or "llama2_70b_down")
+    B = args.lut_batch
+    rng = np.random.default_rng(args.seed)
+    P_np = rng.integers(0, wl.m, size=(wl.d_out, wl.d_in), dtype=np.uint8)
+    C_np = np.sort(rng.standard_normal((wl.d_out, wl.m)).astype(np.float32) * np.float32(0.02),
+                   axis=1)
+    x_bits = synth.f32_to_bf16_bits(rng.standard_normal((B, wl.d_in)).astype(np.float32))
+    P = torch.from_numpy(P_np).to(dev)
+    C = torch.from_numpy(C_np).to(dev)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    Q = gq.lut_pack_codes(P, wl.bits)
+    y = torch.empty((B, wl.d_out), dtype=torch.float32, device=dev)
+    R = args.lut_reps
+    print(f"[bench] lut product {wl.d_in} -> {wl.d_out}, {wl.bits}-bit, batch {B}, "
+          f"{R} products per step", file=sys.stderr, flush=True)
+
+    def step():
+        for _ in range(R):
+            gq.lut_gemv(Q, C, x, wl.bits, y=y)
+
+    for i in range(max(1, args.warmup)):
+        step()
+        torch.cuda.synchronize()
+    gq.gq_timing_read()
+    gq.gq_timing_enable(["lut_gemv"])
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    gq.gq_timing_enable(False)
+    timed = gq.gq_timing_read()
+    ms_step = (t_end - t_start) * 1e3 / args.steps
+    n_launch = timed["lut_gemv"][1]
+    avg_ms = timed["lut_gemv"][0] / n_launch
+    packed = Q.numel() * 4
+    # algorithmic bytes of one product: packed codes, codebooks, activations, outputs
+    alg = packed + wl.d_out * wl.m * 4 + B * wl.d_in * 2 + B * wl.d_out * 4
+    achieved = alg / (avg_ms * 1e-3)
+    result = {
+        "metric": f"LUT dequant GEMV packed-weight GB/s at {wl.d_in}->{wl.d_out}, {wl.bits}-bit, "
+                  f"batch {B}, 1 MI355X",
+        "value": packed * R / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "path": "lut", "d_in": wl.d_in, "d_out": wl.d_out,
+                   "bits": wl.bits, "batch": B, "products_per_step": R},
+        "us_per_product_wall": ms_step * 1e3 / R,
+        "us_per_product_events": avg_ms * 1e3,
+        "roofline": {"kernel": "lut_gemv", "bound": "hbm", "achieved": achieved / 1e9,
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": achieved / PEAK_HBM,
+                     "traffic": _traffic("lut_gemv", wl) if B == 1 else None,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
+                     "avg_launch_ms": avg_ms, "units_per_launch": alg,
+                     "launches_per_step": n_launch / args.steps},
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        rows = min(wl.d_out, 512)
+        x64 = synth.bf16_bits_to_f32(x_bits).astype(np.float64)
+        t0 = time.perf_counter()
+        O.lut_gemv(C_np[:rows], P_np[:rows], x64, True)
+        t = (time.perf_counter() - t0) * wl.d_out / rows
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            cores = 1
+        result["cpu_baseline"] = {"value": packed / t / 1e9, "unit": "GB/s", "cores": cores,
+                                  "kind": "oracle",
+                                  "sample": f"oracle product on the first {rows} of {wl.d_out} "
+                                            f"rows ({t * rows / wl.d_out:.2f}s measured, "
+                                            f"scaled to the layer)"}
     print(json.dumps(result), flush=True)
 
 
