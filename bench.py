@@ -5,13 +5,15 @@ grouped Fisher accumulation from (X, G), then LNQ (init + `iters` x (codebook
 step, assignment pass) + objective trace) on every output row.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--path lnq|grid|lut] [--no-cpu-baseline]
+                    [--path lnq|grid|lut|stream] [--no-cpu-baseline]
 
 --path grid replaces LNQ by the fixed-grid backend (uniform min-max grid per
 row, `iters` assignment passes, no codebook step) and reports that path's own
 metric.  --path lut times the lookup-table product y = W_hat x of the packed
 (C, P) format instead (default layer 28672 -> 8192, 4-bit, one bfloat16
-activation vector): a step is --lut-reps back-to-back products.
+activation vector): a step is --lut-reps back-to-back products.  --path stream
+times the Fisher alone with X and G in pinned host memory, streamed to the GPU
+in chunks of --chunk-tokens tokens (PCIe-bound).
 
 Prints one JSON line.  `value` is rows quantized per second for the whole
 layer (Fisher included); the Fisher TFLOP/s, the LNQ-only rows/s and the
@@ -40,6 +42,7 @@ PEAK_BF16_MFMA = 2500e12      # dense bf16 matrix-core FLOP/s
 PEAK_FP32_VALU = 157.3e12     # fp32 vector FLOP/s (FMA = 2 flops, packed)
 PEAK_HBM = 8e12               # bytes/s
 PEAK_FP32_ADD = 78.6e12       # fp32 vector adds/s (one add per lane per cycle)
+PEAK_PCIE = 63.0e9            # host-to-device bytes/s, PCIe 5.0 x16 (32 GT/s x 16, 128b/130b)
 
 
 def _parse():
@@ -49,7 +52,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=None,
                     help="llama2_7b_attn by default; llama2_70b_down for --path lut")
-    ap.add_argument("--path", choices=("lnq", "grid", "lut"), default="lnq")
+    ap.add_argument("--path", choices=("lnq", "grid", "lut", "stream"), default="lnq")
+    ap.add_argument("--chunk-tokens", type=int, default=16384)
     ap.add_argument("--lut-reps", type=int, default=100)
     ap.add_argument("--lut-batch", type=int, default=1)
     ap.add_argument("--seed", type=int, default=0)
@@ -221,6 +225,9 @@ def main():
         return
     if args.path == "lut":
         run_lut(args)
+        return
+    if args.path == "stream":
+        run_stream(args)
         return
     wl = synth.workload(args.workload or "llama2_7b_attn")
     print(f"[bench] workload {wl.name}: d_in={wl.d_in} d_out={wl.d_out} n={wl.n} "
@@ -436,6 +443,71 @@ def run_lut(args):
                                   "sample": f"oracle product on the first {rows} of {wl.d_out} "
                                             f"rows ({t * rows / wl.d_out:.2f}s measured, "
                                             f"scaled to the layer)"}
+    print(json.dumps(result), flush=True)
+
+
+def run_stream(args):
+    """The Fisher of one layer's calibration data held in pinned host memory."""
+    import torch
+    import post_weight_quantization_gq_amd as gq
+    from post_weight_quantization_gq_amd import synth
+    dev = torch.device("cuda:0")
+    wl = synth.workload(args.workload or "llama2_7b_attn")
+    t0 = time.time()
+    inp = synth.make_inputs(wl, seed=args.seed, want=("X", "G"))
+
+    def host(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
+            else torch.from_numpy(a)
+        return t.pin_memory()
+
+    X, G = host(inp["X"]), host(inp["G"])
+    del inp
+    print(f"[bench] pinned host inputs ready in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    T = args.chunk_tokens
+    F = torch.empty((wl.groups, wl.d_in, wl.d_in), dtype=torch.float32, device=dev)
+    ws = torch.empty(gq.fisher_stream_workspace_size(min(T, wl.n), wl.d_in, wl.d_out, wl.groups),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        gq.gq_fisher_accumulate_host(X, G, wl.groups, F=F, chunk_tokens=T, ws=ws)
+
+    warm = max(1, args.warmup)
+    for i in range(warm):
+        if i == warm - 1:
+            gq.gq_timing_read()
+            gq.gq_timing_enable(True)
+        step()
+        torch.cuda.synchronize()
+    gq.gq_timing_enable(False)
+    per_step = {k: v[0] for k, v in gq.gq_timing_read().items() if v[1]}
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    host_bytes = X.numel() * X.element_size() + G.numel() * G.element_size()
+    achieved = host_bytes / (ms_step * 1e-3)
+    result = {
+        "metric": f"Host-streamed Fisher tokens/s at {wl.d_in}x{wl.d_out}, {wl.n} tokens "
+                  f"(X, G in pinned host memory), 1 MI355X",
+        "value": wl.n / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "path": "stream", "d_in": wl.d_in, "d_out": wl.d_out,
+                   "n_tokens": wl.n, "groups": wl.groups, "chunk_tokens": T},
+        "stage_ms_per_step": {k: round(v, 4) for k, v in per_step.items()},
+        "stage_breakdown_from": "last warmup step; fisher_h2d is timed on the copy stream",
+        "roofline": {"kernel": "host-to-device copies", "bound": "pcie",
+                     "achieved": achieved / 1e9, "peak": PEAK_PCIE / 1e9, "unit": "GB/s",
+                     "frac": achieved / PEAK_PCIE, "traffic": None,
+                     "units_per_launch": host_bytes, "launches_per_step": 1},
+    }
     print(json.dumps(result), flush=True)
 
 

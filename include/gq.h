@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 4
+#define GQ_ABI_VERSION 5
 
 typedef enum {
     GQ_OK = 0,
@@ -131,6 +131,28 @@ gq_status gq_fisher_accumulate(const void* X, gq_dtype x_dt, int64_t n, int64_t 
                                const void* G, gq_dtype g_dt, int64_t d_out, int32_t groups,
                                float* F, int32_t accumulate,
                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The grouped Fisher of gq_fisher_accumulate for calibration data held in host
+ * memory (a token count beyond what device memory holds): X [n][d_in] and
+ * G [n][d_out] are HOST pointers (pinned, e.g. hipHostMalloc, for the copies to
+ * run asynchronously; pageable memory works but each copy then blocks the
+ * caller).  The tokens are taken in chunks of chunk_tokens (the last may be
+ * shorter); each chunk is copied to device memory on a library-created copy
+ * stream while the previous chunk's Fisher runs on `stream`, and every chunk adds
+ * into F (the first with `accumulate`).  Since F is a sum over tokens, the result
+ * is the Fisher of all n tokens, with float32 sums of the per-chunk partials.
+ * F, ws: device memory; ws of at least gq_fisher_stream_workspace_size(chunk_tokens
+ * or n if smaller, ...) bytes (NULL: allocated stream-ordered).  The host arrays
+ * must stay valid and unchanged until `stream` has passed this call's work.
+ */
+size_t gq_fisher_stream_workspace_size(int64_t chunk_tokens, int64_t d_in, int64_t d_out,
+                                       int32_t groups, gq_dtype x_dt);
+gq_status gq_fisher_accumulate_host(const void* X_host, gq_dtype x_dt, int64_t n, int64_t d_in,
+                                    const void* G_host, gq_dtype g_dt, int64_t d_out,
+                                    int32_t groups, float* F, int32_t accumulate,
+                                    int64_t chunk_tokens, void* ws, size_t ws_bytes,
+                                    void* stream);
 
 /* Workspace bytes every lnq_* call below needs for these sizes and W dtype. */
 size_t gq_lnq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_t bits,
@@ -290,6 +312,7 @@ typedef enum {
     GQ_STAGE_LNQ_DELTA,         /* Gram and residual updates from the changed coordinates */
     GQ_STAGE_LUT_PACK,          /* code packing for the lookup-table product */
     GQ_STAGE_LUT_GEMV,          /* the lookup-table product */
+    GQ_STAGE_FISHER_H2D,        /* host-to-device copies of the streamed Fisher (copy stream) */
     GQ_STAGE_COUNT
 } gq_stage;
 

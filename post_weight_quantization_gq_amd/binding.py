@@ -18,16 +18,17 @@ GQ_OK, GQ_EINVAL, GQ_ESHAPE, GQ_EDTYPE, GQ_ENOMEM, GQ_EHIP, GQ_ENOTIMPL = 0, 1, 
 GQ_F32, GQ_BF16 = 0, 1
 GQ_INIT_QUANTILE, GQ_INIT_GIVEN, GQ_INIT_UNIFORM = 0, 1, 2
 GQ_GRAM_AUTO, GQ_GRAM_DENSE = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 # every symbol include/gq.h declares
 EXPORTS = (
     "gq_abi_version", "gq_last_error", "gq_lnq_options_default", "gq_fisher_workspace_size",
     "gq_fisher_accumulate", "gq_lnq_workspace_size", "lnq_codebook_update", "lnq_assign_sweep",
     "lnq_objective", "lnq_quantize", "grid_quantize", "lut_packed_row_words", "lut_pack_codes",
-    "lut_gemv", "gq_timing_enable", "gq_timing_read", "gq_stage_name",
+    "lut_gemv", "gq_fisher_stream_workspace_size", "gq_fisher_accumulate_host",
+    "gq_timing_enable", "gq_timing_read", "gq_stage_name",
 )
-STAGE_COUNT = 15
+STAGE_COUNT = 16
 
 
 class GQError(RuntimeError):
@@ -68,6 +69,9 @@ _SIGS = {
     "lut_packed_row_words": (_i64, [_i64, _i32]),
     "lut_pack_codes": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
     "lut_gemv": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _vp, _i32, _i32, _vp, _vp]),
+    "gq_fisher_stream_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32]),
+    "gq_fisher_accumulate_host": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _i32,
+                                                 _vp, _i32, _i64, _vp, _sz, _vp]),
     "gq_timing_enable": (None, [ctypes.c_int]),
     "gq_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "gq_stage_name": (ctypes.c_char_p, [ctypes.c_int]),
@@ -302,6 +306,40 @@ def grid_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float
     return C, P, tr, nch[:iters]
 
 
+def fisher_stream_workspace_size(chunk_tokens, d_in, d_out, groups, dtype=GQ_BF16) -> int:
+    return int(library().gq_fisher_stream_workspace_size(chunk_tokens, d_in, d_out, groups,
+                                                          dtype))
+
+
+def gq_fisher_accumulate_host(X, G, groups: int, F=None, accumulate: bool = False,
+                              chunk_tokens: int = 16384, ws=None, stream=None,
+                              device=None) -> torch.Tensor:
+    """F[g] (=|+=) X^T diag(s_g) X with X [n][d_in], G [n][d_out] in HOST memory (CPU
+    tensors, pinned for asynchronous copies), streamed to the GPU in chunks of tokens."""
+    lib = library()
+    for t, name in ((X, "X"), (G, "G")):
+        if t.device.type != "cpu" or not t.is_contiguous():
+            raise GQError(GQ_EINVAL, f"{name} must be a contiguous host (CPU) tensor")
+    n, d_in = X.shape
+    d_out = G.shape[1]
+    if G.shape[0] != n:
+        raise GQError(GQ_ESHAPE, "X and G need the same number of tokens")
+    dev = F.device if F is not None else (device or torch.device("cuda", torch.cuda.current_device()))
+    if F is None:
+        F = torch.empty((groups, d_in, d_in), dtype=torch.float32, device=dev)
+        if accumulate:
+            F.zero_()
+    _dev(F, "F", torch.float32)
+    if ws is None:
+        nb = fisher_stream_workspace_size(min(chunk_tokens, n), d_in, d_out, groups, _dt(X))
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    _check(lib.gq_fisher_accumulate_host(ctypes.c_void_p(X.data_ptr()), _dt(X), n, d_in,
+                                         ctypes.c_void_p(G.data_ptr()), _dt(G), d_out, groups,
+                                         _ptr(F), int(accumulate), chunk_tokens, _ptr(ws),
+                                         ws.numel(), _stream(stream)))
+    return F
+
+
 def lut_packed_row_words(d_in: int, bits: int) -> int:
     return int(library().lut_packed_row_words(d_in, bits))
 
@@ -340,7 +378,7 @@ def lut_gemv(Q, C, x, bits: int, d_in: int | None = None, y=None, stream=None) -
 
 STAGES = ("group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain", "lnq_prepare",
           "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep", "lnq_small",
-          "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv")
+          "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv", "fisher_h2d")
 
 
 def gq_timing_enable(on=True) -> None:

@@ -172,7 +172,7 @@ const char* gq_stage_name(int stage) {
     static const char* names[GQ_STAGE_COUNT] = {
         "group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain", "lnq_prepare",
         "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep", "lnq_small",
-        "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv"};
+        "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv", "fisher_h2d"};
     if (stage < 0 || stage >= GQ_STAGE_COUNT) return "";
     return names[stage];
 }
@@ -215,6 +215,83 @@ gq_status gq_fisher_accumulate(const void* X, gq_dtype x_dt, int64_t n, int64_t 
     if (rc != GQ_OK) return rc;
     hipError_t e = gq::fisher_run(X, G, bf16, n, d_in, d_out, groups, F, accumulate, s.ptr, st);
     if (e != hipSuccess) return hip_fail(e, "gq_fisher_accumulate");
+    return GQ_OK;
+}
+
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t gq_fisher_stream_workspace_size(int64_t chunk_tokens, int64_t d_in, int64_t d_out,
+                                       int32_t groups, gq_dtype x_dt) {
+    if (chunk_tokens < 1 || d_in < 1 || d_out < 1 || groups < 1 || !dtype_ok(x_dt)) return 0;
+    const size_t es = x_dt == GQ_BF16 ? 2 : 4;
+    return al256(gq::fisher_workspace(chunk_tokens, d_in, groups, x_dt == GQ_BF16)) +
+           2 * al256((size_t)chunk_tokens * d_in * es) + 2 * al256((size_t)chunk_tokens * d_out * es);
+}
+
+// Host-resident X and G, streamed in chunks of T tokens.  Chunk k is copied on a copy
+// stream into device buffer k % 2 while chunk k - 1's Fisher runs on `stream` and adds
+// into F (the first chunk with the caller's `accumulate`).  Events order the buffers:
+// chunk k's Fisher waits for its copy, chunk k + 2's copy waits for chunk k's Fisher,
+// and the first copy waits for the work already on `stream` (which may still use ws).
+gq_status gq_fisher_accumulate_host(const void* X, gq_dtype x_dt, int64_t n, int64_t d_in,
+                                    const void* G, gq_dtype g_dt, int64_t d_out, int32_t groups,
+                                    float* F, int32_t accumulate, int64_t chunk_tokens, void* ws,
+                                    size_t ws_bytes, void* stream) {
+    if (!X || !G || !F) return fail(GQ_EINVAL, "null X, G or F");
+    if (!dtype_ok(x_dt) || !dtype_ok(g_dt)) return fail(GQ_EDTYPE, "unsupported dtype");
+    if (x_dt != g_dt) return fail(GQ_EDTYPE, "X and G must share a dtype");
+    if (n < 1 || d_in < 1 || d_out < 1) return fail(GQ_ESHAPE, "empty shape");
+    if (groups < 1) return fail(GQ_EINVAL, "groups must be >= 1");
+    if (d_out % groups) return fail(GQ_ESHAPE, "d_out=%lld is not a multiple of groups=%d",
+                                    (long long)d_out, groups);
+    if (accumulate != 0 && accumulate != 1) return fail(GQ_EINVAL, "accumulate must be 0 or 1");
+    if (chunk_tokens < 1) return fail(GQ_EINVAL, "chunk_tokens must be >= 1");
+    if (!al16(F) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "F must be 16-byte and ws 256-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    const bool bf16 = x_dt == GQ_BF16;
+    const int64_t T = chunk_tokens < n ? chunk_tokens : n;
+    const size_t es = bf16 ? 2 : 4;
+    const size_t fws = al256(gq::fisher_workspace(T, d_in, groups, bf16));
+    const size_t xbytes = al256((size_t)T * d_in * es), gbytes = al256((size_t)T * d_out * es);
+    Scratch s;
+    gq_status rc = s.acquire(ws, ws_bytes, fws + 2 * xbytes + 2 * gbytes, st);
+    if (rc != GQ_OK) return rc;
+    char* base = (char*)s.ptr;
+    void* xb[2] = {base + fws, base + fws + xbytes};
+    void* gb[2] = {base + fws + 2 * xbytes, base + fws + 2 * xbytes + gbytes};
+
+    hipStream_t cs = nullptr;
+    hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};   // copied x2, consumed x2, start
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    for (int i = 0; i < 5 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(ev[4], st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev[4], 0);
+    const int64_t nchunks = (n + T - 1) / T;
+    for (int64_t k = 0; k < nchunks && e == hipSuccess; ++k) {
+        const int b = (int)(k & 1);
+        const int64_t t0 = k * T;
+        const int64_t tk = (n - t0) < T ? (n - t0) : T;
+        if (k >= 2) e = hipStreamWaitEvent(cs, ev[2 + b], 0);
+        if (e == hipSuccess) {
+            gq::StageTimer tm(gq::ST_FISHER_H2D, cs);
+            e = hipMemcpyAsync(xb[b], (const char*)X + (size_t)t0 * d_in * es, (size_t)tk * d_in * es,
+                               hipMemcpyHostToDevice, cs);
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(gb[b], (const char*)G + (size_t)t0 * d_out * es,
+                                   (size_t)tk * d_out * es, hipMemcpyHostToDevice, cs);
+        }
+        if (e == hipSuccess) e = hipEventRecord(ev[b], cs);
+        if (e == hipSuccess) e = hipStreamWaitEvent(st, ev[b], 0);
+        if (e == hipSuccess)
+            e = gq::fisher_run(xb[b], gb[b], bf16, tk, d_in, d_out, groups, F,
+                               (k == 0) ? accumulate : 1, base, st);
+        if (e == hipSuccess) e = hipEventRecord(ev[2 + b], st);
+    }
+    // the stream and events are released once their pending work completes
+    for (int i = 0; i < 5; ++i)
+        if (ev[i]) (void)hipEventDestroy(ev[i]);
+    if (cs) (void)hipStreamDestroy(cs);
+    if (e != hipSuccess) return hip_fail(e, "gq_fisher_accumulate_host");
     return GQ_OK;
 }
 

@@ -10,7 +10,7 @@ namespace gq {
 enum Stage {
     ST_GROUP_SCALE = 0, ST_FISHER_MFMA, ST_FISHER_FINALIZE, ST_FISHER_PLAIN, ST_LNQ_PREPARE,
     ST_LNQ_RESID, ST_LNQ_INIT, ST_LNQ_GRAM, ST_LNQ_SOLVE, ST_LNQ_SWEEP, ST_LNQ_SMALL, ST_FISHER_PACK,
-    ST_LNQ_DELTA, ST_LUT_PACK, ST_LUT_GEMV, ST_COUNT
+    ST_LNQ_DELTA, ST_LUT_PACK, ST_LUT_GEMV, ST_FISHER_H2D, ST_COUNT
 };
 bool timing_on(Stage s);
 void timing_mark(Stage s, hipStream_t st, bool begin);

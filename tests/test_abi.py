@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(B.EXPORTS), declared ^ set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert gq.abi_version() == 4
+    assert gq.abi_version() == 5
 
 
 def test_options_default():
@@ -135,6 +135,26 @@ def test_grid_argument_errors():
     assert q(opt=ctypes.byref(o), wsb=100) == B.GQ_EINVAL and "workspace" in _err(lib)
 
 
+def test_fisher_host_argument_errors():
+    lib = gq.library()
+    call = lambda **k: lib.gq_fisher_accumulate_host(
+        k.get("X", FAKE), k.get("xdt", 1), k.get("n", 1000), k.get("d_in", 256),
+        k.get("G", FAKE), k.get("gdt", 1), k.get("d_out", 64), k.get("groups", 2),
+        k.get("F", FAKE), k.get("acc", 0), k.get("chunk", 256), k.get("ws", FAKE),
+        k.get("wsb", 0), None)
+    assert call(X=None) == B.GQ_EINVAL
+    assert call(gdt=0) == B.GQ_EDTYPE
+    assert call(n=0) == B.GQ_ESHAPE
+    assert call(d_out=63) == B.GQ_ESHAPE
+    assert call(acc=3) == B.GQ_EINVAL
+    assert call(chunk=0) == B.GQ_EINVAL and "chunk" in _err(lib)
+    assert call(F=FAKE_ODD) == B.GQ_EINVAL
+    assert call(wsb=16) == B.GQ_EINVAL and "workspace too small" in _err(lib)
+    assert gq.fisher_stream_workspace_size(256, 256, 64, 2) > \
+        gq.fisher_workspace_size(256, 256, 64, 2)
+    assert gq.fisher_stream_workspace_size(0, 256, 64, 2) == 0
+
+
 def test_lut_argument_errors():
     lib = gq.library()
     assert gq.lut_packed_row_words(4096, 3) == 412        # 410 words of 10 codes, to 4k
@@ -173,5 +193,6 @@ def test_timing_read_empty():
     t = gq.gq_timing_read()
     assert set(t) == {"group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain",
                       "lnq_prepare", "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep",
-                      "lnq_small", "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv"}
+                      "lnq_small", "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv",
+                      "fisher_h2d"}
     assert all(v == (0.0, 0) for v in t.values())
