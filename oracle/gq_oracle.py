@@ -18,6 +18,9 @@ the pages' order), in float64 with NumPy.  Sources:
              closed form and the "(assignment)" coordinate loop i = 1..d_in.
   [GQ-abs]   aitopics.org "squeezellm" page, GuidedQuant abstract: the
              non-uniform scalar algorithm decreases the objective monotonically.
+  [GANQ]     atlas.scime.ai GANQ summary page, "Approach": alternating updates, an
+             assignment of the codebook indices by Cholesky / back-substitution
+             and a closed-form least-squares codebook update.
 
 Readings where the pages are silent (the same readings the GPU library uses):
   * F_j = X^T diag(G[:, j]^2) X without the 1/n factor (the objective equation
@@ -34,6 +37,9 @@ Readings where the pages are silent (the same readings the GPU library uses):
   * Empty code q (no coordinate assigned): c_q is kept unchanged.
   * Assignment: coordinates in ascending order; a coordinate moves only on a
     strict decrease of the objective, to the lowest-index minimiser.
+  * GANQ-style assignment ([GANQ] below): back-substitution over F' = L L^T,
+    coordinates from the last to the first, each taking the entry nearest to
+    w_j - s_j / L_jj; the codebook step is LNQ's.
   * LUT dequantisation GEMV: y = W_hat x with W_hat[j][i] = c^(j)[p_ji]; the
     packed index layout is this library's own (the pages fix none).  For
     bfloat16 activations the lookup table holds the codebook rounded to
@@ -52,7 +58,8 @@ __all__ = [
     "damped", "init_quantile", "one_hot", "codebook_system", "codebook_update",
     "assign_deltas", "assign_sweep", "objective", "lnq_row", "guided_loss",
     "replay_sweep", "init_uniform_grid", "grid_row", "lut_codes_per_word", "lut_row_words",
-    "lut_pack", "lut_unpack", "bf16_round", "lut_gemv",
+    "lut_pack", "lut_unpack", "bf16_round", "lut_gemv", "ganq_assign", "ganq_row",
+    "ganq_replay",
 ]
 
 
@@ -396,3 +403,90 @@ def lut_gemv(C: np.ndarray, P: np.ndarray, x: np.ndarray, lut_bf16: bool) -> np.
     W_hat = np.take_along_axis(Cv, np.asarray(P, np.int64), axis=1)
     x = np.atleast_2d(np.asarray(x, np.float64))
     return x @ W_hat.T
+
+
+# ----------------------------------------------------------------------------
+# GANQ-style assignment [GANQ]
+# ----------------------------------------------------------------------------
+# The GANQ summary page describes the per-row problem solved by alternating a
+# closed-form least-squares codebook update with an assignment of the indices by
+# Cholesky / back-substitution.  Reading: with F' = L L^T (L lower triangular) the
+# row objective is ||L^T e||^2, e = w_hat - w, whose j-th term
+# (L^T e)_j = L_jj e_j + sum_{k>j} L_kj e_k involves only coordinates j..d-1; the
+# assignment visits j = d-1 down to 0 and gives coordinate j the codebook entry
+# that minimises that term with the later coordinates already fixed, i.e. the
+# entry nearest to w_j - s_j / L_jj with s_j = sum_{k>j} L_kj e_k (lowest index on
+# ties).  The codebook step is the LNQ closed form above.
+
+def ganq_assign(Fp: np.ndarray, w: np.ndarray, c: np.ndarray, L: np.ndarray | None = None,
+                return_targets: bool = False):
+    """Back-substitution assignment of one row against F' = L L^T  [GANQ]."""
+    if L is None:
+        L = np.linalg.cholesky(np.asarray(Fp, np.float64))
+    w = np.asarray(w, np.float64)
+    c = np.asarray(c, np.float64)
+    d = w.shape[0]
+    e = np.zeros(d)
+    p = np.empty(d, dtype=np.int64)
+    targets = np.empty(d)
+    for j in range(d - 1, -1, -1):
+        s = float(L[j + 1:, j] @ e[j + 1:])
+        t = w[j] - s / L[j, j]
+        q = int(np.argmin(np.abs(t - c)))       # first occurrence = lowest index
+        p[j] = q
+        e[j] = c[q] - w[j]
+        targets[j] = t
+    if return_targets:
+        return p, targets
+    return p
+
+
+def ganq_row(Fp: np.ndarray, w: np.ndarray, m: int, iters: int, c0=None, p0=None):
+    """GANQ-style alternation for one row: init, then `iters` x (codebook, assignment).
+
+    Returns (c, p, trace) laid out as lnq_row's: trace[2t-1] after the codebook step
+    and trace[2t] after the assignment of pass t.  The assignment solves the
+    back-substitution problem, so the trace need not decrease.
+    """
+    L = np.linalg.cholesky(np.asarray(Fp, np.float64))
+    if c0 is None:
+        c, p = init_quantile(w, m)
+    else:
+        c = np.asarray(c0, np.float64).copy()
+        p = np.asarray(p0, np.int64).copy()
+    trace = [objective(Fp, w, c, p)]
+    for _ in range(iters):
+        c = codebook_update(Fp, w, p, c)
+        trace.append(objective(Fp, w, c, p))
+        p = ganq_assign(Fp, w, c, L)
+        trace.append(objective(Fp, w, c, p))
+    return c, p, np.array(trace)
+
+
+def ganq_replay(Fp: np.ndarray, w: np.ndarray, c: np.ndarray, p_dev: np.ndarray, tol: float,
+                L: np.ndarray | None = None):
+    """Follow the device's decisions of one assignment pass (from the last coordinate
+    down) and check each: with the device's later decisions fixed, its entry must be
+    within `tol` * L_jj * (largest codebook gap) of the nearest one to the target,
+    measured on the term |L_jj (c_q - w_j) + s_j|.  Returns (worst excess over the
+    allowance, number of decisions that differ from the fp64 choice)."""
+    if L is None:
+        L = np.linalg.cholesky(np.asarray(Fp, np.float64))
+    w = np.asarray(w, np.float64)
+    c = np.asarray(c, np.float64)
+    p_dev = np.asarray(p_dev, np.int64)
+    d = w.shape[0]
+    gap = float(np.max(np.diff(np.sort(c)))) if c.shape[0] > 1 else 0.0
+    e = np.zeros(d)
+    worst = -np.inf
+    differ = 0
+    for j in range(d - 1, -1, -1):
+        s = float(L[j + 1:, j] @ e[j + 1:])
+        term = np.abs(L[j, j] * (c - w[j]) + s)
+        q_ref = int(np.argmin(term))
+        q = int(p_dev[j])
+        worst = max(worst, float(term[q] - term[q_ref]) - tol * L[j, j] * gap)
+        if q != q_ref:
+            differ += 1
+        e[j] = c[q] - w[j]
+    return worst, differ

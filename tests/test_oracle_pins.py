@@ -601,3 +601,89 @@ def test_lut_gemv_bruteforce_loops():
             for i in range(d_in):
                 s += float(C[j, P[j, i]]) * x[b, i]
             assert y[b, j] == s
+
+
+# --------------------------------------------------------------------------
+# GANQ-style assignment: back-substitution over F' = L L^T
+# --------------------------------------------------------------------------
+
+def test_ganq_hand_example():
+    """F' = [[4, 2], [2, 2]] = L L^T with L = [[2, 0], [1, 1]]; w = (0.3, 0.6),
+    codebook {0, 1}.  Coordinate 1 first: target 0.6 -> entry 1, e_1 = 0.4; then
+    s_0 = L_10 e_1 = 0.4, target 0.3 - 0.4 / 2 = 0.1 -> entry 0, e_0 = -0.3.
+    Objective e^T F' e = 0.36 - 0.48 + 0.32 = 0.2."""
+    F = np.array([[4.0, 2.0], [2.0, 2.0]])
+    p = O.ganq_assign(F, np.array([0.3, 0.6]), np.array([0.0, 1.0]))
+    np.testing.assert_array_equal(p, [0, 1])
+    assert O.objective(F, np.array([0.3, 0.6]), np.array([0.0, 1.0]), p) == pytest.approx(0.2)
+
+
+def test_ganq_diagonal_F_gives_nearest_codes():
+    rng = _rng(100)
+    d, m = 30, 8
+    F = np.diag(rng.uniform(0.1, 3.0, d))
+    w = rng.standard_normal(d)
+    c = np.sort(rng.standard_normal(m))
+    p = O.ganq_assign(F, w, c)
+    np.testing.assert_array_equal(p, np.argmin(np.abs(w[:, None] - c[None, :]), axis=1))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_ganq_is_the_reverse_lexicographic_minimiser(seed):
+    """Brute force over all m^d codes: the assignment minimises |(L^T e)_{d-1}| first,
+    then |(L^T e)_{d-2}|, ... down to |(L^T e)_0| (lowest index among exact ties),
+    and its objective equals ||L^T e||^2."""
+    rng = _rng(110 + seed)
+    d, m = 5, 3
+    F = _spd(rng, d, n=d + 3)
+    L = np.linalg.cholesky(F)
+    w = rng.standard_normal(d)
+    c = np.sort(rng.standard_normal(m))
+    p = O.ganq_assign(F, w, c)
+    best_key, best = None, None
+    for t in itertools.product(range(m), repeat=d):
+        e = c[np.array(t)] - w
+        terms = np.abs(L.T @ e)
+        key = tuple(terms[::-1])
+        if best_key is None or key < best_key:
+            best_key, best = key, np.array(t)
+    np.testing.assert_array_equal(p, best)
+    e = c[p] - w
+    assert O.objective(F, w, c, p) == pytest.approx(float(np.sum((L.T @ e) ** 2)), rel=1e-12)
+    opt = min(O.objective(F, w, c, np.array(t)) for t in itertools.product(range(m), repeat=d))
+    assert opt <= O.objective(F, w, c, p) + 1e-15
+
+
+def test_ganq_exact_when_weights_are_codebook_entries():
+    rng = _rng(120)
+    d, m = 40, 4
+    F = _spd(rng, d)
+    c = np.sort(rng.standard_normal(m))
+    q = rng.integers(0, m, d)
+    p = O.ganq_assign(F, c[q], c)
+    np.testing.assert_array_equal(p, q)
+
+
+def test_ganq_row_codebook_steps_do_not_increase():
+    rng = _rng(121)
+    d, m = 24, 4
+    F = _spd(rng, d)
+    w = rng.standard_normal(d)
+    _, _, tr = O.ganq_row(F, w, m, 4)
+    for t in range(1, 5):
+        assert tr[2 * t - 1] <= tr[2 * t - 2] * (1 + 1e-12) + 1e-15
+
+
+def test_ganq_replay_accepts_own_decisions_and_rejects_a_planted_one():
+    rng = _rng(122)
+    d, m = 60, 8
+    F = _spd(rng, d)
+    w = rng.standard_normal(d)
+    c = np.sort(rng.standard_normal(m))
+    p = O.ganq_assign(F, w, c)
+    worst, differ = O.ganq_replay(F, w, c, p, 1e-9)
+    assert worst <= 0.0 and differ == 0
+    bad = p.copy()
+    bad[d // 2] = (bad[d // 2] + m // 2) % m
+    worst, differ = O.ganq_replay(F, w, c, bad, 1e-9)
+    assert worst > 0.0 and differ >= 1
