@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 5
+#define GQ_ABI_VERSION 6
 
 typedef enum {
     GQ_OK = 0,
@@ -285,6 +285,44 @@ gq_status lut_gemv(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_i
                    const void* x, gq_dtype x_dt, int32_t batch, float* y, void* stream);
 
 /*
+ * GANQ-style alternation.  The GANQ summary page ("Approach") solves each row by
+ * alternating a closed-form least-squares codebook update with an assignment of
+ * the indices by Cholesky / back-substitution.  Here: F'_g = L L^T (float64
+ * factorization on the GPU); the row objective is ||L^T e||^2 with
+ * e = w_hat - w, and the assignment visits j = d_in - 1 down to 0, giving
+ * coordinate j the codebook entry nearest to w_j - s_j / L_jj,
+ * s_j = sum_{k>j} L_kj e_k (lowest index on ties; the targets are float32).  The
+ * codebook step is LNQ's (lnq_codebook_update).  Unlike LNQ's coordinate pass,
+ * the assignment does not start from the current codes and need not lower the
+ * objective.
+ *
+ * ganq_quantize: init as opt->init (QUANTILE, UNIFORM or GIVEN), then `iters`
+ * times (codebook step, assignment).  Arguments as for lnq_quantize; obj_trace
+ * [2*iters+1] holds the objective before and after every half-step, each
+ * recomputed from (C, P).  not_pd (device int32 [groups], may be NULL): 1 where
+ * F'_g has a non-positive pivot (e.g. all-zero gradients with ridge 0); those
+ * groups keep their codes through every assignment.  opt->gram_update is
+ * ignored.  Requires d_in % 64 == 0, 1 <= bits <= 4.  Workspace:
+ * ganq_workspace_size (the LNQ workspace plus groups * d_in^2 * 8 bytes for the
+ * float64 factor and the bf16 planes of L^T).
+ *
+ * ganq_factor_damped: the factor alone, L [groups][d_in][d_in] float32 (lower
+ * triangle, zeros above) of F'_g = F_g + ridge_rel * mean(diag F_g) I, and the
+ * not_pd flags (may be NULL).  Workspace: ganq_workspace_size(groups, d_in,
+ * groups, 1, ...).
+ */
+size_t ganq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_t bits,
+                           gq_dtype w_dt);
+gq_status ganq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in,
+                        const float* F, int32_t groups, int32_t bits, int32_t iters,
+                        const gq_lnq_options* opt, float* C, uint8_t* P,
+                        double* obj_trace, int64_t* n_changed, int32_t* not_pd,
+                        void* ws, size_t ws_bytes, void* stream);
+gq_status ganq_factor_damped(const float* F, int32_t groups, int64_t d_in, float ridge_rel,
+                             float* L, int32_t* not_pd, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/*
  * Diagnostics: per-stage kernel timing with HIP events.
  * gq_timing_enable(mask) makes every later call bracket each launch sequence of
  * the stages whose bit (1 << gq_stage) is set in `mask` with two events recorded
@@ -313,6 +351,8 @@ typedef enum {
     GQ_STAGE_LUT_PACK,          /* code packing for the lookup-table product */
     GQ_STAGE_LUT_GEMV,          /* the lookup-table product */
     GQ_STAGE_FISHER_H2D,        /* host-to-device copies of the streamed Fisher (copy stream) */
+    GQ_STAGE_GANQ_CHOL,         /* Cholesky factor of F' for the back-substitution assignment */
+    GQ_STAGE_GANQ_PASS,         /* the back-substitution assignment */
     GQ_STAGE_COUNT
 } gq_stage;
 

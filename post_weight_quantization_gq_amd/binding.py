@@ -18,7 +18,7 @@ GQ_OK, GQ_EINVAL, GQ_ESHAPE, GQ_EDTYPE, GQ_ENOMEM, GQ_EHIP, GQ_ENOTIMPL = 0, 1, 
 GQ_F32, GQ_BF16 = 0, 1
 GQ_INIT_QUANTILE, GQ_INIT_GIVEN, GQ_INIT_UNIFORM = 0, 1, 2
 GQ_GRAM_AUTO, GQ_GRAM_DENSE = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 # every symbol include/gq.h declares
 EXPORTS = (
@@ -26,9 +26,10 @@ EXPORTS = (
     "gq_fisher_accumulate", "gq_lnq_workspace_size", "lnq_codebook_update", "lnq_assign_sweep",
     "lnq_objective", "lnq_quantize", "grid_quantize", "lut_packed_row_words", "lut_pack_codes",
     "lut_gemv", "gq_fisher_stream_workspace_size", "gq_fisher_accumulate_host",
+    "ganq_workspace_size", "ganq_quantize", "ganq_factor_damped",
     "gq_timing_enable", "gq_timing_read", "gq_stage_name",
 )
-STAGE_COUNT = 16
+STAGE_COUNT = 18
 
 
 class GQError(RuntimeError):
@@ -72,6 +73,11 @@ _SIGS = {
     "gq_fisher_stream_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "gq_fisher_accumulate_host": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _i32,
                                                  _vp, _i32, _i64, _vp, _sz, _vp]),
+    "ganq_workspace_size": (_sz, [_i64, _i64, _i32, _i32, _i32]),
+    "ganq_quantize": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _i32,
+                                     ctypes.POINTER(lnq_options), _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _sz, _vp]),
+    "ganq_factor_damped": (ctypes.c_int, [_vp, _i32, _i64, _f32, _vp, _vp, _vp, _sz, _vp]),
     "gq_timing_enable": (None, [ctypes.c_int]),
     "gq_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "gq_stage_name": (ctypes.c_char_p, [ctypes.c_int]),
@@ -340,6 +346,54 @@ def gq_fisher_accumulate_host(X, G, groups: int, F=None, accumulate: bool = Fals
     return F
 
 
+def ganq_workspace_size(d_out, d_in, groups, bits, w_dtype=GQ_BF16) -> int:
+    return int(library().ganq_workspace_size(d_out, d_in, groups, bits, w_dtype))
+
+
+def ganq_quantize(W, F, bits: int, iters: int, ridge_rel: float = 1e-6, C=None, P=None,
+                  init: int | None = None, trace: bool = True, ws=None, stream=None):
+    """GANQ-style alternation.  Returns (C, P, obj_trace [2 iters + 1] or None,
+    n_changed [iters], not_pd [groups] int32)."""
+    lib = library()
+    groups = F.shape[0]
+    d_out, d_in = _lnq_common(F, W, groups)
+    m = 1 << bits
+    if init is None:
+        init = GQ_INIT_GIVEN if (C is not None and P is not None) else GQ_INIT_QUANTILE
+    if C is None:
+        C = torch.empty((d_out, m), dtype=torch.float32, device=W.device)
+    if P is None:
+        P = torch.empty((d_out, d_in), dtype=torch.uint8, device=W.device)
+    _dev(C, "C", torch.float32)
+    _dev(P, "P", torch.uint8)
+    tr = torch.empty(2 * iters + 1, dtype=torch.float64, device=W.device) if trace else None
+    nch = torch.zeros(max(iters, 1), dtype=torch.int64, device=W.device)
+    npd = torch.zeros(groups, dtype=torch.int32, device=W.device)
+    opt = options(64, ridge_rel, init)
+    if ws is None:
+        ws = torch.empty(max(ganq_workspace_size(d_out, d_in, groups, bits, _dt(W)), 1),
+                         dtype=torch.uint8, device=W.device)
+    _check(lib.ganq_quantize(_ptr(W), _dt(W), d_out, d_in, _ptr(F), groups, bits, iters,
+                             ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), _ptr(npd),
+                             _ptr(ws), ws.numel(), _stream(stream)))
+    return C, P, tr, nch[:iters], npd
+
+
+def ganq_factor_damped(F, ridge_rel: float = 1e-6, ws=None, stream=None):
+    """(L [groups][d][d] float32 lower, not_pd [groups] int32) of F' = F + lambda I."""
+    lib = library()
+    _dev(F, "F", torch.float32)
+    groups, d_in = F.shape[0], F.shape[1]
+    L = torch.empty_like(F)
+    npd = torch.zeros(groups, dtype=torch.int32, device=F.device)
+    if ws is None:
+        ws = torch.empty(max(ganq_workspace_size(groups, d_in, groups, 1), 1), dtype=torch.uint8,
+                         device=F.device)
+    _check(lib.ganq_factor_damped(_ptr(F), groups, d_in, ridge_rel, _ptr(L), _ptr(npd), _ptr(ws),
+                                  ws.numel(), _stream(stream)))
+    return L, npd
+
+
 def lut_packed_row_words(d_in: int, bits: int) -> int:
     return int(library().lut_packed_row_words(d_in, bits))
 
@@ -378,7 +432,8 @@ def lut_gemv(Q, C, x, bits: int, d_in: int | None = None, y=None, stream=None) -
 
 STAGES = ("group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain", "lnq_prepare",
           "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep", "lnq_small",
-          "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv", "fisher_h2d")
+          "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv", "fisher_h2d", "ganq_chol",
+          "ganq_pass")
 
 
 def gq_timing_enable(on=True) -> None:

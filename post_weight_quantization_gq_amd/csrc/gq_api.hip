@@ -172,7 +172,8 @@ const char* gq_stage_name(int stage) {
     static const char* names[GQ_STAGE_COUNT] = {
         "group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain", "lnq_prepare",
         "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep", "lnq_small",
-        "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv", "fisher_h2d"};
+        "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv", "fisher_h2d", "ganq_chol",
+        "ganq_pass"};
     if (stage < 0 || stage >= GQ_STAGE_COUNT) return "";
     return names[stage];
 }
@@ -539,6 +540,111 @@ gq_status lut_gemv(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_i
                     (long long)d_in, batch);
     hipError_t e = gq::lut_gemv_run(Q, C, d_out, d_in, bits, x, xb, batch, y, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "lut_gemv");
+    return GQ_OK;
+}
+
+size_t ganq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_t bits,
+                           gq_dtype w_dt) {
+    const size_t base = gq_lnq_workspace_size(d_out, d_in, groups, bits, w_dt);
+    if (base == 0) return 0;
+    return al256(base) + gq::ganq_extra_bytes(d_in, groups);
+}
+
+static gq_status ganq_setup(const float* F, int32_t groups, int64_t d_in, int64_t d_out,
+                            int32_t bits, float ridge_rel, void* ws, size_t ws_bytes,
+                            hipStream_t st, Scratch& s, gq::LnqWs& w, gq::GanqWs& gw) {
+    const int m = 1 << bits;
+    gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m);
+    const size_t need = al256(z.total) + gq::ganq_extra_bytes(d_in, groups);
+    gq_status rc = s.acquire(ws, ws_bytes, need, st);
+    if (rc != GQ_OK) return rc;
+    w = gq::lnq_carve(s.ptr, z);
+    gw = gq::ganq_carve((char*)s.ptr + al256(z.total), d_in, groups);
+    hipError_t e;
+    if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
+    if ((e = gq::ganq_factor(F, w.lam, d_in, groups, gw, st)) != hipSuccess) return hip_fail(e, "factor");
+    return GQ_OK;
+}
+
+gq_status ganq_factor_damped(const float* F, int32_t groups, int64_t d_in, float ridge_rel,
+                             float* L, int32_t* not_pd, void* ws, size_t ws_bytes, void* stream) {
+    if (!F || !L) return fail(GQ_EINVAL, "null F or L");
+    if (groups < 1 || d_in < 1) return fail(GQ_ESHAPE, "empty shape");
+    if (d_in % 64) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of 64", (long long)d_in);
+    if (!(ridge_rel >= 0.0f)) return fail(GQ_EINVAL, "ridge_rel must be >= 0");
+    if (!al16(F) || !al16(L) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "F, L 16-byte and ws 256-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    Scratch s;
+    gq::LnqWs w;
+    gq::GanqWs gw;
+    // the factor needs no W-sized buffers: size them for one row
+    gq_status rc = ganq_setup(F, groups, d_in, groups, 1, ridge_rel, ws, ws_bytes, st, s, w, gw);
+    if (rc != GQ_OK) return rc;
+    hipError_t e = gq::ganq_factor_out(gw, d_in, groups, L, (int*)not_pd, st);
+    if (e != hipSuccess) return hip_fail(e, "ganq_factor_damped");
+    return GQ_OK;
+}
+
+gq_status ganq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in, const float* F,
+                        int32_t groups, int32_t bits, int32_t iters, const gq_lnq_options* opt,
+                        float* C, uint8_t* P, double* obj_trace, int64_t* n_changed,
+                        int32_t* not_pd, void* ws, size_t ws_bytes, void* stream) {
+    gq_lnq_options o;
+    gq_lnq_options_default(&o);
+    if (opt) o = *opt;
+    gq_status rc = check_lnq_shape(F, groups, d_in, W, w_dt, d_out, bits, o.ridge_rel);
+    if (rc != GQ_OK) return rc;
+    if (!P || !C) return fail(GQ_EINVAL, "null P or C");
+    if (!al16(P) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "P must be 16-byte and ws 256-byte aligned");
+    if (iters < 0) return fail(GQ_EINVAL, "iters must be >= 0");
+    if (o.init != GQ_INIT_QUANTILE && o.init != GQ_INIT_GIVEN && o.init != GQ_INIT_UNIFORM)
+        return fail(GQ_EINVAL, "unknown init %d", o.init);
+    if (d_in % 64) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of 64", (long long)d_in);
+    hipStream_t st = (hipStream_t)stream;
+    const bool wb = w_dt == GQ_BF16;
+    const int m = 1 << bits;
+    Scratch s;
+    gq::LnqWs w;
+    gq::GanqWs gw;
+    if ((rc = ganq_setup(F, groups, d_in, d_out, bits, o.ridge_rel, ws, ws_bytes, st, s, w, gw)) != GQ_OK)
+        return rc;
+    hipError_t e;
+    if (not_pd && (e = gq::ganq_factor_out(gw, d_in, groups, nullptr, (int*)not_pd, st)) != hipSuccess)
+        return hip_fail(e, "factor flags");
+    if (o.init == GQ_INIT_QUANTILE &&
+        (e = gq::lnq_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
+        return hip_fail(e, "init");
+    if (o.init == GQ_INIT_UNIFORM &&
+        (e = gq::grid_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
+        return hip_fail(e, "init");
+    if (iters > 0 && (e = gq::lnq_zero_counter(w.cnt, 3, st)) != hipSuccess)
+        return hip_fail(e, "counter");
+    for (int t = 1; t <= iters; ++t) {
+        // codebook step (recomputed); objA = objective before it (trace entry 2t - 2)
+        if ((e = gq::lnq_codebook_step(F, W, wb, d_out, d_in, groups, m, P, C, w, w.objA,
+                                       w.cnt + 1, nullptr, st)) != hipSuccess)
+            return hip_fail(e, "codebook");
+        // objective after it (entry 2t - 1)
+        if ((e = gq::lnq_objective_rows(W, wb, d_out, d_in, groups, m, P, C, w, w.objB, st)) !=
+            hipSuccess)
+            return hip_fail(e, "objective");
+        // the back-substitution assignment; the residual buffer serves as its running sums
+        if ((e = gq::ganq_assign_run(gw, d_in, d_out, groups, C, m, P, W, wb, w.R, w.cnt, st)) !=
+            hipSuccess)
+            return hip_fail(e, "assignment");
+        if ((e = gq::lnq_iter_tail(w.objA, w.objB, d_out,
+                                   obj_trace ? obj_trace + 2 * t - 2 : nullptr, w.cnt,
+                                   n_changed ? n_changed + (t - 1) : nullptr, -1, st)) !=
+            hipSuccess)
+            return hip_fail(e, "iteration tail");
+    }
+    if (obj_trace) {
+        if ((e = gq::lnq_objective_rows(W, wb, d_out, d_in, groups, m, P, C, w, w.objA, st)) !=
+            hipSuccess)
+            return hip_fail(e, "final objective");
+        if ((e = gq::lnq_reduce(w.objA, d_out, obj_trace + 2 * iters, st)) != hipSuccess)
+            return hip_fail(e, "trace");
+    }
     return GQ_OK;
 }
 

@@ -1,0 +1,504 @@
+// GANQ-style assignment on gfx950: back-substitution over the Cholesky factor of F'.
+//
+// GANQ summary page (atlas.scime.ai, "GANQ: GPU-Adaptive Non-Uniform Quantization"),
+// "Approach": per row, alternating updates of a closed-form least-squares codebook and
+// an assignment of the indices by Cholesky / back-substitution.  With F' = L L^T the
+// row objective is ||L^T e||^2 (e = w_hat - w), whose j-th term
+// (L^T e)_j = L_jj e_j + s_j,  s_j = sum_{k>j} L_kj e_k,
+// involves coordinates j..d-1 only.  The assignment visits j = d-1 down to 0 and gives
+// coordinate j the codebook entry nearest to w_j - s_j / L_jj.
+//
+// Work split on the GPU
+//   k_chol_init    A = F + lambda I as float64 (lower triangle), per group
+//   k_chol_diag    one 64 x 64 diagonal block: unblocked Cholesky in LDS, its inverse
+//   k_chol_panel   the panel below it: L21 = A21 L11^{-T}
+//   k_chol_update  trailing lower triangle: A22 -= L21 L21^T (float64 FMAs, 64 x 64 tiles)
+//   k_ganq_prep    U = L^T as k-blocked bfloat16 planes (hi + lo) for the matrix cores,
+//                  diag(L) in float32
+//   k_ganq         the pass: 16 rows per block, coordinates from the last to the first
+//                  in 64-blocks grouped into super-blocks of 512:
+//                    * s from later super-blocks: a running array S, updated at the end
+//                      of each super-block for all earlier coordinates on the matrix
+//                      cores, S[:, :sb] += E_sb U[:sb, sb]^T (three bf16 products);
+//                    * s from later 64-blocks of the same super-block: the same product
+//                      before each block;
+//                    * inside a block, 64 dependent steps: lane t takes its entry, and
+//                      every lane i < t adds L[t][i] e_t (the block of L staged in LDS).
+#include "gq_common.h"
+#include "gq_internal.h"
+
+namespace gq {
+
+constexpr int CB = 64;                 // panel width of the factorization
+
+// ---------------------------------------------------------------------------
+// Cholesky of F' = F + lambda I (float64), in place in A [groups][d][d] (lower)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_chol_init(const float* __restrict__ F,
+                                                  const double* __restrict__ lam, int64_t d,
+                                                  double* __restrict__ A,
+                                                  int* __restrict__ bad) {
+    const int g = blockIdx.y;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e == 0) bad[g] = 0;
+    if (e >= d * d) return;
+    const int64_t i = e / d, j = e - i * d;
+    const float* Fg = F + (size_t)g * d * d;
+    A[(size_t)g * d * d + e] = (j <= i) ? (double)Fg[e] + (i == j ? lam[g] : 0.0) : 0.0;
+}
+
+// One block per group factors diagonal block p in LDS and writes L_pp (lower) back to A
+// and its inverse to Linv [groups][64][64].  A pivot that is not positive (F' singular,
+// e.g. a group whose gradients vanish) marks the group in `bad` and is replaced by 1 so
+// the rest of the factorization stays finite; a marked group's codes are left as they are.
+__global__ __launch_bounds__(256) void k_chol_diag(double* __restrict__ A, int64_t d, int p,
+                                                  double* __restrict__ Linv,
+                                                  int* __restrict__ bad) {
+    __shared__ double a[CB][CB + 1];
+    __shared__ double x[CB][CB + 1];
+    const int g = blockIdx.x;
+    const int tid = threadIdx.x;
+    double* Ag = A + (size_t)g * d * d;
+    const int64_t o = (int64_t)p * CB;
+    for (int e = tid; e < CB * CB; e += 256) {
+        const int i = e / CB, j = e % CB;
+        a[i][j] = (j <= i) ? Ag[(o + i) * d + o + j] : 0.0;
+        x[i][j] = 0.0;
+    }
+    __syncthreads();
+    for (int c = 0; c < CB; ++c) {
+        if (tid == 0) {
+            double piv = a[c][c];
+            if (!(piv > 0.0)) {
+                bad[g] = 1;
+                piv = 1.0;
+            }
+            a[c][c] = sqrt(piv);
+        }
+        __syncthreads();
+        for (int i = c + 1 + tid; i < CB; i += 256) a[i][c] = a[i][c] / a[c][c];
+        __syncthreads();
+        // trailing update of the lower triangle: pairs (i, j), c < j <= i < CB
+        const int n = CB - 1 - c;
+        for (int e = tid; e < n * n; e += 256) {
+            const int i = c + 1 + e / n, j = c + 1 + e % n;
+            if (j <= i) a[i][j] -= a[i][c] * a[j][c];
+        }
+        __syncthreads();
+    }
+    // inverse of the lower-triangular block, one column per thread:
+    // X_cc = 1 / L_cc,  X_ic = -(sum_{k=c}^{i-1} L_ik X_kc) / L_ii
+    if (tid < CB) {
+        const int c = tid;
+        x[c][c] = 1.0 / a[c][c];
+        for (int i = c + 1; i < CB; ++i) {
+            double s = 0.0;
+            for (int k = c; k < i; ++k) s += a[i][k] * x[k][c];
+            x[i][c] = -s / a[i][i];
+        }
+    }
+    __syncthreads();
+    double* Lg = Linv + (size_t)g * CB * CB;
+    for (int e = tid; e < CB * CB; e += 256) {
+        const int i = e / CB, j = e % CB;
+        if (j <= i) Ag[(o + i) * d + o + j] = a[i][j];
+        Lg[e] = x[i][j];
+    }
+}
+
+// Rows below diagonal block p, 64 at a time: L[r][c] = sum_k A[r][k] Linv[c][k]
+// (Linv lower, so k <= c).  Grid (row tiles, groups), 256 threads, 4 x 4 outputs each.
+__global__ __launch_bounds__(256) void k_chol_panel(double* __restrict__ A, int64_t d, int p,
+                                                   const double* __restrict__ Linv) {
+    __shared__ double li[CB][CB + 1];
+    __shared__ double ar[CB][CB + 1];
+    const int g = blockIdx.y;
+    const int tid = threadIdx.x;
+    double* Ag = A + (size_t)g * d * d;
+    const int64_t o = (int64_t)p * CB;
+    const int64_t r0 = o + CB + (int64_t)blockIdx.x * CB;
+    const double* Lg = Linv + (size_t)g * CB * CB;
+    for (int e = tid; e < CB * CB; e += 256) {
+        const int i = e / CB, j = e % CB;
+        li[i][j] = Lg[e];
+        ar[i][j] = (r0 + i < d) ? Ag[(r0 + i) * d + o + j] : 0.0;
+    }
+    __syncthreads();
+    const int tr = tid / 16, tc = tid % 16;        // rows tr + 16 u, columns tc + 16 v
+    double acc[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+    for (int k = 0; k < CB; ++k) {
+        double av[4], lv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) av[u] = ar[tr + 16 * u][k];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) lv[v] = li[tc + 16 * v][k];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[u][v] = fma(av[u], lv[v], acc[u][v]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t r = r0 + tr + 16 * u;
+        if (r < d) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) Ag[r * d + o + tc + 16 * v] = acc[u][v];
+        }
+    }
+}
+
+// Trailing update after panel p: tiles (ti, tj), p < tj <= ti < nt, of the lower
+// triangle: A[ti][tj] -= L[ti][p] L[tj][p]^T.  Linear tile index t over the triangle.
+__global__ __launch_bounds__(256) void k_chol_update(double* __restrict__ A, int64_t d, int p,
+                                                    int nt) {
+    __shared__ double li[CB][CB + 1];
+    __shared__ double lj[CB][CB + 1];
+    const int g = blockIdx.y;
+    const int tid = threadIdx.x;
+    // t -> (ti, tj) with tj <= ti, both counted from p + 1
+    int t = blockIdx.x, ti = 0;
+    while (t > ti) { t -= ti + 1; ++ti; }
+    const int tj = t;
+    const int64_t oi = (int64_t)(p + 1 + ti) * CB, oj = (int64_t)(p + 1 + tj) * CB;
+    const int64_t o = (int64_t)p * CB;
+    double* Ag = A + (size_t)g * d * d;
+    for (int e = tid; e < CB * CB; e += 256) {
+        const int i = e / CB, k = e % CB;
+        li[i][k] = Ag[(oi + i) * d + o + k];
+        lj[i][k] = Ag[(oj + i) * d + o + k];
+    }
+    __syncthreads();
+    const int tr = tid / 16, tc = tid % 16;
+    double acc[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+    for (int k = 0; k < CB; ++k) {
+        double av[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) av[u] = li[tr + 16 * u][k];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) bv[v] = lj[tc + 16 * v][k];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[u][v] = fma(av[u], bv[v], acc[u][v]);
+    }
+    (void)nt;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = tr + 16 * u, j = tc + 16 * v;
+            if (ti != tj || j <= i) Ag[(oi + i) * d + oj + j] -= acc[u][v];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// U = L^T as k-blocked bf16 planes: element (a, k) = U[a][k] = L[k][a] for k > a, else
+// 0, at ((k / 16) * a_pad + a) * 16 + k % 16 (the layout of the F' planes); dL = diag L.
+// One thread per (group, 16-block of k, a).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_ganq_prep(const double* __restrict__ A, int64_t d,
+                                                  int64_t a_pad, uint16_t* __restrict__ Uhi,
+                                                  uint16_t* __restrict__ Ulo,
+                                                  float* __restrict__ dL) {
+    const int g = blockIdx.y;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t nkb = d / 16;
+    if (t >= nkb * a_pad) return;
+    const int64_t kb = t / a_pad, a = t - kb * a_pad;
+    const double* Ag = A + (size_t)g * d * d;
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        float v2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t k = kb * 16 + 2 * q + h;
+            v2[h] = (a < d && k > a) ? (float)Ag[k * d + a] : 0.f;
+        }
+        hi[q] = pack_bf16x2(v2[0], v2[1]);
+        const float r0 = v2[0] - bf16_bits_to_f32(hi[q] & 0xffffu);
+        const float r1 = v2[1] - bf16_bits_to_f32(hi[q] >> 16);
+        lo[q] = pack_bf16x2(r0, r1);
+    }
+    const size_t off = ((size_t)g * nkb * a_pad + (size_t)t) * 16;
+    u32x4* H = (u32x4*)(Uhi + off);
+    u32x4* Lo = (u32x4*)(Ulo + off);
+    H[0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    H[1] = u32x4{hi[4], hi[5], hi[6], hi[7]};
+    Lo[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    Lo[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
+    if (kb == 0 && a < d) dL[(size_t)g * d + a] = (float)Ag[a * d + a];
+}
+
+// the factor as float32, zeros above the diagonal
+__global__ void k_ganq_export(const double* __restrict__ A, int64_t n, float* __restrict__ L) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) L[i] = (float)A[i];
+}
+
+__device__ __forceinline__ float ganq_readlane_f(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__global__ void k_zero_f32(float* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// The assignment pass.  One block = 16 rows of one group (one row per wave).
+// ---------------------------------------------------------------------------
+constexpr int GQ_ROWS = 16;
+constexpr int GQ_SUB = 64;
+constexpr int GQ_SB = 512;
+constexpr int GQ_DP = GQ_SB + 8;
+
+template <bool WBF16, int M>
+__global__ __launch_bounds__(1024, 1) void k_ganq(
+    const double* __restrict__ A, const float* __restrict__ dL,
+    const uint16_t* __restrict__ Uhi, const uint16_t* __restrict__ Ulo, int64_t d,
+    int64_t rows_per_group, int wgs_per_group, int total_wgs, const float* __restrict__ C,
+    uint8_t* __restrict__ P, const void* __restrict__ W, float* __restrict__ S,
+    const int* __restrict__ bad, unsigned long long* __restrict__ n_changed) {
+    __shared__ __attribute__((aligned(16))) uint16_t esb_hi[GQ_ROWS][GQ_DP];
+    __shared__ __attribute__((aligned(16))) uint16_t esb_lo[GQ_ROWS][GQ_DP];
+    __shared__ float corr_p[4][GQ_ROWS][GQ_SUB];
+    __shared__ float lb[GQ_SUB][GQ_SUB];         // lb[t][i] = L[bs + t][bs + i] for t > i, else 0
+    __shared__ float ldiag[GQ_SUB];
+
+    const int nb = gridDim.x;
+    const int hw = blockIdx.x;
+    const int lin = (hw & 7) * (nb >> 3) + (hw >> 3);
+    if (lin >= total_wgs) return;                 // whole block exits together
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lin / wgs_per_group;
+    if (bad[g]) return;                           // F' not positive definite: codes kept
+    const int64_t local = (int64_t)(lin % wgs_per_group) * GQ_ROWS;
+    const int64_t jl = local + wave;
+    const bool rvalid = jl < rows_per_group;
+    const int64_t j = (int64_t)g * rows_per_group + (rvalid ? jl : 0);
+    const int64_t row0 = (int64_t)g * rows_per_group + local;
+    const int nrows = (int)((rows_per_group - local) < GQ_ROWS ? (rows_per_group - local) : GQ_ROWS);
+
+    const double* Ag = A + (size_t)g * d * d;
+    const float* dLg = dL + (size_t)g * d;
+    const int64_t a_pad = lnq_pad256(d);
+    const uint16_t* Uh = Uhi + (size_t)g * d * a_pad;
+    const uint16_t* Ul = Ulo + (size_t)g * d * a_pad;
+    const uint32_t kstep32 = (uint32_t)(32 * a_pad);
+    auto plane_at = [&](const uint16_t* base, int64_t a, int64_t k) {
+        return base + ((k >> 4) * a_pad + a) * 16 + (k & 15);
+    };
+    float cq[M];
+#pragma unroll
+    for (int q = 0; q < M; ++q) cq[q] = rvalid ? C[j * M + q] : 0.f;
+    unsigned moves = 0;
+    const int ko = 8 * (lane >> 4);
+    const int mrow = lane & 15;
+
+    const int64_t last_sb = ((d - 1) / GQ_SB) * GQ_SB;
+    for (int64_t sb0 = last_sb; sb0 >= 0; sb0 -= GQ_SB) {
+        const int sblen = (int)((d - sb0) < GQ_SB ? (d - sb0) : GQ_SB);
+        const int nch = sblen / 32;
+        for (int o = sblen - GQ_SUB; o >= 0; o -= GQ_SUB) {
+            const int64_t bs = sb0 + o;
+            // ---- the super-block's later blocks: corr_i = sum_{k in sb, k >= o + 64}
+            // U[bs + i][sb0 + k] e_k, 4 column tiles x 4 k-slices of 32-chunks
+            {
+                const int ct = wave & 3, sl = wave >> 2;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                const int64_t fcol = bs + ct * 16 + mrow;
+                const uint16_t* Uh_c = plane_at(Uh, fcol, sb0 + ko);
+                const uint16_t* Ul_c = plane_at(Ul, fcol, sb0 + ko);
+                for (int c = (o + GQ_SUB) / 32 + sl; c < nch; c += 4) {
+                    const u32x4 fh = *(const u32x4*)(Uh_c + (uint32_t)c * kstep32);
+                    const u32x4 fl = *(const u32x4*)(Ul_c + (uint32_t)c * kstep32);
+                    const u32x4 eh = *(const u32x4*)(&esb_hi[mrow][c * 32 + ko]);
+                    const u32x4 el = *(const u32x4*)(&esb_lo[mrow][c * 32 + ko]);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(eh), as_bf16x8(fh), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(eh), as_bf16x8(fl), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(el), as_bf16x8(fh), acc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) corr_p[sl][4 * (lane >> 4) + t][ct * 16 + mrow] = acc[t];
+            }
+            // ---- stage the block of L (strictly lower part) and its diagonal
+            for (int e = tid; e < GQ_SUB * GQ_SUB; e += 1024) {
+                const int t = e >> 6, i = e & 63;
+                lb[t][i] = (t > i) ? (float)Ag[(bs + t) * d + bs + i] : 0.f;
+            }
+            if (tid < GQ_SUB) ldiag[tid] = dLg[bs + tid];
+            __syncthreads();
+
+            float ev = 0.f;
+            if (rvalid) {
+                const int64_t col = bs + lane;
+                float s = S[j * d + col];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) s += corr_p[k][wave][lane];
+                const float wv = load_elem<WBF16>(W, j * d + col);
+                const float u = ldiag[lane];
+                const int old = P[j * d + col];
+                int code = 0;
+                for (int t = GQ_SUB - 1; t >= 0; --t) {
+                    // lane t's entry: nearest to w - s / L_tt (lowest index on ties)
+                    const float tgt = wv - s / u;
+                    float best = fabsf(tgt - cq[0]);
+                    int bq = 0;
+#pragma unroll
+                    for (int q = 1; q < M; ++q) {
+                        const float dq = fabsf(tgt - cq[q]);
+                        if (dq < best) { best = dq; bq = q; }
+                    }
+                    float en = cq[0];
+#pragma unroll
+                    for (int q = 1; q < M; ++q) en = (bq == q) ? cq[q] : en;
+                    en -= wv;
+                    const float et = ganq_readlane_f(en, t);
+                    if (lane == t) { code = bq; ev = en; }
+                    s = fmaf(lb[t][lane], et, s);     // lanes i < t: s_i += L[t][i] e_t
+                }
+                P[j * d + col] = (uint8_t)code;
+                const unsigned long long chg = __ballot(code != old);
+                moves += (unsigned)__popcll(chg);
+            }
+            const uint32_t hb = f32_to_bf16_bits(ev);
+            esb_hi[wave][o + lane] = (uint16_t)hb;
+            esb_lo[wave][o + lane] = (uint16_t)f32_to_bf16_bits(ev - __uint_as_float(hb << 16));
+            __syncthreads();
+        }
+        // ---- earlier coordinates: S[rows, :sb0] += E_sb U[:sb0, sb]^T, one 16-column
+        // tile per wave
+        const int ntiles = (int)(sb0 / 16);
+        for (int ctile = wave; ctile < ntiles; ctile += GQ_ROWS) {
+            const int64_t fcol = (int64_t)ctile * 16 + mrow;
+            const uint16_t* Uh_c = plane_at(Uh, fcol, sb0 + ko);
+            const uint16_t* Ul_c = plane_at(Ul, fcol, sb0 + ko);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < nch; ++c) {
+                const u32x4 fh = *(const u32x4*)(Uh_c + (uint32_t)c * kstep32);
+                const u32x4 fl = *(const u32x4*)(Ul_c + (uint32_t)c * kstep32);
+                const u32x4 eh = *(const u32x4*)(&esb_hi[mrow][c * 32 + ko]);
+                const u32x4 el = *(const u32x4*)(&esb_lo[mrow][c * 32 + ko]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(eh), as_bf16x8(fh), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(eh), as_bf16x8(fl), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(el), as_bf16x8(fh), acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int rr = 4 * (lane >> 4) + t;
+                if (rr < nrows) S[(row0 + rr) * d + fcol] += acc[t];
+            }
+        }
+        __syncthreads();
+    }
+    if (rvalid && lane == 0 && n_changed) atomicAdd(n_changed, (unsigned long long)moves);
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+size_t ganq_extra_bytes(int64_t d, int groups) {
+    const int64_t a_pad = lnq_pad256(d);
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    return al((size_t)groups * d * d * 8) + 2 * al((size_t)groups * d * a_pad * 2) +
+           al((size_t)groups * d * 4) + al((size_t)groups * CB * CB * 8) + al((size_t)groups * 4);
+}
+
+GanqWs ganq_carve(void* base, int64_t d, int groups) {
+    const int64_t a_pad = lnq_pad256(d);
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    char* b = (char*)base;
+    GanqWs w;
+    w.A = (double*)b;            b += al((size_t)groups * d * d * 8);
+    w.uhi = (uint16_t*)b;        b += al((size_t)groups * d * a_pad * 2);
+    w.ulo = (uint16_t*)b;        b += al((size_t)groups * d * a_pad * 2);
+    w.dL = (float*)b;            b += al((size_t)groups * d * 4);
+    w.Linv = (double*)b;         b += al((size_t)groups * CB * CB * 8);
+    w.bad = (int*)b;
+    return w;
+}
+
+hipError_t ganq_factor(const float* F, const double* lam, int64_t d, int groups, const GanqWs& w,
+                       hipStream_t st) {
+    StageTimer tm(ST_GANQ_CHOL, st);
+    {
+        const dim3 grid((unsigned)((d * d + 255) / 256), (unsigned)groups);
+        hipLaunchKernelGGL(k_chol_init, grid, dim3(256), 0, st, F, lam, d, w.A, w.bad);
+        GQ_LAUNCH_CHECK();
+    }
+    const int nt = (int)(d / CB);               // d % 64 == 0
+    for (int p = 0; p < nt; ++p) {
+        hipLaunchKernelGGL(k_chol_diag, dim3((unsigned)groups), dim3(256), 0, st, w.A, d, p, w.Linv,
+                           w.bad);
+        GQ_LAUNCH_CHECK();
+        const int rest = nt - p - 1;
+        if (rest == 0) break;
+        hipLaunchKernelGGL(k_chol_panel, dim3((unsigned)rest, (unsigned)groups), dim3(256), 0, st,
+                           w.A, d, p, w.Linv);
+        GQ_LAUNCH_CHECK();
+        const int ntri = rest * (rest + 1) / 2;
+        hipLaunchKernelGGL(k_chol_update, dim3((unsigned)ntri, (unsigned)groups), dim3(256), 0, st,
+                           w.A, d, p, nt);
+        GQ_LAUNCH_CHECK();
+    }
+    const int64_t a_pad = lnq_pad256(d);
+    const dim3 grid((unsigned)(((d / 16) * a_pad + 255) / 256), (unsigned)groups);
+    hipLaunchKernelGGL(k_ganq_prep, grid, dim3(256), 0, st, w.A, d, a_pad, w.uhi, w.ulo, w.dL);
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
+}
+
+hipError_t ganq_factor_out(const GanqWs& w, int64_t d, int groups, float* L, int* bad_out,
+                           hipStream_t st) {
+    // L [groups][d][d] float32 (lower triangle; zeros above) and the per-group flags
+    if (L) {
+        const int64_t n = (int64_t)groups * d * d;
+        hipLaunchKernelGGL(k_ganq_export, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, w.A,
+                           n, L);
+        GQ_LAUNCH_CHECK();
+    }
+    if (bad_out) {
+        hipError_t e = hipMemcpyAsync(bad_out, w.bad, (size_t)groups * 4, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <bool WB>
+static hipError_t launch_ganq(const GanqWs& g, int64_t d, int64_t d_out, int groups,
+                              const float* C, int m, uint8_t* P, const void* W, float* S,
+                              unsigned long long* counter, hipStream_t st) {
+    const int64_t rpg = d_out / groups;
+    const int wgs = (int)((rpg + GQ_ROWS - 1) / GQ_ROWS);
+    const int total = wgs * groups;
+    const int grid = (total + 7) / 8 * 8;
+    auto kern = (m == 2) ? k_ganq<WB, 2> : (m == 4) ? k_ganq<WB, 4> : (m == 8) ? k_ganq<WB, 8>
+                                                                  : k_ganq<WB, 16>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(1024), 0, st, g.A, g.dL, g.uhi, g.ulo, d,
+                       rpg, wgs, total, C, P, W, S, g.bad, counter);
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
+}
+
+hipError_t ganq_assign_run(const GanqWs& g, int64_t d, int64_t d_out, int groups, const float* C,
+                           int m, uint8_t* P, const void* W, bool w_bf16, float* S,
+                           unsigned long long* counter, hipStream_t st) {
+    StageTimer tm(ST_GANQ_PASS, st);
+    const int64_t n = d_out * d;
+    hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, S, n);
+    GQ_LAUNCH_CHECK();
+    return w_bf16 ? launch_ganq<true>(g, d, d_out, groups, C, m, P, W, S, counter, st)
+                  : launch_ganq<false>(g, d, d_out, groups, C, m, P, W, S, counter, st);
+}
+
+}  // namespace gq

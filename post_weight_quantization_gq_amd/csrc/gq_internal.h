@@ -10,7 +10,7 @@ namespace gq {
 enum Stage {
     ST_GROUP_SCALE = 0, ST_FISHER_MFMA, ST_FISHER_FINALIZE, ST_FISHER_PLAIN, ST_LNQ_PREPARE,
     ST_LNQ_RESID, ST_LNQ_INIT, ST_LNQ_GRAM, ST_LNQ_SOLVE, ST_LNQ_SWEEP, ST_LNQ_SMALL, ST_FISHER_PACK,
-    ST_LNQ_DELTA, ST_LUT_PACK, ST_LUT_GEMV, ST_FISHER_H2D, ST_COUNT
+    ST_LNQ_DELTA, ST_LUT_PACK, ST_LUT_GEMV, ST_FISHER_H2D, ST_GANQ_CHOL, ST_GANQ_PASS, ST_COUNT
 };
 bool timing_on(Stage s);
 void timing_mark(Stage s, hipStream_t st, bool begin);
@@ -119,5 +119,23 @@ hipError_t lut_pack_run(const uint8_t* P, int64_t d_out, int64_t d_in, int bits,
                         hipStream_t st);
 hipError_t lut_gemv_run(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in, int bits,
                         const void* x, bool x_bf16, int batch, float* y, hipStream_t st);
+
+// GANQ-style assignment (gq_ganq.hip)
+struct GanqWs {
+    double* A;                    // F' then its Cholesky factor L (lower) [groups][d][d]
+    uint16_t *uhi, *ulo;          // U = L^T as k-blocked bf16 planes [groups][d / 16][a_pad][16]
+    float* dL;                    // diag L [groups][d]
+    double* Linv;                 // inverse of the current diagonal block [groups][64][64]
+    int* bad;                     // F'_g not positive definite [groups]
+};
+size_t ganq_extra_bytes(int64_t d, int groups);
+GanqWs ganq_carve(void* base, int64_t d, int groups);
+hipError_t ganq_factor(const float* F, const double* lam, int64_t d, int groups, const GanqWs& w,
+                       hipStream_t st);
+hipError_t ganq_factor_out(const GanqWs& w, int64_t d, int groups, float* L, int* bad_out,
+                           hipStream_t st);
+hipError_t ganq_assign_run(const GanqWs& g, int64_t d, int64_t d_out, int groups, const float* C,
+                           int m, uint8_t* P, const void* W, bool w_bf16, float* S,
+                           unsigned long long* counter, hipStream_t st);
 
 }  // namespace gq

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(B.EXPORTS), declared ^ set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert gq.abi_version() == 5
+    assert gq.abi_version() == 6
 
 
 def test_options_default():
@@ -155,6 +155,32 @@ def test_fisher_host_argument_errors():
     assert gq.fisher_stream_workspace_size(0, 256, 64, 2) == 0
 
 
+def test_ganq_argument_errors():
+    lib = gq.library()
+    q = lambda **k: lib.ganq_quantize(
+        k.get("W", FAKE), k.get("wdt", 1), k.get("d_out", 64), k.get("d_in", 256),
+        k.get("F", FAKE), k.get("groups", 2), k.get("bits", 3), k.get("iters", 2),
+        k.get("opt", None), k.get("C", FAKE), k.get("P", FAKE), None, None, None,
+        k.get("ws", FAKE), k.get("wsb", 0), None)
+    assert q(F=None) == B.GQ_EINVAL
+    assert q(wdt=5) == B.GQ_EDTYPE
+    assert q(d_out=63) == B.GQ_ESHAPE
+    assert q(d_in=96) == B.GQ_ESHAPE and "64" in _err(lib)
+    assert q(bits=5) == B.GQ_EINVAL
+    assert q(iters=-1) == B.GQ_EINVAL
+    assert q(wsb=100) == B.GQ_EINVAL and "workspace" in _err(lib)
+    assert gq.ganq_workspace_size(64, 256, 2, 3) > gq.lnq_workspace_size(64, 256, 2, 3) + \
+        2 * 256 * 256 * 8
+    f = lambda **k: lib.ganq_factor_damped(k.get("F", FAKE), k.get("groups", 2),
+                                           k.get("d_in", 256), k.get("rho", 1e-6),
+                                           k.get("L", FAKE), None, k.get("ws", FAKE),
+                                           k.get("wsb", 0), None)
+    assert f(L=None) == B.GQ_EINVAL
+    assert f(d_in=100) == B.GQ_ESHAPE
+    assert f(rho=-1.0) == B.GQ_EINVAL
+    assert f(wsb=100) == B.GQ_EINVAL and "workspace" in _err(lib)
+
+
 def test_lut_argument_errors():
     lib = gq.library()
     assert gq.lut_packed_row_words(4096, 3) == 412        # 410 words of 10 codes, to 4k
@@ -194,5 +220,5 @@ def test_timing_read_empty():
     assert set(t) == {"group_scale", "fisher_mfma", "fisher_finalize", "fisher_plain",
                       "lnq_prepare", "lnq_resid", "lnq_init", "lnq_gram", "lnq_solve", "lnq_sweep",
                       "lnq_small", "fisher_pack", "lnq_delta", "lut_pack", "lut_gemv",
-                      "fisher_h2d"}
+                      "fisher_h2d", "ganq_chol", "ganq_pass"}
     assert all(v == (0.0, 0) for v in t.values())
