@@ -5,11 +5,13 @@ grouped Fisher accumulation from (X, G), then LNQ (init + `iters` x (codebook
 step, assignment pass) + objective trace) on every output row.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--path lnq|grid|lut|stream] [--no-cpu-baseline]
+                    [--path lnq|grid|ganq|lut|stream] [--no-cpu-baseline]
 
 --path grid replaces LNQ by the fixed-grid backend (uniform min-max grid per
 row, `iters` assignment passes, no codebook step) and reports that path's own
-metric.  --path lut times the lookup-table product y = W_hat x of the packed
+metric.  --path ganq replaces LNQ's assignment pass by the GANQ-style
+back-substitution over the Cholesky factor of F' (factor included in the step).
+--path lut times the lookup-table product y = W_hat x of the packed
 (C, P) format instead (default layer 28672 -> 8192, 4-bit, one bfloat16
 activation vector): a step is --lut-reps back-to-back products.  --path stream
 times the Fisher alone with X and G in pinned host memory, streamed to the GPU
@@ -42,6 +44,7 @@ PEAK_BF16_MFMA = 2500e12      # dense bf16 matrix-core FLOP/s
 PEAK_FP32_VALU = 157.3e12     # fp32 vector FLOP/s (FMA = 2 flops, packed)
 PEAK_HBM = 8e12               # bytes/s
 PEAK_FP32_ADD = 78.6e12       # fp32 vector adds/s (one add per lane per cycle)
+PEAK_FP64_VALU = 78.6e12      # fp64 vector FLOP/s (FMA = 2 flops)
 PEAK_PCIE = 63.0e9            # host-to-device bytes/s, PCIe 5.0 x16 (32 GT/s x 16, 128b/130b)
 
 
@@ -52,7 +55,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=None,
                     help="llama2_7b_attn by default; llama2_70b_down for --path lut")
-    ap.add_argument("--path", choices=("lnq", "grid", "lut", "stream"), default="lnq")
+    ap.add_argument("--path", choices=("lnq", "grid", "ganq", "lut", "stream"), default="lnq")
     ap.add_argument("--chunk-tokens", type=int, default=16384)
     ap.add_argument("--lut-reps", type=int, default=100)
     ap.add_argument("--lut-batch", type=int, default=1)
@@ -127,6 +130,25 @@ def _grid_roofline(wl, nchg, ms_step):
                          "passes_bytes": t_bytes * 1e3, "passes_alu": t_alu * 1e3}}
 
 
+def _ganq_roofline(wl, nchg, ms_step):
+    """Composite lower bound on one layer with the GANQ-style alternation: group scale and
+    Fisher as for LNQ; the float64 Cholesky of every group (G d_in^3 / 3 FMAs at the fp64
+    vector peak); per iteration the codebook systems as for LNQ and the back-substitution's
+    matrix-core product (3 bf16 products over the triangle, d_out d_in^2 flops each).
+    frac = t_roof / t_measured."""
+    n, d, d_out, G, m, it = wl.n, wl.d_in, wl.d_out, wl.groups, wl.m, wl.iters
+    t_scale = (2 * n * d_out + 4 * G * n) / PEAK_HBM
+    t_fisher = n * d * (d + 1) * G / PEAK_BF16_MFMA
+    t_chol = 2 * G * d ** 3 / 3 / PEAK_FP64_VALU
+    t_gram = it * max(d_out * d * d / PEAK_FP32_ADD, (4 * G * d * d + d_out * d) / PEAK_HBM)
+    t_back = it * 3 * d_out * d * d / PEAK_BF16_MFMA
+    t_roof = t_scale + t_fisher + t_chol + t_gram + t_back
+    return {"t_roof_ms": t_roof * 1e3, "t_measured_ms": ms_step, "frac": t_roof * 1e3 / ms_step,
+            "terms_ms": {"group_scale": t_scale * 1e3, "fisher": t_fisher * 1e3,
+                         "cholesky": t_chol * 1e3, "codebook_systems": t_gram * 1e3,
+                         "back_substitution": t_back * 1e3}}
+
+
 def _layer_roofline(wl, nchg, ms_step):
     """Composite lower bound on the time of one layer (Fisher + LNQ), term by term:
       group scale        bytes 2 n d_out + 4 G n at the HBM peak;
@@ -147,7 +169,7 @@ def _layer_roofline(wl, nchg, ms_step):
                          "codebook_systems": t_gram * 1e3, "residual_and_moves": t_upd * 1e3}}
 
 
-def _stage_units(stage, wl, nchg, grid=False):
+def _stage_units(stage, wl, nchg, grid=False, ganq=False):
     """Algorithmic work of a stage in one step: (bound, amount, peak, unit, launches).
 
     The contractions count the flops of the bf16 products the method runs: F' and the
@@ -159,7 +181,7 @@ def _stage_units(stage, wl, nchg, grid=False):
     once), or None when every launch does.
     """
     n, d, d_out, G, m, it = wl.n, wl.d_in, wl.d_out, wl.groups, wl.m, wl.iters
-    incr = [] if grid else _incremental_iters(wl, nchg)
+    incr = [] if (grid or ganq) else _incremental_iters(wl, nchg)
     dense = 0 if grid else it - len(incr)
     if stage == "fisher_mfma":
         # unique entries of the symmetric F_g: n d (d + 1) flops per group
@@ -168,10 +190,18 @@ def _stage_units(stage, wl, nchg, grid=False):
         ntile = (d + 255) // 256
         tri = sum(min(256, d - 256 * t) * (d - 256 * t) for t in range(ntile))
         return "mfma", dense * 2 * 2 * tri * d_out * m, PEAK_BF16_MFMA, "TFLOP/s", dense
+    if stage == "ganq_chol":
+        # float64 Cholesky of every group's F': d^3 / 3 FMAs per group
+        return "alu", 2 * G * d ** 3 / 3, PEAK_FP64_VALU, "TFLOP/s", None
+    if stage == "ganq_pass":
+        # the matrix-core part of the back-substitution: E U^T over the strict upper
+        # triangle of U = L^T as three bf16 products
+        return "mfma", it * 3 * 2 * d_out * d * d / 2, PEAK_BF16_MFMA, "TFLOP/s", None
     if stage == "lnq_resid":
         # before each recomputed codebook step, before each pass, and the final objective;
         # each E F' per group as three bf16 products (the fixed-grid path: before each
-        # pass and the final objective)
+        # pass and the final objective; GANQ: in each codebook step, after it, and the
+        # final objective)
         calls = dense + it + 1
         return "mfma", calls * 3 * 2 * d_out * d * d, PEAK_BF16_MFMA, "TFLOP/s", calls
     if stage == "lnq_delta":
@@ -248,8 +278,10 @@ def main():
     F = torch.empty((wl.groups, wl.d_in, wl.d_in), dtype=torch.float32, device=dev)
     ws_f = torch.empty(max(1, gq.fisher_workspace_size(wl.n, wl.d_in, wl.d_out, wl.groups)),
                        dtype=torch.uint8, device=dev)
-    ws_l = torch.empty(max(1, gq.lnq_workspace_size(wl.d_out, wl.d_in, wl.groups, wl.bits)),
-                       dtype=torch.uint8, device=dev)
+    ganq = args.path == "ganq"
+    ws_size = (gq.ganq_workspace_size if ganq else gq.lnq_workspace_size)(
+        wl.d_out, wl.d_in, wl.groups, wl.bits)
+    ws_l = torch.empty(max(1, ws_size), dtype=torch.uint8, device=dev)
     C = torch.empty((wl.d_out, wl.m), dtype=torch.float32, device=dev)
     P = torch.empty((wl.d_out, wl.d_in), dtype=torch.uint8, device=dev)
 
@@ -260,6 +292,9 @@ def main():
         if grid:
             return gq.grid_quantize(W, F, wl.bits, wl.iters, block=64, ridge_rel=1e-6, C=C,
                                     P=P, init=gq.GQ_INIT_UNIFORM, ws=ws_l)
+        if ganq:
+            return gq.ganq_quantize(W, F, wl.bits, wl.iters, ridge_rel=1e-6, C=C, P=P,
+                                    init=gq.GQ_INIT_QUANTILE, ws=ws_l)
         return gq.lnq_quantize(W, F, wl.bits, wl.iters, block=64, ridge_rel=1e-6, C=C,
                                P=P, init=gq.GQ_INIT_QUANTILE, ws=ws_l)
 
@@ -304,7 +339,7 @@ def main():
     # roofline of the stage with the largest share of the step, from the events of
     # the timed region
     roof = None
-    spec = _stage_units(dom, wl, nchg, grid)
+    spec = _stage_units(dom, wl, nchg, grid, ganq)
     if spec is not None and timed[dom][1]:
         bound, amount, peak, unit, working = spec
         n_launch = timed[dom][1] / args.steps if working is None else working
@@ -321,6 +356,8 @@ def main():
 
     metric = ("Fixed-grid GuidedQuant rows quantized/s (Fisher + uniform grid + assignment "
               f"passes) at {wl.d_in}x{wl.d_out}, {wl.bits}-bit, 1 MI355X" if grid else
+              "GANQ-style rows quantized/s (Fisher + Cholesky + codebook / back-substitution "
+              f"alternation) at {wl.d_in}x{wl.d_out}, {wl.bits}-bit, 1 MI355X" if ganq else
               "LNQ rows quantized/s + Fisher TFLOP/s at 4096x4096, 3-bit, 1 MI355X")
     result = {
         "metric": metric,
@@ -347,10 +384,11 @@ def main():
         "stage_launches_per_step": launches,
         "stage_breakdown_from": "last warmup step, every stage bracketed by HIP events",
         "changed_per_sweep": [int(x) for x in nchg],
-        "codebook_steps_from_changes": [] if grid else _incremental_iters(wl, nchg),
+        "codebook_steps_from_changes": [] if (grid or ganq) else _incremental_iters(wl, nchg),
         "objective_trace": [float(x) for x in trace],
         "monotone": bool(np.all(trace[1:] <= trace[:-1] * (1 + 1e-6))),
-        "layer_roofline": (_grid_roofline if grid else _layer_roofline)(wl, nchg, ms_step),
+        "layer_roofline": (_grid_roofline if grid else _ganq_roofline if ganq else
+                           _layer_roofline)(wl, nchg, ms_step),
         "roofline": roof,
     }
 
@@ -534,7 +572,7 @@ def cpu_baseline(wl, inp, F, args):
     rpg = wl.d_out // wl.groups
     rows = [(r * rpg) % wl.d_out for r in range(args.cpu_rows)]
     t_rows = 0.0
-    row_fn = O.grid_row if args.path == "grid" else O.lnq_row
+    row_fn = {"grid": O.grid_row, "ganq": O.ganq_row}.get(args.path, O.lnq_row)
     for j in rows:
         Fp = O.damped(F64[j // rpg], 1e-6)
         t0 = time.perf_counter()
@@ -545,7 +583,7 @@ def cpu_baseline(wl, inp, F, args):
     return {"value": wl.d_out / t_layer, "unit": "rows/s", "cores": blas_threads,
             "kind": "oracle",
             "sample": f"Fisher on the first {nt} of {wl.n} tokens (scaled x{wl.n / nt:g}, "
-                      f"{t_f * nt / wl.n:.1f}s measured) + {'fixed-grid passes' if args.path == 'grid' else 'LNQ'} on {len(rows)} rows "
+                      f"{t_f * nt / wl.n:.1f}s measured) + {args.path} on {len(rows)} rows "
                       f"({t_row:.2f}s/row, scaled to {wl.d_out} rows); LNQ rows run on one "
                       f"core, the Fisher matmul on {blas_threads} BLAS threads",
             "fisher_s_est": t_f, "lnq_s_per_row": t_row}
