@@ -47,54 +47,96 @@ __global__ __launch_bounds__(256) void k_chol_init(const float* __restrict__ F,
     A[(size_t)g * d * d + e] = (j <= i) ? (double)Fg[e] + (i == j ? lam[g] : 0.0) : 0.0;
 }
 
-// One block per group factors diagonal block p in LDS and writes L_pp (lower) back to A
-// and its inverse to Linv [groups][64][64].  A pivot that is not positive (F' singular,
-// e.g. a group whose gradients vanish) marks the group in `bad` and is replaced by 1 so
-// the rest of the factorization stays finite; a marked group's codes are left as they are.
+// One block per group factors diagonal block p and writes L_pp (lower) back to A and
+// its inverse to Linv [groups][64][64].  Thread (ti, tj) of a 16 x 16 grid keeps
+// a[ti + 16 u][tj + 16 v] (u, v < 4) in registers; at step c the owner of (c, c) takes
+// the pivot, the owners of column c scale it by 1 / L_cc and publish it in LDS, and
+// every thread updates its elements with c < j <= i.  A pivot that is not positive (F'
+// singular, e.g. a group whose gradients vanish) marks the group in `bad` and is replaced
+// by 1 so the rest of the factorization stays finite; a marked group's codes are left as
+// they are.
 __global__ __launch_bounds__(256) void k_chol_diag(double* __restrict__ A, int64_t d, int p,
                                                   double* __restrict__ Linv,
                                                   int* __restrict__ bad) {
     __shared__ double a[CB][CB + 1];
     __shared__ double x[CB][CB + 1];
+    __shared__ double col[CB];            // column c of L below the diagonal, at step c
+    __shared__ double rpiv[CB];           // 1 / L_cc
     const int g = blockIdx.x;
     const int tid = threadIdx.x;
     double* Ag = A + (size_t)g * d * d;
     const int64_t o = (int64_t)p * CB;
-    for (int e = tid; e < CB * CB; e += 256) {
-        const int i = e / CB, j = e % CB;
-        a[i][j] = (j <= i) ? Ag[(o + i) * d + o + j] : 0.0;
-        x[i][j] = 0.0;
-    }
-    __syncthreads();
+    const int ti = tid >> 4, tj = tid & 15;
+    double r[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = ti + 16 * u, j = tj + 16 * v;
+            r[u][v] = (j <= i) ? Ag[(o + i) * d + o + j] : 0.0;
+        }
     for (int c = 0; c < CB; ++c) {
-        if (tid == 0) {
-            double piv = a[c][c];
-            if (!(piv > 0.0)) {
+        const int cu = c >> 4, cr = c & 15;
+        if (ti == cr && tj == cr) {
+            double pv = r[cu][cu];
+            if (!(pv > 0.0)) {
                 bad[g] = 1;
-                piv = 1.0;
+                pv = 1.0;
             }
-            a[c][c] = sqrt(piv);
+            pv = sqrt(pv);
+            r[cu][cu] = pv;
+            rpiv[c] = 1.0 / pv;
         }
         __syncthreads();
-        for (int i = c + 1 + tid; i < CB; i += 256) a[i][c] = a[i][c] / a[c][c];
-        __syncthreads();
-        // trailing update of the lower triangle: pairs (i, j), c < j <= i < CB
-        const int n = CB - 1 - c;
-        for (int e = tid; e < n * n; e += 256) {
-            const int i = c + 1 + e / n, j = c + 1 + e % n;
-            if (j <= i) a[i][j] -= a[i][c] * a[j][c];
+        if (tj == cr) {
+            const double rp = rpiv[c];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = ti + 16 * u;
+                if (i > c) {
+                    r[u][cu] = r[u][cu] * rp;
+                    col[i] = r[u][cu];
+                }
+            }
         }
         __syncthreads();
+        double ci[4], cj[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ci[u] = col[ti + 16 * u];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) cj[v] = col[tj + 16 * v];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = ti + 16 * u, j = tj + 16 * v;
+                if (j > c && j <= i) r[u][v] = fma(-ci[u], cj[v], r[u][v]);
+            }
+        // col is rewritten at step c + 1 only after that step's first barrier
     }
-    // inverse of the lower-triangular block, one column per thread:
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            a[ti + 16 * u][tj + 16 * v] = r[u][v];
+            x[ti + 16 * u][tj + 16 * v] = 0.0;
+        }
+    __syncthreads();
+    // inverse of the lower-triangular block, column c by the four adjacent lanes
+    // 4c .. 4c + 3 (lane q of the four takes k = c + q, c + q + 4, ...; the four partial
+    // sums are combined across the lanes):
     // X_cc = 1 / L_cc,  X_ic = -(sum_{k=c}^{i-1} L_ik X_kc) / L_ii
-    if (tid < CB) {
-        const int c = tid;
-        x[c][c] = 1.0 / a[c][c];
+    {
+        const int c = tid >> 2, q = tid & 3;
+        if (q == 0) x[c][c] = 1.0 / a[c][c];
         for (int i = c + 1; i < CB; ++i) {
             double s = 0.0;
-            for (int k = c; k < i; ++k) s += a[i][k] * x[k][c];
-            x[i][c] = -s / a[i][i];
+            for (int k = c + q; k < i; k += 4) s += a[i][k] * x[k][c];
+            s += __shfl_xor(s, 1, 64);
+            s += __shfl_xor(s, 2, 64);
+            if (q == 0) x[i][c] = -s / a[i][i];
+            // the four lanes of column c read x[i][c] in the next row: the write above
+            // and those reads come from one wave, in order
         }
     }
     __syncthreads();
@@ -300,7 +342,12 @@ __global__ __launch_bounds__(1024, 1) void k_ganq(
     };
     float cq[M];
 #pragma unroll
-    for (int q = 0; q < M; ++q) cq[q] = rvalid ? C[j * M + q] : 0.f;
+    for (int q = 0; q < M; ++q) {
+        cq[q] = rvalid ? C[j * M + q] : 0.f;
+        // keep the codebook in vector registers: the nearest-entry scan selects from it
+        // with v_cndmask, which takes its second operand from a vector register
+        asm volatile("" : "+v"(cq[q]));
+    }
     unsigned moves = 0;
     const int ko = 8 * (lane >> 4);
     const int mrow = lane & 15;
@@ -346,23 +393,20 @@ __global__ __launch_bounds__(1024, 1) void k_ganq(
 #pragma unroll
                 for (int k = 0; k < 4; ++k) s += corr_p[k][wave][lane];
                 const float wv = load_elem<WBF16>(W, j * d + col);
-                const float u = ldiag[lane];
+                const float inv_u = 1.f / ldiag[lane];
                 const int old = P[j * d + col];
                 int code = 0;
                 for (int t = GQ_SUB - 1; t >= 0; --t) {
                     // lane t's entry: nearest to w - s / L_tt (lowest index on ties)
-                    const float tgt = wv - s / u;
-                    float best = fabsf(tgt - cq[0]);
+                    const float tgt = fmaf(-s, inv_u, wv);
+                    float best = fabsf(tgt - cq[0]), bc = cq[0];
                     int bq = 0;
 #pragma unroll
                     for (int q = 1; q < M; ++q) {
                         const float dq = fabsf(tgt - cq[q]);
-                        if (dq < best) { best = dq; bq = q; }
+                        if (dq < best) { best = dq; bq = q; bc = cq[q]; }
                     }
-                    float en = cq[0];
-#pragma unroll
-                    for (int q = 1; q < M; ++q) en = (bq == q) ? cq[q] : en;
-                    en -= wv;
+                    const float en = bc - wv;
                     const float et = ganq_readlane_f(en, t);
                     if (lane == t) { code = bq; ev = en; }
                     s = fmaf(lb[t][lane], et, s);     // lanes i < t: s_i += L[t][i] e_t
