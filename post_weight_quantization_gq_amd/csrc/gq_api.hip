@@ -425,12 +425,9 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
                                        w.cnt + 1, incremental ? w.cnt + 2 : nullptr, st)) !=
             hipSuccess)
             return hip_fail(e, "codebook");
-        // the codes before the pass, for the next step's update
-        if (incremental && t < iters &&
-            (e = hipMemcpyAsync(w.pprev, P, (size_t)d_out * d_in, hipMemcpyDeviceToDevice, st)) !=
-                hipSuccess)
-            return hip_fail(e, "code copy");
-        // assignment pass; objB = objective after the codebook step (entry 2t-1), from scratch
+        // assignment pass; objB = objective after the codebook step (entry 2t-1), from
+        // scratch; when recording, it also keeps the codes before it for the next step's
+        // update
         if ((e = gq::lnq_sweep_step(o.block, F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB,
                                     w.objC, w.cnt, incremental && t < iters, st)) != hipSuccess)
             return hip_fail(e, "sweep");

@@ -638,7 +638,9 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
 //     of 64 dependent steps, with the same decisions and the same arithmetic.
 //   * The row objective e.r at the start of the pass is summed (float64) before
 //     any update; the objective after it adds the accepted changes.
-//   The residual array R is updated in place (it is workspace).
+//   The residual array R is updated in place (it is workspace).  When recording (for a
+//   codebook step updated from the moved coordinates) the pass also writes its moves
+//   (clist, ccount) and the codes as they were before it (pprev).
 // ---------------------------------------------------------------------------
 constexpr int SW_ROWS = 16;     // rows (= waves) per block
 constexpr int SW_SUB = 64;      // coordinates per chain block (one per lane)
@@ -681,7 +683,7 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
     const float* __restrict__ C, int m, uint8_t* __restrict__ P, const void* __restrict__ W,
     float* __restrict__ R, double* __restrict__ obj_start, double* __restrict__ obj_end,
     unsigned long long* __restrict__ n_changed, uint32_t* __restrict__ clist,
-    int* __restrict__ ccount) {
+    int* __restrict__ ccount, uint8_t* __restrict__ pprev) {
     __shared__ __attribute__((aligned(16))) uint16_t dsb_hi[SW_ROWS][SW_DP];   // 16.3 KB
     __shared__ __attribute__((aligned(16))) uint16_t dsb_lo[SW_ROWS][SW_DP];   // 16.3 KB
     __shared__ float corr_p[4][SW_ROWS][SW_SUB];                               // 16 KB
@@ -782,6 +784,7 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
 #pragma unroll
                 for (int k = 0; k < 4; ++k) r += corr_p[k][wave][lane];
                 int code = P[j * d + col];
+                if (pprev) pprev[j * d + col] = (uint8_t)code;   // the code before the pass
                 float wh = __shfl(cl, code, 64);
                 const float wh0 = wh;
                 const float fdiag = fdd[lane];            // F'[col][col]
@@ -1485,7 +1488,8 @@ static hipError_t launch_sweep(const float* F, const void* W, int64_t d_out, int
                                                                          : k_sweep<WB, 16>;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(1024), 0, st, F, w.dF, w.fhi,
                        w.flo, d, rpg, wgs, total, C, m, P, W, w.R, obj_start, obj_end, counter,
-                       record ? w.clist : nullptr, record ? w.ccount : nullptr);
+                       record ? w.clist : nullptr, record ? w.ccount : nullptr,
+                       record ? w.pprev : nullptr);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }
