@@ -78,12 +78,12 @@ _CSRC = os.path.join(ROOT, "post_weight_quantization_gq_amd", "csrc")
 _TRAFFIC = {
     # stage: (workload, source file, digest, bytes read, bytes written) of its main kernel,
     # averaged over the launches that do the work
-    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "cf26376348bd061a", 269416178, 16777216),
-    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "4f32b7880a60cc1d", 16796171389, 1140850688),
-    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "f6c039f94e59cf18", 759671762, 254990306),
-    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "cf26376348bd061a", 604188042, 67108864),
-    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "f6c039f94e59cf18", 1880225299, 85658867),
-    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "6af0965646e0e749", 118503969, 48253),
+    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "cf26376348bd061a", 269411071, 16777216),
+    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "4f32b7880a60cc1d", 16843666162, 1140850688),
+    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "ebbacca8a3e52d0f", 755435218, 270175408),
+    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "cf26376348bd061a", 604188214, 67108864),
+    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "ebbacca8a3e52d0f", 1879307807, 85658099),
+    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "be331b4ec2c19da1", 118506667, 47501),
 }
 
 
