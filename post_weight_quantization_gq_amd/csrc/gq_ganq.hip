@@ -22,10 +22,13 @@
 //                      cores, S[:, :sb] += E_sb U[:sb, sb]^T (three bf16 products);
 //                    * s from later 64-blocks of the same super-block: the same product
 //                      before each block;
-//                    * inside a block, 64 dependent steps: lane t takes its entry, and
+//                    * inside a block, 64 dependent steps: lane t takes its entry (a
+//                      binary search over the midpoints of the sorted codebook), and
 //                      every lane i < t adds L[t][i] e_t (the block of L staged in LDS).
 #include "gq_common.h"
 #include "gq_internal.h"
+
+#include <utility>
 
 namespace gq {
 
@@ -290,6 +293,61 @@ __device__ __forceinline__ float ganq_readlane_f(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// The row's codebook in ascending order (equal values keep their index order) and the
+// midpoints between neighbours.  For ascending a <= b, b is nearer to x than a exactly
+// when x > (a + b) / 2.  Entries are placed by rank, so every register index is a
+// compile-time constant.
+template <int M>
+__device__ __forceinline__ void ganq_sorted_codebook(const float (&cq)[M], float (&sv)[M],
+                                                     float (&mid)[M - 1]) {
+    int rank[M];
+#pragma unroll
+    for (int q = 0; q < M; ++q) {
+        rank[q] = 0;
+#pragma unroll
+        for (int p = 0; p < M; ++p)
+            rank[q] += (cq[p] < cq[q] || (cq[p] == cq[q] && p < q)) ? 1 : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+        sv[r] = 0.f;
+#pragma unroll
+        for (int q = 0; q < M; ++q) sv[r] = (rank[q] == r) ? cq[q] : sv[r];
+    }
+#pragma unroll
+    for (int k = 0; k < M - 1; ++k) mid[k] = 0.5f * sv[k] + 0.5f * sv[k + 1];
+}
+
+// The entry nearest to x: a binary search over the midpoints.  Each level compares x
+// with the middle midpoint and keeps the upper or lower half of the candidate values and
+// midpoints with selects (log2 N compares).  At a midpoint itself the lower entry.  The
+// halves are built from index packs so that no register array is indexed by a variable.
+template <int N>
+struct GanqNearest {
+    template <int... K, int... J>
+    static __device__ __forceinline__ float level(float x, const float (&v)[N],
+                                                  const float (&b)[N - 1],
+                                                  std::integer_sequence<int, K...>,
+                                                  std::integer_sequence<int, J...>) {
+        constexpr int H = N / 2;
+        const bool up = x > b[H - 1];
+        const float v2[H] = {(up ? v[K + H] : v[K])...};
+        const float b2[H - 1] = {(up ? b[J + H] : b[J])...};
+        return GanqNearest<H>::run(x, v2, b2);
+    }
+    static __device__ __forceinline__ float run(float x, const float (&v)[N],
+                                                const float (&b)[N - 1]) {
+        return level(x, v, b, std::make_integer_sequence<int, N / 2>{},
+                     std::make_integer_sequence<int, N / 2 - 1>{});
+    }
+};
+template <>
+struct GanqNearest<2> {
+    static __device__ __forceinline__ float run(float x, const float (&v)[2], const float (&b)[1]) {
+        return x > b[0] ? v[1] : v[0];
+    }
+};
+
 __global__ void k_zero_f32(float* __restrict__ p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = 0.f;
@@ -348,6 +406,8 @@ __global__ __launch_bounds__(1024, 1) void k_ganq(
         // with v_cndmask, which takes its second operand from a vector register
         asm volatile("" : "+v"(cq[q]));
     }
+    float sv[M], mid[M - 1];
+    ganq_sorted_codebook<M>(cq, sv, mid);
     unsigned moves = 0;
     const int ko = 8 * (lane >> 4);
     const int mrow = lane & 15;
@@ -395,22 +455,22 @@ __global__ __launch_bounds__(1024, 1) void k_ganq(
                 const float wv = load_elem<WBF16>(W, j * d + col);
                 const float inv_u = 1.f / ldiag[lane];
                 const int old = P[j * d + col];
-                int code = 0;
-                for (int t = GQ_SUB - 1; t >= 0; --t) {
-                    // lane t's entry: nearest to w - s / L_tt (lowest index on ties)
-                    const float tgt = fmaf(-s, inv_u, wv);
-                    float best = fabsf(tgt - cq[0]), bc = cq[0];
-                    int bq = 0;
+                // step t: lane t's entry, nearest to w - s / L_tt, then lanes i < t add
+                // L[t][i] e_t (lb[t][i] = 0 for i >= t).  A lane's s is final from its
+                // own step on.
 #pragma unroll
-                    for (int q = 1; q < M; ++q) {
-                        const float dq = fabsf(tgt - cq[q]);
-                        if (dq < best) { best = dq; bq = q; bc = cq[q]; }
-                    }
-                    const float en = bc - wv;
-                    const float et = ganq_readlane_f(en, t);
-                    if (lane == t) { code = bq; ev = en; }
-                    s = fmaf(lb[t][lane], et, s);     // lanes i < t: s_i += L[t][i] e_t
+                for (int t = GQ_SUB - 1; t >= 0; --t) {
+                    const float bc = GanqNearest<M>::run(fmaf(-s, inv_u, wv), sv, mid);
+                    s = fmaf(lb[t][lane], ganq_readlane_f(bc - wv, t), s);
                 }
+                // every lane's own entry, from its final s: the same arithmetic as at its step
+                const float bsel = GanqNearest<M>::run(fmaf(-s, inv_u, wv), sv, mid);
+                ev = bsel - wv;
+                // its code: the lowest index holding the chosen value
+                int code = 0;
+#pragma unroll
+                for (int q = M - 1; q >= 0; --q)
+                    if (cq[q] == bsel) code = q;
                 P[j * d + col] = (uint8_t)code;
                 const unsigned long long chg = __ballot(code != old);
                 moves += (unsigned)__popcll(chg);
