@@ -196,18 +196,26 @@ __global__ __launch_bounds__(256) void k_chol_panel(double* __restrict__ A, int6
     }
 }
 
-// Trailing update after panel p: tiles (ti, tj), p < tj <= ti < nt, of the lower
-// triangle: A[ti][tj] -= L[ti][p] L[tj][p]^T.  Linear tile index t over the triangle.
+// Trailing update after panel p: tiles (ti, tj), tj <= ti, of the lower triangle
+// (counted from tile p + 1): A[ti][tj] -= L[ti][p] L[tj][p]^T.  `part` 1 takes the
+// next panel's column (tj = 0, one tile per block), `part` 2 the rest (tj >= 1, a
+// linear index over that triangle).
 __global__ __launch_bounds__(256) void k_chol_update(double* __restrict__ A, int64_t d, int p,
-                                                    int nt) {
+                                                    int part) {
     __shared__ double li[CB][CB + 1];
     __shared__ double lj[CB][CB + 1];
     const int g = blockIdx.y;
     const int tid = threadIdx.x;
-    // t -> (ti, tj) with tj <= ti, both counted from p + 1
-    int t = blockIdx.x, ti = 0;
-    while (t > ti) { t -= ti + 1; ++ti; }
-    const int tj = t;
+    int ti, tj;
+    if (part == 1) {
+        ti = blockIdx.x;
+        tj = 0;
+    } else {
+        int t = blockIdx.x, r = 0;
+        while (t > r) { t -= r + 1; ++r; }
+        ti = r + 1;
+        tj = t + 1;
+    }
     const int64_t oi = (int64_t)(p + 1 + ti) * CB, oj = (int64_t)(p + 1 + tj) * CB;
     const int64_t o = (int64_t)p * CB;
     double* Ag = A + (size_t)g * d * d;
@@ -234,7 +242,6 @@ __global__ __launch_bounds__(256) void k_chol_update(double* __restrict__ A, int
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[u][v] = fma(av[u], bv[v], acc[u][v]);
     }
-    (void)nt;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -532,6 +539,13 @@ GanqWs ganq_carve(void* base, int64_t d, int groups) {
     return w;
 }
 
+// The factorization with one panel of lookahead.  Per panel p, on the caller's stream:
+// the diagonal block and the panel, then the part of the trailing update that the next
+// panel needs (its column); on a second stream, once panel p is done, the rest of the
+// trailing update.  The next diagonal block and panel thus run beside the bulk of the
+// update.  Ordering: the column update of panel p waits for the rest-update of panel
+// p - 1 (both write tile column p + 1 and later); the rest-update of panel p writes
+// columns p + 2 on, which the next diagonal block and panel do not touch.
 hipError_t ganq_factor(const float* F, const double* lam, int64_t d, int groups, const GanqWs& w,
                        hipStream_t st) {
     StageTimer tm(ST_GANQ_CHOL, st);
@@ -541,20 +555,42 @@ hipError_t ganq_factor(const float* F, const double* lam, int64_t d, int groups,
         GQ_LAUNCH_CHECK();
     }
     const int nt = (int)(d / CB);               // d % 64 == 0
-    for (int p = 0; p < nt; ++p) {
+    hipStream_t side = nullptr;
+    hipEvent_t panel_done = nullptr, rest_done = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&panel_done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&rest_done, hipEventDisableTiming);
+    bool rest_recorded = false;
+    for (int p = 0; p < nt && e == hipSuccess; ++p) {
         hipLaunchKernelGGL(k_chol_diag, dim3((unsigned)groups), dim3(256), 0, st, w.A, d, p, w.Linv,
                            w.bad);
-        GQ_LAUNCH_CHECK();
+        if ((e = hipGetLastError()) != hipSuccess) break;
         const int rest = nt - p - 1;
         if (rest == 0) break;
         hipLaunchKernelGGL(k_chol_panel, dim3((unsigned)rest, (unsigned)groups), dim3(256), 0, st,
                            w.A, d, p, w.Linv);
-        GQ_LAUNCH_CHECK();
-        const int ntri = rest * (rest + 1) / 2;
-        hipLaunchKernelGGL(k_chol_update, dim3((unsigned)ntri, (unsigned)groups), dim3(256), 0, st,
-                           w.A, d, p, nt);
-        GQ_LAUNCH_CHECK();
+        if ((e = hipGetLastError()) != hipSuccess) break;
+        if ((e = hipEventRecord(panel_done, st)) != hipSuccess) break;
+        if (rest_recorded && (e = hipStreamWaitEvent(st, rest_done, 0)) != hipSuccess) break;
+        hipLaunchKernelGGL(k_chol_update, dim3((unsigned)rest, (unsigned)groups), dim3(256), 0, st,
+                           w.A, d, p, 1);
+        if ((e = hipGetLastError()) != hipSuccess) break;
+        if (rest > 1) {
+            if ((e = hipStreamWaitEvent(side, panel_done, 0)) != hipSuccess) break;
+            const int ntri = (rest - 1) * rest / 2;
+            hipLaunchKernelGGL(k_chol_update, dim3((unsigned)ntri, (unsigned)groups), dim3(256), 0,
+                               side, w.A, d, p, 2);
+            if ((e = hipGetLastError()) != hipSuccess) break;
+            if ((e = hipEventRecord(rest_done, side)) != hipSuccess) break;
+            rest_recorded = true;
+        }
     }
+    // the caller's stream resumes after the side stream's last update
+    if (e == hipSuccess && rest_recorded) e = hipStreamWaitEvent(st, rest_done, 0);
+    if (panel_done) (void)hipEventDestroy(panel_done);
+    if (rest_done) (void)hipEventDestroy(rest_done);
+    if (side) (void)hipStreamDestroy(side);
+    if (e != hipSuccess) return e;
     const int64_t a_pad = lnq_pad256(d);
     const dim3 grid((unsigned)(((d / 16) * a_pad + 255) / 256), (unsigned)groups);
     hipLaunchKernelGGL(k_ganq_prep, grid, dim3(256), 0, st, w.A, d, a_pad, w.uhi, w.ulo, w.dL);
