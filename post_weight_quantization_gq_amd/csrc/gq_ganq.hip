@@ -50,6 +50,14 @@ __global__ __launch_bounds__(256) void k_chol_init(const float* __restrict__ F,
     A[(size_t)g * d * d + e] = (j <= i) ? (double)Fg[e] + (i == j ? lam[g] : 0.0) : 0.0;
 }
 
+// v from the lane given by a quad permutation (all four lanes of a quad active)
+template <int CTRL>
+__device__ __forceinline__ double quad_dpp_f64(double v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+
 // One block per group factors diagonal block p and writes L_pp (lower) back to A and
 // its inverse to Linv [groups][64][64].  Thread (ti, tj) of a 16 x 16 grid keeps
 // a[ti + 16 u][tj + 16 v] (u, v < 4) in registers; at step c the owner of (c, c) takes
@@ -70,6 +78,7 @@ __global__ __launch_bounds__(256) void k_chol_diag(double* __restrict__ A, int64
     double* Ag = A + (size_t)g * d * d;
     const int64_t o = (int64_t)p * CB;
     const int ti = tid >> 4, tj = tid & 15;
+    if (tid < CB) col[tid] = 0.0;         // finite before any step reads it
     double r[4][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -103,18 +112,21 @@ __global__ __launch_bounds__(256) void k_chol_diag(double* __restrict__ A, int64
             }
         }
         __syncthreads();
+        // every column j > c takes the update, without branches: the entries above the
+        // diagonal that this also changes are never read or stored; finished columns
+        // (j <= c) see a zero factor
         double ci[4], cj[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) ci[u] = col[ti + 16 * u];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) cj[v] = col[tj + 16 * v];
+        for (int v = 0; v < 4; ++v) {
+            const double cv = col[tj + 16 * v];
+            cj[v] = (tj + 16 * v > c) ? cv : 0.0;
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int i = ti + 16 * u, j = tj + 16 * v;
-                if (j > c && j <= i) r[u][v] = fma(-ci[u], cj[v], r[u][v]);
-            }
+            for (int v = 0; v < 4; ++v) r[u][v] = fma(-ci[u], cj[v], r[u][v]);
         // col is rewritten at step c + 1 only after that step's first barrier
     }
 #pragma unroll
@@ -127,17 +139,18 @@ __global__ __launch_bounds__(256) void k_chol_diag(double* __restrict__ A, int64
     __syncthreads();
     // inverse of the lower-triangular block, column c by the four adjacent lanes
     // 4c .. 4c + 3 (lane q of the four takes k = c + q, c + q + 4, ...; the four partial
-    // sums are combined across the lanes):
-    // X_cc = 1 / L_cc,  X_ic = -(sum_{k=c}^{i-1} L_ik X_kc) / L_ii
+    // sums are combined across the quad with DPP moves):
+    // X_cc = 1 / L_cc,  X_ic = -(sum_{k=c}^{i-1} L_ik X_kc) / L_ii, the division as a
+    // product with the pivot reciprocal kept from the factorization
     {
         const int c = tid >> 2, q = tid & 3;
-        if (q == 0) x[c][c] = 1.0 / a[c][c];
+        if (q == 0) x[c][c] = rpiv[c];
         for (int i = c + 1; i < CB; ++i) {
             double s = 0.0;
             for (int k = c + q; k < i; k += 4) s += a[i][k] * x[k][c];
-            s += __shfl_xor(s, 1, 64);
-            s += __shfl_xor(s, 2, 64);
-            if (q == 0) x[i][c] = -s / a[i][i];
+            s += quad_dpp_f64<0xB1>(s);       // quad_perm [1,0,3,2]
+            s += quad_dpp_f64<0x4E>(s);       // quad_perm [2,3,0,1]
+            if (q == 0) x[i][c] = -s * rpiv[i];
             // the four lanes of column c read x[i][c] in the next row: the write above
             // and those reads come from one wave, in order
         }
