@@ -28,7 +28,7 @@
 
 namespace gq {
 
-constexpr int LUT_WAVES = 8;          // waves per block of the GEMV
+constexpr int LUT_WAVES = 8;          // waves per block of the GEMV (16 where one block fits)
 constexpr int LUT_UNROLL = 8;         // code words in flight per lane
 constexpr int LUT_SPAN = 64 * LUT_UNROLL;   // words per chunk of a row
 
@@ -76,9 +76,9 @@ __host__ __device__ inline int64_t lut_staged_words(int64_t rw) { return rw + 1;
 
 // LDS: one table of M * M words per wave (wave w's at w * M * M, so a table index is
 // or-ed onto its base), then x pairs [B][staged words * XST].  Rows: block r takes rows
-// r * rows_per_block .. + rows_per_block - 1, wave w every LUT_WAVES-th.
-template <int BITS, int B>
-__global__ __launch_bounds__(64 * LUT_WAVES) void k_lut_gemv_bf16(
+// r * rows_per_block .. + rows_per_block - 1, wave w every WAVES-th.
+template <int BITS, int B, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_lut_gemv_bf16(
     const uint32_t* __restrict__ Q, int64_t rw, const float* __restrict__ C, int64_t d_out,
     int64_t d_in, const uint16_t* __restrict__ x, int whole_pairs, int rows_per_block,
     float* __restrict__ y) {
@@ -88,23 +88,23 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void k_lut_gemv_bf16(
     constexpr uint32_t PMASK = (uint32_t)(M * M - 1);
     extern __shared__ uint32_t lut_lds[];
     const int64_t xwords = lut_staged_words(rw) * XST;
-    uint32_t* const xlds = lut_lds + LUT_WAVES * M * M;
+    uint32_t* const xlds = lut_lds + WAVES * M * M;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint32_t* tab = lut_lds + wave * (M * M);
     const uint32_t tab_bytes = (uint32_t)(wave * M * M) * 4u;
 
-    // Work of a wave: its rows (every LUT_WAVES-th of the block's), each in chunks of
+    // Work of a wave: its rows (every WAVES-th of the block's), each in chunks of
     // LUT_SPAN words; item t = (row k, chunk c).  The codes (and, at a row's start, the
     // codebook) of item t + 1 are loaded while item t is computed.
     const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
     int nrows = 0;
-    for (int rr = wave; rr < rows_per_block && r0 + rr < d_out; rr += LUT_WAVES) ++nrows;
+    for (int rr = wave; rr < rows_per_block && r0 + rr < d_out; rr += WAVES) ++nrows;
     const int nch = (int)((rw + LUT_SPAN - 1) / LUT_SPAN);
     const int nitems = nrows * nch;
     auto fetch = [&](int t, uint32_t (&wv)[LUT_UNROLL], float& cv) {
         const int k = t / nch, c = t - k * nch;
-        const int64_t j = r0 + wave + (int64_t)LUT_WAVES * k;
+        const int64_t j = r0 + wave + (int64_t)WAVES * k;
         const uint32_t* Qj = Q + j * rw;
         const int w0 = c * LUT_SPAN + lane;
         if ((int64_t)(c + 1) * LUT_SPAN <= rw) {
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void k_lut_gemv_bf16(
     for (int b = 0; b < B; ++b) {
         const uint16_t* xb = x + (int64_t)b * d_in;
         uint32_t* xs = xlds + (int64_t)b * xwords;
-        for (int64_t pr = tid; pr < npairs; pr += 64 * LUT_WAVES) {
+        for (int64_t pr = tid; pr < npairs; pr += 64 * WAVES) {
             uint32_t v;
             if (even) {
                 v = pr < dpairs ? ((const uint32_t*)xb)[pr] : 0u;
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void k_lut_gemv_bf16(
             }
         }
         if (c == nch - 1) {
-            const int64_t j = r0 + wave + (int64_t)LUT_WAVES * k;
+            const int64_t j = r0 + wave + (int64_t)WAVES * k;
 #pragma unroll
             for (int b = 0; b < B; ++b) {
                 const float s = wave_sum_f32(acc[0][b] + acc[1][b]);
@@ -268,33 +268,56 @@ hipError_t lut_pack_run(const uint8_t* P, int64_t d_out, int64_t d_in, int bits,
     return hipSuccess;
 }
 
-size_t lut_gemv_lds_bytes(int64_t d_in, int bits, int batch) {
+static size_t lut_lds_bytes(int64_t d_in, int bits, int batch, int waves) {
     const int64_t rw = lut_row_words(d_in, bits);
     const int m = 1 << bits;
-    return (size_t)(batch * lut_staged_words(rw) * lut_xst(bits) + LUT_WAVES * m * m) * 4;
+    return (size_t)(batch * lut_staged_words(rw) * lut_xst(bits) + waves * m * m) * 4;
 }
 
-template <int BITS, int B>
-static hipError_t launch_bf16(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in,
-                              const uint16_t* x, float* y, hipStream_t st) {
+// the LDS the 8-wave form needs: above 160 KiB no form fits
+size_t lut_gemv_lds_bytes(int64_t d_in, int bits, int batch) {
+    return lut_lds_bytes(d_in, bits, batch, LUT_WAVES);
+}
+
+template <int BITS, int B, int WAVES>
+static hipError_t launch_bf16_w(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in,
+                                const uint16_t* x, float* y, int64_t blocks_target,
+                                hipStream_t st) {
     const int64_t rw = lut_row_words(d_in, BITS);
-    const size_t lds = lut_gemv_lds_bytes(d_in, BITS, B);
+    const size_t lds = lut_lds_bytes(d_in, BITS, B, WAVES);
     static size_t attr = 0;          // dynamic LDS the kernel is enabled for
     if (lds > attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_lut_gemv_bf16<BITS, B>,
+        hipError_t e = hipFuncSetAttribute((const void*)k_lut_gemv_bf16<BITS, B, WAVES>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr = lds;
     }
-    // about two blocks per compute unit, at least one row per wave
-    int64_t rpb = (d_out + 511) / 512;
-    if (rpb < LUT_WAVES) rpb = LUT_WAVES;
+    // about blocks_target blocks, at least one row per wave
+    int64_t rpb = (d_out + blocks_target - 1) / blocks_target;
+    if (rpb < WAVES) rpb = WAVES;
     const int64_t grid = (d_out + rpb - 1) / rpb;
-    hipLaunchKernelGGL((k_lut_gemv_bf16<BITS, B>), dim3((unsigned)grid), dim3(64 * LUT_WAVES), lds,
-                       st, Q, rw, C, d_out, d_in, x,
+    hipLaunchKernelGGL((k_lut_gemv_bf16<BITS, B, WAVES>), dim3((unsigned)grid), dim3(64 * WAVES),
+                       lds, st, Q, rw, C, d_out, d_in, x,
                        (int)((d_in % 2 == 0) && (((uintptr_t)x & 3u) == 0)), (int)rpb, y);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
+}
+
+// Two 8-wave blocks per compute unit where their LDS fits; else, where the kernel stays
+// within the 128 registers of a 16-wave block without spilling (3- and 4-bit codes, and
+// 2-bit codes with up to 4 vectors), one 16-wave block, so the unit still holds 16 waves;
+// else one 8-wave block.
+template <int BITS, int B>
+static hipError_t launch_bf16(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in,
+                              const uint16_t* x, float* y, hipStream_t st) {
+    constexpr size_t LDS_CU = 160 * 1024;
+    if (2 * lut_lds_bytes(d_in, BITS, B, LUT_WAVES) <= LDS_CU)
+        return launch_bf16_w<BITS, B, LUT_WAVES>(Q, C, d_out, d_in, x, y, 512, st);
+    if constexpr (BITS >= 3 || (BITS == 2 && B <= 4)) {
+        if (lut_lds_bytes(d_in, BITS, B, 2 * LUT_WAVES) <= LDS_CU)
+            return launch_bf16_w<BITS, B, 2 * LUT_WAVES>(Q, C, d_out, d_in, x, y, 256, st);
+    }
+    return launch_bf16_w<BITS, B, LUT_WAVES>(Q, C, d_out, d_in, x, y, 512, st);
 }
 
 template <int BITS>
