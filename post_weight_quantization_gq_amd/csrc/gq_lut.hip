@@ -28,7 +28,7 @@
 
 namespace gq {
 
-constexpr int LUT_WAVES = 8;          // waves per block of the GEMV (16 where one block fits)
+constexpr int LUT_WAVES = 8;          // waves per block of the GEMV (16 where that form fits)
 constexpr int LUT_UNROLL = 8;         // code words in flight per lane
 constexpr int LUT_SPAN = 64 * LUT_UNROLL;   // words per chunk of a row
 
@@ -303,21 +303,20 @@ static hipError_t launch_bf16_w(const uint32_t* Q, const float* C, int64_t d_out
     return hipSuccess;
 }
 
-// Two 8-wave blocks per compute unit where their LDS fits; else, where the kernel stays
-// within the 128 registers of a 16-wave block without spilling (3- and 4-bit codes, and
-// 2-bit codes with up to 4 vectors), one 16-wave block, so the unit still holds 16 waves;
-// else one 8-wave block.
+// One 16-wave block per compute unit where the kernel stays within the 128 registers of
+// such a block without spilling (3- and 4-bit codes, and 2-bit codes with up to 4 vectors)
+// and its LDS fits: the activations are staged once per 16 waves' rows.  Else two 8-wave
+// blocks per unit where their LDS fits, else one.
 template <int BITS, int B>
 static hipError_t launch_bf16(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in,
                               const uint16_t* x, float* y, hipStream_t st) {
     constexpr size_t LDS_CU = 160 * 1024;
-    if (2 * lut_lds_bytes(d_in, BITS, B, LUT_WAVES) <= LDS_CU)
-        return launch_bf16_w<BITS, B, LUT_WAVES>(Q, C, d_out, d_in, x, y, 512, st);
     if constexpr (BITS >= 3 || (BITS == 2 && B <= 4)) {
         if (lut_lds_bytes(d_in, BITS, B, 2 * LUT_WAVES) <= LDS_CU)
             return launch_bf16_w<BITS, B, 2 * LUT_WAVES>(Q, C, d_out, d_in, x, y, 256, st);
     }
-    return launch_bf16_w<BITS, B, LUT_WAVES>(Q, C, d_out, d_in, x, y, 512, st);
+    const int64_t blocks = 2 * lut_lds_bytes(d_in, BITS, B, LUT_WAVES) <= LDS_CU ? 512 : 256;
+    return launch_bf16_w<BITS, B, LUT_WAVES>(Q, C, d_out, d_in, x, y, blocks, st);
 }
 
 template <int BITS>
