@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_lut_gemv_bf16(
     constexpr int PPW = lut_ppw(BITS);
     constexpr int XST = lut_xst(BITS);
     constexpr uint32_t PMASK = (uint32_t)(M * M - 1);
-    extern __shared__ uint32_t lut_lds[];
+    extern __shared__ __attribute__((aligned(16))) uint32_t lut_lds[];
     const int64_t xwords = lut_staged_words(rw) * XST;
     uint32_t* const xlds = lut_lds + WAVES * M * M;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -124,13 +124,27 @@ __global__ __launch_bounds__(64 * WAVES) void k_lut_gemv_bf16(
     if (nitems > 0) fetch(0, cur, ccur);
 
     // stage x: pair pr = w * PPW + p holds elements 2 pr, 2 pr + 1 (zero past d_in);
-    // whole_pairs (even d_in, x 4-byte aligned): each pair is one 4-byte load
+    // whole_pairs (even d_in, x 4-byte aligned): each pair is one 4-byte load.  With
+    // XST == PPW the staged pairs are x itself, zero-padded, so when every vector's start
+    // and its staged copy are 16-byte aligned, 16-byte loads copy them, all in flight at
+    // once.
+    static_assert(XST == PPW, "staged words hold their pairs contiguously");
     const int64_t npairs = lut_staged_words(rw) * PPW;
     const int64_t dpairs = d_in >> 1;
     const bool even = whole_pairs != 0;
+    const bool vec = even && (((uintptr_t)x & 15u) == 0) && (d_in % 8 == 0) && (xwords % 4 == 0);
     for (int b = 0; b < B; ++b) {
         const uint16_t* xb = x + (int64_t)b * d_in;
         uint32_t* xs = xlds + (int64_t)b * xwords;
+        if (vec) {
+            const u32x4* src = (const u32x4*)xb;
+            u32x4* dst = (u32x4*)xs;
+            const int64_t nv = npairs / 4, dv = dpairs / 4;
+#pragma unroll 4
+            for (int64_t i = tid; i < nv; i += 64 * WAVES)
+                dst[i] = i < dv ? src[i] : u32x4{0u, 0u, 0u, 0u};
+            continue;
+        }
         for (int64_t pr = tid; pr < npairs; pr += 64 * WAVES) {
             uint32_t v;
             if (even) {
