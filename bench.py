@@ -83,7 +83,7 @@ _TRAFFIC = {
     "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "ebbacca8a3e52d0f", 755435218, 270175408),
     "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "cf26376348bd061a", 604188214, 67108864),
     "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "ebbacca8a3e52d0f", 1879307807, 85658099),
-    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "2c248c0b1fdf2f79", 118492267, 42874),
+    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "bc0e62e46cd7fb17", 118515825, 42747),
 }
 
 
