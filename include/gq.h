@@ -68,7 +68,7 @@ typedef enum {
     GQ_EDTYPE = 3,    /* unsupported dtype code */
     GQ_ENOMEM = 4,    /* library-side workspace allocation failed */
     GQ_EHIP = 5,      /* a HIP runtime call or kernel launch failed */
-    GQ_ENOTIMPL = 8   /* valid request outside what this build supports */
+    GQ_ENOTIMPL = 8   /* valid request outside what the library supports */
 } gq_status;
 
 typedef enum { GQ_F32 = 0, GQ_BF16 = 1 } gq_dtype;
