@@ -353,6 +353,18 @@ def main():
                 "avg_launch_ms": avg_ms, "units_per_launch": per_launch,
                 "launches_per_step": n_launch}
 
+    # every stage's fraction of its own bound, from the warm-up step's per-stage times
+    stage_roof = {}
+    for k, ms in per_step.items():
+        sp = _stage_units(k, wl, nchg, grid, ganq)
+        if sp is None or ms <= 0:
+            continue
+        bound, amount, peak, unit, _ = sp
+        ach = amount / (ms * 1e-3)
+        scale = 1e9 if unit == "GB/s" else 1e12
+        stage_roof[k] = {"bound": bound, "achieved": round(ach / scale, 2), "peak": peak / scale,
+                         "unit": unit, "frac": round(ach / peak, 4)}
+
     metric = ("Fixed-grid GuidedQuant rows quantized/s (Fisher + uniform grid + assignment "
               f"passes) at {wl.d_in}x{wl.d_out}, {wl.bits}-bit, 1 MI355X" if grid else
               "GANQ-style rows quantized/s (Fisher + Cholesky + codebook / back-substitution "
@@ -389,6 +401,9 @@ def main():
         "layer_roofline": (_grid_roofline if grid else _ganq_roofline if ganq else
                            _layer_roofline)(wl, nchg, ms_step),
         "roofline": roof,
+        "stage_rooflines": stage_roof,
+        "stage_rooflines_from": "last warmup step (per-stage HIP events); each stage's "
+                                "algorithmic work over its time against its own bound",
     }
 
     if not args.no_cpu_baseline:
