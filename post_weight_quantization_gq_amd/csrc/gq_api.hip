@@ -10,6 +10,7 @@ static_assert((int)gq::ST_COUNT == (int)GQ_STAGE_COUNT, "stage ids of gq.h and t
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -43,6 +44,20 @@ hipEvent_t take_event() {
 }  // namespace
 
 bool timing_on(Stage s) { return (g_timing.load(std::memory_order_relaxed) >> (int)s) & 1; }
+
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::mutex mu;
+    static std::map<std::pair<const void*, int>, size_t> raised;
+    std::lock_guard<std::mutex> lk(mu);
+    size_t& have = raised[{kernel, dev}];
+    if (bytes <= have) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) have = bytes;
+    return e;
+}
 
 void timing_mark(Stage s, hipStream_t st, bool begin) {
     std::lock_guard<std::mutex> lk(g_tmu);

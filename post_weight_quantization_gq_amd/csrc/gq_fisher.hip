@@ -500,13 +500,9 @@ static hipError_t fisher_pass(const FisherPlan& p, const void* X, const void* G,
         uint16_t* YT = (uint16_t*)(w + p.xt_bytes);
         float* part = (float*)(w + p.xt_bytes + p.yt_bytes);
         const int64_t n_pad = (n + PK - 1) / PK * PK;
-        static bool attr_set = false;
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute((const void*)k_fisher_mfma,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)F_LDS_BYTES);
+        {
+            hipError_t e = ensure_dynamic_lds((const void*)k_fisher_mfma, F_LDS_BYTES);
             if (e != hipSuccess) return e;
-            attr_set = true;
         }
         {
             StageTimer tm(ST_FISHER_PACK, st);

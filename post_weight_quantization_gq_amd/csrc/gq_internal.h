@@ -12,6 +12,10 @@ enum Stage {
     ST_LNQ_RESID, ST_LNQ_INIT, ST_LNQ_GRAM, ST_LNQ_SOLVE, ST_LNQ_SWEEP, ST_LNQ_SMALL, ST_FISHER_PACK,
     ST_LNQ_DELTA, ST_LUT_PACK, ST_LUT_GEMV, ST_FISHER_H2D, ST_GANQ_CHOL, ST_GANQ_PASS, ST_COUNT
 };
+// Raise a kernel's dynamic-LDS limit to at least `bytes` on the current device, once per
+// kernel, device and size (the attribute belongs to the device that is current).
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
+
 bool timing_on(Stage s);
 void timing_mark(Stage s, hipStream_t st, bool begin);
 // Records a start event on construction and a stop event on destruction when

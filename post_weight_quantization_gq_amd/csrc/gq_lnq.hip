@@ -1351,8 +1351,7 @@ hipError_t lnq_init_run(const void* W, bool w_bf16, int64_t d_out, int64_t d, in
         hipLaunchKernelGGL(k_lnq_init_select, dim3((unsigned)d_out), dim3(256), 0, st,
                            (const uint16_t*)W, d, m, C, P);
     } else {
-        hipError_t e = hipFuncSetAttribute((const void*)k_lnq_init<false>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = ensure_dynamic_lds((const void*)k_lnq_init<false>, lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k_lnq_init<false>, dim3((unsigned)d_out), dim3(1024), lds, st, W, d,
                            npow2, m, C, P);

@@ -423,13 +423,9 @@ hipError_t lnq_residual(const uint16_t* Ehi, const uint16_t* Elo, int64_t d_out,
     const int nta = (int)(a_pad / MT);
     const int total = ntn * nta * groups;
     const int grid = (total + 255) / 256 * 256;        // whole rounds for the XCD remap
-    static bool attr_done = false;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_resid,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)RESID_LDS);
+    {
+        hipError_t e = ensure_dynamic_lds((const void*)k_resid, RESID_LDS);
         if (e != hipSuccess) return e;
-        attr_done = true;
     }
     StageTimer tm(ST_LNQ_RESID, st);
     hipLaunchKernelGGL(k_resid, dim3((unsigned)grid), dim3(512), RESID_LDS, st, Ehi, Elo,
@@ -448,13 +444,9 @@ static hipError_t launch_gram(const uint8_t* P, int64_t d_out, int64_t d, int gr
     const int nta = (int)((d + MT - 1) / MT);
     const int total = ntn * nta * groups;
     const int grid = (total + 255) / 256 * 256;
-    static bool attr_done = false;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_gram<M>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)GRAM_LDS);
+    {
+        hipError_t e = ensure_dynamic_lds((const void*)k_gram<M>, GRAM_LDS);
         if (e != hipSuccess) return e;
-        attr_done = true;
     }
     StageTimer tm(ST_LNQ_GRAM, st);
     hipLaunchKernelGGL((k_gram<M>), dim3((unsigned)grid), dim3(512), GRAM_LDS, st, P, rpg, d_out,

@@ -299,12 +299,9 @@ static hipError_t launch_bf16_w(const uint32_t* Q, const float* C, int64_t d_out
                                 hipStream_t st) {
     const int64_t rw = lut_row_words(d_in, BITS);
     const size_t lds = lut_lds_bytes(d_in, BITS, B, WAVES);
-    static size_t attr = 0;          // dynamic LDS the kernel is enabled for
-    if (lds > attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_lut_gemv_bf16<BITS, B, WAVES>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    {
+        hipError_t e = ensure_dynamic_lds((const void*)k_lut_gemv_bf16<BITS, B, WAVES>, lds);
         if (e != hipSuccess) return e;
-        attr = lds;
     }
     // about blocks_target blocks, at least one row per wave
     int64_t rpb = (d_out + blocks_target - 1) / blocks_target;
