@@ -46,6 +46,28 @@ def test_ganq_factor_matches_numpy(device, mid):
         assert e <= 1e-6
 
 
+@pytest.mark.parametrize("d,groups", [(64, 1), (128, 2), (192, 3), (320, 1)])
+def test_ganq_factor_panel_counts(device, d, groups):
+    """One to five 64-wide panels: no trailing update, a column update only, and the
+    second-stream rest-updates of the lookahead.  F'_g = F_g + rho mean(diag F_g) I of
+    seeded SPD F_g against numpy's float64 Cholesky, within 1e-6 relative Frobenius."""
+    rng = np.random.default_rng(d + groups)
+    X = rng.standard_normal((groups, 3 * d, d))
+    F32 = np.einsum("gni,gnj->gij", X, X).astype(np.float32) / np.float32(3 * d)
+    F32 = (F32 + np.transpose(F32, (0, 2, 1))) * np.float32(0.5)
+    L, npd = gq.ganq_factor_damped(to_dev(np.ascontiguousarray(F32), "cuda"), RHO)
+    torch.cuda.synchronize()
+    assert npd.cpu().numpy().tolist() == [0] * groups
+    Ln = L.cpu().double().numpy()
+    for g in range(groups):
+        F64 = F32[g].astype(np.float64)
+        Fp = F64 + RHO * np.mean(np.diag(F64)) * np.eye(d)
+        e = rel_fro(Ln[g], np.linalg.cholesky(Fp))
+        print(f"d={d} group {g}: factor rel Frobenius {e:.2e}")
+        assert np.all(np.triu(Ln[g], 1) == 0.0)
+        assert e <= 1e-6
+
+
 def _check_assignment(prob, C1, P1, rows=None, tol=1e-4, frac=0.999):
     Ls = _factors(prob)
     rows = range(prob.wl.d_out) if rows is None else rows
