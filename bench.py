@@ -78,12 +78,12 @@ _CSRC = os.path.join(ROOT, "post_weight_quantization_gq_amd", "csrc")
 _TRAFFIC = {
     # stage: (workload, source file, digest, bytes read, bytes written) of its main kernel,
     # averaged over the launches that do the work
-    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "cf26376348bd061a", 269411071, 16777216),
-    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "4f32b7880a60cc1d", 16843666162, 1140850688),
-    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "ebbacca8a3e52d0f", 755435218, 270175408),
-    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "cf26376348bd061a", 604188214, 67108864),
-    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "ebbacca8a3e52d0f", 1879307807, 85658099),
-    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "bc0e62e46cd7fb17", 118515825, 42747),
+    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "1c17160de8a8a0c3", 269428325, 16777216),
+    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "067be7df92de2bcb", 16823031928, 1140850688),
+    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "620d603df40a7656", 764045202, 270180621),
+    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "1c17160de8a8a0c3", 604187898, 67108864),
+    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "620d603df40a7656", 1879913589, 85658726),
+    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "e07fedba8ab0ec7a", 118515791, 43038),
 }
 
 
