@@ -276,10 +276,12 @@ gq_status lut_pack_codes(const uint8_t* P, int64_t d_out, int64_t d_in, int32_t 
  * 1 <= batch <= 8, Q from lut_pack_codes, C [d_out][2^bits] float32.
  * bfloat16 x: the codebook enters as bfloat16 (rounded to nearest even, as a
  * 16-bit lookup table holds it), each product of two bfloat16 values is exact
- * and the sums are float32; the staged activations must fit the LDS
- * (batch * (row words + 1) * X * 4 + 8 * 4^bits * 4 <= 160 KiB with X = 16 / bits for
- * bits 1, 2, 4 and X = 5 for bits 3, else
- * GQ_ENOTIMPL).  float32 x: float32 codebook and float32 fused multiply-adds.
+ * and the sums are float32.  The activations are staged in LDS, a whole row's worth
+ * when it fits, else in segments of a multiple of 512 packed words; one chunk of them
+ * must fit: batch * (min(row words, 512) + 1) * X * 4 + 8 * 4^bits * 4 <= 160 KiB with
+ * X = 16 / bits for bits 1, 2, 4 and X = 5 for bits 3, else GQ_ENOTIMPL.  With segments
+ * each output is the float32 sum of the segments' sums.  float32 x: float32 codebook and
+ * float32 fused multiply-adds.
  */
 gq_status lut_gemv(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in, int32_t bits,
                    const void* x, gq_dtype x_dt, int32_t batch, float* y, void* stream);

@@ -547,9 +547,9 @@ gq_status lut_gemv(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_i
         ((uintptr_t)x & (x_dt == GQ_BF16 ? 1u : 3u)))
         return fail(GQ_EINVAL, "Q must be 16-byte aligned, C, y and x element-aligned");
     const bool xb = x_dt == GQ_BF16;
-    if (xb && gq::lut_gemv_lds_bytes(d_in, bits, batch) > 160 * 1024)
-        return fail(GQ_ENOTIMPL, "d_in=%lld with batch=%d: the staged activations exceed the LDS",
-                    (long long)d_in, batch);
+    if (xb && !gq::lut_gemv_fits(d_in, bits, batch))
+        return fail(GQ_ENOTIMPL, "d_in=%lld with batch=%d: one chunk of staged activations "
+                    "exceeds the LDS", (long long)d_in, batch);
     hipError_t e = gq::lut_gemv_run(Q, C, d_out, d_in, bits, x, xb, batch, y, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "lut_gemv");
     return GQ_OK;

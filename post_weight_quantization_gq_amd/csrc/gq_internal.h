@@ -118,7 +118,7 @@ hipError_t lnq_store_counter(const unsigned long long* c, int64_t* dst, hipStrea
 
 // LUT dequantisation GEMV (gq_lut.hip)
 int64_t lut_row_words(int64_t d_in, int bits);          // 32-bit words per packed row
-size_t lut_gemv_lds_bytes(int64_t d_in, int bits, int batch);
+bool lut_gemv_fits(int64_t d_in, int bits, int batch);
 hipError_t lut_pack_run(const uint8_t* P, int64_t d_out, int64_t d_in, int bits, uint32_t* Q,
                         hipStream_t st);
 hipError_t lut_gemv_run(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in, int bits,

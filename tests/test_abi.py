@@ -201,7 +201,8 @@ def test_lut_argument_errors():
     assert mv(bits=0) == B.GQ_EINVAL
     assert mv(batch=9) == B.GQ_EINVAL and "batch" in _err(lib)
     assert mv(Q=FAKE_ODD) == B.GQ_EINVAL
-    assert mv(d_in=1 << 20) == B.GQ_ENOTIMPL and "LDS" in _err(lib)
+    # 1-bit codes and 8 vectors: one 512-word chunk of staged activations exceeds the LDS
+    assert mv(d_in=1 << 20, bits=1, batch=8) == B.GQ_ENOTIMPL and "LDS" in _err(lib)
     assert mv(d_in=1 << 20, xdt=0, y=None) == B.GQ_EINVAL
 
 

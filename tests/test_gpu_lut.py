@@ -110,13 +110,35 @@ def test_lut_gemv_full_size(device, name, batch):
     _check(y, C, P, xv, True, wl.d_in)
 
 
-def test_lut_gemv_rejects_oversized_staging(device):
-    """28672 inputs with 8 bfloat16 vectors do not fit the LDS: an error, before any launch."""
+@pytest.mark.parametrize("d_out,d_in,bits,batch", [
+    (37, 40000, 3, 8),       # 8 segments of 512 words, the last ragged (416)
+    (37, 40001, 3, 3),       # odd d_in: the pair-by-pair staging
+    (64, 20000, 2, 8),       # 2-bit: 3 segments, 8 pairs per word
+    (40, 28672, 1, 4),       # 1-bit: 32 codes per word
+])
+def test_lut_gemv_segmented_staging(device, d_out, d_in, bits, batch):
+    """Rows too wide for one block's LDS at this batch: x staged in segments of whole
+    chunks, each output the sum of its segments' sums."""
+    Q, y, C, P, xv = _run(device, d_out, d_in, bits, batch, "bf16", seed=d_in + batch)
+    _check(y, C, P, xv, True, d_in)
+
+
+@pytest.mark.parametrize("batch", [4, 8])
+def test_lut_gemv_full_size_segmented(device, batch):
+    """Every row of the 28672 -> 8192 4-bit product with 4 and 8 vectors (segments)."""
     wl = synth.workload("llama2_70b_down")
-    Q = torch.zeros((wl.d_out, gq.lut_packed_row_words(wl.d_in, wl.bits)), dtype=torch.int32,
+    Q, y, C, P, xv = _run(device, wl.d_out, wl.d_in, wl.bits, batch, "bf16", seed=9)
+    _check(y, C, P, xv, True, wl.d_in)
+
+
+def test_lut_gemv_rejects_oversized_staging(device):
+    """1-bit codes with 8 bfloat16 vectors: one 512-word chunk of staged activations
+    (513 x 16 pairs x 8 vectors x 4 bytes) exceeds the LDS: an error, before any launch."""
+    d_out, d_in, bits = 64, 28672, 1
+    Q = torch.zeros((d_out, gq.lut_packed_row_words(d_in, bits)), dtype=torch.int32,
                     device=device)
-    C = torch.zeros((wl.d_out, wl.m), dtype=torch.float32, device=device)
-    x = torch.zeros((8, wl.d_in), dtype=torch.bfloat16, device=device)
+    C = torch.zeros((d_out, 2), dtype=torch.float32, device=device)
+    x = torch.zeros((8, d_in), dtype=torch.bfloat16, device=device)
     with pytest.raises(gq.GQError) as e:
-        gq.lut_gemv(Q, C, x, wl.bits)
+        gq.lut_gemv(Q, C, x, bits)
     assert e.value.status == 8
