@@ -360,7 +360,7 @@ static hipError_t launch_bf16_w(const uint32_t* Q, const float* C, int64_t d_out
 // such a block without spilling (3- and 4-bit codes, and 2-bit codes with up to 4 vectors)
 // and its LDS fits: the activations are staged once per 16 waves' rows.  Else two 8-wave
 // blocks per unit where their LDS fits, else one.  Where no whole row fits, the row is
-// staged in segments, in the 16-wave form where it applies.
+// staged in segments, in a 16-wave block where that kernel does not spill.
 template <int BITS, int B>
 static hipError_t launch_bf16(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_in,
                               const uint16_t* x, float* y, hipStream_t st) {
@@ -375,6 +375,14 @@ static hipError_t launch_bf16(const uint32_t* Q, const float* C, int64_t d_out, 
     if (lut_lds_bytes(rw, BITS, B, LUT_WAVES) <= LUT_LDS_CU) {
         const int64_t blocks = 2 * lut_lds_bytes(rw, BITS, B, LUT_WAVES) <= LUT_LDS_CU ? 512 : 256;
         return launch_bf16_w<BITS, B, LUT_WAVES, false>(Q, C, d_out, d_in, x, y, blocks, whole, st);
+    }
+    // the segmented kernel holds a few more registers: 16 waves where that still fits
+    constexpr bool SEG_WIDE = (BITS == 4 && B <= 4) || (BITS == 3 && B <= 3) || (BITS == 2 && B <= 2);
+    if constexpr (SEG_WIDE) {
+        const int64_t s16 = lut_segment_words(BITS, B, 2 * LUT_WAVES);
+        if (s16 >= LUT_SPAN)
+            return launch_bf16_w<BITS, B, 2 * LUT_WAVES, true>(Q, C, d_out, d_in, x, y, 256, s16,
+                                                               st);
     }
     const int64_t seg = lut_segment_words(BITS, B, LUT_WAVES);
     if (seg < LUT_SPAN) return hipErrorInvalidValue;   // rejected before any launch
