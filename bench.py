@@ -78,12 +78,12 @@ _CSRC = os.path.join(ROOT, "post_weight_quantization_gq_amd", "csrc")
 _TRAFFIC = {
     # stage: (workload, source file, digest, bytes read, bytes written) of its main kernel,
     # averaged over the launches that do the work
-    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "1c17160de8a8a0c3", 269428325, 16777216),
-    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "067be7df92de2bcb", 16823031928, 1140850688),
-    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "620d603df40a7656", 764045202, 270180621),
-    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "1c17160de8a8a0c3", 604187898, 67108864),
-    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "620d603df40a7656", 1879913589, 85658726),
-    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "e07fedba8ab0ec7a", 118515791, 43038),
+    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "0fa6c7f1b4e712e4", 269384781, 16777216),
+    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "78bf7677018ff226", 16761345164, 1140850688),
+    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "43c0933b8168e2e2", 762537402, 270166547),
+    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "0fa6c7f1b4e712e4", 604188602, 67108864),
+    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "43c0933b8168e2e2", 1879270573, 85658560),
+    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "0bc11711f539992b", 118512673, 42098),
 }
 
 
