@@ -83,6 +83,7 @@ _TRAFFIC = {
     "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "43c0933b8168e2e2", 762537402, 270166547),
     "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "0fa6c7f1b4e712e4", 604188602, 67108864),
     "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "43c0933b8168e2e2", 1879270573, 85658560),
+    "ganq_pass": ("llama2_7b_attn", "gq_ganq.hip", "c0476d200f4da953", 598439224, 252128512),
     "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "0bc11711f539992b", 118512673, 42098),
 }
 
