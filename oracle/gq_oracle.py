@@ -27,8 +27,8 @@ Readings where the pages are silent (the same readings the GPU library uses):
     carries a leading n and leaves F_j undefined; LNQ is invariant to scaling F).
   * Groups are contiguous equal blocks of output channels; averaging F_j over a
     group equals using s_g[t] = mean_{j in g} G[t, j]^2 (linearity).
-  * Damping: F' = F_g + lambda_g I with lambda_g = rho * mean(diag F_g); F' is
-    used everywhere (objective, codebook, sweep).
+  * Damping: F' = F_g + lambda_g I with lambda_g = rho * mean(diag F_g) (plus an
+    optional fixed term); F' is used everywhere (objective, codebook, sweep).
   * Initial codebook: m quantiles of w_j at levels (q + 1/2)/m with linear
     interpolation between order statistics, stored as float32; initial codes
     are the nearest entry (lowest index on ties).  Parity unpinned by the pages
@@ -116,16 +116,22 @@ def guided_loss(X: np.ndarray, G: np.ndarray, W: np.ndarray, W_hat: np.ndarray) 
 # Damping (reading: GPTQ-style relative ridge on F itself)
 # ----------------------------------------------------------------------------
 
-def ridge_lambda(F_g: np.ndarray, rho: float) -> float:
-    """lambda_g = rho * mean(diag F_g)."""
+def ridge_lambda(F_g: np.ndarray, rho: float, lam_abs: float = 0.0) -> float:
+    """lambda_g = rho * mean(diag F_g) + lam_abs.
+
+    The relative term is the ridge the tiny 128 -> 64 workload states (1e-6 times
+    the mean of diag F), which scales with the Fisher ("adaptive"); lam_abs is a
+    fixed ridge independent of F, the alternative the GANQ summary page's ablation
+    table sets against adaptive preconditioning.  Only the diagonal enters.
+    """
     F_g = np.asarray(F_g, np.float64)
-    return float(rho * np.trace(F_g) / F_g.shape[0])
+    return float(rho * np.trace(F_g) / F_g.shape[0]) + float(lam_abs)
 
 
-def damped(F_g: np.ndarray, rho: float) -> np.ndarray:
+def damped(F_g: np.ndarray, rho: float, lam_abs: float = 0.0) -> np.ndarray:
     """F' = F_g + lambda_g I."""
     F_g = np.asarray(F_g, np.float64)
-    return F_g + ridge_lambda(F_g, rho) * np.eye(F_g.shape[0])
+    return F_g + ridge_lambda(F_g, rho, lam_abs) * np.eye(F_g.shape[0])
 
 
 # ----------------------------------------------------------------------------
@@ -215,7 +221,9 @@ def assign_sweep(Fp: np.ndarray, w: np.ndarray, c: np.ndarray, p: np.ndarray,
 
     For each coordinate, pick the codebook entry minimising the row objective
     with every other coordinate fixed; keep the current entry unless some entry
-    strictly decreases it, then take the lowest-index minimiser.
+    strictly decreases it, then take the lowest-index minimiser.  F' is
+    symmetric (a damped Fisher X^T diag(s) X + lambda I), so the residual update
+    r += delta F'[:, i] reads row i, the same numbers as column i.
     """
     c = np.asarray(c, np.float64)
     p = np.array(p, dtype=np.int64, copy=True)
@@ -228,31 +236,38 @@ def assign_sweep(Fp: np.ndarray, w: np.ndarray, c: np.ndarray, p: np.ndarray,
         if return_steps:
             steps.append(D.copy())
         if D[q] < 0.0:
-            r += (c[q] - c[p[i]]) * Fp[:, i]
+            r += (c[q] - c[p[i]]) * Fp[i]
             p[i] = q
     if return_steps:
         return p, steps
     return p
 
 
-def lnq_row(Fp: np.ndarray, w: np.ndarray, m: int, iters: int, c0=None, p0=None):
+def lnq_row(Fp: np.ndarray, w: np.ndarray, m: int, iters: int, c0=None, p0=None,
+            trace: bool = True):
     """LNQ for one row: init, then `iters` x (codebook, assignment)  [LNQ-alg].
 
     Returns (c, p, trace) with trace[0] the objective at the start and
     trace[2t-1], trace[2t] after the codebook and assignment steps of pass t.
+    With trace=False the steps are the same and only the final objective is
+    evaluated (trace = [objective at the end]).
     """
     if c0 is None:
         c, p = init_quantile(w, m)
     else:
         c = np.asarray(c0, np.float64).copy()
         p = np.asarray(p0, np.int64).copy()
-    trace = [objective(Fp, w, c, p)]
+    tr = [objective(Fp, w, c, p)] if trace else []
     for _ in range(iters):
         c = codebook_update(Fp, w, p, c)
-        trace.append(objective(Fp, w, c, p))
+        if trace:
+            tr.append(objective(Fp, w, c, p))
         p = assign_sweep(Fp, w, c, p)
-        trace.append(objective(Fp, w, c, p))
-    return c, p, np.array(trace)
+        if trace:
+            tr.append(objective(Fp, w, c, p))
+    if not trace:
+        tr = [objective(Fp, w, c, p)]
+    return c, p, np.array(tr)
 
 
 def replay_sweep(Fp: np.ndarray, w: np.ndarray, c: np.ndarray, p_start: np.ndarray,
@@ -285,7 +300,7 @@ def replay_sweep(Fp: np.ndarray, w: np.ndarray, c: np.ndarray, p_start: np.ndarr
         if q != q_ref:
             differ += 1
         if q != p[i]:
-            r += (c[q] - c[p[i]]) * Fp[:, i]
+            r += (c[q] - c[p[i]]) * Fp[i]          # row i = column i (F' symmetric)
             obj += float(D[q])
             p[i] = q
     return worst, differ

@@ -58,6 +58,35 @@ def test_golden_sweep():
     assert O.objective(F, w, c, p1) == pytest.approx(ex["objective_end"], abs=1e-14)
 
 
+def test_golden_ridge():
+    """lambda = rho * mean(diag F) + lam_abs, worked by hand: only the diagonal
+    enters, through its mean (not its sum, not the mean of every entry)."""
+    ex = json.load(open(GOLDEN))["ridge"]
+    for case in ex["cases"]:
+        F = np.array(case["F"], dtype=np.float64)
+        lam = O.ridge_lambda(F, case["rho"], case["lam_abs"])
+        assert lam == pytest.approx(case["lambda"], rel=1e-15, abs=1e-15)
+        Fp = O.damped(F, case["rho"], case["lam_abs"])
+        np.testing.assert_allclose(np.diag(Fp), case["damped_diag"], rtol=1e-15)
+        off = ~np.eye(F.shape[0], dtype=bool)
+        np.testing.assert_array_equal(Fp[off], F[off])
+    # the default is the relative ridge alone
+    F = np.array(ex["cases"][0]["F"])
+    assert O.ridge_lambda(F, 0.5) == 1.5
+
+
+def test_lnq_row_without_trace_takes_the_same_steps():
+    rng = _rng(5)
+    d, m = 48, 4
+    Fp = O.damped(_spd(rng, d), 1e-6)
+    w = rng.standard_normal(d)
+    c1, p1, t1 = O.lnq_row(Fp, w, m, 3)
+    c2, p2, t2 = O.lnq_row(Fp, w, m, 3, trace=False)
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(p1, p2)
+    assert t2.shape == (1,) and t2[0] == t1[-1]
+
+
 # --------------------------------------------------------------------------
 # Fisher: brute-force sums, the GuidedQuant identity, invariants
 # --------------------------------------------------------------------------
