@@ -24,7 +24,8 @@
  *             1/n of the objective equation is not applied; LNQ does not
  *             depend on the scale of F).
  *   Damping.  Every LNQ call works with F'_g = F_g + lambda_g I,
- *             lambda_g = ridge_rel * mean(diag F_g), formed on the fly.
+ *             lambda_g = ridge_rel * mean(diag F_g) (+ ridge_abs, see
+ *             gq_lnq_options), formed on the fly.
  *   Memory.   Every array argument is a device pointer (HIP global memory)
  *             unless stated otherwise.  The caller owns all buffers; the
  *             library keeps no pointer after a call returns.
@@ -37,11 +38,19 @@
  *             hipFreeAsync on `stream`).
  *   Streams.  `stream` is a hipStream_t (NULL = default stream).  Calls only
  *             enqueue work; outputs are valid once the stream is synchronised.
- *             Calls on one stream are ordered; the library holds no global
- *             mutable state besides the thread-local error string.
+ *             Calls on one stream are ordered.  A checked call (check_finite,
+ *             GQ_FISHER_CHECK_FINITE) synchronises its stream before returning.
+ *   State.    Calls on different streams may run concurrently: the library's
+ *             only state shared between calls is (a) the cache of kernel LDS
+ *             limits already raised on each device (set once, under a lock),
+ *             (b) the per-stage timing record (diagnostics, off unless
+ *             gq_timing_enable is called; its marks are kept per stream), and
+ *             the thread-local error string.
  *   Errors.   Arguments are validated before anything is enqueued; on a
  *             non-OK status no output has been touched and gq_last_error()
  *             (thread-local) says why.  GQ_EHIP reports a failed HIP call.
+ *             The one exception is GQ_ENOTPD from a checked call: the run has
+ *             completed and its outputs are written (see gq_lnq_options).
  *   Precision. Fisher: bfloat16 inputs, MFMA with float32 accumulation; the
  *             gradient-square scale is applied to one operand, rounded to
  *             bfloat16.  float32 inputs take a float64-accumulating path.
@@ -59,15 +68,20 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 6
+#define GQ_ABI_VERSION 7
 
 typedef enum {
     GQ_OK = 0,
     GQ_EINVAL = 1,    /* bad argument value (null pointer, bits, block, iters, workspace too small) */
-    GQ_ESHAPE = 2,    /* inconsistent sizes (d_out % groups, d_in % block, empty shapes) */
+    GQ_ESHAPE = 2,    /* inconsistent sizes (d_out % groups, d_in % 32 or 64, empty shapes) */
     GQ_EDTYPE = 3,    /* unsupported dtype code */
     GQ_ENOMEM = 4,    /* library-side workspace allocation failed */
     GQ_EHIP = 5,      /* a HIP runtime call or kernel launch failed */
+    GQ_ENOTPD = 6,    /* checked call: some codebook system P^T F' P (or GANQ's F') was not
+                         positive definite, so the closed form of the "(codebook)" step (or the
+                         Cholesky factor) does not exist there; those rows kept their codebook
+                         (codes).  Outputs are written. */
+    GQ_ENONFINITE = 7, /* checked call: an input holds NaN or +-Inf; nothing was written */
     GQ_ENOTIMPL = 8   /* valid request outside what the library supports */
 } gq_status;
 
@@ -78,13 +92,17 @@ typedef enum { GQ_INIT_QUANTILE = 0, GQ_INIT_GIVEN = 1, GQ_INIT_UNIFORM = 2 } gq
 typedef enum { GQ_GRAM_AUTO = 0, GQ_GRAM_DENSE = 1 } gq_gram_update;
 
 typedef struct {
-    int32_t block;      /* assignment block: coordinates decided exactly in registers (one per
-                           lane of a 64-wide wavefront) before the effect of their moves on the
-                           following coordinates is applied on the matrix cores.  Must be 64
-                           (d_in % 64 == 0); the block size changes only the float32 summation
-                           order, never the order in which coordinates are visited.
-                           Default 64. */
-    float ridge_rel;    /* rho in lambda_g = rho * mean(diag F_g).  Default 1e-6. */
+    int32_t block;      /* assignment block B: 64, 128, 256 or 512 coordinates.  Inside a block
+                           the pass decides 64 coordinates at a time exactly in registers (one per
+                           lane of a 64-wide wavefront) and carries their moves to the block's
+                           later coordinates on the matrix cores; at the end of a block the
+                           deferred update R[:, later] += Delta_B F'[B, later] of all its moves is
+                           pushed into the residual array on the matrix cores.  B changes only
+                           the float32 summation order, never the order in which coordinates
+                           are visited or the tie rule.  d_in must be a multiple of 64 (the
+                           last block may be shorter than B).  Default 512. */
+    float ridge_rel;    /* rho in lambda_g = rho * mean(diag F_g) + ridge_abs: the relative
+                           ("adaptive") ridge, scaling with F.  Default 1e-6. */
     int32_t init;       /* gq_lnq_init.  QUANTILE: c_j = m quantiles of w_j at levels
                            (q + 1/2)/m (linear interpolation between order statistics),
                            codes = nearest entry (lowest index on ties).  UNIFORM: the
@@ -100,7 +118,18 @@ typedef struct {
                            codes (see lnq_quantize), updated from the changed coordinates
                            only (equal up to float rounding), else recomputed.
                            Default AUTO. */
+    float ridge_abs;    /* fixed ridge added to lambda_g whatever F is (ridge_rel = 0 and
+                           ridge_abs = lambda is the fixed-lambda preconditioning of the GANQ
+                           summary page's ablation).  Finite, >= 0.  Default 0. */
+    int32_t check_finite; /* 1: a checked call.  Before anything is written, W and F are
+                           scanned for NaN and +-Inf (GQ_ENONFINITE if any, outputs
+                           untouched); after the run, GQ_ENOTPD if any codebook system (GANQ:
+                           any group's F') was not positive definite.  The call synchronises
+                           its stream.  0: no data checks, fully asynchronous.  Default 0. */
 } gq_lnq_options;
+
+/* The options under the name the problem statement uses. */
+typedef gq_lnq_options lnq_options;
 
 /* ABI version of the loaded library (GQ_ABI_VERSION). */
 int gq_abi_version(void);
@@ -109,8 +138,10 @@ int gq_abi_version(void);
    Owned by the library; valid until the next call on this thread. */
 const char* gq_last_error(void);
 
-/* Fills *opt with the defaults listed in gq_lnq_options.  opt: host pointer. */
+/* Fills *opt with the defaults listed in gq_lnq_options.  opt: host pointer.
+   lnq_options_default is the same function under the problem statement's name. */
 void gq_lnq_options_default(gq_lnq_options* opt);
+void lnq_options_default(lnq_options* opt);
 
 /* Workspace bytes gq_fisher_accumulate needs for these sizes. */
 size_t gq_fisher_workspace_size(int64_t n, int64_t d_in, int64_t d_out, int32_t groups,
@@ -122,11 +153,15 @@ size_t gq_fisher_workspace_size(int64_t n, int64_t d_in, int64_t d_out, int32_t 
  *   s_g[t] = (1/|g|) sum_{j in g} G[t, j]^2.
  * X [n][d_in] of dtype x_dt, G [n][d_out] of dtype g_dt, F [groups][d_in][d_in]
  * float32 output; accumulate = 0 overwrites F, 1 adds to it (token chunks can be
- * streamed through repeated calls, F being a sum over tokens).  The result is
- * exactly symmetric (the upper triangle is computed and mirrored).
+ * streamed through repeated calls, F being a sum over tokens).  OR-ing
+ * GQ_FISHER_CHECK_FINITE into `accumulate` makes the call checked: X and G are
+ * scanned for NaN and +-Inf first (GQ_ENONFINITE, F untouched) and the call
+ * synchronises its stream.  The result is exactly symmetric (the upper triangle is
+ * computed and mirrored).
  * Requires n >= 1, d_in >= 1, d_out >= 1, 1 <= groups, d_out % groups == 0,
  * x_dt == g_dt.
  */
+#define GQ_FISHER_CHECK_FINITE 2
 gq_status gq_fisher_accumulate(const void* X, gq_dtype x_dt, int64_t n, int64_t d_in,
                                const void* G, gq_dtype g_dt, int64_t d_out, int32_t groups,
                                float* F, int32_t accumulate,
@@ -154,9 +189,12 @@ gq_status gq_fisher_accumulate_host(const void* X_host, gq_dtype x_dt, int64_t n
                                     int64_t chunk_tokens, void* ws, size_t ws_bytes,
                                     void* stream);
 
-/* Workspace bytes every lnq_* call below needs for these sizes and W dtype. */
+/* Workspace bytes every lnq_* call below needs for these sizes and W dtype
+   (lnq_workspace_size: the same function under the problem statement's name). */
 size_t gq_lnq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_t bits,
                              gq_dtype w_dt);
+size_t lnq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_t bits,
+                          gq_dtype w_dt);
 
 /*
  * One "(codebook)" step of the LNQ algorithm box for every row j:
@@ -170,7 +208,8 @@ size_t gq_lnq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_
  * F' = 0), and can happen with ridge_rel == 0.
  * Shape limits shared by every lnq_* call: 1 <= bits <= 4, d_out % groups == 0,
  * d_in % 32 == 0, 32 <= d_in <= 32768, ridge_rel finite and >= 0 (GQ_EINVAL /
- * GQ_ESHAPE otherwise).
+ * GQ_ESHAPE otherwise); the assignment pass (lnq_assign_sweep, lnq_quantize,
+ * grid_quantize) and ganq_* also need d_in % 64 == 0.
  */
 gq_status lnq_codebook_update(const float* F, int32_t groups, int64_t d_in,
                               const void* W, gq_dtype w_dt, int64_t d_out,
@@ -185,7 +224,7 @@ gq_status lnq_codebook_update(const float* F, int32_t groups, int64_t d_in,
  * objective, and among equal minimisers the lowest index wins.
  * P [d_out][d_in] is read and overwritten; C [d_out][m] is read.  The number of
  * coordinates that changed is added to *n_changed (device int64, may be NULL).
- * block: as gq_lnq_options.block (64).
+ * block: as gq_lnq_options.block (64, 128, 256 or 512).
  */
 gq_status lnq_assign_sweep(const float* F, int32_t groups, int64_t d_in,
                            const void* W, gq_dtype w_dt, int64_t d_out,

@@ -14,16 +14,20 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libgq.so")
 
-GQ_OK, GQ_EINVAL, GQ_ESHAPE, GQ_EDTYPE, GQ_ENOMEM, GQ_EHIP, GQ_ENOTIMPL = 0, 1, 2, 3, 4, 5, 8
+GQ_OK, GQ_EINVAL, GQ_ESHAPE, GQ_EDTYPE, GQ_ENOMEM, GQ_EHIP = 0, 1, 2, 3, 4, 5
+GQ_ENOTPD, GQ_ENONFINITE, GQ_ENOTIMPL = 6, 7, 8
 GQ_F32, GQ_BF16 = 0, 1
 GQ_INIT_QUANTILE, GQ_INIT_GIVEN, GQ_INIT_UNIFORM = 0, 1, 2
 GQ_GRAM_AUTO, GQ_GRAM_DENSE = 0, 1
-ABI_VERSION = 6
+GQ_FISHER_CHECK_FINITE = 2
+ABI_VERSION = 7
+DEFAULT_BLOCK = 512
 
 # every symbol include/gq.h declares
 EXPORTS = (
-    "gq_abi_version", "gq_last_error", "gq_lnq_options_default", "gq_fisher_workspace_size",
-    "gq_fisher_accumulate", "gq_lnq_workspace_size", "lnq_codebook_update", "lnq_assign_sweep",
+    "gq_abi_version", "gq_last_error", "gq_lnq_options_default", "lnq_options_default",
+    "gq_fisher_workspace_size", "gq_fisher_accumulate", "gq_lnq_workspace_size",
+    "lnq_workspace_size", "lnq_codebook_update", "lnq_assign_sweep",
     "lnq_objective", "lnq_quantize", "grid_quantize", "lut_packed_row_words", "lut_pack_codes",
     "lut_gemv", "gq_fisher_stream_workspace_size", "gq_fisher_accumulate_host",
     "ganq_workspace_size", "ganq_quantize", "ganq_factor_damped",
@@ -40,9 +44,10 @@ class GQError(RuntimeError):
 
 
 class lnq_options(ctypes.Structure):
-    """gq_lnq_options (block, ridge_rel, init, gram_update)."""
+    """gq_lnq_options (block, ridge_rel, init, gram_update, ridge_abs, check_finite)."""
     _fields_ = [("block", ctypes.c_int32), ("ridge_rel", ctypes.c_float),
-                ("init", ctypes.c_int32), ("gram_update", ctypes.c_int32)]
+                ("init", ctypes.c_int32), ("gram_update", ctypes.c_int32),
+                ("ridge_abs", ctypes.c_float), ("check_finite", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -51,10 +56,12 @@ _SIGS = {
     "gq_abi_version": (ctypes.c_int, []),
     "gq_last_error": (ctypes.c_char_p, []),
     "gq_lnq_options_default": (None, [ctypes.POINTER(lnq_options)]),
+    "lnq_options_default": (None, [ctypes.POINTER(lnq_options)]),
     "gq_fisher_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "gq_fisher_accumulate": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _i32, _vp,
                                             _i32, _vp, _sz, _vp]),
     "gq_lnq_workspace_size": (_sz, [_i64, _i64, _i32, _i32, _i32]),
+    "lnq_workspace_size": (_sz, [_i64, _i64, _i32, _i32, _i32]),
     "lnq_codebook_update": (ctypes.c_int, [_vp, _i32, _i64, _vp, _i32, _i64, _vp, _i32, _vp, _f32,
                                            _vp, _vp, _sz, _vp]),
     "lnq_assign_sweep": (ctypes.c_int, [_vp, _i32, _i64, _vp, _i32, _i64, _vp, _i32, _vp, _f32,
@@ -129,6 +136,31 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
     return t
 
 
+def _shape(t, shape, name):
+    """GQ_ESHAPE unless tensor t has exactly this shape (checked before any launch: the
+    C ABI sees only pointers, so a mis-shaped buffer would be read or written out of
+    bounds on the device)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise GQError(GQ_ESHAPE, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _counter(t, name, n=1):
+    """Optional device counter: int64 with at least n elements (its device is checked
+    with the other tensors)."""
+    if t is None:
+        return
+    if t.dtype != torch.int64 or t.numel() < n:
+        raise GQError(GQ_ESHAPE, f"{name} must be an int64 tensor of at least {n} element(s)")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise GQError(GQ_EINVAL, f"tensors on different devices: {sorted(map(str, devs))}")
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -144,15 +176,25 @@ def _ws(nbytes: int, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def _ws_arg(ws):
+    """(pointer, bytes) of a workspace tensor; ws=False passes NULL, which makes the
+    library allocate its scratch stream-ordered (hipMallocAsync / hipFreeAsync)."""
+    if ws is False or ws is None:
+        return None, 0
+    return _ptr(ws), ws.numel()
+
+
 def abi_version() -> int:
     return library().gq_abi_version()
 
 
-def options(block: int = 64, ridge_rel: float = 1e-6, init: int = GQ_INIT_QUANTILE,
-            gram_update: int = GQ_GRAM_AUTO) -> lnq_options:
+def options(block: int = DEFAULT_BLOCK, ridge_rel: float = 1e-6, init: int = GQ_INIT_QUANTILE,
+            gram_update: int = GQ_GRAM_AUTO, ridge_abs: float = 0.0,
+            check_finite: bool = False) -> lnq_options:
     o = lnq_options()
     library().gq_lnq_options_default(ctypes.byref(o))
     o.block, o.ridge_rel, o.init, o.gram_update = block, ridge_rel, init, gram_update
+    o.ridge_abs, o.check_finite = ridge_abs, int(bool(check_finite))
     return o
 
 
@@ -165,46 +207,63 @@ def lnq_workspace_size(d_out, d_in, groups, bits, w_dtype=GQ_BF16) -> int:
 
 
 def gq_fisher_accumulate(X, G, groups: int, F=None, accumulate: bool = False, ws=None,
-                         stream=None) -> torch.Tensor:
-    """F[g] (=|+=) X^T diag(s_g) X; X [n][d_in], G [n][d_out] (float32 or bfloat16)."""
+                         stream=None, check_finite: bool = False) -> torch.Tensor:
+    """F[g] (=|+=) X^T diag(s_g) X; X [n][d_in], G [n][d_out] (float32 or bfloat16).
+    check_finite: scan X and G for NaN / Inf first (GQError GQ_ENONFINITE, F untouched;
+    the call then synchronises the stream)."""
     lib = library()
-    _dev(X, "X")
-    _dev(G, "G")
+    if X.dim() != 2 or G.dim() != 2:
+        raise GQError(GQ_ESHAPE, "X and G must be 2-D")
     n, d_in = X.shape
     d_out = G.shape[1]
     if G.shape[0] != n:
         raise GQError(GQ_ESHAPE, "X and G need the same number of tokens")
+    _shape(F, (groups, d_in, d_in), "F")
+    _dev(X, "X")
+    _dev(G, "G")
     if F is None:
         F = torch.empty((groups, d_in, d_in), dtype=torch.float32, device=X.device)
         if accumulate:
             raise GQError(GQ_EINVAL, "accumulate needs an existing F")
     _dev(F, "F", torch.float32)
-    if tuple(F.shape) != (groups, d_in, d_in):
-        raise GQError(GQ_ESHAPE, "F must be [groups][d_in][d_in]")
+    _same_device(X, G, F, ws if isinstance(ws, torch.Tensor) else None)
     if ws is None:
         ws = _ws(fisher_workspace_size(n, d_in, d_out, groups, _dt(X)), X.device)
+    wp, wn = _ws_arg(ws)
+    flags = int(bool(accumulate)) | (GQ_FISHER_CHECK_FINITE if check_finite else 0)
     _check(lib.gq_fisher_accumulate(_ptr(X), _dt(X), n, d_in, _ptr(G), _dt(G), d_out, groups,
-                                    _ptr(F), int(bool(accumulate)), _ptr(ws),
-                                    0 if ws is None else ws.numel(), _stream(stream)))
+                                    _ptr(F), flags, wp, wn, _stream(stream)))
     return F
 
 
 fisher = gq_fisher_accumulate
 
 
-def _lnq_common(F, W, groups):
+def _lnq_common(F, W, groups, bits=None, C=None, P=None):
+    """Shapes first (no device needed), then device, dtype and contiguity."""
+    if W.dim() != 2 or F.dim() != 3:
+        raise GQError(GQ_ESHAPE, "W must be 2-D and F 3-D")
+    d_out, d_in = W.shape
+    _shape(F, (groups, d_in, d_in), "F")
+    if bits is not None:
+        _shape(C, (d_out, 1 << bits), "C")
+        _shape(P, (d_out, d_in), "P")
     _dev(F, "F", torch.float32)
     _dev(W, "W")
-    d_out, d_in = W.shape
-    if tuple(F.shape) != (groups, d_in, d_in):
-        raise GQError(GQ_ESHAPE, "F must be [groups][d_in][d_in]")
+    if C is not None:
+        _dev(C, "C", torch.float32)
+    if P is not None:
+        _dev(P, "P", torch.uint8)
+    _same_device(F, W, C, P)
     return d_out, d_in
 
 
 def _lnq_ws(ws, d_out, d_in, groups, bits, W):
     if ws is None:
         ws = _ws(lnq_workspace_size(d_out, d_in, groups, bits, _dt(W)), W.device)
-    return ws, (0 if ws is None else ws.numel())
+    elif ws is not False:
+        _same_device(W, ws)
+    return _ws_arg(ws)
 
 
 def lnq_codebook_update(F, W, P, C, bits: int, ridge_rel: float = 1e-6, n_not_pd=None,
@@ -212,27 +271,32 @@ def lnq_codebook_update(F, W, P, C, bits: int, ridge_rel: float = 1e-6, n_not_pd
     """One codebook step; C [d_out][2^bits] float32 is updated in place."""
     lib = library()
     groups = F.shape[0]
-    d_out, d_in = _lnq_common(F, W, groups)
-    _dev(P, "P", torch.uint8)
-    _dev(C, "C", torch.float32)
-    ws, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
+    _counter(n_not_pd, "n_not_pd")
+    d_out, d_in = _lnq_common(F, W, groups, bits, C, P)
+    if n_not_pd is not None:
+        _dev(n_not_pd, "n_not_pd")
+        _same_device(W, n_not_pd)
+    wp, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
     _check(lib.lnq_codebook_update(_ptr(F), groups, d_in, _ptr(W), _dt(W), d_out, _ptr(P), bits,
-                                   _ptr(C), ridge_rel, _ptr(n_not_pd), _ptr(ws), nb,
+                                   _ptr(C), ridge_rel, _ptr(n_not_pd), wp, nb,
                                    _stream(stream)))
     return C
 
 
-def lnq_assign_sweep(F, W, C, P, bits: int, ridge_rel: float = 1e-6, block: int = 64,
-                     n_changed=None, ws=None, stream=None) -> torch.Tensor:
+def lnq_assign_sweep(F, W, C, P, bits: int, ridge_rel: float = 1e-6,
+                     block: int = DEFAULT_BLOCK, n_changed=None, ws=None,
+                     stream=None) -> torch.Tensor:
     """One assignment pass; P [d_out][d_in] uint8 is updated in place."""
     lib = library()
     groups = F.shape[0]
-    d_out, d_in = _lnq_common(F, W, groups)
-    _dev(P, "P", torch.uint8)
-    _dev(C, "C", torch.float32)
-    ws, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
+    _counter(n_changed, "n_changed")
+    d_out, d_in = _lnq_common(F, W, groups, bits, C, P)
+    if n_changed is not None:
+        _dev(n_changed, "n_changed")
+        _same_device(W, n_changed)
+    wp, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
     _check(lib.lnq_assign_sweep(_ptr(F), groups, d_in, _ptr(W), _dt(W), d_out, _ptr(C), bits,
-                                _ptr(P), ridge_rel, block, _ptr(n_changed), _ptr(ws), nb,
+                                _ptr(P), ridge_rel, block, _ptr(n_changed), wp, nb,
                                 _stream(stream)))
     return P
 
@@ -242,49 +306,61 @@ def lnq_objective(F, W, C, P, bits: int, ridge_rel: float = 1e-6, obj_total=None
     """Per-row objectives e_j^T F' e_j (float64 [d_out])."""
     lib = library()
     groups = F.shape[0]
-    d_out, d_in = _lnq_common(F, W, groups)
-    _dev(P, "P", torch.uint8)
-    _dev(C, "C", torch.float32)
+    if obj_total is not None and (obj_total.dtype != torch.float64 or obj_total.numel() < 1):
+        raise GQError(GQ_ESHAPE, "obj_total must be a float64 tensor of at least one element")
+    d_out, d_in = _lnq_common(F, W, groups, bits, C, P)
+    if obj_total is not None:
+        _dev(obj_total, "obj_total")
+        _same_device(W, obj_total)
     rows = torch.empty(d_out, dtype=torch.float64, device=W.device)
-    ws, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
+    wp, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
     _check(lib.lnq_objective(_ptr(F), groups, d_in, _ptr(W), _dt(W), d_out, _ptr(C), _ptr(P),
-                             bits, ridge_rel, _ptr(rows), _ptr(obj_total), _ptr(ws), nb,
+                             bits, ridge_rel, _ptr(rows), _ptr(obj_total), wp, nb,
                              _stream(stream)))
     return rows
 
 
-def lnq_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float = 1e-6,
-                 C=None, P=None, init: int | None = None, trace: bool = True,
-                 ws=None, stream=None, gram_update: int = GQ_GRAM_AUTO):
-    """Whole LNQ on a layer.  Returns (C, P, obj_trace or None, n_changed).
-
-    With C and P given and init unset, starts from them (GQ_INIT_GIVEN).
-    """
-    lib = library()
-    groups = F.shape[0]
-    d_out, d_in = _lnq_common(F, W, groups)
+def _outputs(W, d_out, d_in, bits, C, P):
     m = 1 << bits
-    if init is None:
-        init = GQ_INIT_GIVEN if (C is not None and P is not None) else GQ_INIT_QUANTILE
     if C is None:
         C = torch.empty((d_out, m), dtype=torch.float32, device=W.device)
     if P is None:
         P = torch.empty((d_out, d_in), dtype=torch.uint8, device=W.device)
-    _dev(C, "C", torch.float32)
-    _dev(P, "P", torch.uint8)
+    return C, P
+
+
+def lnq_quantize(W, F, bits: int, iters: int, block: int = DEFAULT_BLOCK,
+                 ridge_rel: float = 1e-6, C=None, P=None, init: int | None = None,
+                 trace: bool = True, ws=None, stream=None, gram_update: int = GQ_GRAM_AUTO,
+                 ridge_abs: float = 0.0, check_finite: bool = False):
+    """Whole LNQ on a layer.  Returns (C, P, obj_trace or None, n_changed).
+
+    With C and P given and init unset, starts from them (GQ_INIT_GIVEN).
+    ridge_abs: fixed ridge added to ridge_rel * mean(diag F_g).  check_finite: a checked
+    call (GQ_ENONFINITE for NaN / Inf in W or F before anything is written, GQ_ENOTPD
+    after the run if a codebook system was not positive definite).  ws=False lets the
+    library allocate its scratch.
+    """
+    lib = library()
+    groups = F.shape[0]
+    if init is None:
+        init = GQ_INIT_GIVEN if (C is not None and P is not None) else GQ_INIT_QUANTILE
+    d_out, d_in = _lnq_common(F, W, groups, bits, C, P)
+    C, P = _outputs(W, d_out, d_in, bits, C, P)
     tr = torch.empty(2 * iters + 1, dtype=torch.float64, device=W.device) if trace else None
     nch = torch.zeros(max(iters, 1), dtype=torch.int64, device=W.device)
-    opt = options(block, ridge_rel, init, gram_update)
-    ws, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
+    opt = options(block, ridge_rel, init, gram_update, ridge_abs, check_finite)
+    wp, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
     _check(lib.lnq_quantize(_ptr(W), _dt(W), d_out, d_in, _ptr(F), groups, bits, iters,
-                            ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), _ptr(ws),
+                            ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), wp,
                             nb, _stream(stream)))
     return C, P, tr, nch[:iters]
 
 
-def grid_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float = 1e-6,
-                  C=None, P=None, init: int | None = None, trace: bool = True,
-                  ws=None, stream=None):
+def grid_quantize(W, F, bits: int, iters: int, block: int = DEFAULT_BLOCK,
+                  ridge_rel: float = 1e-6, C=None, P=None, init: int | None = None,
+                  trace: bool = True, ws=None, stream=None, ridge_abs: float = 0.0,
+                  check_finite: bool = False):
     """Fixed-grid backend: uniform grid per row, `iters` assignment passes.
 
     Returns (C, P, obj_trace [iters+1] or None, n_changed [iters]).  With C and P
@@ -292,22 +368,16 @@ def grid_quantize(W, F, bits: int, iters: int, block: int = 64, ridge_rel: float
     """
     lib = library()
     groups = F.shape[0]
-    d_out, d_in = _lnq_common(F, W, groups)
-    m = 1 << bits
     if init is None:
         init = GQ_INIT_GIVEN if (C is not None and P is not None) else GQ_INIT_UNIFORM
-    if C is None:
-        C = torch.empty((d_out, m), dtype=torch.float32, device=W.device)
-    if P is None:
-        P = torch.empty((d_out, d_in), dtype=torch.uint8, device=W.device)
-    _dev(C, "C", torch.float32)
-    _dev(P, "P", torch.uint8)
+    d_out, d_in = _lnq_common(F, W, groups, bits, C, P)
+    C, P = _outputs(W, d_out, d_in, bits, C, P)
     tr = torch.empty(iters + 1, dtype=torch.float64, device=W.device) if trace else None
     nch = torch.zeros(max(iters, 1), dtype=torch.int64, device=W.device)
-    opt = options(block, ridge_rel, init)
-    ws, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
+    opt = options(block, ridge_rel, init, GQ_GRAM_AUTO, ridge_abs, check_finite)
+    wp, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
     _check(lib.grid_quantize(_ptr(W), _dt(W), d_out, d_in, _ptr(F), groups, bits, iters,
-                             ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), _ptr(ws),
+                             ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), wp,
                              nb, _stream(stream)))
     return C, P, tr, nch[:iters]
 
@@ -330,12 +400,17 @@ def gq_fisher_accumulate_host(X, G, groups: int, F=None, accumulate: bool = Fals
     d_out = G.shape[1]
     if G.shape[0] != n:
         raise GQError(GQ_ESHAPE, "X and G need the same number of tokens")
+    if X.dtype != G.dtype:
+        raise GQError(GQ_EDTYPE, "X and G must share a dtype")
+    _shape(F, (groups, d_in, d_in), "F")
     dev = F.device if F is not None else (device or torch.device("cuda", torch.cuda.current_device()))
     if F is None:
         F = torch.empty((groups, d_in, d_in), dtype=torch.float32, device=dev)
         if accumulate:
             F.zero_()
     _dev(F, "F", torch.float32)
+    if ws is not None:
+        _same_device(F, ws)
     if ws is None:
         nb = fisher_stream_workspace_size(min(chunk_tokens, n), d_in, d_out, groups, _dt(X))
         ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
@@ -351,37 +426,35 @@ def ganq_workspace_size(d_out, d_in, groups, bits, w_dtype=GQ_BF16) -> int:
 
 
 def ganq_quantize(W, F, bits: int, iters: int, ridge_rel: float = 1e-6, C=None, P=None,
-                  init: int | None = None, trace: bool = True, ws=None, stream=None):
+                  init: int | None = None, trace: bool = True, ws=None, stream=None,
+                  ridge_abs: float = 0.0, check_finite: bool = False):
     """GANQ-style alternation.  Returns (C, P, obj_trace [2 iters + 1] or None,
     n_changed [iters], not_pd [groups] int32)."""
     lib = library()
     groups = F.shape[0]
-    d_out, d_in = _lnq_common(F, W, groups)
-    m = 1 << bits
     if init is None:
         init = GQ_INIT_GIVEN if (C is not None and P is not None) else GQ_INIT_QUANTILE
-    if C is None:
-        C = torch.empty((d_out, m), dtype=torch.float32, device=W.device)
-    if P is None:
-        P = torch.empty((d_out, d_in), dtype=torch.uint8, device=W.device)
-    _dev(C, "C", torch.float32)
-    _dev(P, "P", torch.uint8)
+    d_out, d_in = _lnq_common(F, W, groups, bits, C, P)
+    C, P = _outputs(W, d_out, d_in, bits, C, P)
     tr = torch.empty(2 * iters + 1, dtype=torch.float64, device=W.device) if trace else None
     nch = torch.zeros(max(iters, 1), dtype=torch.int64, device=W.device)
     npd = torch.zeros(groups, dtype=torch.int32, device=W.device)
-    opt = options(64, ridge_rel, init)
+    opt = options(DEFAULT_BLOCK, ridge_rel, init, GQ_GRAM_AUTO, ridge_abs, check_finite)
     if ws is None:
         ws = torch.empty(max(ganq_workspace_size(d_out, d_in, groups, bits, _dt(W)), 1),
                          dtype=torch.uint8, device=W.device)
+    wp, nb = _ws_arg(ws)
     _check(lib.ganq_quantize(_ptr(W), _dt(W), d_out, d_in, _ptr(F), groups, bits, iters,
                              ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), _ptr(npd),
-                             _ptr(ws), ws.numel(), _stream(stream)))
+                             wp, nb, _stream(stream)))
     return C, P, tr, nch[:iters], npd
 
 
 def ganq_factor_damped(F, ridge_rel: float = 1e-6, ws=None, stream=None):
     """(L [groups][d][d] float32 lower, not_pd [groups] int32) of F' = F + lambda I."""
     lib = library()
+    if F.dim() != 3 or F.shape[1] != F.shape[2]:
+        raise GQError(GQ_ESHAPE, "F must be [groups][d_in][d_in]")
     _dev(F, "F", torch.float32)
     groups, d_in = F.shape[0], F.shape[1]
     L = torch.empty_like(F)
@@ -402,29 +475,42 @@ def lut_pack_codes(P, bits: int, Q=None, stream=None) -> torch.Tensor:
     """P [d_out][d_in] uint8 -> packed codes Q [d_out][row words] (int32 storage of the
     uint32 words)."""
     lib = library()
-    _dev(P, "P", torch.uint8)
+    if P.dim() != 2:
+        raise GQError(GQ_ESHAPE, "P must be [d_out][d_in]")
     d_out, d_in = P.shape
     rw = lut_packed_row_words(d_in, bits)
+    _shape(Q, (d_out, max(rw, 1)), "Q")
+    _dev(P, "P", torch.uint8)
     if Q is None:
         Q = torch.empty((d_out, max(rw, 1)), dtype=torch.int32, device=P.device)
     _dev(Q, "Q", torch.int32)
+    _same_device(P, Q)
     _check(lib.lut_pack_codes(_ptr(P), d_out, d_in, bits, _ptr(Q), _stream(stream)))
     return Q
 
 
 def lut_gemv(Q, C, x, bits: int, d_in: int | None = None, y=None, stream=None) -> torch.Tensor:
-    """y [batch][d_out] = sum_i C[j][code_ji] x[b][i]; x [batch][d_in] or [d_in]."""
+    """y [batch][d_out] = sum_i C[j][code_ji] x[b][i]; x [batch][d_in] or [d_in]
+    (d_in, if given, must be x's last dimension)."""
     lib = library()
+    if x.dim() not in (1, 2) or C.dim() != 2:
+        raise GQError(GQ_ESHAPE, "x must be [batch][d_in] or [d_in] and C [d_out][2^bits]")
+    xx = x if x.dim() == 2 else x.unsqueeze(0)
+    batch, dx = xx.shape
+    if d_in is not None and d_in != dx:
+        raise GQError(GQ_ESHAPE, f"d_in={d_in} differs from the activations' {dx}")
+    d_in = dx
+    d_out = C.shape[0]
+    _shape(C, (d_out, 1 << bits), "C")
+    _shape(Q, (d_out, max(lut_packed_row_words(d_in, bits), 1)), "Q")
+    _shape(y, (batch, d_out), "y")
     _dev(Q, "Q", torch.int32)
     _dev(C, "C", torch.float32)
     _dev(x, "x")
-    xx = x if x.dim() == 2 else x.unsqueeze(0)
-    batch, dx = xx.shape
-    d_in = dx if d_in is None else d_in
-    d_out = C.shape[0]
     if y is None:
         y = torch.empty((batch, d_out), dtype=torch.float32, device=x.device)
     _dev(y, "y", torch.float32)
+    _same_device(Q, C, x, y)
     _check(lib.lut_gemv(_ptr(Q), _ptr(C), d_out, d_in, bits, _ptr(xx), _dt(xx), batch, _ptr(y),
                         _stream(stream)))
     return y if x.dim() == 2 else y[0]

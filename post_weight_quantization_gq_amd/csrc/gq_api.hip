@@ -19,7 +19,8 @@ static_assert((int)gq::ST_COUNT == (int)GQ_STAGE_COUNT, "stage ids of gq.h and t
 // Per-stage HIP-event timing.  When enabled, every launch sequence of a stage is
 // bracketed by two events recorded on the stream the kernels run on; reading
 // synchronises the recorded events, sums their elapsed times per stage and
-// returns the events to a pool.
+// returns the events to a pool.  A start mark is kept per (stage, stream), so
+// timed calls on different streams pair their own events.
 // ---------------------------------------------------------------------------
 namespace gq {
 namespace {
@@ -28,7 +29,7 @@ std::mutex g_tmu;
 struct Mark { int stage; hipEvent_t start, stop; };
 std::vector<Mark> g_marks;          // completed (start, stop) pairs
 std::vector<hipEvent_t> g_pool;     // reusable events
-hipEvent_t g_open[ST_COUNT];        // start event of a stage in progress
+std::map<std::pair<int, hipStream_t>, hipEvent_t> g_open;   // start event of a stage in progress
 bool g_err = false;                 // an event call failed since the last read
 
 hipEvent_t take_event() {
@@ -61,19 +62,25 @@ hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
 
 void timing_mark(Stage s, hipStream_t st, bool begin) {
     std::lock_guard<std::mutex> lk(g_tmu);
+    const std::pair<int, hipStream_t> key{(int)s, st};
+    auto it = g_open.find(key);
     hipEvent_t e = take_event();
     if (!e || hipEventRecord(e, st) != hipSuccess) {
         g_err = true;
         if (e) g_pool.push_back(e);
-        if (!begin && g_open[s]) { g_pool.push_back(g_open[s]); g_open[s] = nullptr; }
+        if (!begin && it != g_open.end()) { g_pool.push_back(it->second); g_open.erase(it); }
         return;
     }
     if (begin) {
-        if (g_open[s]) g_pool.push_back(g_open[s]);
-        g_open[s] = e;
-    } else if (g_open[s]) {
-        g_marks.push_back({(int)s, g_open[s], e});
-        g_open[s] = nullptr;
+        if (it != g_open.end()) {
+            g_pool.push_back(it->second);
+            it->second = e;
+        } else {
+            g_open.emplace(key, e);
+        }
+    } else if (it != g_open.end()) {
+        g_marks.push_back({(int)s, it->second, e});
+        g_open.erase(it);
     } else {
         g_pool.push_back(e);
     }
@@ -149,7 +156,48 @@ gq_status check_lnq_shape(const float* F, int32_t groups, int64_t d_in, const vo
     return GQ_OK;
 }
 
-bool block_ok(int32_t b) { return b == 64; }
+bool block_ok(int32_t b) { return b == 64 || b == 128 || b == 256 || b == 512; }
+
+int log2i(int32_t b) {
+    int k = 0;
+    while ((1 << k) < b) ++k;
+    return k;
+}
+
+// Checked calls: copy a device flag to the host once the stream has reached it.
+gq_status read_flag(const unsigned long long* dflag, hipStream_t st, unsigned long long* out) {
+    hipError_t e = hipMemcpyAsync(out, dflag, sizeof(*out), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "checked call");
+    return GQ_OK;
+}
+
+// NaN / Inf anywhere in W [d_out][d_in] or F [groups][d_in][d_in]: GQ_ENONFINITE, nothing
+// written (the flag lives in the workspace).
+gq_status check_lnq_inputs(const void* W, bool wb, int64_t d_out, int64_t d_in, const float* F,
+                           int groups, unsigned long long* dflag, hipStream_t st) {
+    hipError_t e = gq::lnq_zero_counter(dflag, 1, st);
+    if (e == hipSuccess) e = gq::scan_nonfinite(W, wb, d_out * d_in, dflag, st);
+    if (e == hipSuccess) e = gq::scan_nonfinite(F, false, (int64_t)groups * d_in * d_in, dflag, st);
+    if (e != hipSuccess) return hip_fail(e, "finite check");
+    unsigned long long bad = 0;
+    gq_status rc = read_flag(dflag, st, &bad);
+    if (rc != GQ_OK) return rc;
+    if (bad) return fail(GQ_ENONFINITE, "W or F holds NaN or Inf; nothing was written");
+    return GQ_OK;
+}
+
+bool ridge_ok(float r) { return r >= 0.f && std::isfinite(r); }
+
+// Option checks shared by the whole-layer entry points.
+gq_status check_options(const gq_lnq_options& o, int64_t d_in) {
+    if (!ridge_ok(o.ridge_abs)) return fail(GQ_EINVAL, "ridge_abs must be finite and >= 0");
+    if (o.check_finite != 0 && o.check_finite != 1) return fail(GQ_EINVAL, "check_finite must be 0 or 1");
+    if (!block_ok(o.block))
+        return fail(GQ_EINVAL, "block=%d: the assignment block is 64, 128, 256 or 512", o.block);
+    if (d_in % 64) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of 64", (long long)d_in);
+    return GQ_OK;
+}
 
 }  // namespace
 
@@ -197,17 +245,28 @@ const char* gq_last_error(void) { return g_last_error.c_str(); }
 
 void gq_lnq_options_default(gq_lnq_options* opt) {
     if (!opt) return;
-    opt->block = 64;
+    opt->block = 512;
     opt->ridge_rel = 1e-6f;
     opt->init = GQ_INIT_QUANTILE;
     opt->gram_update = GQ_GRAM_AUTO;
+    opt->ridge_abs = 0.f;
+    opt->check_finite = 0;
+}
+
+void lnq_options_default(lnq_options* opt) { gq_lnq_options_default(opt); }
+
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The Fisher kernels' scratch, then one 256-byte slot for the flag of a checked call.
+static size_t fisher_need(int64_t n, int64_t d_in, int32_t groups, bool bf16) {
+    return al256(gq::fisher_workspace(n, d_in, groups, bf16)) + 256;
 }
 
 size_t gq_fisher_workspace_size(int64_t n, int64_t d_in, int64_t d_out, int32_t groups,
                                 gq_dtype x_dt) {
     (void)d_out;
     if (n < 1 || d_in < 1 || groups < 1) return 0;
-    return gq::fisher_workspace(n, d_in, groups, x_dt == GQ_BF16);
+    return fisher_need(n, d_in, groups, x_dt == GQ_BF16);
 }
 
 gq_status gq_fisher_accumulate(const void* X, gq_dtype x_dt, int64_t n, int64_t d_in,
@@ -221,20 +280,31 @@ gq_status gq_fisher_accumulate(const void* X, gq_dtype x_dt, int64_t n, int64_t 
     if (groups < 1) return fail(GQ_EINVAL, "groups must be >= 1");
     if (d_out % groups) return fail(GQ_ESHAPE, "d_out=%lld is not a multiple of groups=%d",
                                     (long long)d_out, groups);
-    if (accumulate != 0 && accumulate != 1) return fail(GQ_EINVAL, "accumulate must be 0 or 1");
-    if (!al16(X) || !al16(G) || !al16(F) || !al16(ws))
-        return fail(GQ_EINVAL, "X, G, F and ws must be 16-byte aligned");
+    if (accumulate & ~(1 | GQ_FISHER_CHECK_FINITE))
+        return fail(GQ_EINVAL, "accumulate must be 0 or 1, optionally | GQ_FISHER_CHECK_FINITE");
+    if (!al16(X) || !al16(G) || !al16(F) || ((uintptr_t)ws & 255u))
+        return fail(GQ_EINVAL, "X, G and F must be 16-byte aligned, ws 256-byte aligned");
     hipStream_t st = (hipStream_t)stream;
     const bool bf16 = x_dt == GQ_BF16;
+    const size_t need = fisher_need(n, d_in, groups, bf16);
     Scratch s;
-    gq_status rc = s.acquire(ws, ws_bytes, gq::fisher_workspace(n, d_in, groups, bf16), st);
+    gq_status rc = s.acquire(ws, ws_bytes, need, st);
     if (rc != GQ_OK) return rc;
-    hipError_t e = gq::fisher_run(X, G, bf16, n, d_in, d_out, groups, F, accumulate, s.ptr, st);
+    hipError_t e;
+    if (accumulate & GQ_FISHER_CHECK_FINITE) {
+        unsigned long long* dflag = (unsigned long long*)((char*)s.ptr + need - 256);
+        e = gq::lnq_zero_counter(dflag, 1, st);
+        if (e == hipSuccess) e = gq::scan_nonfinite(X, bf16, n * d_in, dflag, st);
+        if (e == hipSuccess) e = gq::scan_nonfinite(G, bf16, n * d_out, dflag, st);
+        if (e != hipSuccess) return hip_fail(e, "finite check");
+        unsigned long long bad = 0;
+        if ((rc = read_flag(dflag, st, &bad)) != GQ_OK) return rc;
+        if (bad) return fail(GQ_ENONFINITE, "X or G holds NaN or Inf; F was not written");
+    }
+    e = gq::fisher_run(X, G, bf16, n, d_in, d_out, groups, F, accumulate & 1, s.ptr, st);
     if (e != hipSuccess) return hip_fail(e, "gq_fisher_accumulate");
     return GQ_OK;
 }
-
-static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t gq_fisher_stream_workspace_size(int64_t chunk_tokens, int64_t d_in, int64_t d_out,
                                        int32_t groups, gq_dtype x_dt) {
@@ -313,8 +383,14 @@ gq_status gq_fisher_accumulate_host(const void* X, gq_dtype x_dt, int64_t n, int
 
 size_t gq_lnq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_t bits,
                              gq_dtype w_dt) {
+    (void)w_dt;
     if (d_out < 1 || d_in < 1 || groups < 1 || bits < 1 || bits > 8) return 0;
     return gq::lnq_sizes(d_out, d_in, groups, 1 << bits).total;
+}
+
+size_t lnq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_t bits,
+                          gq_dtype w_dt) {
+    return gq_lnq_workspace_size(d_out, d_in, groups, bits, w_dt);
 }
 
 gq_status lnq_codebook_update(const float* F, int32_t groups, int64_t d_in, const void* W,
@@ -333,7 +409,7 @@ gq_status lnq_codebook_update(const float* F, int32_t groups, int64_t d_in, cons
     if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
     gq::LnqWs w = gq::lnq_carve(s.ptr, z);
     hipError_t e;
-    if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
+    if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, 0.0, w, st)) != hipSuccess) return hip_fail(e, "prepare");
     if ((e = gq::lnq_codebook_step(F, W, wb, d_out, d_in, groups, m, P, C, w, w.objA,
                                    (unsigned long long*)n_not_pd, nullptr, st)) != hipSuccess)
         return hip_fail(e, "codebook");
@@ -348,9 +424,8 @@ gq_status lnq_assign_sweep(const float* F, int32_t groups, int64_t d_in, const v
     if (rc != GQ_OK) return rc;
     if (!P || !C) return fail(GQ_EINVAL, "null P or C");
     if (!al16(P) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "P must be 16-byte and ws 256-byte aligned");
-    if (!block_ok(block)) return fail(GQ_EINVAL, "block=%d: the pass uses blocks of 64 coordinates", block);
-    if (d_in % block) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of block=%d",
-                                  (long long)d_in, block);
+    if (!block_ok(block)) return fail(GQ_EINVAL, "block=%d: the assignment block is 64, 128, 256 or 512", block);
+    if (d_in % 64) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of 64", (long long)d_in);
     hipStream_t st = (hipStream_t)stream;
     const bool wb = w_dt == GQ_BF16;
     const int m = 1 << bits;
@@ -358,9 +433,10 @@ gq_status lnq_assign_sweep(const float* F, int32_t groups, int64_t d_in, const v
     Scratch s;
     if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
     gq::LnqWs w = gq::lnq_carve(s.ptr, z);
+    w.sb_shift = log2i(block);
     hipError_t e;
-    if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
-    if ((e = gq::lnq_sweep_step(block, F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB, w.objC,
+    if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, 0.0, w, st)) != hipSuccess) return hip_fail(e, "prepare");
+    if ((e = gq::lnq_sweep_step(F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB, w.objC,
                                 (unsigned long long*)n_changed, false, st)) != hipSuccess)
         return hip_fail(e, "sweep");
     return GQ_OK;
@@ -382,7 +458,7 @@ gq_status lnq_objective(const float* F, int32_t groups, int64_t d_in, const void
     if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
     gq::LnqWs w = gq::lnq_carve(s.ptr, z);
     hipError_t e;
-    if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
+    if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, 0.0, w, st)) != hipSuccess) return hip_fail(e, "prepare");
     if ((e = gq::lnq_objective_rows(W, wb, d_out, d_in, groups, m, P, C, w, obj_rows, st)) != hipSuccess)
         return hip_fail(e, "objective");
     if (obj_total && (e = gq::lnq_reduce(obj_rows, d_out, obj_total, st)) != hipSuccess)
@@ -406,9 +482,7 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
         return fail(GQ_EINVAL, "unknown gram_update %d", o.gram_update);
     if (o.init != GQ_INIT_QUANTILE && o.init != GQ_INIT_GIVEN && o.init != GQ_INIT_UNIFORM)
         return fail(GQ_EINVAL, "unknown init %d", o.init);
-    if (!block_ok(o.block)) return fail(GQ_EINVAL, "block=%d: the pass uses blocks of 64 coordinates", o.block);
-    if (d_in % o.block) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of block=%d",
-                                    (long long)d_in, o.block);
+    if ((rc = check_options(o, d_in)) != GQ_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
     const bool wb = w_dt == GQ_BF16;
     const int m = 1 << bits;
@@ -416,8 +490,12 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
     Scratch s;
     if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
     gq::LnqWs w = gq::lnq_carve(s.ptr, z);
+    w.sb_shift = log2i(o.block);
+    if (o.check_finite && (rc = check_lnq_inputs(W, wb, d_out, d_in, F, groups, w.cnt + 8, st)) != GQ_OK)
+        return rc;
     hipError_t e;
-    if ((e = gq::lnq_prepare(F, groups, d_in, o.ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
+    if ((e = gq::lnq_prepare(F, groups, d_in, o.ridge_rel, o.ridge_abs, w, st)) != hipSuccess)
+        return hip_fail(e, "prepare");
     if (o.init == GQ_INIT_QUANTILE &&
         (e = gq::lnq_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
         return hip_fail(e, "init");
@@ -425,8 +503,7 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
         (e = gq::grid_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
         return hip_fail(e, "init");
     // w.cnt: [0] moves of the pass, [1] rows not positive definite, [2] update mode
-    if (iters > 0 && (e = gq::lnq_zero_counter(w.cnt, 3, st)) != hipSuccess)
-        return hip_fail(e, "counter");
+    if ((e = gq::lnq_zero_counter(w.cnt, 3, st)) != hipSuccess) return hip_fail(e, "counter");
     // A codebook step after a pass that changed at most incr_max codes updates A and the
     // residual from the changed coordinates (4 d bytes of F read per change, about
     // 3.5 ns per change at d = 4096) instead of recomputing them (2 d^2 d_out (m + 3)
@@ -443,7 +520,7 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
         // assignment pass; objB = objective after the codebook step (entry 2t-1), from
         // scratch; when recording, it also keeps the codes before it for the next step's
         // update
-        if ((e = gq::lnq_sweep_step(o.block, F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB,
+        if ((e = gq::lnq_sweep_step(F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB,
                                     w.objC, w.cnt, incremental && t < iters, st)) != hipSuccess)
             return hip_fail(e, "sweep");
         // trace entries 2t-2 and 2t-1, the pass's move count, counter cleared, next mode
@@ -460,6 +537,13 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
             return hip_fail(e, "final objective");
         if ((e = gq::lnq_reduce(w.objA, d_out, obj_trace + 2 * iters, st)) != hipSuccess)
             return hip_fail(e, "trace");
+    }
+    if (o.check_finite) {
+        unsigned long long npd = 0;
+        if ((rc = read_flag(w.cnt + 1, st, &npd)) != GQ_OK) return rc;
+        if (npd)
+            return fail(GQ_ENOTPD, "%llu codebook systems (rows x iterations) were not positive "
+                        "definite; those rows kept their codebook", npd);
     }
     return GQ_OK;
 }
@@ -480,9 +564,7 @@ gq_status grid_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_i
     if (o.init != GQ_INIT_UNIFORM && o.init != GQ_INIT_GIVEN)
         return fail(GQ_EINVAL, "grid_quantize keeps a uniform grid: init must be UNIFORM or GIVEN, not %d",
                     o.init);
-    if (!block_ok(o.block)) return fail(GQ_EINVAL, "block=%d: the pass uses blocks of 64 coordinates", o.block);
-    if (d_in % o.block) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of block=%d",
-                                    (long long)d_in, o.block);
+    if ((rc = check_options(o, d_in)) != GQ_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
     const bool wb = w_dt == GQ_BF16;
     const int m = 1 << bits;
@@ -490,8 +572,12 @@ gq_status grid_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_i
     Scratch s;
     if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
     gq::LnqWs w = gq::lnq_carve(s.ptr, z);
+    w.sb_shift = log2i(o.block);
+    if (o.check_finite && (rc = check_lnq_inputs(W, wb, d_out, d_in, F, groups, w.cnt + 8, st)) != GQ_OK)
+        return rc;
     hipError_t e;
-    if ((e = gq::lnq_prepare(F, groups, d_in, o.ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
+    if ((e = gq::lnq_prepare(F, groups, d_in, o.ridge_rel, o.ridge_abs, w, st)) != hipSuccess)
+        return hip_fail(e, "prepare");
     if (o.init == GQ_INIT_UNIFORM &&
         (e = gq::grid_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
         return hip_fail(e, "init");
@@ -500,7 +586,7 @@ gq_status grid_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_i
     for (int t = 1; t <= iters; ++t) {
         // assignment pass; objB = the objective before it, from the residual recomputed
         // from (C, P) at its start (trace entry t - 1)
-        if ((e = gq::lnq_sweep_step(o.block, F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB,
+        if ((e = gq::lnq_sweep_step(F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB,
                                     w.objC, w.cnt, false, st)) != hipSuccess)
             return hip_fail(e, "sweep");
         if (obj_trace && (e = gq::lnq_reduce(w.objB, d_out, obj_trace + t - 1, st)) != hipSuccess)
@@ -563,8 +649,9 @@ size_t ganq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_t 
 }
 
 static gq_status ganq_setup(const float* F, int32_t groups, int64_t d_in, int64_t d_out,
-                            int32_t bits, float ridge_rel, void* ws, size_t ws_bytes,
-                            hipStream_t st, Scratch& s, gq::LnqWs& w, gq::GanqWs& gw) {
+                            int32_t bits, float ridge_rel, float ridge_abs, const void* W,
+                            bool wb, bool check, void* ws, size_t ws_bytes, hipStream_t st,
+                            Scratch& s, gq::LnqWs& w, gq::GanqWs& gw) {
     const int m = 1 << bits;
     gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m);
     const size_t need = al256(z.total) + gq::ganq_extra_bytes(d_in, groups);
@@ -572,8 +659,11 @@ static gq_status ganq_setup(const float* F, int32_t groups, int64_t d_in, int64_
     if (rc != GQ_OK) return rc;
     w = gq::lnq_carve(s.ptr, z);
     gw = gq::ganq_carve((char*)s.ptr + al256(z.total), d_in, groups);
+    if (check && (rc = check_lnq_inputs(W, wb, d_out, d_in, F, groups, w.cnt + 8, st)) != GQ_OK)
+        return rc;
     hipError_t e;
-    if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, w, st)) != hipSuccess) return hip_fail(e, "prepare");
+    if ((e = gq::lnq_prepare(F, groups, d_in, ridge_rel, ridge_abs, w, st)) != hipSuccess)
+        return hip_fail(e, "prepare");
     if ((e = gq::ganq_factor(F, w.lam, d_in, groups, gw, st)) != hipSuccess) return hip_fail(e, "factor");
     return GQ_OK;
 }
@@ -590,7 +680,8 @@ gq_status ganq_factor_damped(const float* F, int32_t groups, int64_t d_in, float
     gq::LnqWs w;
     gq::GanqWs gw;
     // the factor needs no W-sized buffers: size them for one row
-    gq_status rc = ganq_setup(F, groups, d_in, groups, 1, ridge_rel, ws, ws_bytes, st, s, w, gw);
+    gq_status rc = ganq_setup(F, groups, d_in, groups, 1, ridge_rel, 0.f, nullptr, false, false,
+                              ws, ws_bytes, st, s, w, gw);
     if (rc != GQ_OK) return rc;
     hipError_t e = gq::ganq_factor_out(gw, d_in, groups, L, (int*)not_pd, st);
     if (e != hipSuccess) return hip_fail(e, "ganq_factor_damped");
@@ -611,14 +702,15 @@ gq_status ganq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_i
     if (iters < 0) return fail(GQ_EINVAL, "iters must be >= 0");
     if (o.init != GQ_INIT_QUANTILE && o.init != GQ_INIT_GIVEN && o.init != GQ_INIT_UNIFORM)
         return fail(GQ_EINVAL, "unknown init %d", o.init);
-    if (d_in % 64) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of 64", (long long)d_in);
+    if ((rc = check_options(o, d_in)) != GQ_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
     const bool wb = w_dt == GQ_BF16;
     const int m = 1 << bits;
     Scratch s;
     gq::LnqWs w;
     gq::GanqWs gw;
-    if ((rc = ganq_setup(F, groups, d_in, d_out, bits, o.ridge_rel, ws, ws_bytes, st, s, w, gw)) != GQ_OK)
+    if ((rc = ganq_setup(F, groups, d_in, d_out, bits, o.ridge_rel, o.ridge_abs, W, wb,
+                         o.check_finite != 0, ws, ws_bytes, st, s, w, gw)) != GQ_OK)
         return rc;
     hipError_t e;
     if (not_pd && (e = gq::ganq_factor_out(gw, d_in, groups, nullptr, (int*)not_pd, st)) != hipSuccess)
@@ -656,6 +748,17 @@ gq_status ganq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_i
             return hip_fail(e, "final objective");
         if ((e = gq::lnq_reduce(w.objA, d_out, obj_trace + 2 * iters, st)) != hipSuccess)
             return hip_fail(e, "trace");
+    }
+    if (o.check_finite) {
+        std::vector<int> bad(groups, 0);
+        e = hipMemcpyAsync(bad.data(), gw.bad, sizeof(int) * groups, hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_fail(e, "checked call");
+        int nbad = 0;
+        for (int b : bad) nbad += b != 0;
+        if (nbad)
+            return fail(GQ_ENOTPD, "%d groups' F' had a non-positive pivot; their rows kept their "
+                        "codes", nbad);
     }
     return GQ_OK;
 }

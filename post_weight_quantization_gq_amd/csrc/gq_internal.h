@@ -71,13 +71,16 @@ struct LnqWs {
     unsigned long long* items;    // work items of the update, longest first
     int* nitems;                  // their number
     float* dA;                    // per (row, coordinate slice): share of A_new - A_old
+    int sb_shift = 9;             // log2 of the assignment pass's super-block (64 .. 512),
+                                  // shared by the pass and the update from its moves
 };
 
 LnqSizes lnq_sizes(int64_t d_out, int64_t d, int groups, int m);
 LnqWs lnq_carve(void* base, const LnqSizes& z);
 size_t lnq_gram_partial_floats(int64_t d_out, int64_t d, int m);
-hipError_t lnq_prepare(const float* F, int groups, int64_t d, double rho, const LnqWs& w,
-                       hipStream_t st);
+// lambda_g = rho * mean(diag F_g) + lam_abs, the F' planes and diag(F')
+hipError_t lnq_prepare(const float* F, int groups, int64_t d, double rho, double lam_abs,
+                       const LnqWs& w, hipStream_t st);
 hipError_t lnq_init_run(const void* W, bool w_bf16, int64_t d_out, int64_t d, int m, float* C,
                         uint8_t* P, hipStream_t st);
 // uniform min-max grid per row (float32) and nearest codes
@@ -101,9 +104,10 @@ hipError_t lnq_codebook_step(const float* F, const void* W, bool w_bf16, int64_t
 hipError_t lnq_objective_rows(const void* W, bool w_bf16, int64_t d_out, int64_t d, int groups,
                               int m, const uint8_t* P, const float* C, const LnqWs& w,
                               double* obj, hipStream_t st);
-// assignment pass; obj_start/obj_end[j] = objective before / after it (may be null);
-// record: list the moves of each row (w.clist, w.ccount) for an update from them
-hipError_t lnq_sweep_step(int block, const float* F, const void* W, bool w_bf16, int64_t d_out,
+// assignment pass (super-blocks of 1 << w.sb_shift coordinates); obj_start/obj_end[j] =
+// objective before / after it (may be null); record: list the moves of each row (w.clist,
+// w.ccount) for an update from them
+hipError_t lnq_sweep_step(const float* F, const void* W, bool w_bf16, int64_t d_out,
                           int64_t d, int groups, const float* C, int m, uint8_t* P,
                           const LnqWs& w, double* obj_start, double* obj_end,
                           unsigned long long* counter, bool record, hipStream_t st);
@@ -115,6 +119,9 @@ hipError_t lnq_iter_tail(const double* objA, const double* objB, int64_t n, doub
                          unsigned long long* cnt, int64_t* n_changed, int64_t incr_max,
                          hipStream_t st);
 hipError_t lnq_store_counter(const unsigned long long* c, int64_t* dst, hipStream_t st);
+// *flag |= 1 when any of the n float32 / bfloat16 values at p is NaN or +-Inf
+hipError_t scan_nonfinite(const void* p, bool bf16, int64_t n, unsigned long long* flag,
+                          hipStream_t st);
 
 // LUT dequantisation GEMV (gq_lut.hip)
 int64_t lut_row_words(int64_t d_in, int bits);          // 32-bit words per packed row

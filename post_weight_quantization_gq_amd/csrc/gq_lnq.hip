@@ -33,10 +33,11 @@ namespace gq {
 constexpr int MAX_M = 16;
 
 // ---------------------------------------------------------------------------
-// lambda_g = rho * mean(diag F_g)
+// lambda_g = rho * mean(diag F_g) + lam_abs
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_ridge(const float* __restrict__ F, int64_t d,
-                                              double rho, double* __restrict__ lam) {
+                                              double rho, double lam_abs,
+                                              double* __restrict__ lam) {
     __shared__ double red[256];
     const int g = blockIdx.x;
     const float* Fg = F + (size_t)g * d * d;
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(256) void k_ridge(const float* __restrict__ F, int6
         if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
         __syncthreads();
     }
-    if (threadIdx.x == 0) lam[g] = (rho * red[0]) / (double)d;
+    if (threadIdx.x == 0) lam[g] = (rho * red[0]) / (double)d + lam_abs;
 }
 
 // ---------------------------------------------------------------------------
@@ -614,7 +615,8 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
 // ---------------------------------------------------------------------------
 // k_sweep: the assignment pass.  One block = 16 rows of one group, one row per
 // wave (16 waves).  Coordinates are visited in ascending order in blocks of 64
-// (one coordinate per lane), grouped into super-blocks of 512.
+// (one coordinate per lane), grouped into super-blocks of sbsz = 64 .. 512 (the
+// assignment block B of the options).
 //   * Effect of earlier moves on later residuals, in two levels on the matrix
 //     cores (v_mfma_f32_16x16x32_bf16, three products of bf16 hi/lo planes,
 //     D hi.F hi + D hi.F lo + D lo.F hi, float32 accumulation):
@@ -644,7 +646,7 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
 // ---------------------------------------------------------------------------
 constexpr int SW_ROWS = 16;     // rows (= waves) per block
 constexpr int SW_SUB = 64;      // coordinates per chain block (one per lane)
-constexpr int SW_SB = 512;      // coordinates per super-block
+constexpr int SW_SB = 512;      // largest super-block (the LDS arrays are sized for it)
 constexpr int SW_DP = SW_SB + 8;  // bf16 pitch of the LDS rows of D_sb
 constexpr int SW_RB = 4;        // F' chunks in flight per wave in the right-looking update
 
@@ -683,7 +685,7 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
     const float* __restrict__ C, int m, uint8_t* __restrict__ P, const void* __restrict__ W,
     float* __restrict__ R, double* __restrict__ obj_start, double* __restrict__ obj_end,
     unsigned long long* __restrict__ n_changed, uint32_t* __restrict__ clist,
-    int* __restrict__ ccount, uint8_t* __restrict__ pprev) {
+    int* __restrict__ ccount, uint8_t* __restrict__ pprev, int sbsz) {
     __shared__ __attribute__((aligned(16))) uint16_t dsb_hi[SW_ROWS][SW_DP];   // 16.3 KB
     __shared__ __attribute__((aligned(16))) uint16_t dsb_lo[SW_ROWS][SW_DP];   // 16.3 KB
     __shared__ float corr_p[4][SW_ROWS][SW_SUB];                               // 16 KB
@@ -742,8 +744,8 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
     const int ko = 8 * (lane >> 4);      // k offset of this lane in a 32-wide MFMA step
     const int mrow = lane & 15;          // A-operand row / B-operand column of this lane
 
-    for (int64_t sb0 = 0; sb0 < d; sb0 += SW_SB) {
-        const int sblen = (int)((d - sb0) < SW_SB ? (d - sb0) : SW_SB);
+    for (int64_t sb0 = 0; sb0 < d; sb0 += sbsz) {
+        const int sblen = (int)((d - sb0) < sbsz ? (d - sb0) : sbsz);
         if (tid < SW_SB / 32) chunk_moved[tid] = 0u;
         __syncthreads();
         for (int o = 0; o < sblen; o += SW_SUB) {
@@ -935,7 +937,8 @@ __device__ __forceinline__ void delta_pass(int n, const int* s_i, const float* s
                                            const float* __restrict__ Fg,
                                            const float* __restrict__ dFg, float* __restrict__ Rj,
                                            int64_t d, int c_begin, int c_end, int wave,
-                                           int lane, float (*hw)[16 * ((2 * M + 15) / 16)]) {
+                                           int lane, float (*hw)[16 * ((2 * M + 15) / 16)],
+                                           int sbshift) {
     constexpr int NB = (2 * M + 15) / 16;
     constexpr int CB = NT == 1 ? 4 : NT == 2 ? 2 : 1;
     const int mr = lane & 15, ko = 8 * (lane >> 4);
@@ -948,7 +951,7 @@ __device__ __forceinline__ void delta_pass(int n, const int* s_i, const float* s
         const bool ok = idx < n;
         ci[t] = ok ? s_i[idx] : -1;
         dl[t] = ok ? s_dl[idx] : 0.f;
-        sbi[t] = ok ? ci[t] / SW_SB : -1;
+        sbi[t] = ok ? ci[t] >> sbshift : -1;
         frow[t] = Fg + (ok ? (int64_t)ci[t] * d : 0);
     }
     f32x4 acc[NT][NB];
@@ -988,7 +991,7 @@ __device__ __forceinline__ void delta_pass(int n, const int* s_i, const float* s
             const int c = cb + 4 * b;
             if (c >= c_end) continue;                    // uniform in the wave
             const int k0 = 32 * c + ko;                  // this lane's 8 coordinates
-            const int sbk = (32 * c) / SW_SB;
+            const int sbk = (32 * c) >> sbshift;
             u32x4 oh[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -1130,7 +1133,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(M <= 8 ? 3 
     const uint8_t* __restrict__ Pold, const uint8_t* __restrict__ Pnew,
     const float* __restrict__ C, float* __restrict__ R, const uint32_t* __restrict__ clist,
     const int* __restrict__ ccount, const unsigned long long* __restrict__ items,
-    const int* __restrict__ nitems, int nslices, float* __restrict__ dA) {
+    const int* __restrict__ nitems, int nslices, float* __restrict__ dA, int sbshift) {
     constexpr int NB = (2 * M + 15) / 16;     // 16-column blocks of [old | new] one-hots
     __shared__ int s_i[DL_G];                 // coordinate of each change of the group
     __shared__ int s_uv[DL_G];                // old code | new code << 8
@@ -1170,10 +1173,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(M <= 8 ? 3 
         }
         __syncthreads();
         switch ((n + 15) >> 4) {
-            case 1: delta_pass<M, 1>(n, s_i, s_dl, po, pn, Fg, dFg, Rj, d, c_begin, c_end, wave, lane, s_h[wave]); break;
-            case 2: delta_pass<M, 2>(n, s_i, s_dl, po, pn, Fg, dFg, Rj, d, c_begin, c_end, wave, lane, s_h[wave]); break;
-            case 3: delta_pass<M, 3>(n, s_i, s_dl, po, pn, Fg, dFg, Rj, d, c_begin, c_end, wave, lane, s_h[wave]); break;
-            default: delta_pass<M, 4>(n, s_i, s_dl, po, pn, Fg, dFg, Rj, d, c_begin, c_end, wave, lane, s_h[wave]); break;
+            case 1: delta_pass<M, 1>(n, s_i, s_dl, po, pn, Fg, dFg, Rj, d, c_begin, c_end, wave, lane, s_h[wave], sbshift); break;
+            case 2: delta_pass<M, 2>(n, s_i, s_dl, po, pn, Fg, dFg, Rj, d, c_begin, c_end, wave, lane, s_h[wave], sbshift); break;
+            case 3: delta_pass<M, 3>(n, s_i, s_dl, po, pn, Fg, dFg, Rj, d, c_begin, c_end, wave, lane, s_h[wave], sbshift); break;
+            default: delta_pass<M, 4>(n, s_i, s_dl, po, pn, Fg, dFg, Rj, d, c_begin, c_end, wave, lane, s_h[wave], sbshift); break;
         }
         __syncthreads();
         // ---- this slice's part of A_new - A_old, entry (aq, aqq): X[aq][aqq] + Y[aqq][aq]
@@ -1259,6 +1262,35 @@ __global__ __launch_bounds__(256) void k_iter_tail(const double* __restrict__ ob
     if (threadIdx.x == 0) trace[blockIdx.x] = red[0];
 }
 
+// ---------------------------------------------------------------------------
+// Checked calls: *flag |= 1 if any of the n values (float32 or bfloat16) is NaN or
+// +-Inf (all exponent bits set).  16-byte vectors where whole, elements at the tail.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_nonfinite(const void* __restrict__ p, int64_t n,
+                                                  int bf16, unsigned long long* __restrict__ flag) {
+    const int64_t per_vec = bf16 ? 8 : 4;
+    const int64_t nvec = n / per_vec;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    bool bad = false;
+    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += stride) {
+        const u32x4 x = ((const u32x4*)p)[v];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (bf16) {
+                bad |= (x[k] & 0x7f80u) == 0x7f80u;
+                bad |= (x[k] & 0x7f800000u) == 0x7f800000u;
+            } else {
+                bad |= (x[k] & 0x7f800000u) == 0x7f800000u;
+            }
+        }
+    }
+    for (int64_t e = nvec * per_vec + (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += stride) {
+        if (bf16) bad |= (((const uint16_t*)p)[e] & 0x7f80u) == 0x7f80u;
+        else bad |= (((const uint32_t*)p)[e] & 0x7f800000u) == 0x7f800000u;
+    }
+    if (__ballot(bad) != 0ull && (threadIdx.x & 63) == 0) atomicOr(flag, 1ull);
+}
+
 __global__ void k_zero_u64(unsigned long long* __restrict__ p, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0ull;
@@ -1328,10 +1360,10 @@ LnqWs lnq_carve(void* base, const LnqSizes& z) {
     return w;
 }
 
-hipError_t lnq_prepare(const float* F, int groups, int64_t d, double rho, const LnqWs& w,
-                       hipStream_t st) {
+hipError_t lnq_prepare(const float* F, int groups, int64_t d, double rho, double lam_abs,
+                       const LnqWs& w, hipStream_t st) {
     StageTimer tm(ST_LNQ_PREPARE, st);
-    hipLaunchKernelGGL(k_ridge, dim3(groups), dim3(256), 0, st, F, d, rho, w.lam);
+    hipLaunchKernelGGL(k_ridge, dim3(groups), dim3(256), 0, st, F, d, rho, lam_abs, w.lam);
     GQ_LAUNCH_CHECK();
     const int64_t a_pad = lnq_pad256(d);
     const int64_t total = (int64_t)groups * (d / 16) * a_pad;
@@ -1427,7 +1459,7 @@ static hipError_t launch_delta(const unsigned long long* mode, const float* F, i
     GQ_LAUNCH_CHECK();
     hipLaunchKernelGGL((k_delta<M>), dim3((unsigned)(d_out * nsl)), dim3(256), 0, st, mode, F,
                        w.dF, d, d_out / groups, w.pprev, P, C, w.R, w.clist, w.ccount, w.items, w.nitems,
-                       nsl, w.dA);
+                       nsl, w.dA, w.sb_shift);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }
@@ -1488,18 +1520,18 @@ static hipError_t launch_sweep(const float* F, const void* W, int64_t d_out, int
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(1024), 0, st, F, w.dF, w.fhi,
                        w.flo, d, rpg, wgs, total, C, m, P, W, w.R, obj_start, obj_end, counter,
                        record ? w.clist : nullptr, record ? w.ccount : nullptr,
-                       record ? w.pprev : nullptr);
+                       record ? w.pprev : nullptr, 1 << w.sb_shift);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }
 
-hipError_t lnq_sweep_step(int block, const float* F, const void* W, bool w_bf16, int64_t d_out,
+hipError_t lnq_sweep_step(const float* F, const void* W, bool w_bf16, int64_t d_out,
                           int64_t d, int groups, const float* C, int m, uint8_t* P,
                           const LnqWs& w, double* obj_start, double* obj_end,
                           unsigned long long* counter, bool record, hipStream_t st) {
+    if (w.sb_shift < 6 || w.sb_shift > 9 || d % SW_SUB) return hipErrorInvalidValue;
     hipError_t e = lnq_residual_from(C, m, P, W, w_bf16, d_out, d, groups, w, nullptr, st);
     if (e != hipSuccess) return e;
-    if (block != SW_SUB) return hipErrorInvalidValue;
     StageTimer tm(ST_LNQ_SWEEP, st);
     return w_bf16 ? launch_sweep<true>(F, W, d_out, d, groups, C, m, P, w, obj_start, obj_end, counter, record, st)
                   : launch_sweep<false>(F, W, d_out, d, groups, C, m, P, w, obj_start, obj_end, counter, record, st);
@@ -1525,6 +1557,17 @@ hipError_t lnq_iter_tail(const double* objA, const double* objB, int64_t n, doub
 hipError_t lnq_zero_counter(unsigned long long* c, int n, hipStream_t st) {
     StageTimer tm(ST_LNQ_SMALL, st);
     hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, st, c, n);
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
+}
+
+hipError_t scan_nonfinite(const void* p, bool bf16, int64_t n, unsigned long long* flag,
+                          hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int64_t vecs = n / (bf16 ? 8 : 4) + 1;
+    const int64_t blocks = (vecs + 255) / 256;
+    hipLaunchKernelGGL(k_nonfinite, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0,
+                       st, p, n, bf16 ? 1 : 0, flag);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }

@@ -30,16 +30,23 @@ def test_exports_every_declared_symbol():
     assert declared == set(B.EXPORTS), declared ^ set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert gq.abi_version() == 6
+    assert gq.abi_version() == 7
 
 
 def test_options_default():
     o = gq.options()
     d = B.lnq_options()
     gq.library().gq_lnq_options_default(ctypes.byref(d))
-    assert (d.block, d.init, d.gram_update) == (64, 0, 0)
-    assert d.ridge_rel == pytest.approx(1e-6)
-    assert o.block == 64
+    assert (d.block, d.init, d.gram_update, d.check_finite) == (512, 0, 0, 0)
+    assert d.ridge_rel == pytest.approx(1e-6) and d.ridge_abs == 0.0
+    assert o.block == 512
+    # the problem statement's names are the same functions
+    e = B.lnq_options()
+    gq.library().lnq_options_default(ctypes.byref(e))
+    assert bytes(e) == bytes(d)
+    lib = gq.library()
+    for args in ((64, 256, 2, 3, 1), (4096, 4096, 4, 3, 1), (8192, 28672, 4, 4, 1)):
+        assert lib.lnq_workspace_size(*args) == lib.gq_lnq_workspace_size(*args) > 0
 
 
 def _err(lib):
@@ -58,7 +65,9 @@ def test_fisher_argument_errors():
     assert call(n=0) == B.GQ_ESHAPE
     assert call(d_out=9) == B.GQ_ESHAPE and "multiple" in _err(lib)
     assert call(groups=0) == B.GQ_EINVAL
-    assert call(acc=2) == B.GQ_EINVAL
+    assert call(acc=4) == B.GQ_EINVAL and "accumulate" in _err(lib)
+    assert call(acc=1 | B.GQ_FISHER_CHECK_FINITE, wsb=16) == B.GQ_EINVAL and \
+        "workspace too small" in _err(lib)
     assert call(F=FAKE_ODD) == B.GQ_EINVAL and "aligned" in _err(lib)
     assert call(wsb=16) == B.GQ_EINVAL and "workspace too small" in _err(lib)
 
@@ -85,9 +94,20 @@ def test_lnq_argument_errors():
     lib.gq_lnq_options_default(ctypes.byref(o))
     o.block = 96
     assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "block" in _err(lib)
-    o.block = 128
-    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL
-    assert q(d_in=352) == B.GQ_ESHAPE          # multiple of 32, not of the 64-wide block
+    for blk in (64, 128, 256, 512):           # every assignment block is accepted
+        o.block = blk
+        assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "workspace" in _err(lib)
+    o.block = 1024
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "block" in _err(lib)
+    o.block = 512
+    assert q(d_in=352) == B.GQ_ESHAPE          # multiple of 32, not of the 64-wide chain
+    o.ridge_abs = -1.0
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "ridge_abs" in _err(lib)
+    o.ridge_abs = float("nan")
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "ridge_abs" in _err(lib)
+    o.ridge_abs, o.check_finite = 0.0, 2
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "check_finite" in _err(lib)
+    o.check_finite = 0
     o.block, o.init = 64, 9
     assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL
     o.init, o.ridge_rel = 0, -1.0
@@ -125,6 +145,9 @@ def test_grid_argument_errors():
     # the options' default init (QUANTILE) is not a grid
     assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "UNIFORM" in _err(lib)
     o.init = B.GQ_INIT_UNIFORM
+    o.ridge_abs = -0.5
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "ridge_abs" in _err(lib)
+    o.ridge_abs = 0.0
     o.block = 96
     assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "block" in _err(lib)
     o.block = 64
@@ -213,6 +236,47 @@ def test_workspace_sizes_grow_with_shape():
     assert gq.lnq_workspace_size(0, 256, 2, 3) == 0
     assert gq.fisher_workspace_size(131072, 4096, 4096, 4) > gq.fisher_workspace_size(
         1024, 256, 64, 4) > 0
+
+
+def test_binding_rejects_mis_shaped_buffers_before_any_launch():
+    """The C ABI sees only pointers, so the binding checks every caller-supplied
+    buffer's shape (and counters' dtype) first: these CPU tensors never reach the
+    device check, let alone a kernel."""
+    import torch
+    W = torch.zeros(64, 256, dtype=torch.bfloat16)
+    F = torch.zeros(2, 256, 256)
+    C, P = torch.zeros(64, 8), torch.zeros(64, 256, dtype=torch.uint8)
+
+    def status(fn, *a, **k):
+        with pytest.raises(B.GQError) as ei:
+            fn(*a, **k)
+        return ei.value.status
+
+    assert status(gq.lnq_quantize, W, F, 3, 2, C=torch.zeros(64, 4), P=P) == B.GQ_ESHAPE
+    assert status(gq.lnq_quantize, W, F, 3, 2, C=C, P=P[:, :128]) == B.GQ_ESHAPE
+    assert status(gq.lnq_quantize, W, torch.zeros(2, 128, 128), 3, 2) == B.GQ_ESHAPE
+    assert status(gq.lnq_codebook_update, F, W, P, torch.zeros(64, 16), 3) == B.GQ_ESHAPE
+    assert status(gq.lnq_assign_sweep, F, W, C, P[:32], 3) == B.GQ_ESHAPE
+    assert status(gq.lnq_assign_sweep, F, W, C, P, 3,
+                  n_changed=torch.zeros(1, dtype=torch.int32)) == B.GQ_ESHAPE
+    assert status(gq.lnq_codebook_update, F, W, P, C, 3,
+                  n_not_pd=torch.zeros(0, dtype=torch.int64)) == B.GQ_ESHAPE
+    assert status(gq.lnq_objective, F, W, C, P, 3,
+                  obj_total=torch.zeros(1, dtype=torch.float32)) == B.GQ_ESHAPE
+    assert status(gq.grid_quantize, W, F, 2, 2, C=torch.zeros(64, 8), P=P) == B.GQ_ESHAPE
+    assert status(gq.ganq_quantize, W, F, 4, 1, C=torch.zeros(64, 8), P=P) == B.GQ_ESHAPE
+    X, G = torch.zeros(100, 256), torch.zeros(100, 64)
+    assert status(gq.gq_fisher_accumulate, X, G, 2, F=torch.zeros(2, 256, 255)) == B.GQ_ESHAPE
+    assert status(gq.gq_fisher_accumulate, X, G[:99], 2) == B.GQ_ESHAPE
+    Q = torch.zeros(64, gq.lut_packed_row_words(256, 3), dtype=torch.int32)
+    x = torch.zeros(2, 256, dtype=torch.bfloat16)
+    assert status(gq.lut_gemv, Q[:, :4], C, x, 3) == B.GQ_ESHAPE
+    assert status(gq.lut_gemv, Q, torch.zeros(64, 4), x, 3) == B.GQ_ESHAPE
+    assert status(gq.lut_gemv, Q, C, x, 3, d_in=300) == B.GQ_ESHAPE
+    assert status(gq.lut_gemv, Q, C, x, 3, y=torch.zeros(1, 64)) == B.GQ_ESHAPE
+    assert status(gq.lut_pack_codes, P, 3, Q=Q[:, :2]) == B.GQ_ESHAPE
+    # well-shaped host tensors only fail the device check
+    assert status(gq.lnq_quantize, W, F, 3, 2, C=C, P=P) == B.GQ_EINVAL
 
 
 def test_timing_read_empty():
