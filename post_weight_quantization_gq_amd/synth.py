@@ -18,7 +18,10 @@ Draw recipe (fixed order, one counter-based stream per tensor and chunk):
     then k outlier columns (chosen without replacement from their own stream)
     are multiplied by a factor;
   * W: N(0, std^2) or Student-t(4) rescaled to standard deviation std;
-  * G (end-loss output gradients): Laplace(0, b);
+  * G (end-loss output gradients): Laplace(0, b); optionally every token row
+    multiplied by exp(sigma z_t), z_t ~ N(0, 1) from its own stream (a strongly
+    token-dependent gradient scale, so the per-token weights of the Fisher vary
+    over orders of magnitude instead of a few percent);
   * every value is drawn in float32 (Laplace in float64, then cast) and
     rounded to bfloat16 with round-to-nearest-even where the workload stores
     bfloat16.
@@ -33,8 +36,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "make_inputs", "f32_to_bf16_bits",
-    "bf16_bits_to_f32", "decode", "random_codes", "random_codebooks",
-    "random_spd_fisher",
+    "bf16_bits_to_f32", "decode",
 ]
 
 
@@ -56,6 +58,7 @@ class Workload:
     w_std: float
     g_scale: float        # Laplace scale b of the output gradients
     index: int            # position in WORKLOADS (part of the stream key)
+    g_row_sigma: float = 0.0   # sigma of the log-normal per-token factor of G (0: none)
 
     @property
     def m(self) -> int:
@@ -85,7 +88,7 @@ WORKLOADS = {
                                 "gated", _outliers(0.001, 28672), 50.0, "t4", 0.01, 5e-5, 4),
 }
 
-_TENSOR_X, _TENSOR_XA, _TENSOR_XB, _TENSOR_OUT, _TENSOR_W, _TENSOR_G = range(6)
+_TENSOR_X, _TENSOR_XA, _TENSOR_XB, _TENSOR_OUT, _TENSOR_W, _TENSOR_G, _TENSOR_GROW = range(7)
 _CHUNK_ROWS = 4096
 
 
@@ -193,37 +196,11 @@ def make_inputs(wl: Workload | str, seed: int = 0, rows: int | None = None,
     if "G" in want:
         def fill_g(c, k):
             g = _gen(seed, wl.index, _TENSOR_G, c)
-            return g.laplace(0.0, wl.g_scale, size=(k, wl.d_out)).astype(np.float32)
+            x = g.laplace(0.0, wl.g_scale, size=(k, wl.d_out)).astype(np.float32)
+            if wl.g_row_sigma > 0:
+                z = _gen(seed, wl.index, _TENSOR_GROW, c).standard_normal((k, 1), dtype=np.float32)
+                x *= np.exp(np.float32(wl.g_row_sigma) * z)
+            return x
 
         res["G"] = _draw_rows(n, wl.d_out, fill_g, wl.dtype, out_dtype)
     return res
-
-
-# ----------------------------------------------------------------------------
-# Small helpers for per-stage tests: random LNQ states and random SPD Fishers.
-# ----------------------------------------------------------------------------
-
-def random_codes(rng: np.random.Generator, rows: int, d_in: int, m: int) -> np.ndarray:
-    return rng.integers(0, m, size=(rows, d_in), dtype=np.uint8)
-
-
-def random_codebooks(rng: np.random.Generator, rows: int, m: int, scale: float) -> np.ndarray:
-    return np.sort(rng.standard_normal((rows, m)).astype(np.float32) * np.float32(scale), axis=1)
-
-
-def random_spd_fisher(rng: np.random.Generator, groups: int, d_in: int, n: int,
-                      row_scale_sigma: float = 0.0) -> np.ndarray:
-    """float32 [groups][d_in][d_in] matrices Y^T Y from random Y (n x d_in).
-
-    With row_scale_sigma > 0 each token row of Y is multiplied by a log-normal
-    factor, which makes the per-token weighting strongly non-uniform.
-    """
-    out = np.empty((groups, d_in, d_in), dtype=np.float32)
-    for g in range(groups):
-        y = rng.standard_normal((n, d_in))
-        if row_scale_sigma > 0:
-            y *= np.exp(row_scale_sigma * rng.standard_normal((n, 1)))
-        out[g] = (y.T @ y / n).astype(np.float32)
-    # enforce exact symmetry of the stored float32 matrix
-    out = np.triu(out) + np.transpose(np.triu(out, 1), (0, 2, 1))
-    return np.ascontiguousarray(out, dtype=np.float32)

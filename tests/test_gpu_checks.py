@@ -1,0 +1,188 @@
+"""Checked calls, library-allocated workspace and the fixed ridge, on the GPU.
+
+  * check_finite / GQ_FISHER_CHECK_FINITE: a NaN or Inf planted in W, F, X or G
+    gives GQ_ENONFINITE and leaves every output untouched (sentinel values
+    survive); on clean inputs a checked call gives bitwise the unchecked result.
+  * GQ_ENOTPD: with ridge_rel = 0 and a group whose output gradients all vanish,
+    F'_g = 0 and the codebook system P^T F' P of its rows is singular (the closed
+    form of the blog page's "(codebook)" step does not exist there).  A checked
+    run reports it after completing; its outputs equal the unchecked run's.  The
+    GANQ alternation reports the group whose F' has no Cholesky factor.
+  * ws == NULL: the library allocates its scratch stream-ordered; results are
+    bitwise those of a caller workspace.
+  * fixed ridge (ridge_rel = 0, ridge_abs = lambda; the fixed-lambda
+    preconditioning of the GANQ summary page's ablation table): LNQ and GANQ end
+    to end within 1e-3 of the oracle's own runs with F' = F + lambda I.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import post_weight_quantization_gq_amd as gq
+from post_weight_quantization_gq_amd import synth
+
+from _util import f64, to_dev
+from test_gpu_lnq import MID, Problem, RHO, _wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mid(device):
+    return Problem(device, MID, seed=1)
+
+
+def _status(fn, *a, **k):
+    with pytest.raises(gq.GQError) as ei:
+        fn(*a, **k)
+    return ei.value.status
+
+
+def _sentinels(device, d_out, d_in, m):
+    C = torch.full((d_out, m), 7.25, dtype=torch.float32, device=device)
+    P = torch.full((d_out, d_in), 3, dtype=torch.uint8, device=device)
+    return C, P
+
+
+@pytest.mark.parametrize("where", ["W_nan", "W_inf", "F_nan", "F_inf"])
+def test_checked_quantizers_reject_nonfinite_untouched(device, mid, where):
+    W, F = mid.W.clone(), mid.F.clone()
+    bad = float("nan") if where.endswith("nan") else float("-inf")
+    if where.startswith("W"):
+        W[17, 300] = bad
+    else:
+        F[1, 5, 9] = bad
+    for fn, extra in ((gq.lnq_quantize, {}), (gq.grid_quantize, {}), (gq.ganq_quantize, {})):
+        C, P = _sentinels(device, MID.d_out, MID.d_in, 8)
+        init = gq.GQ_INIT_UNIFORM if fn is gq.grid_quantize else gq.GQ_INIT_QUANTILE
+        st = _status(fn, W, F, 3, 2, C=C, P=P, init=init, check_finite=True, **extra)
+        torch.cuda.synchronize()
+        assert st == gq.GQ_ENONFINITE, (fn.__name__, st)
+        assert torch.all(C == 7.25) and torch.all(P == 3), fn.__name__
+
+
+@pytest.mark.parametrize("where", ["X", "G"])
+def test_checked_fisher_rejects_nonfinite_untouched(device, where):
+    wl = _wl("chk", 256, 64, 1000, 2, 3, index=36)
+    inp = synth.make_inputs(wl, seed=2)
+    X, G = to_dev(inp["X"], device), to_dev(inp["G"], device)
+    if where == "X":
+        X[999, 255] = float("inf")
+    else:
+        G[0, 0] = float("nan")
+    F = torch.full((2, 256, 256), -1.5, dtype=torch.float32, device=device)
+    st = _status(gq.gq_fisher_accumulate, X, G, 2, F=F, check_finite=True)
+    torch.cuda.synchronize()
+    assert st == gq.GQ_ENONFINITE
+    assert torch.all(F == -1.5)
+
+
+def test_checked_calls_on_clean_inputs_equal_unchecked(device, mid):
+    a = gq.lnq_quantize(mid.W, mid.F, 3, 3)
+    b = gq.lnq_quantize(mid.W, mid.F, 3, 3, check_finite=True)
+    wl = _wl("chk2", 256, 64, 1000, 2, 3, index=37)
+    inp = synth.make_inputs(wl, seed=4)
+    X, G = to_dev(inp["X"], device), to_dev(inp["G"], device)
+    Fa = gq.gq_fisher_accumulate(X, G, 2)
+    Fb = gq.gq_fisher_accumulate(X, G, 2, check_finite=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert torch.equal(Fa, Fb)
+
+
+def _zero_group_problem(device):
+    wl = _wl("npd", 256, 64, 1024, 2, 3, index=38)
+    inp = synth.make_inputs(wl, seed=5)
+    G = synth.decode(inp["G"]).copy()
+    G[:, 32:] = 0.0
+    F32 = O.fisher(synth.decode(inp["X"]), G, 2).astype(np.float32)
+    F32 = np.ascontiguousarray((F32 + np.transpose(F32, (0, 2, 1))) * np.float32(0.5))
+    return to_dev(F32, device), to_dev(inp["W"], device)
+
+
+def test_checked_run_reports_singular_codebook_systems(device):
+    F, W = _zero_group_problem(device)
+    ref = gq.lnq_quantize(W, F, 3, 2, ridge_rel=0.0)
+    C, P = torch.empty_like(ref[0]), torch.empty_like(ref[1])
+    st = _status(gq.lnq_quantize, W, F, 3, 2, ridge_rel=0.0, C=C, P=P,
+                 init=gq.GQ_INIT_QUANTILE, check_finite=True)
+    torch.cuda.synchronize()
+    assert st == gq.GQ_ENOTPD
+    assert torch.equal(C, ref[0]) and torch.equal(P, ref[1])
+    # the GANQ alternation: group 1's F' = 0 has no factor
+    refg = gq.ganq_quantize(W, F, 3, 1, ridge_rel=0.0)
+    Cg, Pg = torch.empty_like(refg[0]), torch.empty_like(refg[1])
+    st = _status(gq.ganq_quantize, W, F, 3, 1, ridge_rel=0.0, C=Cg, P=Pg,
+                 init=gq.GQ_INIT_QUANTILE, check_finite=True)
+    torch.cuda.synchronize()
+    assert st == gq.GQ_ENOTPD
+    assert torch.equal(Cg, refg[0]) and torch.equal(Pg, refg[1])
+    # with the default ridge every group of this layer is positive definite except the
+    # zero one (lambda = rho * 0 = 0), which is still reported
+    assert _status(gq.lnq_quantize, W, F, 3, 1, check_finite=True) == gq.GQ_ENOTPD
+
+
+def test_library_allocated_workspace_matches(device, mid):
+    a = gq.lnq_quantize(mid.W, mid.F, 3, 3)
+    b = gq.lnq_quantize(mid.W, mid.F, 3, 3, ws=False)
+    c = gq.ganq_quantize(mid.W, mid.F, 3, 2)
+    d = gq.ganq_quantize(mid.W, mid.F, 3, 2, ws=False)
+    e = gq.grid_quantize(mid.W, mid.F, 3, 2)
+    f = gq.grid_quantize(mid.W, mid.F, 3, 2, ws=False)
+    wl = _wl("wsnull", 520, 64, 3000, 2, 3, index=39)
+    inp = synth.make_inputs(wl, seed=6)
+    X, G = to_dev(inp["X"], device), to_dev(inp["G"], device)
+    Fa = gq.gq_fisher_accumulate(X, G, 2)
+    Fb = gq.gq_fisher_accumulate(X, G, 2, ws=False)
+    rng = np.random.default_rng(3)
+    P0 = to_dev(rng.integers(0, 8, size=(MID.d_out, MID.d_in), dtype=np.uint8), device)
+    C0 = to_dev(np.sort(rng.standard_normal((MID.d_out, 8)).astype(np.float32) * 0.02, axis=1),
+                device)
+    Pa, Pb = P0.clone(), P0.clone()
+    gq.lnq_assign_sweep(mid.F, mid.W, C0, Pa, 3)
+    gq.lnq_assign_sweep(mid.F, mid.W, C0, Pb, 3, ws=False)
+    Ca, Cb = C0.clone(), C0.clone()
+    gq.lnq_codebook_update(mid.F, mid.W, P0, Ca, 3)
+    gq.lnq_codebook_update(mid.F, mid.W, P0, Cb, 3, ws=False)
+    oa = gq.lnq_objective(mid.F, mid.W, C0, P0, 3)
+    ob = gq.lnq_objective(mid.F, mid.W, C0, P0, 3, ws=False)
+    torch.cuda.synchronize()
+    for x, y in list(zip(a, b)) + list(zip(c, d)) + list(zip(e, f)):
+        assert torch.equal(x, y)
+    assert torch.equal(Fa, Fb) and torch.equal(Pa, Pb) and torch.equal(Ca, Cb)
+    assert torch.equal(oa, ob)
+
+
+def _fixed_lambda(prob, frac):
+    """A fixed ridge of `frac` times the mean diagonal of group 0's F: one absolute value
+    for every group (unlike the relative ridge, which follows each group's scale)."""
+    return float(frac * np.mean(np.diag(prob.F64[0])))
+
+
+@pytest.mark.parametrize("frac", [1e-6, 1e-2])
+def test_fixed_ridge_end_to_end(device, mid, frac):
+    lam = _fixed_lambda(mid, frac)
+    iters = 4
+    C, P, tr, _ = gq.lnq_quantize(mid.W, mid.F, 3, iters, ridge_rel=0.0, ridge_abs=lam)
+    Cg, Pg, trg, _, _ = gq.ganq_quantize(mid.W, mid.F, 3, iters, ridge_rel=0.0, ridge_abs=lam)
+    torch.cuda.synchronize()
+    C, P, Cg, Pg = f64(C), P.cpu().numpy(), f64(Cg), Pg.cpu().numpy()
+    tr = tr.cpu().numpy()
+    assert np.all(tr[1:] <= tr[:-1] * (1 + 1e-6)), tr
+    Fps = [O.damped(mid.F64[g], 0.0, lam) for g in range(MID.groups)]
+    gpu = ref = gpu_g = ref_g = 0.0
+    for j in range(MID.d_out):
+        Fp = Fps[j // mid.rpg]
+        _, _, t = O.lnq_row(Fp, mid.w[j], 8, iters, trace=False)
+        ref += t[-1]
+        gpu += O.objective(Fp, mid.w[j], C[j], P[j])
+        _, _, tg = O.ganq_row(Fp, mid.w[j], 8, iters)
+        ref_g += tg[-1]
+        gpu_g += O.objective(Fp, mid.w[j], Cg[j], Pg[j])
+    print(f"fixed lambda {lam:.3e}: LNQ gpu {gpu:.6e} oracle {ref:.6e}; GANQ gpu {gpu_g:.6e} "
+          f"oracle {ref_g:.6e}")
+    assert abs(gpu - ref) <= 1e-3 * ref
+    assert abs(gpu_g - ref_g) <= 1e-3 * ref_g
+    assert abs(tr[-1] - gpu) <= 1e-4 * gpu

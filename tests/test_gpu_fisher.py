@@ -1,9 +1,15 @@
 """GPU parity of the grouped Fisher (gq_fisher_accumulate) against the fp64 oracle.
 
-Bar: per group, ||F_gpu - F_ref||_F / ||F_ref||_F <= 2e-3 for bfloat16 inputs
-(bfloat16 operands, float32 accumulation); float32 inputs take the
-float64-accumulating path and must agree to float32 rounding (1e-6).
-The result must be exactly symmetric.
+Bars, for bfloat16 inputs (bfloat16 operands, float32 accumulation), per group:
+  * every entry: |F_gpu[a,b] - F_ref[a,b]| <= 2e-3 sqrt(F_ref[a,a] F_ref[b,b]).
+    The scaled operand s_g[t] X[t,b] is rounded once to bfloat16 (relative error
+    at most 2^-9 per token), so by Cauchy-Schwarz the error of an entry is at most
+    2^-9 sum_t s_g[t] |X[t,a] X[t,b]| <= 2^-9 sqrt(F_aa F_bb) < 1.96e-3 of that
+    scale, plus float32 summation error.  The bar holds on every entry, so an
+    off-diagonal tile cannot hide behind a few large diagonal entries;
+  * ||F_gpu - F_ref||_F / ||F_ref||_F <= 2e-3.
+float32 inputs take the float64-accumulating path and must agree to float32
+rounding (1e-6).  The result must be exactly symmetric.
 """
 import numpy as np
 import pytest
@@ -36,6 +42,25 @@ def _run(device, inp, groups, **kw):
 def _check_symmetric(F):
     assert torch.equal(F, F.transpose(1, 2)), "F is not exactly symmetric"
     assert torch.isfinite(F).all()
+
+
+def _check_entries(F64, ref, tol=BF16_TOL):
+    """Every entry within tol * sqrt(F_aa F_bb) of the oracle's, and the relative
+    Frobenius error within tol, per group."""
+    worst = 0.0
+    for g in range(ref.shape[0]):
+        dg = np.sqrt(np.maximum(np.diag(ref[g]), 0.0))
+        scale = np.outer(dg, dg)
+        err = np.abs(F64[g] - ref[g])
+        ok = err <= tol * scale
+        assert ok.all(), (g, np.argwhere(~ok)[:5], err[~ok][:5], scale[~ok][:5])
+        nz = scale > 0
+        if nz.any():
+            worst = max(worst, float(np.max(err[nz] / scale[nz])))
+        e = rel_fro(F64[g], ref[g]) if np.any(ref[g]) else float(np.abs(F64[g]).max())
+        assert e <= tol, (g, e)
+    print(f"worst entry error / sqrt(F_aa F_bb): {worst:.3e}")
+    return worst
 
 
 def test_fisher_tiny_f32(device):
@@ -71,11 +96,7 @@ def test_fisher_bf16_parity(device, d_in, d_out, n, groups, x_kind, outl):
     F = _run(device, inp, groups)
     ref = O.fisher(synth.decode(inp["X"]), synth.decode(inp["G"]), groups)
     _check_symmetric(F)
-    F64 = f64(F)
-    for g in range(groups):
-        err = rel_fro(F64[g], ref[g])
-        print(f"group {g}: rel Frobenius error {err:.3e}")
-        assert err <= BF16_TOL
+    _check_entries(f64(F), ref)
 
 
 def test_fisher_accumulate_streams_tokens(device):
@@ -88,8 +109,26 @@ def test_fisher_accumulate_streams_tokens(device):
     torch.cuda.synchronize()
     ref = O.fisher(synth.decode(inp["X"]), synth.decode(inp["G"]), 2)
     _check_symmetric(F)
-    for g in range(2):
-        assert rel_fro(f64(F[g]), ref[g]) <= BF16_TOL
+    _check_entries(f64(F), ref)
+
+
+@pytest.mark.parametrize("sigma", [1.0, 2.5])
+def test_fisher_token_dependent_gradients(device, sigma):
+    """Every token row of G scaled by a log-normal factor exp(sigma z_t): the per-token
+    weights s_g[t] then span orders of magnitude (not the few percent of i.i.d.
+    Laplace gradients), so F_g is far from a multiple of X^T X and the scaled operand
+    carries the guided weighting.  Same element-wise bar."""
+    wl = synth.Workload("lognormal", 776, 96, 5000, 3, 3, 1, 32, "bf16", "gated", 4, 30.0,
+                        "normal", 0.02, 1e-3, 25, g_row_sigma=sigma)
+    inp = synth.make_inputs(wl, seed=7)
+    S = O.group_scale(synth.decode(inp["G"]), 3)
+    spread = np.percentile(S, 99, axis=1) / np.percentile(S, 1, axis=1)
+    print(f"sigma {sigma}: s_g 99th / 1st percentile {spread}")
+    assert np.all(spread > 20.0)
+    F = _run(device, inp, 3)
+    ref = O.fisher(synth.decode(inp["X"]), synth.decode(inp["G"]), 3)
+    _check_symmetric(F)
+    _check_entries(f64(F), ref)
 
 
 def test_fisher_deterministic(device):

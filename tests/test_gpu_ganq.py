@@ -148,3 +148,32 @@ def test_ganq_zero_fisher_group_keeps_codes(device):
     torch.cuda.synchronize()
     assert npd.cpu().numpy().tolist() == [0, 1]
     assert torch.equal(P1[32:], P0[32:])
+
+
+def test_ganq_deterministic(device, mid):
+    """The factor runs its trailing updates on a second stream ordered by events; two
+    runs of the whole alternation give bitwise identical codebooks, codes, traces and
+    factors."""
+    a = gq.ganq_quantize(mid.W, mid.F, 3, 3, ridge_rel=RHO)
+    b = gq.ganq_quantize(mid.W, mid.F, 3, 3, ridge_rel=RHO)
+    La, _ = gq.ganq_factor_damped(mid.F, RHO)
+    Lb, _ = gq.ganq_factor_damped(mid.F, RHO)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert torch.equal(La, Lb)
+
+
+def test_ganq_deterministic_many_panels(device):
+    """Twelve 64-wide panels (the lookahead's second stream active for ten of them):
+    two factorizations are bitwise identical."""
+    rng = np.random.default_rng(99)
+    d = 768
+    X = rng.standard_normal((2 * d, d))
+    F32 = (X.T @ X / (2 * d)).astype(np.float32)
+    F32 = np.ascontiguousarray(((F32 + F32.T) * np.float32(0.5))[None])
+    F = to_dev(F32, "cuda")
+    La, _ = gq.ganq_factor_damped(F, RHO)
+    Lb, _ = gq.ganq_factor_damped(F, RHO)
+    torch.cuda.synchronize()
+    assert torch.equal(La, Lb)

@@ -33,7 +33,7 @@ def mid(device):
     return Problem(device, MID, seed=1)
 
 
-def _passes_one_at_a_time(prob, bits, iters, block=64):
+def _passes_one_at_a_time(prob, bits, iters, block=gq.DEFAULT_BLOCK):
     """The GPU trajectory pass by pass (each call starts from the previous C, P)."""
     C, P, tr0, _ = gq.grid_quantize(prob.W, prob.F, bits, 0, block=block, ridge_rel=RHO)
     states = [(f64(C), P.cpu().numpy())]
@@ -45,7 +45,7 @@ def _passes_one_at_a_time(prob, bits, iters, block=64):
     return states
 
 
-def _check_trajectory(prob, bits, iters, rows=None, block=64):
+def _check_trajectory(prob, bits, iters, rows=None, block=gq.DEFAULT_BLOCK):
     m = 1 << bits
     C, P, tr, nch = gq.grid_quantize(prob.W, prob.F, bits, iters, block=block, ridge_rel=RHO)
     torch.cuda.synchronize()

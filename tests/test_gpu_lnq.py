@@ -166,10 +166,12 @@ def _sweep_check(prob, C, P0, P1, tol=1e-5, frac=0.999):
     return P_ref
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_sweep_parity(device, mid, seed):
+@pytest.mark.parametrize("seed,block", [(0, 64), (1, 128), (2, 256), (0, 512)])
+def test_sweep_parity(device, mid, seed, block):
+    """One pass from a random state with every assignment block B (the super-block
+    whose moves are pushed into the residual array together): B changes only the
+    float32 summation order, so every decision must pass the replay for each."""
     rng = np.random.default_rng(100 + seed)
-    block = 64
     m = 8
     P0, C = _random_state(rng, MID.d_out, MID.d_in, m)
     Pd = to_dev(P0, device)
@@ -193,12 +195,12 @@ def test_sweep_from_codebook_state(device, mid):
         C[j] = c.astype(np.float32)
         P0[j] = p
     Pd = to_dev(P0, device)
-    gq.lnq_assign_sweep(mid.F, mid.W, to_dev(C, device), Pd, 3, RHO, block=64)
+    gq.lnq_assign_sweep(mid.F, mid.W, to_dev(C, device), Pd, 3, RHO)
     torch.cuda.synchronize()
     _sweep_check(mid, C, P0, Pd.cpu().numpy())
 
 
-def _end_to_end(device, prob, bits, iters, block=64, rows_checked=None, tol=1e-3):
+def _end_to_end(device, prob, bits, iters, block=gq.DEFAULT_BLOCK, rows_checked=None, tol=1e-3):
     wl = prob.wl
     m = 1 << bits
     C, P, tr, nch = gq.lnq_quantize(prob.W, prob.F, bits, iters, block=block, ridge_rel=RHO)
@@ -257,9 +259,10 @@ def test_lnq_deterministic(device, mid):
 
 
 @pytest.mark.parametrize("d_in,d_out,groups,bits,block", [
-    (576, 200, 2, 2, 64),      # ragged matrix-core tiles, ragged 16-row sweep groups
-    (256, 48, 1, 4, 64),       # m = 16
-    (1024, 64, 4, 1, 64),      # m = 2, four groups of 16 rows
+    (576, 200, 2, 2, 128),     # ragged matrix-core tiles and 16-row groups, a 64-wide last block
+    (256, 48, 1, 4, 256),      # m = 16
+    (1024, 64, 4, 1, 512),     # m = 2, four groups of 16 rows
+    (640, 96, 2, 3, 64),       # every 64 coordinates pushed into the residual array
 ])
 def test_lnq_end_to_end_shapes(device, d_in, d_out, groups, bits, block):
     wl = _wl("shape", d_in, d_out, 1536, groups, bits, block=block, index=31)
@@ -294,8 +297,8 @@ def _incr_max(d_out, d_in, m):
     return d_out * d_in * (m + 3) * 17 // 10000
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
-def test_incremental_codebook_step(device, mid, bits):
+@pytest.mark.parametrize("bits,block", [(2, 512), (3, 128), (4, 256), (3, 64)])
+def test_incremental_codebook_step(device, mid, bits, block):
     """The codebook step that follows a pass with few changes takes A = P^T F' P and
     the residual from the changed coordinates.  From the state the dense run reaches
     just before the first such step: the codebook it produces matches the oracle's
@@ -303,16 +306,19 @@ def test_incremental_codebook_step(device, mid, bits):
     before it, from the updated residual, matches the oracle's (1e-4)."""
     m = 1 << bits
     T = 40
-    Cd, Pd, trd, nchd = gq.lnq_quantize(mid.W, mid.F, bits, T, gram_update=gq.GQ_GRAM_DENSE)
+    Cd, Pd, trd, nchd = gq.lnq_quantize(mid.W, mid.F, bits, T, block=block,
+                                        gram_update=gq.GQ_GRAM_DENSE)
     torch.cuda.synchronize()
     nch = nchd.cpu().numpy()
     lim = _incr_max(MID.d_out, MID.d_in, m)
     ts = [t for t in range(2, T + 1) if nch[t - 2] <= lim]
     assert ts, (nch, lim)
     t = ts[0]                       # first iteration whose codebook step is incremental
-    Cp, Pp, trp, _ = gq.lnq_quantize(mid.W, mid.F, bits, t - 1, gram_update=gq.GQ_GRAM_DENSE)
-    Ca, Pa, tra, ncha = gq.lnq_quantize(mid.W, mid.F, bits, t)
-    Cb, Pb, trb, _ = gq.lnq_quantize(mid.W, mid.F, bits, t, gram_update=gq.GQ_GRAM_DENSE)
+    Cp, Pp, trp, _ = gq.lnq_quantize(mid.W, mid.F, bits, t - 1, block=block,
+                                     gram_update=gq.GQ_GRAM_DENSE)
+    Ca, Pa, tra, ncha = gq.lnq_quantize(mid.W, mid.F, bits, t, block=block)
+    Cb, Pb, trb, _ = gq.lnq_quantize(mid.W, mid.F, bits, t, block=block,
+                                     gram_update=gq.GQ_GRAM_DENSE)
     torch.cuda.synchronize()
     # identical up to the switch
     assert torch.equal(ncha[:t - 1].cpu(), nchd[:t - 1].cpu())
@@ -347,3 +353,59 @@ def test_incremental_and_dense_runs_agree(device, mid):
     assert np.all(a[1:] <= a[:-1] * (1 + 1e-6)), a
     print(f"final objective auto {a[-1]:.9e} dense {b[-1]:.9e}")
     assert abs(a[-1] - b[-1]) <= 1e-4 * b[-1]
+
+
+# ----------------------------------------------------------------------------
+# Strongly token-dependent gradients: every token row of G scaled by exp(2 z_t)
+# (log-normal), so the per-token Fisher weights span orders of magnitude and F_g is
+# far from a multiple of X^T X.  The guided weighting then matters; per-stage and end
+# to end parity as above.
+# ----------------------------------------------------------------------------
+
+LOGN = synth.Workload("lognormal", 512, 256, 2048, 2, 3, 5, 128, "bf16", "gated", 2, 30.0,
+                      "t4", 0.02, 1e-3, 35, g_row_sigma=2.0)
+
+
+@pytest.fixture(scope="module")
+def logn(device):
+    return Problem(device, LOGN, seed=3)
+
+
+def test_token_dependent_gradients_weighting_matters(logn):
+    """The guided F_g differs from the scaled unweighted X^T X by far more than the
+    parity bars (so these cases do exercise the weighting)."""
+    inp = synth.make_inputs(LOGN, seed=3)
+    X = synth.decode(inp["X"])
+    XtX = X.T @ X
+    for g in range(LOGN.groups):
+        Fg = logn.F64[g]
+        a = np.sum(Fg * XtX) / np.sum(XtX * XtX)
+        dev = np.linalg.norm(Fg - a * XtX) / np.linalg.norm(Fg)
+        print(f"group {g}: ||F_g - a X^T X|| / ||F_g|| = {dev:.3f}")
+        assert dev > 0.1
+
+
+def test_token_dependent_gradients_sweep_and_codebook(device, logn):
+    rng = np.random.default_rng(7)
+    m = 8
+    P0, C = _random_state(rng, LOGN.d_out, LOGN.d_in, m)
+    Pd = to_dev(P0, device)
+    gq.lnq_assign_sweep(logn.F, logn.W, to_dev(C, device), Pd, 3, RHO)
+    torch.cuda.synchronize()
+    _sweep_check(logn, C, P0, Pd.cpu().numpy())
+    Cs = np.empty((LOGN.d_out, m), np.float32)
+    Ps = np.empty((LOGN.d_out, LOGN.d_in), np.uint8)
+    for j in range(LOGN.d_out):
+        c, p = O.init_quantile(logn.w[j], m)
+        Cs[j], Ps[j] = c.astype(np.float32), p
+    got = _codebook_gpu(device, logn, Ps, Cs, 3)
+    worst = 0.0
+    for j in range(LOGN.d_out):
+        ref = O.codebook_update(logn.Fp_row(j), logn.w[j], Ps[j], Cs[j].astype(np.float64))
+        worst = max(worst, np.linalg.norm(got[j] - ref) / np.linalg.norm(ref))
+    print("token-dependent gradients: max codebook rel error", worst)
+    assert worst <= 1e-4
+
+
+def test_token_dependent_gradients_end_to_end(device, logn):
+    _end_to_end(device, logn, 3, 5)
