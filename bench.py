@@ -41,9 +41,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_MFMA = 2500e12      # dense bf16 matrix-core FLOP/s
-PEAK_FP32_VALU = 157.3e12     # fp32 vector FLOP/s (FMA = 2 flops, packed)
+# fp32 vector arithmetic: 256 compute units x 4 SIMDs x 16 lanes at 2.4 GHz = 39.3e12 lane
+# operations/s.  An FMA is 2 flops, so 78.6e12 FLOP/s with one FMA per lane per cycle, the
+# rate this build issues (its device code is compiled without packed fp32 instructions);
+# packed fp32 (two per lane per cycle) doubles it to the published 157.3e12.
+PEAK_FP32_VALU = 78.6e12      # fp32 vector FLOP/s this build can issue (unpacked FMA)
+PEAK_FP32_VALU_PACKED = 157.3e12
 PEAK_HBM = 8e12               # bytes/s
-PEAK_FP32_ADD = 78.6e12       # fp32 vector adds/s (one add per lane per cycle)
+PEAK_FP32_ADD = 78.6e12       # fp32 vector adds/s of the chip (packed: two adds per lane per cycle)
 PEAK_FP64_VALU = 78.6e12      # fp64 vector FLOP/s (FMA = 2 flops)
 PEAK_PCIE = 63.0e9            # host-to-device bytes/s, PCIe 5.0 x16 (32 GT/s x 16, 128b/130b)
 
@@ -64,8 +69,13 @@ def _parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (calibrates "
                          "the HBM byte counters against a kernel of known traffic)")
-    ap.add_argument("--cpu-rows", type=int, default=2)
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-rows", type=int, default=64,
+                    help="rows of the CPU baseline's LNQ sample (spread over the host cores)")
+    ap.add_argument("--cpu-tokens", type=int, default=16384,
+                    help="tokens of the CPU baseline's Fisher sample")
+    ap.add_argument("--block", type=int, default=512,
+                    help="assignment block B (64, 128, 256 or 512; the result is the same up "
+                         "to float32 summation order)")
     return ap.parse_args()
 
 
@@ -123,7 +133,7 @@ def _grid_roofline(wl, nchg, ms_step):
     t_scale = (2 * n * d_out + 4 * G * n) / PEAK_HBM
     t_fisher = n * d * (d + 1) * G / PEAK_BF16_MFMA
     t_bytes = it * (4 * G * d * d + d_out * d) / PEAK_HBM
-    t_alu = (it * d_out * 3 * m * d + 2 * d * float(np.sum(nchg))) / PEAK_FP32_VALU
+    t_alu = (it * d_out * 3 * m * d + 2 * d * float(np.sum(nchg))) / PEAK_FP32_VALU_PACKED
     t_roof = t_scale + t_fisher + t_bytes + t_alu
     return {"t_roof_ms": t_roof * 1e3, "t_measured_ms": ms_step, "frac": t_roof * 1e3 / ms_step,
             "terms_ms": {"group_scale": t_scale * 1e3, "fisher": t_fisher * 1e3,
@@ -162,7 +172,7 @@ def _layer_roofline(wl, nchg, ms_step):
     t_scale = (2 * n * d_out + 4 * G * n) / PEAK_HBM
     t_fisher = n * d * (d + 1) * G / PEAK_BF16_MFMA
     t_gram = it * max(d_out * d * d / PEAK_FP32_ADD, (4 * G * d * d + d_out * d) / PEAK_HBM)
-    t_upd = (it * d_out * 2 * d * m + 2 * d * float(np.sum(nchg))) / PEAK_FP32_VALU
+    t_upd = (it * d_out * 2 * d * m + 2 * d * float(np.sum(nchg))) / PEAK_FP32_VALU_PACKED
     t_roof = t_scale + t_fisher + t_gram + t_upd
     return {"t_roof_ms": t_roof * 1e3, "t_measured_ms": ms_step, "frac": t_roof * 1e3 / ms_step,
             "terms_ms": {"group_scale": t_scale * 1e3, "fisher": t_fisher * 1e3,
@@ -290,12 +300,12 @@ def main():
     def step():
         gq.gq_fisher_accumulate(X, G, wl.groups, F=F, ws=ws_f)
         if grid:
-            return gq.grid_quantize(W, F, wl.bits, wl.iters, block=64, ridge_rel=1e-6, C=C,
-                                    P=P, init=gq.GQ_INIT_UNIFORM, ws=ws_l)
+            return gq.grid_quantize(W, F, wl.bits, wl.iters, block=args.block, ridge_rel=1e-6,
+                                    C=C, P=P, init=gq.GQ_INIT_UNIFORM, ws=ws_l)
         if ganq:
             return gq.ganq_quantize(W, F, wl.bits, wl.iters, ridge_rel=1e-6, C=C, P=P,
                                     init=gq.GQ_INIT_QUANTILE, ws=ws_l)
-        return gq.lnq_quantize(W, F, wl.bits, wl.iters, block=64, ridge_rel=1e-6, C=C,
+        return gq.lnq_quantize(W, F, wl.bits, wl.iters, block=args.block, ridge_rel=1e-6, C=C,
                                P=P, init=gq.GQ_INIT_QUANTILE, ws=ws_l)
 
     warm = max(1, args.warmup)
@@ -331,8 +341,9 @@ def main():
 
     trace = outs[2].cpu().numpy()
     nchg = outs[3].cpu().numpy()
-    fisher_ms = per_step.get("group_scale", 0) + per_step.get("fisher_mfma", 0) + \
-        per_step.get("fisher_finalize", 0) + per_step.get("fisher_plain", 0)
+    fisher_stages = ("group_scale", "fisher_pack", "fisher_mfma", "fisher_finalize",
+                     "fisher_plain")
+    fisher_ms = sum(per_step.get(k, 0) for k in fisher_stages)
     lnq_ms = sum(v for k, v in per_step.items() if k.startswith("lnq"))
     sym_flops = wl.n * wl.d_in * (wl.d_in + 1) * wl.groups
 
@@ -353,6 +364,11 @@ def main():
                                 "copy-calibrated)",
                 "avg_launch_ms": avg_ms, "units_per_launch": per_launch,
                 "launches_per_step": n_launch}
+        if bound == "alu":
+            roof["peak_note"] = ("fp32 vector: 256 CUs x 64 lanes x 2.4 GHz x 2 (FMA) = 78.6 "
+                                 "TFLOP/s, the rate this build issues (packed fp32 off); the "
+                                 "published packed peak is 157.3")
+            roof["frac_of_packed_peak"] = achieved / PEAK_FP32_VALU_PACKED
 
     # every stage's fraction of its own bound, from the warm-up step's per-stage times
     stage_roof = {}
@@ -386,10 +402,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "path": args.path, "d_in": wl.d_in, "d_out": wl.d_out,
                    "n_tokens": wl.n, "groups": wl.groups, "bits": wl.bits, "iters": wl.iters,
-                   "block": 64},
+                   "block": args.block},
+        "fisher_ms": fisher_ms,
+        "fisher_ms_stages": list(k for k in fisher_stages if k in per_step),
         "fisher_tflops": sym_flops / (fisher_ms * 1e-3) / 1e12 if fisher_ms else None,
         "fisher_tflops_gemm_convention": (2 * wl.n * wl.d_in ** 2 * wl.groups) /
         (fisher_ms * 1e-3) / 1e12 if fisher_ms else None,
+        "fisher_contraction_only_tflops": sym_flops / (per_step["fisher_mfma"] * 1e-3) / 1e12
+        if per_step.get("fisher_mfma") else None,
         "lnq_rows_per_s": wl.d_out / (lnq_ms * 1e-3) if lnq_ms else None,
         "s_per_layer": ms_step * 1e-3,
         "stage_ms_per_step": {k: round(v, 4) for k, v in per_step.items()},
@@ -564,8 +584,46 @@ def run_stream(args):
     print(json.dumps(result), flush=True)
 
 
+def _cpu_info():
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        info["affinity"] = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        info["affinity"] = info["os_cpu_count"]
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return info
+
+
+def _oracle_row_worker(args):
+    """One row of the oracle in a worker process (spawned, single-threaded BLAS; F'
+    memory-mapped from the file the parent wrote).  Returns the row's seconds."""
+    path, w, m, iters, kind = args
+    import oracle as O
+    Fp = np.load(path, mmap_mode="r")
+    fn = {"grid": O.grid_row, "ganq": O.ganq_row}.get(kind, O.lnq_row)
+    t0 = time.perf_counter()
+    fn(Fp, w, m, iters)
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(wl, inp, F, args):
-    """Time the fp64 oracle on a bounded sample of the same layer, scaled to rows/s."""
+    """Time the fp64 oracle on a bounded sample of the same layer, scaled to rows/s.
+
+    Fisher leg: the oracle's float64 Fisher of the first --cpu-tokens tokens (numpy's
+    matmul on the host's BLAS threads), scaled to all tokens (the Fisher is a sum over
+    tokens).  LNQ leg: --cpu-rows rows of group 0 (rows are independent given F'_g),
+    one row per worker process at a time over min(16, host cores) spawned workers, each
+    on one BLAS thread; the sample's wall time is scaled to all rows."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
     import oracle as O
     from post_weight_quantization_gq_amd import synth
     try:
@@ -573,35 +631,60 @@ def cpu_baseline(wl, inp, F, args):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    info = _cpu_info()
+    workers = max(1, min(16, info["affinity"]))
     print("[bench] cpu baseline: oracle Fisher on a token sample", file=sys.stderr, flush=True)
     nt = min(args.cpu_tokens, wl.n)
     Xs = synth.decode(inp["X"][:nt])
     Gs = synth.decode(inp["G"][:nt])
     t0 = time.perf_counter()
     O.fisher(Xs, Gs, wl.groups)
-    t_f = (time.perf_counter() - t0) * (wl.n / nt)
-    print(f"[bench] cpu baseline: oracle {args.path} on {args.cpu_rows} rows", file=sys.stderr,
-          flush=True)
-    F64 = F.cpu().double().numpy()
-    w = synth.decode(inp["W"])
-    rpg = wl.d_out // wl.groups
-    rows = [(r * rpg) % wl.d_out for r in range(args.cpu_rows)]
-    t_rows = 0.0
-    row_fn = {"grid": O.grid_row, "ganq": O.ganq_row}.get(args.path, O.lnq_row)
-    for j in rows:
-        Fp = O.damped(F64[j // rpg], 1e-6)
-        t0 = time.perf_counter()
-        row_fn(Fp, w[j], wl.m, wl.iters)
-        t_rows += time.perf_counter() - t0
-    t_row = t_rows / len(rows)
-    t_layer = t_f + t_row * wl.d_out
-    return {"value": wl.d_out / t_layer, "unit": "rows/s", "cores": blas_threads,
+    t_f_meas = time.perf_counter() - t0
+    t_f = t_f_meas * (wl.n / nt)
+    del Xs, Gs
+    rows = min(args.cpu_rows, wl.d_out // wl.groups)
+    print(f"[bench] cpu baseline: oracle {args.path} on {rows} rows over {workers} worker "
+          f"processes", file=sys.stderr, flush=True)
+    Fp = O.damped(F[0].cpu().double().numpy(), 1e-6)
+    base = "/dev/shm" if os.path.isdir("/dev/shm") and \
+        shutil.disk_usage("/dev/shm").free > 2 * Fp.nbytes + (64 << 20) else None
+    tmp = tempfile.mkdtemp(prefix="gq_bench_", dir=base)
+    try:
+        path = os.path.join(tmp, "Fp.npy")
+        np.save(path, Fp)
+        del Fp
+        w = synth.decode(inp["W"][:rows])
+        saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}
+        for k in saved:
+            os.environ[k] = "1"
+        try:
+            pool = mp.get_context("spawn").Pool(workers)
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+        with pool:
+            pool.map(_oracle_row_worker, [(path, w[0], wl.m, 0, args.path)] * workers)  # warm
+            t0 = time.perf_counter()
+            per_row = pool.map(_oracle_row_worker,
+                               [(path, w[j], wl.m, wl.iters, args.path) for j in range(rows)])
+            t_rows = time.perf_counter() - t0
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    t_lnq = t_rows * wl.d_out / rows
+    t_layer = t_f + t_lnq
+    return {"value": wl.d_out / t_layer, "unit": "rows/s", "cores": max(workers, blas_threads),
             "kind": "oracle",
-            "sample": f"Fisher on the first {nt} of {wl.n} tokens (scaled x{wl.n / nt:g}, "
-                      f"{t_f * nt / wl.n:.1f}s measured) + {args.path} on {len(rows)} rows "
-                      f"({t_row:.2f}s/row, scaled to {wl.d_out} rows); LNQ rows run on one "
-                      f"core, the Fisher matmul on {blas_threads} BLAS threads",
-            "fisher_s_est": t_f, "lnq_s_per_row": t_row}
+            "sample": f"Fisher on the first {nt} of {wl.n} tokens ({t_f_meas:.1f}s measured on "
+                      f"{blas_threads} BLAS threads, scaled x{wl.n / nt:g}) + {args.path} on "
+                      f"{rows} rows of group 0 ({t_rows:.1f}s wall over {workers} worker "
+                      f"processes, {float(np.mean(per_row)):.2f}s per row on one core, scaled "
+                      f"to {wl.d_out} rows)",
+            "fisher_cores": blas_threads, "lnq_workers": workers, "lnq_rows": rows,
+            "fisher_s_est": t_f, "lnq_s_est": t_lnq, "lnq_s_per_row_one_core":
+            float(np.mean(per_row)), **info}
 
 
 if __name__ == "__main__":
