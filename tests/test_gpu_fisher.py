@@ -1,12 +1,16 @@
 """GPU parity of the grouped Fisher (gq_fisher_accumulate) against the fp64 oracle.
 
-Bars, for bfloat16 inputs (bfloat16 operands, float32 accumulation), per group:
-  * every entry: |F_gpu[a,b] - F_ref[a,b]| <= 2e-3 sqrt(F_ref[a,a] F_ref[b,b]).
-    The scaled operand s_g[t] X[t,b] is rounded once to bfloat16 (relative error
-    at most 2^-9 per token), so by Cauchy-Schwarz the error of an entry is at most
-    2^-9 sum_t s_g[t] |X[t,a] X[t,b]| <= 2^-9 sqrt(F_aa F_bb) < 1.96e-3 of that
-    scale, plus float32 summation error.  The bar holds on every entry, so an
-    off-diagonal tile cannot hide behind a few large diagonal entries;
+Bars, for bfloat16 inputs (bfloat16 operands, float32 accumulation), per group and
+on every entry, so an off-diagonal tile cannot hide behind a few large diagonal
+entries:
+  * |F_gpu[a,b] - F_ref[a,b]| <= (2^-8 + (n + 64) 2^-24) A[a,b] with
+    A[a,b] = sum_t s_g[t] |X[t,a] X[t,b]| (the oracle's Fisher of |X|).  The scaled
+    operand s_g[t] X[t,b] is rounded once to bfloat16 (8 significant bits: relative
+    error below 2^-8), the product with X[t,a] is exact, and float32 sums of n terms
+    add at most n 2^-24 of the absolute sum.  This bound holds for any token count;
+  * with n >= 64 tokens, |F_gpu[a,b] - F_ref[a,b]| <= 2e-3 sqrt(F_ref[a,a] F_ref[b,b])
+    (the rounding errors of many tokens average out; with a handful of tokens one
+    rounding alone can reach 2^-8 = 3.9e-3 of a diagonal entry);
   * ||F_gpu - F_ref||_F / ||F_ref||_F <= 2e-3.
 float32 inputs take the float64-accumulating path and must agree to float32
 rounding (1e-6).  The result must be exactly symmetric.
@@ -44,22 +48,34 @@ def _check_symmetric(F):
     assert torch.isfinite(F).all()
 
 
-def _check_entries(F64, ref, tol=BF16_TOL):
-    """Every entry within tol * sqrt(F_aa F_bb) of the oracle's, and the relative
-    Frobenius error within tol, per group."""
-    worst = 0.0
-    for g in range(ref.shape[0]):
+def _check_entries(F64, inp, groups, tol=BF16_TOL):
+    """The three bars of the module docstring, against the oracle's Fisher of the
+    stored inputs."""
+    X, G = synth.decode(inp["X"]), synth.decode(inp["G"])
+    n = X.shape[0]
+    ref = O.fisher(X, G, groups)
+    absref = O.fisher(np.abs(X), G, groups)
+    rigorous = 2.0 ** -8 + (n + 64) * 2.0 ** -24
+    worst = worst_abs = 0.0
+    for g in range(groups):
+        err = np.abs(F64[g] - ref[g])
+        ok = err <= rigorous * absref[g]
+        assert ok.all(), ("bound", g, np.argwhere(~ok)[:5], err[~ok][:5], absref[g][~ok][:5])
+        nz = absref[g] > 0
+        if nz.any():
+            worst_abs = max(worst_abs, float(np.max(err[nz] / absref[g][nz])))
         dg = np.sqrt(np.maximum(np.diag(ref[g]), 0.0))
         scale = np.outer(dg, dg)
-        err = np.abs(F64[g] - ref[g])
-        ok = err <= tol * scale
-        assert ok.all(), (g, np.argwhere(~ok)[:5], err[~ok][:5], scale[~ok][:5])
+        if n >= 64:
+            ok = err <= tol * scale
+            assert ok.all(), ("entry", g, np.argwhere(~ok)[:5], err[~ok][:5], scale[~ok][:5])
         nz = scale > 0
         if nz.any():
             worst = max(worst, float(np.max(err[nz] / scale[nz])))
         e = rel_fro(F64[g], ref[g]) if np.any(ref[g]) else float(np.abs(F64[g]).max())
         assert e <= tol, (g, e)
-    print(f"worst entry error / sqrt(F_aa F_bb): {worst:.3e}")
+    print(f"n={n}: worst entry error / sqrt(F_aa F_bb) {worst:.3e}, / sum_t s|x_a x_b| "
+          f"{worst_abs:.3e} (bound {rigorous:.3e})")
     return worst
 
 
@@ -94,9 +110,8 @@ def test_fisher_bf16_parity(device, d_in, d_out, n, groups, x_kind, outl):
                  index=22)
     inp = synth.make_inputs(wl, seed=d_in)
     F = _run(device, inp, groups)
-    ref = O.fisher(synth.decode(inp["X"]), synth.decode(inp["G"]), groups)
     _check_symmetric(F)
-    _check_entries(f64(F), ref)
+    _check_entries(f64(F), inp, groups)
 
 
 def test_fisher_accumulate_streams_tokens(device):
@@ -107,9 +122,8 @@ def test_fisher_accumulate_streams_tokens(device):
     gq.gq_fisher_accumulate(X[1500:].contiguous(), G[1500:].contiguous(), 2, F=F,
                             accumulate=True)
     torch.cuda.synchronize()
-    ref = O.fisher(synth.decode(inp["X"]), synth.decode(inp["G"]), 2)
     _check_symmetric(F)
-    _check_entries(f64(F), ref)
+    _check_entries(f64(F), inp, 2)
 
 
 @pytest.mark.parametrize("sigma", [1.0, 2.5])
@@ -126,9 +140,8 @@ def test_fisher_token_dependent_gradients(device, sigma):
     print(f"sigma {sigma}: s_g 99th / 1st percentile {spread}")
     assert np.all(spread > 20.0)
     F = _run(device, inp, 3)
-    ref = O.fisher(synth.decode(inp["X"]), synth.decode(inp["G"]), 3)
     _check_symmetric(F)
-    _check_entries(f64(F), ref)
+    _check_entries(f64(F), inp, 3)
 
 
 def test_fisher_deterministic(device):
