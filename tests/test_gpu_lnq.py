@@ -150,19 +150,28 @@ def test_codebook_parity_random_states(device, mid, bits, empty):
     assert worst_obj <= 1e-7
 
 
-def _sweep_check(prob, C, P0, P1, tol=1e-5, frac=0.999):
+def _sweep_check(prob, C, P0, P1, tol=1e-5, frac=0.999, codes_frac=0.999):
+    """Every GPU decision valid under the teacher-forced replay, >= frac of the
+    decisions identical to the fp64 choice from the same state (reading R14), and
+    (codes_frac, unless None) that share of the final codes identical."""
     d_out = P0.shape[0]
     P_ref = np.stack([O.assign_sweep(prob.Fp_row(j), prob.w[j], C[j].astype(np.float64), P0[j])
                       for j in range(d_out)])
     agree = float(np.mean(P_ref == P1))
     worst = -np.inf
+    differ = 0
     for j in range(d_out):
-        wj, _ = O.replay_sweep(prob.Fp_row(j), prob.w[j], C[j].astype(np.float64), P0[j], P1[j],
-                               tol)
+        wj, dj = O.replay_sweep(prob.Fp_row(j), prob.w[j], C[j].astype(np.float64), P0[j], P1[j],
+                                tol)
         worst = max(worst, wj)
-    print(f"sweep agreement {agree:.6f}, worst replay excess {worst:.3e}")
+        differ += dj
+    dec = 1.0 - differ / P0.size
+    print(f"sweep: decisions identical {dec:.6f}, final codes identical {agree:.6f}, worst "
+          f"replay excess {worst:.3e}")
     assert worst <= 0.0
-    assert agree >= frac
+    assert dec >= frac
+    if codes_frac is not None:
+        assert agree >= codes_frac
     return P_ref
 
 
@@ -392,7 +401,9 @@ def test_token_dependent_gradients_sweep_and_codebook(device, logn):
     Pd = to_dev(P0, device)
     gq.lnq_assign_sweep(logn.F, logn.W, to_dev(C, device), Pd, 3, RHO)
     torch.cuda.synchronize()
-    _sweep_check(logn, C, P0, Pd.cpu().numpy())
+    # after one valid near-tie a row may continue on another valid path, so the final
+    # codes are printed, and the bar is per decision
+    _sweep_check(logn, C, P0, Pd.cpu().numpy(), codes_frac=None)
     Cs = np.empty((LOGN.d_out, m), np.float32)
     Ps = np.empty((LOGN.d_out, LOGN.d_in), np.uint8)
     for j in range(LOGN.d_out):
