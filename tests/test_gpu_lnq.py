@@ -418,5 +418,72 @@ def test_token_dependent_gradients_sweep_and_codebook(device, logn):
     assert worst <= 1e-4
 
 
+def _teacher_forced(prob, states, rows):
+    """Every codebook step of a GPU trajectory within 1e-4 of the oracle's closed form
+    from the GPU's state before it (objective excess <= 1e-7), every pass replayed
+    decision by decision (all valid, >= 99.9 % identical); initial state identical."""
+    m = states[0][0].shape[1]
+    step = obj = rep = -np.inf
+    differ = dec = 0
+    for j in rows:
+        Fp, w = prob.Fp_row(j), prob.w[j]
+        c_init, p_init = O.init_quantile(w, m)
+        np.testing.assert_array_equal(states[0][0][j], c_init)
+        np.testing.assert_array_equal(states[0][1][j], p_init)
+        for t in range(1, len(states)):
+            c_prev, p_prev = states[t - 1][0][j], states[t - 1][1][j]
+            c_t, p_t = states[t][0][j], states[t][1][j]
+            ref = O.codebook_update(Fp, w, p_prev, c_prev)
+            step = max(step, np.linalg.norm(c_t - ref) / np.linalg.norm(ref))
+            o_ref = O.objective(Fp, w, ref, p_prev)
+            obj = max(obj, (O.objective(Fp, w, c_t, p_prev) - o_ref) / o_ref)
+            ex, dif = O.replay_sweep(Fp, w, c_t, p_prev, p_t, 1e-5)
+            rep = max(rep, ex)
+            differ += dif
+            dec += w.shape[0]
+    frac = 1.0 - differ / dec
+    print(f"teacher-forced: codebook {step:.2e}, objective excess {obj:.2e}, decisions "
+          f"identical {frac:.6f}, worst replay excess {rep:.2e}")
+    assert step <= 1e-4 and obj <= 1e-7 and rep <= 0.0 and frac >= 0.999
+
+
 def test_token_dependent_gradients_end_to_end(device, logn):
-    _end_to_end(device, logn, 3, 5)
+    """End to end on the token-dependent-gradient layer, teacher-forced on every row,
+    for the run that recomputes every step (one iteration per call; the chain equals one
+    call bit for bit) and the default mode (runs of 1 .. iters iterations).
+
+    A free-running comparison is printed but carries no bar here: LNQ's end point on
+    this layer is chaotic at the level of the GPU's float error.  Perturbing F by
+    random relative amounts of 7.6e-6 (the size of F' ~= hi + lo in two bfloat16
+    planes) moved the oracle's own 256-row sum by -7.9e-3 .. +1.9e-4 in six draws, and
+    single rows by up to 15 %, each run still a valid LNQ descent."""
+    iters, bits = 5, 3
+    C, P, tr, _ = gq.lnq_quantize(logn.W, logn.F, bits, iters, ridge_rel=RHO)
+    Cx, Px, _, _ = gq.lnq_quantize(logn.W, logn.F, bits, iters, ridge_rel=RHO,
+                                   gram_update=gq.GQ_GRAM_DENSE)
+    Ct, Pt, _, _ = gq.lnq_quantize(logn.W, logn.F, bits, 0)
+    dense = [(f64(Ct), Pt.cpu().numpy())]
+    for _ in range(iters):
+        Ct, Pt, _, _ = gq.lnq_quantize(logn.W, logn.F, bits, 1, C=Ct.clone(), P=Pt.clone(),
+                                       ridge_rel=RHO, gram_update=gq.GQ_GRAM_DENSE)
+        dense.append((f64(Ct), Pt.cpu().numpy()))
+    auto = [dense[0]]
+    for t in range(1, iters + 1):
+        Ca, Pa, _, _ = gq.lnq_quantize(logn.W, logn.F, bits, t, ridge_rel=RHO)
+        auto.append((f64(Ca), Pa.cpu().numpy()))
+    torch.cuda.synchronize()
+    assert torch.equal(Ct, Cx) and torch.equal(Pt, Px)
+    assert torch.equal(Ca, C) and torch.equal(Pa, P)
+    tr = tr.cpu().numpy()
+    assert np.all(tr[1:] <= tr[:-1] * (1 + 1e-6)), tr
+    rows = range(LOGN.d_out)
+    _teacher_forced(logn, dense, rows)
+    _teacher_forced(logn, auto, rows)
+    gpu = ref = 0.0
+    Cf, Pf = f64(C), P.cpu().numpy()
+    for j in rows:
+        _, _, t = O.lnq_row(logn.Fp_row(j), logn.w[j], 8, iters, trace=False)
+        ref += t[-1]
+        gpu += O.objective(logn.Fp_row(j), logn.w[j], Cf[j], Pf[j])
+    print(f"free running (no bar on this layer): gpu {gpu:.6e} oracle {ref:.6e} "
+          f"rel {(gpu - ref) / ref:+.2e}")
