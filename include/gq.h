@@ -44,8 +44,9 @@
  *             only state shared between calls is (a) the cache of kernel LDS
  *             limits already raised on each device (set once, under a lock),
  *             (b) the per-stage timing record (diagnostics, off unless
- *             gq_timing_enable is called; its marks are kept per stream), and
- *             the thread-local error string.
+ *             gq_timing_enable is called; its marks are kept per stream), (c)
+ *             the per-device scratch array of lnq_quantize_static, and the
+ *             thread-local error string.
  *   Errors.   Arguments are validated before anything is enqueued; on a
  *             non-OK status no output has been touched and gq_last_error()
  *             (thread-local) says why.  GQ_EHIP reports a failed HIP call.
@@ -264,6 +265,25 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
                        const gq_lnq_options* opt, float* C, uint8_t* P,
                        double* obj_trace, int64_t* n_changed,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * lnq_quantize for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments and
+ * results as lnq_quantize without ws / ws_bytes: the call's scratch is a fixed array of
+ * GQ_STATIC_SCRATCH_BYTES (64 MiB) per device inside the library (lnq_static_scratch_bytes
+ * returns it), held until the process ends, and the call itself allocates nothing.
+ * Layers whose gq_lnq_workspace_size exceeds it (e.g. beyond about 1536 x 1536 with
+ * m = 8) get GQ_ENOTIMPL before anything is enqueued.  Every call on one device shares
+ * that device's array, which keeps the previous call's contents (each call initialises
+ * what it reads): calls that overlap on one device, on any streams, race and corrupt
+ * each other's results, so serialise them.
+ */
+#define GQ_STATIC_SCRATCH_BYTES (64u << 20)
+size_t lnq_static_scratch_bytes(void);
+gq_status lnq_quantize_static(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in,
+                              const float* F, int32_t groups, int32_t bits, int32_t iters,
+                              const gq_lnq_options* opt, float* C, uint8_t* P,
+                              double* obj_trace, int64_t* n_changed, void* stream);
 
 /*
  * Fixed-grid scalar backend with the GuidedQuant objective.  The blog page says

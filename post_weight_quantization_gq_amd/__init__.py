@@ -6,7 +6,8 @@ on the CPU, and nothing here imports the oracle.
 """
 from .binding import (  # noqa: F401
     GQError, library, abi_version, options, fisher, gq_fisher_accumulate, lnq_codebook_update,
-    lnq_assign_sweep, lnq_objective, lnq_quantize, grid_quantize, lut_packed_row_words,
+    lnq_assign_sweep, lnq_objective, lnq_quantize, lnq_quantize_static, lnq_static_scratch_bytes,
+    grid_quantize, lut_packed_row_words,
     lut_pack_codes, lut_gemv, gq_fisher_accumulate_host, fisher_stream_workspace_size,
     ganq_workspace_size, ganq_quantize, ganq_factor_damped,
     fisher_workspace_size,

@@ -28,7 +28,8 @@ EXPORTS = (
     "gq_abi_version", "gq_last_error", "gq_lnq_options_default", "lnq_options_default",
     "gq_fisher_workspace_size", "gq_fisher_accumulate", "gq_lnq_workspace_size",
     "lnq_workspace_size", "lnq_codebook_update", "lnq_assign_sweep",
-    "lnq_objective", "lnq_quantize", "grid_quantize", "lut_packed_row_words", "lut_pack_codes",
+    "lnq_objective", "lnq_quantize", "lnq_quantize_static", "lnq_static_scratch_bytes",
+    "grid_quantize", "lut_packed_row_words", "lut_pack_codes",
     "lut_gemv", "gq_fisher_stream_workspace_size", "gq_fisher_accumulate_host",
     "ganq_workspace_size", "ganq_quantize", "ganq_factor_damped",
     "gq_timing_enable", "gq_timing_read", "gq_stage_name",
@@ -71,6 +72,10 @@ _SIGS = {
     "lnq_quantize": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _i32,
                                     ctypes.POINTER(lnq_options), _vp, _vp, _vp, _vp, _vp, _sz,
                                     _vp]),
+    "lnq_quantize_static": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _i32,
+                                           ctypes.POINTER(lnq_options), _vp, _vp, _vp, _vp,
+                                           _vp]),
+    "lnq_static_scratch_bytes": (_sz, []),
     "grid_quantize": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _i32,
                                      ctypes.POINTER(lnq_options), _vp, _vp, _vp, _vp, _vp, _sz,
                                      _vp]),
@@ -355,6 +360,32 @@ def lnq_quantize(W, F, bits: int, iters: int, block: int = DEFAULT_BLOCK,
                             ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), wp,
                             nb, _stream(stream)))
     return C, P, tr, nch[:iters]
+
+
+def lnq_quantize_static(W, F, bits: int, iters: int, block: int = DEFAULT_BLOCK,
+                        ridge_rel: float = 1e-6, C=None, P=None, init: int | None = None,
+                        trace: bool = True, stream=None, gram_update: int = GQ_GRAM_AUTO,
+                        ridge_abs: float = 0.0, check_finite: bool = False):
+    """lnq_quantize on the library's fixed per-device scratch (no workspace, nothing
+    allocated by the library; the outputs are still the caller's).  Calls that overlap
+    on one device race.  Returns (C, P, obj_trace or None, n_changed)."""
+    lib = library()
+    groups = F.shape[0]
+    if init is None:
+        init = GQ_INIT_GIVEN if (C is not None and P is not None) else GQ_INIT_QUANTILE
+    d_out, d_in = _lnq_common(F, W, groups, bits, C, P)
+    C, P = _outputs(W, d_out, d_in, bits, C, P)
+    tr = torch.empty(2 * iters + 1, dtype=torch.float64, device=W.device) if trace else None
+    nch = torch.zeros(max(iters, 1), dtype=torch.int64, device=W.device)
+    opt = options(block, ridge_rel, init, gram_update, ridge_abs, check_finite)
+    _check(lib.lnq_quantize_static(_ptr(W), _dt(W), d_out, d_in, _ptr(F), groups, bits, iters,
+                                   ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch),
+                                   _stream(stream)))
+    return C, P, tr, nch[:iters]
+
+
+def lnq_static_scratch_bytes() -> int:
+    return int(library().lnq_static_scratch_bytes())
 
 
 def grid_quantize(W, F, bits: int, iters: int, block: int = DEFAULT_BLOCK,

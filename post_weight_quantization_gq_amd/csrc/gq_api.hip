@@ -466,30 +466,37 @@ gq_status lnq_objective(const float* F, int32_t groups, int64_t d_in, const void
     return GQ_OK;
 }
 
-gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in, const float* F,
-                       int32_t groups, int32_t bits, int32_t iters, const gq_lnq_options* opt,
-                       float* C, uint8_t* P, double* obj_trace, int64_t* n_changed, void* ws,
-                       size_t ws_bytes, void* stream) {
-    gq_lnq_options o;
-    gq_lnq_options_default(&o);
-    if (opt) o = *opt;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of lnq_quantize (before anything is enqueued).
+gq_status lnq_quantize_check(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in,
+                             const float* F, int32_t groups, int32_t bits, int32_t iters,
+                             const gq_lnq_options& o, const float* C, const uint8_t* P) {
     gq_status rc = check_lnq_shape(F, groups, d_in, W, w_dt, d_out, bits, o.ridge_rel);
     if (rc != GQ_OK) return rc;
     if (!P || !C) return fail(GQ_EINVAL, "null P or C");
-    if (!al16(P) || ((uintptr_t)ws & 255u)) return fail(GQ_EINVAL, "P must be 16-byte and ws 256-byte aligned");
+    if (!al16(P)) return fail(GQ_EINVAL, "P must be 16-byte aligned");
     if (iters < 0) return fail(GQ_EINVAL, "iters must be >= 0");
     if (o.gram_update != GQ_GRAM_AUTO && o.gram_update != GQ_GRAM_DENSE)
         return fail(GQ_EINVAL, "unknown gram_update %d", o.gram_update);
     if (o.init != GQ_INIT_QUANTILE && o.init != GQ_INIT_GIVEN && o.init != GQ_INIT_UNIFORM)
         return fail(GQ_EINVAL, "unknown init %d", o.init);
-    if ((rc = check_options(o, d_in)) != GQ_OK) return rc;
-    hipStream_t st = (hipStream_t)stream;
+    return check_options(o, d_in);
+}
+
+// The LNQ run of lnq_quantize on a workspace `base` of at least lnq_sizes().total bytes
+// (arguments already checked).
+gq_status lnq_quantize_run(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in,
+                           const float* F, int32_t groups, int32_t bits, int32_t iters,
+                           const gq_lnq_options& o, float* C, uint8_t* P, double* obj_trace,
+                           int64_t* n_changed, void* base, hipStream_t st) {
+    gq_status rc;
     const bool wb = w_dt == GQ_BF16;
     const int m = 1 << bits;
     gq::LnqSizes z = gq::lnq_sizes(d_out, d_in, groups, m);
-    Scratch s;
-    if ((rc = s.acquire(ws, ws_bytes, z.total, st)) != GQ_OK) return rc;
-    gq::LnqWs w = gq::lnq_carve(s.ptr, z);
+    gq::LnqWs w = gq::lnq_carve(base, z);
     w.sb_shift = log2i(o.block);
     if (o.check_finite && (rc = check_lnq_inputs(W, wb, d_out, d_in, F, groups, w.cnt + 8, st)) != GQ_OK)
         return rc;
@@ -546,6 +553,80 @@ gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in
                         "definite; those rows kept their codebook", npd);
     }
     return GQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The scratch of lnq_quantize_static: one array per device, of fixed size, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address is taken once per device, with that device current, and
+// only that address is used (kernel arguments, workspace carving).
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)GQ_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;     // device ordinal -> device address of `scratch`
+
+gq_status static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it != g_scratch_ptr.end()) {
+        *out = it->second;
+        return GQ_OK;
+    }
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr.emplace(dev, ptr);
+    *out = ptr;
+    return GQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gq_status lnq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in, const float* F,
+                       int32_t groups, int32_t bits, int32_t iters, const gq_lnq_options* opt,
+                       float* C, uint8_t* P, double* obj_trace, int64_t* n_changed, void* ws,
+                       size_t ws_bytes, void* stream) {
+    gq_lnq_options o;
+    gq_lnq_options_default(&o);
+    if (opt) o = *opt;
+    gq_status rc = lnq_quantize_check(W, w_dt, d_out, d_in, F, groups, bits, iters, o, C, P);
+    if (rc != GQ_OK) return rc;
+    if ((uintptr_t)ws & 255u) return fail(GQ_EINVAL, "ws must be 256-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    Scratch s;
+    if ((rc = s.acquire(ws, ws_bytes, gq::lnq_sizes(d_out, d_in, groups, 1 << bits).total, st)) !=
+        GQ_OK)
+        return rc;
+    return lnq_quantize_run(W, w_dt, d_out, d_in, F, groups, bits, iters, o, C, P, obj_trace,
+                            n_changed, s.ptr, st);
+}
+
+size_t lnq_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+gq_status lnq_quantize_static(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in,
+                              const float* F, int32_t groups, int32_t bits, int32_t iters,
+                              const gq_lnq_options* opt, float* C, uint8_t* P, double* obj_trace,
+                              int64_t* n_changed, void* stream) {
+    gq_lnq_options o;
+    gq_lnq_options_default(&o);
+    if (opt) o = *opt;
+    gq_status rc = lnq_quantize_check(W, w_dt, d_out, d_in, F, groups, bits, iters, o, C, P);
+    if (rc != GQ_OK) return rc;
+    const size_t need = gq::lnq_sizes(d_out, d_in, groups, 1 << bits).total;
+    if (need > kStaticScratchBytes)
+        return fail(GQ_ENOTIMPL, "this layer needs %zu bytes of scratch; lnq_quantize_static "
+                    "holds %zu (use lnq_quantize with a workspace)", need, kStaticScratchBytes);
+    void* base = nullptr;
+    if ((rc = static_scratch(&base)) != GQ_OK) return rc;
+    return lnq_quantize_run(W, w_dt, d_out, d_in, F, groups, bits, iters, o, C, P, obj_trace,
+                            n_changed, base, (hipStream_t)stream);
 }
 
 gq_status grid_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in, const float* F,

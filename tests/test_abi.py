@@ -126,6 +126,23 @@ def test_lnq_argument_errors():
                              None) == B.GQ_EINVAL
 
 
+def test_static_entry_rejects_layers_beyond_its_scratch():
+    """lnq_quantize_static takes no workspace: a layer whose scratch exceeds the fixed
+    per-device array is refused before anything is enqueued (no pointer is touched)."""
+    lib = gq.library()
+    cap = gq.lnq_static_scratch_bytes()
+    assert cap == 64 << 20
+    assert gq.lnq_workspace_size(1024, 1024, 1, 3) <= cap < gq.lnq_workspace_size(4096, 4096, 4, 3)
+    st = lib.lnq_quantize_static(FAKE, 1, 4096, 4096, FAKE, 4, 3, 2, None, FAKE, FAKE, None, None,
+                                 None)
+    assert st == B.GQ_ENOTIMPL and "scratch" in _err(lib)
+    # argument checks come first, as for lnq_quantize
+    assert lib.lnq_quantize_static(FAKE, 1, 64, 256, None, 2, 3, 2, None, FAKE, FAKE, None, None,
+                                   None) == B.GQ_EINVAL
+    assert lib.lnq_quantize_static(FAKE, 1, 64, 256, FAKE, 2, 9, 2, None, FAKE, FAKE, None, None,
+                                   None) == B.GQ_EINVAL
+
+
 def test_grid_argument_errors():
     lib = gq.library()
     q = lambda **k: lib.grid_quantize(
