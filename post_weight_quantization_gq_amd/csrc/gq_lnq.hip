@@ -744,9 +744,28 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
     const int ko = 8 * (lane >> 4);      // k offset of this lane in a 32-wide MFMA step
     const int mrow = lane & 15;          // A-operand row / B-operand column of this lane
 
+    // Loads of the next 64-block of the same super-block, issued while the current
+    // block's chain runs: the diagonal 64 x 64 block of F (one float4 per thread), diag
+    // F' of the block, and this row's code and residual at its coordinate.  The first
+    // block of a super-block loads them itself, after the right-looking update that
+    // rewrites later residuals (nothing is carried across that update).
+    const int frr = tid >> 4, fcc = (tid & 15) * 4;
+    float4 pf_f = make_float4(0.f, 0.f, 0.f, 0.f);
+    float pf_d = 0.f, pf_r = 0.f;
+    int pf_code = 0;
+    auto prefetch = [&](int64_t bsn) {
+        pf_f = *(const float4*)(Fg + (bsn + frr) * d + bsn + fcc);
+        if (tid < SW_SUB) pf_d = dFg[bsn + tid];
+        if (rvalid) {
+            pf_code = P[j * d + bsn + lane];
+            pf_r = R[j * d + bsn + lane];
+        }
+    };
+
     for (int64_t sb0 = 0; sb0 < d; sb0 += sbsz) {
         const int sblen = (int)((d - sb0) < sbsz ? (d - sb0) : sbsz);
         if (tid < SW_SB / 32) chunk_moved[tid] = 0u;
+        prefetch(sb0);
         __syncthreads();
         for (int o = 0; o < sblen; o += SW_SUB) {
             const int64_t bs = sb0 + o;
@@ -771,21 +790,21 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
 #pragma unroll
                 for (int t = 0; t < 4; ++t) corr_p[sl][4 * (lane >> 4) + t][ct * 16 + mrow] = acc[t];
             }
-            // stage the diagonal 64 x 64 block of F (rows bs.., columns bs..)
-            {
-                const int rr = tid >> 4, cc = (tid & 15) * 4;
-                *(float4*)&fdb[rr][cc] = *(const float4*)(Fg + (bs + rr) * d + bs + cc);
-                if (tid < SW_SUB) fdd[tid] = dFg[bs + tid];
-            }
+            // the diagonal 64 x 64 block of F (rows bs.., columns bs..), loaded ahead
+            *(float4*)&fdb[frr][fcc] = pf_f;
+            if (tid < SW_SUB) fdd[tid] = pf_d;
+            const int code_in = pf_code;
+            const float r_in = pf_r;
             __syncthreads();
+            if (o + SW_SUB < sblen) prefetch(bs + SW_SUB);
 
             float dv = 0.f;
             if (rvalid) {
                 const int64_t col = bs + lane;
-                float r = R[j * d + col];
+                float r = r_in;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) r += corr_p[k][wave][lane];
-                int code = P[j * d + col];
+                int code = code_in;
                 if (pprev) pprev[j * d + col] = (uint8_t)code;   // the code before the pass
                 float wh = __shfl(cl, code, 64);
                 const float wh0 = wh;
