@@ -236,8 +236,8 @@ def _stage_units(stage, wl, nchg, grid=False, ganq=False):
     if stage == "group_scale":
         return "hbm", 2 * n * d_out + 4 * G * n, PEAK_HBM, "GB/s", None
     if stage == "fisher_pack":
-        # read X, write XT and YT (bf16)
-        return "hbm", 2 * n * d + 2 * (1 + G) * n * d, PEAK_HBM, "GB/s", None
+        # read X, write XT (bf16)
+        return "hbm", 2 * n * d + 2 * n * d, PEAK_HBM, "GB/s", None
     return None
 
 

@@ -57,7 +57,10 @@ def _wl(name, d_in, d_out, n, groups, bits=3, dtype="bf16", x_kind="gated", outl
 
 @pytest.mark.timeout(600)
 def test_fisher_multi_pass_sampled(device):
-    wl = _wl("multipass", 4096, 64, 40003, 64, index=41)
+    """A call beyond one pass's token limit (2^20 tokens) runs as two passes, the
+    second a ragged 4003 tokens, each adding into F; d_in 520 is three tiles, the last
+    ragged.  Sampled entries against the oracle's, each to the entry bar."""
+    wl = _wl("multipass", 520, 64, (1 << 20) + 4003, 4, index=41)
     inp = synth.make_inputs(wl, seed=0)
     _progress(f"multi-pass Fisher: n={wl.n} d_in={wl.d_in} groups={wl.groups}")
     X, G = to_dev(inp["X"], device), to_dev(inp["G"], device)
@@ -67,13 +70,13 @@ def test_fisher_multi_pass_sampled(device):
     assert torch.isfinite(F).all()
     S = O.group_scale(synth.decode(inp["G"]), wl.groups)
     rng = np.random.default_rng(3)
-    cols = set(int(c) for c in rng.choice(wl.d_in, 10, replace=False))
-    cols |= set(int(c) for c in inp["outlier_cols"][:2]) | {0, wl.d_in - 1}
+    cols = set(int(c) for c in rng.choice(wl.d_in, 16, replace=False))
+    cols |= set(int(c) for c in inp["outlier_cols"][:2]) | {0, 255, 256, 511, 512, wl.d_in - 1}
     cols = sorted(cols)
     xc = {c: synth.decode(inp["X"][:, c]) for c in cols}
     idx = torch.tensor(cols, device=device)
     num = den = 0.0
-    for g in range(0, wl.groups, 3):
+    for g in range(wl.groups):
         sub = F[g].index_select(0, idx).index_select(1, idx).cpu().double().numpy()
         np.testing.assert_array_equal(sub, sub.T)
         diag = {c: O.fisher_entry(xc[c], xc[c], S[g]) for c in cols}
