@@ -730,10 +730,30 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
     double dsum = 0.0;       // sum of the accepted changes (uniform in the wave)
     unsigned moves = 0;
 
-    // objective at the start of the pass, before R is updated
+    // objective at the start of the pass, before R is updated; the loads of 8 columns
+    // per lane are issued together (d % 64 == 0), the sum keeps the column order
     double ostart = 0.0;
     if (rvalid) {
-        for (int64_t col = lane; col < d; col += 64) {
+        const int64_t nck = d / 64;
+        int64_t c = 0;
+        for (; c + 8 <= nck; c += 8) {
+            float wv[8], rv[8];
+            int pv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t col = (c + u) * 64 + lane;
+                wv[u] = load_elem<WBF16>(W, j * d + col);
+                pv[u] = (int)P[j * d + col];
+                rv[u] = R[j * d + col];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float cv = __shfl(cl, pv[u], 64);
+                ostart += (double)(cv - wv[u]) * (double)rv[u];
+            }
+        }
+        for (; c < nck; ++c) {
+            const int64_t col = c * 64 + lane;
             const float wv = load_elem<WBF16>(W, j * d + col);
             const float cv = __shfl(cl, (int)P[j * d + col], 64);
             ostart += (double)(cv - wv) * (double)R[j * d + col];
