@@ -88,13 +88,13 @@ _CSRC = os.path.join(ROOT, "post_weight_quantization_gq_amd", "csrc")
 _TRAFFIC = {
     # stage: (workload, source file, digest, bytes read, bytes written) of its main kernel,
     # averaged over the launches that do the work
-    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "0fa6c7f1b4e712e4", 269384781, 16777216),
-    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "78bf7677018ff226", 16761345164, 1140850688),
-    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "43c0933b8168e2e2", 762537402, 270166547),
-    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "0fa6c7f1b4e712e4", 604188602, 67108864),
-    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "43c0933b8168e2e2", 1879270573, 85658560),
-    "ganq_pass": ("llama2_7b_attn", "gq_ganq.hip", "c0476d200f4da953", 598439224, 252128512),
-    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "0bc11711f539992b", 118512673, 42098),
+    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "88cb63b8bb84a182", 269513258, 16777216),
+    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "800812fb5c50d14e", 7103006310, 1384120320),
+    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "3223f1245850606c", 767232756, 270277845),
+    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "88cb63b8bb84a182", 604181256, 67108864),
+    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "3223f1245850606c", 1879904447, 85693056),
+    "ganq_pass": ("llama2_7b_attn", "gq_ganq.hip", "7d07aa3da51d8a77", 596667759, 252090160),
+    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "7d0df77c3a864263", 118509837, 42155),
 }
 
 
