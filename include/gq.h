@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 7
+#define GQ_ABI_VERSION 8
 
 typedef enum {
     GQ_OK = 0,
@@ -83,7 +83,10 @@ typedef enum {
                          Cholesky factor) does not exist there; those rows kept their codebook
                          (codes).  Outputs are written. */
     GQ_ENONFINITE = 7, /* checked call: an input holds NaN or +-Inf; nothing was written */
-    GQ_ENOTIMPL = 8   /* valid request outside what the library supports */
+    GQ_ENOTIMPL = 8,  /* valid request outside what the library supports */
+    GQ_ECHECK = 9     /* debug check (option check_residual) failed: an assignment pass's
+                         running residual disagreed with a fresh F'(C[P] - W); outputs are
+                         written, but they come from a faulty pass */
 } gq_status;
 
 typedef enum { GQ_F32 = 0, GQ_BF16 = 1 } gq_dtype;
@@ -127,6 +130,18 @@ typedef struct {
                            untouched); after the run, GQ_ENOTPD if any codebook system (GANQ:
                            any group's F') was not positive definite.  The call synchronises
                            its stream.  0: no data checks, fully asynchronous.  Default 0. */
+    int32_t check_residual; /* 1: debug check of the coordinate-descent pass (lnq_quantize,
+                           grid_quantize; GQ_EINVAL for ganq_quantize and
+                           lnq_quantize_static).  The pass decides every coordinate from a
+                           running residual r = F'(w_hat - w) that it updates move by move;
+                           after each pass, every row's objective is recomputed from scratch
+                           with a residual array of its own and compared with the objective
+                           the pass reached through r (its start plus the accepted changes).
+                           Rows differing by more than 1e-4 of their objective at the pass
+                           start are counted, and the call returns GQ_ECHECK if there are any.
+                           Costs one residual product per pass and d_out * d_in * 4 + d_out * 8
+                           bytes allocated stream-ordered for the call; the run's results are
+                           unchanged; the call synchronises its stream.  Default 0. */
 } gq_lnq_options;
 
 /* The options under the name the problem statement uses. */

@@ -13,5 +13,5 @@ from .binding import (  # noqa: F401
     fisher_workspace_size,
     lnq_workspace_size, gq_timing_enable, gq_timing_read, EXPORTS, GQ_F32, GQ_BF16,
     GQ_INIT_QUANTILE, GQ_INIT_GIVEN, GQ_INIT_UNIFORM, GQ_GRAM_AUTO, GQ_GRAM_DENSE,
-    GQ_ENOTPD, GQ_ENONFINITE, GQ_ESHAPE, GQ_EINVAL, DEFAULT_BLOCK,
+    GQ_ENOTPD, GQ_ENONFINITE, GQ_ECHECK, GQ_ESHAPE, GQ_EINVAL, DEFAULT_BLOCK,
 )

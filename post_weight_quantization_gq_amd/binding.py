@@ -4,6 +4,8 @@ Argument marshalling only: torch tensors supply device memory and the HIP
 stream; every step of the computation runs in the library's kernels.  Each
 function has the name of the C entry point it calls.  A non-OK status raises
 GQError(status, message).  If the built library is missing, loading raises.
+GQ_LIBRARY=<path> loads another build of the same library instead (for instance the
+host-sanitized libgq_asan.so, see build.py).
 """
 from __future__ import annotations
 
@@ -12,15 +14,16 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libgq.so")
+_LIB_PATH = os.environ.get("GQ_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "_lib", "libgq.so")
 
 GQ_OK, GQ_EINVAL, GQ_ESHAPE, GQ_EDTYPE, GQ_ENOMEM, GQ_EHIP = 0, 1, 2, 3, 4, 5
-GQ_ENOTPD, GQ_ENONFINITE, GQ_ENOTIMPL = 6, 7, 8
+GQ_ENOTPD, GQ_ENONFINITE, GQ_ENOTIMPL, GQ_ECHECK = 6, 7, 8, 9
 GQ_F32, GQ_BF16 = 0, 1
 GQ_INIT_QUANTILE, GQ_INIT_GIVEN, GQ_INIT_UNIFORM = 0, 1, 2
 GQ_GRAM_AUTO, GQ_GRAM_DENSE = 0, 1
 GQ_FISHER_CHECK_FINITE = 2
-ABI_VERSION = 7
+ABI_VERSION = 8
 DEFAULT_BLOCK = 512
 
 # every symbol include/gq.h declares
@@ -45,10 +48,12 @@ class GQError(RuntimeError):
 
 
 class lnq_options(ctypes.Structure):
-    """gq_lnq_options (block, ridge_rel, init, gram_update, ridge_abs, check_finite)."""
+    """gq_lnq_options (block, ridge_rel, init, gram_update, ridge_abs, check_finite,
+    check_residual)."""
     _fields_ = [("block", ctypes.c_int32), ("ridge_rel", ctypes.c_float),
                 ("init", ctypes.c_int32), ("gram_update", ctypes.c_int32),
-                ("ridge_abs", ctypes.c_float), ("check_finite", ctypes.c_int32)]
+                ("ridge_abs", ctypes.c_float), ("check_finite", ctypes.c_int32),
+                ("check_residual", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -195,11 +200,12 @@ def abi_version() -> int:
 
 def options(block: int = DEFAULT_BLOCK, ridge_rel: float = 1e-6, init: int = GQ_INIT_QUANTILE,
             gram_update: int = GQ_GRAM_AUTO, ridge_abs: float = 0.0,
-            check_finite: bool = False) -> lnq_options:
+            check_finite: bool = False, check_residual: bool = False) -> lnq_options:
     o = lnq_options()
     library().gq_lnq_options_default(ctypes.byref(o))
     o.block, o.ridge_rel, o.init, o.gram_update = block, ridge_rel, init, gram_update
     o.ridge_abs, o.check_finite = ridge_abs, int(bool(check_finite))
+    o.check_residual = int(bool(check_residual))
     return o
 
 
@@ -337,14 +343,16 @@ def _outputs(W, d_out, d_in, bits, C, P):
 def lnq_quantize(W, F, bits: int, iters: int, block: int = DEFAULT_BLOCK,
                  ridge_rel: float = 1e-6, C=None, P=None, init: int | None = None,
                  trace: bool = True, ws=None, stream=None, gram_update: int = GQ_GRAM_AUTO,
-                 ridge_abs: float = 0.0, check_finite: bool = False):
+                 ridge_abs: float = 0.0, check_finite: bool = False,
+                 check_residual: bool = False):
     """Whole LNQ on a layer.  Returns (C, P, obj_trace or None, n_changed).
 
     With C and P given and init unset, starts from them (GQ_INIT_GIVEN).
     ridge_abs: fixed ridge added to ridge_rel * mean(diag F_g).  check_finite: a checked
     call (GQ_ENONFINITE for NaN / Inf in W or F before anything is written, GQ_ENOTPD
     after the run if a codebook system was not positive definite).  ws=False lets the
-    library allocate its scratch.
+    library allocate its scratch.  check_residual: the debug check of every assignment
+    pass against a fresh F'(C[P] - W) (GQError GQ_ECHECK on a mismatch).
     """
     lib = library()
     groups = F.shape[0]
@@ -354,7 +362,7 @@ def lnq_quantize(W, F, bits: int, iters: int, block: int = DEFAULT_BLOCK,
     C, P = _outputs(W, d_out, d_in, bits, C, P)
     tr = torch.empty(2 * iters + 1, dtype=torch.float64, device=W.device) if trace else None
     nch = torch.zeros(max(iters, 1), dtype=torch.int64, device=W.device)
-    opt = options(block, ridge_rel, init, gram_update, ridge_abs, check_finite)
+    opt = options(block, ridge_rel, init, gram_update, ridge_abs, check_finite, check_residual)
     wp, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
     _check(lib.lnq_quantize(_ptr(W), _dt(W), d_out, d_in, _ptr(F), groups, bits, iters,
                             ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), wp,
@@ -365,7 +373,8 @@ def lnq_quantize(W, F, bits: int, iters: int, block: int = DEFAULT_BLOCK,
 def lnq_quantize_static(W, F, bits: int, iters: int, block: int = DEFAULT_BLOCK,
                         ridge_rel: float = 1e-6, C=None, P=None, init: int | None = None,
                         trace: bool = True, stream=None, gram_update: int = GQ_GRAM_AUTO,
-                        ridge_abs: float = 0.0, check_finite: bool = False):
+                        ridge_abs: float = 0.0, check_finite: bool = False,
+                        check_residual: bool = False):
     """lnq_quantize on the library's fixed per-device scratch (no workspace, nothing
     allocated by the library; the outputs are still the caller's).  Calls that overlap
     on one device race.  Returns (C, P, obj_trace or None, n_changed)."""
@@ -377,7 +386,7 @@ def lnq_quantize_static(W, F, bits: int, iters: int, block: int = DEFAULT_BLOCK,
     C, P = _outputs(W, d_out, d_in, bits, C, P)
     tr = torch.empty(2 * iters + 1, dtype=torch.float64, device=W.device) if trace else None
     nch = torch.zeros(max(iters, 1), dtype=torch.int64, device=W.device)
-    opt = options(block, ridge_rel, init, gram_update, ridge_abs, check_finite)
+    opt = options(block, ridge_rel, init, gram_update, ridge_abs, check_finite, check_residual)
     _check(lib.lnq_quantize_static(_ptr(W), _dt(W), d_out, d_in, _ptr(F), groups, bits, iters,
                                    ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch),
                                    _stream(stream)))
@@ -391,7 +400,7 @@ def lnq_static_scratch_bytes() -> int:
 def grid_quantize(W, F, bits: int, iters: int, block: int = DEFAULT_BLOCK,
                   ridge_rel: float = 1e-6, C=None, P=None, init: int | None = None,
                   trace: bool = True, ws=None, stream=None, ridge_abs: float = 0.0,
-                  check_finite: bool = False):
+                  check_finite: bool = False, check_residual: bool = False):
     """Fixed-grid backend: uniform grid per row, `iters` assignment passes.
 
     Returns (C, P, obj_trace [iters+1] or None, n_changed [iters]).  With C and P
@@ -405,7 +414,7 @@ def grid_quantize(W, F, bits: int, iters: int, block: int = DEFAULT_BLOCK,
     C, P = _outputs(W, d_out, d_in, bits, C, P)
     tr = torch.empty(iters + 1, dtype=torch.float64, device=W.device) if trace else None
     nch = torch.zeros(max(iters, 1), dtype=torch.int64, device=W.device)
-    opt = options(block, ridge_rel, init, GQ_GRAM_AUTO, ridge_abs, check_finite)
+    opt = options(block, ridge_rel, init, GQ_GRAM_AUTO, ridge_abs, check_finite, check_residual)
     wp, nb = _lnq_ws(ws, d_out, d_in, groups, bits, W)
     _check(lib.grid_quantize(_ptr(W), _dt(W), d_out, d_in, _ptr(F), groups, bits, iters,
                              ctypes.byref(opt), _ptr(C), _ptr(P), _ptr(tr), _ptr(nch), wp,

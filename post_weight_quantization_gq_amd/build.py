@@ -1,9 +1,16 @@
 """Build libgq.so (the C-ABI HIP library) for gfx950 in-tree.
 
-    python -m post_weight_quantization_gq_amd.build
+    python -m post_weight_quantization_gq_amd.build [--asan]
 
 compiles every csrc/*.hip into an object with hipcc and links
 post_weight_quantization_gq_amd/_lib/libgq.so.  Every call recompiles.
+
+With --asan it also links _lib/libgq_asan.so, the same library with AddressSanitizer
+on the host code only (the device code is built as usual).  It leaves the sanitizer's
+symbols to the runtime, so a process loads it with that runtime preloaded
+(LD_PRELOAD=asan_runtime()) and selects it with GQ_LIBRARY=<path>; the argument
+checks, workspace sizing and error reporting of the C ABI then run under the
+sanitizer on the CPU.
 """
 from __future__ import annotations
 
@@ -19,6 +26,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libgq.so")
+LIB_ASAN = os.path.join(LIBDIR, "libgq_asan.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -28,6 +36,8 @@ HIPCC_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
 ]
+# host-side AddressSanitizer (GPU sanitizers are not used)
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
 def _hipcc() -> str:
@@ -47,23 +57,34 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
+def asan_runtime() -> str | None:
+    """The AddressSanitizer runtime of the ROCm compiler, or None."""
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build(verbose: bool = False, asan: bool = False) -> str:
+    """Compile and link libgq.so (and, with asan, libgq_asan.so); returns libgq.so's path."""
     hipcc = _hipcc()
-    objdir = os.path.join(PKG, "_build")
-    os.makedirs(objdir, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    variants = [("_build", [], LIB)]
+    if asan:
+        variants.append(("_build_asan", ASAN_FLAGS, LIB_ASAN))
+    jobs = []
+    for objdir, extra, _ in variants:
+        os.makedirs(os.path.join(PKG, objdir), exist_ok=True)
+        for src in srcs:
+            obj = os.path.join(PKG, objdir, os.path.basename(src)[:-4] + ".o")
+            jobs.append([hipcc, *HIPCC_FLAGS, *extra, "-c", "-o", obj, src])
 
-    def compile_one(pair):
-        src, obj = pair
-        return _run([hipcc, *HIPCC_FLAGS, "-c", "-o", obj, src])
-
-    with ThreadPoolExecutor(max(1, min(len(srcs), os.cpu_count() or 1))) as ex:
-        outs = list(ex.map(compile_one, zip(srcs, objs)))
-    tmp = LIB + ".tmp"
-    outs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]))
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(max(1, min(len(jobs), os.cpu_count() or 1))) as ex:
+        outs = list(ex.map(_run, jobs))
+    for objdir, _, lib in variants:
+        objs = [os.path.join(PKG, objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+        tmp = lib + ".tmp"
+        outs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]))
+        os.replace(tmp, lib)
     if verbose:
         for o in outs:
             if o.strip():
@@ -72,5 +93,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    path = build(verbose="-v" in sys.argv)
+    path = build(verbose="-v" in sys.argv, asan="--asan" in sys.argv)
     print(path)

@@ -193,6 +193,8 @@ bool ridge_ok(float r) { return r >= 0.f && std::isfinite(r); }
 gq_status check_options(const gq_lnq_options& o, int64_t d_in) {
     if (!ridge_ok(o.ridge_abs)) return fail(GQ_EINVAL, "ridge_abs must be finite and >= 0");
     if (o.check_finite != 0 && o.check_finite != 1) return fail(GQ_EINVAL, "check_finite must be 0 or 1");
+    if (o.check_residual != 0 && o.check_residual != 1)
+        return fail(GQ_EINVAL, "check_residual must be 0 or 1");
     if (!block_ok(o.block))
         return fail(GQ_EINVAL, "block=%d: the assignment block is 64, 128, 256 or 512", o.block);
     if (d_in % 64) return fail(GQ_ESHAPE, "d_in=%lld is not a multiple of 64", (long long)d_in);
@@ -251,6 +253,7 @@ void gq_lnq_options_default(gq_lnq_options* opt) {
     opt->gram_update = GQ_GRAM_AUTO;
     opt->ridge_abs = 0.f;
     opt->check_finite = 0;
+    opt->check_residual = 0;
 }
 
 void lnq_options_default(lnq_options* opt) { gq_lnq_options_default(opt); }
@@ -470,6 +473,48 @@ gq_status lnq_objective(const float* F, int32_t groups, int64_t d_in, const void
 
 namespace {
 
+// Debug check of the assignment passes (option check_residual): after a pass, every
+// row's objective recomputed from scratch, with a residual array of its own, against
+// the objective the pass reached through its running residual.  Its buffers are
+// allocated stream-ordered for the call; the run itself is unchanged (the recomputation
+// writes only its own residual, its own objectives and the error planes, which every
+// residual product rewrites before reading).
+constexpr double kPassCheckTol = 1e-4;   // relative to the row's objective at the pass start
+
+struct PassCheck {
+    Scratch s;
+    float* R = nullptr;
+    double* obj = nullptr;
+    gq_status init(int64_t d_out, int64_t d_in, hipStream_t st) {
+        const size_t rb = ((size_t)d_out * d_in * sizeof(float) + 255) & ~(size_t)255;
+        gq_status rc = s.acquire(nullptr, 0, rb + (size_t)d_out * sizeof(double), st);
+        if (rc != GQ_OK) return rc;
+        R = (float*)s.ptr;
+        obj = (double*)((char*)s.ptr + rb);
+        return GQ_OK;
+    }
+    // w.objB / w.objC hold each row's objective at the pass start and the one it claims
+    // at its end; mismatches are counted into w.cnt[9]
+    hipError_t after_pass(const void* W, bool wb, int64_t d_out, int64_t d_in, int groups, int m,
+                          const uint8_t* P, const float* C, const gq::LnqWs& w, hipStream_t st) {
+        gq::LnqWs wd = w;
+        wd.R = R;
+        hipError_t e = gq::lnq_objective_rows(W, wb, d_out, d_in, groups, m, P, C, wd, obj, st);
+        if (e != hipSuccess) return e;
+        return gq::lnq_check_claim(w.objB, w.objC, obj, d_out, kPassCheckTol, w.cnt + 9, st);
+    }
+    gq_status verdict(const gq::LnqWs& w, hipStream_t st) {
+        unsigned long long bad = 0;
+        gq_status rc = read_flag(w.cnt + 9, st, &bad);
+        if (rc != GQ_OK) return rc;
+        if (bad)
+            return fail(GQ_ECHECK, "%llu (row, pass) objectives reached through the running "
+                        "residual differ from a fresh F'e by more than %g of the row's "
+                        "objective", bad, kPassCheckTol);
+        return GQ_OK;
+    }
+};
+
 // Argument checks of lnq_quantize (before anything is enqueued).
 gq_status lnq_quantize_check(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_in,
                              const float* F, int32_t groups, int32_t bits, int32_t iters,
@@ -500,6 +545,8 @@ gq_status lnq_quantize_run(const void* W, gq_dtype w_dt, int64_t d_out, int64_t 
     w.sb_shift = log2i(o.block);
     if (o.check_finite && (rc = check_lnq_inputs(W, wb, d_out, d_in, F, groups, w.cnt + 8, st)) != GQ_OK)
         return rc;
+    PassCheck pc;
+    if (o.check_residual && (rc = pc.init(d_out, d_in, st)) != GQ_OK) return rc;
     hipError_t e;
     if ((e = gq::lnq_prepare(F, groups, d_in, o.ridge_rel, o.ridge_abs, w, st)) != hipSuccess)
         return hip_fail(e, "prepare");
@@ -509,8 +556,11 @@ gq_status lnq_quantize_run(const void* W, gq_dtype w_dt, int64_t d_out, int64_t 
     if (o.init == GQ_INIT_UNIFORM &&
         (e = gq::grid_init_run(W, wb, d_out, d_in, m, C, P, st)) != hipSuccess)
         return hip_fail(e, "init");
-    // w.cnt: [0] moves of the pass, [1] rows not positive definite, [2] update mode
+    // w.cnt: [0] moves of the pass, [1] rows not positive definite, [2] update mode,
+    // [9] rows failing the pass check
     if ((e = gq::lnq_zero_counter(w.cnt, 3, st)) != hipSuccess) return hip_fail(e, "counter");
+    if (o.check_residual && (e = gq::lnq_zero_counter(w.cnt + 9, 1, st)) != hipSuccess)
+        return hip_fail(e, "counter");
     // A codebook step after a pass that changed at most incr_max codes updates A and the
     // residual from the changed coordinates (4 d bytes of F read per change, about
     // 3.5 ns per change at d = 4096) instead of recomputing them (2 d^2 d_out (m + 3)
@@ -530,6 +580,9 @@ gq_status lnq_quantize_run(const void* W, gq_dtype w_dt, int64_t d_out, int64_t 
         if ((e = gq::lnq_sweep_step(F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB,
                                     w.objC, w.cnt, incremental && t < iters, st)) != hipSuccess)
             return hip_fail(e, "sweep");
+        if (o.check_residual &&
+            (e = pc.after_pass(W, wb, d_out, d_in, groups, m, P, C, w, st)) != hipSuccess)
+            return hip_fail(e, "pass check");
         // trace entries 2t-2 and 2t-1, the pass's move count, counter cleared, next mode
         if ((e = gq::lnq_iter_tail(w.objA, w.objB, d_out,
                                    obj_trace ? obj_trace + 2 * t - 2 : nullptr, w.cnt,
@@ -552,6 +605,7 @@ gq_status lnq_quantize_run(const void* W, gq_dtype w_dt, int64_t d_out, int64_t 
             return fail(GQ_ENOTPD, "%llu codebook systems (rows x iterations) were not positive "
                         "definite; those rows kept their codebook", npd);
     }
+    if (o.check_residual) return pc.verdict(w, st);
     return GQ_OK;
 }
 
@@ -619,6 +673,9 @@ gq_status lnq_quantize_static(const void* W, gq_dtype w_dt, int64_t d_out, int64
     if (opt) o = *opt;
     gq_status rc = lnq_quantize_check(W, w_dt, d_out, d_in, F, groups, bits, iters, o, C, P);
     if (rc != GQ_OK) return rc;
+    if (o.check_residual)
+        return fail(GQ_EINVAL, "check_residual allocates its buffers; lnq_quantize_static "
+                    "allocates nothing (use lnq_quantize)");
     const size_t need = gq::lnq_sizes(d_out, d_in, groups, 1 << bits).total;
     if (need > kStaticScratchBytes)
         return fail(GQ_ENOTIMPL, "this layer needs %zu bytes of scratch; lnq_quantize_static "
@@ -656,6 +713,8 @@ gq_status grid_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_i
     w.sb_shift = log2i(o.block);
     if (o.check_finite && (rc = check_lnq_inputs(W, wb, d_out, d_in, F, groups, w.cnt + 8, st)) != GQ_OK)
         return rc;
+    PassCheck pc;
+    if (o.check_residual && (rc = pc.init(d_out, d_in, st)) != GQ_OK) return rc;
     hipError_t e;
     if ((e = gq::lnq_prepare(F, groups, d_in, o.ridge_rel, o.ridge_abs, w, st)) != hipSuccess)
         return hip_fail(e, "prepare");
@@ -664,12 +723,17 @@ gq_status grid_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_i
         return hip_fail(e, "init");
     if (iters > 0 && (e = gq::lnq_zero_counter(w.cnt, 3, st)) != hipSuccess)
         return hip_fail(e, "counter");
+    if (o.check_residual && (e = gq::lnq_zero_counter(w.cnt + 9, 1, st)) != hipSuccess)
+        return hip_fail(e, "counter");
     for (int t = 1; t <= iters; ++t) {
         // assignment pass; objB = the objective before it, from the residual recomputed
         // from (C, P) at its start (trace entry t - 1)
         if ((e = gq::lnq_sweep_step(F, W, wb, d_out, d_in, groups, C, m, P, w, w.objB,
                                     w.objC, w.cnt, false, st)) != hipSuccess)
             return hip_fail(e, "sweep");
+        if (o.check_residual &&
+            (e = pc.after_pass(W, wb, d_out, d_in, groups, m, P, C, w, st)) != hipSuccess)
+            return hip_fail(e, "pass check");
         if (obj_trace && (e = gq::lnq_reduce(w.objB, d_out, obj_trace + t - 1, st)) != hipSuccess)
             return hip_fail(e, "trace");
         // the pass's move count, counter cleared
@@ -684,6 +748,7 @@ gq_status grid_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_i
         if ((e = gq::lnq_reduce(w.objA, d_out, obj_trace + iters, st)) != hipSuccess)
             return hip_fail(e, "trace");
     }
+    if (o.check_residual) return pc.verdict(w, st);
     return GQ_OK;
 }
 
@@ -784,6 +849,9 @@ gq_status ganq_quantize(const void* W, gq_dtype w_dt, int64_t d_out, int64_t d_i
     if (o.init != GQ_INIT_QUANTILE && o.init != GQ_INIT_GIVEN && o.init != GQ_INIT_UNIFORM)
         return fail(GQ_EINVAL, "unknown init %d", o.init);
     if ((rc = check_options(o, d_in)) != GQ_OK) return rc;
+    if (o.check_residual)
+        return fail(GQ_EINVAL, "check_residual checks the coordinate-descent pass's running "
+                    "residual; the back-substitution pass keeps none");
     hipStream_t st = (hipStream_t)stream;
     const bool wb = w_dt == GQ_BF16;
     const int m = 1 << bits;

@@ -119,6 +119,9 @@ hipError_t lnq_iter_tail(const double* objA, const double* objB, int64_t n, doub
                          unsigned long long* cnt, int64_t* n_changed, int64_t incr_max,
                          hipStream_t st);
 hipError_t lnq_store_counter(const unsigned long long* c, int64_t* dst, hipStream_t st);
+// *bad += number of rows j with |claimed[j] - fresh[j]| > tol |start[j]| (or not finite)
+hipError_t lnq_check_claim(const double* start, const double* claimed, const double* fresh,
+                           int64_t n, double tol, unsigned long long* bad, hipStream_t st);
 // *flag |= 1 when any of the n float32 / bfloat16 values at p is NaN or +-Inf
 hipError_t scan_nonfinite(const void* p, bool bf16, int64_t n, unsigned long long* flag,
                           hipStream_t st);

@@ -25,6 +25,7 @@
 //   k_sweep        per 16-row group: the ascending coordinate pass (see there)
 //   k_reduce_rows  float64 layer sums in a fixed order
 //   k_iter_tail    per iteration: the two trace sums, the move count, counter reset
+//   k_check_claim  debug check: a pass's claimed row objectives against fresh ones
 #include "gq_common.h"
 #include "gq_internal.h"
 
@@ -1302,6 +1303,23 @@ __global__ __launch_bounds__(256) void k_iter_tail(const double* __restrict__ ob
 }
 
 // ---------------------------------------------------------------------------
+// Debug check of an assignment pass: the objective each row reached through the pass's
+// running residual (its start plus the accepted changes, `claimed`) against the same
+// row's objective recomputed from scratch (`fresh`).  Rows whose two figures differ by
+// more than tol |start| (or are not finite) are counted into *bad.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_check_claim(const double* __restrict__ start,
+                                                    const double* __restrict__ claimed,
+                                                    const double* __restrict__ fresh, int64_t n,
+                                                    double tol,
+                                                    unsigned long long* __restrict__ bad) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= n) return;
+    const double d = fabs(claimed[j] - fresh[j]);
+    if (!(d <= tol * fabs(start[j]))) atomicAdd(bad, 1ull);
+}
+
+// ---------------------------------------------------------------------------
 // Checked calls: *flag |= 1 if any of the n values (float32 or bfloat16) is NaN or
 // +-Inf (all exponent bits set).  16-byte vectors where whole, elements at the tail.
 // ---------------------------------------------------------------------------
@@ -1589,6 +1607,16 @@ hipError_t lnq_iter_tail(const double* objA, const double* objB, int64_t n, doub
     StageTimer tm(ST_LNQ_SMALL, st);
     hipLaunchKernelGGL(k_iter_tail, dim3(3), dim3(256), 0, st, objA, objB, n, trace, cnt,
                        n_changed, incr_max);
+    GQ_LAUNCH_CHECK();
+    return hipSuccess;
+}
+
+hipError_t lnq_check_claim(const double* start, const double* claimed, const double* fresh,
+                           int64_t n, double tol, unsigned long long* bad, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    StageTimer tm(ST_LNQ_SMALL, st);
+    hipLaunchKernelGGL(k_check_claim, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, start,
+                       claimed, fresh, n, tol, bad);
     GQ_LAUNCH_CHECK();
     return hipSuccess;
 }

@@ -30,14 +30,14 @@ def test_exports_every_declared_symbol():
     assert declared == set(B.EXPORTS), declared ^ set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert gq.abi_version() == 7
+    assert gq.abi_version() == 8
 
 
 def test_options_default():
     o = gq.options()
     d = B.lnq_options()
     gq.library().gq_lnq_options_default(ctypes.byref(d))
-    assert (d.block, d.init, d.gram_update, d.check_finite) == (512, 0, 0, 0)
+    assert (d.block, d.init, d.gram_update, d.check_finite, d.check_residual) == (512, 0, 0, 0, 0)
     assert d.ridge_rel == pytest.approx(1e-6) and d.ridge_abs == 0.0
     assert o.block == 512
     # the problem statement's names are the same functions
@@ -108,6 +108,11 @@ def test_lnq_argument_errors():
     o.ridge_abs, o.check_finite = 0.0, 2
     assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "check_finite" in _err(lib)
     o.check_finite = 0
+    o.check_residual = 2
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "check_residual" in _err(lib)
+    o.check_residual = 1           # valid: fails only on the workspace
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "workspace" in _err(lib)
+    o.check_residual = 0
     o.block, o.init = 64, 9
     assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL
     o.init, o.ridge_rel = 0, -1.0
@@ -141,6 +146,13 @@ def test_static_entry_rejects_layers_beyond_its_scratch():
                                    None) == B.GQ_EINVAL
     assert lib.lnq_quantize_static(FAKE, 1, 64, 256, FAKE, 2, 9, 2, None, FAKE, FAKE, None, None,
                                    None) == B.GQ_EINVAL
+    # the debug pass check allocates its buffers, which this entry point never does
+    o = B.lnq_options()
+    lib.gq_lnq_options_default(ctypes.byref(o))
+    o.check_residual = 1
+    assert lib.lnq_quantize_static(FAKE, 1, 64, 256, FAKE, 2, 3, 2, ctypes.byref(o), FAKE, FAKE,
+                                   None, None, None) == B.GQ_EINVAL
+    assert "check_residual" in _err(lib)
 
 
 def test_grid_argument_errors():
@@ -209,6 +221,10 @@ def test_ganq_argument_errors():
     assert q(bits=5) == B.GQ_EINVAL
     assert q(iters=-1) == B.GQ_EINVAL
     assert q(wsb=100) == B.GQ_EINVAL and "workspace" in _err(lib)
+    o = B.lnq_options()
+    lib.gq_lnq_options_default(ctypes.byref(o))
+    o.check_residual = 1           # the back-substitution pass keeps no running residual
+    assert q(opt=ctypes.byref(o)) == B.GQ_EINVAL and "check_residual" in _err(lib)
     assert gq.ganq_workspace_size(64, 256, 2, 3) > gq.lnq_workspace_size(64, 256, 2, 3) + \
         2 * 256 * 256 * 8
     f = lambda **k: lib.ganq_factor_damped(k.get("F", FAKE), k.get("groups", 2),

@@ -13,6 +13,9 @@
   * fixed ridge (ridge_rel = 0, ridge_abs = lambda; the fixed-lambda
     preconditioning of the GANQ summary page's ablation table): LNQ and GANQ end
     to end within 1e-3 of the oracle's own runs with F' = F + lambda I.
+  * check_residual (debug): after every assignment pass each row's objective from a
+    fresh F'(C[P] - W) matches the one the pass reached through its running
+    residual; the checked run passes and its outputs are bitwise the unchecked run's.
 """
 import numpy as np
 import pytest
@@ -217,3 +220,32 @@ def test_fixed_ridge_overdamps_small_scale_groups(device):
         print(f"{fn.__name__}: adaptive {a}, fixed lambda {lam:.3e}: {f}")
         assert f[1] >= 1.2 * a[1]
         assert abs(f[0] - a[0]) <= 0.1 * a[0]
+
+
+@pytest.mark.parametrize("path", ["lnq_auto", "lnq_dense", "grid"])
+def test_pass_check_holds_and_changes_nothing(device, mid, path):
+    """The debug check of the assignment pass's running residual: every pass of a
+    16-iteration run (LNQ in both update modes; the fixed grid) agrees with a fresh F'e
+    to 1e-4 of the row objective, so the call succeeds, and the check alters nothing:
+    codes, codebooks and trace are bitwise those of the unchecked call.  In the AUTO
+    mode the later codebook steps update A and the residual from the moved
+    coordinates (passes with at most d_out d_in (m + 3) 17 / 10000 moves), so the
+    passes after them run on that updated residual."""
+    iters = 16
+    if path == "grid":
+        run = lambda **k: gq.grid_quantize(mid.W, mid.F, 3, iters, init=gq.GQ_INIT_UNIFORM,
+                                           ridge_rel=RHO, **k)
+    else:
+        mode = gq.GQ_GRAM_AUTO if path == "lnq_auto" else gq.GQ_GRAM_DENSE
+        run = lambda **k: gq.lnq_quantize(mid.W, mid.F, 3, iters, ridge_rel=RHO,
+                                          gram_update=mode, **k)
+    C0, P0, tr0, n0 = run()
+    C1, P1, tr1, n1 = run(check_residual=True)
+    torch.cuda.synchronize()
+    assert torch.equal(C0, C1) and torch.equal(P0, P1)
+    assert torch.equal(tr0, tr1) and torch.equal(n0, n1)
+    moves = n1.tolist()
+    print(f"{path}: moves per pass {moves}")
+    if path == "lnq_auto":
+        lim = MID.d_out * MID.d_in * (8 + 3) * 17 // 10000
+        assert any(c <= lim for c in moves[:-1]), (lim, moves)   # the update mode ran
