@@ -225,7 +225,11 @@ size_t lnq_workspace_size(int64_t d_out, int64_t d_in, int32_t groups, int32_t b
  * Shape limits shared by every lnq_* call: 1 <= bits <= 4, d_out % groups == 0,
  * d_in % 32 == 0, 32 <= d_in <= 32768, ridge_rel finite and >= 0 (GQ_EINVAL /
  * GQ_ESHAPE otherwise); the assignment pass (lnq_assign_sweep, lnq_quantize,
- * grid_quantize) and ganq_* also need d_in % 64 == 0.
+ * grid_quantize) and ganq_* also need d_in % 64 == 0.  bits 5..8 (codebooks of
+ * 32..256 entries, which the uint8 codes could hold) are valid requests that this
+ * library does not build: GQ_ENOTIMPL (bits outside 1..8: GQ_EINVAL).  The pages'
+ * LNQ runs use 2..4 bits; larger codebooks would grow the Gram partials as m^2 and
+ * exceed the one-row-per-lane solve at m > 64.
  */
 gq_status lnq_codebook_update(const float* F, int32_t groups, int64_t d_in,
                               const void* W, gq_dtype w_dt, int64_t d_out,

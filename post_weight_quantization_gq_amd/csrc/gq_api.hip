@@ -149,7 +149,10 @@ gq_status check_lnq_shape(const float* F, int32_t groups, int64_t d_in, const vo
                                     (long long)d_out, groups);
     if (d_in % 32) return fail(GQ_ESHAPE, "d_in=%lld must be a multiple of 32", (long long)d_in);
     if (d_in > 32768) return fail(GQ_ENOTIMPL, "d_in=%lld above 32768", (long long)d_in);
-    if (bits < 1 || bits > 4) return fail(GQ_EINVAL, "bits=%d outside [1, 4]", bits);
+    if (bits < 1 || bits > 8) return fail(GQ_EINVAL, "bits=%d outside [1, 8]", bits);
+    if (bits > 4)
+        return fail(GQ_ENOTIMPL, "bits=%d: codebooks of more than 16 entries are not built "
+                    "(the library takes 1..4 bits)", bits);
     if (!(ridge_rel >= 0.f) || !std::isfinite(ridge_rel))
         return fail(GQ_EINVAL, "ridge_rel must be finite and >= 0");
     if (!al16(F) || !al16(W)) return fail(GQ_EINVAL, "F and W must be 16-byte aligned");
@@ -761,7 +764,8 @@ gq_status lut_pack_codes(const uint8_t* P, int64_t d_out, int64_t d_in, int32_t 
                          void* stream) {
     if (!P || !Q) return fail(GQ_EINVAL, "null P or Q");
     if (d_out < 1 || d_in < 1) return fail(GQ_ESHAPE, "empty shape");
-    if (bits < 1 || bits > 4) return fail(GQ_EINVAL, "bits=%d: the packed layout takes 1..4", bits);
+    if (bits < 1 || bits > 8) return fail(GQ_EINVAL, "bits=%d outside [1, 8]", bits);
+    if (bits > 4) return fail(GQ_ENOTIMPL, "bits=%d: the packed layout takes 1..4", bits);
     if ((uintptr_t)Q & 15u) return fail(GQ_EINVAL, "Q must be 16-byte aligned");
     hipError_t e = gq::lut_pack_run(P, d_out, d_in, bits, Q, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "lut_pack_codes");
@@ -773,7 +777,8 @@ gq_status lut_gemv(const uint32_t* Q, const float* C, int64_t d_out, int64_t d_i
     if (!Q || !C || !x || !y) return fail(GQ_EINVAL, "null Q, C, x or y");
     if (!dtype_ok(x_dt)) return fail(GQ_EDTYPE, "unsupported dtype");
     if (d_out < 1 || d_in < 1) return fail(GQ_ESHAPE, "empty shape");
-    if (bits < 1 || bits > 4) return fail(GQ_EINVAL, "bits=%d: the packed layout takes 1..4", bits);
+    if (bits < 1 || bits > 8) return fail(GQ_EINVAL, "bits=%d outside [1, 8]", bits);
+    if (bits > 4) return fail(GQ_ENOTIMPL, "bits=%d: the packed layout takes 1..4", bits);
     if (batch < 1 || batch > 8) return fail(GQ_EINVAL, "batch=%d: 1..8 activation vectors", batch);
     if (((uintptr_t)Q & 15u) || ((uintptr_t)C & 3u) || ((uintptr_t)y & 3u) ||
         ((uintptr_t)x & (x_dt == GQ_BF16 ? 1u : 3u)))

@@ -86,7 +86,8 @@ def test_lnq_argument_errors():
     assert q(d_in=0) == B.GQ_ESHAPE and "empty" in _err(lib)
     assert q(d_in=250) == B.GQ_ESHAPE
     assert q(d_in=65536) == B.GQ_ENOTIMPL
-    assert q(bits=5) == B.GQ_EINVAL and "bits" in _err(lib)
+    assert q(bits=5) == B.GQ_ENOTIMPL and "bits" in _err(lib)
+    assert q(bits=9) == B.GQ_EINVAL and "bits" in _err(lib)
     assert q(bits=0) == B.GQ_EINVAL
     assert q(iters=-1) == B.GQ_EINVAL
     assert q(P=FAKE_ODD) == B.GQ_EINVAL
@@ -166,7 +167,8 @@ def test_grid_argument_errors():
     assert q(wdt=5) == B.GQ_EDTYPE
     assert q(d_out=63) == B.GQ_ESHAPE
     assert q(d_in=0) == B.GQ_ESHAPE
-    assert q(bits=5) == B.GQ_EINVAL and "bits" in _err(lib)
+    assert q(bits=5) == B.GQ_ENOTIMPL and "bits" in _err(lib)
+    assert q(bits=9) == B.GQ_EINVAL and "bits" in _err(lib)
     assert q(iters=-1) == B.GQ_EINVAL
     assert q(P=FAKE_ODD) == B.GQ_EINVAL
     o = B.lnq_options()
@@ -218,7 +220,7 @@ def test_ganq_argument_errors():
     assert q(wdt=5) == B.GQ_EDTYPE
     assert q(d_out=63) == B.GQ_ESHAPE
     assert q(d_in=96) == B.GQ_ESHAPE and "64" in _err(lib)
-    assert q(bits=5) == B.GQ_EINVAL
+    assert q(bits=5) == B.GQ_ENOTIMPL and q(bits=9) == B.GQ_EINVAL
     assert q(iters=-1) == B.GQ_EINVAL
     assert q(wsb=100) == B.GQ_EINVAL and "workspace" in _err(lib)
     o = B.lnq_options()
@@ -246,7 +248,8 @@ def test_lut_argument_errors():
                                         k.get("bits", 3), k.get("Q", FAKE), None)
     assert pk(P=None) == B.GQ_EINVAL
     assert pk(d_in=0) == B.GQ_ESHAPE
-    assert pk(bits=5) == B.GQ_EINVAL and "bits" in _err(lib)
+    assert pk(bits=5) == B.GQ_ENOTIMPL and "bits" in _err(lib)
+    assert pk(bits=9) == B.GQ_EINVAL
     assert pk(Q=FAKE_ODD) == B.GQ_EINVAL
     mv = lambda **k: lib.lut_gemv(k.get("Q", FAKE), k.get("C", FAKE), k.get("d_out", 8),
                                   k.get("d_in", 64), k.get("bits", 3), k.get("x", FAKE),
