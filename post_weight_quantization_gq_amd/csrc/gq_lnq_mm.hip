@@ -21,10 +21,10 @@
 // Both operands live in k-blocked bf16 planes (element (row, k) at
 // ((k / 16) * rows + row) * 16 + k % 16, rows padded to whole 256-row tiles), so
 // one 16-deep stage of a 256-row band is 8 KB of contiguous memory.  Block tile
-// 256 x 256, 8 waves (two per SIMD) of 128 x 64 as 4 x 2 v_mfma_f32_32x32x16_bf16
-// tiles.  The
+// 256 x 256: k_resid runs 4 waves (one per SIMD) of 128 x 128, k_gram 8 waves (two
+// per SIMD) of 128 x 64, as 32 x 32 v_mfma_f32_32x32x16_bf16 tiles.  The
 // stages go through a ring of 4 LDS stages filled by direct buffer-to-LDS loads
-// three stages ahead; a 32-byte operand row sits in two 16-byte slots, chunk c
+// ahead of use; a 32-byte operand row sits in two 16-byte slots, chunk c
 // of row r in slot 2 r + (c ^ ((r >> 3) & 1)), so each quarter-wave fragment
 // read (16 consecutive rows) touches 16 distinct bank groups.  The one-hot
 // operand of k_gram is built once per stage into LDS, one stage ahead; k_gram
@@ -76,9 +76,33 @@ __device__ __forceinline__ int frag_slot(int row, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// R = E F'.  Tile (256 rows j of a group) x (256 coordinates a).
+// R = E F'.  Tile (256 rows j of a group) x (256 coordinates a), 4 waves (one per
+// SIMD); wave w owns rows 128 (w % 2) .. + 127 and coordinates 128 (w / 2) .. + 127
+// as 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators (256 registers), so each 16-byte
+// fragment read from LDS feeds 12 MFMAs (3 products x 4 partners).
+//   Each 16-deep stage of the four bands (Ehi, Elo, Fhi, Flo) is refilled into the ring
+// four stages ahead with the same 8 loads per wave at every stage (stages past the
+// last reload it into a slot that is never read), so fixed vmcnt waits hold.  One
+// barrier per stage, between the two halves of its 48 MFMAs: after it the stage's
+// slot is refilled and the next stage's fragments are read while the second half runs.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_resid(
+struct RFrag {
+    u32x4 eh[4], el[4];     // rows 128 (w % 2) + 32 i
+    u32x4 fh[4], fl[4];     // coordinates 128 (w / 2) + 32 j
+};
+
+// MFMA t (0..23) of one half (rows i0, i0 + 1): product t / 8 (Ehi Fhi, Ehi Flo,
+// Elo Fhi) of accumulator (i0 + (t % 8) / 4, t % 4), so the same accumulator
+// comes back only every 8 MFMAs.
+template <int I0>
+__device__ __forceinline__ void resid_mfma(f32x16 (&acc)[4][4], const RFrag& f, int t) {
+    const int p = t >> 3, i = I0 + ((t & 7) >> 2), j = t & 3;
+    const u32x4 a = p == 2 ? f.el[i] : f.eh[i];
+    const u32x4 b = p == 1 ? f.fl[j] : f.fh[j];
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), acc[i][j], 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_resid(
     const uint16_t* __restrict__ Ehi, const uint16_t* __restrict__ Elo, int64_t erows,
     int64_t rpg_pad, const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo,
     int64_t a_pad, int64_t d, int64_t rpg, int ntn, int nta, int total, float* __restrict__ R,
@@ -104,64 +128,106 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t* Fh = Fhi + fg + a0 * 16;
     const uint16_t* Fl = Flo + fg + a0 * 16;
     const int64_t estep = erows * 16, fstep = a_pad * 16;
-    const int nst = (int)(d / 16);
+    const int nst = (int)(d / 16);                      // even: d % 32 == 0
 
+    // Stages are refilled in order; eo / fo is the element offset of the next one,
+    // held at the last stage once it is reached.
+    int64_t eo = 0, fo = 0;
+    __amdgpu_buffer_rsrc_t rs[4];
+    auto next_rsrc = [&]() {
+        rs[0] = band_rsrc(Eh + eo);
+        rs[1] = band_rsrc(El + eo);
+        rs[2] = band_rsrc(Fh + fo);
+        rs[3] = band_rsrc(Fl + fo);
+    };
+    auto advance = [&](int s) {
+        if (s + 1 < nst) { eo += estep; fo += fstep; }
+    };
+    // load k (0..7) of a stage's refill: band k % 4, rows 32 (wave + 4 (k / 4)) .. + 31
+    auto issue_one = [&](u32x4* base, int k) {
+        band_to_lds(rs[k & 3], base + (k & 3) * M_SLOTS, wave + 4 * (k >> 2), voff);
+    };
     auto issue = [&](int s) {
         u32x4* base = mm_lds + (s % MRING) * (4 * M_SLOTS);
-        band_to_lds(band_rsrc(Eh + s * estep), base, wave, voff);
-        band_to_lds(band_rsrc(El + s * estep), base + M_SLOTS, wave, voff);
-        band_to_lds(band_rsrc(Fh + s * fstep), base + 2 * M_SLOTS, wave, voff);
-        band_to_lds(band_rsrc(Fl + s * fstep), base + 3 * M_SLOTS, wave, voff);
+        next_rsrc();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) issue_one(base, k);
+        advance(s);
+    };
+    // fragment read k (0..15) of stage s, in the order the first half uses them
+    auto read_one = [&](int s, RFrag& f, int k) {
+        const u32x4* S = mm_lds + (s % MRING) * (4 * M_SLOTS);
+        const int ei = 128 * w0 + (lane & 31), fj = 128 * w1 + (lane & 31);
+        switch (k) {
+            case 0: f.eh[0] = S[frag_slot(ei, lane)]; break;
+            case 1: f.fh[0] = S[2 * M_SLOTS + frag_slot(fj, lane)]; break;
+            case 2: f.fh[1] = S[2 * M_SLOTS + frag_slot(fj + 32, lane)]; break;
+            case 3: f.fh[2] = S[2 * M_SLOTS + frag_slot(fj + 64, lane)]; break;
+            case 4: f.fh[3] = S[2 * M_SLOTS + frag_slot(fj + 96, lane)]; break;
+            case 5: f.eh[1] = S[frag_slot(ei + 32, lane)]; break;
+            case 6: f.fl[0] = S[3 * M_SLOTS + frag_slot(fj, lane)]; break;
+            case 7: f.fl[1] = S[3 * M_SLOTS + frag_slot(fj + 32, lane)]; break;
+            case 8: f.fl[2] = S[3 * M_SLOTS + frag_slot(fj + 64, lane)]; break;
+            case 9: f.fl[3] = S[3 * M_SLOTS + frag_slot(fj + 96, lane)]; break;
+            case 10: f.el[0] = S[M_SLOTS + frag_slot(ei, lane)]; break;
+            case 11: f.el[1] = S[M_SLOTS + frag_slot(ei + 32, lane)]; break;
+            case 12: f.eh[2] = S[frag_slot(ei + 64, lane)]; break;
+            case 13: f.eh[3] = S[frag_slot(ei + 96, lane)]; break;
+            case 14: f.el[2] = S[M_SLOTS + frag_slot(ei + 64, lane)]; break;
+            default: f.el[3] = S[M_SLOTS + frag_slot(ei + 96, lane)]; break;
+        }
     };
 
-    f32x16 acc[4][2];
+    f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    {
-        const int pre = nst < MRING - 1 ? nst : MRING - 1;
-        for (int s = 0; s < pre; ++s) issue(s);
-    }
-    int slot = 0;
-    for (int s = 0; s < nst; ++s) {
-        // 4 load instructions per stage and wave: stage s has landed once at most
-        // 4 x (later stages issued) are outstanding
-        const int newer = ((s + MRING - 2 < nst) ? s + MRING - 2 : nst - 1) - s;
-        if (newer >= 2) mm_wait_vmcnt<8>();
-        else if (newer == 1) mm_wait_vmcnt<4>();
-        else mm_wait_vmcnt<0>();
+    // 8 loads per wave and stage: when stage s's second half is due, stage s + 1 has
+    // landed once at most the 2 x 8 loads of stages s + 2 and s + 3 are outstanding
+    RFrag f0, f1;
+    if (nst > 0) {
+#pragma unroll
+        for (int s = 0; s < MRING; ++s) issue(s);
+        mm_wait_vmcnt<(MRING - 1) * 8>();
         __builtin_amdgcn_s_barrier();
-        if (s + MRING - 1 < nst) issue(s + MRING - 1);
-        const u32x4* S = mm_lds + slot * (4 * M_SLOTS);
-        bf16x8 eh[4], el[4], fh[2], fl[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int sl = frag_slot(128 * w0 + 32 * i + (lane & 31), lane);
-            eh[i] = as_bf16x8(S[sl]);
-            el[i] = as_bf16x8(S[M_SLOTS + sl]);
-        }
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int sl = frag_slot(64 * w1 + 32 * jj + (lane & 31), lane);
-            fh[jj] = as_bf16x8(S[2 * M_SLOTS + sl]);
-            fl[jj] = as_bf16x8(S[3 * M_SLOTS + sl]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(eh[i], fh[jj], acc[i][jj], 0, 0, 0);
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(eh[i], fl[jj], acc[i][jj], 0, 0, 0);
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(el[i], fh[jj], acc[i][jj], 0, 0, 0);
-            }
-        __builtin_amdgcn_sched_barrier(0);
-        slot = (slot + 1 == MRING) ? 0 : slot + 1;
+        for (int k = 0; k < 16; ++k) read_one(0, f0, k);
     }
+    auto stage = [&](int s, RFrag& cur, RFrag& nxt) {
+#pragma unroll
+        for (int t = 0; t < 24; ++t) resid_mfma<0>(acc, cur, t);
+        __builtin_amdgcn_sched_barrier(0);
+        mm_wait_vmcnt<(MRING - 2) * 8>();   // also: this wave's reads of stage s are done
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // second half, one MFMA per step: the next stage's 16 fragment reads (two a
+        // step), then the 8 loads refilling this stage's slot, read by everyone by now
+        u32x4* base = mm_lds + (s % MRING) * (4 * M_SLOTS);
+#pragma unroll
+        for (int t = 0; t < 24; ++t) {
+            resid_mfma<2>(acc, cur, t);
+            if (t < 8) {
+                read_one(s + 1, nxt, 2 * t);
+                read_one(s + 1, nxt, 2 * t + 1);
+            } else if (t == 8) {
+                next_rsrc();
+            } else if (t < 17) {
+                issue_one(base, t - 9);
+            } else if (t == 17) {
+                advance(s + MRING);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    for (int s = 0; s < nst; s += 2) {
+        stage(s, f0, f1);
+        stage(s + 1, f1, f0);
+    }
+    mm_wait_vmcnt<0>();      // no load into this block's LDS may land after it ends
 
     float* O = R + ((int64_t)g * rpg) * d;
     const int nrem = (int)((rpg - n0) < MT ? (rpg - n0) : MT);
@@ -169,13 +235,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int acol = 64 * w1 + 32 * jj + (lane & 31);
+        for (int j = 0; j < 4; ++j) {
+            const int acol = 128 * w1 + 32 * j + (lane & 31);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int nrow = 128 * w0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                 if (nrow < nrem && acol < arem)
-                    O[(n0 + nrow) * d + a0 + acol] = acc[i][jj][v];
+                    O[(n0 + nrow) * d + a0 + acol] = acc[i][j][v];
             }
         }
 }
@@ -428,7 +494,7 @@ hipError_t lnq_residual(const uint16_t* Ehi, const uint16_t* Elo, int64_t d_out,
         if (e != hipSuccess) return e;
     }
     StageTimer tm(ST_LNQ_RESID, st);
-    hipLaunchKernelGGL(k_resid, dim3((unsigned)grid), dim3(512), RESID_LDS, st, Ehi, Elo,
+    hipLaunchKernelGGL(k_resid, dim3((unsigned)grid), dim3(256), RESID_LDS, st, Ehi, Elo,
                        (int64_t)groups * rpg_pad, rpg_pad, Fhi, Flo, a_pad, d, rpg, ntn, nta,
                        total, R, skip);
     GQ_LAUNCH_CHECK();
