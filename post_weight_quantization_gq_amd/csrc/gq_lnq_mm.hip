@@ -21,14 +21,13 @@
 // Both operands live in k-blocked bf16 planes (element (row, k) at
 // ((k / 16) * rows + row) * 16 + k % 16, rows padded to whole 256-row tiles), so
 // one 16-deep stage of a 256-row band is 8 KB of contiguous memory.  Block tile
-// 256 x 256: k_resid runs 4 waves (one per SIMD) of 128 x 128, k_gram 8 waves (two
-// per SIMD) of 128 x 64, as 32 x 32 v_mfma_f32_32x32x16_bf16 tiles.  The
-// stages go through a ring of 4 LDS stages filled by direct buffer-to-LDS loads
-// ahead of use; a 32-byte operand row sits in two 16-byte slots, chunk c
-// of row r in slot 2 r + (c ^ ((r >> 3) & 1)), so each quarter-wave fragment
-// read (16 consecutive rows) touches 16 distinct bank groups.  The one-hot
-// operand of k_gram is built once per stage into LDS, one stage ahead; k_gram
-// takes 32-deep stages (two k-blocks) through a ring of 3.
+// 256 x 256, 4 waves (one per SIMD) of 128 x 128 as 4 x 4 v_mfma_f32_32x32x16_bf16
+// tiles.  The stages go through a ring of 4 LDS stages filled by direct
+// buffer-to-LDS loads ahead of use; a 32-byte operand row sits in two 16-byte
+// slots, chunk c of row r in slot 2 r + (c ^ ((r >> 3) & 1)), so each quarter-wave
+// fragment read (16 consecutive rows) touches 16 distinct bank groups.  k_gram takes
+// 32-deep stages (two k-blocks) and builds its one-hot operand in registers from
+// the codes, which travel through LDS beside the F' bands.
 #include "gq_common.h"
 #include "gq_internal.h"
 
@@ -263,24 +262,93 @@ __device__ __forceinline__ u32x2 onehot4(uint32_t codes, uint32_t qq, uint32_t o
     return r;
 }
 
-// The Gram kernel runs 32-deep stages (two 16-deep k-blocks) through a ring of
-// GRING stages, to halve the per-stage barrier and fragment-read overhead against
-// its 16 MFMAs per k-block and wave.
-constexpr int GRING = 3;
+// One-hot B fragment (8 k-values of one (j, q) column, two k per dword, bf16) from
+// the 8 codes c (one byte each) of row j.  For M <= 8 each code selects a byte of a
+// per-lane table through v_perm_b32: tl / th hold, at byte q, the low / high byte
+// of the bf16 weight (1.0 = 0x3F80, 0.5 = 0x3F00) and zero elsewhere, so the lookup
+// yields the weight's two bytes where the code equals q and zero where it does not;
+// two more byte permutes interleave them into bf16 pairs.  M = 16 takes codes up to
+// 15, past the 8-byte table, and compares bytes instead.
+template <int M>
+__device__ __forceinline__ u32x4 gram_onehot(u32x2 c, uint32_t tl0, uint32_t tl1,
+                                             uint32_t th0, uint32_t th1, uint32_t qq,
+                                             uint32_t onepair) {
+    u32x4 r;
+    if constexpr (M <= 8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t lo = __builtin_amdgcn_perm(tl1, tl0, c[h]);
+            const uint32_t hi = __builtin_amdgcn_perm(th1, th0, c[h]);
+            r[2 * h] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+            r[2 * h + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+        }
+    } else {
+        const u32x2 a = onehot4(c[0], qq, onepair), b = onehot4(c[1], qq, onepair);
+        r = u32x4{a[0], a[1], b[0], b[1]};
+    }
+    return r;
+}
+
+// An accumulator value read out of its AGPR where it is used: keeps the 256
+// accumulators in AGPRs until the epilogue bins them, one fragment at a time, instead
+// of all being copied to (and spilled from) the 256 arch VGPRs at the loop's exit.
+// Every use follows the last MFMA by a global-memory wait and two barriers, far past
+// the MFMA result latency.
+__device__ __forceinline__ float acc_read(float a) {
+    float v;
+    asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
+// bins[OFF + k] += x[e] for the 4 values x[0..3] whose codes are the bytes of cw,
+// each a bin index k < NB (<= 8) or 0x0C (no bin).  The codes are spread into byte-permute
+// selectors (0x0C selects a zero byte), and for each bin a lookup in an 8-byte table
+// holding 0x3C at byte k yields, per value, the high byte of the half-precision 1.0
+// or 0; each accumulation is then one fused multiply-add of a float32 by a half.
+template <int NB, int OFF, int M>
+__device__ __forceinline__ void gram_bin4(float (&bins)[M], uint32_t cw, const float (&x)[4]) {
+    const uint32_t s0 = __builtin_amdgcn_perm(cw, 0x0C0C0C0Cu, 0x05000400u);   // 0C c0 0C c1
+    const uint32_t s1 = __builtin_amdgcn_perm(cw, 0x0C0C0C0Cu, 0x07000600u);   // 0C c2 0C c3
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+        const uint32_t t0 = k < 4 ? 0x3Cu << (8 * k) : 0u;
+        const uint32_t t1 = k < 4 ? 0u : 0x3Cu << (8 * (k - 4));
+        const uint32_t h0 = __builtin_amdgcn_perm(t1, t0, s0);
+        const uint32_t h1 = __builtin_amdgcn_perm(t1, t0, s1);
+        float b = bins[OFF + k];
+        b = __builtin_fmaf(x[0], (float)__builtin_bit_cast(_Float16, (uint16_t)(h0 & 0xffffu)), b);
+        b = __builtin_fmaf(x[1], (float)__builtin_bit_cast(_Float16, (uint16_t)(h0 >> 16)), b);
+        b = __builtin_fmaf(x[2], (float)__builtin_bit_cast(_Float16, (uint16_t)(h1 & 0xffffu)), b);
+        b = __builtin_fmaf(x[3], (float)__builtin_bit_cast(_Float16, (uint16_t)(h1 >> 16)), b);
+        bins[OFF + k] = b;
+    }
+}
+
+// The Gram kernel: 32-deep stages (two 16-deep k-blocks) through a ring of GRING
+// stages, each stage the four F' bands (hi and lo of both k-blocks, 32 KB) and the
+// codes of the block's rows j for those 32 coordinates (32 bytes a row, 4 KB); 4
+// waves (one per SIMD), wave w owning coordinates a = 128 (w % 2) .. + 127 and
+// columns (j, q) = 128 (w / 2) .. + 127 as 4 x 4 accumulators.  The one-hot operand
+// is built in registers from the codes, one k-block ahead of its MFMAs.  One barrier
+// per stage, between the k-blocks: after it the stage's slot is refilled and the next
+// stage's fragments and codes are read, spread between the second k-block's MFMAs.
+constexpr int GRING = 4;
+constexpr int G_CSLOTS = 256;           // 16-byte slots of one code stage (128 rows x 32 B)
+
+struct GFrag {
+    u32x4 fh[2][4], fl[2][4];           // [k-block][i]: coordinates 128 (w % 2) + 32 i
+    u32x2 c[2][4];                      // [k-block][jj]: codes of this lane's column
+};
 
 template <int M>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gram(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gram(
     const uint8_t* __restrict__ P, int64_t rpg, int64_t d_out, int groups,
     const uint16_t* __restrict__ Fhi, const uint16_t* __restrict__ Flo, int64_t a_pad,
     int64_t d, int ntn, int nta, int total, float* __restrict__ out,
     const unsigned long long* __restrict__ skip) {
     extern __shared__ u32x4 mm_lds[];
     if (skip && *skip != 0ull) return;
-    // LDS: ring of GRING stages of four bands (Fhi and Flo of two k-blocks); two
-    // one-hot stages of two k-blocks (512 slots each); ring of GRING code stages
-    // (slot 64 w + 32 h + c for column 32 w + c, codes 16 h .. 16 h + 15)
-    u32x4* ohbuf = mm_lds + GRING * 4 * M_SLOTS;
-    u32x4* cring = ohbuf + 4 * M_SLOTS;
+    u32x4* cring = mm_lds + GRING * 4 * M_SLOTS;
     const int lin = mm_remap(blockIdx.x);
     if (lin >= total) return;
     const int tn = lin % ntn;
@@ -297,140 +365,182 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint32_t voff = band_voff(lane);
 
     const int64_t fg = (int64_t)g * d * a_pad;
-    const int64_t k_begin = a0;
-    const int nst = (int)((d - k_begin) / 32);          // d % 32 == 0, a0 % 256 == 0
-    const int ndiag = (int)((((d - a0) < MT ? (d - a0) : MT)) / 16);   // k-blocks at half weight
-    const uint16_t* Fh = Fhi + fg + ((k_begin >> 4) * a_pad + a0) * 16;
-    const uint16_t* Fl = Flo + fg + ((k_begin >> 4) * a_pad + a0) * 16;
+    const int nst = (int)((d - a0) / 32);               // d % 32 == 0, a0 % 256 == 0
+    const int ndst = (int)((((d - a0) < MT ? (d - a0) : MT)) / 32);   // stages at half weight
+    const uint16_t* Fh = Fhi + fg + ((a0 >> 4) * a_pad + a0) * 16;
+    const uint16_t* Fl = Flo + fg + ((a0 >> 4) * a_pad + a0) * 16;
     const int64_t fstep = a_pad * 16;                   // one 16-deep k-block
 
-    // code load: lane L of wave w copies codes 16 (L / 32) .. + 15 of stage x for
-    // one-hot column c = 32 w + L % 32 ((j, q) = n0 + c); a row past the group's end
-    // reads the group's first row and is masked when the one-hot is built
-    const int ccol = 32 * wave + (lane & 31);
-    const int64_t jl = n0 / M + ccol / M;
-    const bool jvalid = jl < rpg;
-    const uint8_t* Pg = P + row_base * d + k_begin;
-    const uint32_t coff = (uint32_t)((jvalid ? jl : 0) * d) + 16u * (uint32_t)(lane >> 5);
-    auto issue_codes = [&](int x) {
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(Pg + (int64_t)x * 32), (short)0, (int)0x7fffffff, 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(cring + (x % GRING) * 512 + 64 * wave),
-                                                 16, coff, 0, 0, 0);
+    // codes: wave w copies rows j = n0 / M + 32 w .. + 31 (lane L: row 32 w + L / 2,
+    // bytes 16 (L % 2) .. + 15 of the stage's 32), rows past the group's end clamped
+    // to its last row; their columns (j, q) are past N and never stored
+    const int64_t j0 = n0 / M;
+    const int64_t jb = (j0 + 32 * wave < rpg) ? j0 + 32 * wave : rpg - 1;
+    const int64_t jr = (j0 + 32 * wave + (lane >> 1) < rpg) ? j0 + 32 * wave + (lane >> 1) : rpg - 1;
+    const uint8_t* Pw = P + (row_base + jb) * d + a0;
+    const uint32_t coff = (uint32_t)((jr - jb) * d) + 16u * (uint32_t)(lane & 1);
+
+    // this lane's one-hot column: q = (lane % 32) % M in every 32-column fragment
+    const int q = (lane & 31) % M;
+    const uint64_t tl = (uint64_t)0x80u << (8 * (q & 7)), th = (uint64_t)0x3Fu << (8 * (q & 7));
+    const uint32_t tl0 = (uint32_t)tl, tl1 = (uint32_t)(tl >> 32);
+    const uint32_t th0 = (uint32_t)th, th1 = (uint32_t)(th >> 32);
+    const uint32_t qq = (uint32_t)q * 0x01010101u;
+    // code LDS offset (bytes, within a code stage) of fragment jj's row for this lane:
+    // row (128 w1 + 32 jj + lane % 32) / M, i.e. cofs + jj (32 / M) rows (M divides 32)
+    const int cofs = ((128 * w1 + (lane & 31)) / M) * 32 + 8 * (lane >> 5);
+
+    // Stages are refilled in order; fo / co locate the next one, held at the last
+    // stage once it is reached.
+    int64_t fo = 0;
+    uint32_t co = 0;
+    __amdgpu_buffer_rsrc_t rs[5];
+    auto next_rsrc = [&]() {
+        rs[0] = band_rsrc(Fh + fo);
+        rs[1] = band_rsrc(Fh + fo + fstep);
+        rs[2] = band_rsrc(Fl + fo);
+        rs[3] = band_rsrc(Fl + fo + fstep);
+        rs[4] = __builtin_amdgcn_make_buffer_rsrc((void*)(Pw + co), (short)0, (int)0x7fffffff,
+                                                  0x00020000);
     };
-    // thread t builds k-block kb = t / 256 of column c = t % 256
-    const int bcol = tid & 255, bkb = tid >> 8;
-    const int64_t bjl = n0 / M + bcol / M;
-    const uint32_t bqq = (uint32_t)(bcol % M) * 0x01010101u;
-    const bool bvalid = bjl < rpg;
-    const int csl = 64 * (bcol >> 5) + 32 * bkb + (bcol & 31);
-    const int osw = (bcol >> 3) & 1;
-    auto build = [&](int x) {
-        u32x4 cv = cring[(x % GRING) * 512 + csl];
-        if (!bvalid) cv = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-        const uint32_t one = (2 * x + bkb < ndiag) ? 0x3F00u : 0x3F80u;   // 0.5 on the diagonal tile
-        const uint32_t onepair = one | (one << 16);
-        const u32x2 h0 = onehot4(cv[0], bqq, onepair), h1 = onehot4(cv[1], bqq, onepair);
-        const u32x2 h2 = onehot4(cv[2], bqq, onepair), h3 = onehot4(cv[3], bqq, onepair);
-        u32x4* O = ohbuf + ((x & 1) * 2 + bkb) * M_SLOTS + bcol * 2;
-        O[0 ^ osw] = u32x4{h0[0], h0[1], h1[0], h1[1]};          // k 0..7 of the k-block
-        O[1 ^ osw] = u32x4{h2[0], h2[1], h3[0], h3[1]};          // k 8..15
+    auto advance = [&](int x) {
+        if (x + 1 < nst) { fo += 2 * fstep; co += 32u; }
     };
-    // batch x: the four bands of stage x, then the codes of stage x + 1 (5 loads per wave)
+    // load k (0..8) of a stage's refill: bands (k % 4) for rows 32 (wave + 4 (k / 4)),
+    // then the codes
+    auto issue_one = [&](int x, int k) {
+        if (k < 8) {
+            u32x4* base = mm_lds + (x % GRING) * (4 * M_SLOTS);
+            band_to_lds(rs[k & 3], base + (k & 3) * M_SLOTS, wave + 4 * (k >> 2), voff);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs[4], (lds_ptr_t)(cring + (x % GRING) * G_CSLOTS + 64 * wave), 16, coff, 0, 0, 0);
+        }
+    };
     auto issue = [&](int x) {
-        u32x4* base = mm_lds + (x % GRING) * (4 * M_SLOTS);
-        band_to_lds(band_rsrc(Fh + (2 * x) * fstep), base, wave, voff);
-        band_to_lds(band_rsrc(Fh + (2 * x + 1) * fstep), base + M_SLOTS, wave, voff);
-        band_to_lds(band_rsrc(Fl + (2 * x) * fstep), base + 2 * M_SLOTS, wave, voff);
-        band_to_lds(band_rsrc(Fl + (2 * x + 1) * fstep), base + 3 * M_SLOTS, wave, voff);
-        if (x + 1 < nst) issue_codes(x + 1);
+        next_rsrc();
+#pragma unroll
+        for (int k = 0; k < 9; ++k) issue_one(x, k);
+        advance(x);
+    };
+    // read k (0..23) of stage x: the 8 code reads, then the 16 F' fragments
+    auto read_one = [&](int x, GFrag& f, int k) {
+        if (k < 8) {
+            const uint8_t* C = (const uint8_t*)(cring + (x % GRING) * G_CSLOTS);
+            const int kb = k >> 2, jj = k & 3;
+            f.c[kb][jj] = *(const u32x2*)(C + cofs + jj * (32 / M) * 32 + 16 * kb);
+        } else {
+            const u32x4* S = mm_lds + (x % GRING) * (4 * M_SLOTS);
+            const int kk = k - 8, pl = kk >> 3, kb = (kk >> 2) & 1, i = kk & 3;
+            const u32x4 v = S[(2 * pl + kb) * M_SLOTS + frag_slot(128 * w0 + 32 * i + (lane & 31), lane)];
+            if (pl == 0) f.fh[kb][i] = v;
+            else f.fl[kb][i] = v;
+        }
+    };
+    // weight 0.5 on the diagonal tile, 1 above it, 0 on the padding stage past the end
+    auto onehot = [&](const GFrag& f, int x, int kb, int jj) {
+        const bool half = x < ndst, none = x >= nst;
+        const uint32_t one = none ? 0u : (half ? 0x3F00u : 0x3F80u);
+        return gram_onehot<M>(f.c[kb][jj], (half || none) ? 0u : tl0, (half || none) ? 0u : tl1,
+                              none ? 0u : th0, none ? 0u : th1, qq, one | (one << 16));
     };
 
-    f32x16 acc[4][2];
+    f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
 
+    // MFMA t (0..31) of k-block kb: plane t / 16 (hi, lo) of accumulator
+    // ((t % 16) / 4, t % 4), so the same accumulator comes back every 16 MFMAs
+    auto mfma = [&](const GFrag& f, const u32x4 (&oh)[4], int kb, int t) {
+        const int pl = t >> 4, i = (t & 15) >> 2, jj = t & 3;
+        const u32x4 av = pl ? f.fl[kb][i] : f.fh[kb][i];
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(oh[jj]),
+                                                             acc[i][jj], 0, 0, 0);
+    };
+
+    // 9 loads per wave and stage: when stage x's second k-block is due, stage x + 1 has
+    // landed once at most the loads of stages x + 2 .. x + GRING - 1 are outstanding
+    GFrag f0, f1;
+    u32x4 oh0[4], oh1[4];
     if (nst > 0) {
-        issue_codes(0);
-        const int pre = nst < GRING - 1 ? nst : GRING - 1;
-        for (int x = 0; x < pre; ++x) issue(x);
-        // codes of stage 0: the oldest load of this wave
-        if (pre >= 2) mm_wait_vmcnt<9>();
-        else mm_wait_vmcnt<4>();
+#pragma unroll
+        for (int x = 0; x < GRING; ++x) issue(x);
+        mm_wait_vmcnt<(GRING - 1) * 9>();
         __builtin_amdgcn_s_barrier();
-        build(0);
+#pragma unroll
+        for (int k = 0; k < 24; ++k) read_one(0, f0, k);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) oh0[jj] = onehot(f0, 0, 0, jj);
     }
-    int slot = 0;
-    for (int s = 0; s < nst; ++s) {
-        // batch s (bands of s, codes of s + 1) has landed once at most 4 loads of
-        // this wave (batch s + 1, if issued) are outstanding
-        if (s + 1 < nst) mm_wait_vmcnt<4>();
-        else mm_wait_vmcnt<0>();
+    auto stage = [&](int x, GFrag& cur, GFrag& nxt) {
+        // first k-block, with the one-hot of the second built between its MFMAs
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+            mfma(cur, oh0, 0, t);
+            if ((t & 3) == 1 && t < 16) oh1[t >> 2] = onehot(cur, x, 1, t >> 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mm_wait_vmcnt<(GRING - 2) * 9>();   // also: this wave's reads of stage x are done
         __builtin_amdgcn_s_barrier();
-        if (s + GRING - 1 < nst) issue(s + GRING - 1);
-        const u32x4* S = mm_lds + slot * (4 * M_SLOTS);
-        const u32x4* OH = ohbuf + (s & 1) * 2 * M_SLOTS;
-        bf16x8 fh[2][4], fl[2][4], oh[2][2];
+        __builtin_amdgcn_sched_barrier(0);
+        // second k-block: the next stage's codes and fragments (two reads a step), the
+        // refill of this stage's slot (one load a step), the next stage's first one-hot
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sl = frag_slot(128 * w0 + 32 * i + (lane & 31), lane);
-                fh[kb][i] = as_bf16x8(S[kb * M_SLOTS + sl]);
-                fl[kb][i] = as_bf16x8(S[(2 + kb) * M_SLOTS + sl]);
+        for (int t = 0; t < 32; ++t) {
+            mfma(cur, oh1, 1, t);
+            if (t < 12) {
+                read_one(x + 1, nxt, 2 * t);
+                read_one(x + 1, nxt, 2 * t + 1);
+            } else if (t == 12) {
+                next_rsrc();
+            } else if (t < 22) {
+                issue_one(x + GRING, t - 13);
+            } else if (t == 22) {
+                advance(x + GRING);
+            } else if (t >= 24 && t < 28) {
+                oh0[t - 24] = onehot(nxt, x + 1, 0, t - 24);
             }
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-                oh[kb][jj] = as_bf16x8(OH[kb * M_SLOTS + frag_slot(64 * w1 + 32 * jj + (lane & 31), lane)]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // the one-hot of stage s + 1 (past the last stage it fills a buffer no one
-        // reads, from a ring slot in bounds), built while the MFMAs of stage s run
-        build(s + 1);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[kb][i], oh[kb][jj], acc[i][jj], 0, 0, 0);
-                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[kb][i], oh[kb][jj], acc[i][jj], 0, 0, 0);
-                }
-        // order: the 20 fragment reads and the code read, then one MFMA per two
-        // VALU operations of the build, its LDS writes, the remaining MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 21, 0);
-#pragma unroll
-        for (int k = 0; k < 22; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
-        slot = (slot + 1 == GRING) ? 0 : slot + 1;
+    };
+    // an even number of stages: an odd count gets one more, a reload of the last stage
+    // (as every refill past the end is) that adds nothing, its one-hot being zero
+    const int nst2 = (nst + 1) & ~1;
+    for (int x = 0; x < nst2; x += 2) {
+        stage(x, f0, f1);
+        stage(x + 1, f1, f0);
     }
+    mm_wait_vmcnt<0>();      // no load into this block's LDS may land after it ends
+    __syncthreads();
+
     __syncthreads();
 
     // ---- epilogue: bin T[a][(j,q)] by the code of coordinate a
     // stage the codes of the block's rows for its 256 coordinates: jrows x 256 bytes
+    // (0x0C past d or past the group's rows: T is zero at a >= d, as the padded rows of
+    // the F' planes are, and columns past N are not stored)
     constexpr int jrows = MT / M;
     uint8_t* ctile = (uint8_t*)mm_lds;
-    for (int e = tid; e < jrows * (MT / 16); e += 512) {
+    for (int e = tid; e < jrows * (MT / 16); e += 256) {
         const int r = e / (MT / 16), c16 = (e - r * (MT / 16)) * 16;
-        const int64_t jr = n0 / M + r;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (jr < rpg && a0 + c16 < d) v = *(const u32x4*)(P + (row_base + jr) * d + a0 + c16);
+        const int64_t jrow = j0 + r;
+        u32x4 v = {0x0C0C0C0Cu, 0x0C0C0C0Cu, 0x0C0C0C0Cu, 0x0C0C0C0Cu};
+        if (jrow < rpg && a0 + c16 < d) v = *(const u32x4*)(P + (row_base + jrow) * d + a0 + c16);
         *(u32x4*)(ctile + r * MT + c16) = v;
     }
     __syncthreads();
     float* xch = (float*)(ctile + jrows * MT);
-    const int arem = (int)((d - a0) < MT ? (d - a0) : MT);
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const int nl = 64 * w1 + 32 * jj + (lane & 31);
-        const int jr = nl / M;
+    // one column fragment jj at a time (a compile-time index, so the accumulators stay
+    // in registers)
+    auto bin_fragment = [&](auto jjc) {
+        constexpr int jj = decltype(jjc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        const int nl = 128 * w1 + 32 * jj + (lane & 31);
+        const int jl = nl / M;
         float bins[M];
 #pragma unroll
         for (int k = 0; k < M; ++k) bins[k] = 0.f;
@@ -439,13 +549,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const int al = 128 * w0 + 32 * i + 8 * v4 + 4 * (lane >> 5);
-                const uint32_t cw = *(const uint32_t*)(ctile + jr * MT + al);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t code = (cw >> (8 * e)) & 0xffu;
-                    const float x = (al + e < arem) ? acc[i][jj][4 * v4 + e] : 0.f;
-#pragma unroll
-                    for (int k = 0; k < M; ++k) bins[k] += (code == (uint32_t)k) ? x : 0.f;
+                const uint32_t cw = *(const uint32_t*)(ctile + jl * MT + al);
+                const float xv[4] = {acc_read(acc[i][jj][4 * v4]), acc_read(acc[i][jj][4 * v4 + 1]),
+                                     acc_read(acc[i][jj][4 * v4 + 2]),
+                                     acc_read(acc[i][jj][4 * v4 + 3])};
+                if constexpr (M <= 8) {
+                    gram_bin4<M, 0>(bins, cw, xv);
+                } else {
+                    // codes 8..15 -> 0..7 for the upper bins, 0..7 -> 0x0C for them, and
+                    // the other way round for the lower bins
+                    const uint32_t b3 = (cw >> 3) & 0x01010101u;
+                    const uint32_t hi = (b3 << 8) - b3;                  // 0xFF per code >= 8
+                    const uint32_t clo = (hi & 0x0C0C0C0Cu) | (~hi & cw);
+                    const uint32_t chi = (hi & cw & 0x07070707u) | (~hi & 0x0C0C0C0Cu);
+                    gram_bin4<8, 0>(bins, clo, xv);
+                    gram_bin4<8, 8>(bins, chi, xv);
                 }
             }
         // lanes l and l + 32 hold the same (j, q) for the other half of the a's
@@ -466,14 +584,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
         __syncthreads();
-    }
+    };
+    bin_fragment(std::integral_constant<int, 0>{});
+    bin_fragment(std::integral_constant<int, 1>{});
+    bin_fragment(std::integral_constant<int, 2>{});
+    bin_fragment(std::integral_constant<int, 3>{});
 }
 
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
 constexpr size_t RESID_LDS = (size_t)MRING * 4 * M_SLOTS * 16;          // 128 KB
-constexpr size_t GRAM_LDS = ((size_t)(GRING * 4 + 4) * M_SLOTS + GRING * 512) * 16;   // 152 KB
+constexpr size_t GRAM_LDS = (size_t)GRING * (4 * M_SLOTS + G_CSLOTS) * 16;   // 144 KB
 
 size_t lnq_gram_partial_floats(int64_t d_out, int64_t d, int m) {
     const int64_t nta = (d + MT - 1) / MT;
@@ -505,6 +627,7 @@ template <int M>
 static hipError_t launch_gram(const uint8_t* P, int64_t d_out, int64_t d, int groups,
                               const uint16_t* Fhi, const uint16_t* Flo, float* part,
                               const unsigned long long* skip, hipStream_t st) {
+    static_assert((MT / M) * MT + 64 * M * 4 <= GRAM_LDS, "Gram epilogue exceeds the LDS");
     const int64_t rpg = d_out / groups;
     const int ntn = (int)((rpg * M + MT - 1) / MT);
     const int nta = (int)((d + MT - 1) / MT);
@@ -515,7 +638,7 @@ static hipError_t launch_gram(const uint8_t* P, int64_t d_out, int64_t d, int gr
         if (e != hipSuccess) return e;
     }
     StageTimer tm(ST_LNQ_GRAM, st);
-    hipLaunchKernelGGL((k_gram<M>), dim3((unsigned)grid), dim3(512), GRAM_LDS, st, P, rpg, d_out,
+    hipLaunchKernelGGL((k_gram<M>), dim3((unsigned)grid), dim3(256), GRAM_LDS, st, P, rpg, d_out,
                        groups, Fhi, Flo, lnq_pad256(d), d, ntn, nta, total, part, skip);
     GQ_LAUNCH_CHECK();
     return hipSuccess;

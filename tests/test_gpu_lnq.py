@@ -128,26 +128,46 @@ def test_codebook_parity_random_states(device, mid, bits, empty):
     ||c_ref - c_old||) per row; on every row the objective at the GPU codebook
     within 1e-7 relative of the oracle's minimum (the step's defining property).
     """
-    rng = np.random.default_rng(bits * 10 + empty)
+    _check_random_codebook(device, mid, MID, bits, empty, np.random.default_rng(bits * 10 + empty))
+
+
+def _check_random_codebook(device, prob, wl, bits, empty, rng):
     m = 1 << bits
-    P, C = _random_state(rng, MID.d_out, MID.d_in, m, empty=empty)
-    got = _codebook_gpu(device, mid, P, C, bits)
+    P, C = _random_state(rng, wl.d_out, wl.d_in, m, empty=empty)
+    got = _codebook_gpu(device, prob, P, C, bits)
     worst = worst_obj = 0.0
-    for j in range(MID.d_out):
-        Fp = mid.Fp_row(j)
+    for j in range(wl.d_out):
+        Fp = prob.Fp_row(j)
         c_old = C[j].astype(np.float64)
-        ref = O.codebook_update(Fp, mid.w[j], P[j], c_old)
+        ref = O.codebook_update(Fp, prob.w[j], P[j], c_old)
         if empty:
             np.testing.assert_array_equal(got[j][m - empty:], c_old[m - empty:])
         scale = max(np.linalg.norm(ref), np.linalg.norm(ref - c_old))
         worst = max(worst, np.linalg.norm(got[j] - ref) / scale)
-        o_ref = O.objective(Fp, mid.w[j], ref, P[j])
-        o_gpu = O.objective(Fp, mid.w[j], got[j], P[j])
+        o_ref = O.objective(Fp, prob.w[j], ref, P[j])
+        o_gpu = O.objective(Fp, prob.w[j], got[j], P[j])
         worst_obj = max(worst_obj, (o_gpu - o_ref) / o_ref)
     print(f"random states: max step-relative error {worst:.2e}, max objective excess "
           f"{worst_obj:.2e}")
     assert worst <= 1e-4
     assert worst_obj <= 1e-7
+
+
+ODD = _wl("odd", 544, 200, 1536, 2, 3, index=32)
+
+
+@pytest.fixture(scope="module")
+def odd(device):
+    return Problem(device, ODD, seed=5)
+
+
+@pytest.mark.parametrize("bits,empty", [(1, 0), (3, 1), (4, 0)])
+def test_codebook_parity_odd_stage_count(device, odd, bits, empty):
+    """d_in = 544 = 17 x 32, so the Gram product over the upper-triangle tiles of F'
+    takes an odd number of 32-deep stages on every coordinate tile (17, 9 and 1;
+    the last tile is 32 coordinates of a 256-wide tile), and 100-row groups leave
+    the last column tile of each group ragged.  Same bars as from random states."""
+    _check_random_codebook(device, odd, ODD, bits, empty, np.random.default_rng(77 + bits))
 
 
 def _sweep_check(prob, C, P0, P1, tol=1e-5, frac=0.999, codes_frac=0.999):
