@@ -88,13 +88,13 @@ _CSRC = os.path.join(ROOT, "post_weight_quantization_gq_amd", "csrc")
 _TRAFFIC = {
     # stage: (workload, source file, digest, bytes read, bytes written) of its main kernel,
     # averaged over the launches that do the work
-    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "88cb63b8bb84a182", 269513258, 16777216),
-    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "800812fb5c50d14e", 7103006310, 1384120320),
-    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "3223f1245850606c", 767232756, 270277845),
-    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "88cb63b8bb84a182", 604181256, 67108864),
-    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "3223f1245850606c", 1879904447, 85693056),
-    "ganq_pass": ("llama2_7b_attn", "gq_ganq.hip", "7d07aa3da51d8a77", 596667759, 252090160),
-    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "7d0df77c3a864263", 118509837, 42155),
+    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "5ce8e738139a103e", 267307051, 16777216),
+    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "cddf0c6a79bd9111", 7078678834, 1384120320),
+    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "d4f7a4583dfb7d39", 760506029, 270266368),
+    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "5ce8e738139a103e", 604401136, 67108864),
+    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "d4f7a4583dfb7d39", 1879252984, 85692416),
+    "ganq_pass": ("llama2_7b_attn", "gq_ganq.hip", "68f68676aeca3ee4", 597764805, 252109462),
+    "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "623cb61e64e42808", 118509837, 41842),
 }
 
 
