@@ -108,10 +108,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const unsigned long long* __restrict__ skip) {
     extern __shared__ u32x4 mm_lds[];
     if (skip && *skip != 0ull) return;
+    // row tiles fastest: the blocks one XCD runs together share their F' bands (the larger
+    // operand) in its L2, a band being read by all ntn row tiles of its group
     const int lin = mm_remap(blockIdx.x);
     if (lin >= total) return;
-    const int ta = lin % nta;
-    const int tn = (lin / nta) % ntn;
+    const int tn = lin % ntn;
+    const int ta = (lin / ntn) % nta;
     const int g = lin / (nta * ntn);
     const int64_t a0 = (int64_t)ta * MT, n0 = (int64_t)tn * MT;
 
