@@ -56,13 +56,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t band_rsrc(const uint16_t* p) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, M_SLOTS * 16, 0x00020000);
 }
 
-// Copy one stage of a 256-row band (rows of 32 bytes) into 512 LDS slots: wave w
-// (of 8) issues one instruction filling rows 32w .. 32w + 31; lane L takes row
-// 32w + L/2 and slot L%2, i.e. chunk (L%2) ^ ((L/16)%2).
-__device__ __forceinline__ void band_to_lds(__amdgpu_buffer_rsrc_t r, u32x4* dst, int wave,
+// Copy rows 32 q .. 32 q + 31 (q of 8) of one stage of a 256-row band (rows of 32
+// bytes) into their LDS slots with one instruction; lane L takes row 32 q + L/2 and slot
+// L%2, i.e. chunk (L%2) ^ ((L/16)%2).  The 8 instructions of a stage are spread over
+// the block's waves.
+__device__ __forceinline__ void band_to_lds(__amdgpu_buffer_rsrc_t r, u32x4* dst, int q,
                                             uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 64 * wave), 16, voff,
-                                             (uint32_t)wave * 1024u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 64 * q), 16, voff,
+                                             (uint32_t)q * 1024u, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t band_voff(int lane) {
