@@ -88,10 +88,10 @@ _CSRC = os.path.join(ROOT, "post_weight_quantization_gq_amd", "csrc")
 _TRAFFIC = {
     # stage: (workload, source file, digest, bytes read, bytes written) of its main kernel,
     # averaged over the launches that do the work
-    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "fc4ec8a748cbc00e", 267327530, 16777216),
+    "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "80dc741c80ab9adb", 267327530, 16777216),
     "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "cddf0c6a79bd9111", 7079510290, 1384120320),
     "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "d4f7a4583dfb7d39", 765787620, 270284800),
-    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "fc4ec8a748cbc00e", 403082224, 67108864),
+    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "80dc741c80ab9adb", 403082224, 67108864),
     "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "d4f7a4583dfb7d39", 1882017679, 85692416),
     "ganq_pass": ("llama2_7b_attn", "gq_ganq.hip", "68f68676aeca3ee4", 594707889, 252086758),
     "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "623cb61e64e42808", 118509837, 42933),

@@ -78,8 +78,8 @@ __device__ __forceinline__ int frag_slot(int row, int lane) {
 // ---------------------------------------------------------------------------
 // R = E F'.  Tile (256 rows j of a group) x (256 coordinates a), 4 waves (one per
 // SIMD); wave w owns rows 128 (w % 2) .. + 127 and coordinates 128 (w / 2) .. + 127
-// as 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators (256 registers), so each 16-byte
-// fragment read from LDS feeds 12 MFMAs (3 products x 4 partners).
+// as 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators (256 registers), so a stage's 16
+// fragment reads from LDS feed 48 MFMAs (a hi fragment 8, a lo fragment 4).
 //   Each 16-deep stage of the four bands (Ehi, Elo, Fhi, Flo) is refilled into the ring
 // four stages ahead with the same 8 loads per wave at every stage (stages past the
 // last reload it into a slot that is never read), so fixed vmcnt waits hold.  One
