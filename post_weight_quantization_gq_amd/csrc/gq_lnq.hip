@@ -626,8 +626,14 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
 //         with D_sb (the value changes of the super-block) held in LDS;
 //       - at the end of a super-block, right-looking into the residual array,
 //         R[:, later] += D_sb F'[sb, later], streaming long contiguous panels
-//         of F' (each residual element is owned by one wave; no atomics).
-//     32-coordinate chunks in which no row of the block moved are skipped.
+//         of F' with the next two chunks' loads in flight during the current
+//         two chunks' products.  Each residual element belongs to one wave and
+//         takes one float atomic add per super-block, performed in L2 (no read
+//         back); the barrier between super-blocks orders them, so the sums are
+//         the same on every run.
+//     The products of 32-coordinate chunks in which no row of the block moved
+//     are skipped (the right-looking update still loads them, keeping its loads
+//     a fixed distance ahead); a super-block without moves skips the update.
 //   * Chain (per wave), first-mover form: every lane t of the 64-block not yet
 //     visited evaluates, from the current residual, its m candidate changes
 //         Delta_q = delta_q (F'_tt delta_q + 2 r_t),  delta_q = c_q - w_hat_t,
@@ -649,7 +655,6 @@ constexpr int SW_ROWS = 16;     // rows (= waves) per block
 constexpr int SW_SUB = 64;      // coordinates per chain block (one per lane)
 constexpr int SW_SB = 512;      // largest super-block (the LDS arrays are sized for it)
 constexpr int SW_DP = SW_SB + 8;  // bf16 pitch of the LDS rows of D_sb
-constexpr int SW_RB = 4;        // F' chunks in flight per wave in the right-looking update
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_mov_i(int v) {
@@ -877,40 +882,48 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
         uint32_t mv = 0u;                                  // moved chunks as a bit mask
         for (int c = 0; c < nch; ++c) mv |= (chunk_moved[c] != 0u ? 1u : 0u) << c;
         mv = __builtin_amdgcn_readfirstlane(mv);
-        for (int ctile = wave; ctile < ntiles; ctile += SW_ROWS) {
+        for (int ctile = wave; mv != 0u && ctile < ntiles; ctile += SW_ROWS) {
             const int64_t fcol = sb_end + (int64_t)ctile * 16 + mrow;
             const uint16_t* Fh_c = plane_at(Fh, fcol, sb0 + ko);
             const uint16_t* Fl_c = plane_at(Fl, fcol, sb0 + ko);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int c0 = 0; c0 < nch; c0 += SW_RB) {
-                u32x4 fh[SW_RB], fl[SW_RB];
+            // two register sets of two 32-coordinate chunks each: the loads of one set
+            // are in flight while the other's products run (nch is even: sblen % 64 == 0)
+            u32x4 ah[2], al[2], bh[2], bl[2];
+            auto load2 = [&](u32x4 (&h)[2], u32x4 (&l)[2], int c0) {
 #pragma unroll
-                for (int u = 0; u < SW_RB; ++u) {
-                    const int c = c0 + u;
-                    if (c < nch && ((mv >> c) & 1u)) {
-                        fh[u] = *(const u32x4*)(Fh_c + (uint32_t)c * kstep32);
-                        fl[u] = *(const u32x4*)(Fl_c + (uint32_t)c * kstep32);
-                    }
+                for (int u = 0; u < 2; ++u) {
+                    h[u] = *(const u32x4*)(Fh_c + (uint32_t)(c0 + u) * kstep32);
+                    l[u] = *(const u32x4*)(Fl_c + (uint32_t)(c0 + u) * kstep32);
                 }
+            };
+            auto mfma2 = [&](const u32x4 (&h)[2], const u32x4 (&l)[2], int c0) {
 #pragma unroll
-                for (int u = 0; u < SW_RB; ++u) {
+                for (int u = 0; u < 2; ++u) {
                     const int c = c0 + u;
-                    if (c < nch && ((mv >> c) & 1u)) {
+                    if ((mv >> c) & 1u) {
                         const u32x4 dh = *(const u32x4*)(&dsb_hi[mrow][c * 32 + ko]);
                         const u32x4 dl = *(const u32x4*)(&dsb_lo[mrow][c * 32 + ko]);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fh[u]), acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fl[u]), acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dl), as_bf16x8(fh[u]), acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(h[u]), acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(l[u]), acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dl), as_bf16x8(h[u]), acc, 0, 0, 0);
                     }
                 }
+            };
+            load2(ah, al, 0);
+            for (int c0 = 0; c0 < nch; c0 += 4) {
+                if (c0 + 2 < nch) load2(bh, bl, c0 + 2);
+                mfma2(ah, al, c0);
+                if (c0 + 4 < nch) load2(ah, al, c0 + 4);
+                if (c0 + 2 < nch) mfma2(bh, bl, c0 + 2);
             }
+            // one float add per residual element and super-block, performed in L2 (no
+            // read back into the wave); the barrier below orders the super-blocks
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int rr = 4 * (lane >> 4) + t;
-                if (rr < nrows) {
-                    float* dst = R + (row0 + rr) * d + sb_end + (int64_t)ctile * 16 + mrow;
-                    *dst += acc[t];
-                }
+                if (rr < nrows)
+                    unsafeAtomicAdd(R + (row0 + rr) * d + sb_end + (int64_t)ctile * 16 + mrow, acc[t]);
             }
         }
         __syncthreads();
