@@ -627,10 +627,8 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
 //       - at the end of a super-block, right-looking into the residual array,
 //         R[:, later] += D_sb F'[sb, later], streaming long contiguous panels
 //         of F' with the next two chunks' loads in flight during the current
-//         two chunks' products.  Each residual element belongs to one wave and
-//         takes one float atomic add per super-block, performed in L2 (no read
-//         back); the barrier between super-blocks orders them, so the sums are
-//         the same on every run.
+//         two chunks' products (each residual element is owned by one wave,
+//         which adds a 16 x 16 tile with 16-byte read-modify-writes; no atomics).
 //     The products of 32-coordinate chunks in which no row of the block moved
 //     are skipped (the right-looking update still loads them, keeping its loads
 //     a fixed distance ahead); a super-block without moves skips the update.
@@ -694,7 +692,7 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
     int* __restrict__ ccount, uint8_t* __restrict__ pprev, int sbsz) {
     __shared__ __attribute__((aligned(16))) uint16_t dsb_hi[SW_ROWS][SW_DP];   // 16.3 KB
     __shared__ __attribute__((aligned(16))) uint16_t dsb_lo[SW_ROWS][SW_DP];   // 16.3 KB
-    __shared__ float corr_p[4][SW_ROWS][SW_SUB];                               // 16 KB
+    __shared__ __attribute__((aligned(16))) float corr_p[4][SW_ROWS][SW_SUB];   // 16 KB
     __shared__ __attribute__((aligned(16))) float fdb[SW_SUB][SW_SUB];         // 16 KB
     __shared__ float fdd[SW_SUB];                      // diag(F') of the block
     __shared__ uint32_t chunk_moved[SW_SB / 32];       // a move in a 32-chunk of the super-block
@@ -917,13 +915,21 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
                 if (c0 + 4 < nch) load2(ah, al, c0 + 4);
                 if (c0 + 2 < nch) mfma2(bh, bl, c0 + 2);
             }
-            // one float add per residual element and super-block, performed in L2 (no
-            // read back into the wave); the barrier below orders the super-blocks
+            // the 16 x 16 tile (row 4 (lane / 16) + t, column lane % 16 in acc[t]) is
+            // transposed through this wave's quarter of corr_p (unused during the
+            // update) so that lane l adds columns 4 (l % 4) .. + 3 of row l / 4 with one
+            // 16-byte read-modify-write
+            {
+                float* xp = &corr_p[0][0][0] + wave * 256;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int rr = 4 * (lane >> 4) + t;
-                if (rr < nrows)
-                    unsafeAtomicAdd(R + (row0 + rr) * d + sb_end + (int64_t)ctile * 16 + mrow, acc[t]);
+                for (int t = 0; t < 4; ++t) xp[(4 * (lane >> 4) + t) * 16 + mrow] = acc[t];
+                const int rr = lane >> 2;
+                if (rr < nrows) {
+                    f32x4* dst = (f32x4*)(R + (row0 + rr) * d + sb_end + (int64_t)ctile * 16 +
+                                          4 * (lane & 3));
+                    const f32x4 rv = *dst;
+                    *dst = rv + *(const f32x4*)(xp + 4 * lane);
+                }
             }
         }
         __syncthreads();
