@@ -692,7 +692,8 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
     int* __restrict__ ccount, uint8_t* __restrict__ pprev, int sbsz) {
     __shared__ __attribute__((aligned(16))) uint16_t dsb_hi[SW_ROWS][SW_DP];   // 16.3 KB
     __shared__ __attribute__((aligned(16))) uint16_t dsb_lo[SW_ROWS][SW_DP];   // 16.3 KB
-    __shared__ __attribute__((aligned(16))) float corr_p[4][SW_ROWS][SW_SUB];   // 16 KB
+    __shared__ __attribute__((aligned(16))) float corr_p[2][4][SW_ROWS][SW_SUB];   // 32 KB
+    __shared__ int ll_next;                            // next left-looking item to take
     __shared__ __attribute__((aligned(16))) float fdb[SW_SUB][SW_SUB];         // 16 KB
     __shared__ float fdd[SW_SUB];                      // diag(F') of the block
     __shared__ uint32_t chunk_moved[SW_SB / 32];       // a move in a 32-chunk of the super-block
@@ -786,39 +787,82 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
         }
     };
 
+    // left-looking item it (0 .. 15) for the block at offset on of the super-block:
+    // column tile it % 4, k-slice it / 4, over the 32-chunks c < cend of that slice
+    // (in ascending order, chunks without moves skipped), into corr_p[buf]
+    auto ll_item = [&](int64_t sb0, int on, int it, int cend, int buf) {
+        const int ct = it & 3, sl = it >> 2;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int64_t fcol = sb0 + on + ct * 16 + mrow;
+        const uint16_t* Fh_c = plane_at(Fh, fcol, sb0 + ko);
+        const uint16_t* Fl_c = plane_at(Fl, fcol, sb0 + ko);
+        for (int c = sl; c < cend; c += 4) {
+            if (__builtin_amdgcn_readfirstlane((int)chunk_moved[c]) == 0) continue;
+            const u32x4 fh = *(const u32x4*)(Fh_c + (uint32_t)c * kstep32);
+            const u32x4 fl = *(const u32x4*)(Fl_c + (uint32_t)c * kstep32);
+            const u32x4 dh = *(const u32x4*)(&dsb_hi[mrow][c * 32 + ko]);
+            const u32x4 dl = *(const u32x4*)(&dsb_lo[mrow][c * 32 + ko]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fh), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fl), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dl), as_bf16x8(fh), acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) corr_p[buf][sl][4 * (lane >> 4) + t][ct * 16 + mrow] = acc[t];
+    };
+    // F' fragments of the last two chunks before the block at offset on, for the column
+    // tile and chunk of waves 0 .. 7 (wave w: tile w % 4, chunk on / 32 - 2 + w / 4)
+    u32x4 lf_h = {0u, 0u, 0u, 0u}, lf_l = {0u, 0u, 0u, 0u};
+    auto ll_tail_load = [&](int64_t sb0, int on) {
+        if (wave < 8) {
+            const int c = on / 32 - 2 + (wave >> 2);
+            const int64_t fcol = sb0 + on + (wave & 3) * 16 + mrow;
+            lf_h = *(const u32x4*)(plane_at(Fh, fcol, sb0 + ko) + (uint32_t)c * kstep32);
+            lf_l = *(const u32x4*)(plane_at(Fl, fcol, sb0 + ko) + (uint32_t)c * kstep32);
+        }
+    };
+
     for (int64_t sb0 = 0; sb0 < d; sb0 += sbsz) {
         const int sblen = (int)((d - sb0) < sbsz ? (d - sb0) : sbsz);
         if (tid < SW_SB / 32) chunk_moved[tid] = 0u;
+        // the first block of the super-block has no left-looking correction
+#pragma unroll
+        for (int k = 0; k < 4; ++k) (&corr_p[0][0][0][0])[tid + 1024 * k] = 0.f;
         prefetch(sb0);
         __syncthreads();
         for (int o = 0; o < sblen; o += SW_SUB) {
             const int64_t bs = sb0 + o;
-            // ---- left-looking correction from this super-block's earlier blocks:
-            // 4 column tiles x 4 k-slices of 32-chunks
-            {
-                const int ct = wave & 3, sl = wave >> 2;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                const int64_t fcol = bs + ct * 16 + mrow;
-                const uint16_t* Fh_c = plane_at(Fh, fcol, sb0 + ko);
-                const uint16_t* Fl_c = plane_at(Fl, fcol, sb0 + ko);
-                for (int c = sl; c < o / 32; c += 4) {
-                    if (__builtin_amdgcn_readfirstlane((int)chunk_moved[c]) == 0) continue;
-                    const u32x4 fh = *(const u32x4*)(Fh_c + (uint32_t)c * kstep32);
-                    const u32x4 fl = *(const u32x4*)(Fl_c + (uint32_t)c * kstep32);
-                    const u32x4 dh = *(const u32x4*)(&dsb_hi[mrow][c * 32 + ko]);
-                    const u32x4 dl = *(const u32x4*)(&dsb_lo[mrow][c * 32 + ko]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fh), acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(fl), acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dl), as_bf16x8(fh), acc, 0, 0, 0);
-                }
+            const int nb = (o / SW_SUB) & 1;      // this block's correction buffer
+            // ---- left-looking correction from this super-block's earlier blocks, in
+            // 4 column tiles x 4 k-slices of 32-chunks (slice = chunk % 4).  The chunks
+            // before the previous block were summed while the previous block's chain ran
+            // (items taken by the waves that finished it first); the previous block's two
+            // chunks are added here, each as the last term of its slice, so every slice
+            // is summed in ascending chunk order.
+            if (o >= SW_SUB) {
+                if (wave < 8) {
+                    const int ct = wave & 3;
+                    const int c = o / 32 - 2 + (wave >> 2);
+                    const int sl = c & 3;
+                    f32x4 acc;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) corr_p[sl][4 * (lane >> 4) + t][ct * 16 + mrow] = acc[t];
+                    for (int t = 0; t < 4; ++t) acc[t] = corr_p[nb][sl][4 * (lane >> 4) + t][ct * 16 + mrow];
+                    if (__builtin_amdgcn_readfirstlane((int)chunk_moved[c]) != 0) {
+                        const u32x4 dh = *(const u32x4*)(&dsb_hi[mrow][c * 32 + ko]);
+                        const u32x4 dl = *(const u32x4*)(&dsb_lo[mrow][c * 32 + ko]);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(lf_h), acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dh), as_bf16x8(lf_l), acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dl), as_bf16x8(lf_h), acc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) corr_p[nb][sl][4 * (lane >> 4) + t][ct * 16 + mrow] = acc[t];
+                }
             }
             // the diagonal 64 x 64 block of F (rows bs.., columns bs..), loaded ahead
             *(float4*)&fdb[frr][fcc] = pf_f;
             if (tid < SW_SUB) fdd[tid] = pf_d;
             const int code_in = pf_code;
             const float r_in = pf_r;
+            if (tid == 0) ll_next = 0;
             __syncthreads();
             if (o + SW_SUB < sblen) prefetch(bs + SW_SUB);
 
@@ -827,7 +871,7 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
                 const int64_t col = bs + lane;
                 float r = r_in;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) r += corr_p[k][wave][lane];
+                for (int k = 0; k < 4; ++k) r += corr_p[nb][k][wave][lane];
                 int code = code_in;
                 if (pprev) pprev[j * d + col] = (uint8_t)code;   // the code before the pass
                 float wh = __shfl(cl, code, 64);
@@ -870,6 +914,20 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
             const uint32_t hb = f32_to_bf16_bits(dv);
             dsb_hi[wave][o + lane] = (uint16_t)hb;
             dsb_lo[wave][o + lane] = (uint16_t)f32_to_bf16_bits(dv - __uint_as_float(hb << 16));
+            if (o + SW_SUB < sblen) {
+                // the next block's correction from the chunks before this block (their
+                // value changes are final), items taken in turn by the waves whose chains
+                // are done, so the slowest row's wait absorbs them; then the F' fragments
+                // of this block's two chunks for the next block's remaining terms
+                for (;;) {
+                    int it = 0;
+                    if (lane == 0) it = atomicAdd(&ll_next, 1);
+                    it = __builtin_amdgcn_readfirstlane(it);
+                    if (it >= 16) break;
+                    ll_item(sb0, o + SW_SUB, it, o / 32, nb ^ 1);
+                }
+                ll_tail_load(sb0, o + SW_SUB);
+            }
             __syncthreads();
         }
         // ---- right-looking update of the later residuals of the block's rows:
@@ -920,7 +978,7 @@ __global__ __launch_bounds__(1024, 1) void k_sweep(
             // update) so that lane l adds columns 4 (l % 4) .. + 3 of row l / 4 with one
             // 16-byte read-modify-write
             {
-                float* xp = &corr_p[0][0][0] + wave * 256;
+                float* xp = &corr_p[0][0][0][0] + wave * 256;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) xp[(4 * (lane >> 4) + t) * 16 + mrow] = acc[t];
                 const int rr = lane >> 2;
