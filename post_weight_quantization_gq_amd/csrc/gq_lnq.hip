@@ -623,7 +623,9 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
 //     D hi.F hi + D hi.F lo + D lo.F hi, float32 accumulation):
 //       - inside a super-block, before each 64-block, left-looking from the
 //         super-block's earlier blocks, corr = D_sb[:, 0:o] F'[sb:sb+o, block],
-//         with D_sb (the value changes of the super-block) held in LDS;
+//         with D_sb (the value changes of the super-block) held in LDS; the
+//         terms from all but the previous block are summed while the previous
+//         block's chain runs, by the waves whose chains are done;
 //       - at the end of a super-block, right-looking into the residual array,
 //         R[:, later] += D_sb F'[sb, later], streaming long contiguous panels
 //         of F' with the next two chunks' loads in flight during the current
