@@ -89,10 +89,10 @@ _TRAFFIC = {
     # stage: (workload, source file, digest, bytes read, bytes written) of its main kernel,
     # averaged over the launches that do the work
     "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "80dc741c80ab9adb", 267339818, 16777216),
-    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "cddf0c6a79bd9111", 7094929094, 1384120320),
-    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "e4ccaeb0272f0958", 718173436, 270514176),
-    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "80dc741c80ab9adb", 403084272, 67108864),
-    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "e4ccaeb0272f0958", 1879164924, 85693440),
+    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "cddf0c6a79bd9111", 7068920486, 1384120320),
+    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "5d9ab040b5acecd8", 712660430, 270518272),
+    "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "80dc741c80ab9adb", 403082224, 67108864),
+    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "5d9ab040b5acecd8", 1880197076, 85692416),
     "ganq_pass": ("llama2_7b_attn", "gq_ganq.hip", "68f68676aeca3ee4", 594707889, 252086758),
     "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "623cb61e64e42808", 118509837, 42933),
 }
