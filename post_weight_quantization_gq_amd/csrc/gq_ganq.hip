@@ -390,7 +390,7 @@ __global__ __launch_bounds__(1024, 1) void k_ganq(
     const int* __restrict__ bad, unsigned long long* __restrict__ n_changed) {
     __shared__ __attribute__((aligned(16))) uint16_t esb_hi[GQ_ROWS][GQ_DP];
     __shared__ __attribute__((aligned(16))) uint16_t esb_lo[GQ_ROWS][GQ_DP];
-    __shared__ float corr_p[4][GQ_ROWS][GQ_SUB];
+    __shared__ __attribute__((aligned(16))) float corr_p[4][GQ_ROWS][GQ_SUB];
     __shared__ float lb[GQ_SUB][GQ_SUB];         // lb[t][i] = L[bs + t][bs + i] for t > i, else 0
     __shared__ float ldiag[GQ_SUB];
 
@@ -501,26 +501,51 @@ __global__ __launch_bounds__(1024, 1) void k_ganq(
             __syncthreads();
         }
         // ---- earlier coordinates: S[rows, :sb0] += E_sb U[:sb0, sb]^T, one 16-column
-        // tile per wave
+        // tile per wave.  Two register sets of two 32-chunks alternate, one set's loads in
+        // flight while the other's products run (nch is even: sblen % 64 == 0); the tile's
+        // 16 x 16 sum is transposed through this wave's quarter of corr_p (unused here) so
+        // that lane l adds columns 4 (l % 4) .. + 3 of row l / 4 with one 16-byte
+        // read-modify-write.
         const int ntiles = (int)(sb0 / 16);
         for (int ctile = wave; ctile < ntiles; ctile += GQ_ROWS) {
             const int64_t fcol = (int64_t)ctile * 16 + mrow;
             const uint16_t* Uh_c = plane_at(Uh, fcol, sb0 + ko);
             const uint16_t* Ul_c = plane_at(Ul, fcol, sb0 + ko);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int c = 0; c < nch; ++c) {
-                const u32x4 fh = *(const u32x4*)(Uh_c + (uint32_t)c * kstep32);
-                const u32x4 fl = *(const u32x4*)(Ul_c + (uint32_t)c * kstep32);
-                const u32x4 eh = *(const u32x4*)(&esb_hi[mrow][c * 32 + ko]);
-                const u32x4 el = *(const u32x4*)(&esb_lo[mrow][c * 32 + ko]);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(eh), as_bf16x8(fh), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(eh), as_bf16x8(fl), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(el), as_bf16x8(fh), acc, 0, 0, 0);
-            }
+            u32x4 ah[2], al[2], bh[2], bl[2];
+            auto load2 = [&](u32x4 (&h)[2], u32x4 (&l)[2], int c0) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int rr = 4 * (lane >> 4) + t;
-                if (rr < nrows) S[(row0 + rr) * d + fcol] += acc[t];
+                for (int u = 0; u < 2; ++u) {
+                    h[u] = *(const u32x4*)(Uh_c + (uint32_t)(c0 + u) * kstep32);
+                    l[u] = *(const u32x4*)(Ul_c + (uint32_t)(c0 + u) * kstep32);
+                }
+            };
+            auto mfma2 = [&](const u32x4 (&h)[2], const u32x4 (&l)[2], int c0) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int c = c0 + u;
+                    const u32x4 eh = *(const u32x4*)(&esb_hi[mrow][c * 32 + ko]);
+                    const u32x4 el = *(const u32x4*)(&esb_lo[mrow][c * 32 + ko]);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(eh), as_bf16x8(h[u]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(eh), as_bf16x8(l[u]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(el), as_bf16x8(h[u]), acc, 0, 0, 0);
+                }
+            };
+            load2(ah, al, 0);
+            for (int c0 = 0; c0 < nch; c0 += 4) {
+                if (c0 + 2 < nch) load2(bh, bl, c0 + 2);
+                mfma2(ah, al, c0);
+                if (c0 + 4 < nch) load2(ah, al, c0 + 4);
+                if (c0 + 2 < nch) mfma2(bh, bl, c0 + 2);
+            }
+            float* xp = &corr_p[0][0][0] + wave * 256;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xp[(4 * (lane >> 4) + t) * 16 + mrow] = acc[t];
+            const int rr = lane >> 2;
+            if (rr < nrows) {
+                f32x4* dst = (f32x4*)(S + (row0 + rr) * d + (int64_t)ctile * 16 + 4 * (lane & 3));
+                const f32x4 sv0 = *dst;
+                *dst = sv0 + *(const f32x4*)(xp + 4 * lane);
             }
         }
         __syncthreads();
