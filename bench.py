@@ -93,7 +93,7 @@ _TRAFFIC = {
     "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "5d9ab040b5acecd8", 712660430, 270518272),
     "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "80dc741c80ab9adb", 403082224, 67108864),
     "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "5d9ab040b5acecd8", 1880197076, 85692416),
-    "ganq_pass": ("llama2_7b_attn", "gq_ganq.hip", "68f68676aeca3ee4", 594707889, 252086758),
+    "ganq_pass": ("llama2_7b_attn", "gq_ganq.hip", "dc6ee64370d8c958", 731559625, 259311091),
     "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "623cb61e64e42808", 118509837, 42933),
 }
 
