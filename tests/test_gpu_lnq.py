@@ -287,6 +287,25 @@ def test_lnq_deterministic(device, mid):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
 
 
+@pytest.mark.parametrize("bits", [2, 3])
+def test_whole_layer_run_equals_single_steps(device, mid, bits):
+    """lnq_quantize recomputing every step equals the chain of the single-step entry points
+    (lnq_codebook_update, lnq_assign_sweep) bit for bit, move counts included."""
+    iters = 4
+    C, P, _, nq = gq.lnq_quantize(mid.W, mid.F, bits, iters, ridge_rel=RHO,
+                                  gram_update=gq.GQ_GRAM_DENSE)
+    Cs, Ps, _, _ = gq.lnq_quantize(mid.W, mid.F, bits, 0)
+    moved = []
+    for _ in range(iters):
+        gq.lnq_codebook_update(mid.F, mid.W, Ps, Cs, bits, ridge_rel=RHO)
+        n = torch.zeros(1, dtype=torch.int64, device=device)
+        gq.lnq_assign_sweep(mid.F, mid.W, Cs, Ps, bits, ridge_rel=RHO, n_changed=n)
+        moved.append(int(n.item()))
+    torch.cuda.synchronize()
+    assert moved == [int(v) for v in nq.cpu()], (moved, nq)
+    assert torch.equal(C, Cs) and torch.equal(P, Ps)
+
+
 @pytest.mark.parametrize("d_in,d_out,groups,bits,block", [
     (576, 200, 2, 2, 128),     # ragged matrix-core tiles and 16-row groups, a 64-wide last block
     (256, 48, 1, 4, 256),      # m = 16
