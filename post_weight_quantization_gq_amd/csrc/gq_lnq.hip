@@ -466,47 +466,53 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
     const bool valid = j0 < d_out;
     const int64_t j = valid ? j0 : 0;
 
-    float cv[M];
-#pragma unroll
-    for (int k = 0; k < M; ++k) cv[k] = C[j * M + k];
+    // lane q < M holds c_q; a coordinate's value is read from the lane of its code
+    const float cl = C[j * M + (lane < M ? lane : 0)];
 
     double o = 0.0;
     float gl[M];
-    int cnt[M];
+    uint32_t used = 0u;                  // bit q: this lane saw code q
 #pragma unroll
-    for (int k = 0; k < M; ++k) { gl[k] = 0.f; cnt[k] = 0; }
+    for (int k = 0; k < M; ++k) gl[k] = 0.f;
     if (valid) {
-        // 4 consecutive coordinates per lane and step (d % 32 == 0: aligned vectors)
+        // 4 consecutive coordinates per lane and step (d % 32 == 0: aligned vectors); the
+        // trip count is the same in every lane, so the lanes holding the codebook are
+        // active at every shuffle
         const uint8_t* Pj = P + j * d;
         const float* Rj = R + j * d;
 #pragma unroll 4
-        for (int64_t a0 = 4 * lane; a0 < d; a0 += 256) {
-            const uint32_t c4 = *(const uint32_t*)(Pj + a0);
-            const float4 r4 = *(const float4*)(Rj + a0);
-            float wv[4];
-            if constexpr (WBF16) {
-                const u32x2 w2 = *(const u32x2*)((const uint16_t*)W + j * d + a0);
-                wv[0] = __uint_as_float(w2[0] << 16); wv[1] = __uint_as_float(w2[0] & 0xffff0000u);
-                wv[2] = __uint_as_float(w2[1] << 16); wv[3] = __uint_as_float(w2[1] & 0xffff0000u);
-            } else {
-                const float4 w4 = *(const float4*)((const float*)W + j * d + a0);
-                wv[0] = w4.x; wv[1] = w4.y; wv[2] = w4.z; wv[3] = w4.w;
+        for (int64_t b0 = 0; b0 < d; b0 += 256) {
+            const int64_t a0 = b0 + 4 * lane;
+            const bool in = a0 < d;
+            uint32_t c4 = 0u;
+            float rv[4] = {0.f, 0.f, 0.f, 0.f}, wv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (in) {
+                c4 = *(const uint32_t*)(Pj + a0);
+                const float4 r4 = *(const float4*)(Rj + a0);
+                rv[0] = r4.x; rv[1] = r4.y; rv[2] = r4.z; rv[3] = r4.w;
+                if constexpr (WBF16) {
+                    const u32x2 w2 = *(const u32x2*)((const uint16_t*)W + j * d + a0);
+                    wv[0] = __uint_as_float(w2[0] << 16); wv[1] = __uint_as_float(w2[0] & 0xffff0000u);
+                    wv[2] = __uint_as_float(w2[1] << 16); wv[3] = __uint_as_float(w2[1] & 0xffff0000u);
+                } else {
+                    const float4 w4 = *(const float4*)((const float*)W + j * d + a0);
+                    wv[0] = w4.x; wv[1] = w4.y; wv[2] = w4.z; wv[3] = w4.w;
+                }
             }
-            const float rv[4] = {r4.x, r4.y, r4.z, r4.w};
+            float ck[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int code = (int)((c4 >> (8 * u)) & 0xffu);
-                const float r = rv[u];
-                float ck = cv[0];
+            for (int u = 0; u < 4; ++u) ck[u] = __shfl(cl, (int)((c4 >> (8 * u)) & 0xffu), 64);
+            if (in) {
 #pragma unroll
-                for (int k = 1; k < M; ++k) ck = (code == k) ? cv[k] : ck;
-                const float e = ck - wv[u];
-                o += (double)e * (double)r;
-                if (SOLVE) {
+                for (int u = 0; u < 4; ++u) {
+                    const int code = (int)((c4 >> (8 * u)) & 0xffu);
+                    const float r = rv[u];
+                    const float e = ck[u] - wv[u];
+                    o += (double)e * (double)r;
+                    if (SOLVE) {
+                        used |= code < M ? 1u << code : 0u;
 #pragma unroll
-                    for (int k = 0; k < M; ++k) {
-                        gl[k] += (code == k) ? r : 0.f;
-                        cnt[k] += (code == k) ? 1 : 0;
+                        for (int k = 0; k < M; ++k) gl[k] += (code == k) ? r : 0.f;
                     }
                 }
             }
@@ -517,12 +523,11 @@ __global__ __launch_bounds__(256) void k_solve(const float* __restrict__ part, i
     if (!SOLVE) return;
 
 #pragma unroll
+    for (int off = 32; off > 0; off >>= 1) used |= (uint32_t)__shfl_xor((int)used, off, 64);
+#pragma unroll
     for (int k = 0; k < M; ++k) {
         const double s = wave_sum_f64((double)gl[k]);
-        int c = cnt[k];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
-        if (lane == 0) { sg[wave][k] = s; scnt[wave][k] = c; }
+        if (lane == 0) { sg[wave][k] = s; scnt[wave][k] = (int)((used >> k) & 1u); }
     }
     // B_j[q'][q] = sum over a-tiles of part[ta][(j M + q) M + q'], stored as sB[q][q'],
     // so that A = B + B^T.  From the changed coordinates instead (mode 1): sB = A / 2
