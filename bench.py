@@ -89,10 +89,10 @@ _TRAFFIC = {
     # stage: (workload, source file, digest, bytes read, bytes written) of its main kernel,
     # averaged over the launches that do the work
     "lnq_gram": ("llama2_7b_attn", "gq_lnq_mm.hip", "80dc741c80ab9adb", 267339818, 16777216),
-    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "cddf0c6a79bd9111", 7068920486, 1384120320),
-    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "5d9ab040b5acecd8", 712660430, 270518272),
+    "fisher_mfma": ("llama2_7b_attn", "gq_fisher.hip", "cddf0c6a79bd9111", 7052849959, 1384120320),
+    "lnq_sweep": ("llama2_7b_attn", "gq_lnq.hip", "683fbfa5a52f52ca", 710898895, 270519898),
     "lnq_resid": ("llama2_7b_attn", "gq_lnq_mm.hip", "80dc741c80ab9adb", 403082224, 67108864),
-    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "5d9ab040b5acecd8", 1880197076, 85692416),
+    "lnq_delta": ("llama2_7b_attn", "gq_lnq.hip", "683fbfa5a52f52ca", 1879248210, 85692275),
     "ganq_pass": ("llama2_7b_attn", "gq_ganq.hip", "dc6ee64370d8c958", 731559625, 259311091),
     "lut_gemv": ("llama2_70b_down", "gq_lut.hip", "623cb61e64e42808", 118509837, 42933),
 }
