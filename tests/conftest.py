@@ -10,6 +10,8 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    import _progress
+    _progress.bind(config)
 
 
 def pytest_runtest_logstart(nodeid, location):

@@ -26,7 +26,6 @@
     float32 product of the seeded activations, made exactly symmetric, so no
     oracle input comes from the library.
 """
-import sys
 
 import numpy as np
 import pytest
@@ -36,6 +35,7 @@ import oracle as O
 import post_weight_quantization_gq_amd as gq
 from post_weight_quantization_gq_amd import synth
 
+from _progress import say as _say
 from _util import f64, rel_fro, symmetric_f32, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -45,8 +45,7 @@ BF16_TOL = 2e-3
 
 
 def _progress(msg):
-    sys.__stderr__.write(f"[edge] {msg}\n")
-    sys.__stderr__.flush()
+    _say(f"[edge] {msg}")
 
 
 def _wl(name, d_in, d_out, n, groups, bits=3, dtype="bf16", x_kind="gated", outliers=4,

@@ -47,7 +47,6 @@ independent given their group's F', so a sampled row is compared exactly.
   * the layer-wide final objective of the default run is within 1e-3 of the
     run that recomputes every step; the default run's trace is monotone.
 """
-import sys
 import time
 
 import numpy as np
@@ -59,6 +58,7 @@ import post_weight_quantization_gq_amd as gq
 from post_weight_quantization_gq_amd import synth
 
 import _oracle_pool
+from _progress import say as _say
 from _util import to_dev
 
 pytestmark = pytest.mark.gpu
@@ -74,8 +74,7 @@ FREE_ROWS = 32
 
 
 def _progress(msg):
-    sys.__stderr__.write(f"[full-size] {msg}\n")
-    sys.__stderr__.flush()
+    _say(f"[full-size] {msg}")
 
 
 @pytest.fixture(scope="module", params=LAYERS)
